@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""KDA forward (prefill) throughput on one MI355X.
+
+One step = one kda_fwd call over the whole workload (all heads, all
+sequences), inputs resident in HBM.  Default workload: 16 packed sequences,
+65,536 tokens, H = 32, d = 128, bf16 q/k/v/o, fp32 g and beta, bf16 initial
+and final states.  The T = 8192 single-sequence prefill is timed as well and
+reported under "secondary".  Prints one JSON line on stdout; progress goes to
+stderr.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd prefill tokens/s (H=32,d=128) at T=8K and 64K varlen; % of roofline"
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_kda_amd", "csrc", "kda_fwd_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_traffic.json")
+KERNEL_NAME = "kda_fwd_kernel"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def state_bytes_of(dtype_name):
+    return {None: 0, "bf16": 2, "fp32": 4}[dtype_name]
+
+
+def time_workload(wid: int, steps: int, warmup: int):
+    import torch
+
+    from linear_attention_kda_amd import binding, perfmodel
+    from linear_attention_kda_amd.workloads import make_inputs
+
+    x = make_inputs(wid, "cuda")
+    w = x["workload"]
+    dev = x["q"].device
+    N, H = w.num_states, w.H
+    sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    final = torch.empty(N, H, 128, 128, dtype=sdt[w.final_state], device=dev) \
+        if w.final_state else None
+    out = torch.empty_like(x["v"])
+
+    def step():
+        binding.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
+                    initial_state=x["initial_state"], final_state=final,
+                    cu_seqlens=x["cu_seqlens"], out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_ms = statistics.fmean(launch_ms)
+    tokens = w.tokens
+    nbytes = perfmodel.workload_bytes(tokens, H, N, state_bytes_of(w.init_state),
+                                      state_bytes_of(w.final_state))
+    flops = perfmodel.workload_flops(tokens, H)
+    res = dict(
+        workload=w, tokens=tokens, N=N, H=H, total_ms=total_ms, wall_s=wall,
+        ms_per_step=total_ms / steps, kernel_ms=kernel_ms,
+        kernel_ms_median=statistics.median(launch_ms), kernel_ms_min=min(launch_ms),
+        tokens_per_s=tokens * steps / (total_ms * 1e-3),
+        bytes_per_launch=nbytes, flops_per_launch=flops,
+        achieved_gbs=nbytes / (kernel_ms * 1e-3) / 1e9,
+        achieved_tflops=flops / (kernel_ms * 1e-3) / 1e12,
+        lengths=x["lengths"],
+    )
+    res["hbm_frac"] = res["achieved_gbs"] / perfmodel.HBM_PEAK_GBS
+    res["mfma_frac"] = res["achieved_tflops"] / perfmodel.BF16_PEAK_TFLOPS
+    host = None
+    del out, final
+    return res, x, host
+
+
+def measured_traffic(wid: int):
+    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha() or t.get("workload") != wid:
+        return None
+    return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+
+
+def cpu_baseline(x, heads: int):
+    """The fp64 oracle, as it stands, on `heads` heads of the same workload."""
+    import numpy as np  # noqa: F401
+
+    from oracle import oracle
+    w = x["workload"]
+    hs = list(range(min(heads, w.H)))
+    sel = lambda t: t[:, :, hs].cpu()  # noqa: E731
+    init = x["initial_state"]
+    args = [sel(x[k]) for k in ("q", "k", "v", "g", "beta")]
+    s0 = None if init is None else init[:, hs].cpu()
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].cpu()
+    threads = oracle.max_threads()
+    col_block = 16
+    tasks = w.num_states * len(hs) * (128 // col_block)
+    t0 = time.perf_counter()
+    oracle.fwd(*args, x["scale"], s0, cu_seqlens=cu, col_block=col_block)
+    dt = time.perf_counter() - t0
+    tokens_equiv = w.tokens * len(hs) / w.H  # all-head-equivalent tokens
+    return dict(value=tokens_equiv / dt, unit="tokens/s", cores=min(threads, tasks),
+                kind="oracle",
+                sample=(f"{w.name}: all {w.tokens} tokens of {len(hs)} of {w.H} heads "
+                        f"({dt:.1f} s); value scaled to all heads"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--secondary", type=int, default=1,
+                    help="second workload timed and reported under 'secondary' (-1: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the KDA forward pass shards by heads and "
+              "sequences with no communication, and this build measures one GPU's share "
+              "(see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(2)
+    from linear_attention_kda_amd import binding, perfmodel
+    binding.load_library()
+
+    log(f"[bench] workload {args.workload}, warmup {args.warmup}, steps {args.steps}")
+    r, x, _ = time_workload(args.workload, args.steps, args.warmup)
+    w = r["workload"]
+    log(f"[bench] {w.name}: {r['ms_per_step']:.3f} ms/step, kernel {r['kernel_ms']:.3f} ms, "
+        f"{r['tokens_per_s'] / 1e6:.2f} M tokens/s, {r['achieved_gbs']:.0f} GB/s "
+        f"({100 * r['hbm_frac']:.1f}% of HBM peak)")
+    wg, ns = binding.plan(r["N"], r["H"])
+    traffic = measured_traffic(args.workload)
+
+    secondary = None
+    if args.secondary >= 0 and args.secondary != args.workload:
+        log(f"[bench] secondary workload {args.secondary}")
+        r2, x2, _ = time_workload(args.secondary, args.steps, args.warmup)
+        w2 = r2["workload"]
+        log(f"[bench] {w2.name}: {r2['kernel_ms']:.3f} ms, "
+            f"{r2['tokens_per_s'] / 1e6:.2f} M tokens/s, {100 * r2['hbm_frac']:.1f}% of HBM peak")
+        secondary = {"workload": w2.name, "value": r2["tokens_per_s"], "unit": "tokens/s",
+                     "ms_per_step": r2["ms_per_step"],
+                     "roofline": {"bound": "hbm", "achieved": r2["achieved_gbs"],
+                                  "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": r2["hbm_frac"], "traffic": None},
+                     "mfma_frac": r2["mfma_frac"]}
+        del x2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads of {w.name}")
+        cpu = cpu_baseline(x, args.cpu_heads)
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": r["tokens"], "sequences": r["N"],
+                   "lengths": r["lengths"], "heads": r["H"], "head_dim": 128, "chunk": 64,
+                   "state_dtype": w.final_state, "global_batch": w.B, "seq_len": w.T,
+                   "parallelism": "single GPU", "workgroups": wg, "value_splits": ns},
+        "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"],
+                     "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s", "frac": r["hbm_frac"],
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "algorithmic_bytes": r["bytes_per_launch"],
+                     "kernel_ms": r["kernel_ms"]},
+        "mfma": {"achieved": r["achieved_tflops"], "peak": perfmodel.BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": r["mfma_frac"],
+                 "flops_model": "6Td^2+3TCd+TC^2 per head"},
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention forward pass.
+ *
+ * The operation (one independent recurrence per sequence n and head h):
+ *
+ *   S_t = (Diag(alpha_t) - beta_t k_t (k_t ⊙ alpha_t)^T) S_{t-1} + beta_t k_t v_t^T,
+ *   alpha_t = exp(g_t)   (a per-channel decay vector),
+ *   o_t     = scale * S_t^T q_t   (readout after the update at t),
+ *
+ * with S a 128 x 128 (d_k x d_v) state
+ *   [core.today "Kimi Linear 특집", ch.4 혁신 1 (channel-wise gate) and 혁신 2
+ *    (state-update equation); ch.2 (linear-attention readout Q(K^T V));
+ *    ch.8 (fixed 128 x 128 state)].
+ * It is evaluated chunk by chunk (64 tokens) with the WY/UT form of the
+ * diagonal-plus-low-rank transition [core.today ch.4 혁신 2, chunkwise remark;
+ * hnts03 "논문 리뷰: Kimi Delta Attention", section "Kimi Delta Attention"].
+ *
+ * Argument conventions follow the kernel API the pages describe
+ * [trend.ondo.sh "MoonshotAI/FlashKDA", section "커널 API와 제약 조건"]:
+ * K = V = 128 only; variable-length packing through cu_seqlens requires
+ * B = 1; the initial and final states are each bf16, fp32 or absent, and
+ * must have the same dtype when both are given.
+ *
+ * Ownership: every pointer is caller-owned memory; the library never retains
+ * or frees it and allocates no device memory of its own.
+ * Asynchrony: kda_fwd enqueues work on `stream` (a hipStream_t, or NULL for
+ * the null stream) and returns; results are valid after the caller
+ * synchronises that stream.  Calls are thread-safe (no global mutable state
+ * except the thread-local error text).
+ * Errors: invalid arguments are rejected before any launch with a negative
+ * status and no output touched; kda_last_error() then holds a description.
+ * There is no fallback path.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+#define KDA_CHUNK 64
+
+typedef enum {
+  KDA_BF16 = 0, /* bfloat16, round-to-nearest-even on store */
+  KDA_FP32 = 1  /* IEEE float32 */
+} kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,         /* a required pointer is NULL */
+  KDA_ERR_HEAD_DIM = -2,     /* K or V is not 128 */
+  KDA_ERR_VARLEN_BATCH = -3, /* cu_seqlens given with B != 1 */
+  KDA_ERR_STATE_DTYPE = -4,  /* both states given with different dtypes */
+  KDA_ERR_DTYPE = -5,        /* a dtype argument is not a kda_dtype */
+  KDA_ERR_SHAPE = -6,        /* B, H, num_seqs <= 0, T < 0, or sizes overflow */
+  KDA_ERR_ALIGN = -7,        /* a pointer is not aligned as required below */
+  KDA_ERR_HIP = -8           /* the HIP runtime reported an error (see kda_last_error) */
+} kda_status;
+
+/*
+ * kda_fwd — chunkwise KDA forward pass (prefill).
+ *
+ *  q, k, v    device, bf16, [B, T, H, 128] contiguous (channel fastest), 16-byte
+ *             aligned.  The kernel does not normalise q or k.
+ *  g          device, fp32, [B, T, H, 128], 16-byte aligned: the log-decay,
+ *             alpha = exp(g) taken as given (g <= 0 expected).  Range limit of
+ *             the chunked evaluation: within each 16-token block aligned to the
+ *             start of a 64-token chunk, the per-channel sum of -g must stay
+ *             below 80 (g >= -5 everywhere is sufficient); beyond that the
+ *             intra-chunk exponent factors overflow fp32.
+ *  beta       device, fp32, [B, T, H], 4-byte aligned: write strength, as given.
+ *  scale      multiplies every output (callers usually pass 1/sqrt(128)).
+ *  initial_state / initial_dtype
+ *             device, [N, H, 128, 128] (d_k-major: element (i, j) at i*128 + j),
+ *             16-byte aligned, or NULL for a zero initial state.
+ *  final_state / final_dtype
+ *             device, [N, H, 128, 128], 16-byte aligned, or NULL when not
+ *             wanted.  It may alias initial_state (each state is read in full
+ *             before it is overwritten).
+ *  cu_seqlens device, int32, [num_seqs + 1], or NULL.  When given: B must be 1,
+ *             cu_seqlens[0] = 0, non-decreasing, cu_seqlens[num_seqs] <= T;
+ *             sequence n is rows [cu_seqlens[n], cu_seqlens[n+1]) and N =
+ *             num_seqs.  The library never reads it on the host; it is not
+ *             validated beyond the pointer.  Zero-length sequences are allowed
+ *             (their final state equals their initial state).
+ *             When NULL: every batch row is one sequence of T tokens, N = B,
+ *             and num_seqs is ignored.
+ *  B, T, H    batch rows, tokens per row (packed total when varlen), heads.
+ *  K, V       head dimensions; must both be 128.
+ *  out        device, bf16, [B, T, H, 128], 16-byte aligned; rows outside every
+ *             sequence (varlen with cu_seqlens[num_seqs] < T) are not written.
+ *  stream     hipStream_t to launch on (NULL = null stream).
+ */
+kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   float scale, const void* initial_state, int initial_dtype, void* final_state,
+                   int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                   int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream);
+
+/*
+ * kda_fwd_check — the host-side validation kda_fwd performs, without any
+ * launch or device access (pointers are only tested for NULL and alignment).
+ * Same arguments and status codes as kda_fwd.
+ */
+kda_status kda_fwd_check(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const void* initial_state,
+                         int initial_dtype, const void* final_state, int final_dtype,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                         int32_t H, int32_t K, int32_t V, const void* out);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/*
+ * kda_plan — the launch plan kda_fwd uses for N independent sequences
+ * (num_seqs, or B without cu_seqlens) and H heads on a device with cu_count
+ * compute units (cu_count <= 0: query the current HIP device): the number of
+ * workgroups launched and the number of value-column slices per (sequence,
+ * head).  The environment variable KDA_VSPLIT (1 or 2) overrides the slice
+ * count.  Host only; returns KDA_ERR_SHAPE for N <= 0 or H <= 0, KDA_ERR_NULL
+ * for NULL outputs, KDA_ERR_HIP if the device query fails.
+ */
+kda_status kda_plan(int32_t n_sequences, int32_t H, int32_t cu_count, int32_t* workgroups,
+                    int32_t* value_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,161 @@
+"""Thin ctypes binding of the C ABI in include/kda.h (argument marshalling only).
+
+Every step of the forward pass runs in the HIP kernels of libkda.so; this
+module checks tensor dtypes, shapes, devices and contiguity, passes raw device
+pointers and the current HIP stream, and turns negative status codes into
+KdaError.  There is no fallback: if libkda.so is missing or was built for
+another target, calls fail loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+KDA_BF16 = 0
+KDA_FP32 = 1
+D = 128
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where} failed with status {status}: {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so from the package directory (raises if it was never built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise FileNotFoundError(
+                f"{_LIB_PATH} is missing: build it with `python -m linear_attention_kda_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.kda_fwd.restype = ctypes.c_int
+        lib.kda_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_int, _vp,
+                                ctypes.c_int, _vp, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp]
+        lib.kda_fwd_check.restype = ctypes.c_int
+        lib.kda_fwd_check.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_int,
+                                      _vp, ctypes.c_int, _vp, _i32, _i32, _i64, _i32, _i32, _i32,
+                                      _vp]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_last_error.argtypes = []
+        lib.kda_plan.restype = ctypes.c_int
+        lib.kda_plan.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        _lib = lib
+        return lib
+
+
+def _detail(lib, status: int) -> str:
+    msg = lib.kda_last_error().decode()
+    return msg or lib.kda_status_string(status).decode()
+
+
+def _state_dtype(t) -> int:
+    import torch
+    if t is None:
+        return KDA_FP32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"states must be bfloat16 or float32, got {t.dtype}")
+
+
+def plan(n_sequences: int, heads: int, cu_count: int = 0) -> tuple[int, int]:
+    """(workgroups, value_splits) that kda_fwd launches for these sizes."""
+    lib = load_library()
+    wg, ns = _i32(0), _i32(0)
+    st = lib.kda_plan(n_sequences, heads, cu_count, ctypes.byref(wg), ctypes.byref(ns))
+    if st != 0:
+        raise KdaError(st, "kda_plan", _detail(lib, st))
+    return wg.value, ns.value
+
+
+def fwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, initial_state=0,
+              initial_dtype=KDA_FP32, final_state=0, final_dtype=KDA_FP32, cu_seqlens=0,
+              num_seqs=0, scale=1.0) -> int:
+    """Host-only validation with raw (never dereferenced) addresses; returns the status."""
+    lib = load_library()
+    return lib.kda_fwd_check(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
+                             final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out)
+
+
+def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_state=None,
+        cu_seqlens=None, out=None, output_final_state: bool = False):
+    """KDA chunkwise forward pass on the current HIP stream.
+
+    q, k, v: bf16 [B, T, H, 128]; g: fp32 [B, T, H, 128] (log-decay, alpha = exp(g));
+    beta: fp32 [B, T, H]; scale defaults to 1/sqrt(128); initial_state /
+    final_state: [N, H, 128, 128] bf16 or fp32 (same dtype when both given;
+    final_state may be the same tensor as initial_state); cu_seqlens: int32
+    [N+1] on the device (requires B = 1).  With output_final_state=True and no
+    final_state tensor, one is allocated (dtype of initial_state, else fp32).
+    Returns out, or (out, final_state) when a final state is produced.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3]:
+        raise ValueError("inconsistent shapes: q, k, g [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev \
+                or not cu_seqlens.is_contiguous():
+            raise TypeError("cu_seqlens must be a contiguous int32 tensor on the same device")
+        num_seqs = cu_seqlens.numel() - 1
+    N = num_seqs if cu_seqlens is not None else B
+    if out is None:
+        out = torch.empty(B, T, H, V, dtype=torch.bfloat16, device=dev)
+    elif out.shape != (B, T, H, V) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [B, T, H, V] tensor")
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and (t.shape != (N, H, K, V) or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous [{N}, {H}, {K}, {V}] tensor on {dev}")
+    if final_state is None and output_final_state:
+        dt = initial_state.dtype if initial_state is not None else torch.float32
+        final_state = torch.empty(N, H, K, V, dtype=dt, device=dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.kda_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale),
+                         ptr(initial_state), _state_dtype(initial_state), ptr(final_state),
+                         _state_dtype(final_state), ptr(cu_seqlens), num_seqs, B, T, H, K, V,
+                         ptr(out), stream)
+    if st != 0:
+        raise KdaError(st, "kda_fwd", _detail(lib, st))
+    return (out, final_state) if final_state is not None else out

@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI boundary: the library loads, exports what the header
+declares, and rejects invalid arguments with the documented status codes
+before touching any device (no compute calls without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_kda_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, ERR_NULL, ERR_HEAD_DIM, ERR_VARLEN_BATCH, ERR_STATE_DTYPE, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+# fake, never dereferenced, 16-byte aligned addresses
+P = 0x10000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libkda.so is not built (run python -m linear_attention_kda_amd.build)")
+    return binding.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == ["kda_fwd", "kda_fwd_check", "kda_last_error", "kda_plan",
+                                  "kda_status_string"]
+
+
+def test_library_exports_every_header_symbol(lib):
+    cdll = ctypes.CDLL(binding.library_path())
+    for name in header_functions():
+        assert hasattr(cdll, name), name
+
+
+def ok_args(**over):
+    a = dict(B=1, T=256, H=4, K=128, V=128, q=P, k=P + 0x1000, v=P + 0x2000, g=P + 0x3000,
+             beta=P + 0x4000, out=P + 0x5000)
+    a.update(over)
+    return a
+
+
+def test_check_accepts_valid_arguments(lib):
+    assert binding.fwd_check(**ok_args()) == OK
+    assert binding.fwd_check(**ok_args(initial_state=P, initial_dtype=0, final_state=P,
+                                       final_dtype=0)) == OK
+    assert binding.fwd_check(**ok_args(cu_seqlens=P, num_seqs=3)) == OK
+    assert binding.fwd_check(**ok_args(T=0, q=0, k=0, v=0, g=0, beta=0, out=0)) == OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(K=64), ERR_HEAD_DIM),
+    (dict(V=256), ERR_HEAD_DIM),
+    (dict(B=2, cu_seqlens=P, num_seqs=2), ERR_VARLEN_BATCH),
+    (dict(cu_seqlens=P, num_seqs=0), ERR_SHAPE),
+    (dict(initial_state=P, initial_dtype=0, final_state=P + 64, final_dtype=1), ERR_STATE_DTYPE),
+    (dict(initial_state=P, initial_dtype=2), ERR_DTYPE),
+    (dict(final_state=P, final_dtype=-1), ERR_DTYPE),
+    (dict(B=0), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(T=-1), ERR_SHAPE),
+    (dict(q=0), ERR_NULL),
+    (dict(beta=0), ERR_NULL),
+    (dict(out=0), ERR_NULL),
+    (dict(k=P + 8), ERR_ALIGN),
+    (dict(g=P + 4), ERR_ALIGN),
+    (dict(beta=P + 2), ERR_ALIGN),
+    (dict(initial_state=P + 8, initial_dtype=1), ERR_ALIGN),
+])
+def test_check_rejections(lib, over, status):
+    assert binding.fwd_check(**ok_args(**over)) == status
+    assert lib.kda_last_error().decode() != ""
+    assert lib.kda_status_string(status).decode() not in ("", "unknown status")
+
+
+def test_state_dtype_ignored_for_absent_state(lib):
+    assert binding.fwd_check(**ok_args(initial_dtype=7)) == OK
+
+
+def test_plan_value_split(lib):
+    # fewer (sequence, head) pairs than CUs -> two value slices per pair
+    assert binding.plan(1, 32, 256) == (64, 2)
+    assert binding.plan(16, 32, 256) == (512, 1)
+    assert binding.plan(4, 32, 256) == (256, 2)
+    assert binding.plan(8, 32, 256) == (256, 1)
+    assert binding.plan(3, 3, 256) == (32, 2)   # 9 pairs padded to 16, times 2 slices
+    with pytest.raises(binding.KdaError):
+        binding.plan(0, 32, 256)
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fwd(x, x, x, x.float(), torch.zeros(1, 4, 1))
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package (Python and native sources) must not import, load or call oracle/."""
+    pkg = os.path.join(ROOT, "linear_attention_kda_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"(from\s+oracle|import\s+oracle|oracle\.\w+\(|kda_oracle)",
+                                     text), f"{f} reaches into oracle/"
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        assert "oracle" not in open(os.path.join(ROOT, "include", f)).read()
