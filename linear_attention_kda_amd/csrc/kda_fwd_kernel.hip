@@ -7,30 +7,40 @@
 // evaluated 64 tokens at a time with the WY/UT form of the diagonal-plus-low-rank
 // transition [same page, ch.4 혁신 2, chunkwise remark].  For one chunk with start
 // state S (128 x 128, S[c][j]: c key channel, j value channel), local rows r, i,
-// G = within-chunk inclusive cumsum of g, Gamma = exp(G):
+// G = within-chunk inclusive cumsum of g:
 //   A[r][i] = b_r sum_c k_rc k_ic exp(G_rc - G_ic)   (i < r)      (L = I + A)
-//   Y       = V - (K*Gamma) S
+//   Y       = V - (K * exp(G)) S
 //   U       = L^-1 diag(b) Y          (= b_r times the delta-rule error of row r)
 //   M[r][i] = sum_c q_rc k_ic exp(G_rc - G_ic)        (i <= r)
-//   O       = scale * ((Q*Gamma) S + M U)
-//   S'      = Diag(Gamma_last) S + (K * exp(G_last - G))^T U
+//   O       = scale * ((Q * exp(G)) S + M U)
+//   S'      = Diag(exp(G_last)) S + (K * exp(G_last - G))^T U
 //
-// Mapping: one workgroup of 4 waves owns one (sequence, head, value-column slice)
-// and walks its chunks in order.  The fp32 state slice lives in MFMA accumulator
-// registers for the whole sequence (never in LDS or HBM); each wave owns 16*JT
-// value columns.  The value-independent per-chunk work (gating, A, M, the
-// diagonal-block inverses) is recomputed by every value slice of a head.
-// Per chunk:  gating (VALU, exp2) -> LDS operand tiles -> A and M tiles (bf16
-// MFMA 16x16x32) and the four 16x16 diagonal-block inverses (fp32 VALU forward
-// substitution) -> per-wave state pass: Y (MFMA), block forward substitution
-// for U (MFMA 16x16x16), O (MFMA, written straight to HBM), S update (MFMA).
-// The next chunk's q/k/v/g/beta loads are issued right after the gating step and
-// stay in flight during the MFMA work.
+// Exponent bookkeeping.  The chunk splits into four 16-row blocks; X_b is G at
+// the last row of block b-1 (X_0 = 0, X_4 = G_last).  With F_r = exp(G_r - X_b)
+// and H_r = exp(X_{b+1} - G_r) for r in block b (both <= 1):
+//  * Kr = K*F and Qr = Q*F are the row operands of A and M, Kh = K*H the column
+//    operand; tile (rb, ib) takes the per-channel factor exp(X_rb - X_{ib+1}) on
+//    the row operand (<= 1 off the diagonal, 1 for ib = rb-1, and bounded by one
+//    block's decay on the diagonal: the per-channel sum of -g over a 16-token block
+//    must stay below ~88 in natural log);
+//  * K*exp(G) = Kr * exp(X_b): the state pass multiplies the rows of its bf16 state
+//    copy by exp(X_b) per row block instead of reading separate K*exp(G), Q*exp(G);
+//  * K*exp(G_last - G) = Kh * exp(G_last - X_{b+1}).
+// F and H are running products of a = exp(g) along the rows.
 //
-// Exponent ranges: every exp factor that multiplies an MFMA operand is <= 1,
-// except exp(G_r - G_{end of r's 16-row block}) on the diagonal blocks of A and
-// M, which is bounded by the decay inside one 16-token block (this is why the
-// per-channel sum of -g over such a block must stay below ~88 in natural log).
+// Mapping: one workgroup of 8 waves owns one (sequence, head, value-column slice)
+// and walks its chunks in order as a two-stage pipeline with three barriers per
+// chunk (phases A, B, C):
+//  * waves 0-3 ("state waves") run chunk c: phase A  Y and (Q exp(G)) S;
+//    phase B  U by block forward substitution, the output, the state update;
+//    phase C  the M tiles of chunk c+1.  The fp32 state slice (16*JT value
+//    columns per wave) lives in MFMA accumulator registers for the whole sequence.
+//  * waves 4-7 ("prep waves") prepare chunk c+1: phase A  the inverses of the
+//    diagonal blocks of L for chunk c and the row sums of g for chunk c+1;
+//    phase B  gating (VALU, exp2) into the operand tiles, and the loads of chunk
+//    c+2; phase C  the A tiles and the state-update operand of chunk c+1.
+// Each tile is rewritten only after the phase in which the state waves last read
+// it.  The value-independent per-chunk work is recomputed by every value slice.
 //
 // MFMA operand layouts used below (64 lanes, q = lane/16, m = lane%16):
 //  16x16x32 bf16:  A[m][8q+e], B[8q+e][m] (e < 8),  D[4q+t][m] (t < 4)
@@ -54,36 +64,38 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // head dimension
-constexpr int NT = 256;      // threads per workgroup (4 waves)
+constexpr int NT = 512;      // threads per workgroup: 4 state waves + 4 prep waves
+constexpr int NP = 256;      // prep threads
 constexpr int TS = D + 8;    // row stride (bf16) of token-major [64][128] tiles: 272 B
 constexpr int CS = C + 4;    // row stride (bf16) of channel-major [.][64] tiles: 136 B
 constexpr int QS = C + 4;    // row stride (bf16) of [64][64] tiles: 136 B
 constexpr int LS = 16 + 4;   // row stride (bf16) of the diagonal-block inverses
-constexpr int NS = 16 + 4;   // row stride (fp32) of the diagonal blocks of A
+constexpr int NS = 16 + 4;   // row stride (fp32) of the transposed diagonal blocks of A
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Shared-memory plan (bytes); one workgroup per CU.
+// Shared-memory plan; one workgroup per CU.
 template <int NV>
 struct alignas(16) Smem {
-  __bf16 kr[C * TS];    // K * exp(G - X_b)            row operand of A      (<= 1)
-  __bf16 qr[C * TS];    // Q * exp(G - X_b)            row operand of M      (<= 1)
-  __bf16 kh[C * TS];    // K * exp(X_{b+1} - G)        column operand of A, M (<= 1)
-  __bf16 kg[C * TS];    // K * Gamma                   for Y = V - (K*Gamma) S
-  __bf16 qg[C * TS];    // Q * Gamma                   for O = (Q*Gamma) S + ...
+  __bf16 kr[C * TS];    // K * F                       A row operand; state pass
+  __bf16 qr[C * TS];    // Q * F                       M row operand; state pass
+  __bf16 kh[C * TS];    // K * H                       A and M column operand
   __bf16 kpt[D * CS];   // (K * exp(G_last - G))^T     channel-major, state update
   __bf16 vt[NV * CS];   // V^T (this slice's columns)  channel-major
   __bf16 mm[C * QS];    // M (lower incl. diagonal), zero elsewhere
   __bf16 an[C * QS];    // -A on the off-diagonal 16x16 blocks
   __bf16 li[C * LS];    // inverses of the 4 diagonal blocks of L = I + A
-  float nd[4 * 16 * NS];  // diagonal 16x16 blocks of A (fp32)
+  float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A, transposed: [b][i][r]
+  float ex[4 * D];      // exp(X_b) per block and channel
   float gamc[D];        // exp(G_last) per channel
-  float beta[C];
-  float seg[8 * D];     // per 8-row group, per channel: sum of g*log2(e)
+  float beta[C];        // beta of the chunk in the state pass
+  float pbeta[C];       // beta of the chunk being prepared
+  float seg[8 * D];     // per 8-row group and channel: sum of g*log2(e)
   float pf[10 * D];     // exp(X_rb - X_{ib+1}) per (rb, ib <= rb) pair and channel
   int order;            // sequence chosen for this workgroup
 };
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16x2 v;
@@ -97,12 +109,10 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 }
 
 __device__ __forceinline__ void unpack4(uint2 u, float* f) {
-  bf16x2 lo = __builtin_bit_cast(bf16x2, u.x);
-  bf16x2 hi = __builtin_bit_cast(bf16x2, u.y);
-  f[0] = bf2f(lo[0]);
-  f[1] = bf2f(lo[1]);
-  f[2] = bf2f(hi[0]);
-  f[3] = bf2f(hi[1]);
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -137,13 +147,58 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // (rb, ib) enumeration of the 10 lower-triangular 16x16 block pairs.
 __device__ __forceinline__ int pair_rb(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
 __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_rb(p) + 1)) / 2; }
 
-// Raw inputs of one chunk held by one thread: rows 8*rg..8*rg+7, channels 4*cg..4*cg+3.
+// One 16x16 tile of A (rowsrc = Kr) or M (rowsrc = Qr): lane (q4, m16) gets
+// tile[r = 16rb + m16][i = 16ib + 4q4 + t].  The row operand is scaled per
+// channel by exp(X_rb - X_{ib+1}) unless ib == rb - 1, where that factor is 1.
+template <int NV>
+__device__ __forceinline__ f32x4 tile_product(const Smem<NV>& sm, const __bf16* rowsrc, int pr,
+                                              int q4, int m16) {
+  const int rb = pair_rb(pr), ib = pair_ib(pr);
+  const bool scaled = ib != rb - 1;
+  bf16x8 rf[4], cf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c0 = 32 * ks + 8 * q4;
+    rf[ks] = ld8(&rowsrc[(16 * rb + m16) * TS + c0]);
+    cf[ks] = ld8(&sm.kh[(16 * ib + m16) * TS + c0]);
+  }
+  if (scaled) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c0 = 32 * ks + 8 * q4;
+      const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0 + 4]);
+      const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rf[ks][e] = (__bf16)(bf2f(rf[ks][e]) * fs[e]);
+    }
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) acc = mfma32(cf[ks], rf[ks], acc);  // D[i][r]
+  return acc;
+}
+
+struct Work {
+  int64_t bos;   // first token of the sequence
+  int64_t len;   // tokens in the sequence
+  int h;         // head
+  int j0;        // first value column of this workgroup's slice
+  int nchunks;
+};
+
+// Buffer descriptor over `bytes` bytes from `base`; loads beyond the range return
+// zero and stores beyond it are dropped (raw buffer, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// ============================================================================ prep waves
+// Prep thread t (0..255) owns rows 8*rg..8*rg+7 and channels 4*cg..4*cg+3 of a chunk.
 template <int NV>
 struct ChunkRegs {
   float4 g[8];
@@ -153,46 +208,467 @@ struct ChunkRegs {
   float beta;
 };
 
+// Loads chunk `ch` of the sequence.  Each tensor gets a descriptor that starts at
+// the chunk's first row and covers exactly its `valid` rows, so rows past the end
+// of a partial last chunk read as zero (zero rows leave the recurrence unchanged:
+// k = 0, v = 0, beta = 0, g = 0).
 template <int NV>
-__device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, int64_t tok0,
-                                           int valid, int h, int j0, int tid) {
-  const int rg = tid >> 5, cg = tid & 31;
-  const int64_t HD = (int64_t)p.H * D;
+__device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, const Work& w,
+                                           int ch, int t) {
+  const int rg = t >> 5, cg = t & 31;
+  const int64_t tok0 = w.bos + (int64_t)ch * C;
+  const int64_t rest = w.len - (int64_t)ch * C;
+  const int valid = rest < C ? (int)rest : C;
+  const int HD = p.H * D;
+  const int64_t base = tok0 * HD + (int64_t)w.h * D;
+  const auto rg_ = rsrc(p.g + base, valid * HD * 4);
+  const auto rq_ = rsrc(p.q + base, valid * HD * 2);
+  const auto rk_ = rsrc(p.k + base, valid * HD * 2);
+  const auto rv_ = rsrc(p.v + base + w.j0, valid * HD * 2);
+  const auto rb_ = rsrc(p.beta + tok0 * p.H + w.h, valid * p.H * 4);
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) {
     const int row = rg * 8 + r8;
-    if (row < valid) {
-      const int64_t base = (tok0 + row) * HD + (int64_t)h * D;
-      R.g[r8] = *reinterpret_cast<const float4*>(p.g + base + 4 * cg);
-      R.q[r8] = *reinterpret_cast<const uint2*>(p.q + base + 4 * cg);
-      R.k[r8] = *reinterpret_cast<const uint2*>(p.k + base + 4 * cg);
-      if constexpr (NV == 128) {
-        uint2 t = *reinterpret_cast<const uint2*>(p.v + base + j0 + 4 * cg);
-        R.v[r8][0] = t.x;
-        R.v[r8][1] = t.y;
-      } else {
-        R.v[r8][0] = *reinterpret_cast<const uint32_t*>(p.v + base + j0 + 2 * cg);
-      }
+    const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg_, row * HD * 4 + 16 * cg, 0, 0);
+    R.g[r8] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+    const auto qv = __builtin_amdgcn_raw_buffer_load_b64(rq_, row * HD * 2 + 8 * cg, 0, 0);
+    const auto kv = __builtin_amdgcn_raw_buffer_load_b64(rk_, row * HD * 2 + 8 * cg, 0, 0);
+    R.q[r8] = make_uint2(qv[0], qv[1]);
+    R.k[r8] = make_uint2(kv[0], kv[1]);
+    if constexpr (NV == 128) {
+      const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rv_, row * HD * 2 + 8 * cg, 0, 0);
+      R.v[r8][0] = vv[0];
+      R.v[r8][1] = vv[1];
     } else {
-      R.g[r8] = make_float4(0.f, 0.f, 0.f, 0.f);
-      R.q[r8] = make_uint2(0u, 0u);
-      R.k[r8] = make_uint2(0u, 0u);
-#pragma unroll
-      for (int x = 0; x < NV / 64; ++x) R.v[r8][x] = 0u;
+      R.v[r8][0] = __builtin_amdgcn_raw_buffer_load_b32(rv_, row * HD * 2 + 4 * cg, 0, 0);
     }
   }
-  R.beta = 0.f;
-  if (tid < C && tid < valid) R.beta = p.beta[(tok0 + tid) * p.H + h];
+  R.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, (t & 63) * p.H * 4, 0, 0));
+}
+
+template <int NV>
+__device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const Work& w) {
+  const int t = threadIdx.x - (NT - NP);   // 0..255
+  const int pw = t >> 6;                   // prep wave 0..3
+  const int lane = t & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int rg = t >> 5, cg = t & 31;
+  const int blk = rg >> 1;                 // 16-row block of this thread's rows
+  const bool second = (rg & 1) != 0;       // rows 8..15 of the block
+  constexpr int VPT = NV / 32;             // value columns per thread
+
+  ChunkRegs<NV> R;
+  if (w.nchunks > 0) load_chunk<NV>(R, p, w, 0, t);
+
+  for (int it = -1; it < w.nchunks; ++it) {
+    const int pc = it + 1;                 // chunk prepared in this iteration
+    const bool act = pc < w.nchunks;
+    uint2 kpt_hold[4][2];                  // channel 4cg+e: rows 8rg..8rg+3, 8rg+4..8rg+7
+    float4 gamc_hold;
+
+    // ---- phase A: inverse of diagonal block pw of L for chunk `it` (used in the
+    // state waves' phase B): right-looking forward substitution, lane j = m16 owns
+    // column j (lanes 16-63 mirror lanes 0-15).
+    if (it >= 0) {
+      const int j = m16;
+      const float* N = &sm.ndt[pw * 16 * NS];  // N[i * NS + r] = A[16pw + r][16pw + i]
+      float xv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xv[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        const float4 c0 = *reinterpret_cast<const float4*>(&N[i * NS + 0]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&N[i * NS + 4]);
+        const float4 c2 = *reinterpret_cast<const float4*>(&N[i * NS + 8]);
+        const float4 c3 = *reinterpret_cast<const float4*>(&N[i * NS + 12]);
+        const float col[16] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                               c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) xv[r] -= col[r] * xv[i];
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.li[(16 * pw + r) * LS + j] = (__bf16)xv[r];
+      }
+    }
+    // per-thread sums of g*log2(e) over its 8 rows, for chunk pc
+    if (act) {
+      float4 s = R.g[0];
+#pragma unroll
+      for (int r8 = 1; r8 < 8; ++r8) {
+        s.x += R.g[r8].x; s.y += R.g[r8].y; s.z += R.g[r8].z; s.w += R.g[r8].w;
+      }
+      *reinterpret_cast<float4*>(&sm.seg[rg * D + 4 * cg]) =
+          make_float4(s.x * LOG2E, s.y * LOG2E, s.z * LOG2E, s.w * LOG2E);
+      if (t < C) sm.pbeta[t] = R.beta;
+    }
+    __syncthreads();  // (A) the state waves are done with Kr, Qr, V^T, beta, exp(X_b)
+
+    // ---- phase B: gated operand tiles of chunk pc
+    if (act) {
+      float X[5][4];  // X[b] = G (log2) at the last row of block b-1; X[0] = 0; X[4] = G_last
+      float sfirst[4], ssecond[4];  // this block's two 8-row sums
+      {
+        float run[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          X[0][e] = 0.f;
+          sfirst[e] = 0.f;
+          ssecond[e] = 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float4 s = *reinterpret_cast<const float4*>(&sm.seg[r * D + 4 * cg]);
+          const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (r == 2 * blk) sfirst[e] = sv[e];
+            if (r == 2 * blk + 1) ssecond[e] = sv[e];
+            run[e] += sv[e];
+            if (r & 1) X[(r + 1) >> 1][e] = run[e];
+          }
+        }
+      }
+      float a[8][4];  // per-token decay a = exp2(g log2 e)
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        a[r8][0] = ex2(R.g[r8].x * LOG2E);
+        a[r8][1] = ex2(R.g[r8].y * LOG2E);
+        a[r8][2] = ex2(R.g[r8].z * LOG2E);
+        a[r8][3] = ex2(R.g[r8].w * LOG2E);
+      }
+      float F[4], Hv[4], eCX[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float Xb1 = blk == 0 ? X[1][e] : blk == 1 ? X[2][e] : blk == 2 ? X[3][e] : X[4][e];
+        F[e] = second ? ex2(sfirst[e]) : 1.f;    // F of the row before this thread's first
+        Hv[e] = second ? 1.f : ex2(ssecond[e]);  // H of this thread's last row
+        eCX[e] = ex2(X[4][e] - Xb1);
+      }
+      // rows are walked last to first for H (H_r = H_{r+1} a_{r+1}); F is then
+      // rebuilt forwards from F_{r} = F_{r-1} a_r, so both need only a[][]
+      float Hs[8][4];
+#pragma unroll
+      for (int r8 = 7; r8 >= 0; --r8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Hs[r8][e] = Hv[e];
+          Hv[e] *= a[r8][e];
+        }
+      }
+      uint32_t kpw[4][4];  // K' of row pairs, per channel
+      float kp_prev[4];
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) {
+        const int row = rg * 8 + r8;
+        float qf[4], kf[4], kr[4], qr[4], kh[4], kp[4];
+        unpack4(R.q[r8], qf);
+        unpack4(R.k[r8], kf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          F[e] *= a[r8][e];
+          kr[e] = kf[e] * F[e];
+          qr[e] = qf[e] * F[e];
+          kh[e] = kf[e] * Hs[r8][e];
+          kp[e] = kh[e] * eCX[e];
+        }
+        const int o = row * TS + 4 * cg;
+        *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
+        *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
+        *reinterpret_cast<uint2*>(&sm.kh[o]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+        if (r8 & 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp_prev[e], kp[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kp_prev[e] = kp[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
+        kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
+      }
+      // V^T (channel-major) and beta
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) {
+        uint32_t hv[8];
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+          const uint32_t word = R.v[r8][e >> 1];
+          hv[r8] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        }
+        const int o = (VPT * cg + e) * CS + rg * 8;
+        *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+      }
+      if (t < C) sm.beta[t] = R.beta;
+      // per-channel factors: exp(X_b) (rows 0-3), pair factors (rows pr, pr+8)
+      if (rg < 4) {
+        float4 f;
+        float* fp = reinterpret_cast<float*>(&f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          fp[e] = ex2(rg == 0 ? X[0][e] : rg == 1 ? X[1][e] : rg == 2 ? X[2][e] : X[3][e]);
+        *reinterpret_cast<float4*>(&sm.ex[rg * D + 4 * cg]) = f;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int pr = rg + 8 * pp;
+        if (pr < 10) {
+          const int rb = pair_rb(pr), ib = pair_ib(pr);
+          float4 f;
+          float* fp = reinterpret_cast<float*>(&f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xr = rb == 0 ? X[0][e] : rb == 1 ? X[1][e] : rb == 2 ? X[2][e] : X[3][e];
+            const float xi = ib == 0 ? X[1][e] : ib == 1 ? X[2][e] : ib == 2 ? X[3][e] : X[4][e];
+            fp[e] = ex2(xr - xi);
+          }
+          *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
+        }
+      }
+      gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
+      // the raw registers are consumed: fetch the chunk after this one
+      if (pc + 1 < w.nchunks) load_chunk<NV>(R, p, w, pc + 1, t);
+    }
+    __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
+
+    // ---- phase C: state-update operand and A tiles of chunk pc
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int o = (4 * cg + e) * CS + rg * 8;
+        *reinterpret_cast<uint2*>(&sm.kpt[o]) = kpt_hold[e][0];
+        *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
+      }
+      if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
+      // A tiles of pairs pw, pw+4, pw+8
+#pragma unroll 1
+      for (int pr = pw; pr < 10; pr += 4) {
+        const int rb = pair_rb(pr), ib = pair_ib(pr);
+        const f32x4 acc = tile_product(sm, sm.kr, pr, q4, m16);
+        const int r = 16 * rb + m16;
+        const float br = sm.pbeta[r];
+        float v4[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) v4[tt] = (16 * ib + 4 * q4 + tt < r) ? br * acc[tt] : 0.f;
+        if (ib == rb) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) sm.ndt[(rb * 16 + 4 * q4 + tt) * NS + m16] = v4[tt];
+        } else {
+          *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
+              pack4(-v4[0], -v4[1], -v4[2], -v4[3]);
+        }
+      }
+    }
+    __syncthreads();  // (C) chunk pc fully published
+  }
+}
+
+// ============================================================================ state waves
+template <int JT>
+__device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, const Work& w,
+                                           int64_t n) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;  // 0..3
+  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int jw_base = w.j0 + 16 * JT * wave;   // first global value column of this wave
+  const int jl_base = 16 * JT * wave;          // first column within the slice
+  const size_t sbase = ((size_t)n * p.H + w.h) * (size_t)(D * D);
+
+  // Sacc[ct][jt][t] = S[16ct + 4q4 + t][jw_base + 16jt + m16]
+  f32x4 Sacc[8][JT];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) Sacc[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.s0 != nullptr) {
+    if (p.s0_fp32) {
+      const float* s0 = reinterpret_cast<const float*>(p.s0) + sbase;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            Sacc[ct][jt][t] = s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16];
+    } else {
+      const __bf16* s0 = reinterpret_cast<const __bf16*>(p.s0) + sbase;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16]);
+    }
+  }
+
+  const int HD = p.H * D;
+  for (int it = -1; it < w.nchunks; ++it) {
+    const bool act = it >= 0;
+    const int64_t tok0 = w.bos + (int64_t)it * C;
+    const int64_t rest = w.len - (int64_t)it * C;
+    const int valid = rest < C ? (int)rest : C;
+    f32x4 Z[4][JT];   // beta * Y, rows 16b + 4q4 + t, column m16
+    f32x4 O[4][JT];   // O^T: row j = 16jt + 4q4 + t, column r = 16rt + m16
+
+    // ---- phase A: per row block b, the state scaled by exp(X_b) gives
+    //      Y_b = V_b - Kr_b (exp(X_b) S)   and   O_b = Qr_b (exp(X_b) S)
+    if (act) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        bf16x8 Sb[4][JT];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float4 e0 = *reinterpret_cast<const float4*>(&sm.ex[b * D + 32 * ks + 4 * q4]);
+          const float4 e1 = *reinterpret_cast<const float4*>(&sm.ex[b * D + 32 * ks + 16 + 4 * q4]);
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) {
+            const f32x4 s0 = Sacc[2 * ks][jt], s1 = Sacc[2 * ks + 1][jt];
+            Sb[ks][jt] = cat(cvt4(f32x4{s0[0] * e0.x, s0[1] * e0.y, s0[2] * e0.z, s0[3] * e0.w}),
+                             cvt4(f32x4{s1[0] * e1.x, s1[1] * e1.y, s1[2] * e1.z, s1[3] * e1.w}));
+          }
+        }
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          Z[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          O[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const __bf16* kp = &sm.kr[(16 * b + m16) * TS + 32 * ks + 4 * q4];
+          const __bf16* qp = &sm.qr[(16 * b + m16) * TS + 32 * ks + 4 * q4];
+          const bf16x8 ka = ld2x4(kp, kp + 16);
+          const bf16x8 qa = ld2x4(qp, qp + 16);
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) {
+            Z[b][jt] = mfma32(ka, Sb[ks][jt], Z[b][jt]);
+            O[b][jt] = mfma32(Sb[ks][jt], qa, O[b][jt]);
+          }
+        }
+        const float4 bb = *reinterpret_cast<const float4*>(&sm.beta[16 * b + 4 * q4]);
+        const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const int jl = jl_base + 16 * jt + m16;
+          float vv[4];
+          unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + 16 * b + 4 * q4]), vv);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Z[b][jt][t] = bv[t] * (vv[t] - Z[b][jt][t]);
+        }
+      }
+    }
+    __syncthreads();  // (A)
+
+    // ---- phase B: U = L^-1 Z (block forward substitution), output, state update
+    if (act) {
+      bf16x4 U[4][JT];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bf16x4 linv = ld4(&sm.li[(16 * b + m16) * LS + 4 * q4]);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          f32x4 z = Z[b][jt];
+#pragma unroll
+          for (int bp = 0; bp < b; ++bp) {
+            const bf16x4 an = ld4(&sm.an[(16 * b + m16) * QS + 16 * bp + 4 * q4]);
+            z = mfma16(an, U[bp][jt], z);
+          }
+          // z = hi + lo in bf16 (the rounding of z would otherwise reach U in full)
+          const bf16x4 zh = cvt4(z);
+          f32x4 zl;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) zl[t] = z[t] - bf2f(zh[t]);
+          f32x4 u = mfma16(linv, zh, f32x4{0.f, 0.f, 0.f, 0.f});
+          u = mfma16(linv, cvt4(zl), u);
+          U[b][jt] = cvt4(u);
+        }
+      }
+      // O^T += U^T M^T, scale, store (rows past `valid` fall outside the descriptor)
+      const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + m16;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          f32x4 o = O[rt][jt];
+#pragma unroll
+          for (int ks = 0; ks <= (rt >> 1); ++ks) {
+            const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
+            o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
+          }
+          const uint2 ov = pack4(p.scale * o[0], p.scale * o[1], p.scale * o[2], p.scale * o[3]);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
+              r * HD * 2 + (jw_base + 16 * jt + 4 * q4) * 2, 0, 0);
+        }
+      }
+      // S <- Diag(exp(G_last)) S + K'^T U
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const float4 gc = *reinterpret_cast<const float4*>(&sm.gamc[16 * ct + 4 * q4]);
+        const float gv[4] = {gc.x, gc.y, gc.z, gc.w};
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          f32x4 s = Sacc[ct][jt];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s[t] *= gv[t];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const __bf16* rowp = &sm.kpt[(16 * ct + m16) * CS + 32 * ks + 4 * q4];
+            s = mfma32(ld2x4(rowp, rowp + 16), cat(U[2 * ks][jt], U[2 * ks + 1][jt]), s);
+          }
+          Sacc[ct][jt] = s;
+        }
+      }
+    }
+    __syncthreads();  // (B)
+
+    // ---- phase C: M tiles of the next chunk (pairs wave, wave+4, wave+8)
+    if (it + 1 < w.nchunks) {
+#pragma unroll 1
+      for (int pr = wave; pr < 10; pr += 4) {
+        const int rb = pair_rb(pr), ib = pair_ib(pr);
+        const f32x4 acc = tile_product(sm, sm.qr, pr, q4, m16);
+        const int r = 16 * rb + m16;
+        float v4[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) v4[tt] = (16 * ib + 4 * q4 + tt <= r) ? acc[tt] : 0.f;
+        *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(v4[0], v4[1], v4[2], v4[3]);
+      }
+    }
+    __syncthreads();  // (C)
+  }
+
+  if (p.s1 != nullptr) {
+    if (p.s1_fp32) {
+      float* s1 = reinterpret_cast<float*>(p.s1) + sbase;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = Sacc[ct][jt][t];
+    } else {
+      __bf16* s1 = reinterpret_cast<__bf16*>(p.s1) + sbase;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = (__bf16)Sacc[ct][jt][t];
+    }
+  }
 }
 
 template <int JT>
 __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   constexpr int NV = 64 * JT;  // value columns per workgroup
   __shared__ Smem<NV> sm;
-
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int q4 = lane >> 4, m16 = lane & 15;
 
   // ---- workgroup -> (sequence rank, head, value slice); slices of one head share an XCD
   const int nsplit = 128 / NV;
@@ -203,13 +679,14 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   const int pidx = grp * 8 + (rem % 8);
   if (pidx >= pairs) return;
   const int rank = pidx / p.H;
-  const int h = pidx % p.H;
-  const int j0 = split * NV;
+  Work w;
+  w.h = pidx % p.H;
+  w.j0 = split * NV;
 
   // ---- longest sequence first: rank -> sequence index (ties by index)
   int n = rank;
   if (p.cu != nullptr && p.nseq > 1 && p.nseq <= kSortLimit) {
-    int* lens = reinterpret_cast<int*>(sm.kr);  // scratch before the first chunk
+    int* lens = reinterpret_cast<int*>(sm.kh);  // scratch before the first chunk
     for (int i = tid; i < p.nseq; i += NT) lens[i] = p.cu[i + 1] - p.cu[i];
     __syncthreads();
     for (int i = tid; i < p.nseq; i += NT) {
@@ -223,356 +700,22 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     }
     __syncthreads();
     n = sm.order;
+    __syncthreads();  // the scratch is reused by the prep waves
   }
-  const int64_t bos = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
-  const int64_t len = p.cu ? (int64_t)p.cu[n + 1] - bos : p.T;
+  w.bos = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
+  w.len = p.cu ? (int64_t)p.cu[n + 1] - w.bos : p.T;
+  w.nchunks = (int)((w.len + C - 1) / C);
 
-  // ---- constant LDS: M tiles above the block diagonal that the 32-wide k-steps touch
+  // constant zeros: M blocks above the diagonal that the 32-wide k-steps touch
   for (int x = tid; x < 16 * 16; x += NT) {
     const int r = x >> 4, i = x & 15;
-    sm.mm[r * QS + 16 + i] = (__bf16)0.f;          // block (0, 1)
-    sm.mm[(32 + r) * QS + 48 + i] = (__bf16)0.f;   // block (2, 3)
+    sm.mm[r * QS + 16 + i] = (__bf16)0.f;         // block (0, 1)
+    sm.mm[(32 + r) * QS + 48 + i] = (__bf16)0.f;  // block (2, 3)
   }
 
-  // ---- state slice: wave owns value columns jw = j0 + 16*JT*wave + 16*jt + m16;
-  // Sacc[ct][jt][t] = S[16ct + 4q4 + t][jw]
-  f32x4 Sacc[8][JT];
-  const int jw_base = j0 + 16 * JT * wave;
-  const size_t sbase = ((size_t)n * p.H + h) * (size_t)(D * D);
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const size_t off = sbase + (size_t)(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16;
-        float s = 0.f;
-        if (p.s0 != nullptr)
-          s = p.s0_fp32 ? reinterpret_cast<const float*>(p.s0)[off]
-                        : bf2f(reinterpret_cast<const __bf16*>(p.s0)[off]);
-        Sacc[ct][jt][t] = s;
-      }
-  bf16x8 Sfrag[4][JT];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
-
-  const int nchunks = (int)((len + C - 1) / C);
-  const int rg = tid >> 5, cg = tid & 31;
-  const int blk = rg >> 1;  // 16-row block of this thread's rows
-
-  ChunkRegs<NV> R;
-  if (nchunks > 0) load_chunk<NV>(R, p, bos, (int)(len < C ? len : C), h, j0, tid);
-
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int64_t tok0 = bos + (int64_t)ch * C;
-    const int valid = (int)((len - (int64_t)ch * C) < C ? (len - (int64_t)ch * C) : C);
-
-    // ================= gating, part 1: chunk-local cumulative log2-decay
-    float lg[8][4];
-#pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      lg[r8][0] = R.g[r8].x * LOG2E;
-      lg[r8][1] = R.g[r8].y * LOG2E;
-      lg[r8][2] = R.g[r8].z * LOG2E;
-      lg[r8][3] = R.g[r8].w * LOG2E;
-      if (r8 > 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lg[r8][e] += lg[r8 - 1][e];
-    }
-    *reinterpret_cast<float4*>(&sm.seg[rg * D + 4 * cg]) =
-        make_float4(lg[7][0], lg[7][1], lg[7][2], lg[7][3]);
-    __syncthreads();  // (1) also: every wave has finished the previous chunk's state pass
-
-    // ================= gating, part 2: reference points and operand tiles
-    float X[5][4];   // X[b] = G (log2) at the last row of block b-1; X[0] = 0; X[4] = G_last
-    float off[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) X[0][e] = 0.f;
-    {
-      float run[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float4 s = *reinterpret_cast<const float4*>(&sm.seg[r * D + 4 * cg]);
-        if (r == rg) {
-          off[0] = run[0]; off[1] = run[1]; off[2] = run[2]; off[3] = run[3];
-        }
-        run[0] += s.x; run[1] += s.y; run[2] += s.z; run[3] += s.w;
-        if (r & 1)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) X[(r + 1) >> 1][e] = run[e];
-      }
-    }
-    float Xb[4], Xb1[4], eXb[4], eCX[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // runtime block index -> select (keeps X in registers)
-      Xb[e] = blk == 0 ? X[0][e] : blk == 1 ? X[1][e] : blk == 2 ? X[2][e] : X[3][e];
-      Xb1[e] = blk == 0 ? X[1][e] : blk == 1 ? X[2][e] : blk == 2 ? X[3][e] : X[4][e];
-      eXb[e] = exp2f(Xb[e]);
-      eCX[e] = exp2f(X[4][e] - Xb1[e]);
-    }
-    float kpv[8][4];  // K * exp(G_last - G), kept for the channel-major writes
-#pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      const int row = rg * 8 + r8;
-      float qf[4], kf[4];
-      unpack4(R.q[r8], qf);
-      unpack4(R.k[r8], kf);
-      float kr[4], qr[4], kh[4], kg[4], qg[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float G = off[e] + lg[r8][e];
-        const float F = exp2f(G - Xb[e]);   // <= 1
-        const float Hh = exp2f(Xb1[e] - G); // <= 1
-        kr[e] = kf[e] * F;
-        qr[e] = qf[e] * F;
-        kh[e] = kf[e] * Hh;
-        kg[e] = kr[e] * eXb[e];
-        qg[e] = qr[e] * eXb[e];
-        kpv[r8][e] = kh[e] * eCX[e];
-      }
-      const int o = row * TS + 4 * cg;
-      *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
-      *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
-      *reinterpret_cast<uint2*>(&sm.kh[o]) = pack4(kh[0], kh[1], kh[2], kh[3]);
-      *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
-      *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
-    }
-    // channel-major K' and V^T: per channel, 8 consecutive rows as two 4-row runs
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int o = (4 * cg + e) * CS + rg * 8;
-      *reinterpret_cast<uint2*>(&sm.kpt[o]) = pack4(kpv[0][e], kpv[1][e], kpv[2][e], kpv[3][e]);
-      *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = pack4(kpv[4][e], kpv[5][e], kpv[6][e], kpv[7][e]);
-    }
-    {
-      constexpr int VPT = NV / 32;  // value columns per thread
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) {
-        float vv[8];
-#pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) {
-          const bf16x2 two = __builtin_bit_cast(bf16x2, R.v[r8][e >> 1]);
-          vv[r8] = bf2f(two[e & 1]);
-        }
-        const int o = (VPT * cg + e) * CS + rg * 8;
-        *reinterpret_cast<uint2*>(&sm.vt[o]) = pack4(vv[0], vv[1], vv[2], vv[3]);
-        *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = pack4(vv[4], vv[5], vv[6], vv[7]);
-      }
-    }
-    // pair factors exp(X_rb - X_{ib+1}); this thread's row group covers pairs rg, rg+8
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int pr = rg + 8 * pp;
-      if (pr < 10) {
-        const int rb = pair_rb(pr), ib = pair_ib(pr);
-        float4 f;
-        float* fp = reinterpret_cast<float*>(&f);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xr = rb == 0 ? X[0][e] : rb == 1 ? X[1][e] : rb == 2 ? X[2][e] : X[3][e];
-          const float xi = ib == 0 ? X[1][e] : ib == 1 ? X[2][e] : ib == 2 ? X[3][e] : X[4][e];
-          fp[e] = exp2f(xr - xi);
-        }
-        *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
-      }
-    }
-    if (rg == 0)
-      *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) =
-          make_float4(exp2f(X[4][0]), exp2f(X[4][1]), exp2f(X[4][2]), exp2f(X[4][3]));
-    if (tid < C) sm.beta[tid] = R.beta;
-
-    // prefetch the next chunk's raw inputs (in flight during the MFMA work below)
-    if (ch + 1 < nchunks) {
-      const int64_t rest = len - (int64_t)(ch + 1) * C;
-      load_chunk<NV>(R, p, tok0 + C, (int)(rest < C ? rest : C), h, j0, tid);
-    }
-    __syncthreads();  // (2) operand tiles ready
-
-    // ================= A (waves 0,1) and M (waves 2,3) 16x16 tiles
-    {
-      const bool isM = wave >= 2;
-      const __bf16* rowsrc = isM ? sm.qr : sm.kr;
-      const int p0 = (wave & 1) ? 5 : 0;
-      for (int pr = p0; pr < p0 + 5; ++pr) {
-        const int rb = pair_rb(pr), ib = pair_ib(pr);
-        const bool scaled = ib != rb - 1;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int c0 = 32 * ks + 8 * q4;
-          bf16x8 rf = ld8(&rowsrc[(16 * rb + m16) * TS + c0]);
-          if (scaled) {
-            const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0]);
-            const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0 + 4]);
-            const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) rf[e] = (__bf16)(bf2f(rf[e]) * fs[e]);
-          }
-          const bf16x8 cf = ld8(&sm.kh[(16 * ib + m16) * TS + c0]);
-          acc = mfma32(cf, rf, acc);  // D[i][r]: lane holds (r = m16, i = 4q4 + t)
-        }
-        const int r = 16 * rb + m16;
-        float v4[4];
-        if (!isM) {
-          const float br = sm.beta[r];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v4[t] = (16 * ib + 4 * q4 + t < r) ? br * acc[t] : 0.f;
-          if (ib == rb) {
-            *reinterpret_cast<float4*>(&sm.nd[(rb * 16 + m16) * NS + 4 * q4]) =
-                make_float4(v4[0], v4[1], v4[2], v4[3]);
-          } else {
-            *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
-                pack4(-v4[0], -v4[1], -v4[2], -v4[3]);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v4[t] = (16 * ib + 4 * q4 + t <= r) ? acc[t] : 0.f;
-          *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(v4[0], v4[1], v4[2], v4[3]);
-        }
-      }
-      if (!isM) {
-        // inverse of the unit lower-triangular diagonal blocks this wave just wrote:
-        // lanes 0-15 -> block 2*wave, lanes 16-31 -> block 2*wave+1 (lanes 32-63 mirror)
-        lds_fence();
-        const int b = 2 * wave + ((lane >> 4) & 1);
-        const int j = m16;
-        const float* N = &sm.nd[b * 16 * NS];
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-          for (int kk = 0; kk < r; ++kk) s -= N[r * NS + kk] * x[kk];
-          x[r] = s;
-        }
-        if (lane < 32) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sm.li[(16 * b + r) * LS + j] = (__bf16)x[r];
-        }
-      }
-    }
-    __syncthreads();  // (3) M, -A, L_bb^-1 ready
-
-    // ================= state pass for this wave's value columns
-    // Y = V - (K*Gamma) S  ->  Z = beta * Y   (D-layout: rows 16it + 4q4 + t, column m16)
-    f32x4 Z[4][JT];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) Z[it][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const __bf16* rowp = &sm.kg[(16 * it + m16) * TS + 32 * ks + 4 * q4];
-        const bf16x8 a = ld2x4(rowp, rowp + 16);
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) Z[it][jt] = mfma32(a, Sfrag[ks][jt], Z[it][jt]);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const float4 bb = *reinterpret_cast<const float4*>(&sm.beta[16 * it + 4 * q4]);
-      const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        const int jl = 16 * JT * wave + 16 * jt + m16;  // column within this slice
-        float vv[4];
-        unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + 16 * it + 4 * q4]), vv);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) Z[it][jt][t] = bv[t] * (vv[t] - Z[it][jt][t]);
-      }
-    }
-    // U = L^-1 Z by block forward substitution: U_b = Linv_b (Z_b - sum_{b'<b} A_bb' U_b')
-    bf16x4 U[4][JT];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bf16x4 linv = ld4(&sm.li[(16 * b + m16) * LS + 4 * q4]);
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        f32x4 z = Z[b][jt];
-#pragma unroll
-        for (int bp = 0; bp < b; ++bp) {
-          const bf16x4 an = ld4(&sm.an[(16 * b + m16) * QS + 16 * bp + 4 * q4]);
-          z = mfma16(an, U[bp][jt], z);
-        }
-        // z = hi + lo in bf16 (the rounding of z would otherwise reach U in full)
-        const bf16x4 zh = cvt4(z);
-        f32x4 zl;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) zl[t] = z[t] - bf2f(zh[t]);
-        f32x4 u = mfma16(linv, zh, f32x4{0.f, 0.f, 0.f, 0.f});
-        u = mfma16(linv, cvt4(zl), u);
-        U[b][jt] = cvt4(u);
-      }
-    }
-    // O^T = S^T (Q*Gamma)^T + U^T M^T  ->  lane holds O[r = 16rt + m16][j = 16jt + 4q4 + t]
-    {
-      const int64_t HD = (int64_t)p.H * D;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int r = 16 * rt + m16;
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const __bf16* rowp = &sm.qg[r * TS + 32 * ks + 4 * q4];
-            o = mfma32(Sfrag[ks][jt], ld2x4(rowp, rowp + 16), o);
-          }
-#pragma unroll
-          for (int ks = 0; ks <= (rt >> 1); ++ks) {
-            const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
-            o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
-          }
-          if (r < valid) {
-            const int64_t addr = (tok0 + r) * HD + (int64_t)h * D + jw_base + 16 * jt + 4 * q4;
-            *reinterpret_cast<uint2*>(p.out + addr) =
-                pack4(p.scale * o[0], p.scale * o[1], p.scale * o[2], p.scale * o[3]);
-          }
-        }
-      }
-    }
-    // S <- Diag(Gamma_last) S + K'^T U
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const float4 gc = *reinterpret_cast<const float4*>(&sm.gamc[16 * ct + 4 * q4]);
-      const float gv[4] = {gc.x, gc.y, gc.z, gc.w};
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        f32x4 s = Sacc[ct][jt];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] *= gv[t];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const __bf16* rowp = &sm.kpt[(16 * ct + m16) * CS + 32 * ks + 4 * q4];
-          s = mfma32(ld2x4(rowp, rowp + 16), cat(U[2 * ks][jt], U[2 * ks + 1][jt]), s);
-        }
-        Sacc[ct][jt] = s;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
-  }
-
-  // ---- final state
-  if (p.s1 != nullptr) {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const size_t off = sbase + (size_t)(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16;
-          if (p.s1_fp32) reinterpret_cast<float*>(p.s1)[off] = Sacc[ct][jt][t];
-          else reinterpret_cast<__bf16*>(p.s1)[off] = (__bf16)Sacc[ct][jt][t];
-        }
-  }
+  // Both roles execute the same barrier sequence; the branch is uniform per wave.
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w, n);
+  else prep_loop<NV>(sm, p, w);
 }
 
 }  // namespace
