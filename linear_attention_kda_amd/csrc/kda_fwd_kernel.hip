@@ -20,11 +20,11 @@
 // and H_r = exp(X_{b+1} - G_r) for r in block b (both <= 1):
 //  * Kr = K*F and Qr = Q*F are the row operands of A and M, Kh = K*H the column
 //    operand; tile (rb, ib) takes the per-channel factor exp(X_rb - X_{ib+1}) on
-//    the row operand (<= 1 off the diagonal, 1 for ib = rb-1, and bounded by one
-//    block's decay on the diagonal: the per-channel sum of -g over a 16-token block
-//    must stay below ~88 in natural log);
-//  * K*exp(G) = Kr * exp(X_b): the state pass multiplies the rows of its bf16 state
-//    copy by exp(X_b) per row block instead of reading separate K*exp(G), Q*exp(G);
+//    the column operand, shared by the A and M tiles of the pair (<= 1 off the
+//    diagonal, 1 for ib = rb-1, and bounded by one block's decay on the diagonal:
+//    the per-channel sum of -g over a 16-token block must stay below ~88 in
+//    natural log);
+//  * K*exp(G) = Kr * exp(X_b), Q*exp(G) = Qr * exp(X_b) (both <= 1);
 //  * K*exp(G_last - G) = Kh * exp(G_last - X_{b+1}).
 // F and H are running products of a = exp(g) along the rows.
 //
@@ -32,13 +32,15 @@
 // and walks its chunks in order as a two-stage pipeline with three barriers per
 // chunk (phases A, B, C):
 //  * waves 0-3 ("state waves") run chunk c: phase A  Y and (Q exp(G)) S;
-//    phase B  U by block forward substitution, the output, the state update;
-//    phase C  the M tiles of chunk c+1.  The fp32 state slice (16*JT value
-//    columns per wave) lives in MFMA accumulator registers for the whole sequence.
+//    phase B  U by block forward substitution, the output, the state update.
+//    The fp32 state slice (16*JT value columns per wave) lives in MFMA
+//    accumulator registers for the whole sequence.
 //  * waves 4-7 ("prep waves") prepare chunk c+1: phase A  the inverses of the
 //    diagonal blocks of L for chunk c and the row sums of g for chunk c+1;
 //    phase B  gating (VALU, exp2) into the operand tiles, and the loads of chunk
-//    c+2; phase C  the A tiles and the state-update operand of chunk c+1.
+//    c+2; phase C  the state-update operand of chunk c+1.
+//  * in phase C all eight waves build the A and M tiles of chunk c+1, one pair of
+//    16-row blocks (both tiles) per wave, the three unscaled pairs on one wave.
 // Each tile is rewritten only after the phase in which the state waves last read
 // it.  The value-independent per-chunk work is recomputed by every value slice.
 //
@@ -66,7 +68,7 @@ constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // head dimension
 constexpr int NT = 512;      // threads per workgroup: 4 state waves + 4 prep waves
 constexpr int NP = 256;      // prep threads
-constexpr int TS = D + 8;    // row stride (bf16) of token-major [64][128] tiles: 272 B
+constexpr int TS = D + 4;    // row stride (bf16) of token-major [64][128] tiles: 264 B
 constexpr int CS = C + 4;    // row stride (bf16) of channel-major [.][64] tiles: 136 B
 constexpr int QS = C + 4;    // row stride (bf16) of [64][64] tiles: 136 B
 constexpr int LS = 16 + 4;   // row stride (bf16) of the diagonal-block inverses
@@ -76,8 +78,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // Shared-memory plan; one workgroup per CU.
 template <int NV>
 struct alignas(16) Smem {
-  __bf16 kr[C * TS];    // K * F                       A row operand; state pass
-  __bf16 qr[C * TS];    // Q * F                       M row operand; state pass
+  __bf16 kg[C * TS];    // K * exp(G)                  for Y = V - (K exp(G)) S
+  __bf16 qg[C * TS];    // Q * exp(G)                  for O = (Q exp(G)) S + ...
+  __bf16 kr[C * TS];    // K * F                       A row operand
+  __bf16 qr[C * TS];    // Q * F                       M row operand
   __bf16 kh[C * TS];    // K * H                       A and M column operand
   __bf16 kpt[D * CS];   // (K * exp(G_last - G))^T     channel-major, state update
   __bf16 vt[NV * CS];   // V^T (this slice's columns)  channel-major
@@ -85,7 +89,6 @@ struct alignas(16) Smem {
   __bf16 an[C * QS];    // -A on the off-diagonal 16x16 blocks
   __bf16 li[C * LS];    // inverses of the 4 diagonal blocks of L = I + A
   float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A, transposed: [b][i][r]
-  float ex[4 * D];      // exp(X_b) per block and channel
   float gamc[D];        // exp(G_last) per channel
   float beta[C];        // beta of the chunk in the state pass
   float pbeta[C];       // beta of the chunk being prepared
@@ -151,20 +154,25 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ int pair_rb(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
 __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_rb(p) + 1)) / 2; }
 
-// One 16x16 tile of A (rowsrc = Kr) or M (rowsrc = Qr): lane (q4, m16) gets
-// tile[r = 16rb + m16][i = 16ib + 4q4 + t].  The row operand is scaled per
-// channel by exp(X_rb - X_{ib+1}) unless ib == rb - 1, where that factor is 1.
+// The A and M tiles of block pair pr = (rb, ib): lane (q4, m16) gets
+// tile[r = 16rb + m16][i = 16ib + 4q4 + t] of sum_c row[r][c] col[i][c] with rows
+// Kr (A) and Qr (M) and the column operand Kh scaled per channel by
+// exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1, where the factor is 1).
 template <int NV>
-__device__ __forceinline__ f32x4 tile_product(const Smem<NV>& sm, const __bf16* rowsrc, int pr,
-                                              int q4, int m16) {
+__device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, int m16,
+                                          f32x4& ta, f32x4& tm) {
   const int rb = pair_rb(pr), ib = pair_ib(pr);
   const bool scaled = ib != rb - 1;
-  bf16x8 rf[4], cf[4];
+  bf16x8 cf[4], kf[4], qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int c0 = 32 * ks + 8 * q4;
-    rf[ks] = ld8(&rowsrc[(16 * rb + m16) * TS + c0]);
-    cf[ks] = ld8(&sm.kh[(16 * ib + m16) * TS + c0]);
+    const __bf16* cp = &sm.kh[(16 * ib + m16) * TS + c0];
+    const __bf16* kp = &sm.kr[(16 * rb + m16) * TS + c0];
+    const __bf16* qp = &sm.qr[(16 * rb + m16) * TS + c0];
+    cf[ks] = ld2x4(cp, cp + 4);
+    kf[ks] = ld2x4(kp, kp + 4);
+    qf[ks] = ld2x4(qp, qp + 4);
   }
   if (scaled) {
 #pragma unroll
@@ -174,13 +182,49 @@ __device__ __forceinline__ f32x4 tile_product(const Smem<NV>& sm, const __bf16* 
       const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0 + 4]);
       const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rf[ks][e] = (__bf16)(bf2f(rf[ks][e]) * fs[e]);
+      for (int e = 0; e < 8; ++e) cf[ks][e] = (__bf16)(bf2f(cf[ks][e]) * fs[e]);
     }
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  ta = f32x4{0.f, 0.f, 0.f, 0.f};
+  tm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) acc = mfma32(cf[ks], rf[ks], acc);  // D[i][r]
-  return acc;
+  for (int ks = 0; ks < 4; ++ks) {
+    ta = mfma32(cf[ks], kf[ks], ta);  // D[i][r]
+    tm = mfma32(cf[ks], qf[ks], tm);
+  }
+}
+
+// Phase C tile work of wave `wave` (0..7): the seven scaled pairs one per wave,
+// the three unscaled pairs (1,0), (2,1), (3,2) together on wave 7.  Writes -A off
+// the diagonal, A's diagonal blocks transposed (fp32, for the inverse), and M.
+template <int NV>
+__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16) {
+  const int npairs = wave < 7 ? 1 : 3;
+#pragma unroll 1
+  for (int x = 0; x < npairs; ++x) {
+    const int pr = wave < 7 ? (wave < 2 ? 2 * wave : wave == 2 ? 3 : wave == 6 ? 9 : wave + 2)
+                            : 1 + 3 * x + (x == 2 ? 1 : 0);
+    const int rb = pair_rb(pr), ib = pair_ib(pr);
+    f32x4 ta, tm;
+    tile_pair(sm, pr, q4, m16, ta, tm);
+    const int r = 16 * rb + m16;
+    const float br = sm.pbeta[r];
+    float va[4], vm[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int i = 16 * ib + 4 * q4 + tt;
+      va[tt] = (i < r) ? br * ta[tt] : 0.f;
+      vm[tt] = (i <= r) ? tm[tt] : 0.f;
+    }
+    if (ib == rb) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) sm.ndt[(rb * 16 + 4 * q4 + tt) * NS + m16] = va[tt];
+    } else {
+      *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
+          pack4(-va[0], -va[1], -va[2], -va[3]);
+    }
+    *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(vm[0], vm[1], vm[2], vm[3]);
+  }
 }
 
 struct Work {
@@ -249,10 +293,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, co
 template <int NV>
 __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const Work& w) {
   const int t = threadIdx.x - (NT - NP);   // 0..255
-  const int pw = t >> 6;                   // prep wave 0..3
+  const int pw = __builtin_amdgcn_readfirstlane(t >> 6);  // prep wave 0..3 (wave-uniform)
   const int lane = t & 63, q4 = lane >> 4, m16 = lane & 15;
   const int rg = t >> 5, cg = t & 31;
-  const int blk = rg >> 1;                 // 16-row block of this thread's rows
+  const int blk = pw;                      // 16-row block of this thread's rows
   const bool second = (rg & 1) != 0;       // rows 8..15 of the block
   constexpr int VPT = NV / 32;             // value columns per thread
 
@@ -301,30 +345,37 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           make_float4(s.x * LOG2E, s.y * LOG2E, s.z * LOG2E, s.w * LOG2E);
       if (t < C) sm.pbeta[t] = R.beta;
     }
-    __syncthreads();  // (A) the state waves are done with Kr, Qr, V^T, beta, exp(X_b)
+    __syncthreads();  // (A) the state waves are done with K exp(G), Q exp(G), V^T, beta
 
     // ---- phase B: gated operand tiles of chunk pc
     if (act) {
-      float X[5][4];  // X[b] = G (log2) at the last row of block b-1; X[0] = 0; X[4] = G_last
-      float sfirst[4], ssecond[4];  // this block's two 8-row sums
+      // X[b] = G (log2) at the last row of block b-1 (X[0] = 0, X[4] = G_last);
+      // Xb, Xb1 = X of this thread's block and the next; sfirst, ssecond = the two
+      // 8-row sums of this block.  Masks are wave-uniform scalars, so no branches.
+      float X[5][4], Xb[4], Xb1[4], sfirst[4], ssecond[4];
       {
         float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           X[0][e] = 0.f;
-          sfirst[e] = 0.f;
-          ssecond[e] = 0.f;
+          Xb[e] = Xb1[e] = sfirst[e] = ssecond[e] = 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const float4 s = *reinterpret_cast<const float4*>(&sm.seg[r * D + 4 * cg]);
-          const float sv[4] = {s.x, s.y, s.z, s.w};
+          const float4 sg = *reinterpret_cast<const float4*>(&sm.seg[r * D + 4 * cg]);
+          const float sv[4] = {sg.x, sg.y, sg.z, sg.w};
+          const float m_b = r < 2 * blk ? 1.f : 0.f;
+          const float m_b1 = r < 2 * blk + 2 ? 1.f : 0.f;
+          const float m_f = r == 2 * blk ? 1.f : 0.f;
+          const float m_s = r == 2 * blk + 1 ? 1.f : 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (r == 2 * blk) sfirst[e] = sv[e];
-            if (r == 2 * blk + 1) ssecond[e] = sv[e];
             run[e] += sv[e];
             if (r & 1) X[(r + 1) >> 1][e] = run[e];
+            Xb[e] = fmaf(m_b, sv[e], Xb[e]);
+            Xb1[e] = fmaf(m_b1, sv[e], Xb1[e]);
+            sfirst[e] = fmaf(m_f, sv[e], sfirst[e]);
+            ssecond[e] = fmaf(m_s, sv[e], ssecond[e]);
           }
         }
       }
@@ -336,13 +387,14 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         a[r8][2] = ex2(R.g[r8].z * LOG2E);
         a[r8][3] = ex2(R.g[r8].w * LOG2E);
       }
-      float F[4], Hv[4], eCX[4];
+      float F[4], Hv[4], eCX[4], eXb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float Xb1 = blk == 0 ? X[1][e] : blk == 1 ? X[2][e] : blk == 2 ? X[3][e] : X[4][e];
-        F[e] = second ? ex2(sfirst[e]) : 1.f;    // F of the row before this thread's first
-        Hv[e] = second ? 1.f : ex2(ssecond[e]);  // H of this thread's last row
-        eCX[e] = ex2(X[4][e] - Xb1);
+        const float pfirst = ex2(sfirst[e]), psecond = ex2(ssecond[e]);
+        F[e] = second ? pfirst : 1.f;    // F of the row before this thread's first
+        Hv[e] = second ? 1.f : psecond;  // H of this thread's last row
+        eCX[e] = ex2(X[4][e] - Xb1[e]);
+        eXb[e] = ex2(Xb[e]);
       }
       // rows are walked last to first for H (H_r = H_{r+1} a_{r+1}); F is then
       // rebuilt forwards from F_{r} = F_{r-1} a_r, so both need only a[][]
@@ -360,7 +412,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 #pragma unroll
       for (int r8 = 0; r8 < 8; ++r8) {
         const int row = rg * 8 + r8;
-        float qf[4], kf[4], kr[4], qr[4], kh[4], kp[4];
+        float qf[4], kf[4], kr[4], qr[4], kh[4], kp[4], kg[4], qg[4];
         unpack4(R.q[r8], qf);
         unpack4(R.k[r8], kf);
 #pragma unroll
@@ -370,11 +422,15 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           qr[e] = qf[e] * F[e];
           kh[e] = kf[e] * Hs[r8][e];
           kp[e] = kh[e] * eCX[e];
+          kg[e] = kr[e] * eXb[e];
+          qg[e] = qr[e] * eXb[e];
         }
         const int o = row * TS + 4 * cg;
         *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
         *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
         *reinterpret_cast<uint2*>(&sm.kh[o]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+        *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
+        *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
         if (r8 & 1) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp_prev[e], kp[e]);
@@ -402,19 +458,11 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
       }
       if (t < C) sm.beta[t] = R.beta;
-      // per-channel factors: exp(X_b) (rows 0-3), pair factors (rows pr, pr+8)
-      if (rg < 4) {
-        float4 f;
-        float* fp = reinterpret_cast<float*>(&f);
+      // pair factors exp(X_rb - X_{ib+1}): prep wave pw covers pairs pw, pw+4, pw+8
+      // (lanes 32-63 hold the same channels as lanes 0-31 and skip the store)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          fp[e] = ex2(rg == 0 ? X[0][e] : rg == 1 ? X[1][e] : rg == 2 ? X[2][e] : X[3][e]);
-        *reinterpret_cast<float4*>(&sm.ex[rg * D + 4 * cg]) = f;
-      }
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int pr = rg + 8 * pp;
-        if (pr < 10) {
+      for (int pr = 0; pr < 10; ++pr) {
+        if ((pr & 3) == pw) {
           const int rb = pair_rb(pr), ib = pair_ib(pr);
           float4 f;
           float* fp = reinterpret_cast<float*>(&f);
@@ -424,7 +472,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
             const float xi = ib == 0 ? X[1][e] : ib == 1 ? X[2][e] : ib == 2 ? X[3][e] : X[4][e];
             fp[e] = ex2(xr - xi);
           }
-          *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
+          if (!second) *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
         }
       }
       gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
@@ -442,24 +490,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
       if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
-      // A tiles of pairs pw, pw+4, pw+8
-#pragma unroll 1
-      for (int pr = pw; pr < 10; pr += 4) {
-        const int rb = pair_rb(pr), ib = pair_ib(pr);
-        const f32x4 acc = tile_product(sm, sm.kr, pr, q4, m16);
-        const int r = 16 * rb + m16;
-        const float br = sm.pbeta[r];
-        float v4[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) v4[tt] = (16 * ib + 4 * q4 + tt < r) ? br * acc[tt] : 0.f;
-        if (ib == rb) {
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) sm.ndt[(rb * 16 + 4 * q4 + tt) * NS + m16] = v4[tt];
-        } else {
-          *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
-              pack4(-v4[0], -v4[1], -v4[2], -v4[3]);
-        }
-      }
+      build_tiles(sm, 4 + pw, q4, m16);
     }
     __syncthreads();  // (C) chunk pc fully published
   }
@@ -504,6 +535,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     }
   }
 
+  bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
+
   const int HD = p.H * D;
   for (int it = -1; it < w.nchunks; ++it) {
     const bool act = it >= 0;
@@ -513,40 +550,32 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     f32x4 Z[4][JT];   // beta * Y, rows 16b + 4q4 + t, column m16
     f32x4 O[4][JT];   // O^T: row j = 16jt + 4q4 + t, column r = 16rt + m16
 
-    // ---- phase A: per row block b, the state scaled by exp(X_b) gives
-    //      Y_b = V_b - Kr_b (exp(X_b) S)   and   O_b = Qr_b (exp(X_b) S)
+    // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
     if (act) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        bf16x8 Sb[4][JT];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float4 e0 = *reinterpret_cast<const float4*>(&sm.ex[b * D + 32 * ks + 4 * q4]);
-          const float4 e1 = *reinterpret_cast<const float4*>(&sm.ex[b * D + 32 * ks + 16 + 4 * q4]);
-#pragma unroll
-          for (int jt = 0; jt < JT; ++jt) {
-            const f32x4 s0 = Sacc[2 * ks][jt], s1 = Sacc[2 * ks + 1][jt];
-            Sb[ks][jt] = cat(cvt4(f32x4{s0[0] * e0.x, s0[1] * e0.y, s0[2] * e0.z, s0[3] * e0.w}),
-                             cvt4(f32x4{s1[0] * e1.x, s1[1] * e1.y, s1[2] * e1.z, s1[3] * e1.w}));
-          }
-        }
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           Z[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
           O[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const __bf16* kp = &sm.kr[(16 * b + m16) * TS + 32 * ks + 4 * q4];
-          const __bf16* qp = &sm.qr[(16 * b + m16) * TS + 32 * ks + 4 * q4];
+          const __bf16* kp = &sm.kg[(16 * b + m16) * TS + 32 * ks + 4 * q4];
+          const __bf16* qp = &sm.qg[(16 * b + m16) * TS + 32 * ks + 4 * q4];
           const bf16x8 ka = ld2x4(kp, kp + 16);
           const bf16x8 qa = ld2x4(qp, qp + 16);
 #pragma unroll
           for (int jt = 0; jt < JT; ++jt) {
-            Z[b][jt] = mfma32(ka, Sb[ks][jt], Z[b][jt]);
-            O[b][jt] = mfma32(Sb[ks][jt], qa, O[b][jt]);
+            Z[b][jt] = mfma32(ka, Sfrag[ks][jt], Z[b][jt]);
+            O[b][jt] = mfma32(Sfrag[ks][jt], qa, O[b][jt]);
           }
         }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
         const float4 bb = *reinterpret_cast<const float4*>(&sm.beta[16 * b + 4 * q4]);
         const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
@@ -622,22 +651,16 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           Sacc[ct][jt] = s;
         }
       }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
     }
     __syncthreads();  // (B)
 
-    // ---- phase C: M tiles of the next chunk (pairs wave, wave+4, wave+8)
-    if (it + 1 < w.nchunks) {
-#pragma unroll 1
-      for (int pr = wave; pr < 10; pr += 4) {
-        const int rb = pair_rb(pr), ib = pair_ib(pr);
-        const f32x4 acc = tile_product(sm, sm.qr, pr, q4, m16);
-        const int r = 16 * rb + m16;
-        float v4[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) v4[tt] = (16 * ib + 4 * q4 + tt <= r) ? acc[tt] : 0.f;
-        *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(v4[0], v4[1], v4[2], v4[3]);
-      }
-    }
+    // ---- phase C: A and M tiles of the next chunk (shared with the prep waves)
+    if (it + 1 < w.nchunks) build_tiles(sm, wave, q4, m16);
     __syncthreads();  // (C)
   }
 
