@@ -114,7 +114,7 @@ def measured_traffic(wid: int):
     return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
 
 
-def cpu_baseline(x, heads: int):
+def cpu_baseline(x, heads: int, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on `heads` heads of the same workload."""
     import numpy as np  # noqa: F401
 
@@ -129,14 +129,48 @@ def cpu_baseline(x, heads: int):
     threads = oracle.max_threads()
     col_block = 16
     tasks = w.num_states * len(hs) * (128 // col_block)
-    t0 = time.perf_counter()
-    oracle.fwd(*args, x["scale"], s0, cu_seqlens=cu, col_block=col_block)
-    dt = time.perf_counter() - t0
-    tokens_equiv = w.tokens * len(hs) / w.H  # all-head-equivalent tokens
+    # Whole passes over the sample until at least min_seconds of CPU work.
+    passes, dt = 0, 0.0
+    while passes == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        oracle.fwd(*args, x["scale"], s0, cu_seqlens=cu, col_block=col_block)
+        dt += time.perf_counter() - t0
+        passes += 1
+    tokens_equiv = passes * w.tokens * len(hs) / w.H  # all-head-equivalent tokens
     return dict(value=tokens_equiv / dt, unit="tokens/s", cores=min(threads, tasks),
                 kind="oracle",
-                sample=(f"{w.name}: all {w.tokens} tokens of {len(hs)} of {w.H} heads "
-                        f"({dt:.1f} s); value scaled to all heads"))
+                sample=(f"{w.name}: {passes} pass(es) over all {w.tokens} tokens of "
+                        f"{len(hs)} of {w.H} heads ({dt:.1f} s); value scaled to all heads"))
+
+
+def counter_run(wid: int):
+    """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes.
+
+    The copy moves exactly 1 GiB in each direction, so its counter readings
+    give the factor that turns a counter reading into bytes."""
+    import torch
+
+    from linear_attention_kda_amd import binding
+    from linear_attention_kda_amd.workloads import make_inputs
+
+    a = torch.rand(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    x = make_inputs(wid, "cuda")
+    w = x["workload"]
+    sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    final = torch.empty(w.num_states, w.H, 128, 128, dtype=sdt[w.final_state],
+                        device="cuda") if w.final_state else None
+    out = torch.empty_like(x["v"])
+    for _ in range(2):
+        binding.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
+                    initial_state=x["initial_state"], final_state=final,
+                    cu_seqlens=x["cu_seqlens"], out=out)
+    torch.cuda.synchronize()
+    log(f"[bench] counter run done: 2 copies of 1 GiB, 2 launches of {w.name}")
 
 
 def main():
@@ -149,13 +183,16 @@ def main():
                     help="second workload timed and reported under 'secondary' (-1: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--counters", action="store_true",
+                    help="untimed run for hardware-counter passes: a 1 GiB device copy "
+                         "(the calibration kernel) twice, then two launches of the workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: the KDA forward pass shards by heads and "
-              "sequences with no communication, and this build measures one GPU's share "
-              "(see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the KDA forward pass splits across GPUs by "
+              "heads and sequences with no communication, so a single GPU's share at its "
+              "real shape is the whole measurement; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -164,6 +201,10 @@ def main():
         sys.exit(2)
     from linear_attention_kda_amd import binding, perfmodel
     binding.load_library()
+
+    if args.counters:
+        counter_run(args.workload)
+        return
 
     log(f"[bench] workload {args.workload}, warmup {args.warmup}, steps {args.steps}")
     r, x, _ = time_workload(args.workload, args.steps, args.warmup)
