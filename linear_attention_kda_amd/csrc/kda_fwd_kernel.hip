@@ -72,7 +72,7 @@ constexpr int TS = D + 4;    // row stride (bf16) of token-major [64][128] tiles
 constexpr int CS = C + 4;    // row stride (bf16) of channel-major [.][64] tiles: 136 B
 constexpr int QS = C + 4;    // row stride (bf16) of [64][64] tiles: 136 B
 constexpr int LS = 16 + 4;   // row stride (bf16) of the diagonal-block inverses
-constexpr int NS = 16 + 4;   // row stride (fp32) of the transposed diagonal blocks of A
+constexpr int NS = 16 + 4;   // row stride (fp32) of the diagonal blocks of A
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Shared-memory plan; one workgroup per CU.
@@ -88,7 +88,7 @@ struct alignas(16) Smem {
   __bf16 mm[C * QS];    // M (lower incl. diagonal), zero elsewhere
   __bf16 an[C * QS];    // -A on the off-diagonal 16x16 blocks
   __bf16 li[C * LS];    // inverses of the 4 diagonal blocks of L = I + A
-  float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A, transposed: [b][i][r]
+  float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A (beta-scaled, fp32): [b][r][i]
   float gamc[D];        // exp(G_last) per channel
   float beta[C];        // beta of the chunk in the state pass
   float pbeta[C];       // beta of the chunk being prepared
@@ -196,7 +196,7 @@ __device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, in
 
 // Phase C tile work of wave `wave` (0..7): the seven scaled pairs one per wave,
 // the three unscaled pairs (1,0), (2,1), (3,2) together on wave 7.  Writes -A off
-// the diagonal, A's diagonal blocks transposed (fp32, for the inverse), and M.
+// the diagonal, A's diagonal blocks (fp32, for the inverse), and M.
 template <int NV>
 __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16) {
   const int npairs = wave < 7 ? 1 : 3;
@@ -217,8 +217,8 @@ __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int 
       vm[tt] = (i <= r) ? tm[tt] : 0.f;
     }
     if (ib == rb) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) sm.ndt[(rb * 16 + 4 * q4 + tt) * NS + m16] = va[tt];
+      *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
+          make_float4(va[0], va[1], va[2], va[3]);
     } else {
       *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
           pack4(-va[0], -va[1], -va[2], -va[3]);
@@ -252,42 +252,122 @@ struct ChunkRegs {
   float beta;
 };
 
-// Loads chunk `ch` of the sequence.  Each tensor gets a descriptor that starts at
-// the chunk's first row and covers exactly its `valid` rows, so rows past the end
-// of a partial last chunk read as zero (zero rows leave the recurrence unchanged:
-// k = 0, v = 0, beta = 0, g = 0).
-template <int NV>
-__device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, const Work& w,
-                                           int ch, int t) {
-  const int rg = t >> 5, cg = t & 31;
+// Buffer descriptors for chunk `ch` of the sequence.  Each tensor's descriptor
+// starts at the chunk's first row and covers exactly its `valid` rows, so rows
+// past the end of a partial last chunk read as zero (zero rows leave the
+// recurrence unchanged: k = 0, v = 0, beta = 0, g = 0).
+struct ChunkSrc {
+  __amdgpu_buffer_rsrc_t g, q, k, v, b;
+};
+
+__device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, int ch) {
   const int64_t tok0 = w.bos + (int64_t)ch * C;
   const int64_t rest = w.len - (int64_t)ch * C;
-  const int valid = rest < C ? (int)rest : C;
+  // chunks past the end of the sequence get empty descriptors: every load is zero
+  const int valid = rest <= 0 ? 0 : rest < C ? (int)rest : C;
   const int HD = p.H * D;
   const int64_t base = tok0 * HD + (int64_t)w.h * D;
-  const auto rg_ = rsrc(p.g + base, valid * HD * 4);
-  const auto rq_ = rsrc(p.q + base, valid * HD * 2);
-  const auto rk_ = rsrc(p.k + base, valid * HD * 2);
-  const auto rv_ = rsrc(p.v + base + w.j0, valid * HD * 2);
-  const auto rb_ = rsrc(p.beta + tok0 * p.H + w.h, valid * p.H * 4);
+  ChunkSrc s;
+  s.g = rsrc(p.g + base, valid * HD * 4);
+  s.q = rsrc(p.q + base, valid * HD * 2);
+  s.k = rsrc(p.k + base, valid * HD * 2);
+  s.v = rsrc(p.v + base + w.j0, valid * HD * 2);
+  s.b = rsrc(p.beta + tok0 * p.H + w.h, valid * p.H * 4);
+  return s;
+}
+
+// Prep thread t loads rows 8*rg..8*rg+7, channels 4*cg..4*cg+3 (rg = t/32,
+// cg = t%32), in pieces so that each register set is refilled as soon as the
+// previous chunk has consumed it.
+template <int NV>
+__device__ __forceinline__ void load_g(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t) {
+  const int rg = t >> 5, cg = t & 31;
+  const int vo = rg * 8 * HD * 4 + 16 * cg;  // lane part; the row goes in soffset
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) {
-    const int row = rg * 8 + r8;
-    const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(rg_, row * HD * 4 + 16 * cg, 0, 0);
+    const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(s.g, vo, r8 * HD * 4, 0);
     R.g[r8] = make_float4(gv[0], gv[1], gv[2], gv[3]);
-    const auto qv = __builtin_amdgcn_raw_buffer_load_b64(rq_, row * HD * 2 + 8 * cg, 0, 0);
-    const auto kv = __builtin_amdgcn_raw_buffer_load_b64(rk_, row * HD * 2 + 8 * cg, 0, 0);
-    R.q[r8] = make_uint2(qv[0], qv[1]);
-    R.k[r8] = make_uint2(kv[0], kv[1]);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void load_qk(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t, int r8) {
+  const int rg = t >> 5, cg = t & 31;
+  const int vo = rg * 8 * HD * 2 + 8 * cg;
+  const auto qv = __builtin_amdgcn_raw_buffer_load_b64(s.q, vo, r8 * HD * 2, 0);
+  const auto kv = __builtin_amdgcn_raw_buffer_load_b64(s.k, vo, r8 * HD * 2, 0);
+  R.q[r8] = make_uint2(qv[0], qv[1]);
+  R.k[r8] = make_uint2(kv[0], kv[1]);
+}
+
+template <int NV>
+__device__ __forceinline__ void load_v(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t) {
+  const int rg = t >> 5, cg = t & 31;
+#pragma unroll
+  for (int r8 = 0; r8 < 8; ++r8) {
     if constexpr (NV == 128) {
-      const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rv_, row * HD * 2 + 8 * cg, 0, 0);
+      const auto vv = __builtin_amdgcn_raw_buffer_load_b64(s.v, rg * 8 * HD * 2 + 8 * cg, r8 * HD * 2, 0);
       R.v[r8][0] = vv[0];
       R.v[r8][1] = vv[1];
     } else {
-      R.v[r8][0] = __builtin_amdgcn_raw_buffer_load_b32(rv_, row * HD * 2 + 4 * cg, 0, 0);
+      R.v[r8][0] = __builtin_amdgcn_raw_buffer_load_b32(s.v, rg * 8 * HD * 2 + 4 * cg, r8 * HD * 2, 0);
     }
   }
-  R.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, (t & 63) * p.H * 4, 0, 0));
+}
+
+template <int NV>
+__device__ __forceinline__ void load_beta(ChunkRegs<NV>& R, const ChunkSrc& s, int H, int t) {
+  R.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.b, (t & 63) * H * 4, 0, 0));
+}
+
+template <int NV>
+__device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, const Work& w,
+                                           int ch, int t) {
+  const ChunkSrc s = chunk_src(p, w, ch);
+  const int HD = p.H * D;
+  load_beta<NV>(R, s, p.H, t);
+  load_g<NV>(R, s, HD, t);
+#pragma unroll
+  for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, s, HD, t, r8);
+  load_v<NV>(R, s, HD, t);
+}
+
+// Value of x in lane `src` of this lane's 16-lane row (DPP row broadcast).
+template <int src>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                           0x150 + src, 0xF, 0xF, false));
+}
+
+// Inverse of the diagonal block b of L = I + A (A strictly lower, beta-scaled, fp32
+// rows in ndt), written as bf16 to li.  One wave: lane (q4, m16) holds
+// X[r = m16][j = 4q4 + t], t < 4, and the right-looking substitution
+// X[r][.] -= N[r][i] X[i][.] (all r at once; N[r][i] = 0 for r <= i) takes row i
+// from lane i of the same 16-lane row once it is final.
+template <int i>
+__device__ __forceinline__ void inverse_step(float (&x)[4], const float (&n)[16]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) x[t] = fmaf(-n[i], row_bcast<i>(x[t]), x[t]);
+}
+
+template <int NV>
+__device__ __forceinline__ void diag_inverse(Smem<NV>& sm, int b, int q4, int m16) {
+  const float* Nr = &sm.ndt[(b * 16 + m16) * NS];
+  float n[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(&Nr[4 * c]);
+    n[4 * c] = v.x; n[4 * c + 1] = v.y; n[4 * c + 2] = v.z; n[4 * c + 3] = v.w;
+  }
+  float x[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) x[t] = (m16 == 4 * q4 + t) ? 1.f : 0.f;
+  inverse_step<0>(x, n);  inverse_step<1>(x, n);  inverse_step<2>(x, n);
+  inverse_step<3>(x, n);  inverse_step<4>(x, n);  inverse_step<5>(x, n);
+  inverse_step<6>(x, n);  inverse_step<7>(x, n);  inverse_step<8>(x, n);
+  inverse_step<9>(x, n);  inverse_step<10>(x, n); inverse_step<11>(x, n);
+  inverse_step<12>(x, n); inverse_step<13>(x, n); inverse_step<14>(x, n);
+  *reinterpret_cast<uint2*>(&sm.li[(16 * b + m16) * LS + 4 * q4]) = pack4(x[0], x[1], x[2], x[3]);
 }
 
 template <int NV>
@@ -299,43 +379,26 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
   const int blk = pw;                      // 16-row block of this thread's rows
   const bool second = (rg & 1) != 0;       // rows 8..15 of the block
   constexpr int VPT = NV / 32;             // value columns per thread
+  const int HD = p.H * D;
+  // wave-uniform 0/1 selectors of this wave's block (multiplied in, never branched on)
+  const float m0 = blk == 0 ? 1.f : 0.f, m1 = blk == 1 ? 1.f : 0.f;
+  const float m2 = blk == 2 ? 1.f : 0.f, m3 = blk == 3 ? 1.f : 0.f;
 
   ChunkRegs<NV> R;
-  if (w.nchunks > 0) load_chunk<NV>(R, p, w, 0, t);
+  load_chunk<NV>(R, p, w, 0, t);
 
-  for (int it = -1; it < w.nchunks; ++it) {
-    const int pc = it + 1;                 // chunk prepared in this iteration
-    const bool act = pc < w.nchunks;
+  // Iteration it prepares chunk pc = it + 1 while the state waves run chunk it.
+  // The loop body has no branches around its loads, so the memory-counter waits
+  // stay exact; the state waves' last chunk is finished after the loop.
+  for (int it = -1; it < w.nchunks - 1; ++it) {
+    const int pc = it + 1;
     uint2 kpt_hold[4][2];                  // channel 4cg+e: rows 8rg..8rg+3, 8rg+4..8rg+7
     float4 gamc_hold;
 
-    // ---- phase A: inverse of diagonal block pw of L for chunk `it` (used in the
-    // state waves' phase B): right-looking forward substitution, lane j = m16 owns
-    // column j (lanes 16-63 mirror lanes 0-15).
-    if (it >= 0) {
-      const int j = m16;
-      const float* N = &sm.ndt[pw * 16 * NS];  // N[i * NS + r] = A[16pw + r][16pw + i]
-      float xv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xv[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) {
-        const float4 c0 = *reinterpret_cast<const float4*>(&N[i * NS + 0]);
-        const float4 c1 = *reinterpret_cast<const float4*>(&N[i * NS + 4]);
-        const float4 c2 = *reinterpret_cast<const float4*>(&N[i * NS + 8]);
-        const float4 c3 = *reinterpret_cast<const float4*>(&N[i * NS + 12]);
-        const float col[16] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
-                               c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
-#pragma unroll
-        for (int r = i + 1; r < 16; ++r) xv[r] -= col[r] * xv[i];
-      }
-      if (lane < 16) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.li[(16 * pw + r) * LS + j] = (__bf16)xv[r];
-      }
-    }
-    // per-thread sums of g*log2(e) over its 8 rows, for chunk pc
-    if (act) {
+    // ---- phase A: inverses for chunk `it` (used in the state waves' phase B) and
+    // the per-thread sums of g*log2(e) over its 8 rows of chunk pc
+    if (it >= 0) diag_inverse(sm, pw, q4, m16);
+    {
       float4 s = R.g[0];
 #pragma unroll
       for (int r8 = 1; r8 < 8; ++r8) {
@@ -348,103 +411,127 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
     __syncthreads();  // (A) the state waves are done with K exp(G), Q exp(G), V^T, beta
 
     // ---- phase B: gated operand tiles of chunk pc
-    if (act) {
-      // X[b] = G (log2) at the last row of block b-1 (X[0] = 0, X[4] = G_last);
-      // Xb, Xb1 = X of this thread's block and the next; sfirst, ssecond = the two
-      // 8-row sums of this block.  Masks are wave-uniform scalars, so no branches.
-      float X[5][4], Xb[4], Xb1[4], sfirst[4], ssecond[4];
+    {
+      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
+      // beta of the next chunk is fetched first: the next phase A waits only for
+      // beta and g (the memory counter retires loads in order)
+      if (t < C) sm.beta[t] = R.beta;
+      load_beta<NV>(R, nsrc, p.H, t);
+      float eCX[4], eXb[4], pother[4];
       {
-        float run[4] = {0.f, 0.f, 0.f, 0.f};
+        // X[k] = G (log2) at the last row of block k-1 per channel (X[0] = 0,
+        // X[4] = G_last): running sums of the 8-row group sums.
+        float X[5][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          X[0][e] = 0.f;
-          Xb[e] = Xb1[e] = sfirst[e] = ssecond[e] = 0.f;
-        }
+        for (int e = 0; e < 4; ++e) X[0][e] = 0.f;
+        float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const float4 sg = *reinterpret_cast<const float4*>(&sm.seg[r * D + 4 * cg]);
-          const float sv[4] = {sg.x, sg.y, sg.z, sg.w};
-          const float m_b = r < 2 * blk ? 1.f : 0.f;
-          const float m_b1 = r < 2 * blk + 2 ? 1.f : 0.f;
-          const float m_f = r == 2 * blk ? 1.f : 0.f;
-          const float m_s = r == 2 * blk + 1 ? 1.f : 0.f;
+          run[0] += sg.x; run[1] += sg.y; run[2] += sg.z; run[3] += sg.w;
+          if (r & 1) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            run[e] += sv[e];
-            if (r & 1) X[(r + 1) >> 1][e] = run[e];
-            Xb[e] = fmaf(m_b, sv[e], Xb[e]);
-            Xb1[e] = fmaf(m_b1, sv[e], Xb1[e]);
-            sfirst[e] = fmaf(m_f, sv[e], sfirst[e]);
-            ssecond[e] = fmaf(m_s, sv[e], ssecond[e]);
+            for (int e = 0; e < 4; ++e) X[(r + 1) >> 1][e] = run[e];
           }
         }
-      }
-      float a[8][4];  // per-token decay a = exp2(g log2 e)
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        a[r8][0] = ex2(R.g[r8].x * LOG2E);
-        a[r8][1] = ex2(R.g[r8].y * LOG2E);
-        a[r8][2] = ex2(R.g[r8].z * LOG2E);
-        a[r8][3] = ex2(R.g[r8].w * LOG2E);
-      }
-      float F[4], Hv[4], eCX[4], eXb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pfirst = ex2(sfirst[e]), psecond = ex2(ssecond[e]);
-        F[e] = second ? pfirst : 1.f;    // F of the row before this thread's first
-        Hv[e] = second ? 1.f : psecond;  // H of this thread's last row
-        eCX[e] = ex2(X[4][e] - Xb1[e]);
-        eXb[e] = ex2(Xb[e]);
-      }
-      // rows are walked last to first for H (H_r = H_{r+1} a_{r+1}); F is then
-      // rebuilt forwards from F_{r} = F_{r-1} a_r, so both need only a[][]
-      float Hs[8][4];
-#pragma unroll
-      for (int r8 = 7; r8 >= 0; --r8) {
+        // the other half of this block: its 8-row sum starts F (second half) or H (first)
+        const float4 sp = *reinterpret_cast<const float4*>(&sm.seg[(rg ^ 1) * D + 4 * cg]);
+        const float spv[4] = {sp.x, sp.y, sp.z, sp.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          Hs[r8][e] = Hv[e];
-          Hv[e] *= a[r8][e];
+          const float Xb = m1 * X[1][e] + m2 * X[2][e] + m3 * X[3][e];
+          const float Xb1 = m0 * X[1][e] + m1 * X[2][e] + m2 * X[3][e] + m3 * X[4][e];
+          pother[e] = ex2(spv[e]);
+          eCX[e] = ex2(X[4][e] - Xb1);
+          eXb[e] = ex2(Xb);
         }
-      }
-      uint32_t kpw[4][4];  // K' of row pairs, per channel
-      float kp_prev[4];
+        // pair factors exp(X_rb - X_{ib+1}): prep wave pw covers pairs pw, pw+4, pw+8
+        // (lanes 32-63 hold the same channels as lanes 0-31 and skip the store)
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        const int row = rg * 8 + r8;
-        float qf[4], kf[4], kr[4], qr[4], kh[4], kp[4], kg[4], qg[4];
-        unpack4(R.q[r8], qf);
-        unpack4(R.k[r8], kf);
+        for (int pr = 0; pr < 10; ++pr) {
+          if ((pr & 3) == pw) {
+            const int rb = pair_rb(pr), ib = pair_ib(pr);
+            float4 f;
+            float* fp = reinterpret_cast<float*>(&f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fp[e] = ex2(X[rb][e] - X[ib + 1][e]);
+            if (!second) *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
+          }
+        }
+        gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
+      }
+      // per-token decay a = exp2(g log2 e), in place of g
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        R.g[r8] = make_float4(ex2(R.g[r8].x * LOG2E), ex2(R.g[r8].y * LOG2E),
+                              ex2(R.g[r8].z * LOG2E), ex2(R.g[r8].w * LOG2E));
+      // H_r = H_{r+1} a_{r+1}, last row first: the column operand K * H and the
+      // state-update operand K * H * exp(G_last - X_{b+1}), packed by row pairs
+      {
+        float Hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Hv[e] = second ? 1.f : pother[e];  // H of the last row
+        float kp_next[4];
+        uint32_t kpw[4][4];  // K' of row pairs (2j, 2j+1), per channel
+#pragma unroll
+        for (int r8 = 7; r8 >= 0; --r8) {
+          const int row = rg * 8 + r8;
+          float kf[4], kh[4], kp[4];
+          unpack4(R.k[r8], kf);
+          const float4 av = R.g[r8];
+          const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kh[e] = kf[e] * Hv[e];
+            kp[e] = kh[e] * eCX[e];
+            Hv[e] *= ar[e];
+          }
+          *reinterpret_cast<uint2*>(&sm.kh[row * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+          if (r8 & 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kp_next[e] = kp[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp[e], kp_next[e]);
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          F[e] *= a[r8][e];
-          kr[e] = kf[e] * F[e];
-          qr[e] = qf[e] * F[e];
-          kh[e] = kf[e] * Hs[r8][e];
-          kp[e] = kh[e] * eCX[e];
-          kg[e] = kr[e] * eXb[e];
-          qg[e] = qr[e] * eXb[e];
-        }
-        const int o = row * TS + 4 * cg;
-        *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
-        *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
-        *reinterpret_cast<uint2*>(&sm.kh[o]) = pack4(kh[0], kh[1], kh[2], kh[3]);
-        *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
-        *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
-        if (r8 & 1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp_prev[e], kp[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kp_prev[e] = kp[e];
+          kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
+          kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
         }
       }
+      // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F and the state
+      // operands K * exp(G) = K * F * exp(X_b), Q * exp(G)
+      {
+        float F[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
-        kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
+        for (int e = 0; e < 4; ++e) F[e] = second ? pother[e] : 1.f;  // F of the row before
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+          const int row = rg * 8 + r8;
+          float qf[4], kf[4], kr[4], qr[4], kg[4], qg[4];
+          unpack4(R.q[r8], qf);
+          unpack4(R.k[r8], kf);
+          const float4 av = R.g[r8];
+          const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F[e] *= ar[e];
+            kr[e] = kf[e] * F[e];
+            qr[e] = qf[e] * F[e];
+            kg[e] = kr[e] * eXb[e];
+            qg[e] = qr[e] * eXb[e];
+          }
+          const int o = row * TS + 4 * cg;
+          *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
+          *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
+          *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
+          *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
+        }
       }
-      // V^T (channel-major) and beta
+      load_g<NV>(R, nsrc, HD, t);  // the decays of this chunk are consumed
+      // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
         uint32_t hv[8];
@@ -457,32 +544,16 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
         *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
       }
-      if (t < C) sm.beta[t] = R.beta;
-      // pair factors exp(X_rb - X_{ib+1}): prep wave pw covers pairs pw, pw+4, pw+8
-      // (lanes 32-63 hold the same channels as lanes 0-31 and skip the store)
-#pragma unroll
-      for (int pr = 0; pr < 10; ++pr) {
-        if ((pr & 3) == pw) {
-          const int rb = pair_rb(pr), ib = pair_ib(pr);
-          float4 f;
-          float* fp = reinterpret_cast<float*>(&f);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float xr = rb == 0 ? X[0][e] : rb == 1 ? X[1][e] : rb == 2 ? X[2][e] : X[3][e];
-            const float xi = ib == 0 ? X[1][e] : ib == 1 ? X[2][e] : ib == 2 ? X[3][e] : X[4][e];
-            fp[e] = ex2(xr - xi);
-          }
-          if (!second) *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
-        }
-      }
-      gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
-      // the raw registers are consumed: fetch the chunk after this one
-      if (pc + 1 < w.nchunks) load_chunk<NV>(R, p, w, pc + 1, t);
     }
     __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
 
     // ---- phase C: state-update operand and A tiles of chunk pc
-    if (act) {
+    {
+      // q, k and v of chunk pc are consumed: fetch those of the next chunk
+      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
+      load_v<NV>(R, nsrc, HD, t);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int o = (4 * cg + e) * CS + rg * 8;
@@ -494,6 +565,11 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
     }
     __syncthreads();  // (C) chunk pc fully published
   }
+  // the state waves' last chunk: its inverses, then the same three barriers
+  if (w.nchunks > 0) diag_inverse(sm, pw, q4, m16);
+  __syncthreads();
+  __syncthreads();
+  __syncthreads();
 }
 
 // ============================================================================ state waves
@@ -535,11 +611,6 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     }
   }
 
-  bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
 
   const int HD = p.H * D;
   for (int it = -1; it < w.nchunks; ++it) {
@@ -552,6 +623,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 
     // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
     if (act) {
+      bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -616,6 +693,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
       }
       // O^T += U^T M^T, scale, store (rows past `valid` fall outside the descriptor)
       const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
+      const int ovo = m16 * HD * 2 + (jw_base + 4 * q4) * 2;  // lane part of the store offset
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + m16;
@@ -630,7 +708,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           const uint2 ov = pack4(p.scale * o[0], p.scale * o[1], p.scale * o[2], p.scale * o[3]);
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-              r * HD * 2 + (jw_base + 16 * jt + 4 * q4) * 2, 0, 0);
+              ovo + 32 * jt, 16 * rt * HD * 2, 0);
         }
       }
       // S <- Diag(exp(G_last)) S + K'^T U
@@ -651,11 +729,6 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           Sacc[ct][jt] = s;
         }
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
-          Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
     }
     __syncthreads();  // (B)
 
