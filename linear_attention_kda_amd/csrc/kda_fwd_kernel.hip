@@ -47,6 +47,7 @@
 // MFMA operand layouts used below (64 lanes, q = lane/16, m = lane%16):
 //  16x16x32 bf16:  A[m][8q+e], B[8q+e][m] (e < 8),  D[4q+t][m] (t < 4)
 //  16x16x16 bf16:  A[m][4q+e], B[4q+e][m] (e < 4),  D[4q+t][m]
+//  16x16x4 fp32:   A[m][q],    B[q][m],                D[4q+t][m]
 // A contraction may permute its k index as long as both operands agree; the
 // state path uses k-slot e <-> k = 32ks + 4q + e (e < 4), 32ks + 16 + 4q + e-4
 // (e >= 4), which is exactly what two D-layout tiles (rows 32ks..+15 and
@@ -71,7 +72,7 @@ constexpr int NP = 256;      // prep threads
 constexpr int TS = D + 4;    // row stride (bf16) of token-major [64][128] tiles: 264 B
 constexpr int CS = C + 4;    // row stride (bf16) of channel-major [.][64] tiles: 136 B
 constexpr int QS = C + 4;    // row stride (bf16) of [64][64] tiles: 136 B
-constexpr int LS = 16 + 4;   // row stride (bf16) of the diagonal-block inverses
+constexpr int LS = 16 + 4;   // row stride (fp32) of the diagonal-block inverses
 constexpr int NS = 16 + 4;   // row stride (fp32) of the diagonal blocks of A
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -87,7 +88,7 @@ struct alignas(16) Smem {
   __bf16 vt[NV * CS];   // V^T (this slice's columns)  channel-major
   __bf16 mm[C * QS];    // M (lower incl. diagonal), zero elsewhere
   __bf16 an[C * QS];    // -A on the off-diagonal 16x16 blocks
-  __bf16 li[C * LS];    // inverses of the 4 diagonal blocks of L = I + A
+  float li[C * LS];     // inverses of the 4 diagonal blocks of L = I + A (fp32)
   float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A (beta-scaled, fp32): [b][r][i]
   float gamc[D];        // exp(G_last) per channel
   float beta[C];        // beta of the chunk in the state pass
@@ -124,6 +125,10 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma4f(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Two 4-element bf16 runs (8-byte aligned) -> one 16x16x32 operand.
@@ -194,16 +199,18 @@ __device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, in
   }
 }
 
-// Phase C tile work of wave `wave` (0..7): the seven scaled pairs one per wave,
-// the three unscaled pairs (1,0), (2,1), (3,2) together on wave 7.  Writes -A off
-// the diagonal, A's diagonal blocks (fp32, for the inverse), and M.
+// Phase C tile work of wave `wave` (0..7, wave-uniform).  Waves 0 and 1 (state
+// waves) take two pairs each: (0,0) + (1,0) and (1,1) + (2,1); the others one
+// each: (2,0), (2,2), (3,0), (3,1), (3,3), (3,2).  Writes -A off the diagonal, A's
+// diagonal blocks (fp32, for the inverse), and scale * M.
 template <int NV>
-__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16) {
-  const int npairs = wave < 7 ? 1 : 3;
+__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16, float scale) {
+  const int npairs = wave < 2 ? 2 : 1;
 #pragma unroll 1
   for (int x = 0; x < npairs; ++x) {
-    const int pr = wave < 7 ? (wave < 2 ? 2 * wave : wave == 2 ? 3 : wave == 6 ? 9 : wave + 2)
-                            : 1 + 3 * x + (x == 2 ? 1 : 0);
+    const int pr = x == 1 ? (wave == 0 ? 1 : 4)
+                          : (wave < 2 ? 2 * wave : wave < 4 ? 2 * wave - 1 : wave < 6 ? wave + 2
+                                                            : wave == 6 ? 9 : 8);
     const int rb = pair_rb(pr), ib = pair_ib(pr);
     f32x4 ta, tm;
     tile_pair(sm, pr, q4, m16, ta, tm);
@@ -214,7 +221,7 @@ __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int 
     for (int tt = 0; tt < 4; ++tt) {
       const int i = 16 * ib + 4 * q4 + tt;
       va[tt] = (i < r) ? br * ta[tt] : 0.f;
-      vm[tt] = (i <= r) ? tm[tt] : 0.f;
+      vm[tt] = (i <= r) ? scale * tm[tt] : 0.f;
     }
     if (ib == rb) {
       *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
@@ -325,10 +332,15 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, co
                                            int ch, int t) {
   const ChunkSrc s = chunk_src(p, w, ch);
   const int HD = p.H * D;
+  // the scheduling barriers keep this issue order, which the loop's memory-counter
+  // waits assume on entry as well
   load_beta<NV>(R, s, p.H, t);
+  __builtin_amdgcn_sched_barrier(0);
   load_g<NV>(R, s, HD, t);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, s, HD, t, r8);
+  __builtin_amdgcn_sched_barrier(0);
   load_v<NV>(R, s, HD, t);
 }
 
@@ -340,7 +352,7 @@ __device__ __forceinline__ float row_bcast(float x) {
 }
 
 // Inverse of the diagonal block b of L = I + A (A strictly lower, beta-scaled, fp32
-// rows in ndt), written as bf16 to li.  One wave: lane (q4, m16) holds
+// rows in ndt), written to li in fp32.  One wave: lane (q4, m16) holds
 // X[r = m16][j = 4q4 + t], t < 4, and the right-looking substitution
 // X[r][.] -= N[r][i] X[i][.] (all r at once; N[r][i] = 0 for r <= i) takes row i
 // from lane i of the same 16-lane row once it is final.
@@ -367,7 +379,7 @@ __device__ __forceinline__ void diag_inverse(Smem<NV>& sm, int b, int q4, int m1
   inverse_step<6>(x, n);  inverse_step<7>(x, n);  inverse_step<8>(x, n);
   inverse_step<9>(x, n);  inverse_step<10>(x, n); inverse_step<11>(x, n);
   inverse_step<12>(x, n); inverse_step<13>(x, n); inverse_step<14>(x, n);
-  *reinterpret_cast<uint2*>(&sm.li[(16 * b + m16) * LS + 4 * q4]) = pack4(x[0], x[1], x[2], x[3]);
+  *reinterpret_cast<float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
 template <int NV>
@@ -502,11 +514,15 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         }
       }
       // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F and the state
-      // operands K * exp(G) = K * F * exp(X_b), Q * exp(G)
+      // operands -K * exp(G) = -K * F * exp(X_b) and scale * Q * exp(G)
       {
-        float F[4];
+        float F[4], nXb[4], sXb[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) F[e] = second ? pother[e] : 1.f;  // F of the row before
+        for (int e = 0; e < 4; ++e) {
+          F[e] = second ? pother[e] : 1.f;  // F of the row before
+          nXb[e] = -eXb[e];
+          sXb[e] = p.scale * eXb[e];
+        }
 #pragma unroll
         for (int r8 = 0; r8 < 8; ++r8) {
           const int row = rg * 8 + r8;
@@ -520,8 +536,8 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
             F[e] *= ar[e];
             kr[e] = kf[e] * F[e];
             qr[e] = qf[e] * F[e];
-            kg[e] = kr[e] * eXb[e];
-            qg[e] = qr[e] * eXb[e];
+            kg[e] = kr[e] * nXb[e];   // -K exp(G)
+            qg[e] = qr[e] * sXb[e];   // scale * Q exp(G)
           }
           const int o = row * TS + 4 * cg;
           *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
@@ -534,15 +550,16 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
-        uint32_t hv[8];
+        // column e of this thread: the low (even e) or high half of each row's word,
+        // two rows per 32-bit word
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t pw2[4];
 #pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) {
-          const uint32_t word = R.v[r8][e >> 1];
-          hv[r8] = (e & 1) ? (word >> 16) : (word & 0xffffu);
-        }
+        for (int j = 0; j < 4; ++j)
+          pw2[j] = __builtin_amdgcn_perm(R.v[2 * j + 1][e >> 1], R.v[2 * j][e >> 1], sel);
         const int o = (VPT * cg + e) * CS + rg * 8;
-        *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+        *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(pw2[0], pw2[1]);
+        *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(pw2[2], pw2[3]);
       }
     }
     __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
@@ -561,7 +578,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
       if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
-      build_tiles(sm, 4 + pw, q4, m16);
+      build_tiles(sm, 4 + pw, q4, m16, p.scale);
     }
     __syncthreads();  // (C) chunk pc fully published
   }
@@ -622,6 +639,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     f32x4 O[4][JT];   // O^T: row j = 16jt + 4q4 + t, column r = 16rt + m16
 
     // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
+    // (the prep waves store -K exp(G) and scale * Q exp(G))
     if (act) {
       bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
 #pragma unroll
@@ -629,11 +647,15 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
           Sfrag[ks][jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
+      // Z starts at V and accumulates (-K exp(G)) S
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
-          Z[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int jl = jl_base + 16 * jt + m16;
+          float vv[4];
+          unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + 16 * b + 4 * q4]), vv);
+          Z[b][jt] = f32x4{vv[0], vv[1], vv[2], vv[3]};
           O[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -656,13 +678,9 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
         const float4 bb = *reinterpret_cast<const float4*>(&sm.beta[16 * b + 4 * q4]);
         const float bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          const int jl = jl_base + 16 * jt + m16;
-          float vv[4];
-          unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + 16 * b + 4 * q4]), vv);
+        for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) Z[b][jt][t] = bv[t] * (vv[t] - Z[b][jt][t]);
-        }
+          for (int t = 0; t < 4; ++t) Z[b][jt][t] *= bv[t];
       }
     }
     __syncthreads();  // (A)
@@ -672,7 +690,9 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
       bf16x4 U[4][JT];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const bf16x4 linv = ld4(&sm.li[(16 * b + m16) * LS + 4 * q4]);
+        // row m16 of the block's inverse, Li[m16][4q4 + kb]; U = Li z in fp32 with
+        // the k index of product kb at 4q4 + kb, so z enters in its D layout
+        const float4 lv = *reinterpret_cast<const float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]);
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           f32x4 z = Z[b][jt];
@@ -681,17 +701,14 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             const bf16x4 an = ld4(&sm.an[(16 * b + m16) * QS + 16 * bp + 4 * q4]);
             z = mfma16(an, U[bp][jt], z);
           }
-          // z = hi + lo in bf16 (the rounding of z would otherwise reach U in full)
-          const bf16x4 zh = cvt4(z);
-          f32x4 zl;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) zl[t] = z[t] - bf2f(zh[t]);
-          f32x4 u = mfma16(linv, zh, f32x4{0.f, 0.f, 0.f, 0.f});
-          u = mfma16(linv, cvt4(zl), u);
+          f32x4 u = mfma4f(lv.x, z[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          u = mfma4f(lv.y, z[1], u);
+          u = mfma4f(lv.z, z[2], u);
+          u = mfma4f(lv.w, z[3], u);
           U[b][jt] = cvt4(u);
         }
       }
-      // O^T += U^T M^T, scale, store (rows past `valid` fall outside the descriptor)
+      // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor)
       const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
       const int ovo = m16 * HD * 2 + (jw_base + 4 * q4) * 2;  // lane part of the store offset
 #pragma unroll
@@ -705,7 +722,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
             o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
           }
-          const uint2 ov = pack4(p.scale * o[0], p.scale * o[1], p.scale * o[2], p.scale * o[3]);
+          const uint2 ov = pack4(o[0], o[1], o[2], o[3]);  // the scale is in Q exp(G) and M
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
               ovo + 32 * jt, 16 * rt * HD * 2, 0);
@@ -733,7 +750,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     __syncthreads();  // (B)
 
     // ---- phase C: A and M tiles of the next chunk (shared with the prep waves)
-    if (it + 1 < w.nchunks) build_tiles(sm, wave, q4, m16);
+    if (it + 1 < w.nchunks) build_tiles(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16, p.scale);
     __syncthreads();  // (C)
   }
 
@@ -795,11 +812,19 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
       if (rk == rank) sm.order = i;
     }
     __syncthreads();
-    n = sm.order;
+    n = __builtin_amdgcn_readfirstlane(sm.order);  // the same for every wave
     __syncthreads();  // the scratch is reused by the prep waves
   }
-  w.bos = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
-  w.len = p.cu ? (int64_t)p.cu[n + 1] - w.bos : p.T;
+  // sequence bounds, made wave-uniform so that every buffer descriptor is scalar
+  if (p.cu) {
+    const int c0 = __builtin_amdgcn_readfirstlane(p.cu[n]);
+    const int c1 = __builtin_amdgcn_readfirstlane(p.cu[n + 1]);
+    w.bos = c0;
+    w.len = (int64_t)c1 - c0;
+  } else {
+    w.bos = (int64_t)n * p.T;
+    w.len = p.T;
+  }
   w.nchunks = (int)((w.len + C - 1) / C);
 
   // constant zeros: M blocks above the diagonal that the 32-wide k-steps touch
