@@ -395,6 +395,22 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
   // wave-uniform 0/1 selectors of this wave's block (multiplied in, never branched on)
   const float m0 = blk == 0 ? 1.f : 0.f, m1 = blk == 1 ? 1.f : 0.f;
   const float m2 = blk == 2 ? 1.f : 0.f, m3 = blk == 3 ? 1.f : 0.f;
+  // Each half-wave (pw, second) produces one per-channel factor: the seven pairs
+  // that scale their column operand, exp(X_rb - X_{ib+1}), and exp(G_last) in the
+  // eighth slot.  Its exponent is sum_k wx[k] X[k] (X[0] = 0 drops out).
+  const int slot = 2 * pw + (second ? 1 : 0);
+  const int spr = slot == 0 ? 0 : slot == 1 ? 2 : slot == 2 ? 3 : slot == 3 ? 5
+                : slot == 4 ? 6 : slot == 5 ? 7 : slot == 6 ? 9 : -1;  // -1: exp(G_last)
+  float wx[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    if (spr < 0) {
+      wx[k] = k == 4 ? 1.f : 0.f;
+    } else {
+      const int rb = pair_rb(spr), ib = pair_ib(spr);
+      wx[k] = (k == rb ? 1.f : 0.f) - (k == ib + 1 ? 1.f : 0.f);
+    }
+  }
 
   ChunkRegs<NV> R;
   load_chunk<NV>(R, p, w, 0, t);
@@ -406,19 +422,48 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
     const int pc = it + 1;
     uint2 kpt_hold[4][2];                  // channel 4cg+e: rows 8rg..8rg+3, 8rg+4..8rg+7
     float4 gamc_hold;
+    float pother[4];                       // exp2 of the other half-block's sum (A -> B)
 
-    // ---- phase A: inverses for chunk `it` (used in the state waves' phase B) and
-    // the per-thread sums of g*log2(e) over its 8 rows of chunk pc
+    // ---- phase A: inverses for chunk `it` (used in the state waves' phase B); for
+    // chunk pc the 8-row sums of g*log2(e), the decays a = exp(g), and the
+    // block-local H pass: H_r = H_{r+1} a_{r+1}, last row first, and K * H
     if (it >= 0) diag_inverse(sm, pw, q4, m16);
     {
-      float4 s = R.g[0];
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r8 = 1; r8 < 8; ++r8) {
-        s.x += R.g[r8].x; s.y += R.g[r8].y; s.z += R.g[r8].z; s.w += R.g[r8].w;
+      for (int r8 = 0; r8 < 8; ++r8) {
+        float4& g = R.g[r8];
+        g.x *= LOG2E; g.y *= LOG2E; g.z *= LOG2E; g.w *= LOG2E;
+        s[0] += g.x; s[1] += g.y; s[2] += g.z; s[3] += g.w;
       }
-      *reinterpret_cast<float4*>(&sm.seg[rg * D + 4 * cg]) =
-          make_float4(s.x * LOG2E, s.y * LOG2E, s.z * LOG2E, s.w * LOG2E);
+      *reinterpret_cast<float4*>(&sm.seg[rg * D + 4 * cg]) = make_float4(s[0], s[1], s[2], s[3]);
+      // the other half of this block is lane ^ 32 of the same wave
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[e]), __float_as_uint(s[e]),
+                                                          false, false);
+        pother[e] = ex2(__uint_as_float(second ? p32[0] : p32[1]));
+      }
       if (t < C) sm.pbeta[t] = R.beta;
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        R.g[r8] = make_float4(ex2(R.g[r8].x), ex2(R.g[r8].y), ex2(R.g[r8].z), ex2(R.g[r8].w));
+      float Hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hv[e] = second ? 1.f : pother[e];  // H of the last row
+#pragma unroll
+      for (int r8 = 7; r8 >= 0; --r8) {
+        float kf[4], kh[4];
+        unpack4(R.k[r8], kf);
+        const float4 av = R.g[r8];
+        const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kh[e] = kf[e] * Hv[e];
+          Hv[e] *= ar[e];
+        }
+        *reinterpret_cast<uint2*>(&sm.kh[(rg * 8 + r8) * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+      }
     }
     __syncthreads();  // (A) the state waves are done with K exp(G), Q exp(G), V^T, beta
 
@@ -429,7 +474,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // beta and g (the memory counter retires loads in order)
       if (t < C) sm.beta[t] = R.beta;
       load_beta<NV>(R, nsrc, p.H, t);
-      float eCX[4], eXb[4], pother[4];
+      float eCX[4], eXb[4];
       {
         // X[k] = G (log2) at the last row of block k-1 per channel (X[0] = 0,
         // X[4] = G_last): running sums of the 8-row group sums.
@@ -446,76 +491,33 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
             for (int e = 0; e < 4; ++e) X[(r + 1) >> 1][e] = run[e];
           }
         }
-        // the other half of this block: its 8-row sum starts F (second half) or H (first)
-        const float4 sp = *reinterpret_cast<const float4*>(&sm.seg[(rg ^ 1) * D + 4 * cg]);
-        const float spv[4] = {sp.x, sp.y, sp.z, sp.w};
+        float fs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float Xb = m1 * X[1][e] + m2 * X[2][e] + m3 * X[3][e];
           const float Xb1 = m0 * X[1][e] + m1 * X[2][e] + m2 * X[3][e] + m3 * X[4][e];
-          pother[e] = ex2(spv[e]);
           eCX[e] = ex2(X[4][e] - Xb1);
           eXb[e] = ex2(Xb);
+          fs[e] = ex2(wx[1] * X[1][e] + wx[2] * X[2][e] + wx[3] * X[3][e] + wx[4] * X[4][e]);
         }
-        // pair factors exp(X_rb - X_{ib+1}): prep wave pw covers pairs pw, pw+4, pw+8
-        // (lanes 32-63 hold the same channels as lanes 0-31 and skip the store)
-#pragma unroll
-        for (int pr = 0; pr < 10; ++pr) {
-          if ((pr & 3) == pw) {
-            const int rb = pair_rb(pr), ib = pair_ib(pr);
-            float4 f;
-            float* fp = reinterpret_cast<float*>(&f);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fp[e] = ex2(X[rb][e] - X[ib + 1][e]);
-            if (!second) *reinterpret_cast<float4*>(&sm.pf[pr * D + 4 * cg]) = f;
-          }
-        }
-        gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
+        // this half-wave's pair factor (or exp(G_last), kept for phase C)
+        gamc_hold = make_float4(fs[0], fs[1], fs[2], fs[3]);
+        if (spr >= 0) *reinterpret_cast<float4*>(&sm.pf[spr * D + 4 * cg]) = gamc_hold;
       }
-      // per-token decay a = exp2(g log2 e), in place of g
+      // Hc_r = H_r exp(G_last - X_{b+1}) (the state-update operand K' = K * Hc)
+      float Hc[8][4];
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8)
-        R.g[r8] = make_float4(ex2(R.g[r8].x * LOG2E), ex2(R.g[r8].y * LOG2E),
-                              ex2(R.g[r8].z * LOG2E), ex2(R.g[r8].w * LOG2E));
-      // H_r = H_{r+1} a_{r+1}, last row first: the column operand K * H and the
-      // state-update operand K * H * exp(G_last - X_{b+1}), packed by row pairs
+      for (int e = 0; e < 4; ++e) Hc[7][e] = (second ? 1.f : pother[e]) * eCX[e];
+#pragma unroll
+      for (int r8 = 6; r8 >= 0; --r8) {
+        const float4 av = R.g[r8 + 1];
+        Hc[r8][0] = Hc[r8 + 1][0] * av.x; Hc[r8][1] = Hc[r8 + 1][1] * av.y;
+        Hc[r8][2] = Hc[r8 + 1][2] * av.z; Hc[r8][3] = Hc[r8 + 1][3] * av.w;
+      }
+      // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F, the state
+      // operands -K * exp(G) = -K * F * exp(X_b), scale * Q * exp(G), and K'
       {
-        float Hv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Hv[e] = second ? 1.f : pother[e];  // H of the last row
-        float kp_next[4];
         uint32_t kpw[4][4];  // K' of row pairs (2j, 2j+1), per channel
-#pragma unroll
-        for (int r8 = 7; r8 >= 0; --r8) {
-          const int row = rg * 8 + r8;
-          float kf[4], kh[4], kp[4];
-          unpack4(R.k[r8], kf);
-          const float4 av = R.g[r8];
-          const float ar[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kh[e] = kf[e] * Hv[e];
-            kp[e] = kh[e] * eCX[e];
-            Hv[e] *= ar[e];
-          }
-          *reinterpret_cast<uint2*>(&sm.kh[row * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
-          if (r8 & 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kp_next[e] = kp[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp[e], kp_next[e]);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
-          kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
-        }
-      }
-      // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F and the state
-      // operands -K * exp(G) = -K * F * exp(X_b) and scale * Q * exp(G)
-      {
         float F[4], nXb[4], sXb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -526,7 +528,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 #pragma unroll
         for (int r8 = 0; r8 < 8; ++r8) {
           const int row = rg * 8 + r8;
-          float qf[4], kf[4], kr[4], qr[4], kg[4], qg[4];
+          float qf[4], kf[4], kr[4], qr[4], kg[4], qg[4], kp[4];
           unpack4(R.q[r8], qf);
           unpack4(R.k[r8], kf);
           const float4 av = R.g[r8];
@@ -538,12 +540,26 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
             qr[e] = qf[e] * F[e];
             kg[e] = kr[e] * nXb[e];   // -K exp(G)
             qg[e] = qr[e] * sXb[e];   // scale * Q exp(G)
+            kp[e] = kf[e] * Hc[r8][e];
+          }
+          if (r8 & 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              kpw[e][r8 >> 1] = pack2(__uint_as_float(kpw[e][r8 >> 1]), kp[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = __float_as_uint(kp[e]);
           }
           const int o = row * TS + 4 * cg;
           *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
           *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
           *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
           *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
+          kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
         }
       }
       load_g<NV>(R, nsrc, HD, t);  // the decays of this chunk are consumed
@@ -577,7 +593,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o]) = kpt_hold[e][0];
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
-      if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
+      if (spr < 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
       build_tiles(sm, 4 + pw, q4, m16, p.scale);
     }
     __syncthreads();  // (C) chunk pc fully published
