@@ -199,18 +199,17 @@ __device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, in
   }
 }
 
-// Phase C tile work of wave `wave` (0..7, wave-uniform).  Waves 0 and 1 (state
-// waves) take two pairs each: (0,0) + (1,0) and (1,1) + (2,1); the others one
-// each: (2,0), (2,2), (3,0), (3,1), (3,3), (3,2).  Writes -A off the diagonal, A's
-// diagonal blocks (fp32, for the inverse), and scale * M.
+// Phase C tile work of state wave `wave` (0..3, wave-uniform): pairs (0,0) (1,0)
+// (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3) -- the seven pairs that
+// scale their column operand spread two per wave.  Writes -A off the diagonal,
+// A's diagonal blocks (fp32, for the inverse), and scale * M.
 template <int NV>
 __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16, float scale) {
-  const int npairs = wave < 2 ? 2 : 1;
+  const int npairs = wave < 2 ? 3 : 2;
+  const int plist = wave == 0 ? 0x810 : wave == 1 ? 0x432 : wave == 2 ? 0x65 : 0x97;
 #pragma unroll 1
   for (int x = 0; x < npairs; ++x) {
-    const int pr = x == 1 ? (wave == 0 ? 1 : 4)
-                          : (wave < 2 ? 2 * wave : wave < 4 ? 2 * wave - 1 : wave < 6 ? wave + 2
-                                                            : wave == 6 ? 9 : 8);
+    const int pr = (plist >> (4 * x)) & 15;
     const int rb = pair_rb(pr), ib = pair_ib(pr);
     f32x4 ta, tm;
     tile_pair(sm, pr, q4, m16, ta, tm);
@@ -563,6 +562,16 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         }
       }
       load_g<NV>(R, nsrc, HD, t);  // the decays of this chunk are consumed
+    }
+    __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
+
+    // ---- phase C: state-update operand, exp(G_last) and V^T of chunk pc (the state
+    // waves build its A and M tiles meanwhile)
+    {
+      // q, k and v of chunk pc are consumed (V^T below): fetch those of the next chunk
+      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
       // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
@@ -577,15 +586,6 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(pw2[0], pw2[1]);
         *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(pw2[2], pw2[3]);
       }
-    }
-    __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
-
-    // ---- phase C: state-update operand and A tiles of chunk pc
-    {
-      // q, k and v of chunk pc are consumed: fetch those of the next chunk
-      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
       load_v<NV>(R, nsrc, HD, t);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -594,7 +594,6 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
       if (spr < 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
-      build_tiles(sm, 4 + pw, q4, m16, p.scale);
     }
     __syncthreads();  // (C) chunk pc fully published
   }
@@ -765,7 +764,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     }
     __syncthreads();  // (B)
 
-    // ---- phase C: A and M tiles of the next chunk (shared with the prep waves)
+    // ---- phase C: A and M tiles of the next chunk
     if (it + 1 < w.nchunks) build_tiles(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16, p.scale);
     __syncthreads();  // (C)
   }
