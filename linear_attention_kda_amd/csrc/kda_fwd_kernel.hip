@@ -159,15 +159,17 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ int pair_rb(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
 __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_rb(p) + 1)) / 2; }
 
-// The A and M tiles of block pair pr = (rb, ib): lane (q4, m16) gets
+// The A and M tiles of block pair PR = (rb, ib): lane (q4, m16) gets
 // tile[r = 16rb + m16][i = 16ib + 4q4 + t] of sum_c row[r][c] col[i][c] with rows
 // Kr (A) and Qr (M) and the column operand Kh scaled per channel by
-// exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1, where the factor is 1).
-template <int NV>
-__device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, int m16,
-                                          f32x4& ta, f32x4& tm) {
-  const int rb = pair_rb(pr), ib = pair_ib(pr);
-  const bool scaled = ib != rb - 1;
+// exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1, where the factor is 1).  Writes
+// -A off the diagonal, A's diagonal block (fp32, beta-scaled, for the inverse),
+// and scale * M, each masked to its triangle.
+template <int NV, int PR>
+__device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float scale) {
+  constexpr int rb = PR < 1 ? 0 : PR < 3 ? 1 : PR < 6 ? 2 : 3;
+  constexpr int ib = PR - rb * (rb + 1) / 2;
+  constexpr bool scaled = ib != rb - 1;
   bf16x8 cf[4], kf[4], qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -179,57 +181,72 @@ __device__ __forceinline__ void tile_pair(const Smem<NV>& sm, int pr, int q4, in
     kf[ks] = ld2x4(kp, kp + 4);
     qf[ks] = ld2x4(qp, qp + 4);
   }
-  if (scaled) {
+  if constexpr (scaled) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 32 * ks + 8 * q4;
-      const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0]);
-      const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[pr * D + c0 + 4]);
+      const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[PR * D + c0]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[PR * D + c0 + 4]);
       const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) cf[ks][e] = (__bf16)(bf2f(cf[ks][e]) * fs[e]);
     }
   }
-  ta = f32x4{0.f, 0.f, 0.f, 0.f};
-  tm = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 tm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     ta = mfma32(cf[ks], kf[ks], ta);  // D[i][r]
     tm = mfma32(cf[ks], qf[ks], tm);
   }
+  const int r = 16 * rb + m16;
+  const float br = sm.pbeta[r];
+  float va[4], vm[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int i = 16 * ib + 4 * q4 + tt;
+    va[tt] = (i < r) ? br * ta[tt] : 0.f;
+    vm[tt] = (i <= r) ? scale * tm[tt] : 0.f;
+  }
+  if constexpr (ib == rb) {
+    *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
+        make_float4(va[0], va[1], va[2], va[3]);
+  } else {
+    *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
+        pack4(-va[0], -va[1], -va[2], -va[3]);
+  }
+  *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(vm[0], vm[1], vm[2], vm[3]);
 }
 
 // Phase C tile work of state wave `wave` (0..3, wave-uniform): pairs (0,0) (1,0)
 // (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3) -- the seven pairs that
-// scale their column operand spread two per wave.  Writes -A off the diagonal,
-// A's diagonal blocks (fp32, for the inverse), and scale * M.
+// scale their column operand spread two per wave.  The pairs of a wave are
+// independent straight-line code, so their loads and products overlap.
 template <int NV>
-__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4, int m16, float scale) {
-  const int npairs = wave < 2 ? 3 : 2;
-  const int plist = wave == 0 ? 0x810 : wave == 1 ? 0x432 : wave == 2 ? 0x65 : 0x97;
-#pragma unroll 1
-  for (int x = 0; x < npairs; ++x) {
-    const int pr = (plist >> (4 * x)) & 15;
-    const int rb = pair_rb(pr), ib = pair_ib(pr);
-    f32x4 ta, tm;
-    tile_pair(sm, pr, q4, m16, ta, tm);
-    const int r = 16 * rb + m16;
-    const float br = sm.pbeta[r];
-    float va[4], vm[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int i = 16 * ib + 4 * q4 + tt;
-      va[tt] = (i < r) ? br * ta[tt] : 0.f;
-      vm[tt] = (i <= r) ? scale * tm[tt] : 0.f;
-    }
-    if (ib == rb) {
-      *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
-          make_float4(va[0], va[1], va[2], va[3]);
-    } else {
-      *reinterpret_cast<uint2*>(&sm.an[r * QS + 16 * ib + 4 * q4]) =
-          pack4(-va[0], -va[1], -va[2], -va[3]);
-    }
-    *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(vm[0], vm[1], vm[2], vm[3]);
+__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int m16_, float scale) {
+  // lane indices through an empty asm: the tile addresses are then formed here on
+  // every call instead of being kept live (or spilled) across the whole loop
+  int q4 = q4_, m16 = m16_;
+  asm volatile("" : "+v"(q4), "+v"(m16));
+  switch (wave) {
+    case 0:
+      tile_pair<NV, 0>(sm, q4, m16, scale);
+      tile_pair<NV, 1>(sm, q4, m16, scale);
+      tile_pair<NV, 8>(sm, q4, m16, scale);
+      break;
+    case 1:
+      tile_pair<NV, 2>(sm, q4, m16, scale);
+      tile_pair<NV, 3>(sm, q4, m16, scale);
+      tile_pair<NV, 4>(sm, q4, m16, scale);
+      break;
+    case 2:
+      tile_pair<NV, 5>(sm, q4, m16, scale);
+      tile_pair<NV, 6>(sm, q4, m16, scale);
+      break;
+    default:
+      tile_pair<NV, 7>(sm, q4, m16, scale);
+      tile_pair<NV, 9>(sm, q4, m16, scale);
+      break;
   }
 }
 
