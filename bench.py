@@ -212,7 +212,7 @@ def main():
     log(f"[bench] {w.name}: {r['ms_per_step']:.3f} ms/step, kernel {r['kernel_ms']:.3f} ms, "
         f"{r['tokens_per_s'] / 1e6:.2f} M tokens/s, {r['achieved_gbs']:.0f} GB/s "
         f"({100 * r['hbm_frac']:.1f}% of HBM peak)")
-    wg, ns = binding.plan(r["N"], r["H"])
+    wg, ns, wsb = binding.plan(r["N"], w.T, r["H"], varlen=bool(w.n_seqs))
     traffic = measured_traffic(args.workload)
 
     secondary = None
@@ -252,7 +252,8 @@ def main():
         "config": {"workload": w.name, "tokens": r["tokens"], "sequences": r["N"],
                    "lengths": r["lengths"], "heads": r["H"], "head_dim": 128, "chunk": 64,
                    "state_dtype": w.final_state, "global_batch": w.B, "seq_len": w.T,
-                   "parallelism": "single GPU", "workgroups": wg, "value_splits": ns},
+                   "parallelism": "single GPU", "workgroups": wg, "value_splits": ns,
+                   "workspace_bytes": wsb},
         "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"],
                      "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s", "frac": r["hbm_frac"],
                      "traffic": traffic, "kernel": KERNEL_NAME,

@@ -21,12 +21,28 @@
  * B = 1; the initial and final states are each bf16, fp32 or absent, and
  * must have the same dtype when both are given.
  *
+ * Sequence splitting: when there are fewer (sequence, head) recurrences than
+ * the device has compute units to keep busy, kda_fwd cuts long sequences into
+ * segments that run in parallel.  The recurrence is affine in the state, so a
+ * segment's end state is A S_start + B with A the product of its transition
+ * matrices [core.today ch.4 혁신 2, state-update equation]: each later segment
+ * runs once from a zero state (B, and outputs without the start state's share)
+ * and once from the identity with zero values (A, and the map from the start
+ * state to the outputs); a scan over the segments gives every start state and
+ * a fix-up pass adds its share to the outputs.  kda_plan reports whether a
+ * call may split.  KDA_SEQSPLIT=0 in the environment turns splitting off;
+ * KDA_SEG_MIN=<chunks> sets the shortest sequence that may be split (default 8).
+ *
  * Ownership: every pointer is caller-owned memory; the library never retains
- * or frees it and allocates no device memory of its own.
+ * or frees it.  A call that may split sequences takes a workspace (size from
+ * kda_plan) from a stream-ordered memory pool the library owns, one per
+ * device, and returns it to the pool in stream order at the end of the call;
+ * the pool keeps its memory for later calls until the process ends.
  * Asynchrony: kda_fwd enqueues work on `stream` (a hipStream_t, or NULL for
  * the null stream) and returns; results are valid after the caller
- * synchronises that stream.  Calls are thread-safe (no global mutable state
- * except the thread-local error text).
+ * synchronises that stream.  Calls are thread-safe (the pool is created under
+ * a lock; otherwise no global mutable state except the thread-local error
+ * text).
  * Errors: invalid arguments are rejected before any launch with a negative
  * status and no output touched; kda_last_error() then holds a description.
  * There is no fallback path.
@@ -118,15 +134,22 @@ const char* kda_last_error(void);
 
 /*
  * kda_plan — the launch plan kda_fwd uses for N independent sequences
- * (num_seqs, or B without cu_seqlens) and H heads on a device with cu_count
- * compute units (cu_count <= 0: query the current HIP device): the number of
- * workgroups launched and the number of value-column slices per (sequence,
- * head).  The environment variable KDA_VSPLIT (1 or 2) overrides the slice
- * count.  Host only; returns KDA_ERR_SHAPE for N <= 0 or H <= 0, KDA_ERR_NULL
- * for NULL outputs, KDA_ERR_HIP if the device query fails.
+ * (num_seqs, or B without cu_seqlens), T tokens (per row; the packed total
+ * when varlen != 0) and H heads on a device with cu_count compute units
+ * (cu_count <= 0: query the current HIP device):
+ *   workgroups       workgroups of the main kernel (some exit at once when
+ *                    fewer sequences are split than the bound allows);
+ *   value_splits     value-column slices per (sequence, head), 1 or 2;
+ *   workspace_bytes  device workspace a call takes from the library's pool;
+ *                    0 when no sequence can be split (the call then launches
+ *                    the main kernel only).
+ * The environment variable KDA_VSPLIT (1 or 2) overrides the slice count
+ * (2 also turns sequence splitting off).  Host only; returns KDA_ERR_SHAPE for
+ * N <= 0, H <= 0 or T < 0, KDA_ERR_NULL for NULL outputs, KDA_ERR_HIP if the
+ * device query fails.
  */
-kda_status kda_plan(int32_t n_sequences, int32_t H, int32_t cu_count, int32_t* workgroups,
-                    int32_t* value_splits);
+kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, int32_t cu_count,
+                    int32_t* workgroups, int32_t* value_splits, int64_t* workspace_bytes);
 
 #ifdef __cplusplus
 }

@@ -59,7 +59,8 @@ def load_library():
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
         lib.kda_plan.restype = ctypes.c_int
-        lib.kda_plan.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                 ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
         _lib = lib
         return lib
 
@@ -80,14 +81,18 @@ def _state_dtype(t) -> int:
     raise TypeError(f"states must be bfloat16 or float32, got {t.dtype}")
 
 
-def plan(n_sequences: int, heads: int, cu_count: int = 0) -> tuple[int, int]:
-    """(workgroups, value_splits) that kda_fwd launches for these sizes."""
+def plan(n_sequences: int, T: int, heads: int, varlen: bool = False,
+         cu_count: int = 0) -> tuple[int, int, int]:
+    """(workgroups, value_splits, workspace_bytes) of kda_fwd for these sizes.
+
+    T is tokens per batch row, or the packed total when varlen."""
     lib = load_library()
-    wg, ns = _i32(0), _i32(0)
-    st = lib.kda_plan(n_sequences, heads, cu_count, ctypes.byref(wg), ctypes.byref(ns))
+    wg, ns, ws = _i32(0), _i32(0), _i64(0)
+    st = lib.kda_plan(n_sequences, T, heads, int(bool(varlen)), cu_count, ctypes.byref(wg),
+                      ctypes.byref(ns), ctypes.byref(ws))
     if st != 0:
         raise KdaError(st, "kda_plan", _detail(lib, st))
-    return wg.value, ns.value
+    return wg.value, ns.value, ws.value
 
 
 def fwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, initial_state=0,

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/kda.h"
@@ -89,11 +90,108 @@ int device_cu_count(int* cus) {
   return 0;
 }
 
-int choose_splits(int32_t N, int32_t H, int32_t cus) {
+int forced_splits() {
   const char* e = std::getenv("KDA_VSPLIT");
   if (e != nullptr && (e[0] == '1' || e[0] == '2') && e[1] == '\0') return e[0] - '0';
+  return 0;
+}
+
+int seg_min_chunks() {
+  const char* e = std::getenv("KDA_SEG_MIN");
+  if (e != nullptr && e[0] != '\0') {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= (1L << 30)) return (int)v;
+  }
+  return kda::kSegMinDefault;
+}
+
+bool seq_split_enabled() {
+  const char* e = std::getenv("KDA_SEQSPLIT");
+  return !(e != nullptr && e[0] == '0' && e[1] == '\0');
+}
+
+// The device's segment plan for N equal sequences of c chunks (fixed-length
+// batches): does it split them?  Same rule as the kernels' plan.
+bool fixed_length_splits(int64_t N, int64_t c, int64_t H, int64_t cus, int seg_min, int emax) {
+  if (c <= seg_min) return false;
+  auto fits = [&](int64_t m) { return H * (N * c + N * (c > m ? c - m : 0)) <= m * cus; };
+  if (!fits(c)) return false;
+  int64_t lo = seg_min, hi = c;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (fits(mid)) hi = mid;
+    else lo = mid + 1;
+  }
+  return hi < c && N * ((c + hi - 1) / hi - 1) <= emax;
+}
+
+struct LaunchPlan {
+  int nsplit;     // value-column slices per (sequence, head)
+  int emax;       // segment state slots (0: no sequence splitting)
+  int seg_min;
+  int64_t workgroups;
+  size_t workspace;
+};
+
+// rows: packed rows (T with cu_seqlens, else B*T); T: tokens per row, or the
+// packed total with cu_seqlens.
+LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus) {
+  LaunchPlan lp{};
+  lp.seg_min = seg_min_chunks();
+  const int forced = forced_splits();
+  const int64_t c_max = (T + KDA_CHUNK - 1) / KDA_CHUNK;  // chunks of the longest possible sequence
+  int emax = 0;
+  // the device plan counts chunks and fix-up units in 32-bit integers
+  const int64_t chunks = (varlen ? c_max + N : (int64_t)N * c_max);
+  const bool small_enough = chunks < (1LL << 30) && chunks * H < (1LL << 30);
+  if (seq_split_enabled() && forced != 2 && N <= kda::kSortLimit && c_max > lp.seg_min &&
+      small_enough) {
+    emax = kda::workspace_slots(cus, H);
+    if (emax > 512) emax = 512;
+    if (emax > 0 && !varlen && !fixed_length_splits(N, c_max, H, cus, lp.seg_min, emax)) emax = 0;
+  }
+  lp.emax = emax;
   // one workgroup per (sequence, head) already covers the CUs: no value split
-  return ((int64_t)N * H >= cus) ? 1 : 2;
+  lp.nsplit = forced ? forced : (emax > 0 || (int64_t)N * H >= cus) ? 1 : 2;
+  if (emax > 0 && lp.nsplit != 1) lp.emax = emax = 0;
+  const int64_t groups = (int64_t)N + (emax > 0 ? 2 * (int64_t)emax : 0);
+  lp.workgroups = (groups * H + 7) / 8 * 8 * lp.nsplit;
+  const int64_t rows = varlen ? T : (int64_t)N * T;
+  lp.workspace = emax > 0 ? kda::workspace_layout(rows, H, emax).total : 0;
+  return lp;
+}
+
+// Library-owned stream-ordered pool for the splitting workspace, one per device.
+// It keeps what it has reserved (release threshold at maximum), so after the
+// first call of a given size a workspace costs no allocation from the driver.
+hipError_t workspace_pool(hipMemPool_t* out) {
+  static std::mutex mu;
+  static hipMemPool_t pools[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (pools[dev] == nullptr) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof props);
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    err = hipMemPoolCreate(&pool, &props);
+    if (err != hipSuccess) return err;
+    uint64_t keep = UINT64_MAX;
+    err = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (err != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return err;
+    }
+    pools[dev] = pool;
+  }
+  *out = pools[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -128,19 +226,20 @@ kda_status kda_fwd_check(const void* q, const void* k, const void* v, const floa
                   cu_seqlens, num_seqs, B, T, H, K, V, out, nullptr);
 }
 
-kda_status kda_plan(int32_t n_sequences, int32_t H, int32_t cu_count, int32_t* workgroups,
-                    int32_t* value_splits) {
+kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, int32_t cu_count,
+                    int32_t* workgroups, int32_t* value_splits, int64_t* workspace_bytes) {
   g_last_error.clear();
-  if (!workgroups || !value_splits) return fail(KDA_ERR_NULL, "kda_plan outputs are NULL");
-  if (n_sequences <= 0 || H <= 0)
-    return fail(KDA_ERR_SHAPE, "kda_plan: N=%d H=%d", n_sequences, H);
+  if (!workgroups || !value_splits || !workspace_bytes)
+    return fail(KDA_ERR_NULL, "kda_plan outputs are NULL");
+  if (n_sequences <= 0 || H <= 0 || T < 0)
+    return fail(KDA_ERR_SHAPE, "kda_plan: N=%d T=%lld H=%d", n_sequences, (long long)T, H);
   int cus = cu_count;
   if (cus <= 0 && device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const int ns = choose_splits(n_sequences, H, cus);
-  const int64_t pairs = (int64_t)n_sequences * H;
-  *value_splits = ns;
-  *workgroups = (int32_t)(((pairs + 7) / 8) * 8 * ns);
+  const LaunchPlan lp = make_plan(n_sequences, T, H, varlen != 0, cus);
+  *value_splits = lp.nsplit;
+  *workgroups = (int32_t)lp.workgroups;
+  *workspace_bytes = (int64_t)lp.workspace;
   return KDA_OK;
 }
 
@@ -158,7 +257,8 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const int ns = choose_splits(N, H, cus);
+  const LaunchPlan lp = make_plan(N, T, H, cu_seqlens != nullptr, cus);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
 
   kda::Params p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -176,10 +276,33 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
   p.scale = scale;
   p.nseq = N;
   p.H = H;
+  p.cus = cus;
+  p.seg_min = lp.seg_min;
+  void* ws = nullptr;
+  if (lp.emax > 0) {
+    hipMemPool_t pool = nullptr;
+    hipError_t e = workspace_pool(&pool);
+    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, lp.workspace, pool, hs);
+    if (e != hipSuccess)
+      return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", lp.workspace, hipGetErrorString(e));
+    const kda::WorkspaceLayout wl =
+        kda::workspace_layout(cu_seqlens ? T : (int64_t)B * T, H, lp.emax);
+    p.emax = lp.emax;
+    p.o0 = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o0);
+    p.st = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.st);
+    p.sb = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.sb);
+  }
   if (log_enabled())
-    std::fprintf(stderr, "[kda] launch: N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d\n", N,
-                 H, (long long)T, ns, cus, cu_seqlens != nullptr);
-  const hipError_t err = kda::launch_fwd(p, ns, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr,
+                 "[kda] launch: N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
+                 "segment_slots=%d workspace=%zu\n",
+                 N, H, (long long)T, lp.nsplit, cus, cu_seqlens != nullptr, lp.emax, lp.workspace);
+  const hipError_t err = kda::launch_fwd(p, lp.nsplit, hs);
+  if (ws != nullptr) {
+    const hipError_t e = hipFreeAsync(ws, hs);
+    if (err == hipSuccess && e != hipSuccess)
+      return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+  }
   if (err != hipSuccess)
     return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return KDA_OK;

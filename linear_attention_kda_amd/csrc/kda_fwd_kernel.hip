@@ -250,12 +250,21 @@ __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int
   }
 }
 
+// One workgroup's task: a run of consecutive chunks of one (sequence, head,
+// value slice) -- a whole sequence, or one segment of a split sequence.
 struct Work {
-  int64_t bos;   // first token of the sequence
-  int64_t len;   // tokens in the sequence
-  int h;         // head
-  int j0;        // first value column of this workgroup's slice
+  int64_t bos;     // first token of the run
+  int64_t len;     // tokens in the run
+  int h;           // head
+  int j0;          // first value column of this workgroup's slice
   int nchunks;
+  int s0_mode;     // start state: 0 zero, 1 bf16 at s0, 2 fp32 at s0, 3 identity
+  int s1_fp32;     // end state stored as fp32 (else bf16)
+  int o_f32;       // outputs stored as fp32 (else bf16)
+  int vzero;       // values read as zero
+  const void* s0;  // this (sequence, head)'s 128 x 128 start state
+  void* s1;        // where its end state goes, or null
+  void* o;         // output rows, [rows][H][128] (bf16 or fp32)
 };
 
 // Buffer descriptor over `bytes` bytes from `base`; loads beyond the range return
@@ -294,7 +303,7 @@ __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, in
   s.g = rsrc(p.g + base, valid * HD * 4);
   s.q = rsrc(p.q + base, valid * HD * 2);
   s.k = rsrc(p.k + base, valid * HD * 2);
-  s.v = rsrc(p.v + base + w.j0, valid * HD * 2);
+  s.v = rsrc(p.v + base + w.j0, w.vzero ? 0 : valid * HD * 2);
   s.b = rsrc(p.beta + tok0 * p.H + w.h, valid * p.H * 4);
   return s;
 }
@@ -623,14 +632,12 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 
 // ============================================================================ state waves
 template <int JT>
-__device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, const Work& w,
-                                           int64_t n) {
+__device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, const Work& w) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;  // 0..3
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
   const int jw_base = w.j0 + 16 * JT * wave;   // first global value column of this wave
   const int jl_base = 16 * JT * wave;          // first column within the slice
-  const size_t sbase = ((size_t)n * p.H + w.h) * (size_t)(D * D);
 
   // Sacc[ct][jt][t] = S[16ct + 4q4 + t][jw_base + 16jt + m16]
   f32x4 Sacc[8][JT];
@@ -638,28 +645,33 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) Sacc[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p.s0 != nullptr) {
-    if (p.s0_fp32) {
-      const float* s0 = reinterpret_cast<const float*>(p.s0) + sbase;
+  if (w.s0_mode == 3) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
+      for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            Sacc[ct][jt][t] = s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16];
-    } else {
-      const __bf16* s0 = reinterpret_cast<const __bf16*>(p.s0) + sbase;
+        for (int t = 0; t < 4; ++t)
+          Sacc[ct][jt][t] = (16 * ct + 4 * q4 + t == jw_base + 16 * jt + m16) ? 1.f : 0.f;
+  } else if (w.s0_mode == 2) {
+    const float* s0 = reinterpret_cast<const float*>(w.s0);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
+      for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16]);
-    }
+        for (int t = 0; t < 4; ++t)
+          Sacc[ct][jt][t] = s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16];
+  } else if (w.s0_mode == 1) {
+    const __bf16* s0 = reinterpret_cast<const __bf16*>(w.s0);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16]);
   }
-
 
   const int HD = p.H * D;
   for (int it = -1; it < w.nchunks; ++it) {
@@ -741,8 +753,10 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
         }
       }
       // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor)
-      const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
-      const int ovo = m16 * HD * 2 + (jw_base + 4 * q4) * 2;  // lane part of the store offset
+      const int osz = w.o_f32 ? 4 : 2;
+      const auto orsrc = rsrc(static_cast<char*>(w.o) + (tok0 * HD + (int64_t)w.h * D) * osz,
+                              valid * HD * osz);
+      const int ovo = (m16 * HD + jw_base + 4 * q4) * osz;  // lane part of the store offset
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + m16;
@@ -754,10 +768,17 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
             o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
           }
-          const uint2 ov = pack4(o[0], o[1], o[2], o[3]);  // the scale is in Q exp(G) and M
-          __builtin_amdgcn_raw_buffer_store_b64(
-              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-              ovo + 32 * jt, 16 * rt * HD * 2, 0);
+          // the scale is in Q exp(G) and M
+          if (w.o_f32) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, o), orsrc,
+                ovo + 64 * jt, 16 * rt * HD * 4, 0);
+          } else {
+            const uint2 ov = pack4(o[0], o[1], o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
+                ovo + 32 * jt, 16 * rt * HD * 2, 0);
+          }
         }
       }
       // S <- Diag(exp(G_last)) S + K'^T U
@@ -786,9 +807,9 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     __syncthreads();  // (C)
   }
 
-  if (p.s1 != nullptr) {
-    if (p.s1_fp32) {
-      float* s1 = reinterpret_cast<float*>(p.s1) + sbase;
+  if (w.s1 != nullptr) {
+    if (w.s1_fp32) {
+      float* s1 = reinterpret_cast<float*>(w.s1);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -797,7 +818,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           for (int t = 0; t < 4; ++t)
             s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = Sacc[ct][jt][t];
     } else {
-      __bf16* s1 = reinterpret_cast<__bf16*>(p.s1) + sbase;
+      __bf16* s1 = reinterpret_cast<__bf16*>(w.s1);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -809,53 +830,320 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
   }
 }
 
+// ============================================================================ segment plan
+// The recurrence is affine in the state: over any run of tokens, the end state
+// is S_end = A S_start + B, where A is the product of the run's transition
+// matrices (Diag(a_t) - b_t k_t (k_t * a_t)^T) and B the end state from a zero
+// start [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update equation].  The
+// same holds for every output: o_t = scale (A_t S_start + B_t)^T q_t.  A
+// sequence of c > M chunks is therefore cut into segments of M chunks (the last
+// one shorter).  Segment 0 runs from the true initial state.  Every later
+// segment p runs twice, in parallel with everything else: from a zero start with
+// its values (outputs O0_t into a workspace, end state B_p) and from the
+// identity with zero values (outputs Q~_t = scale A_t^T q_t into the output
+// rows, end state A_p).  A scan S_{p+1} = A_p S_p + B_p then gives every start
+// state, and the fix-up o_t = O0_t + S_p^T Q~_t completes the outputs.
+//
+// M is the shortest segment for which the whole job -- every chunk once, plus
+// once more for each chunk past a sequence's first segment -- spread over the
+// compute units takes at most M chunk-steps; the longest task then no longer
+// bounds the run.  Every workgroup of the three kernels computes the same plan
+// from the sequence lengths (integer arithmetic only).
+
+constexpr int kNoSplit = 0x7fffffff;
+
+// Wave-wide integer scans and reductions on DPP row shifts and row broadcasts
+// (lanes shifted in from outside a row read zero).
+template <int ctrl, int rmask = 0xf>
+__device__ __forceinline__ int dpp_in(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, ctrl, rmask, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: within rows of 16 by doubling
+// shifts, then row 0's total into rows 1 and 3, lane 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_in<0x111>(x);        // row_shr:1
+  x += dpp_in<0x112>(x);        // row_shr:2
+  x += dpp_in<0x114>(x);        // row_shr:4
+  x += dpp_in<0x118>(x);        // row_shr:8
+  x += dpp_in<0x142, 0xa>(x);   // row_bcast:15
+  x += dpp_in<0x143, 0xc>(x);   // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// Maximum of non-negative values over the 64 lanes.
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, dpp_in<0x111>(x));
+  x = max(x, dpp_in<0x112>(x));
+  x = max(x, dpp_in<0x114>(x));
+  x = max(x, dpp_in<0x118>(x));
+  x = max(x, dpp_in<0x142, 0xa>(x));
+  x = max(x, dpp_in<0x143, 0xc>(x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int64_t seq_bos(const Params& p, int i) {
+  return p.cu ? (int64_t)p.cu[i] : (int64_t)i * p.T;
+}
+
+__device__ __forceinline__ int64_t seq_len(const Params& p, int i) {
+  return p.cu ? (int64_t)p.cu[i + 1] - p.cu[i] : p.T;
+}
+
+// The plan in LDS (ints).
+struct PlanView {
+  int* hdr;   // [0] M (kNoSplit: nothing split) [1] task groups [2] state slots
+              // [3] split sequences [4] fix-up units
+  int* lens;  // [N]   chunks of each sequence
+  int* goff;  // [N+1] first task group of each sequence
+  int* soff;  // [N+1] first state slot (slot of segment p >= 1: soff + p - 1)
+  int* xoff;  // [N+1] split sequences before it
+  int* uoff;  // [N+1] first fix-up unit
+  int* glen;  // [N + 2 emax] chunks of each task group
+  int* gseq;  //              its sequence
+  int* gk;    //              its kind: 0 segment 0; 2p-1 zero start, 2p identity start of segment p
+};
+
+__host__ __device__ constexpr int plan_ints(int N, int emax, bool groups) {
+  return 8 + N + 4 * (N + 1) + (groups ? 3 * (N + 2 * emax) : 0);
+}
+
+__device__ __forceinline__ PlanView plan_view(int* base, int N, int emax) {
+  PlanView v;
+  v.hdr = base;
+  v.lens = base + 8;
+  v.goff = v.lens + N;
+  v.soff = v.goff + N + 1;
+  v.xoff = v.soff + N + 1;
+  v.uoff = v.xoff + N + 1;
+  v.glen = v.uoff + N + 1;
+  v.gseq = v.glen + N + 2 * emax;
+  v.gk = v.gseq + N + 2 * emax;
+  return v;
+}
+
+struct SeqCounts {
+  int groups, slots, split, units;
+};
+
+// Task groups, state slots, split flag and fix-up units (one per chunk and
+// head past segment 0) of a sequence of c chunks.
+__device__ __forceinline__ SeqCounts seq_counts(int c, int M, int H) {
+  SeqCounts r{1, 0, 0, 0};
+  if (M != kNoSplit && c > M) {
+    const int P = (c + M - 1) / M;
+    r.groups = 2 * P - 1;
+    r.slots = P - 1;
+    r.split = 1;
+    r.units = H * (c - M);
+  }
+  return r;
+}
+
+// Builds the plan; every thread of the workgroup calls it (it holds barriers).
+__device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
+  const int N = p.nseq, tid = threadIdx.x, nt = blockDim.x;
+  for (int i = tid; i < N; i += nt) v.lens[i] = (int)((seq_len(p, i) + C - 1) / C);
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int mx = 0, sum = 0;
+    for (int i = lane; i < N; i += 64) {
+      mx = max(mx, v.lens[i]);
+      sum += v.lens[i];
+    }
+    mx = wave_max(mx);
+    sum = wave_sum(sum);
+    auto fits = [&](int m) {
+      int extra = 0;
+      for (int i = lane; i < N; i += 64) extra += max(0, v.lens[i] - m);
+      extra = wave_sum(extra);
+      return (long long)p.H * ((long long)sum + extra) <= (long long)m * p.cus;
+    };
+    int M = kNoSplit;
+    if (p.emax > 0 && mx > p.seg_min && fits(mx)) {
+      int lo = p.seg_min, hi = mx;  // fits(hi)
+      while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        if (fits(mid)) hi = mid;
+        else lo = mid + 1;
+      }
+      if (hi < mx) M = hi;
+    }
+    if (M != kNoSplit) {  // the workspace holds emax segment states per head
+      int slots = 0;
+      for (int i = lane; i < N; i += 64) slots += seq_counts(v.lens[i], M, p.H).slots;
+      if (wave_sum(slots) > p.emax) M = kNoSplit;
+    }
+    // exclusive prefix sums over contiguous runs of sequences, one run per lane
+    const int per = (N + 63) / 64;
+    const int i0 = min(N, lane * per), i1 = min(N, i0 + per);
+    int sg = 0, ss = 0, sx = 0, su = 0;
+    for (int i = i0; i < i1; ++i) {
+      const SeqCounts r = seq_counts(v.lens[i], M, p.H);
+      sg += r.groups;
+      ss += r.slots;
+      sx += r.split;
+      su += r.units;
+    }
+    int eg = wave_incl_scan(sg) - sg, es = wave_incl_scan(ss) - ss;
+    int ex = wave_incl_scan(sx) - sx, eu = wave_incl_scan(su) - su;
+    for (int i = i0; i < i1; ++i) {
+      const SeqCounts r = seq_counts(v.lens[i], M, p.H);
+      v.goff[i] = eg;
+      v.soff[i] = es;
+      v.xoff[i] = ex;
+      v.uoff[i] = eu;
+      eg += r.groups;
+      es += r.slots;
+      ex += r.split;
+      eu += r.units;
+    }
+    if (lane == 63) {  // its run ends at N: the running sums are the totals
+      v.goff[N] = eg;
+      v.soff[N] = es;
+      v.xoff[N] = ex;
+      v.uoff[N] = eu;
+      v.hdr[0] = M;
+      v.hdr[1] = eg;
+      v.hdr[2] = es;
+      v.hdr[3] = ex;
+      v.hdr[4] = eu;
+    }
+  }
+  __syncthreads();
+  if (groups) {
+    const int M = v.hdr[0];
+    for (int i = tid; i < N; i += nt) {
+      const int c = v.lens[i], g = v.goff[i];
+      const bool split = M != kNoSplit && c > M;
+      v.glen[g] = split ? M : c;
+      v.gseq[g] = i;
+      v.gk[g] = 0;
+      if (split) {
+        const int P = (c + M - 1) / M;
+        for (int sp = 1; sp < P; ++sp) {
+          const int len = min(M, c - sp * M);
+#pragma unroll
+          for (int kind = 0; kind < 2; ++kind) {
+            const int gg = g + 2 * sp - 1 + kind;
+            v.glen[gg] = len;
+            v.gseq[gg] = i;
+            v.gk[gg] = 2 * sp - 1 + kind;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Smallest i in [0, N) with off[i + 1] > x (off non-decreasing, off[N] > x).
+__device__ __forceinline__ int find_seq(const int* off, int N, int x) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid + 1] > x) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// ============================================================================ main kernel
 template <int JT>
 __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   constexpr int NV = 64 * JT;  // value columns per workgroup
   __shared__ Smem<NV> sm;
+  static_assert(plan_ints(kSortLimit, 512, true) * 4 <= 5 * sizeof(sm.kg),
+                "the plan fits in the operand tiles");
   const int tid = threadIdx.x;
 
-  // ---- workgroup -> (sequence rank, head, value slice); slices of one head share an XCD
+  // ---- workgroup -> (task rank, head, value slice); slices of one head share an XCD
   const int nsplit = 128 / NV;
-  const int pairs = p.nseq * p.H;
   const int grp = blockIdx.x / (8 * nsplit);
   const int rem = blockIdx.x % (8 * nsplit);
   const int split = rem / 8;
   const int pidx = grp * 8 + (rem % 8);
-  if (pidx >= pairs) return;
   const int rank = pidx / p.H;
   Work w;
   w.h = pidx % p.H;
   w.j0 = split * NV;
 
-  // ---- longest sequence first: rank -> sequence index (ties by index)
-  int n = rank;
-  if (p.cu != nullptr && p.nseq > 1 && p.nseq <= kSortLimit) {
-    int* lens = reinterpret_cast<int*>(sm.kh);  // scratch before the first chunk
-    for (int i = tid; i < p.nseq; i += NT) lens[i] = p.cu[i + 1] - p.cu[i];
-    __syncthreads();
-    for (int i = tid; i < p.nseq; i += NT) {
-      const int li = lens[i];
+  // ---- task of this rank: longest first (ties by sequence, then segment)
+  int n = rank, kind = 0, M = kNoSplit, slot0 = 0;
+  const bool planned = p.nseq <= kSortLimit && (p.emax > 0 || (p.cu != nullptr && p.nseq > 1));
+  if (planned) {
+    const PlanView v = plan_view(reinterpret_cast<int*>(sm.kg), p.nseq, p.emax);
+    build_plan(p, v, true);
+    const int G = __builtin_amdgcn_readfirstlane(v.hdr[1]);
+    if (rank >= G) return;  // the same for the whole workgroup
+    for (int g = tid; g < G; g += NT) {
+      const int lg = v.glen[g];
       int rk = 0;
-      for (int j = 0; j < p.nseq; ++j) {
-        const int lj = lens[j];
-        rk += (lj > li) || (lj == li && j < i);
+      for (int j = 0; j < G; ++j) {
+        const int lj = v.glen[j];
+        rk += (lj > lg) || (lj == lg && j < g);
       }
-      if (rk == rank) sm.order = i;
+      if (rk == rank) sm.order = g;
     }
     __syncthreads();
-    n = __builtin_amdgcn_readfirstlane(sm.order);  // the same for every wave
+    const int g = __builtin_amdgcn_readfirstlane(sm.order);
+    n = __builtin_amdgcn_readfirstlane(v.gseq[g]);
+    kind = __builtin_amdgcn_readfirstlane(v.gk[g]);
+    M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
+    slot0 = __builtin_amdgcn_readfirstlane(v.soff[n]);
     __syncthreads();  // the scratch is reused by the prep waves
+  } else if (rank >= p.nseq) {
+    return;
   }
+
   // sequence bounds, made wave-uniform so that every buffer descriptor is scalar
+  int64_t bos, len;
   if (p.cu) {
     const int c0 = __builtin_amdgcn_readfirstlane(p.cu[n]);
     const int c1 = __builtin_amdgcn_readfirstlane(p.cu[n + 1]);
-    w.bos = c0;
-    w.len = (int64_t)c1 - c0;
+    bos = c0;
+    len = (int64_t)c1 - c0;
   } else {
-    w.bos = (int64_t)n * p.T;
-    w.len = p.T;
+    bos = (int64_t)n * p.T;
+    len = p.T;
+  }
+  const size_t hd2 = (size_t)w.h * (D * D);
+  const bool seq_split = M != kNoSplit && len > (int64_t)M * C;
+  if (kind == 0) {  // the sequence, or its first segment, from the true initial state
+    w.bos = bos;
+    w.len = seq_split ? (int64_t)M * C : len;
+    w.s0_mode = p.s0 == nullptr ? 0 : p.s0_fp32 ? 2 : 1;
+    w.s0 = p.s0 == nullptr ? nullptr
+         : static_cast<const char*>(p.s0) + ((size_t)n * p.H * (D * D) + hd2) * (p.s0_fp32 ? 4 : 2);
+    if (seq_split) {  // the start state of segment 1
+      w.s1 = p.st + ((size_t)slot0 * p.H) * (D * D) + hd2;
+      w.s1_fp32 = 1;
+    } else {
+      w.s1 = p.s1 == nullptr ? nullptr
+           : static_cast<char*>(p.s1) + ((size_t)n * p.H * (D * D) + hd2) * (p.s1_fp32 ? 4 : 2);
+      w.s1_fp32 = p.s1_fp32;
+    }
+    w.o = p.out;
+    w.o_f32 = 0;
+    w.vzero = 0;
+  } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
+    const int sp = (kind + 1) >> 1;
+    const bool ident = (kind & 1) == 0;
+    const int64_t off = (int64_t)sp * M * C;
+    w.bos = bos + off;
+    w.len = len - off < (int64_t)M * C ? len - off : (int64_t)M * C;
+    w.s0_mode = ident ? 3 : 0;
+    w.s0 = nullptr;
+    w.s1 = p.st + ((size_t)((ident ? 1 : 2) * p.emax + slot0 + sp - 1) * p.H) * (D * D) + hd2;
+    w.s1_fp32 = 1;
+    w.o = ident ? static_cast<void*>(p.out) : static_cast<void*>(p.o0);
+    w.o_f32 = ident ? 0 : 1;
+    w.vzero = ident ? 1 : 0;
   }
   w.nchunks = (int)((w.len + C - 1) / C);
 
@@ -867,23 +1155,227 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   }
 
   // Both roles execute the same barrier sequence; the branch is uniform per wave.
-  if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w, n);
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w);
   else prep_loop<NV>(sm, p, w);
+}
+
+// ============================================================================ segment scan
+// One workgroup per (split sequence, head, 16-column block of the state), in a
+// grid-stride loop: S_1 is segment 0's end state; for p = 1 .. P-1 it stores
+// the bf16 operand copy of S_p for the fix-up and forms S_{p+1} = A_p S_p + B_p
+// in fp32.  S_P is the sequence's final state.  The plan lives in dynamic LDS
+// (plan_ints(N, 0, false) ints).
+constexpr int SCAN_NT = 256;
+constexpr int SLS = 16 + 4;  // row stride (fp32) of the state block
+
+__global__ void __launch_bounds__(SCAN_NT) kda_scan_kernel(Params p) {
+  extern __shared__ int plan_lds[];
+  __shared__ __attribute__((aligned(16))) float sl[D * SLS];
+  const int N = p.nseq, tid = threadIdx.x;
+  const PlanView v = plan_view(plan_lds, N, 0);
+  build_plan(p, v, false);
+  const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
+  if (M == kNoSplit) return;
+  const int units = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
+  const size_t slot_stride = (size_t)p.H * (D * D);
+  const int r = tid >> 1, c8 = (tid & 1) * 8;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int sidx = u / (p.H * 8), h = (u / 8) % p.H, cb = u % 8;
+    const int i = __builtin_amdgcn_readfirstlane(find_seq(v.xoff, N, sidx));
+    const int c = __builtin_amdgcn_readfirstlane(v.lens[i]), P = (c + M - 1) / M;
+    const int slot0 = __builtin_amdgcn_readfirstlane(v.soff[i]);
+    const size_t hd2 = (size_t)h * (D * D);
+    {
+      const float* s1 = p.st + slot0 * slot_stride + hd2 + (size_t)r * D + 16 * cb + c8;
+      const float4 a0 = *reinterpret_cast<const float4*>(s1);
+      const float4 a1 = *reinterpret_cast<const float4*>(s1 + 4);
+      *reinterpret_cast<float4*>(&sl[r * SLS + c8]) = a0;
+      *reinterpret_cast<float4*>(&sl[r * SLS + c8 + 4]) = a1;
+    }
+    __syncthreads();
+    for (int sp = 1; sp < P; ++sp) {
+      const int slot = slot0 + sp - 1;
+      // row r of A_p and the thread's 8 entries of B_p, all loads in flight at once
+      const float* am = p.st + ((size_t)p.emax + slot) * slot_stride + hd2 + (size_t)r * D;
+      const float* bm = p.st + ((size_t)2 * p.emax + slot) * slot_stride + hd2 + (size_t)r * D + 16 * cb + c8;
+      float4 arow[D / 4];
+#pragma unroll
+      for (int kq = 0; kq < D / 4; ++kq) arow[kq] = *reinterpret_cast<const float4*>(am + 4 * kq);
+      const float4 b0 = *reinterpret_cast<const float4*>(bm);
+      const float4 b1 = *reinterpret_cast<const float4*>(bm + 4);
+      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+      {  // fix-up operand: element (k, j) of S_p at [(k/32)][j/16][lane][k%8] with
+         // lane = 16 ((k/8)%4) + j%16 -- the A operand (S^T) of a 16x16x32 product
+        const int ks = tid >> 6, lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = sl[(32 * ks + 8 * q4 + e) * SLS + m16];
+        const uint2 lo = pack4(f[0], f[1], f[2], f[3]), hi = pack4(f[4], f[5], f[6], f[7]);
+        uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * 8 + cb) * 64 + lane) * 8;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      float acc[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int kq = 0; kq < D / 4; ++kq) {
+        const float av[4] = {arow[kq].x, arow[kq].y, arow[kq].z, arow[kq].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 s0 = *reinterpret_cast<const float4*>(&sl[(4 * kq + e) * SLS + c8]);
+          const float4 s1v = *reinterpret_cast<const float4*>(&sl[(4 * kq + e) * SLS + c8 + 4]);
+          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1v.x, s1v.y, s1v.z, s1v.w};
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[x] += av[e] * sv[x];
+        }
+      }
+      __syncthreads();  // every read of S_p is done
+      *reinterpret_cast<float4*>(&sl[r * SLS + c8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(&sl[r * SLS + c8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      __syncthreads();
+    }
+    if (p.s1 != nullptr) {
+      const size_t o = ((size_t)i * p.H) * (D * D) + hd2 + (size_t)r * D + 16 * cb + c8;
+      const float4 a0 = *reinterpret_cast<const float4*>(&sl[r * SLS + c8]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&sl[r * SLS + c8 + 4]);
+      if (p.s1_fp32) {
+        float* d = static_cast<float*>(p.s1) + o;
+        *reinterpret_cast<float4*>(d) = a0;
+        *reinterpret_cast<float4*>(d + 4) = a1;
+      } else {
+        const uint2 lo = pack4(a0.x, a0.y, a0.z, a0.w), hi = pack4(a1.x, a1.y, a1.z, a1.w);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.s1) + o) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    __syncthreads();  // before the next unit overwrites the block
+  }
+}
+
+// ============================================================================ output fix-up
+// One work unit = one chunk of a later segment p of one (sequence, head):
+// o_t = O0_t + S_p^T Q~_t, with Q~ read from (and o written back to) the output
+// rows.  Every load of the unit is issued at its start.  Wave w forms output
+// columns 32w..32w+31 as O^T = S_p^T Q~^T on bf16 MFMA 16x16x32; Q~ is staged
+// through LDS so that each wave reads all 64 tokens.  The plan lives in dynamic
+// LDS (plan_ints(N, 0, false) ints).
+constexpr int FIX_NT = 256;
+
+__global__ void __launch_bounds__(FIX_NT) kda_fix_kernel(Params p) {
+  extern __shared__ int plan_lds[];
+  __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
+  const int N = p.nseq, tid = threadIdx.x;
+  const PlanView v = plan_view(plan_lds, N, 0);
+  build_plan(p, v, false);
+  // wave-uniform unit values keep every buffer descriptor scalar
+  const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
+  if (M == kNoSplit) return;
+  const int units = __builtin_amdgcn_readfirstlane(v.hdr[4]);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int HD = p.H * D;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int i = __builtin_amdgcn_readfirstlane(find_seq(v.uoff, N, u));
+    const int r = u - __builtin_amdgcn_readfirstlane(v.uoff[i]);
+    const int h = r % p.H;
+    const int ch = M + r / p.H;  // chunk of the sequence (past segment 0)
+    const int slot = __builtin_amdgcn_readfirstlane(v.soff[i]) + ch / M - 1;
+    int64_t bos, len;
+    if (p.cu) {
+      const int c0 = __builtin_amdgcn_readfirstlane(p.cu[i]);
+      const int c1 = __builtin_amdgcn_readfirstlane(p.cu[i + 1]);
+      bos = c0;
+      len = (int64_t)c1 - c0;
+    } else {
+      bos = (int64_t)i * p.T;
+      len = p.T;
+    }
+    const int64_t tok0 = bos + (int64_t)ch * C;
+    const int64_t rest = len - (int64_t)ch * C;
+    const int valid = rest < C ? (int)rest : C;
+    const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)h * D, valid * HD * 2);
+    const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 4);
+    // loads: Q~ rows of the chunk (rows past `valid` read as zero), S_p^T, O0
+    decltype(__builtin_amdgcn_raw_buffer_load_b128(orsrc, 0, 0, 0)) qv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
+    const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)slot * p.H + h) * (D * D);
+    bf16x8 sa[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
+    f32x4 z[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        z[tt][jj] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 4, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the unit in flight together
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
+      dst[0] = make_uint2(qv[x][0], qv[x][1]);
+      dst[1] = make_uint2(qv[x][2], qv[x][3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
+        const bf16x8 b = ld2x4(bp, bp + 4);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], b, z[tt][jj]);
+      }
+      // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
+            ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+      }
+    }
+    __syncthreads();  // before the next unit's staging
+  }
 }
 
 }  // namespace
 
+int workspace_slots(int cus, int H) { return (H > 0 && H < cus) ? cus / H + 1 : 0; }
+
+WorkspaceLayout workspace_layout(int64_t rows, int H, int emax) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WorkspaceLayout l;
+  l.o0 = 0;
+  l.st = up((size_t)rows * H * D * 4);
+  l.sb = l.st + up((size_t)3 * emax * H * D * D * 4);
+  l.total = l.sb + up((size_t)emax * H * D * D * 2);
+  return l;
+}
+
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
-  const int pairs = p.nseq * p.H;
-  const int groups = (pairs + 7) / 8;
-  const dim3 grid(groups * 8 * nsplit), block(NT);
-  if (nsplit == 1) {
-    hipLaunchKernelGGL(kda_fwd_kernel<2>, grid, block, 0, stream, p);
-  } else if (nsplit == 2) {
-    hipLaunchKernelGGL(kda_fwd_kernel<1>, grid, block, 0, stream, p);
-  } else {
+  if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
+  if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr))
     return hipErrorInvalidValue;
+  // task groups: every sequence, plus two runs per extra segment (fewer than
+  // 2 * emax of them when splitting)
+  const int64_t groups = (int64_t)p.nseq + (p.emax > 0 && p.nseq <= kSortLimit ? 2 * (int64_t)p.emax : 0);
+  const int64_t wgs = (groups * p.H + 7) / 8 * 8 * nsplit;
+  const dim3 block(NT);
+  if (nsplit == 1) {
+    hipLaunchKernelGGL(kda_fwd_kernel<2>, dim3((unsigned)wgs), block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(kda_fwd_kernel<1>, dim3((unsigned)wgs), block, 0, stream, p);
   }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;
+  const size_t plan_bytes = (size_t)plan_ints(p.nseq, 0, false) * sizeof(int);
+  hipLaunchKernelGGL(kda_scan_kernel, dim3(2 * p.cus), dim3(SCAN_NT), plan_bytes, stream, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kda_fix_kernel, dim3(8 * p.cus), dim3(FIX_NT), plan_bytes, stream, p);
   return hipGetLastError();
 }
 

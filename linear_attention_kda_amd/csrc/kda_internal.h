@@ -3,13 +3,18 @@
 #define KDA_INTERNAL_H_
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace kda {
 
-// Sequences longer-first ordering is computed on the device for at most this
-// many packed sequences; beyond it workgroups follow the packing order.
+// Sequences are ordered longest-first, and long ones split into segments, only
+// when there are at most this many packed sequences; beyond it workgroups
+// follow the packing order and every sequence runs whole.
 constexpr int kSortLimit = 1024;
+
+// Shortest sequence (in 64-token chunks) that may be split into segments.
+constexpr int kSegMinDefault = 8;
 
 struct Params {
   const uint16_t* q;      // bf16 [rows][H][128]
@@ -27,9 +32,29 @@ struct Params {
   int s1_fp32;
   int nseq;               // N: sequences (varlen) or batch rows
   int H;
+  // Sequence splitting (all zero / null: every sequence runs whole).
+  int cus;                // parallel width the segment plan fills (compute units)
+  int seg_min;            // shortest sequence, in chunks, that may be split
+  int emax;               // segment state slots in the workspace; 0 disables splitting
+  float* o0;              // fp32 [rows][H][128]: outputs of later segments from a zero state
+  float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
+  uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
 };
 
-// Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence, head).
+// Workspace bytes for splitting with `emax` state slots over `rows` packed
+// rows of H heads, and the offsets of its three parts.
+struct WorkspaceLayout {
+  size_t o0, st, sb, total;
+};
+WorkspaceLayout workspace_layout(int64_t rows, int H, int emax);
+
+// State slots a plan can use on `cus` compute units with H heads: the plan
+// never needs more than cus / H extra segments.
+int workspace_slots(int cus, int H);
+
+// Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
+// head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
+// the segment scan and output fix-up kernels follow the main kernel.
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream);
 
 }  // namespace kda

@@ -87,15 +87,43 @@ def test_state_dtype_ignored_for_absent_state(lib):
     assert binding.fwd_check(**ok_args(initial_dtype=7)) == OK
 
 
-def test_plan_value_split(lib):
-    # fewer (sequence, head) pairs than CUs -> two value slices per pair
-    assert binding.plan(1, 32, 256) == (64, 2)
-    assert binding.plan(16, 32, 256) == (512, 1)
-    assert binding.plan(4, 32, 256) == (256, 2)
-    assert binding.plan(8, 32, 256) == (256, 1)
-    assert binding.plan(3, 3, 256) == (32, 2)   # 9 pairs padded to 16, times 2 slices
+def _split_workspace(rows, H, emax):
+    up = lambda x: (x + 255) // 256 * 256
+    return up(rows * H * 128 * 4) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
+
+
+def test_plan_value_split(lib, monkeypatch):
+    monkeypatch.delenv("KDA_SEQSPLIT", raising=False)
+    monkeypatch.delenv("KDA_SEG_MIN", raising=False)
+    monkeypatch.delenv("KDA_VSPLIT", raising=False)
+    # short sequences (4 chunks <= 8): no splitting; fewer (sequence, head) pairs
+    # than CUs -> two value slices per pair
+    assert binding.plan(1, 256, 32, False, 256) == (64, 2, 0)
+    assert binding.plan(16, 256, 32, False, 256) == (512, 1, 0)
+    assert binding.plan(4, 256, 32, False, 256) == (256, 2, 0)
+    assert binding.plan(3, 256, 3, False, 256) == (32, 2, 0)   # 9 pairs padded to 16, times 2
+    # H >= CUs: never split
+    assert binding.plan(1, 8192, 256, False, 256) == (256, 1, 0)
+    # one 8K sequence, 32 heads: split (segment slots 256/32 + 1 = 9); the grid
+    # covers the sequence plus two runs per possible extra segment
+    assert binding.plan(1, 8192, 32, False, 256) == ((1 + 18) * 32, 1, _split_workspace(8192, 32, 9))
+    # 16 equal sequences of 128 chunks on 256 CUs: 512 pairs already fill the CUs
+    assert binding.plan(16, 8192, 32, False, 256) == (512, 1, 0)
+    # varlen: the lengths live on the device, so the plan allows splitting
+    assert binding.plan(16, 65536, 32, True, 256) == ((16 + 18) * 32, 1, _split_workspace(65536, 32, 9))
     with pytest.raises(binding.KdaError):
-        binding.plan(0, 32, 256)
+        binding.plan(0, 256, 32, False, 256)
+
+
+def test_plan_split_switches(lib, monkeypatch):
+    monkeypatch.setenv("KDA_SEQSPLIT", "0")
+    assert binding.plan(1, 8192, 32, False, 256) == (64, 2, 0)
+    monkeypatch.delenv("KDA_SEQSPLIT")
+    monkeypatch.setenv("KDA_VSPLIT", "2")
+    assert binding.plan(1, 8192, 32, False, 256) == (64, 2, 0)
+    monkeypatch.delenv("KDA_VSPLIT")
+    monkeypatch.setenv("KDA_SEG_MIN", "200")
+    assert binding.plan(1, 8192, 32, False, 256) == (64, 2, 0)   # 128 chunks <= 200
 
 
 def test_binding_rejects_host_tensors(lib):

@@ -187,6 +187,69 @@ def test_rejects_bad_head_dim():
     assert e.value.status == -2
 
 
+# ------------------------------------------------------- split sequences
+# Long sequences on few heads are cut into segments (zero-start and
+# identity-start runs, a scan over the segment maps, an output fix-up).
+# KDA_SEG_MIN lowers the shortest splittable sequence so that small inputs
+# take many segments, ragged last segments and several scan steps.
+
+@pytest.fixture(params=["1", "3"], ids=["segmin1", "segmin3"])
+def segmin(request, monkeypatch):
+    monkeypatch.delenv("KDA_VSPLIT", raising=False)
+    monkeypatch.delenv("KDA_SEQSPLIT", raising=False)
+    monkeypatch.setenv("KDA_SEG_MIN", request.param)
+    return int(request.param)
+
+
+@pytest.mark.parametrize("B,T,H,state", [
+    (1, 300, 2, "fp32"), (1, 256, 1, None), (1, 700, 3, "bf16"), (2, 333, 2, "fp32"),
+    (1, 1000, 4, "fp32"), (1, 2049, 8, "bf16"),
+])
+def test_split_small_shapes(B, T, H, state, segmin):
+    announce(f"split B={B} T={T} H={H} state={state} seg_min={segmin}")
+    assert binding.plan(B, T, H)[2] > 0, "the plan must split these sequences"
+    x = random_inputs(B, T, H, seed=300 + T + H, device=DEV, init_state=state)
+    out, fin = run_gpu(x, final_dtype=torch.bfloat16 if state == "bf16" else torch.float32)
+    check(x, out, fin)
+
+
+def test_split_varlen(segmin):
+    lengths = [1000, 5, 0, 130, 64, 1, 0, 577]
+    announce(f"split varlen lengths={lengths} seg_min={segmin}")
+    x = random_inputs(1, sum(lengths), 2, seed=21, device=DEV, init_state="bf16", lengths=lengths)
+    out, fin = run_gpu(x, final_dtype=torch.bfloat16)
+    check(x, out, fin)
+    for n in (2, 6):
+        assert torch.equal(fin[n], x["initial_state"][n])
+
+
+def test_split_aliased_state_and_no_final(segmin):
+    announce(f"split aliased state / no final state seg_min={segmin}")
+    x = random_inputs(1, 900, 2, seed=22, device=DEV, init_state="fp32")
+    ref_x = dict(x, initial_state=x["initial_state"].clone())
+    state = x["initial_state"]
+    out, fin = run_gpu(x, final_state=state)
+    assert fin.data_ptr() == state.data_ptr()
+    check(ref_x, out, fin)
+    x2 = dict(ref_x, initial_state=ref_x["initial_state"].clone())
+    out2, fin2 = run_gpu(x2)
+    assert fin2 is None
+    check(ref_x, out2, None)
+
+
+def test_split_matches_whole_sequence_run(monkeypatch):
+    announce("split vs whole-sequence run, T=4096 H=4")
+    x = random_inputs(1, 4096, 4, seed=23, device=DEV, init_state="fp32")
+    monkeypatch.setenv("KDA_SEQSPLIT", "0")
+    o1, f1 = run_gpu(x, final_dtype=torch.float32)
+    monkeypatch.delenv("KDA_SEQSPLIT")
+    assert binding.plan(1, 4096, 4)[2] > 0
+    o2, f2 = run_gpu(x, final_dtype=torch.float32)
+    assert rel_err(host(o2), host(o1)) <= 1e-2
+    assert rel_err(host(f2), host(f1)) <= 1e-2
+    check(x, o2, f2)
+
+
 # ------------------------------------------------------------ full-size workloads
 
 def test_workload1_full():
