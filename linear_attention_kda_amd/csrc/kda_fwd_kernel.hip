@@ -47,7 +47,6 @@
 // MFMA operand layouts used below (64 lanes, q = lane/16, m = lane%16):
 //  16x16x32 bf16:  A[m][8q+e], B[8q+e][m] (e < 8),  D[4q+t][m] (t < 4)
 //  16x16x16 bf16:  A[m][4q+e], B[4q+e][m] (e < 4),  D[4q+t][m]
-//  16x16x4 fp32:   A[m][q],    B[q][m],                D[4q+t][m]
 // A contraction may permute its k index as long as both operands agree; the
 // state path uses k-slot e <-> k = 32ks + 4q + e (e < 4), 32ks + 16 + 4q + e-4
 // (e >= 4), which is exactly what two D-layout tiles (rows 32ks..+15 and
@@ -95,7 +94,8 @@ struct alignas(16) Smem {
   float pbeta[C];       // beta of the chunk being prepared
   float seg[8 * D];     // per 8-row group and channel: sum of g*log2(e)
   float pf[10 * D];     // exp(X_rb - X_{ib+1}) per (rb, ib <= rb) pair and channel
-  int order;            // sequence chosen for this workgroup
+  int order;            // task chosen for this workgroup
+  int chunk_ref;        // the chunk being prepared uses the chunk-level exponent reference
 };
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
@@ -127,9 +127,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma4f(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // Two 4-element bf16 runs (8-byte aligned) -> one 16x16x32 operand.
 __device__ __forceinline__ bf16x8 ld2x4(const __bf16* p0, const __bf16* p1) {
@@ -139,9 +136,6 @@ __device__ __forceinline__ bf16x8 ld2x4(const __bf16* p0, const __bf16* p1) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ bf16x8 ld8(const __bf16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
 
 __device__ __forceinline__ bf16x4 ld4(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(p));
@@ -160,23 +154,28 @@ __device__ __forceinline__ int pair_rb(int p) { return p < 1 ? 0 : p < 3 ? 1 : p
 __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_rb(p) + 1)) / 2; }
 
 // The A and M tiles of block pair PR = (rb, ib): lane (q4, m16) gets
-// tile[r = 16rb + m16][i = 16ib + 4q4 + t] of sum_c row[r][c] col[i][c] with rows
-// Kr (A) and Qr (M) and the column operand Kh scaled per channel by
-// exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1, where the factor is 1).  Writes
-// -A off the diagonal, A's diagonal block (fp32, beta-scaled, for the inverse),
-// and scale * M, each masked to its triangle.
-template <int NV, int PR>
+// tile[r = 16rb + m16][i = 16ib + 4q4 + t] of sum_c row[r][c] col[i][c].
+// Writes -A off the diagonal, A's diagonal block (fp32, beta-scaled, for the
+// inverse), and scale * M, each masked to its triangle.
+//  * chunk reference (FAST): rows -K exp(G) (A) and scale Q exp(G) (M), the
+//    tiles the state products use; column K exp(-G).
+//  * block references: rows Kr = K F (A) and Qr = Q F (M), column Kh = K H
+//    scaled per channel by exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1,
+//    where the factor is 1).
+template <int NV, int PR, bool FAST>
 __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float scale) {
   constexpr int rb = PR < 1 ? 0 : PR < 3 ? 1 : PR < 6 ? 2 : 3;
   constexpr int ib = PR - rb * (rb + 1) / 2;
-  constexpr bool scaled = ib != rb - 1;
+  constexpr bool scaled = !FAST && ib != rb - 1;
+  const __bf16* krow = FAST ? sm.kg : sm.kr;
+  const __bf16* qrow = FAST ? sm.qg : sm.qr;
   bf16x8 cf[4], kf[4], qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int c0 = 32 * ks + 8 * q4;
     const __bf16* cp = &sm.kh[(16 * ib + m16) * TS + c0];
-    const __bf16* kp = &sm.kr[(16 * rb + m16) * TS + c0];
-    const __bf16* qp = &sm.qr[(16 * rb + m16) * TS + c0];
+    const __bf16* kp = &krow[(16 * rb + m16) * TS + c0];
+    const __bf16* qp = &qrow[(16 * rb + m16) * TS + c0];
     cf[ks] = ld2x4(cp, cp + 4);
     kf[ks] = ld2x4(kp, kp + 4);
     qf[ks] = ld2x4(qp, qp + 4);
@@ -200,13 +199,14 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float s
     tm = mfma32(cf[ks], qf[ks], tm);
   }
   const int r = 16 * rb + m16;
-  const float br = sm.pbeta[r];
+  const float br = FAST ? -sm.pbeta[r] : sm.pbeta[r];  // the FAST row operand is -K exp(G)
+  const float sm_ = FAST ? 1.f : scale;                // ... and scale * Q exp(G)
   float va[4], vm[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int i = 16 * ib + 4 * q4 + tt;
     va[tt] = (i < r) ? br * ta[tt] : 0.f;
-    vm[tt] = (i <= r) ? scale * tm[tt] : 0.f;
+    vm[tt] = (i <= r) ? sm_ * tm[tt] : 0.f;
   }
   if constexpr (ib == rb) {
     *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
@@ -218,40 +218,45 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float s
   *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(vm[0], vm[1], vm[2], vm[3]);
 }
 
+template <int NV, bool FAST>
+__device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m16, float scale) {
+  switch (wave) {
+    case 0:
+      tile_pair<NV, 0, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 1, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 8, FAST>(sm, q4, m16, scale);
+      break;
+    case 1:
+      tile_pair<NV, 2, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 3, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 4, FAST>(sm, q4, m16, scale);
+      break;
+    case 2:
+      tile_pair<NV, 5, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 6, FAST>(sm, q4, m16, scale);
+      break;
+    default:
+      tile_pair<NV, 7, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 9, FAST>(sm, q4, m16, scale);
+      break;
+  }
+}
+
 // Phase C tile work of state wave `wave` (0..3, wave-uniform): pairs (0,0) (1,0)
-// (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3) -- the seven pairs that
-// scale their column operand spread two per wave.  The pairs of a wave are
-// independent straight-line code, so their loads and products overlap.
+// (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3) -- with block references
+// the seven pairs that scale their column operand spread two per wave.  The
+// pairs of a wave are independent straight-line code, so their loads and
+// products overlap.
 template <int NV>
 __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int m16_, float scale) {
   // lane indices through an empty asm: the tile addresses are then formed here on
   // every call instead of being kept live (or spilled) across the whole loop
   int q4 = q4_, m16 = m16_;
   asm volatile("" : "+v"(q4), "+v"(m16));
-  switch (wave) {
-    case 0:
-      tile_pair<NV, 0>(sm, q4, m16, scale);
-      tile_pair<NV, 1>(sm, q4, m16, scale);
-      tile_pair<NV, 8>(sm, q4, m16, scale);
-      break;
-    case 1:
-      tile_pair<NV, 2>(sm, q4, m16, scale);
-      tile_pair<NV, 3>(sm, q4, m16, scale);
-      tile_pair<NV, 4>(sm, q4, m16, scale);
-      break;
-    case 2:
-      tile_pair<NV, 5>(sm, q4, m16, scale);
-      tile_pair<NV, 6>(sm, q4, m16, scale);
-      break;
-    default:
-      tile_pair<NV, 7>(sm, q4, m16, scale);
-      tile_pair<NV, 9>(sm, q4, m16, scale);
-      break;
-  }
+  if (__builtin_amdgcn_readfirstlane(sm.chunk_ref)) tile_pairs<NV, true>(sm, wave, q4, m16, scale);
+  else tile_pairs<NV, false>(sm, wave, q4, m16, scale);
 }
 
-// One workgroup's task: a run of consecutive chunks of one (sequence, head,
-// value slice) -- a whole sequence, or one segment of a split sequence.
 struct Work {
   int64_t bos;     // first token of the run
   int64_t len;     // tokens in the run
@@ -271,6 +276,40 @@ struct Work {
 // zero and stores beyond it are dropped (raw buffer, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Wave-wide integer scans and reductions on DPP row shifts and row broadcasts
+// (lanes shifted in from outside a row read zero).
+template <int ctrl, int rmask = 0xf>
+__device__ __forceinline__ int dpp_in(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, ctrl, rmask, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: within rows of 16 by doubling
+// shifts, then row 0's total into rows 1 and 3, lane 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_in<0x111>(x);        // row_shr:1
+  x += dpp_in<0x112>(x);        // row_shr:2
+  x += dpp_in<0x114>(x);        // row_shr:4
+  x += dpp_in<0x118>(x);        // row_shr:8
+  x += dpp_in<0x142, 0xa>(x);   // row_bcast:15
+  x += dpp_in<0x143, 0xc>(x);   // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// Maximum of non-negative values over the 64 lanes.
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, dpp_in<0x111>(x));
+  x = max(x, dpp_in<0x112>(x));
+  x = max(x, dpp_in<0x114>(x));
+  x = max(x, dpp_in<0x118>(x));
+  x = max(x, dpp_in<0x142, 0xa>(x));
+  x = max(x, dpp_in<0x143, 0xc>(x));
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 // ============================================================================ prep waves
@@ -448,6 +487,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
     uint2 kpt_hold[4][2];                  // channel 4cg+e: rows 8rg..8rg+3, 8rg+4..8rg+7
     float4 gamc_hold;
     float pother[4];                       // exp2 of the other half-block's sum (A -> B)
+    float sother[4], sown[4];              // the other half-block's and this group's sums
 
     // ---- phase A: inverses for chunk `it` (used in the state waves' phase B); for
     // chunk pc the 8-row sums of g*log2(e), the decays a = exp(g), and the
@@ -467,27 +507,16 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       for (int e = 0; e < 4; ++e) {
         const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[e]), __float_as_uint(s[e]),
                                                           false, false);
-        pother[e] = ex2(__uint_as_float(second ? p32[0] : p32[1]));
+        sown[e] = s[e];
+        sother[e] = __uint_as_float(second ? p32[0] : p32[1]);
+        pother[e] = ex2(sother[e]);
       }
       if (t < C) sm.pbeta[t] = R.beta;
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8)
+      for (int r8 = 0; r8 < 8; ++r8) {
         R.g[r8] = make_float4(ex2(R.g[r8].x), ex2(R.g[r8].y), ex2(R.g[r8].z), ex2(R.g[r8].w));
-      float Hv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Hv[e] = second ? 1.f : pother[e];  // H of the last row
-#pragma unroll
-      for (int r8 = 7; r8 >= 0; --r8) {
-        float kf[4], kh[4];
-        unpack4(R.k[r8], kf);
-        const float4 av = R.g[r8];
-        const float ar[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kh[e] = kf[e] * Hv[e];
-          Hv[e] *= ar[e];
-        }
-        *reinterpret_cast<uint2*>(&sm.kh[(rg * 8 + r8) * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+        // the decays are formed here, not rematerialised next to their uses in phase B
+        asm volatile("" : "+v"(R.g[r8].x), "+v"(R.g[r8].y), "+v"(R.g[r8].z), "+v"(R.g[r8].w));
       }
     }
     __syncthreads();  // (A) the state waves are done with K exp(G), Q exp(G), V^T, beta
@@ -499,13 +528,12 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // beta and g (the memory counter retires loads in order)
       if (t < C) sm.beta[t] = R.beta;
       load_beta<NV>(R, nsrc, p.H, t);
-      float eCX[4], eXb[4];
-      {
-        // X[k] = G (log2) at the last row of block k-1 per channel (X[0] = 0,
-        // X[4] = G_last): running sums of the 8-row group sums.
-        float X[5][4];
+      // X[k] = G (log2) at the last row of block k-1 per channel (X[0] = 0,
+      // X[4] = G_last): running sums of the 8-row group sums.
+      float X[5][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[0][e] = 0.f;
+      for (int e = 0; e < 4; ++e) X[0][e] = 0.f;
+      {
         float run[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -516,75 +544,169 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
             for (int e = 0; e < 4; ++e) X[(r + 1) >> 1][e] = run[e];
           }
         }
-        float fs[4];
+      }
+      gamc_hold = make_float4(ex2(X[4][0]), ex2(X[4][1]), ex2(X[4][2]), ex2(X[4][3]));
+      // Chunk-level reference when exp(+-G) stays within 2^+-96 on every channel
+      // (G falls along the chunk for g <= 0, so G_last bounds it); otherwise the
+      // 16-row block references.  All prep waves reach the same decision.
+      int span = 0;
+#pragma unroll
+      for (int k = 1; k < 5; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = X[k][e];
+          span = max(span, __float_as_int(x < 0.f ? -x : 4.f * x));
+        }
+      const bool chunk_ref = wave_max(span) < __float_as_int(96.f);
+      if (t == 0) sm.chunk_ref = chunk_ref ? 1 : 0;
+      if (chunk_ref) {
+        // G before this thread's first row (Xg) and after its last row (Xe)
+        float nE[4], Hc[4], ig[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float Xb = m1 * X[1][e] + m2 * X[2][e] + m3 * X[3][e];
-          const float Xb1 = m0 * X[1][e] + m1 * X[2][e] + m2 * X[3][e] + m3 * X[4][e];
-          eCX[e] = ex2(X[4][e] - Xb1);
-          eXb[e] = ex2(Xb);
-          fs[e] = ex2(wx[1] * X[1][e] + wx[2] * X[2][e] + wx[3] * X[3][e] + wx[4] * X[4][e]);
+          const float Xg = second ? Xb + sother[e] : Xb;
+          nE[e] = -ex2(Xg);
+          Hc[e] = ex2(X[4][e] - (Xg + sown[e]));
+          ig[e] = ex2(-X[4][e]);
         }
-        // this half-wave's pair factor (or exp(G_last), kept for phase C)
-        gamc_hold = make_float4(fs[0], fs[1], fs[2], fs[3]);
-        if (spr >= 0) *reinterpret_cast<float4*>(&sm.pf[spr * D + 4 * cg]) = gamc_hold;
-      }
-      // Hc_r = H_r exp(G_last - X_{b+1}) (the state-update operand K' = K * Hc)
-      float Hc[8][4];
+        // last row first: K' = K exp(G_last - G) and K exp(-G) = K' exp(-G_last)
+        uint32_t kpw[4][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Hc[7][e] = (second ? 1.f : pother[e]) * eCX[e];
+        for (int r8 = 7; r8 >= 0; --r8) {
+          float kf[4], kp[4], kh[4];
+          unpack4(R.k[r8], kf);
+          const float4 av = R.g[r8];
+          const float ar[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-      for (int r8 = 6; r8 >= 0; --r8) {
-        const float4 av = R.g[r8 + 1];
-        Hc[r8][0] = Hc[r8 + 1][0] * av.x; Hc[r8][1] = Hc[r8 + 1][1] * av.y;
-        Hc[r8][2] = Hc[r8 + 1][2] * av.z; Hc[r8][3] = Hc[r8 + 1][3] * av.w;
-      }
-      // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F, the state
-      // operands -K * exp(G) = -K * F * exp(X_b), scale * Q * exp(G), and K'
-      {
-        uint32_t kpw[4][4];  // K' of row pairs (2j, 2j+1), per channel
-        float F[4], nXb[4], sXb[4];
+          for (int e = 0; e < 4; ++e) {
+            kp[e] = kf[e] * Hc[e];
+            kh[e] = kp[e] * ig[e];
+            Hc[e] *= ar[e];
+          }
+          if (r8 & 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = __float_as_uint(kp[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = pack2(kp[e], __uint_as_float(kpw[e][r8 >> 1]));
+          }
+          *reinterpret_cast<uint2*>(&sm.kh[(rg * 8 + r8) * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          F[e] = second ? pother[e] : 1.f;  // F of the row before
-          nXb[e] = -eXb[e];
-          sXb[e] = p.scale * eXb[e];
+          kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
+          kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
         }
+        // first row first: -K exp(G) and scale * Q exp(G)
 #pragma unroll
         for (int r8 = 0; r8 < 8; ++r8) {
-          const int row = rg * 8 + r8;
-          float qf[4], kf[4], kr[4], qr[4], kg[4], qg[4], kp[4];
+          float qf[4], kf[4], kg[4], qg[4];
           unpack4(R.q[r8], qf);
           unpack4(R.k[r8], kf);
           const float4 av = R.g[r8];
           const float ar[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            F[e] *= ar[e];
-            kr[e] = kf[e] * F[e];
-            qr[e] = qf[e] * F[e];
-            kg[e] = kr[e] * nXb[e];   // -K exp(G)
-            qg[e] = qr[e] * sXb[e];   // scale * Q exp(G)
-            kp[e] = kf[e] * Hc[r8][e];
+            nE[e] *= ar[e];
+            kg[e] = kf[e] * nE[e];
+            qg[e] = -(qf[e] * nE[e]) * p.scale;
           }
-          if (r8 & 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              kpw[e][r8 >> 1] = pack2(__uint_as_float(kpw[e][r8 >> 1]), kp[e]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = __float_as_uint(kp[e]);
-          }
-          const int o = row * TS + 4 * cg;
-          *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
-          *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
+          const int o = (rg * 8 + r8) * TS + 4 * cg;
           *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
           *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
         }
+      } else {
+        // 16-row block references: block-local H pass, H_r = H_{r+1} a_{r+1}, last row first
+        {
+          float Hv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
-          kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
+          for (int e = 0; e < 4; ++e) Hv[e] = second ? 1.f : pother[e];  // H of the last row
+#pragma unroll
+          for (int r8 = 7; r8 >= 0; --r8) {
+            float kf[4], kh[4];
+            unpack4(R.k[r8], kf);
+            const float4 av = R.g[r8];
+            const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kh[e] = kf[e] * Hv[e];
+              Hv[e] *= ar[e];
+            }
+            *reinterpret_cast<uint2*>(&sm.kh[(rg * 8 + r8) * TS + 4 * cg]) = pack4(kh[0], kh[1], kh[2], kh[3]);
+          }
+        }
+        float eCX[4], eXb[4];
+        {
+          float fs[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float Xb = m1 * X[1][e] + m2 * X[2][e] + m3 * X[3][e];
+            const float Xb1 = m0 * X[1][e] + m1 * X[2][e] + m2 * X[3][e] + m3 * X[4][e];
+            eCX[e] = ex2(X[4][e] - Xb1);
+            eXb[e] = ex2(Xb);
+            fs[e] = ex2(wx[1] * X[1][e] + wx[2] * X[2][e] + wx[3] * X[3][e] + wx[4] * X[4][e]);
+          }
+          // this half-wave's pair factor
+          if (spr >= 0) *reinterpret_cast<float4*>(&sm.pf[spr * D + 4 * cg]) = make_float4(fs[0], fs[1], fs[2], fs[3]);
+        }
+        // Hc_r = H_r exp(G_last - X_{b+1}) (the state-update operand K' = K * Hc)
+        float Hc[8][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Hc[7][e] = (second ? 1.f : pother[e]) * eCX[e];
+#pragma unroll
+        for (int r8 = 6; r8 >= 0; --r8) {
+          const float4 av = R.g[r8 + 1];
+          Hc[r8][0] = Hc[r8 + 1][0] * av.x; Hc[r8][1] = Hc[r8 + 1][1] * av.y;
+          Hc[r8][2] = Hc[r8 + 1][2] * av.z; Hc[r8][3] = Hc[r8 + 1][3] * av.w;
+        }
+        // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F, the state
+        // operands -K * exp(G) = -K * F * exp(X_b), scale * Q * exp(G), and K'
+        {
+          uint32_t kpw[4][4];  // K' of row pairs (2j, 2j+1), per channel
+          float F[4], nXb[4], sXb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F[e] = second ? pother[e] : 1.f;  // F of the row before
+            nXb[e] = -eXb[e];
+            sXb[e] = p.scale * eXb[e];
+          }
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8) {
+            const int row = rg * 8 + r8;
+            float qf[4], kf[4], kr[4], qr[4], kg[4], qg[4], kp[4];
+            unpack4(R.q[r8], qf);
+            unpack4(R.k[r8], kf);
+            const float4 av = R.g[r8];
+            const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              F[e] *= ar[e];
+              kr[e] = kf[e] * F[e];
+              qr[e] = qf[e] * F[e];
+              kg[e] = kr[e] * nXb[e];   // -K exp(G)
+              qg[e] = qr[e] * sXb[e];   // scale * Q exp(G)
+              kp[e] = kf[e] * Hc[r8][e];
+            }
+            if (r8 & 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+              kpw[e][r8 >> 1] = pack2(__uint_as_float(kpw[e][r8 >> 1]), kp[e]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) kpw[e][r8 >> 1] = __float_as_uint(kp[e]);
+            }
+            const int o = row * TS + 4 * cg;
+            *reinterpret_cast<uint2*>(&sm.kr[o]) = pack4(kr[0], kr[1], kr[2], kr[3]);
+            *reinterpret_cast<uint2*>(&sm.qr[o]) = pack4(qr[0], qr[1], qr[2], qr[3]);
+            *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
+            *reinterpret_cast<uint2*>(&sm.qg[o]) = pack4(qg[0], qg[1], qg[2], qg[3]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
+            kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
+          }
         }
       }
       load_g<NV>(R, nsrc, HD, t);  // the decays of this chunk are consumed
@@ -619,7 +741,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o]) = kpt_hold[e][0];
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
-      if (spr < 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
+      if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
     }
     __syncthreads();  // (C) chunk pc fully published
   }
@@ -734,9 +856,13 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
       bf16x4 U[4][JT];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        // row m16 of the block's inverse, Li[m16][4q4 + kb]; U = Li z in fp32 with
-        // the k index of product kb at 4q4 + kb, so z enters in its D layout
+        // row m16 of the block's inverse, Li[m16][4q4 + e], and z in its D layout are
+        // exactly the operands of a 16x16x16 product; U = Li z from high and low
+        // bf16 parts of both (the low-by-low term dropped), close to fp32
         const float4 lv = *reinterpret_cast<const float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]);
+        const f32x4 lf = f32x4{lv.x, lv.y, lv.z, lv.w};
+        const bf16x4 lh = cvt4(lf);
+        const bf16x4 ll = cvt4(f32x4{lf[0] - bf2f(lh[0]), lf[1] - bf2f(lh[1]), lf[2] - bf2f(lh[2]), lf[3] - bf2f(lh[3])});
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           f32x4 z = Z[b][jt];
@@ -745,10 +871,11 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             const bf16x4 an = ld4(&sm.an[(16 * b + m16) * QS + 16 * bp + 4 * q4]);
             z = mfma16(an, U[bp][jt], z);
           }
-          f32x4 u = mfma4f(lv.x, z[0], f32x4{0.f, 0.f, 0.f, 0.f});
-          u = mfma4f(lv.y, z[1], u);
-          u = mfma4f(lv.z, z[2], u);
-          u = mfma4f(lv.w, z[3], u);
+          const bf16x4 zh = cvt4(z);
+          const bf16x4 zl = cvt4(f32x4{z[0] - bf2f(zh[0]), z[1] - bf2f(zh[1]), z[2] - bf2f(zh[2]), z[3] - bf2f(zh[3])});
+          f32x4 u = mfma16(lh, zh, f32x4{0.f, 0.f, 0.f, 0.f});
+          u = mfma16(lh, zl, u);
+          u = mfma16(ll, zh, u);
           U[b][jt] = cvt4(u);
         }
       }
@@ -851,44 +978,6 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 // from the sequence lengths (integer arithmetic only).
 
 constexpr int kNoSplit = 0x7fffffff;
-
-// Wave-wide integer scans and reductions on DPP row shifts and row broadcasts
-// (lanes shifted in from outside a row read zero).
-template <int ctrl, int rmask = 0xf>
-__device__ __forceinline__ int dpp_in(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, ctrl, rmask, 0xf, true);
-}
-
-// Inclusive prefix sum over the 64 lanes: within rows of 16 by doubling
-// shifts, then row 0's total into rows 1 and 3, lane 31's into rows 2 and 3.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += dpp_in<0x111>(x);        // row_shr:1
-  x += dpp_in<0x112>(x);        // row_shr:2
-  x += dpp_in<0x114>(x);        // row_shr:4
-  x += dpp_in<0x118>(x);        // row_shr:8
-  x += dpp_in<0x142, 0xa>(x);   // row_bcast:15
-  x += dpp_in<0x143, 0xc>(x);   // row_bcast:31
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
-}
-
-// Maximum of non-negative values over the 64 lanes.
-__device__ __forceinline__ int wave_max(int x) {
-  x = max(x, dpp_in<0x111>(x));
-  x = max(x, dpp_in<0x112>(x));
-  x = max(x, dpp_in<0x114>(x));
-  x = max(x, dpp_in<0x118>(x));
-  x = max(x, dpp_in<0x142, 0xa>(x));
-  x = max(x, dpp_in<0x143, 0xc>(x));
-  return __builtin_amdgcn_readlane(x, 63);
-}
-
-__device__ __forceinline__ int64_t seq_bos(const Params& p, int i) {
-  return p.cu ? (int64_t)p.cu[i] : (int64_t)i * p.T;
-}
 
 __device__ __forceinline__ int64_t seq_len(const Params& p, int i) {
   return p.cu ? (int64_t)p.cu[i + 1] - p.cu[i] : p.T;

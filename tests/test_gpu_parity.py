@@ -172,6 +172,23 @@ def test_strong_decay_edge_of_range():
     check(x, out, fin)
 
 
+def test_mixed_decay_chunks():
+    """Chunks whose decay over the chunk exceeds the chunk-level exponent range
+    (here -g up to 4.5 on some channels) take the 16-row block references, the
+    others the chunk-level reference; both within one sequence."""
+    announce("mixed decay regimes across chunks")
+    x = random_inputs(1, 600, 2, seed=14, device=DEV, init_state="fp32")
+    gen = torch.Generator().manual_seed(15)
+    g = x["g"].cpu()
+    strong = -(1.5 + 3.0 * torch.rand(g.shape, generator=gen))
+    chan = torch.rand(1, 1, g.shape[2], g.shape[3], generator=gen) < 0.25
+    for a, b in ((64, 128), (256, 320), (500, 600)):
+        g[:, a:b] = torch.where(chan, strong[:, a:b], g[:, a:b])
+    x["g"] = g.to(DEV)
+    out, fin = run_gpu(x, final_dtype=torch.float32)
+    check(x, out, fin)
+
+
 def test_deterministic():
     announce("determinism")
     x = random_inputs(1, 1000, 4, seed=13, device=DEV, init_state="fp32")
