@@ -270,6 +270,7 @@ struct Work {
   const void* s0;  // this (sequence, head)'s 128 x 128 start state
   void* s1;        // where its end state goes, or null
   void* o;         // output rows, [rows][H][128] (bf16 or fp32)
+  uint16_t* sb;    // also the end state in the fix-up's bf16 operand order, or null
 };
 
 // Buffer descriptor over `bytes` bytes from `base`; loads beyond the range return
@@ -955,6 +956,19 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = (__bf16)Sacc[ct][jt][t];
     }
   }
+  if (w.sb != nullptr) {
+    // element (k, j) at [k/32][j/16][16 ((k/8) % 4) + j % 16][k % 8]: this lane's
+    // rows 16ct + 4q4 .. +3 of column j are four consecutive entries
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        const int k0 = 16 * ct + 4 * q4;
+        const int jg = (jw_base >> 4) + jt;
+        uint16_t* dst = w.sb + (((k0 >> 5) * 8 + jg) * 64 + 16 * ((k0 >> 3) & 3) + m16) * 8 + (k0 & 7);
+        *reinterpret_cast<uint2*>(dst) = pack4(Sacc[ct][jt][0], Sacc[ct][jt][1], Sacc[ct][jt][2], Sacc[ct][jt][3]);
+      }
+  }
 }
 
 // ============================================================================ segment plan
@@ -986,19 +1000,20 @@ __device__ __forceinline__ int64_t seq_len(const Params& p, int i) {
 // The plan in LDS (ints).
 struct PlanView {
   int* hdr;   // [0] M (kNoSplit: nothing split) [1] task groups [2] state slots
-              // [3] split sequences [4] fix-up units
+              // [3] split sequences [4] fix-up units of segment 1 [5] of later segments
   int* lens;  // [N]   chunks of each sequence
   int* goff;  // [N+1] first task group of each sequence
   int* soff;  // [N+1] first state slot (slot of segment p >= 1: soff + p - 1)
   int* xoff;  // [N+1] split sequences before it
-  int* uoff;  // [N+1] first fix-up unit
+  int* uoff;  // [N+1] first fix-up unit of segment 1
+  int* voff;  // [N+1] first fix-up unit of the later segments
   int* glen;  // [N + 2 emax] chunks of each task group
   int* gseq;  //              its sequence
   int* gk;    //              its kind: 0 segment 0; 2p-1 zero start, 2p identity start of segment p
 };
 
 __host__ __device__ constexpr int plan_ints(int N, int emax, bool groups) {
-  return 8 + N + 4 * (N + 1) + (groups ? 3 * (N + 2 * emax) : 0);
+  return 8 + N + 5 * (N + 1) + (groups ? 3 * (N + 2 * emax) : 0);
 }
 
 __device__ __forceinline__ PlanView plan_view(int* base, int N, int emax) {
@@ -1009,26 +1024,28 @@ __device__ __forceinline__ PlanView plan_view(int* base, int N, int emax) {
   v.soff = v.goff + N + 1;
   v.xoff = v.soff + N + 1;
   v.uoff = v.xoff + N + 1;
-  v.glen = v.uoff + N + 1;
+  v.voff = v.uoff + N + 1;
+  v.glen = v.voff + N + 1;
   v.gseq = v.glen + N + 2 * emax;
   v.gk = v.gseq + N + 2 * emax;
   return v;
 }
 
 struct SeqCounts {
-  int groups, slots, split, units;
+  int groups, slots, split, units1, units2;
 };
 
 // Task groups, state slots, split flag and fix-up units (one per chunk and
-// head past segment 0) of a sequence of c chunks.
+// head) of segment 1 and of the later segments, for a sequence of c chunks.
 __device__ __forceinline__ SeqCounts seq_counts(int c, int M, int H) {
-  SeqCounts r{1, 0, 0, 0};
+  SeqCounts r{1, 0, 0, 0, 0};
   if (M != kNoSplit && c > M) {
     const int P = (c + M - 1) / M;
     r.groups = 2 * P - 1;
     r.slots = P - 1;
     r.split = 1;
-    r.units = H * (c - M);
+    r.units1 = H * min(c - M, M);
+    r.units2 = H * max(c - 2 * M, 0);
   }
   return r;
 }
@@ -1071,37 +1088,42 @@ __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
     // exclusive prefix sums over contiguous runs of sequences, one run per lane
     const int per = (N + 63) / 64;
     const int i0 = min(N, lane * per), i1 = min(N, i0 + per);
-    int sg = 0, ss = 0, sx = 0, su = 0;
+    int sg = 0, ss = 0, sx = 0, su = 0, sv = 0;
     for (int i = i0; i < i1; ++i) {
       const SeqCounts r = seq_counts(v.lens[i], M, p.H);
       sg += r.groups;
       ss += r.slots;
       sx += r.split;
-      su += r.units;
+      su += r.units1;
+      sv += r.units2;
     }
     int eg = wave_incl_scan(sg) - sg, es = wave_incl_scan(ss) - ss;
-    int ex = wave_incl_scan(sx) - sx, eu = wave_incl_scan(su) - su;
+    int ex = wave_incl_scan(sx) - sx, eu = wave_incl_scan(su) - su, ev = wave_incl_scan(sv) - sv;
     for (int i = i0; i < i1; ++i) {
       const SeqCounts r = seq_counts(v.lens[i], M, p.H);
       v.goff[i] = eg;
       v.soff[i] = es;
       v.xoff[i] = ex;
       v.uoff[i] = eu;
+      v.voff[i] = ev;
       eg += r.groups;
       es += r.slots;
       ex += r.split;
-      eu += r.units;
+      eu += r.units1;
+      ev += r.units2;
     }
     if (lane == 63) {  // its run ends at N: the running sums are the totals
       v.goff[N] = eg;
       v.soff[N] = es;
       v.xoff[N] = ex;
       v.uoff[N] = eu;
+      v.voff[N] = ev;
       v.hdr[0] = M;
       v.hdr[1] = eg;
       v.hdr[2] = es;
       v.hdr[3] = ex;
       v.hdr[4] = eu;
+      v.hdr[5] = ev;
     }
   }
   __syncthreads();
@@ -1209,9 +1231,11 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.s0_mode = p.s0 == nullptr ? 0 : p.s0_fp32 ? 2 : 1;
     w.s0 = p.s0 == nullptr ? nullptr
          : static_cast<const char*>(p.s0) + ((size_t)n * p.H * (D * D) + hd2) * (p.s0_fp32 ? 4 : 2);
-    if (seq_split) {  // the start state of segment 1
+    w.sb = nullptr;
+    if (seq_split) {  // the start state of segment 1, also as the fix-up operand
       w.s1 = p.st + ((size_t)slot0 * p.H) * (D * D) + hd2;
       w.s1_fp32 = 1;
+      w.sb = p.sb + ((size_t)slot0 * p.H) * (D * D) + hd2;
     } else {
       w.s1 = p.s1 == nullptr ? nullptr
            : static_cast<char*>(p.s1) + ((size_t)n * p.H * (D * D) + hd2) * (p.s1_fp32 ? 4 : 2);
@@ -1233,6 +1257,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.o = ident ? static_cast<void*>(p.out) : static_cast<void*>(p.o0);
     w.o_f32 = ident ? 0 : 1;
     w.vzero = ident ? 1 : 0;
+    w.sb = nullptr;
   }
   w.nchunks = (int)((w.len + C - 1) / C);
 
@@ -1248,185 +1273,224 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   else prep_loop<NV>(sm, p, w);
 }
 
-// ============================================================================ segment scan
-// One workgroup per (split sequence, head, 16-column block of the state), in a
-// grid-stride loop: S_1 is segment 0's end state; for p = 1 .. P-1 it stores
-// the bf16 operand copy of S_p for the fix-up and forms S_{p+1} = A_p S_p + B_p
-// in fp32.  S_P is the sequence's final state.  The plan lives in dynamic LDS
-// (plan_ints(N, 0, false) ints).
-constexpr int SCAN_NT = 256;
-constexpr int SLS = 16 + 4;  // row stride (fp32) of the state block
+// ============================================================================ scan and fix-up
+// Two launches follow the main kernel when sequences were split.
+//  * phase 0: the scan, one unit per (split sequence, head, 16-column block of
+//    the state): S_1 is segment 0's end state; for p = 1 .. P-1 it forms
+//    S_{p+1} = A_p S_p + B_p in fp32 and stores the bf16 operand copy of S_p for
+//    p >= 2 (segment 0's task stored that of S_1); S_P is the final state.  The
+//    same launch fixes up the outputs of segment 1, which need only S_1.
+//  * phase 1: the output fix-up of the later segments.
+// A fix-up unit is one chunk of one (sequence, head): o_t = O0_t + S_p^T Q~_t,
+// with Q~ read from (and o written back to) the output rows.  Every load of a
+// unit is issued at its start.  Wave w forms output columns 32w..32w+31 as
+// O^T = S_p^T Q~^T on bf16 MFMA 16x16x32; Q~ is staged through LDS so that each
+// wave reads all 64 tokens.  The plan lives in dynamic LDS (plan_ints(N, 0,
+// false) ints); every launch walks its units in a grid-stride loop.
+constexpr int TAIL_NT = 256;
+constexpr int SLT = D + 4;  // row stride (fp32) of the scan's state block, stored transposed
 
-__global__ void __launch_bounds__(SCAN_NT) kda_scan_kernel(Params p) {
-  extern __shared__ int plan_lds[];
-  __shared__ __attribute__((aligned(16))) float sl[D * SLS];
-  const int N = p.nseq, tid = threadIdx.x;
-  const PlanView v = plan_view(plan_lds, N, 0);
-  build_plan(p, v, false);
-  const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
-  if (M == kNoSplit) return;
-  const int units = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
-  const size_t slot_stride = (size_t)p.H * (D * D);
-  const int r = tid >> 1, c8 = (tid & 1) * 8;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int sidx = u / (p.H * 8), h = (u / 8) % p.H, cb = u % 8;
-    const int i = __builtin_amdgcn_readfirstlane(find_seq(v.xoff, N, sidx));
-    const int c = __builtin_amdgcn_readfirstlane(v.lens[i]), P = (c + M - 1) / M;
-    const int slot0 = __builtin_amdgcn_readfirstlane(v.soff[i]);
-    const size_t hd2 = (size_t)h * (D * D);
-    {
-      const float* s1 = p.st + slot0 * slot_stride + hd2 + (size_t)r * D + 16 * cb + c8;
-      const float4 a0 = *reinterpret_cast<const float4*>(s1);
-      const float4 a1 = *reinterpret_cast<const float4*>(s1 + 4);
-      *reinterpret_cast<float4*>(&sl[r * SLS + c8]) = a0;
-      *reinterpret_cast<float4*>(&sl[r * SLS + c8 + 4]) = a1;
-    }
-    __syncthreads();
-    for (int sp = 1; sp < P; ++sp) {
-      const int slot = slot0 + sp - 1;
-      // row r of A_p and the thread's 8 entries of B_p, all loads in flight at once
-      const float* am = p.st + ((size_t)p.emax + slot) * slot_stride + hd2 + (size_t)r * D;
-      const float* bm = p.st + ((size_t)2 * p.emax + slot) * slot_stride + hd2 + (size_t)r * D + 16 * cb + c8;
-      float4 arow[D / 4];
+__device__ __forceinline__ void split_hilo(const float* f, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-      for (int kq = 0; kq < D / 4; ++kq) arow[kq] = *reinterpret_cast<const float4*>(am + 4 * kq);
-      const float4 b0 = *reinterpret_cast<const float4*>(bm);
-      const float4 b1 = *reinterpret_cast<const float4*>(bm + 4);
-      __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
-      {  // fix-up operand: element (k, j) of S_p at [(k/32)][j/16][lane][k%8] with
-         // lane = 16 ((k/8)%4) + j%16 -- the A operand (S^T) of a 16x16x32 product
-        const int ks = tid >> 6, lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = sl[(32 * ks + 8 * q4 + e) * SLS + m16];
-        const uint2 lo = pack4(f[0], f[1], f[2], f[3]), hi = pack4(f[4], f[5], f[6], f[7]);
-        uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * 8 + cb) * 64 + lane) * 8;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-      float acc[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-      for (int kq = 0; kq < D / 4; ++kq) {
-        const float av[4] = {arow[kq].x, arow[kq].y, arow[kq].z, arow[kq].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float4 s0 = *reinterpret_cast<const float4*>(&sl[(4 * kq + e) * SLS + c8]);
-          const float4 s1v = *reinterpret_cast<const float4*>(&sl[(4 * kq + e) * SLS + c8 + 4]);
-          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1v.x, s1v.y, s1v.z, s1v.w};
-#pragma unroll
-          for (int x = 0; x < 8; ++x) acc[x] += av[e] * sv[x];
-        }
-      }
-      __syncthreads();  // every read of S_p is done
-      *reinterpret_cast<float4*>(&sl[r * SLS + c8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(&sl[r * SLS + c8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      __syncthreads();
-    }
-    if (p.s1 != nullptr) {
-      const size_t o = ((size_t)i * p.H) * (D * D) + hd2 + (size_t)r * D + 16 * cb + c8;
-      const float4 a0 = *reinterpret_cast<const float4*>(&sl[r * SLS + c8]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&sl[r * SLS + c8 + 4]);
-      if (p.s1_fp32) {
-        float* d = static_cast<float*>(p.s1) + o;
-        *reinterpret_cast<float4*>(d) = a0;
-        *reinterpret_cast<float4*>(d + 4) = a1;
-      } else {
-        const uint2 lo = pack4(a0.x, a0.y, a0.z, a0.w), hi = pack4(a1.x, a1.y, a1.z, a1.w);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.s1) + o) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-    __syncthreads();  // before the next unit overwrites the block
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (__bf16)f[e];
+    lo[e] = (__bf16)(f[e] - bf2f(hi[e]));
   }
 }
 
-// ============================================================================ output fix-up
-// One work unit = one chunk of a later segment p of one (sequence, head):
-// o_t = O0_t + S_p^T Q~_t, with Q~ read from (and o written back to) the output
-// rows.  Every load of the unit is issued at its start.  Wave w forms output
-// columns 32w..32w+31 as O^T = S_p^T Q~^T on bf16 MFMA 16x16x32; Q~ is staged
-// through LDS so that each wave reads all 64 tokens.  The plan lives in dynamic
-// LDS (plan_ints(N, 0, false) ints).
-constexpr int FIX_NT = 256;
-
-__global__ void __launch_bounds__(FIX_NT) kda_fix_kernel(Params p) {
-  extern __shared__ int plan_lds[];
-  __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
+// One scan unit: columns 16cb .. 16cb+15 of the states of split sequence
+// `sidx`, head h.  The block lives transposed in LDS, slt[j][k].  A_p S_p runs on
+// bf16 16x16x32 products of high and low parts (the low-by-low term dropped);
+// wave w forms rows 32w .. 32w+31.
+__device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, int M, int u, float* slt) {
   const int N = p.nseq, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const size_t slot_stride = (size_t)p.H * (D * D);
+  const int sidx = u / (p.H * 8), h = (u / 8) % p.H, cb = u % 8;
+  const int i = __builtin_amdgcn_readfirstlane(find_seq(v.xoff, N, sidx));
+  const int c = __builtin_amdgcn_readfirstlane(v.lens[i]), P = (c + M - 1) / M;
+  const int slot0 = __builtin_amdgcn_readfirstlane(v.soff[i]);
+  const size_t hd2 = (size_t)h * (D * D);
+  {  // S_1 (row-major in the workspace) -> slt
+    const float* s1 = p.st + slot0 * slot_stride + hd2 + 16 * cb;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int k = 16 * x + (tid >> 4), j = tid & 15;
+      slt[j * SLT + k] = s1[(size_t)k * D + j];
+    }
+  }
+  __syncthreads();
+  for (int sp = 1; sp < P; ++sp) {
+    const int slot = slot0 + sp - 1;
+    // rows 32w + 16it + m16 of A_p (k = 32ks + 8q4 .. +7) and the matching
+    // entries of B_p, all loads in flight before the products
+    const float* am = p.st + ((size_t)p.emax + slot) * slot_stride + hd2;
+    const float* bm = p.st + ((size_t)2 * p.emax + slot) * slot_stride + hd2 + 16 * cb + m16;
+    float4 ar[2][4][2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float* rp = am + (size_t)(32 * wave + 16 * it + m16) * D + 32 * ks + 8 * q4;
+        ar[it][ks][0] = *reinterpret_cast<const float4*>(rp);
+        ar[it][ks][1] = *reinterpret_cast<const float4*>(rp + 4);
+      }
+    f32x4 acc[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[it][t] = bm[(size_t)(32 * wave + 16 * it + 4 * q4 + t) * D];
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+    if (sp >= 2) {  // fix-up operand copy of S_p: element (k, j) at [k/32][j/16][16 ((k/8)%4) + j%16][k%8]
+      const int ks = tid >> 6;
+      const float4 f0 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4 + 4]);
+      const uint2 lo = pack4(f0.x, f0.y, f0.z, f0.w), hi = pack4(f1.x, f1.y, f1.z, f1.w);
+      uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * 8 + cb) * 64 + lane) * 8;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // B operand: S_p[32ks + 8q4 + e][m16] = slt[m16][32ks + 8q4 + e]
+      const float4 g0 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4 + 4]);
+      const float sf[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      bf16x8 sh, sl;
+      split_hilo(sf, sh, sl);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const float af[8] = {ar[it][ks][0].x, ar[it][ks][0].y, ar[it][ks][0].z, ar[it][ks][0].w,
+                             ar[it][ks][1].x, ar[it][ks][1].y, ar[it][ks][1].z, ar[it][ks][1].w};
+        bf16x8 ah, al;
+        split_hilo(af, ah, al);
+        acc[it] = mfma32(ah, sh, acc[it]);
+        acc[it] = mfma32(ah, sl, acc[it]);
+        acc[it] = mfma32(al, sh, acc[it]);
+      }
+    }
+    __syncthreads();  // every read of S_p is done
+    // lane holds S_{p+1}[32w + 16it + 4q4 + t][m16]: four consecutive entries of slt row m16
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      *reinterpret_cast<float4*>(&slt[m16 * SLT + 32 * wave + 16 * it + 4 * q4]) =
+          make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
+    __syncthreads();
+  }
+  if (p.s1 != nullptr) {
+    const size_t base = ((size_t)i * p.H) * (D * D) + hd2 + 16 * cb;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int k = 16 * x + (tid >> 4), j = tid & 15;
+      const float val = slt[j * SLT + k];
+      if (p.s1_fp32) static_cast<float*>(p.s1)[base + (size_t)k * D + j] = val;
+      else static_cast<__bf16*>(p.s1)[base + (size_t)k * D + j] = (__bf16)val;
+    }
+  }
+  __syncthreads();  // before the next unit overwrites the block
+}
+
+// Fix-up of chunk ch (>= M) of sequence i, head h.
+__device__ __forceinline__ void fix_unit(const Params& p, const PlanView& v, int M, int i, int h, int ch,
+                                         __bf16* ot) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int HD = p.H * D;
+  const int slot = __builtin_amdgcn_readfirstlane(v.soff[i]) + ch / M - 1;
+  int64_t bos, len;
+  if (p.cu) {
+    const int c0 = __builtin_amdgcn_readfirstlane(p.cu[i]);
+    const int c1 = __builtin_amdgcn_readfirstlane(p.cu[i + 1]);
+    bos = c0;
+    len = (int64_t)c1 - c0;
+  } else {
+    bos = (int64_t)i * p.T;
+    len = p.T;
+  }
+  const int64_t tok0 = bos + (int64_t)ch * C;
+  const int64_t rest = len - (int64_t)ch * C;
+  const int valid = rest < C ? (int)rest : C;
+  const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)h * D, valid * HD * 2);
+  const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 4);
+  // loads: Q~ rows of the chunk (rows past `valid` read as zero), S_p^T, O0
+  decltype(__builtin_amdgcn_raw_buffer_load_b128(orsrc, 0, 0, 0)) qv[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
+  const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)slot * p.H + h) * (D * D);
+  bf16x8 sa[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
+  f32x4 z[4][2];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      z[tt][jj] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 4, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);  // all loads of the unit in flight together
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
+    dst[0] = make_uint2(qv[x][0], qv[x][1]);
+    dst[1] = make_uint2(qv[x][2], qv[x][3]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
+      const bf16x8 b = ld2x4(bp, bp + 4);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], b, z[tt][jj]);
+    }
+    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
+          ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+    }
+  }
+  __syncthreads();  // before the next unit's staging
+}
+
+__global__ void __launch_bounds__(TAIL_NT) kda_tail_kernel(Params p, int phase) {
+  extern __shared__ int plan_lds[];
+  __shared__ __attribute__((aligned(16))) float slt[16 * SLT];
+  __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
+  const int N = p.nseq;
   const PlanView v = plan_view(plan_lds, N, 0);
   build_plan(p, v, false);
   // wave-uniform unit values keep every buffer descriptor scalar
   const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
   if (M == kNoSplit) return;
-  const int units = __builtin_amdgcn_readfirstlane(v.hdr[4]);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
-  const int HD = p.H * D;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int i = __builtin_amdgcn_readfirstlane(find_seq(v.uoff, N, u));
-    const int r = u - __builtin_amdgcn_readfirstlane(v.uoff[i]);
-    const int h = r % p.H;
-    const int ch = M + r / p.H;  // chunk of the sequence (past segment 0)
-    const int slot = __builtin_amdgcn_readfirstlane(v.soff[i]) + ch / M - 1;
-    int64_t bos, len;
-    if (p.cu) {
-      const int c0 = __builtin_amdgcn_readfirstlane(p.cu[i]);
-      const int c1 = __builtin_amdgcn_readfirstlane(p.cu[i + 1]);
-      bos = c0;
-      len = (int64_t)c1 - c0;
-    } else {
-      bos = (int64_t)i * p.T;
-      len = p.T;
-    }
-    const int64_t tok0 = bos + (int64_t)ch * C;
-    const int64_t rest = len - (int64_t)ch * C;
-    const int valid = rest < C ? (int)rest : C;
-    const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)h * D, valid * HD * 2);
-    const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 4);
-    // loads: Q~ rows of the chunk (rows past `valid` read as zero), S_p^T, O0
-    decltype(__builtin_amdgcn_raw_buffer_load_b128(orsrc, 0, 0, 0)) qv[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
-    const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)slot * p.H + h) * (D * D);
-    bf16x8 sa[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
-    f32x4 z[4][2];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        z[tt][jj] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 4, 0, 0));
-    __builtin_amdgcn_sched_barrier(0);  // all loads of the unit in flight together
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
-      dst[0] = make_uint2(qv[x][0], qv[x][1]);
-      dst[1] = make_uint2(qv[x][2], qv[x][3]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
-        const bf16x8 b = ld2x4(bp, bp + 4);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], b, z[tt][jj]);
-      }
-      // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-            ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+  if (phase == 0) {
+    const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
+    const int units = nscan + __builtin_amdgcn_readfirstlane(v.hdr[4]);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+      if (u < nscan) {
+        scan_unit(p, v, M, u, slt);
+      } else {
+        const int uu = u - nscan;
+        const int i = __builtin_amdgcn_readfirstlane(find_seq(v.uoff, N, uu));
+        const int r = uu - __builtin_amdgcn_readfirstlane(v.uoff[i]);
+        fix_unit(p, v, M, i, r % p.H, M + r / p.H, ot);
       }
     }
-    __syncthreads();  // before the next unit's staging
+  } else {
+    const int units = __builtin_amdgcn_readfirstlane(v.hdr[5]);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+      const int i = __builtin_amdgcn_readfirstlane(find_seq(v.voff, N, u));
+      const int r = u - __builtin_amdgcn_readfirstlane(v.voff[i]);
+      fix_unit(p, v, M, i, r % p.H, 2 * M + r / p.H, ot);
+    }
   }
 }
 
@@ -1461,10 +1525,10 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;
   const size_t plan_bytes = (size_t)plan_ints(p.nseq, 0, false) * sizeof(int);
-  hipLaunchKernelGGL(kda_scan_kernel, dim3(2 * p.cus), dim3(SCAN_NT), plan_bytes, stream, p);
+  hipLaunchKernelGGL(kda_tail_kernel, dim3(4 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kda_fix_kernel, dim3(8 * p.cus), dim3(FIX_NT), plan_bytes, stream, p);
+  hipLaunchKernelGGL(kda_tail_kernel, dim3(4 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 1);
   return hipGetLastError();
 }
 
