@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA fwd prefill tokens/s (H=32,d=128) at T=8K and 64K varlen; % of roofline"
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_kda_amd", "csrc", "kda_fwd_kernel.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_traffic.json")
-KERNEL_NAME = "kda_fwd_kernel"
+KERNEL_NAME = "kda_fwd call: kda_fwd_kernel + kda_tail_kernel (scan, fix-up)"
 
 
 def log(msg):
