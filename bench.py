@@ -143,6 +143,43 @@ def cpu_baseline(x, heads: int, min_seconds: float = 10.0):
                         f"{len(hs)} of {w.H} heads ({dt:.1f} s); value scaled to all heads"))
 
 
+def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32):
+    """One decode step for N sequences x H heads with fp32 states: HBM-bound on the state."""
+    import torch
+
+    from linear_attention_kda_amd import binding, perfmodel
+    from linear_attention_kda_amd.workloads import random_inputs
+
+    x = random_inputs(N, 1, H, seed=1300, device="cuda", init_state="fp32")
+    one = {k: x[k][:, 0].contiguous() for k in ("q", "k", "v", "g", "beta")}
+    S = x["initial_state"]
+    out = torch.empty(N, H, 128, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        binding.decode(one["q"], one["k"], one["v"], one["g"], one["beta"], S, x["scale"], out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per (sequence, head): state read + write (fp32), q/k/v/o bf16, g fp32, beta
+    nbytes = N * H * (2 * 128 * 128 * 4 + 4 * 128 * 2 + 128 * 4 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode N={N} H={H} fp32 state: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s "
+        f"({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return {"workload": f"decode step N={N} sequences H={H} fp32 state", "unit": "steps/s",
+            "value": 1e3 / ms, "us_per_step": ms * 1e3, "tokens_per_s": N * 1e3 / ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kda_decode_kernel", "algorithmic_bytes": nbytes}}
+
+
 def counter_run(wid: int):
     """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes.
 
@@ -182,6 +219,7 @@ def main():
     ap.add_argument("--secondary", type=int, default=1,
                     help="second workload timed and reported under 'secondary' (-1: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--counters", action="store_true",
                     help="untimed run for hardware-counter passes: a 1 GiB device copy "
@@ -230,6 +268,10 @@ def main():
                      "mfma_frac": r2["mfma_frac"]}
         del x2
 
+    decode = None
+    if not args.no_decode:
+        decode = decode_bench(max(args.steps, 20), args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads of {w.name}")
@@ -263,6 +305,7 @@ def main():
                  "unit": "TFLOP/s", "frac": r["mfma_frac"],
                  "flops_model": "6Td^2+3TCd+TC^2 per head"},
         "secondary": secondary,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -151,6 +151,42 @@ const char* kda_last_error(void);
 kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, int32_t cu_count,
                     int32_t* workgroups, int32_t* value_splits, int64_t* workspace_bytes);
 
+/*
+ * kda_decode — one recurrent step per sequence (decoding), the state updated in
+ * place [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update equation; the
+ * decoding-speed comparison there rests on the state's fixed 128 x 128 size].
+ * For each sequence n < N and head h, with S the state of slot s(n):
+ *   S <- Diag(exp(g)) S;  e = v - S^T k;  S <- S + beta k e^T;  o = scale S^T q
+ * -- the same step kda_fwd takes per token, so a prefill's final state can be
+ * continued here.
+ *
+ *  q, k, v       device, bf16, [N, H, 128] (one token per sequence), 16-byte aligned.
+ *  g             device, fp32, [N, H, 128], 16-byte aligned (log-decay).
+ *  beta          device, fp32, [N, H], 4-byte aligned.
+ *  state         device, [slots, H, 128, 128] (d_k-major), bf16 or fp32 per
+ *                state_dtype, 16-byte aligned; read and overwritten in place
+ *                (bf16 states are rounded to nearest even on store).
+ *  state_indices device, int32, [N], or NULL: the slot s(n) of each sequence
+ *                (NULL: s(n) = n).  A negative entry skips the sequence: neither
+ *                its state nor its output row is touched.  Distinct sequences must
+ *                name distinct slots (not checked).
+ *  out           device, bf16, [N, H, 128], 16-byte aligned.
+ *  stream        hipStream_t (NULL = null stream); asynchronous like kda_fwd.
+ * Memory: no workspace; each (sequence, head) reads and writes its state once.
+ * Errors: as kda_fwd (KDA_ERR_HEAD_DIM, KDA_ERR_SHAPE for N < 0 or H <= 0,
+ * KDA_ERR_DTYPE, KDA_ERR_NULL, KDA_ERR_ALIGN, KDA_ERR_HIP); N = 0 is a no-op.
+ */
+kda_status kda_decode(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, float scale, void* state, int state_dtype,
+                      const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
+                      void* out, void* stream);
+
+/* kda_decode_check — kda_decode's host-side validation, with no launch. */
+kda_status kda_decode_check(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, float scale, const void* state, int state_dtype,
+                            const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
+                            int32_t V, const void* out);
+
 #ifdef __cplusplus
 }
 #endif

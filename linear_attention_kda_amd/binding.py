@@ -58,6 +58,12 @@ def load_library():
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
+        lib.kda_decode.restype = ctypes.c_int
+        lib.kda_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_int, _vp,
+                                   _i32, _i32, _i32, _i32, _vp, _vp]
+        lib.kda_decode_check.restype = ctypes.c_int
+        lib.kda_decode_check.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                         ctypes.c_int, _vp, _i32, _i32, _i32, _i32, _vp]
         lib.kda_plan.restype = ctypes.c_int
         lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
@@ -164,3 +170,63 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
     if st != 0:
         raise KdaError(st, "kda_fwd", _detail(lib, st))
     return (out, final_state) if final_state is not None else out
+
+
+def decode_check(*, N, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, state=0,
+                 state_dtype=KDA_FP32, state_indices=0, scale=1.0) -> int:
+    """Host-only validation of a decode step with raw (never dereferenced) addresses."""
+    lib = load_library()
+    return lib.kda_decode_check(q, k, v, g, beta, scale, state, state_dtype, state_indices, N, H,
+                                K, V, out)
+
+
+def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=None, out=None):
+    """One recurrent KDA step per sequence on the current HIP stream; `state` is updated in place.
+
+    q, k, v: bf16 [N, H, 128] (one token per sequence); g: fp32 [N, H, 128];
+    beta: fp32 [N, H]; state: [slots, H, 128, 128] bf16 or fp32; state_indices:
+    optional int32 [N] slot per sequence (negative: skip); scale defaults to
+    1/sqrt(128).  Returns out (bf16 [N, H, 128]).
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, 128]")
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:2] != q.shape[:2] \
+            or beta.shape != q.shape[:2]:
+        raise ValueError("inconsistent shapes: q, k, g [N,H,K]; v [N,H,V]; beta [N,H]")
+    if state.dim() != 4 or state.shape[1:] != (H, K, V) or not state.is_contiguous() \
+            or state.device != dev:
+        raise ValueError(f"state must be a contiguous [slots, {H}, {K}, {V}] tensor on {dev}")
+    if state_indices is not None:
+        if state_indices.dtype != torch.int32 or state_indices.device != dev \
+                or not state_indices.is_contiguous() or state_indices.shape != (N,):
+            raise TypeError("state_indices must be a contiguous int32 [N] tensor on the same device")
+    elif state.shape[0] < N:
+        raise ValueError("without state_indices the state needs at least N slots")
+    if out is None:
+        out = torch.empty(N, H, V, dtype=torch.bfloat16, device=dev)
+    elif out.shape != (N, H, V) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [N, H, V] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.kda_decode(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(state),
+                            _state_dtype(state), ptr(state_indices), N, H, K, V, ptr(out), stream)
+    if st != 0:
+        raise KdaError(st, "kda_decode", _detail(lib, st))
+    return out

@@ -309,3 +309,74 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
 }
 
 }  // extern "C"
+
+namespace {
+
+kda_status validate_decode(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const void* state, int state_dtype,
+                           const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
+                           int32_t V, const void* out) {
+  if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
+    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: only K = V = 128 is supported", K, V);
+  if (N < 0 || H <= 0) return fail(KDA_ERR_SHAPE, "invalid sizes N=%d H=%d", N, H);
+  if ((int64_t)N * H > (int64_t)INT_MAX)
+    return fail(KDA_ERR_SHAPE, "N*H=%lld too large", (long long)N * H);
+  if (state_dtype != KDA_BF16 && state_dtype != KDA_FP32)
+    return fail(KDA_ERR_DTYPE, "state_dtype=%d is not KDA_BF16 or KDA_FP32", state_dtype);
+  if (N > 0) {
+    if (!q || !k || !v || !g || !beta || !out || !state)
+      return fail(KDA_ERR_NULL, "q, k, v, g, beta, state and out are required when N > 0");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(out, 16) || !aligned(state, 16))
+      return fail(KDA_ERR_ALIGN, "q, k, v, g, out and state must be 16-byte aligned");
+    if (!aligned(beta, 4) || (state_indices && !aligned(state_indices, 4)))
+      return fail(KDA_ERR_ALIGN, "beta and state_indices must be 4-byte aligned");
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_check(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, float scale, const void* state, int state_dtype,
+                            const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
+                            int32_t V, const void* out) {
+  (void)scale;
+  g_last_error.clear();
+  return validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K, V, out);
+}
+
+kda_status kda_decode(const void* q, const void* k, const void* v, const float* g,
+                      const float* beta, float scale, void* state, int state_dtype,
+                      const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
+                      void* out, void* stream) {
+  g_last_error.clear();
+  kda_status st = validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K,
+                                  V, out);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  kda::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = g;
+  p.beta = beta;
+  p.out = static_cast<uint16_t*>(out);
+  p.state = state;
+  p.idx = state_indices;
+  p.scale = scale;
+  p.state_fp32 = state_dtype == KDA_FP32;
+  p.nseq = N;
+  p.H = H;
+  if (log_enabled())
+    std::fprintf(stderr, "[kda] decode: N=%d H=%d state=%s indexed=%d\n", N, H,
+                 p.state_fp32 ? "fp32" : "bf16", state_indices != nullptr);
+  const hipError_t err = kda::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+  return KDA_OK;
+}
+
+}  // extern "C"

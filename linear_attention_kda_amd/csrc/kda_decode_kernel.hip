@@ -1,0 +1,148 @@
+// Recurrent KDA decode step for gfx950 (MI355X): one token per sequence.
+//
+// Per sequence n and head h, with the 128 x 128 state S (S[i][j]: i key channel,
+// j value channel) [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update
+// equation; ch.4 혁신 1, channel-wise gate; ch.2, readout]:
+//   S~  = Diag(exp(g)) S                      (decay first)
+//   e   = v - S~^T k                          (delta-rule error, per value column)
+//   S'  = S~ + beta k e^T                     (rank-1 write)
+//   o   = scale S'^T q = scale (S~^T q + beta (k . q) e)
+// The state is the only sizeable operand (64 KiB fp32 per head), so the step is
+// bound by reading and writing it once; the fixed state size is why decoding
+// cost does not grow with the context [same page, decoding-speed comparison].
+//
+// Mapping: one workgroup of 256 threads per (sequence, head).  Thread t owns
+// value columns 4 (t % 32) .. +3 and key rows t / 32 + 8 r (r < 16): every state
+// row is read by 32 consecutive threads as 512 contiguous bytes.  The two column
+// dot products (S~^T k, S~^T q) are summed over the 8 row groups in LDS; the
+// state stays in registers between its load and its store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;
+constexpr int DNT = 256;   // threads per workgroup
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f_u16(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <bool F32>
+__global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
+  __shared__ float vk[D], vq[D], va[D];   // k, q and exp(g) of the token
+  __shared__ float part[2][8][D];         // per row group: partial S~^T k and S~^T q
+  __shared__ float kq_part[2];
+
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int slot = p.idx != nullptr ? __builtin_amdgcn_readfirstlane(p.idx[n]) : n;
+  if (slot < 0) return;  // padding entry: no state, no output (the same for the whole workgroup)
+  const int t = threadIdx.x, cb = t & 31, rg = t >> 5;
+  const size_t tok = (size_t)n * p.H + h;
+
+  // stage the token's vectors; k . q by the first two waves
+  if (t < D) {
+    const float kf = bf2f_u16(p.k[tok * D + t]);
+    const float qf = bf2f_u16(p.q[tok * D + t]);
+    vk[t] = kf;
+    vq[t] = qf;
+    va[t] = __builtin_amdgcn_exp2f(p.g[tok * D + t] * LOG2E);
+    float s = kf * qf;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if ((t & 63) == 0) kq_part[t >> 6] = s;
+  }
+  // this thread's 16 rows of its 4 columns
+  const size_t sbase = ((size_t)slot * p.H + h) * (size_t)(D * D) + 4 * cb;
+  float4 srow[16];
+  if constexpr (F32) {
+    const float* s = static_cast<const float*>(p.state) + sbase;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) srow[r] = *reinterpret_cast<const float4*>(s + (size_t)(rg + 8 * r) * D);
+  } else {
+    const uint16_t* s = static_cast<const uint16_t*>(p.state) + sbase;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint2 u = *reinterpret_cast<const uint2*>(s + (size_t)(rg + 8 * r) * D);
+      srow[r] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+  }
+  __syncthreads();
+
+  // decay and the partial dot products over this thread's rows
+  float dk[4] = {0.f, 0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = rg + 8 * r;
+    const float a = va[i], ki = vk[i], qi = vq[i];
+    srow[r].x *= a; srow[r].y *= a; srow[r].z *= a; srow[r].w *= a;
+    dk[0] += srow[r].x * ki; dk[1] += srow[r].y * ki; dk[2] += srow[r].z * ki; dk[3] += srow[r].w * ki;
+    dq[0] += srow[r].x * qi; dq[1] += srow[r].y * qi; dq[2] += srow[r].z * qi; dq[3] += srow[r].w * qi;
+  }
+  *reinterpret_cast<float4*>(&part[0][rg][4 * cb]) = make_float4(dk[0], dk[1], dk[2], dk[3]);
+  *reinterpret_cast<float4*>(&part[1][rg][4 * cb]) = make_float4(dq[0], dq[1], dq[2], dq[3]);
+  __syncthreads();
+
+  // column sums, error and output for this thread's 4 columns
+  float sk[4] = {0.f, 0.f, 0.f, 0.f}, sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g8 = 0; g8 < 8; ++g8) {
+    const float4 a = *reinterpret_cast<const float4*>(&part[0][g8][4 * cb]);
+    const float4 b = *reinterpret_cast<const float4*>(&part[1][g8][4 * cb]);
+    sk[0] += a.x; sk[1] += a.y; sk[2] += a.z; sk[3] += a.w;
+    sq[0] += b.x; sq[1] += b.y; sq[2] += b.z; sq[3] += b.w;
+  }
+  const float beta = p.beta[tok];
+  const float kq = kq_part[0] + kq_part[1];
+  float be[4];
+  {
+    const uint2 vu = *reinterpret_cast<const uint2*>(p.v + tok * D + 4 * cb);
+    const float vv[4] = {__uint_as_float(vu.x << 16), __uint_as_float(vu.x & 0xffff0000u),
+                         __uint_as_float(vu.y << 16), __uint_as_float(vu.y & 0xffff0000u)};
+    float o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      be[c] = beta * (vv[c] - sk[c]);
+      o[c] = p.scale * (sq[c] + kq * be[c]);
+    }
+    if (rg == 0)
+      *reinterpret_cast<uint2*>(p.out + tok * D + 4 * cb) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+  }
+
+  // S' = S~ + k (beta e)^T, stored in place
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float ki = vk[rg + 8 * r];
+    srow[r].x += ki * be[0]; srow[r].y += ki * be[1]; srow[r].z += ki * be[2]; srow[r].w += ki * be[3];
+  }
+  if constexpr (F32) {
+    float* s = static_cast<float*>(p.state) + sbase;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) *reinterpret_cast<float4*>(s + (size_t)(rg + 8 * r) * D) = srow[r];
+  } else {
+    uint16_t* s = static_cast<uint16_t*>(p.state) + sbase;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      *reinterpret_cast<uint2*>(s + (size_t)(rg + 8 * r) * D) =
+          make_uint2(pack2_bf16(srow[r].x, srow[r].y), pack2_bf16(srow[r].z, srow[r].w));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.nseq * p.H)), block(DNT);
+  if (p.state_fp32) hipLaunchKernelGGL(kda_decode_kernel<true>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(kda_decode_kernel<false>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kda

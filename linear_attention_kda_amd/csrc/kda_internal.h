@@ -52,6 +52,24 @@ WorkspaceLayout workspace_layout(int64_t rows, int H, int emax);
 // never needs more than cus / H extra segments.
 int workspace_slots(int cus, int H);
 
+// One decode step: one token per sequence, state updated in place.
+struct DecodeParams {
+  const uint16_t* q;      // bf16 [N][H][128]
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;         // fp32 [N][H][128]
+  const float* beta;      // fp32 [N][H]
+  uint16_t* out;          // bf16 [N][H][128]
+  void* state;            // [slots][H][128][128], bf16 or fp32
+  const int32_t* idx;     // [N] state slot of each sequence (negative: skip), or null (slot n)
+  float scale;
+  int state_fp32;
+  int nseq;
+  int H;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
 // the segment scan and output fix-up kernels follow the main kernel.

@@ -33,8 +33,8 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert header_functions() == ["kda_fwd", "kda_fwd_check", "kda_last_error", "kda_plan",
-                                  "kda_status_string"]
+    assert header_functions() == ["kda_decode", "kda_decode_check", "kda_fwd", "kda_fwd_check",
+                                  "kda_last_error", "kda_plan", "kda_status_string"]
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -81,6 +81,38 @@ def test_check_rejections(lib, over, status):
     assert binding.fwd_check(**ok_args(**over)) == status
     assert lib.kda_last_error().decode() != ""
     assert lib.kda_status_string(status).decode() not in ("", "unknown status")
+
+
+def dec_args(**over):
+    a = dict(N=8, H=4, K=128, V=128, q=P, k=P + 0x1000, v=P + 0x2000, g=P + 0x3000,
+             beta=P + 0x4000, out=P + 0x5000, state=P + 0x10000, state_dtype=1)
+    a.update(over)
+    return a
+
+
+def test_decode_check_accepts_valid_arguments(lib):
+    assert binding.decode_check(**dec_args()) == OK
+    assert binding.decode_check(**dec_args(state_dtype=0, state_indices=P + 0x8000)) == OK
+    assert binding.decode_check(**dec_args(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state=0)) == OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(K=64), ERR_HEAD_DIM),
+    (dict(V=256), ERR_HEAD_DIM),
+    (dict(N=-1), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(state_dtype=2), ERR_DTYPE),
+    (dict(state=0), ERR_NULL),
+    (dict(q=0), ERR_NULL),
+    (dict(out=0), ERR_NULL),
+    (dict(v=P + 8), ERR_ALIGN),
+    (dict(state=P + 8), ERR_ALIGN),
+    (dict(beta=P + 2), ERR_ALIGN),
+    (dict(state_indices=P + 2), ERR_ALIGN),
+])
+def test_decode_check_rejections(lib, over, status):
+    assert binding.decode_check(**dec_args(**over)) == status
+    assert lib.kda_last_error().decode() != ""
 
 
 def test_state_dtype_ignored_for_absent_state(lib):
