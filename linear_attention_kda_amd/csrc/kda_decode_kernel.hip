@@ -24,6 +24,9 @@
 namespace kda {
 namespace {
 
+typedef __attribute__((ext_vector_type(4))) float v4f;
+typedef __attribute__((ext_vector_type(2))) unsigned v2u;
+
 constexpr int D = 128;
 constexpr int DNT = 256;   // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
@@ -65,14 +68,18 @@ __global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
   if constexpr (F32) {
     const float* s = static_cast<const float*>(p.state) + sbase;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) srow[r] = *reinterpret_cast<const float4*>(s + (size_t)(rg + 8 * r) * D);
+    for (int r = 0; r < 16; ++r) {
+      // the state is touched once per step: nontemporal loads and stores
+      const v4f t4 = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(s + (size_t)(rg + 8 * r) * D));
+      srow[r] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+    }
   } else {
     const uint16_t* s = static_cast<const uint16_t*>(p.state) + sbase;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const uint2 u = *reinterpret_cast<const uint2*>(s + (size_t)(rg + 8 * r) * D);
-      srow[r] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+      const v2u u = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(s + (size_t)(rg + 8 * r) * D));
+      srow[r] = make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                            __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
     }
   }
   __syncthreads();
@@ -126,13 +133,15 @@ __global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
   if constexpr (F32) {
     float* s = static_cast<float*>(p.state) + sbase;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) *reinterpret_cast<float4*>(s + (size_t)(rg + 8 * r) * D) = srow[r];
+    for (int r = 0; r < 16; ++r)
+      __builtin_nontemporal_store(v4f{srow[r].x, srow[r].y, srow[r].z, srow[r].w},
+                                  reinterpret_cast<v4f*>(s + (size_t)(rg + 8 * r) * D));
   } else {
     uint16_t* s = static_cast<uint16_t*>(p.state) + sbase;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      *reinterpret_cast<uint2*>(s + (size_t)(rg + 8 * r) * D) =
-          make_uint2(pack2_bf16(srow[r].x, srow[r].y), pack2_bf16(srow[r].z, srow[r].w));
+      __builtin_nontemporal_store(v2u{pack2_bf16(srow[r].x, srow[r].y), pack2_bf16(srow[r].z, srow[r].w)},
+                                  reinterpret_cast<v2u*>(s + (size_t)(rg + 8 * r) * D));
   }
 }
 
