@@ -288,7 +288,7 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
     const kda::WorkspaceLayout wl =
         kda::workspace_layout(cu_seqlens ? T : (int64_t)B * T, H, lp.emax);
     p.emax = lp.emax;
-    p.o0 = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o0);
+    p.o0 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.o0);
     p.st = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.st);
     p.sb = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.sb);
   }

@@ -27,6 +27,10 @@
 //  * K*exp(G) = Kr * exp(X_b), Q*exp(G) = Qr * exp(X_b) (both <= 1);
 //  * K*exp(G_last - G) = Kh * exp(G_last - X_{b+1}).
 // F and H are running products of a = exp(g) along the rows.
+// Chunk-level reference: when exp(+-G) stays within 2^+-96 on every channel of a
+// chunk (the common case), the tiles use G itself as the reference instead --
+// rows K*exp(G) and Q*exp(G) (the operands the state products use anyway),
+// column K*exp(-G) -- and no pair needs a per-channel factor.
 //
 // Mapping: one workgroup of 8 waves owns one (sequence, head, value-column slice)
 // and walks its chunks in order as a two-stage pipeline with three barriers per
@@ -37,10 +41,10 @@
 //    accumulator registers for the whole sequence.
 //  * waves 4-7 ("prep waves") prepare chunk c+1: phase A  the inverses of the
 //    diagonal blocks of L for chunk c and the row sums of g for chunk c+1;
-//    phase B  gating (VALU, exp2) into the operand tiles, and the loads of chunk
-//    c+2; phase C  the state-update operand of chunk c+1.
-//  * in phase C all eight waves build the A and M tiles of chunk c+1, one pair of
-//    16-row blocks (both tiles) per wave, the three unscaled pairs on one wave.
+//    phase B  gating (VALU, exp2) into the operand tiles; phase C  V^T and the
+//    state-update operand of chunk c+1, then the loads of chunk c+2.
+//  * in phase C the state waves build the A and M tiles of chunk c+1 from the
+//    gated tiles, two or three pairs of 16-row blocks (both tiles) per wave.
 // Each tile is rewritten only after the phase in which the state waves last read
 // it.  The value-independent per-chunk work is recomputed by every value slice.
 //
@@ -156,14 +160,15 @@ __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_r
 // The A and M tiles of block pair PR = (rb, ib): lane (q4, m16) gets
 // tile[r = 16rb + m16][i = 16ib + 4q4 + t] of sum_c row[r][c] col[i][c].
 // Writes -A off the diagonal, A's diagonal block (fp32, beta-scaled, for the
-// inverse), and scale * M, each masked to its triangle.
-//  * chunk reference (FAST): rows -K exp(G) (A) and scale Q exp(G) (M), the
+// inverse), and M without the attention scale (the output applies it), each
+// masked to its triangle.
+//  * chunk reference (FAST): rows -K exp(G) (A) and Q exp(G) (M), the
 //    tiles the state products use; column K exp(-G).
 //  * block references: rows Kr = K F (A) and Qr = Q F (M), column Kh = K H
 //    scaled per channel by exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1,
 //    where the factor is 1).
 template <int NV, int PR, bool FAST>
-__device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float scale) {
+__device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16) {
   constexpr int rb = PR < 1 ? 0 : PR < 3 ? 1 : PR < 6 ? 2 : 3;
   constexpr int ib = PR - rb * (rb + 1) / 2;
   constexpr bool scaled = !FAST && ib != rb - 1;
@@ -200,13 +205,12 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float s
   }
   const int r = 16 * rb + m16;
   const float br = FAST ? -sm.pbeta[r] : sm.pbeta[r];  // the FAST row operand is -K exp(G)
-  const float sm_ = FAST ? 1.f : scale;                // ... and scale * Q exp(G)
   float va[4], vm[4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int i = 16 * ib + 4 * q4 + tt;
     va[tt] = (i < r) ? br * ta[tt] : 0.f;
-    vm[tt] = (i <= r) ? sm_ * tm[tt] : 0.f;
+    vm[tt] = (i <= r) ? tm[tt] : 0.f;
   }
   if constexpr (ib == rb) {
     *reinterpret_cast<float4*>(&sm.ndt[(rb * 16 + m16) * NS + 4 * q4]) =
@@ -219,25 +223,25 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16, float s
 }
 
 template <int NV, bool FAST>
-__device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m16, float scale) {
+__device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m16) {
   switch (wave) {
     case 0:
-      tile_pair<NV, 0, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 1, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 8, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 0, FAST>(sm, q4, m16);
+      tile_pair<NV, 1, FAST>(sm, q4, m16);
+      tile_pair<NV, 8, FAST>(sm, q4, m16);
       break;
     case 1:
-      tile_pair<NV, 2, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 3, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 4, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 2, FAST>(sm, q4, m16);
+      tile_pair<NV, 3, FAST>(sm, q4, m16);
+      tile_pair<NV, 4, FAST>(sm, q4, m16);
       break;
     case 2:
-      tile_pair<NV, 5, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 6, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 5, FAST>(sm, q4, m16);
+      tile_pair<NV, 6, FAST>(sm, q4, m16);
       break;
     default:
-      tile_pair<NV, 7, FAST>(sm, q4, m16, scale);
-      tile_pair<NV, 9, FAST>(sm, q4, m16, scale);
+      tile_pair<NV, 7, FAST>(sm, q4, m16);
+      tile_pair<NV, 9, FAST>(sm, q4, m16);
       break;
   }
 }
@@ -248,13 +252,13 @@ __device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m
 // pairs of a wave are independent straight-line code, so their loads and
 // products overlap.
 template <int NV>
-__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int m16_, float scale) {
+__device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int m16_) {
   // lane indices through an empty asm: the tile addresses are then formed here on
   // every call instead of being kept live (or spilled) across the whole loop
   int q4 = q4_, m16 = m16_;
   asm volatile("" : "+v"(q4), "+v"(m16));
-  if (__builtin_amdgcn_readfirstlane(sm.chunk_ref)) tile_pairs<NV, true>(sm, wave, q4, m16, scale);
-  else tile_pairs<NV, false>(sm, wave, q4, m16, scale);
+  if (__builtin_amdgcn_readfirstlane(sm.chunk_ref)) tile_pairs<NV, true>(sm, wave, q4, m16);
+  else tile_pairs<NV, false>(sm, wave, q4, m16);
 }
 
 struct Work {
@@ -265,11 +269,10 @@ struct Work {
   int nchunks;
   int s0_mode;     // start state: 0 zero, 1 bf16 at s0, 2 fp32 at s0, 3 identity
   int s1_fp32;     // end state stored as fp32 (else bf16)
-  int o_f32;       // outputs stored as fp32 (else bf16)
   int vzero;       // values read as zero
   const void* s0;  // this (sequence, head)'s 128 x 128 start state
   void* s1;        // where its end state goes, or null
-  void* o;         // output rows, [rows][H][128] (bf16 or fp32)
+  __bf16* o;       // output rows, bf16 [rows][H][128]
   uint16_t* sb;    // also the end state in the fix-up's bf16 operand order, or null
 };
 
@@ -550,14 +553,15 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // Chunk-level reference when exp(+-G) stays within 2^+-96 on every channel
       // (G falls along the chunk for g <= 0, so G_last bounds it); otherwise the
       // 16-row block references.  All prep waves reach the same decision.
-      int span = 0;
+      float xmn = X[1][0], xmx = X[1][0];
 #pragma unroll
       for (int k = 1; k < 5; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x = X[k][e];
-          span = max(span, __float_as_int(x < 0.f ? -x : 4.f * x));
+          xmn = fminf(xmn, X[k][e]);
+          xmx = fmaxf(xmx, X[k][e]);
         }
+      const int span = __float_as_int(fmaxf(-xmn, 4.f * xmx));
       const bool chunk_ref = wave_max(span) < __float_as_int(96.f);
       if (t == 0) sm.chunk_ref = chunk_ref ? 1 : 0;
       if (chunk_ref) {
@@ -599,7 +603,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           kpt_hold[e][0] = make_uint2(kpw[e][0], kpw[e][1]);
           kpt_hold[e][1] = make_uint2(kpw[e][2], kpw[e][3]);
         }
-        // first row first: -K exp(G) and scale * Q exp(G)
+        // first row first: -K exp(G) and Q exp(G)
 #pragma unroll
         for (int r8 = 0; r8 < 8; ++r8) {
           float qf[4], kf[4], kg[4], qg[4];
@@ -611,7 +615,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           for (int e = 0; e < 4; ++e) {
             nE[e] *= ar[e];
             kg[e] = kf[e] * nE[e];
-            qg[e] = -(qf[e] * nE[e]) * p.scale;
+            qg[e] = -(qf[e] * nE[e]);
           }
           const int o = (rg * 8 + r8) * TS + 4 * cg;
           *reinterpret_cast<uint2*>(&sm.kg[o]) = pack4(kg[0], kg[1], kg[2], kg[3]);
@@ -662,15 +666,14 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           Hc[r8][2] = Hc[r8 + 1][2] * av.z; Hc[r8][3] = Hc[r8 + 1][3] * av.w;
         }
         // F_r = F_{r-1} a_r, first row first: row operands K * F, Q * F, the state
-        // operands -K * exp(G) = -K * F * exp(X_b), scale * Q * exp(G), and K'
+        // operands -K * exp(G) = -K * F * exp(X_b), Q * exp(G), and K'
         {
           uint32_t kpw[4][4];  // K' of row pairs (2j, 2j+1), per channel
-          float F[4], nXb[4], sXb[4];
+          float F[4], nXb[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             F[e] = second ? pother[e] : 1.f;  // F of the row before
             nXb[e] = -eXb[e];
-            sXb[e] = p.scale * eXb[e];
           }
 #pragma unroll
           for (int r8 = 0; r8 < 8; ++r8) {
@@ -686,7 +689,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
               kr[e] = kf[e] * F[e];
               qr[e] = qf[e] * F[e];
               kg[e] = kr[e] * nXb[e];   // -K exp(G)
-              qg[e] = qr[e] * sXb[e];   // scale * Q exp(G)
+              qg[e] = qr[e] * eXb[e];   // Q exp(G)
               kp[e] = kf[e] * Hc[r8][e];
             }
             if (r8 & 1) {
@@ -717,10 +720,10 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
     // ---- phase C: state-update operand, exp(G_last) and V^T of chunk pc (the state
     // waves build its A and M tiles meanwhile)
     {
-      // q, k and v of chunk pc are consumed (V^T below): fetch those of the next chunk
+      // q, k and v of chunk pc are consumed once V^T is stored; the next chunk's are
+      // fetched after this phase's stores, which would otherwise wait behind the
+      // issue of the loads
       const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
       // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
@@ -735,7 +738,6 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(pw2[0], pw2[1]);
         *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(pw2[2], pw2[3]);
       }
-      load_v<NV>(R, nsrc, HD, t);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int o = (4 * cg + e) * CS + rg * 8;
@@ -743,6 +745,9 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
         *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
       }
       if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
+      load_v<NV>(R, nsrc, HD, t);
     }
     __syncthreads();  // (C) chunk pc fully published
   }
@@ -806,7 +811,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     f32x4 O[4][JT];   // O^T: row j = 16jt + 4q4 + t, column r = 16rt + m16
 
     // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
-    // (the prep waves store -K exp(G) and scale * Q exp(G))
+    // (the prep waves store -K exp(G) and Q exp(G))
     if (act) {
       bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
 #pragma unroll
@@ -858,12 +863,11 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         // row m16 of the block's inverse, Li[m16][4q4 + e], and z in its D layout are
-        // exactly the operands of a 16x16x16 product; U = Li z from high and low
-        // bf16 parts of both (the low-by-low term dropped), close to fp32
+        // exactly the operands of a 16x16x16 product; U = Li z with z split into
+        // high and low bf16 parts (z carries the cancellation of V - (K exp(G)) S;
+        // Li in bf16 costs no measurable accuracy)
         const float4 lv = *reinterpret_cast<const float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]);
-        const f32x4 lf = f32x4{lv.x, lv.y, lv.z, lv.w};
-        const bf16x4 lh = cvt4(lf);
-        const bf16x4 ll = cvt4(f32x4{lf[0] - bf2f(lh[0]), lf[1] - bf2f(lh[1]), lf[2] - bf2f(lh[2]), lf[3] - bf2f(lh[3])});
+        const bf16x4 lh = cvt4(f32x4{lv.x, lv.y, lv.z, lv.w});
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           f32x4 z = Z[b][jt];
@@ -876,15 +880,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           const bf16x4 zl = cvt4(f32x4{z[0] - bf2f(zh[0]), z[1] - bf2f(zh[1]), z[2] - bf2f(zh[2]), z[3] - bf2f(zh[3])});
           f32x4 u = mfma16(lh, zh, f32x4{0.f, 0.f, 0.f, 0.f});
           u = mfma16(lh, zl, u);
-          u = mfma16(ll, zh, u);
           U[b][jt] = cvt4(u);
         }
       }
       // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor)
-      const int osz = w.o_f32 ? 4 : 2;
-      const auto orsrc = rsrc(static_cast<char*>(w.o) + (tok0 * HD + (int64_t)w.h * D) * osz,
-                              valid * HD * osz);
-      const int ovo = (m16 * HD + jw_base + 4 * q4) * osz;  // lane part of the store offset
+      const auto orsrc = rsrc(w.o + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
+      const int ovo = (m16 * HD + jw_base + 4 * q4) * 2;  // lane part of the store offset
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + m16;
@@ -896,17 +897,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
             o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
           }
-          // the scale is in Q exp(G) and M
-          if (w.o_f32) {
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, o), orsrc,
-                ovo + 64 * jt, 16 * rt * HD * 4, 0);
-          } else {
-            const uint2 ov = pack4(o[0], o[1], o[2], o[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-                ovo + 32 * jt, 16 * rt * HD * 2, 0);
-          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[t] *= p.scale;  // Q exp(G) and M are unscaled
+          const uint2 ov = pack4(o[0], o[1], o[2], o[3]);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
+              ovo + 32 * jt, 16 * rt * HD * 2, 0);
         }
       }
       // S <- Diag(exp(G_last)) S + K'^T U
@@ -931,7 +927,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     __syncthreads();  // (B)
 
     // ---- phase C: A and M tiles of the next chunk
-    if (it + 1 < w.nchunks) build_tiles(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16, p.scale);
+    if (it + 1 < w.nchunks) build_tiles(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16);
     __syncthreads();  // (C)
   }
 
@@ -1241,8 +1237,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
            : static_cast<char*>(p.s1) + ((size_t)n * p.H * (D * D) + hd2) * (p.s1_fp32 ? 4 : 2);
       w.s1_fp32 = p.s1_fp32;
     }
-    w.o = p.out;
-    w.o_f32 = 0;
+    w.o = reinterpret_cast<__bf16*>(p.out);
     w.vzero = 0;
   } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
     const int sp = (kind + 1) >> 1;
@@ -1254,8 +1249,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.s0 = nullptr;
     w.s1 = p.st + ((size_t)((ident ? 1 : 2) * p.emax + slot0 + sp - 1) * p.H) * (D * D) + hd2;
     w.s1_fp32 = 1;
-    w.o = ident ? static_cast<void*>(p.out) : static_cast<void*>(p.o0);
-    w.o_f32 = ident ? 0 : 1;
+    w.o = reinterpret_cast<__bf16*>(ident ? p.out : p.o0);
     w.vzero = ident ? 1 : 0;
     w.sb = nullptr;
   }
@@ -1412,7 +1406,7 @@ __device__ __forceinline__ void fix_unit(const Params& p, const PlanView& v, int
   const int64_t rest = len - (int64_t)ch * C;
   const int valid = rest < C ? (int)rest : C;
   const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)h * D, valid * HD * 2);
-  const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 4);
+  const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 2);
   // loads: Q~ rows of the chunk (rows past `valid` read as zero), S_p^T, O0
   decltype(__builtin_amdgcn_raw_buffer_load_b128(orsrc, 0, 0, 0)) qv[4];
 #pragma unroll
@@ -1425,13 +1419,13 @@ __device__ __forceinline__ void fix_unit(const Params& p, const PlanView& v, int
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
-  f32x4 z[4][2];
+  decltype(__builtin_amdgcn_raw_buffer_load_b64(zrsrc, 0, 0, 0)) zv[4][2];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
-      z[tt][jj] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 4, 0, 0));
+      zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
+          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
   __builtin_amdgcn_sched_barrier(0);  // all loads of the unit in flight together
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -1440,6 +1434,15 @@ __device__ __forceinline__ void fix_unit(const Params& p, const PlanView& v, int
     dst[1] = make_uint2(qv[x][2], qv[x][3]);
   }
   __syncthreads();
+  f32x4 z[4][2];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float f[4];
+      unpack4(make_uint2(zv[tt][jj][0], zv[tt][jj][1]), f);
+      z[tt][jj] = f32x4{f[0], f[1], f[2], f[3]};
+    }
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
@@ -1502,7 +1505,7 @@ WorkspaceLayout workspace_layout(int64_t rows, int H, int emax) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout l;
   l.o0 = 0;
-  l.st = up((size_t)rows * H * D * 4);
+  l.st = up((size_t)rows * H * D * 2);
   l.sb = l.st + up((size_t)3 * emax * H * D * D * 4);
   l.total = l.sb + up((size_t)emax * H * D * D * 2);
   return l;

@@ -36,7 +36,7 @@ struct Params {
   int cus;                // parallel width the segment plan fills (compute units)
   int seg_min;            // shortest sequence, in chunks, that may be split
   int emax;               // segment state slots in the workspace; 0 disables splitting
-  float* o0;              // fp32 [rows][H][128]: outputs of later segments from a zero state
+  uint16_t* o0;           // bf16 [rows][H][128]: outputs of later segments from a zero state
   float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
   uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
 };

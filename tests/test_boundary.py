@@ -121,7 +121,7 @@ def test_state_dtype_ignored_for_absent_state(lib):
 
 def _split_workspace(rows, H, emax):
     up = lambda x: (x + 255) // 256 * 256
-    return up(rows * H * 128 * 4) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
+    return up(rows * H * 128 * 2) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
 
 
 def test_plan_value_split(lib, monkeypatch):
