@@ -114,7 +114,9 @@ bool seq_split_enabled() {
 // batches): does it split them?  Same rule as the kernels' plan.
 bool fixed_length_splits(int64_t N, int64_t c, int64_t H, int64_t cus, int seg_min, int emax) {
   if (c <= seg_min) return false;
-  auto fits = [&](int64_t m) { return H * (N * c + N * (c > m ? c - m : 0)) <= m * cus; };
+  auto fits = [&](int64_t m) {
+    return kda::kSlackDen * H * (N * c + N * (c > m ? c - m : 0)) <= kda::kSlackNum * m * cus;
+  };
   if (!fits(c)) return false;
   int64_t lo = seg_min, hi = c;
   while (lo < hi) {

@@ -89,7 +89,7 @@ struct alignas(16) Smem {
   __bf16 kh[C * TS];    // K * H                       A and M column operand
   __bf16 kpt[D * CS];   // (K * exp(G_last - G))^T     channel-major, state update
   __bf16 vt[NV * CS];   // V^T (this slice's columns)  channel-major
-  __bf16 mm[C * QS];    // M (lower incl. diagonal), zero elsewhere
+  __bf16 mm[C * QS];    // M (lower incl. diagonal; blocks above the diagonal unused)
   __bf16 an[C * QS];    // -A on the off-diagonal 16x16 blocks
   float li[C * LS];     // inverses of the 4 diagonal blocks of L = I + A (fp32)
   float ndt[4 * 16 * NS];  // diagonal 16x16 blocks of A (beta-scaled, fp32): [b][r][i]
@@ -895,7 +895,10 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 #pragma unroll
           for (int ks = 0; ks <= (rt >> 1); ++ks) {
             const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
-            o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
+            if ((rt & 1) == 0 && ks == (rt >> 1))  // M block (rt, rt + 1) is zero: 16-wide k
+              o = mfma16(U[2 * ks][jt], ld4(rowp), o);
+            else
+              o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) o[t] *= p.scale;  // Q exp(G) and M are unscaled
@@ -983,9 +986,10 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 //
 // M is the shortest segment for which the whole job -- every chunk once, plus
 // once more for each chunk past a sequence's first segment -- spread over the
-// compute units takes at most M chunk-steps; the longest task then no longer
-// bounds the run.  Every workgroup of the three kernels computes the same plan
-// from the sequence lengths (integer arithmetic only).
+// compute units takes at most 95% of M chunk-steps (kSlackNum / kSlackDen); the
+// longest task then bounds the run only by that margin.  Every workgroup of
+// the three kernels computes the same plan from the sequence lengths (integer
+// arithmetic only).
 
 constexpr int kNoSplit = 0x7fffffff;
 
@@ -1064,7 +1068,7 @@ __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
       int extra = 0;
       for (int i = lane; i < N; i += 64) extra += max(0, v.lens[i] - m);
       extra = wave_sum(extra);
-      return (long long)p.H * ((long long)sum + extra) <= (long long)m * p.cus;
+      return (long long)kSlackDen * p.H * ((long long)sum + extra) <= (long long)kSlackNum * m * p.cus;
     };
     int M = kNoSplit;
     if (p.emax > 0 && mx > p.seg_min && fits(mx)) {
@@ -1255,13 +1259,6 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   }
   w.nchunks = (int)((w.len + C - 1) / C);
 
-  // constant zeros: M blocks above the diagonal that the 32-wide k-steps touch
-  for (int x = tid; x < 16 * 16; x += NT) {
-    const int r = x >> 4, i = x & 15;
-    sm.mm[r * QS + 16 + i] = (__bf16)0.f;         // block (0, 1)
-    sm.mm[(32 + r) * QS + 48 + i] = (__bf16)0.f;  // block (2, 3)
-  }
-
   // Both roles execute the same barrier sequence; the branch is uniform per wave.
   if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w);
   else prep_loop<NV>(sm, p, w);
@@ -1384,87 +1381,148 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
   __syncthreads();  // before the next unit overwrites the block
 }
 
-// Fix-up of chunk ch (>= M) of sequence i, head h.
-__device__ __forceinline__ void fix_unit(const Params& p, const PlanView& v, int M, int i, int h, int ch,
-                                         __bf16* ot) {
+// Fix-up units: one per (sequence, head, chunk past the first segment), numbered
+// within a sequence by head, then chunk, so that consecutive units share the
+// segment start state S_p.  Segment-1 units (seg0 = 1) cover chunks M ..
+// M + min(c - M, M) - 1, later-segment units (seg0 = 2) chunks 2M .. c - 1.
+struct FixUnit {
+  int i, h, ch, slot, valid;
+  int64_t tok0;
+};
+
+__device__ __forceinline__ FixUnit fix_decode(const Params& p, const PlanView& v, int M, const int* off,
+                                              int seg0, int u) {
+  FixUnit f;
+  f.i = __builtin_amdgcn_readfirstlane(find_seq(off, p.nseq, u));
+  const int r = u - __builtin_amdgcn_readfirstlane(off[f.i]);
+  const int c = __builtin_amdgcn_readfirstlane(v.lens[f.i]);
+  const int n = seg0 == 1 ? min(c - M, M) : c - 2 * M;  // chunks per head in this range
+  f.h = r / n;
+  f.ch = seg0 * M + r % n;
+  f.slot = __builtin_amdgcn_readfirstlane(v.soff[f.i]) + f.ch / M - 1;
+  int64_t bos, len;
+  if (p.cu) {
+    const int c0 = __builtin_amdgcn_readfirstlane(p.cu[f.i]);
+    const int c1 = __builtin_amdgcn_readfirstlane(p.cu[f.i + 1]);
+    bos = c0;
+    len = (int64_t)c1 - c0;
+  } else {
+    bos = (int64_t)f.i * p.T;
+    len = p.T;
+  }
+  f.tok0 = bos + (int64_t)f.ch * C;
+  const int64_t rest = len - (int64_t)f.ch * C;
+  f.valid = rest < C ? (int)rest : C;
+  return f;
+}
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// Q~ rows of the unit's chunk (rows past `valid` read as zero) and its O0 entries.
+struct FixLoads {
+  u32x4 qv[4];
+  u32x2 zv[4][2];
+};
+
+__device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, FixLoads& L) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
   const int HD = p.H * D;
-  const int slot = __builtin_amdgcn_readfirstlane(v.soff[i]) + ch / M - 1;
-  int64_t bos, len;
-  if (p.cu) {
-    const int c0 = __builtin_amdgcn_readfirstlane(p.cu[i]);
-    const int c1 = __builtin_amdgcn_readfirstlane(p.cu[i + 1]);
-    bos = c0;
-    len = (int64_t)c1 - c0;
-  } else {
-    bos = (int64_t)i * p.T;
-    len = p.T;
-  }
-  const int64_t tok0 = bos + (int64_t)ch * C;
-  const int64_t rest = len - (int64_t)ch * C;
-  const int valid = rest < C ? (int)rest : C;
-  const auto orsrc = rsrc(p.out + tok0 * HD + (int64_t)h * D, valid * HD * 2);
-  const auto zrsrc = rsrc(p.o0 + tok0 * HD + (int64_t)h * D, valid * HD * 2);
-  // loads: Q~ rows of the chunk (rows past `valid` read as zero), S_p^T, O0
-  decltype(__builtin_amdgcn_raw_buffer_load_b128(orsrc, 0, 0, 0)) qv[4];
+  const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
+  const auto zrsrc = rsrc(p.o0 + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
 #pragma unroll
   for (int x = 0; x < 4; ++x)
-    qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
-  const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)slot * p.H + h) * (D * D);
-  bf16x8 sa[4][2];
+    L.qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      L.zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
+          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+}
+
+// S_p^T as the products' A operand (bf16, the order the segment's first run wrote).
+__device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f, bf16x8 (&sa)[4][2]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)f.slot * p.H + f.h) * (D * D);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
-  decltype(__builtin_amdgcn_raw_buffer_load_b64(zrsrc, 0, 0, 0)) zv[4][2];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
-          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);  // all loads of the unit in flight together
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
-    dst[0] = make_uint2(qv[x][0], qv[x][1]);
-    dst[1] = make_uint2(qv[x][2], qv[x][3]);
-  }
-  __syncthreads();
-  f32x4 z[4][2];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      float f[4];
-      unpack4(make_uint2(zv[tt][jj][0], zv[tt][jj][1]), f);
-      z[tt][jj] = f32x4{f[0], f[1], f[2], f[3]};
-    }
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
-      const bf16x8 b = ld2x4(bp, bp + 4);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], b, z[tt][jj]);
-    }
-    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
-      __builtin_amdgcn_raw_buffer_store_b64(
-          __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-          ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
-    }
-  }
-  __syncthreads();  // before the next unit's staging
 }
 
-__global__ void __launch_bounds__(TAIL_NT) kda_tail_kernel(Params p, int phase) {
+// This workgroup's contiguous share of `units` fix-up units: o = O0 + S_p^T Q~ for
+// every row of each unit's chunk.  The next unit's loads are in flight while the
+// current one is multiplied; S_p is reloaded only when the segment or head changes.
+__device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0, int units,
+                          __bf16* ot) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int u_lo = (int)((int64_t)units * b / G), u_hi = (int)((int64_t)units * (b + 1) / G);
+  if (u_lo >= u_hi) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int HD = p.H * D;
+  FixUnit cur = fix_decode(p, v, M, off, seg0, u_lo);
+  FixLoads L;
+  fix_issue(p, cur, L);
+  bf16x8 sa[4][2];
+  fix_state(p, cur, sa);
+  for (int u = u_lo; u < u_hi; ++u) {
+    // stage Q~ of the current unit (its B operand order) in LDS
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
+      dst[0] = make_uint2(L.qv[x][0], L.qv[x][1]);
+      dst[1] = make_uint2(L.qv[x][2], L.qv[x][3]);
+    }
+    f32x4 z[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float f[4];
+        unpack4(make_uint2(L.zv[tt][jj][0], L.zv[tt][jj][1]), f);
+        z[tt][jj] = f32x4{f[0], f[1], f[2], f[3]};
+      }
+    const FixUnit f = cur;
+    const bool more = u + 1 < u_hi;
+    if (more) {
+      cur = fix_decode(p, v, M, off, seg0, u + 1);
+      fix_issue(p, cur, L);  // the next unit's loads fly during this unit's products
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
+        const bf16x8 bb = ld2x4(bp, bp + 4);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], bb, z[tt][jj]);
+      }
+    }
+    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
+    const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, ov), orsrc,
+            ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+      }
+    if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state(p, cur, sa);
+    __syncthreads();  // before the next unit's staging
+  }
+}
+
+__global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phase) {
   extern __shared__ int plan_lds[];
   __shared__ __attribute__((aligned(16))) float slt[16 * SLT];
   __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
@@ -1475,25 +1533,13 @@ __global__ void __launch_bounds__(TAIL_NT) kda_tail_kernel(Params p, int phase) 
   const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
   if (M == kNoSplit) return;
   if (phase == 0) {
+    // scan units spread over the grid, then every workgroup's share of the
+    // segment-1 fix-ups (they need only S_1, written by the main kernel)
     const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
-    const int units = nscan + __builtin_amdgcn_readfirstlane(v.hdr[4]);
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-      if (u < nscan) {
-        scan_unit(p, v, M, u, slt);
-      } else {
-        const int uu = u - nscan;
-        const int i = __builtin_amdgcn_readfirstlane(find_seq(v.uoff, N, uu));
-        const int r = uu - __builtin_amdgcn_readfirstlane(v.uoff[i]);
-        fix_unit(p, v, M, i, r % p.H, M + r / p.H, ot);
-      }
-    }
+    for (int u = blockIdx.x; u < nscan; u += gridDim.x) scan_unit(p, v, M, u, slt);
+    fix_range(p, v, M, v.uoff, 1, __builtin_amdgcn_readfirstlane(v.hdr[4]), ot);
   } else {
-    const int units = __builtin_amdgcn_readfirstlane(v.hdr[5]);
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-      const int i = __builtin_amdgcn_readfirstlane(find_seq(v.voff, N, u));
-      const int r = u - __builtin_amdgcn_readfirstlane(v.voff[i]);
-      fix_unit(p, v, M, i, r % p.H, 2 * M + r / p.H, ot);
-    }
+    fix_range(p, v, M, v.voff, 2, __builtin_amdgcn_readfirstlane(v.hdr[5]), ot);
   }
 }
 
@@ -1528,10 +1574,10 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;
   const size_t plan_bytes = (size_t)plan_ints(p.nseq, 0, false) * sizeof(int);
-  hipLaunchKernelGGL(kda_tail_kernel, dim3(4 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 0);
+  hipLaunchKernelGGL(kda_tail_kernel, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kda_tail_kernel, dim3(4 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 1);
+  hipLaunchKernelGGL(kda_tail_kernel, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 1);
   return hipGetLastError();
 }
 

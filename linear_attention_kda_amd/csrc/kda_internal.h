@@ -15,6 +15,12 @@ constexpr int kSortLimit = 1024;
 
 // Shortest sequence (in 64-token chunks) that may be split into segments.
 constexpr int kSegMinDefault = 8;
+// Segment length rule: the shortest M for which H * (chunks + chunks past the
+// first segment) <= kSlackNum / kSlackDen * M * compute units.  The slack keeps
+// a little imbalance rather than splitting more: each split chunk costs an
+// extra identity-start run and a fix-up, while the last tasks of a nearly
+// balanced run finish with most of the device idle (and its power budget free).
+constexpr int kSlackNum = 19, kSlackDen = 20;
 
 struct Params {
   const uint16_t* q;      // bf16 [rows][H][128]
