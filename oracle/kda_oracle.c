@@ -214,6 +214,76 @@ int kda_oracle_fwd_literal(const double* q, const double* k, const double* v, co
   return 0;
 }
 
+/*
+ * Gated DeltaNet (scalar gate), the special case KDA generalises:
+ *   alpha_t = exp(g_t)            ONE decay per token and head
+ *   S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale * S_t^T q_t
+ *       [core.today "Kimi Linear 특집", ch.4 혁신 1 (GDN forgets the whole state
+ *        with one scalar; KDA makes it a per-channel vector); hnts03 "논문 리뷰:
+ *        Kimi Delta Attention", section "Kimi Delta Attention" (previous state times
+ *        a scalar decay)]
+ * The printed KDA update with Diag(alpha_t) = alpha_t I is exactly this form.
+ * Evaluated as: S~ = alpha S (every entry scaled by the same number);
+ * e = v - S~^T k; S = S~ + beta k e^T; o = scale S^T q.
+ * Layout as kda_oracle_fwd except g: [rows][H] (one gate per token and head).
+ * Every (sequence, head) pair is an independent task; nthreads > 0 caps the
+ * OpenMP threads.
+ */
+int gdn_oracle_fwd(const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, double scale, const double* S0, double* S_out, double* o,
+                   const int64_t* seq_start, const int64_t* seq_len, int64_t N, int64_t H,
+                   int64_t DK, int64_t DV, int nthreads) {
+  if (check_sizes(N, H, DK, DV, seq_len)) return -1;
+  const int64_t sdim = DK * DV;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)sdim);
+    double* e = (double*)malloc(sizeof(double) * (size_t)DV);
+    if (!S || !e) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < N * H; ++task) {
+        const int64_t n = task / H, h = task % H;
+        if (S0) memcpy(S, S0 + (n * H + h) * sdim, sizeof(double) * (size_t)sdim);
+        else memset(S, 0, sizeof(double) * (size_t)sdim);
+        for (int64_t t = seq_start[n]; t < seq_start[n] + seq_len[n]; ++t) {
+          const double* qt = q + (t * H + h) * DK;
+          const double* kt = k + (t * H + h) * DK;
+          const double* vt = v + (t * H + h) * DV;
+          const double alpha = exp(g[t * H + h]);
+          const double bt = beta[t * H + h];
+          double* ot = o + (t * H + h) * DV;
+          for (int64_t x = 0; x < sdim; ++x) S[x] *= alpha;
+          for (int64_t j = 0; j < DV; ++j) {
+            double acc = vt[j];
+            for (int64_t i = 0; i < DK; ++i) acc -= S[i * DV + j] * kt[i];
+            e[j] = acc;
+          }
+          for (int64_t i = 0; i < DK; ++i)
+            for (int64_t j = 0; j < DV; ++j) S[i * DV + j] += bt * kt[i] * e[j];
+          for (int64_t j = 0; j < DV; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < DK; ++i) acc += S[i * DV + j] * qt[i];
+            ot[j] = scale * acc;
+          }
+        }
+        if (S_out) memcpy(S_out + (n * H + h) * sdim, S, sizeof(double) * (size_t)sdim);
+      }
+    }
+    free(S);
+    free(e);
+  }
+  return failed ? -2 : 0;
+}
+
 int kda_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -57,6 +57,10 @@ def _load():
         lib.kda_oracle_fwd_literal.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp,
                                                _dp, _ip, _ip, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int64, ctypes.c_int64]
+        lib.gdn_oracle_fwd.restype = ctypes.c_int
+        lib.gdn_oracle_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp,
+                                       _ip, _ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -139,4 +143,33 @@ def fwd(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=None, hea
                                 0 if hs is None else hs.shape[0], int(col_block), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"kda oracle failed with code {rc}")
+    return o, S_out
+
+
+def gdn_fwd(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=None, nthreads: int = 0):
+    """Scalar-gate (Gated DeltaNet) oracle: one decay exp(g) per token and head.
+
+    q, k: [B, T, H, DK]; v: [B, T, H, DV]; g, beta: [B, T, H]; initial_state:
+    [N, H, DK, DV] or None.  Sequences as in fwd().  Returns (o, final_state)
+    in float64.  The recurrence is documented at gdn_oracle_fwd in kda_oracle.c.
+    """
+    lib = _load()
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or g.shape != q.shape[:3] \
+            or beta.shape != q.shape[:3]:
+        raise ValueError("inconsistent input shapes")
+    start, length = _sequences(B, T, cu_seqlens)
+    N = start.shape[0]
+    S0 = None if initial_state is None else _f64(initial_state)
+    if S0 is not None and S0.shape != (N, H, DK, DV):
+        raise ValueError(f"initial_state must be {(N, H, DK, DV)}, got {S0.shape}")
+    o = np.zeros((B, T, H, DV), dtype=np.float64)
+    S_out = np.zeros((N, H, DK, DV), dtype=np.float64)
+    rc = lib.gdn_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                            _ptr(S0), _ptr(S_out), _ptr(o), start.ctypes.data_as(_ip),
+                            length.ctypes.data_as(_ip), N, H, DK, DV, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"gdn oracle failed with code {rc}")
     return o, S_out

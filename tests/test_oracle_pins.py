@@ -315,3 +315,69 @@ def test_column_block_tasks_are_bitwise_identical():
         o2, S2 = oracle.fwd(q, k, v, g, beta, SCALE, S0, col_block=cb)
         np.testing.assert_array_equal(o2, o)
         np.testing.assert_array_equal(S2, S)
+
+
+# --- scalar-gate (Gated DeltaNet) oracle ----------------------------------------
+
+def rnd_scalar_gate(seed, B=1, T=24, H=2, DK=8, DV=6):
+    q, k, v, _, beta, S0 = rnd(seed, B=B, T=T, H=H, DK=DK, DV=DV)
+    gamma = -np.random.default_rng(seed + 1000).uniform(0.01, 0.4, (B, T, H))
+    return q, k, v, gamma, beta, S0
+
+
+def test_gdn_literal_scalar_transition():
+    """Brute force in numpy: S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+    o_t = scale S_t^T q_t, with one scalar decay per token and head
+    [core.today "Kimi Linear 특집", ch.4 혁신 1; hnts03 "논문 리뷰: Kimi Delta
+    Attention", section "Kimi Delta Attention"]."""
+    T, H, DK, DV = 15, 2, 5, 4
+    q, k, v, gamma, beta, S0 = rnd_scalar_gate(31, T=T, H=H, DK=DK, DV=DV)
+    o, S = oracle.gdn_fwd(q, k, v, gamma, beta, SCALE, S0)
+    for h in range(H):
+        St = S0[0, h].copy()
+        for t in range(T):
+            kk = k[0, t, h]
+            A = math.exp(gamma[0, t, h]) * (np.eye(DK) - beta[0, t, h] * np.outer(kk, kk))
+            St = A @ St + beta[0, t, h] * np.outer(kk, v[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], SCALE * St.T @ q[0, t, h], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S[0, h], St, rtol=1e-12, atol=1e-13)
+
+
+def test_gdn_is_kda_with_the_gate_repeated_over_channels():
+    """The per-channel gate of KDA generalises the scalar one: the KDA oracle fed
+    the same gate on every channel gives the scalar-gate result (the two oracle
+    functions are separate loops)."""
+    q, k, v, gamma, beta, S0 = rnd_scalar_gate(32, B=2, T=21, H=3, DK=8, DV=6)
+    o1, S1 = oracle.gdn_fwd(q, k, v, gamma, beta, SCALE, S0)
+    o2, S2 = oracle.fwd(q, k, v, np.repeat(gamma[..., None], 8, axis=-1), beta, SCALE, S0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S1, S2, rtol=1e-12, atol=1e-14)
+
+
+def test_gdn_beta_zero_is_pure_scalar_decay():
+    """beta = 0: o_t = scale exp(sum_{s<=t} g_s) S0^T q_t and S_T = exp(sum g) S0."""
+    T, H, DK, DV = 17, 2, 6, 5
+    q, k, v, gamma, beta, S0 = rnd_scalar_gate(33, T=T, H=H, DK=DK, DV=DV)
+    beta[:] = 0.0
+    o, S = oracle.gdn_fwd(q, k, v, gamma, beta, SCALE, S0)
+    P = np.exp(np.cumsum(gamma, axis=1))
+    for h in range(H):
+        for t in range(T):
+            np.testing.assert_allclose(o[0, t, h], SCALE * P[0, t, h] * (S0[0, h].T @ q[0, t, h]),
+                                       rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(S[0, h], P[0, -1, h] * S0[0, h], rtol=1e-12, atol=1e-14)
+
+
+def test_gdn_varlen_packing_equals_separate_runs():
+    lens = [5, 0, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, gamma, beta, _ = rnd_scalar_gate(34, T=T, H=2)
+    S0 = 0.2 * np.random.default_rng(35).standard_normal((len(lens), 2, 8, 6))
+    o, S = oracle.gdn_fwd(q, k, v, gamma, beta, SCALE, S0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        on, Sn = oracle.gdn_fwd(q[:, sl], k[:, sl], v[:, sl], gamma[:, sl], beta[:, sl], SCALE,
+                                S0[n:n + 1])
+        np.testing.assert_allclose(o[:, sl], on, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(S[n], Sn[0], rtol=1e-13, atol=1e-15)
