@@ -187,6 +187,49 @@ kda_status kda_decode_check(const void* q, const void* k, const void* v, const f
                             const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
                             int32_t V, const void* out);
 
+/*
+ * kda_gdn_fwd — the scalar-gate special case (Gated DeltaNet): one decay per
+ * token and head instead of one per key channel [core.today "Kimi Linear 특집",
+ * ch.4 혁신 1: GDN forgets the whole state with a single scalar, KDA with a
+ * per-channel vector; hnts03 "논문 리뷰: Kimi Delta Attention", section "Kimi
+ * Delta Attention"].  Per token:
+ *   S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale S_t^T q_t
+ * which is kda_fwd's update with Diag(alpha_t) = exp(g_t) I.
+ *  g          device, fp32, [B, T, H] (one value per token and head), 4-byte
+ *             aligned; range limit as kda_fwd's with the same g on every channel.
+ * Every other argument, the layouts, the workspace, asynchrony and the status
+ * codes are those of kda_fwd (the same kernels run; only the gate load differs,
+ * and it reads 4 bytes per token and head instead of 512).
+ */
+kda_status kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float scale, const void* initial_state,
+                       int initial_dtype, void* final_state, int final_dtype,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                       int32_t H, int32_t K, int32_t V, void* out, void* stream);
+
+/* kda_gdn_fwd_check — kda_gdn_fwd's host-side validation, with no launch. */
+kda_status kda_gdn_fwd_check(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float scale, const void* initial_state,
+                             int initial_dtype, const void* final_state, int final_dtype,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                             int32_t H, int32_t K, int32_t V, const void* out);
+
+/*
+ * kda_gdn_decode — kda_decode with the scalar gate: g is fp32 [N, H], 4-byte
+ * aligned, and S <- exp(g) S is the decay.  Arguments, in-place state update,
+ * slot indices and errors as kda_decode.
+ */
+kda_status kda_gdn_decode(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, float scale, void* state, int state_dtype,
+                          const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
+                          void* out, void* stream);
+
+/* kda_gdn_decode_check — kda_gdn_decode's host-side validation, with no launch. */
+kda_status kda_gdn_decode_check(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float scale, const void* state, int state_dtype,
+                                const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
+                                int32_t V, const void* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,11 @@ def load_library():
         lib.kda_decode_check.restype = ctypes.c_int
         lib.kda_decode_check.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                          ctypes.c_int, _vp, _i32, _i32, _i32, _i32, _vp]
+        for name in ("kda_gdn_fwd", "kda_gdn_fwd_check", "kda_gdn_decode", "kda_gdn_decode_check"):
+            base = getattr(lib, name.replace("gdn_", ""))
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = base.argtypes
         lib.kda_plan.restype = ctypes.c_int
         lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
@@ -110,6 +115,15 @@ def fwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, initial_s
                              final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out)
 
 
+def gdn_fwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, initial_state=0,
+                  initial_dtype=KDA_FP32, final_state=0, final_dtype=KDA_FP32, cu_seqlens=0,
+                  num_seqs=0, scale=1.0) -> int:
+    """Host-only validation of the scalar-gate forward (g is [B, T, H])."""
+    lib = load_library()
+    return lib.kda_gdn_fwd_check(q, k, v, g, beta, scale, initial_state, initial_dtype,
+                                 final_state, final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out)
+
+
 def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_state=None,
         cu_seqlens=None, out=None, output_final_state: bool = False):
     """KDA chunkwise forward pass on the current HIP stream.
@@ -122,6 +136,20 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
     final_state tensor, one is allocated (dtype of initial_state, else fp32).
     Returns out, or (out, final_state) when a final state is produced.
     """
+    return _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
+                output_final_state, scalar_gate=False)
+
+
+def gdn_fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_state=None,
+            cu_seqlens=None, out=None, output_final_state: bool = False):
+    """Scalar-gate (Gated DeltaNet) forward: as fwd() with g fp32 [B, T, H], one
+    log-decay per token and head."""
+    return _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
+                output_final_state, scalar_gate=True)
+
+
+def _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
+         output_final_state, scalar_gate):
     import torch
     lib = load_library()
     if q.dim() != 4:
@@ -138,9 +166,11 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
         if t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on {dev}")
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+    g_shape = q.shape[:3] if scalar_gate else q.shape
+    if k.shape != q.shape or g.shape != g_shape or v.shape[:3] != q.shape[:3] \
             or beta.shape != q.shape[:3]:
-        raise ValueError("inconsistent shapes: q, k, g [B,T,H,K]; v [B,T,H,V]; beta [B,T,H]")
+        raise ValueError("inconsistent shapes: q, k [B,T,H,K]; g [B,T,H,K] ([B,T,H] for the "
+                         "scalar gate); v [B,T,H,V]; beta [B,T,H]")
     num_seqs = 0
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev \
@@ -162,13 +192,14 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
         scale = 1.0 / math.sqrt(K)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     stream = torch.cuda.current_stream(dev).cuda_stream
+    entry = lib.kda_gdn_fwd if scalar_gate else lib.kda_fwd
     with torch.cuda.device(dev):
-        st = lib.kda_fwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale),
-                         ptr(initial_state), _state_dtype(initial_state), ptr(final_state),
-                         _state_dtype(final_state), ptr(cu_seqlens), num_seqs, B, T, H, K, V,
-                         ptr(out), stream)
+        st = entry(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale),
+                   ptr(initial_state), _state_dtype(initial_state), ptr(final_state),
+                   _state_dtype(final_state), ptr(cu_seqlens), num_seqs, B, T, H, K, V,
+                   ptr(out), stream)
     if st != 0:
-        raise KdaError(st, "kda_fwd", _detail(lib, st))
+        raise KdaError(st, "kda_gdn_fwd" if scalar_gate else "kda_fwd", _detail(lib, st))
     return (out, final_state) if final_state is not None else out
 
 
@@ -180,6 +211,14 @@ def decode_check(*, N, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, state=0,
                                 K, V, out)
 
 
+def gdn_decode_check(*, N, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, state=0,
+                     state_dtype=KDA_FP32, state_indices=0, scale=1.0) -> int:
+    """Host-only validation of a scalar-gate decode step (g is [N, H])."""
+    lib = load_library()
+    return lib.kda_gdn_decode_check(q, k, v, g, beta, scale, state, state_dtype, state_indices,
+                                    N, H, K, V, out)
+
+
 def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=None, out=None):
     """One recurrent KDA step per sequence on the current HIP stream; `state` is updated in place.
 
@@ -188,6 +227,15 @@ def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=No
     optional int32 [N] slot per sequence (negative: skip); scale defaults to
     1/sqrt(128).  Returns out (bf16 [N, H, 128]).
     """
+    return _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate=False)
+
+
+def gdn_decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=None, out=None):
+    """Scalar-gate decode step: as decode() with g fp32 [N, H]."""
+    return _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate=True)
+
+
+def _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate):
     import torch
     lib = load_library()
     if q.dim() != 3:
@@ -204,9 +252,11 @@ def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=No
             raise TypeError(f"{name} must be {dt}, got {t.dtype}")
         if t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on {dev}")
-    if k.shape != q.shape or g.shape != q.shape or v.shape[:2] != q.shape[:2] \
+    g_shape = q.shape[:2] if scalar_gate else q.shape
+    if k.shape != q.shape or g.shape != g_shape or v.shape[:2] != q.shape[:2] \
             or beta.shape != q.shape[:2]:
-        raise ValueError("inconsistent shapes: q, k, g [N,H,K]; v [N,H,V]; beta [N,H]")
+        raise ValueError("inconsistent shapes: q, k [N,H,K]; g [N,H,K] ([N,H] for the scalar "
+                         "gate); v [N,H,V]; beta [N,H]")
     if state.dim() != 4 or state.shape[1:] != (H, K, V) or not state.is_contiguous() \
             or state.device != dev:
         raise ValueError(f"state must be a contiguous [slots, {H}, {K}, {V}] tensor on {dev}")
@@ -224,9 +274,10 @@ def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=No
         scale = 1.0 / math.sqrt(K)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     stream = torch.cuda.current_stream(dev).cuda_stream
+    entry = lib.kda_gdn_decode if scalar_gate else lib.kda_decode
     with torch.cuda.device(dev):
-        st = lib.kda_decode(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(state),
-                            _state_dtype(state), ptr(state_indices), N, H, K, V, ptr(out), stream)
+        st = entry(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale), ptr(state),
+                   _state_dtype(state), ptr(state_indices), N, H, K, V, ptr(out), stream)
     if st != 0:
-        raise KdaError(st, "kda_decode", _detail(lib, st))
+        raise KdaError(st, "kda_gdn_decode" if scalar_gate else "kda_decode", _detail(lib, st))
     return out

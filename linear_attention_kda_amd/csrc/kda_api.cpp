@@ -45,7 +45,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 kda_status validate(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     const void* s0, int s0_dtype, const void* s1, int s1_dtype, const int32_t* cu,
                     int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                    const void* out, int32_t* n_out) {
+                    const void* out, int32_t* n_out, bool g_scalar) {
   if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
     return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: only K = V = 128 is supported", K, V);
   if (B <= 0 || H <= 0 || T < 0)
@@ -71,9 +71,10 @@ kda_status validate(const void* q, const void* k, const void* v, const float* g,
   if (T > 0) {
     if (!q || !k || !v || !g || !beta || !out)
       return fail(KDA_ERR_NULL, "q, k, v, g, beta and out are required when T > 0");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
-        !aligned(out, 16))
-      return fail(KDA_ERR_ALIGN, "q, k, v, g and out must be 16-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+      return fail(KDA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(g, g_scalar ? 4 : 16))
+      return fail(KDA_ERR_ALIGN, "g must be %d-byte aligned", g_scalar ? 4 : 16);
     if (!aligned(beta, 4)) return fail(KDA_ERR_ALIGN, "beta must be 4-byte aligned");
   }
   if ((s0 && !aligned(s0, 16)) || (s1 && !aligned(s1, 16)))
@@ -196,63 +197,16 @@ hipError_t workspace_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* kda_status_string(int status) {
-  switch (status) {
-    case KDA_OK: return "ok";
-    case KDA_ERR_NULL: return "required pointer is NULL";
-    case KDA_ERR_HEAD_DIM: return "head dimension must be 128";
-    case KDA_ERR_VARLEN_BATCH: return "cu_seqlens requires B = 1";
-    case KDA_ERR_STATE_DTYPE: return "initial and final state dtypes differ";
-    case KDA_ERR_DTYPE: return "invalid dtype";
-    case KDA_ERR_SHAPE: return "invalid sizes";
-    case KDA_ERR_ALIGN: return "misaligned pointer";
-    case KDA_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-const char* kda_last_error(void) { return g_last_error.c_str(); }
-
-kda_status kda_fwd_check(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, float scale, const void* initial_state,
-                         int initial_dtype, const void* final_state, int final_dtype,
-                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
-                         int32_t H, int32_t K, int32_t V, const void* out) {
-  (void)scale;
-  g_last_error.clear();
-  return validate(q, k, v, g, beta, initial_state, initial_dtype, final_state, final_dtype,
-                  cu_seqlens, num_seqs, B, T, H, K, V, out, nullptr);
-}
-
-kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, int32_t cu_count,
-                    int32_t* workgroups, int32_t* value_splits, int64_t* workspace_bytes) {
-  g_last_error.clear();
-  if (!workgroups || !value_splits || !workspace_bytes)
-    return fail(KDA_ERR_NULL, "kda_plan outputs are NULL");
-  if (n_sequences <= 0 || H <= 0 || T < 0)
-    return fail(KDA_ERR_SHAPE, "kda_plan: N=%d T=%lld H=%d", n_sequences, (long long)T, H);
-  int cus = cu_count;
-  if (cus <= 0 && device_cu_count(&cus) != 0)
-    return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const LaunchPlan lp = make_plan(n_sequences, T, H, varlen != 0, cus);
-  *value_splits = lp.nsplit;
-  *workgroups = (int32_t)lp.workgroups;
-  *workspace_bytes = (int64_t)lp.workspace;
-  return KDA_OK;
-}
-
-kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                   float scale, const void* initial_state, int initial_dtype, void* final_state,
-                   int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
-                   int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream) {
+kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    float scale, const void* initial_state, int initial_dtype, void* final_state,
+                    int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                    int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream,
+                    bool g_scalar) {
   g_last_error.clear();
   int32_t N = 0;
   kda_status st = validate(q, k, v, g, beta, initial_state, initial_dtype, final_state,
-                           final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out, &N);
+                           final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out, &N,
+                           g_scalar);
   if (st != KDA_OK) return st;
   if (T == 0 && final_state == nullptr) return KDA_OK;  // nothing observable to compute
 
@@ -267,6 +221,7 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.g = g;
+  p.g_scalar = g_scalar ? 1 : 0;
   p.beta = beta;
   p.out = static_cast<uint16_t*>(out);
   p.s0 = initial_state;
@@ -296,9 +251,10 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
   }
   if (log_enabled())
     std::fprintf(stderr,
-                 "[kda] launch: N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
+                 "[kda] launch: %s N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
                  "segment_slots=%d workspace=%zu\n",
-                 N, H, (long long)T, lp.nsplit, cus, cu_seqlens != nullptr, lp.emax, lp.workspace);
+                 g_scalar ? "gdn" : "kda", N, H, (long long)T, lp.nsplit, cus,
+                 cu_seqlens != nullptr, lp.emax, lp.workspace);
   const hipError_t err = kda::launch_fwd(p, lp.nsplit, hs);
   if (ws != nullptr) {
     const hipError_t e = hipFreeAsync(ws, hs);
@@ -310,6 +266,83 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
   return KDA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "required pointer is NULL";
+    case KDA_ERR_HEAD_DIM: return "head dimension must be 128";
+    case KDA_ERR_VARLEN_BATCH: return "cu_seqlens requires B = 1";
+    case KDA_ERR_STATE_DTYPE: return "initial and final state dtypes differ";
+    case KDA_ERR_DTYPE: return "invalid dtype";
+    case KDA_ERR_SHAPE: return "invalid sizes";
+    case KDA_ERR_ALIGN: return "misaligned pointer";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status kda_fwd_check(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const void* initial_state,
+                         int initial_dtype, const void* final_state, int final_dtype,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                         int32_t H, int32_t K, int32_t V, const void* out) {
+  (void)scale;
+  g_last_error.clear();
+  return validate(q, k, v, g, beta, initial_state, initial_dtype, final_state, final_dtype,
+                  cu_seqlens, num_seqs, B, T, H, K, V, out, nullptr, false);
+}
+
+kda_status kda_gdn_fwd_check(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float scale, const void* initial_state,
+                             int initial_dtype, const void* final_state, int final_dtype,
+                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                             int32_t H, int32_t K, int32_t V, const void* out) {
+  (void)scale;
+  g_last_error.clear();
+  return validate(q, k, v, g, beta, initial_state, initial_dtype, final_state, final_dtype,
+                  cu_seqlens, num_seqs, B, T, H, K, V, out, nullptr, true);
+}
+
+kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, int32_t cu_count,
+                    int32_t* workgroups, int32_t* value_splits, int64_t* workspace_bytes) {
+  g_last_error.clear();
+  if (!workgroups || !value_splits || !workspace_bytes)
+    return fail(KDA_ERR_NULL, "kda_plan outputs are NULL");
+  if (n_sequences <= 0 || H <= 0 || T < 0)
+    return fail(KDA_ERR_SHAPE, "kda_plan: N=%d T=%lld H=%d", n_sequences, (long long)T, H);
+  int cus = cu_count;
+  if (cus <= 0 && device_cu_count(&cus) != 0)
+    return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
+  const LaunchPlan lp = make_plan(n_sequences, T, H, varlen != 0, cus);
+  *value_splits = lp.nsplit;
+  *workgroups = (int32_t)lp.workgroups;
+  *workspace_bytes = (int64_t)lp.workspace;
+  return KDA_OK;
+}
+
+kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   float scale, const void* initial_state, int initial_dtype, void* final_state,
+                   int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                   int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream) {
+  return fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state, final_dtype,
+                  cu_seqlens, num_seqs, B, T, H, K, V, out, stream, false);
+}
+
+kda_status kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float scale, const void* initial_state,
+                       int initial_dtype, void* final_state, int final_dtype,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                       int32_t H, int32_t K, int32_t V, void* out, void* stream) {
+  return fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state, final_dtype,
+                  cu_seqlens, num_seqs, B, T, H, K, V, out, stream, true);
+}
+
 }  // extern "C"
 
 namespace {
@@ -317,7 +350,7 @@ namespace {
 kda_status validate_decode(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const void* state, int state_dtype,
                            const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
-                           int32_t V, const void* out) {
+                           int32_t V, const void* out, bool g_scalar) {
   if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
     return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: only K = V = 128 is supported", K, V);
   if (N < 0 || H <= 0) return fail(KDA_ERR_SHAPE, "invalid sizes N=%d H=%d", N, H);
@@ -328,14 +361,49 @@ kda_status validate_decode(const void* q, const void* k, const void* v, const fl
   if (N > 0) {
     if (!q || !k || !v || !g || !beta || !out || !state)
       return fail(KDA_ERR_NULL, "q, k, v, g, beta, state and out are required when N > 0");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
-        !aligned(out, 16) || !aligned(state, 16))
-      return fail(KDA_ERR_ALIGN, "q, k, v, g, out and state must be 16-byte aligned");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(state, 16))
+      return fail(KDA_ERR_ALIGN, "q, k, v, out and state must be 16-byte aligned");
+    if (!aligned(g, g_scalar ? 4 : 16))
+      return fail(KDA_ERR_ALIGN, "g must be %d-byte aligned", g_scalar ? 4 : 16);
     if (!aligned(beta, 4) || (state_indices && !aligned(state_indices, 4)))
       return fail(KDA_ERR_ALIGN, "beta and state_indices must be 4-byte aligned");
   }
   return KDA_OK;
 }
+
+kda_status decode_impl(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float scale, void* state, int state_dtype,
+                       const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
+                       void* out, void* stream, bool g_scalar) {
+  g_last_error.clear();
+  kda_status st = validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K,
+                                  V, out, g_scalar);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  kda::DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = g;
+  p.g_scalar = g_scalar ? 1 : 0;
+  p.beta = beta;
+  p.out = static_cast<uint16_t*>(out);
+  p.state = state;
+  p.idx = state_indices;
+  p.scale = scale;
+  p.state_fp32 = state_dtype == KDA_FP32;
+  p.nseq = N;
+  p.H = H;
+  if (log_enabled())
+    std::fprintf(stderr, "[kda] decode: %s N=%d H=%d state=%s indexed=%d\n", g_scalar ? "gdn" : "kda",
+                 N, H, p.state_fp32 ? "fp32" : "bf16", state_indices != nullptr);
+  const hipError_t err = kda::launch_decode(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+  return KDA_OK;
+}
+
 
 }  // namespace
 
@@ -347,38 +415,34 @@ kda_status kda_decode_check(const void* q, const void* k, const void* v, const f
                             int32_t V, const void* out) {
   (void)scale;
   g_last_error.clear();
-  return validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K, V, out);
+  return validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K, V, out,
+                         false);
+}
+
+kda_status kda_gdn_decode_check(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float scale, const void* state, int state_dtype,
+                                const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
+                                int32_t V, const void* out) {
+  (void)scale;
+  g_last_error.clear();
+  return validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K, V, out,
+                         true);
 }
 
 kda_status kda_decode(const void* q, const void* k, const void* v, const float* g,
                       const float* beta, float scale, void* state, int state_dtype,
                       const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
                       void* out, void* stream) {
-  g_last_error.clear();
-  kda_status st = validate_decode(q, k, v, g, beta, state, state_dtype, state_indices, N, H, K,
-                                  V, out);
-  if (st != KDA_OK) return st;
-  if (N == 0) return KDA_OK;
-  kda::DecodeParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.g = g;
-  p.beta = beta;
-  p.out = static_cast<uint16_t*>(out);
-  p.state = state;
-  p.idx = state_indices;
-  p.scale = scale;
-  p.state_fp32 = state_dtype == KDA_FP32;
-  p.nseq = N;
-  p.H = H;
-  if (log_enabled())
-    std::fprintf(stderr, "[kda] decode: N=%d H=%d state=%s indexed=%d\n", N, H,
-                 p.state_fp32 ? "fp32" : "bf16", state_indices != nullptr);
-  const hipError_t err = kda::launch_decode(p, static_cast<hipStream_t>(stream));
-  if (err != hipSuccess)
-    return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
-  return KDA_OK;
+  return decode_impl(q, k, v, g, beta, scale, state, state_dtype, state_indices, N, H, K, V, out,
+                     stream, false);
+}
+
+kda_status kda_gdn_decode(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, float scale, void* state, int state_dtype,
+                          const int32_t* state_indices, int32_t N, int32_t H, int32_t K, int32_t V,
+                          void* out, void* stream) {
+  return decode_impl(q, k, v, g, beta, scale, state, state_dtype, state_indices, N, H, K, V, out,
+                     stream, true);
 }
 
 }  // extern "C"

@@ -38,7 +38,9 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <bool F32>
+// GS: one gate per token and head (Gated DeltaNet), the same decay for every
+// key channel [core.today "Kimi Linear 특집", ch.4 혁신 1].
+template <bool F32, bool GS>
 __global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
   __shared__ float vk[D], vq[D], va[D];   // k, q and exp(g) of the token
   __shared__ float part[2][8][D];         // per row group: partial S~^T k and S~^T q
@@ -56,7 +58,7 @@ __global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
     const float qf = bf2f_u16(p.q[tok * D + t]);
     vk[t] = kf;
     vq[t] = qf;
-    va[t] = __builtin_amdgcn_exp2f(p.g[tok * D + t] * LOG2E);
+    va[t] = __builtin_amdgcn_exp2f((GS ? p.g[tok] : p.g[tok * D + t]) * LOG2E);
     float s = kf * qf;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -149,8 +151,13 @@ __global__ void __launch_bounds__(DNT) kda_decode_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.nseq * p.H)), block(DNT);
-  if (p.state_fp32) hipLaunchKernelGGL(kda_decode_kernel<true>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(kda_decode_kernel<false>, grid, block, 0, stream, p);
+  if (p.g_scalar) {
+    if (p.state_fp32) hipLaunchKernelGGL((kda_decode_kernel<true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((kda_decode_kernel<false, true>), grid, block, 0, stream, p);
+  } else {
+    if (p.state_fp32) hipLaunchKernelGGL((kda_decode_kernel<true, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((kda_decode_kernel<false, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -335,6 +335,7 @@ struct ChunkSrc {
   __amdgpu_buffer_rsrc_t g, q, k, v, b;
 };
 
+template <bool GS>
 __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, int ch) {
   const int64_t tok0 = w.bos + (int64_t)ch * C;
   const int64_t rest = w.len - (int64_t)ch * C;
@@ -343,7 +344,8 @@ __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, in
   const int HD = p.H * D;
   const int64_t base = tok0 * HD + (int64_t)w.h * D;
   ChunkSrc s;
-  s.g = rsrc(p.g + base, valid * HD * 4);
+  // the gate: per channel [rows][H][128], or one value per token and head [rows][H]
+  s.g = GS ? rsrc(p.g + tok0 * p.H + w.h, valid * p.H * 4) : rsrc(p.g + base, valid * HD * 4);
   s.q = rsrc(p.q + base, valid * HD * 2);
   s.k = rsrc(p.k + base, valid * HD * 2);
   s.v = rsrc(p.v + base + w.j0, w.vzero ? 0 : valid * HD * 2);
@@ -354,9 +356,19 @@ __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, in
 // Prep thread t loads rows 8*rg..8*rg+7, channels 4*cg..4*cg+3 (rg = t/32,
 // cg = t%32), in pieces so that each register set is refilled as soon as the
 // previous chunk has consumed it.
-template <int NV>
+template <int NV, bool GS>
 __device__ __forceinline__ void load_g(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t) {
   const int rg = t >> 5, cg = t & 31;
+  if constexpr (GS) {
+    // one gate per row, the same for the thread's four channels
+    const int H = HD / D;
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) {
+      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.g, rg * 8 * H * 4, r8 * H * 4, 0));
+      R.g[r8] = make_float4(x, x, x, x);
+    }
+    return;
+  }
   const int vo = rg * 8 * HD * 4 + 16 * cg;  // lane part; the row goes in soffset
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) {
@@ -395,16 +407,16 @@ __device__ __forceinline__ void load_beta(ChunkRegs<NV>& R, const ChunkSrc& s, i
   R.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.b, (t & 63) * H * 4, 0, 0));
 }
 
-template <int NV>
+template <int NV, bool GS>
 __device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, const Work& w,
                                            int ch, int t) {
-  const ChunkSrc s = chunk_src(p, w, ch);
+  const ChunkSrc s = chunk_src<GS>(p, w, ch);
   const int HD = p.H * D;
   // the scheduling barriers keep this issue order, which the loop's memory-counter
   // waits assume on entry as well
   load_beta<NV>(R, s, p.H, t);
   __builtin_amdgcn_sched_barrier(0);
-  load_g<NV>(R, s, HD, t);
+  load_g<NV, GS>(R, s, HD, t);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, s, HD, t, r8);
@@ -450,7 +462,7 @@ __device__ __forceinline__ void diag_inverse(Smem<NV>& sm, int b, int q4, int m1
   *reinterpret_cast<float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-template <int NV>
+template <int NV, bool GS>
 __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const Work& w) {
   const int t = threadIdx.x - (NT - NP);   // 0..255
   const int pw = __builtin_amdgcn_readfirstlane(t >> 6);  // prep wave 0..3 (wave-uniform)
@@ -481,7 +493,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
   }
 
   ChunkRegs<NV> R;
-  load_chunk<NV>(R, p, w, 0, t);
+  load_chunk<NV, GS>(R, p, w, 0, t);
 
   // Iteration it prepares chunk pc = it + 1 while the state waves run chunk it.
   // The loop body has no branches around its loads, so the memory-counter waits
@@ -527,7 +539,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 
     // ---- phase B: gated operand tiles of chunk pc
     {
-      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
+      const ChunkSrc nsrc = chunk_src<GS>(p, w, pc + 1);
       // beta of the next chunk is fetched first: the next phase A waits only for
       // beta and g (the memory counter retires loads in order)
       if (t < C) sm.beta[t] = R.beta;
@@ -713,7 +725,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           }
         }
       }
-      load_g<NV>(R, nsrc, HD, t);  // the decays of this chunk are consumed
+      load_g<NV, GS>(R, nsrc, HD, t);  // the decays of this chunk are consumed
     }
     __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
 
@@ -723,7 +735,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // q, k and v of chunk pc are consumed once V^T is stored; the next chunk's are
       // fetched after this phase's stores, which would otherwise wait behind the
       // issue of the loads
-      const ChunkSrc nsrc = chunk_src(p, w, pc + 1);
+      const ChunkSrc nsrc = chunk_src<GS>(p, w, pc + 1);
       // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
@@ -1165,7 +1177,9 @@ __device__ __forceinline__ int find_seq(const int* off, int N, int x) {
 }
 
 // ============================================================================ main kernel
-template <int JT>
+// GS: the gate is one scalar per token and head (Gated DeltaNet), broadcast over
+// the key channels as it is loaded; everything after the load is the KDA path.
+template <int JT, bool GS>
 __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   constexpr int NV = 64 * JT;  // value columns per workgroup
   __shared__ Smem<NV> sm;
@@ -1261,7 +1275,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
 
   // Both roles execute the same barrier sequence; the branch is uniform per wave.
   if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w);
-  else prep_loop<NV>(sm, p, w);
+  else prep_loop<NV, GS>(sm, p, w);
 }
 
 // ============================================================================ scan and fix-up
@@ -1567,9 +1581,11 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   const int64_t wgs = (groups * p.H + 7) / 8 * 8 * nsplit;
   const dim3 block(NT);
   if (nsplit == 1) {
-    hipLaunchKernelGGL(kda_fwd_kernel<2>, dim3((unsigned)wgs), block, 0, stream, p);
+    if (p.g_scalar) hipLaunchKernelGGL((kda_fwd_kernel<2, true>), dim3((unsigned)wgs), block, 0, stream, p);
+    else hipLaunchKernelGGL((kda_fwd_kernel<2, false>), dim3((unsigned)wgs), block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL(kda_fwd_kernel<1>, dim3((unsigned)wgs), block, 0, stream, p);
+    if (p.g_scalar) hipLaunchKernelGGL((kda_fwd_kernel<1, true>), dim3((unsigned)wgs), block, 0, stream, p);
+    else hipLaunchKernelGGL((kda_fwd_kernel<1, false>), dim3((unsigned)wgs), block, 0, stream, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;

@@ -26,9 +26,10 @@ struct Params {
   const uint16_t* q;      // bf16 [rows][H][128]
   const uint16_t* k;
   const uint16_t* v;
-  const float* g;         // fp32 [rows][H][128]
+  const float* g;         // fp32 [rows][H][128], or [rows][H] when g_scalar
   const float* beta;      // fp32 [rows][H]
   uint16_t* out;          // bf16 [rows][H][128]
+  int g_scalar;           // one gate per token and head (Gated DeltaNet)
   const void* s0;         // [N][H][128][128] or null
   void* s1;               // [N][H][128][128] or null
   const int32_t* cu;      // [N+1] or null
@@ -63,9 +64,10 @@ struct DecodeParams {
   const uint16_t* q;      // bf16 [N][H][128]
   const uint16_t* k;
   const uint16_t* v;
-  const float* g;         // fp32 [N][H][128]
+  const float* g;         // fp32 [N][H][128], or [N][H] when g_scalar
   const float* beta;      // fp32 [N][H]
   uint16_t* out;          // bf16 [N][H][128]
+  int g_scalar;           // one gate per token and head (Gated DeltaNet)
   void* state;            // [slots][H][128][128], bf16 or fp32
   const int32_t* idx;     // [N] state slot of each sequence (negative: skip), or null (slot n)
   float scale;

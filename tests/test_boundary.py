@@ -34,7 +34,9 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == ["kda_decode", "kda_decode_check", "kda_fwd", "kda_fwd_check",
-                                  "kda_last_error", "kda_plan", "kda_status_string"]
+                                  "kda_gdn_decode", "kda_gdn_decode_check", "kda_gdn_fwd",
+                                  "kda_gdn_fwd_check", "kda_last_error", "kda_plan",
+                                  "kda_status_string"]
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -113,6 +115,22 @@ def test_decode_check_accepts_valid_arguments(lib):
 def test_decode_check_rejections(lib, over, status):
     assert binding.decode_check(**dec_args(**over)) == status
     assert lib.kda_last_error().decode() != ""
+
+
+def test_gdn_checks_take_a_scalar_gate(lib):
+    """The scalar-gate entry points validate like the KDA ones, except that g holds
+    one fp32 per token and head and needs only 4-byte alignment."""
+    assert binding.gdn_fwd_check(**ok_args(g=P + 4)) == OK
+    assert binding.fwd_check(**ok_args(g=P + 4)) == ERR_ALIGN
+    assert binding.gdn_fwd_check(**ok_args(g=P + 2)) == ERR_ALIGN
+    assert binding.gdn_fwd_check(**ok_args(K=64)) == ERR_HEAD_DIM
+    assert binding.gdn_fwd_check(**ok_args(B=2, cu_seqlens=P, num_seqs=2)) == ERR_VARLEN_BATCH
+    assert binding.gdn_fwd_check(**ok_args(g=0)) == ERR_NULL
+    assert binding.gdn_decode_check(**dec_args(g=P + 4)) == OK
+    assert binding.decode_check(**dec_args(g=P + 4)) == ERR_ALIGN
+    assert binding.gdn_decode_check(**dec_args(g=P + 2)) == ERR_ALIGN
+    assert binding.gdn_decode_check(**dec_args(state_dtype=2)) == ERR_DTYPE
+    assert binding.gdn_decode_check(**dec_args(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state=0)) == OK
 
 
 def test_state_dtype_ignored_for_absent_state(lib):
