@@ -180,6 +180,50 @@ def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32):
                          "kernel": "kda_decode_kernel", "algorithmic_bytes": nbytes}}
 
 
+def gdn_bench(wid: int, steps: int, warmup: int):
+    """The scalar-gate forward (kda_gdn_fwd) on workload `wid`'s tensors, with the
+    first channel of the per-channel gate as the gate of each token and head."""
+    import torch
+
+    from linear_attention_kda_amd import binding, perfmodel
+    from linear_attention_kda_amd.workloads import make_inputs
+
+    x = make_inputs(wid, "cuda")
+    w = x["workload"]
+    gs = x["g"][..., 0].contiguous()
+    N, H = w.num_states, w.H
+    sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    final = torch.empty(N, H, 128, 128, dtype=sdt[w.final_state], device="cuda") \
+        if w.final_state else None
+    out = torch.empty_like(x["v"])
+
+    def step():
+        binding.gdn_fwd(x["q"], x["k"], x["v"], gs, x["beta"], x["scale"],
+                        initial_state=x["initial_state"], final_state=final,
+                        cu_seqlens=x["cu_seqlens"], out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = perfmodel.workload_bytes(w.tokens, H, N, state_bytes_of(w.init_state),
+                                      state_bytes_of(w.final_state), scalar_gate=True)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] gdn {w.name}: {ms:.3f} ms, {w.tokens / ms / 1e3:.2f} M tokens/s, "
+        f"{gbs:.0f} GB/s ({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return {"workload": f"scalar gate (Gated DeltaNet), {w.name}", "unit": "tokens/s",
+            "value": w.tokens / (ms * 1e-3), "ms_per_step": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kda_gdn_fwd call", "algorithmic_bytes": nbytes}}
+
+
 def counter_run(wid: int):
     """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes.
 
@@ -220,6 +264,7 @@ def main():
                     help="second workload timed and reported under 'secondary' (-1: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate line")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--counters", action="store_true",
                     help="untimed run for hardware-counter passes: a 1 GiB device copy "
@@ -272,6 +317,10 @@ def main():
     if not args.no_decode:
         decode = decode_bench(max(args.steps, 20), args.warmup)
 
+    gdn = None
+    if not args.no_gdn:
+        gdn = gdn_bench(args.workload, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads of {w.name}")
@@ -306,6 +355,7 @@ def main():
                  "flops_model": "6Td^2+3TCd+TC^2 per head"},
         "secondary": secondary,
         "decode": decode,
+        "gdn": gdn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -20,6 +20,8 @@ def test_cost_model_matches_the_pages_worked_example():
 def test_bytes_per_token_head():
     # q, k, v, o bf16 + g fp32 + beta fp32
     assert perfmodel.bytes_per_token_head() == 1540
+    # scalar gate: one fp32 per token and head instead of 128
+    assert perfmodel.bytes_per_token_head(scalar_gate=True) == 1032
 
 
 def test_varlen_workload_bytes():
