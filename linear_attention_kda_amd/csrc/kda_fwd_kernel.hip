@@ -1019,13 +1019,14 @@ struct PlanView {
   int* xoff;  // [N+1] split sequences before it
   int* uoff;  // [N+1] first fix-up unit of segment 1
   int* voff;  // [N+1] first fix-up unit of the later segments
+  int* tok;   // [N+1] first token of each sequence (with cu_seqlens only)
   int* glen;  // [N + 2 emax] chunks of each task group
   int* gseq;  //              its sequence
   int* gk;    //              its kind: 0 segment 0; 2p-1 zero start, 2p identity start of segment p
 };
 
 __host__ __device__ constexpr int plan_ints(int N, int emax, bool groups) {
-  return 8 + N + 5 * (N + 1) + (groups ? 3 * (N + 2 * emax) : 0);
+  return 8 + N + 6 * (N + 1) + (groups ? 3 * (N + 2 * emax) : 0);
 }
 
 __device__ __forceinline__ PlanView plan_view(int* base, int N, int emax) {
@@ -1037,7 +1038,8 @@ __device__ __forceinline__ PlanView plan_view(int* base, int N, int emax) {
   v.xoff = v.soff + N + 1;
   v.uoff = v.xoff + N + 1;
   v.voff = v.uoff + N + 1;
-  v.glen = v.voff + N + 1;
+  v.tok = v.voff + N + 1;
+  v.glen = v.tok + N + 1;
   v.gseq = v.glen + N + 2 * emax;
   v.gk = v.gseq + N + 2 * emax;
   return v;
@@ -1066,6 +1068,8 @@ __device__ __forceinline__ SeqCounts seq_counts(int c, int M, int H) {
 __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
   const int N = p.nseq, tid = threadIdx.x, nt = blockDim.x;
   for (int i = tid; i < N; i += nt) v.lens[i] = (int)((seq_len(p, i) + C - 1) / C);
+  if (p.cu)
+    for (int i = tid; i <= N; i += nt) v.tok[i] = p.cu[i];
   __syncthreads();
   if (tid < 64) {
     const int lane = tid;
@@ -1312,7 +1316,10 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
   const size_t slot_stride = (size_t)p.H * (D * D);
-  const int sidx = u / (p.H * 8), h = (u / 8) % p.H, cb = u % 8;
+  // u = (split sequence * 8 + column block) * H + head: the eight column blocks of one
+  // (sequence, head), which all read the same A_p, land on one XCD when 8 divides H
+  // (workgroups go to XCDs round robin)
+  const int sidx = u / (p.H * 8), cb = (u / p.H) % 8, h = u % p.H;
   const int i = __builtin_amdgcn_readfirstlane(find_seq(v.xoff, N, sidx));
   const int c = __builtin_amdgcn_readfirstlane(v.lens[i]), P = (c + M - 1) / M;
   const int slot0 = __builtin_amdgcn_readfirstlane(v.soff[i]);
@@ -1415,9 +1422,9 @@ __device__ __forceinline__ FixUnit fix_decode(const Params& p, const PlanView& v
   f.ch = seg0 * M + r % n;
   f.slot = __builtin_amdgcn_readfirstlane(v.soff[f.i]) + f.ch / M - 1;
   int64_t bos, len;
-  if (p.cu) {
-    const int c0 = __builtin_amdgcn_readfirstlane(p.cu[f.i]);
-    const int c1 = __builtin_amdgcn_readfirstlane(p.cu[f.i + 1]);
+  if (p.cu) {  // from the plan in LDS: no global load on the unit's critical path
+    const int c0 = __builtin_amdgcn_readfirstlane(v.tok[f.i]);
+    const int c1 = __builtin_amdgcn_readfirstlane(v.tok[f.i + 1]);
     bos = c0;
     len = (int64_t)c1 - c0;
   } else {
