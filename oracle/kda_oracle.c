@@ -284,6 +284,155 @@ int gdn_oracle_fwd(const double* q, const double* k, const double* v, const doub
   return failed ? -2 : 0;
 }
 
+/*
+ * Backward pass of the KDA recurrence (reverse-mode gradient), fp64, token by
+ * token.  For a scalar loss with upstream gradients dO = dL/do_t (same layout as
+ * o) and dS_T = dL/dS_final (or NULL = zero), it returns dL/dq, dL/dk, dL/dv,
+ * dL/dg, dL/dbeta and dL/dS0 (dS0 may be NULL when not wanted).
+ *
+ * It differentiates the decay-then-delta evaluation of kda_oracle_fwd step by
+ * step, in reverse token order [core.today "Kimi Linear 특집", ch.4 혁신 2,
+ * state-update equation; ch.2 readout]:
+ *   S~ = Diag(a) S_prev,  a = exp(g);  e = v - S~^T k;  S = S~ + beta k e^T;  o = scale S^T q
+ * With dS the gradient arriving at S (from later tokens) the local rules are
+ *   dS += scale q do^T;          dq = scale S do
+ *   de = beta dS^T k;            dbeta = k^T dS e;       dk  = beta dS e
+ *   dS~ = dS - k de^T;           dv = de;                dk -= S~ de
+ *   dg_i = a_i sum_j dS~_ij Sprev_ij;                    dS_prev = Diag(a) dS~
+ * The forward states of each (sequence, head) are recomputed and kept in full
+ * (len + 1 states), so memory is O(len * DK * DV) per running task.
+ */
+int kda_oracle_bwd(const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, double scale, const double* S0, const double* dO,
+                   const double* dST, double* dq, double* dk, double* dv, double* dg,
+                   double* dbeta, double* dS0, const int64_t* seq_start, const int64_t* seq_len,
+                   int64_t N, int64_t H, int64_t DK, int64_t DV, int nthreads) {
+  if (check_sizes(N, H, DK, DV, seq_len)) return -1;
+  const int64_t sdim = DK * DV;
+  int64_t Lmax = 0;
+  for (int64_t n = 0; n < N; ++n) Lmax = seq_len[n] > Lmax ? seq_len[n] : Lmax;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* St = (double*)malloc(sizeof(double) * (size_t)((Lmax + 1) * sdim));  /* S_0..S_len */
+    double* dS = (double*)malloc(sizeof(double) * (size_t)sdim);
+    double* Sd = (double*)malloc(sizeof(double) * (size_t)sdim);                 /* S~ */
+    double* e = (double*)malloc(sizeof(double) * (size_t)DV);
+    double* de = (double*)malloc(sizeof(double) * (size_t)DV);
+    double* a = (double*)malloc(sizeof(double) * (size_t)DK);
+    if (!St || !dS || !Sd || !e || !de || !a) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < N * H; ++task) {
+        const int64_t n = task / H, h = task % H;
+        const int64_t t0 = seq_start[n], len = seq_len[n];
+        /* forward, keeping every state */
+        if (S0) memcpy(St, S0 + (n * H + h) * sdim, sizeof(double) * (size_t)sdim);
+        else memset(St, 0, sizeof(double) * (size_t)sdim);
+        for (int64_t s = 0; s < len; ++s) {
+          const int64_t t = t0 + s;
+          const double* kt = k + (t * H + h) * DK;
+          const double* vt = v + (t * H + h) * DV;
+          const double* gt = g + (t * H + h) * DK;
+          const double bt = beta[t * H + h];
+          const double* Sp = St + s * sdim;
+          double* Sn = St + (s + 1) * sdim;
+          for (int64_t i = 0; i < DK; ++i) {
+            const double ai = exp(gt[i]);
+            for (int64_t j = 0; j < DV; ++j) Sn[i * DV + j] = ai * Sp[i * DV + j];
+          }
+          for (int64_t j = 0; j < DV; ++j) {
+            double acc = vt[j];
+            for (int64_t i = 0; i < DK; ++i) acc -= Sn[i * DV + j] * kt[i];
+            e[j] = acc;
+          }
+          for (int64_t i = 0; i < DK; ++i)
+            for (int64_t j = 0; j < DV; ++j) Sn[i * DV + j] += bt * kt[i] * e[j];
+        }
+        /* backward */
+        if (dST) memcpy(dS, dST + (n * H + h) * sdim, sizeof(double) * (size_t)sdim);
+        else memset(dS, 0, sizeof(double) * (size_t)sdim);
+        for (int64_t s = len - 1; s >= 0; --s) {
+          const int64_t t = t0 + s;
+          const double* qt = q + (t * H + h) * DK;
+          const double* kt = k + (t * H + h) * DK;
+          const double* vt = v + (t * H + h) * DV;
+          const double* gt = g + (t * H + h) * DK;
+          const double* dot = dO + (t * H + h) * DV;
+          const double bt = beta[t * H + h];
+          const double* Sp = St + s * sdim;        /* S_{t-1} */
+          const double* Sc = St + (s + 1) * sdim;  /* S_t */
+          double* dqt = dq + (t * H + h) * DK;
+          double* dkt = dk + (t * H + h) * DK;
+          double* dvt = dv + (t * H + h) * DV;
+          double* dgt = dg + (t * H + h) * DK;
+          for (int64_t i = 0; i < DK; ++i) a[i] = exp(gt[i]);
+          /* readout o = scale S^T q */
+          for (int64_t i = 0; i < DK; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < DV; ++j) {
+              dS[i * DV + j] += scale * qt[i] * dot[j];
+              acc += Sc[i * DV + j] * dot[j];
+            }
+            dqt[i] = scale * acc;
+          }
+          /* S~ and e of the forward step */
+          for (int64_t i = 0; i < DK; ++i)
+            for (int64_t j = 0; j < DV; ++j) Sd[i * DV + j] = a[i] * Sp[i * DV + j];
+          for (int64_t j = 0; j < DV; ++j) {
+            double acc = vt[j];
+            for (int64_t i = 0; i < DK; ++i) acc -= Sd[i * DV + j] * kt[i];
+            e[j] = acc;
+          }
+          /* write S = S~ + beta k e^T */
+          double db = 0.0;
+          for (int64_t j = 0; j < DV; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < DK; ++i) acc += dS[i * DV + j] * kt[i];
+            de[j] = bt * acc;
+            db += acc * e[j];
+          }
+          dbeta[t * H + h] = db;
+          for (int64_t i = 0; i < DK; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < DV; ++j) acc += dS[i * DV + j] * e[j];
+            dkt[i] = bt * acc;
+          }
+          /* error e = v - S~^T k */
+          for (int64_t j = 0; j < DV; ++j) dvt[j] = de[j];
+          for (int64_t i = 0; i < DK; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < DV; ++j) {
+              dS[i * DV + j] -= kt[i] * de[j];   /* dS now holds dS~ */
+              acc += Sd[i * DV + j] * de[j];
+            }
+            dkt[i] -= acc;
+          }
+          /* decay S~ = Diag(a) S_prev */
+          for (int64_t i = 0; i < DK; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < DV; ++j) {
+              acc += dS[i * DV + j] * Sp[i * DV + j];
+              dS[i * DV + j] *= a[i];
+            }
+            dgt[i] = a[i] * acc;
+          }
+        }
+        if (dS0) memcpy(dS0 + (n * H + h) * sdim, dS, sizeof(double) * (size_t)sdim);
+      }
+    }
+    free(St); free(dS); free(Sd); free(e); free(de); free(a);
+  }
+  return failed ? -2 : 0;
+}
+
 int kda_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -61,6 +61,11 @@ def _load():
         lib.gdn_oracle_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp,
                                        _ip, _ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int]
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, ctypes.c_double, _dp, _dp, _dp,
+                                       _dp, _dp, _dp, _dp, _dp, _dp, _ip, _ip, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -173,3 +178,43 @@ def gdn_fwd(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=None,
     if rc != 0:
         raise RuntimeError(f"gdn oracle failed with code {rc}")
     return o, S_out
+
+
+def bwd(q, k, v, g, beta, scale: float, do, initial_state=None, d_final_state=None,
+        cu_seqlens=None, nthreads: int = 0):
+    """Reverse-mode gradients of the KDA forward (oracle.fwd's recurrence) in fp64.
+
+    do: dL/do, [B, T, H, DV]; d_final_state: dL/dS_final [N, H, DK, DV] or None.
+    Returns a dict with dq, dk, dg ([B, T, H, DK]), dv ([B, T, H, DV]),
+    dbeta ([B, T, H]) and dS0 ([N, H, DK, DV], the gradient of the initial state).
+    Keeps every forward state of a running task: memory grows with the longest
+    sequence (T * DK * DV * 8 bytes per thread).
+    """
+    lib = _load()
+    q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3] or do.shape != v.shape:
+        raise ValueError("inconsistent input shapes")
+    start, length = _sequences(B, T, cu_seqlens)
+    N = start.shape[0]
+    S0 = None if initial_state is None else _f64(initial_state)
+    dST = None if d_final_state is None else _f64(d_final_state)
+    for name, a in (("initial_state", S0), ("d_final_state", dST)):
+        if a is not None and a.shape != (N, H, DK, DV):
+            raise ValueError(f"{name} must be {(N, H, DK, DV)}, got {a.shape}")
+    out = {n: np.zeros(x.shape, dtype=np.float64) for n, x in
+           (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    out["dS0"] = np.zeros((N, H, DK, DV), dtype=np.float64)
+    if nthreads <= 0:  # every running task holds its sequence's states
+        per = (int(length.max()) + 1 if length.size else 1) * DK * DV * 8
+        nthreads = max(1, min(max_threads(), int(8e9 // max(per, 1))))
+    rc = lib.kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(S0),
+                            _ptr(do), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                            _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                            _ptr(out["dS0"]), start.ctypes.data_as(_ip),
+                            length.ctypes.data_as(_ip), N, H, DK, DV, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda oracle backward failed with code {rc}")
+    return out

@@ -381,3 +381,68 @@ def test_gdn_varlen_packing_equals_separate_runs():
                                 S0[n:n + 1])
         np.testing.assert_allclose(o[:, sl], on, rtol=1e-13, atol=1e-15)
         np.testing.assert_allclose(S[n], Sn[0], rtol=1e-13, atol=1e-15)
+
+
+# --- backward oracle ---------------------------------------------------------------
+
+def _loss(o, S, Wo, WS):
+    return float((o * Wo).sum() + (S * WS).sum())
+
+
+def _fd_grad(f, x, h=1e-6):
+    """Central finite differences of scalar f over every entry of array x."""
+    gr = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        old = x[idx]
+        x[idx] = old + h
+        fp = f()
+        x[idx] = old - h
+        fm = f()
+        x[idx] = old
+        gr[idx] = (fp - fm) / (2 * h)
+    return gr
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_backward_matches_finite_differences(varlen):
+    """Brute force: every gradient of L = <o, Wo> + <S_final, WS> against central
+    finite differences of the forward oracle, on tiny shapes (an independent
+    evaluation of the derivative of the printed recurrence)."""
+    DK, DV, H = 4, 3, 2
+    if varlen:
+        lens = [3, 0, 4]
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        B, T, N = 1, int(cu[-1]), len(lens)
+    else:
+        cu, B, T, N = None, 2, 4, 2
+    q, k, v, g, beta, _ = rnd(40 + varlen, B=B, T=T, H=H, DK=DK, DV=DV, g_lo=0.05, g_hi=0.8)
+    S0 = 0.3 * np.random.default_rng(41).standard_normal((N, H, DK, DV))
+    r = np.random.default_rng(42)
+    Wo = r.standard_normal(v.shape)
+    WS = r.standard_normal(S0.shape)
+    gr = oracle.bwd(q, k, v, g, beta, SCALE, Wo, S0, WS, cu_seqlens=cu)
+
+    def L():
+        o, S = oracle.fwd(q, k, v, g, beta, SCALE, S0, cu_seqlens=cu)
+        return _loss(o, S, Wo, WS)
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta), ("dS0", S0)):
+        np.testing.assert_allclose(gr[name], _fd_grad(L, x), rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_without_final_state_gradient_and_state():
+    """dS_final = None and S0 = None: the gradient of <o, Wo> alone from a zero
+    state (checked by finite differences on the inputs that still matter)."""
+    DK, DV, H, T = 3, 2, 1, 5
+    q, k, v, g, beta, _ = rnd(43, T=T, H=H, DK=DK, DV=DV)
+    Wo = np.random.default_rng(44).standard_normal(v.shape)
+    gr = oracle.bwd(q, k, v, g, beta, SCALE, Wo)
+
+    def L():
+        o, _ = oracle.fwd(q, k, v, g, beta, SCALE, None)
+        return float((o * Wo).sum())
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta)):
+        np.testing.assert_allclose(gr[name], _fd_grad(L, x), rtol=1e-6, atol=1e-8, err_msg=name)
