@@ -230,6 +230,53 @@ kda_status kda_gdn_decode_check(const void* q, const void* k, const void* v, con
                                 const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
                                 int32_t V, const void* out);
 
+/*
+ * kda_bwd — gradients of kda_fwd (training backward pass).  Given dL/do and
+ * optionally dL/dS_final, returns dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and
+ * optionally dL/dS_initial, all fp32.  It differentiates the recurrence of
+ * kda_fwd [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update equation and
+ * its chunkwise form; ch.2 readout]: a forward pass stores every chunk's start
+ * state, chunk-local gradient products follow, and one serial pass per
+ * (sequence, head) carries the state gradient from the last chunk to the first.
+ *
+ *  q, k, v, g, beta, scale, initial_state / initial_dtype, cu_seqlens, num_seqs,
+ *  B, T, H, K, V    as kda_fwd.
+ *  d_out            device, bf16, [B, T, H, 128], 16-byte aligned: dL/do.
+ *  d_final_state / d_final_dtype
+ *                   device, [N, H, 128, 128] bf16 or fp32, 16-byte aligned, or NULL
+ *                   (zero).
+ *  dq, dk, dg       device, fp32, [B, T, H, 128], 16-byte aligned (outputs).
+ *  dv               device, fp32, [B, T, H, 128], 16-byte aligned (output).
+ *  dbeta            device, fp32, [B, T, H], 4-byte aligned (output).
+ *  d_initial_state  device, fp32, [N, H, 128, 128], 16-byte aligned, or NULL when
+ *                   not wanted (output).
+ * Rows outside every sequence (varlen) get zero gradients.  Range limit: the
+ * per-channel sum of -g over each 64-token chunk must stay below 80 (natural
+ * log); the chunk-local factors exp(+-G) are formed in fp32.
+ * Memory: a workspace of kda_bwd_workspace_bytes(N, rows, H) bytes (rows = T with
+ * cu_seqlens, else B*T) taken from the library's stream-ordered pool for the
+ * call.  Asynchrony and errors as kda_fwd.
+ */
+kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   float scale, const void* initial_state, int initial_dtype, const void* d_out,
+                   const void* d_final_state, int d_final_dtype, const int32_t* cu_seqlens,
+                   int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                   float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                   float* d_initial_state, void* stream);
+
+/* kda_bwd_check — kda_bwd's host-side validation, with no launch. */
+kda_status kda_bwd_check(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const void* initial_state,
+                         int initial_dtype, const void* d_out, const void* d_final_state,
+                         int d_final_dtype, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t B, int64_t T, int32_t H, int32_t K, int32_t V, const float* dq,
+                         const float* dk, const float* dv, const float* dg, const float* dbeta,
+                         const float* d_initial_state);
+
+/* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
+ * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only. */
+int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H);
+
 #ifdef __cplusplus
 }
 #endif

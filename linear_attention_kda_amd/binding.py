@@ -69,6 +69,16 @@ def load_library():
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = base.argtypes
+        lib.kda_bwd.restype = ctypes.c_int
+        lib.kda_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_int, _vp,
+                                _vp, ctypes.c_int, _vp, _i32, _i32, _i64, _i32, _i32, _i32,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.kda_bwd_check.restype = ctypes.c_int
+        lib.kda_bwd_check.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, ctypes.c_int,
+                                      _vp, _vp, ctypes.c_int, _vp, _i32, _i32, _i64, _i32, _i32,
+                                      _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.kda_bwd_workspace_bytes.restype = _i64
+        lib.kda_bwd_workspace_bytes.argtypes = [_i32, _i64, _i32]
         lib.kda_plan.restype = ctypes.c_int
         lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
@@ -280,4 +290,76 @@ def _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate):
                    _state_dtype(state), ptr(state_indices), N, H, K, V, ptr(out), stream)
     if st != 0:
         raise KdaError(st, "kda_gdn_decode" if scalar_gate else "kda_decode", _detail(lib, st))
+    return out
+
+
+def bwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, d_out=0, initial_state=0,
+              initial_dtype=KDA_FP32, d_final_state=0, d_final_dtype=KDA_FP32, cu_seqlens=0,
+              num_seqs=0, dq=0, dk=0, dv=0, dg=0, dbeta=0, d_initial_state=0, scale=1.0) -> int:
+    """Host-only validation of a backward call with raw (never dereferenced) addresses."""
+    lib = load_library()
+    return lib.kda_bwd_check(q, k, v, g, beta, scale, initial_state, initial_dtype, d_out,
+                             d_final_state, d_final_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                             dq, dk, dv, dg, dbeta, d_initial_state)
+
+
+def bwd_workspace_bytes(n_sequences: int, rows: int, heads: int) -> int:
+    return int(load_library().kda_bwd_workspace_bytes(n_sequences, rows, heads))
+
+
+def bwd(q, k, v, g, beta, d_out, scale: float | None = None, initial_state=None,
+        d_final_state=None, cu_seqlens=None, want_d_initial_state: bool = True):
+    """Gradients of the KDA forward pass on the current HIP stream.
+
+    Inputs as fwd(); d_out: bf16 [B, T, H, 128] (dL/do); d_final_state: dL/dS_final,
+    [N, H, 128, 128] bf16 or fp32, or None.  Returns a dict with fp32 dq, dk, dv, dg
+    ([B, T, H, 128]), dbeta ([B, T, H]) and dS0 ([N, H, 128, 128], the gradient of
+    the initial state; None when want_d_initial_state is False).
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("g", g, torch.float32),
+                        ("beta", beta, torch.float32), ("d_out", d_out, torch.bfloat16)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3] or d_out.shape != v.shape:
+        raise ValueError("inconsistent shapes")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev \
+                or not cu_seqlens.is_contiguous():
+            raise TypeError("cu_seqlens must be a contiguous int32 tensor on the same device")
+        num_seqs = cu_seqlens.numel() - 1
+    N = num_seqs if cu_seqlens is not None else B
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None and (t.shape != (N, H, K, V) or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous [{N}, {H}, {K}, {V}] tensor on {dev}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty(B, T, H, K, **f32), "dk": torch.empty(B, T, H, K, **f32),
+           "dv": torch.empty(B, T, H, V, **f32), "dg": torch.empty(B, T, H, K, **f32),
+           "dbeta": torch.empty(B, T, H, **f32),
+           "dS0": torch.empty(N, H, K, V, **f32) if want_d_initial_state else None}
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.kda_bwd(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale),
+                         ptr(initial_state), _state_dtype(initial_state), ptr(d_out),
+                         ptr(d_final_state), _state_dtype(d_final_state), ptr(cu_seqlens),
+                         num_seqs, B, T, H, K, V, ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]),
+                         ptr(out["dg"]), ptr(out["dbeta"]), ptr(out["dS0"]), stream)
+    if st != 0:
+        raise KdaError(st, "kda_bwd", _detail(lib, st))
     return out

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, "kda_api.cpp"), os.path.join(CSRC, "kda_fwd_kernel.hip"),
-           os.path.join(CSRC, "kda_decode_kernel.hip")]
+           os.path.join(CSRC, "kda_decode_kernel.hip"), os.path.join(CSRC, "kda_bwd.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code; the host pass

@@ -446,3 +446,162 @@ kda_status kda_gdn_decode(const void* q, const void* k, const void* v, const flo
 }
 
 }  // extern "C"
+
+namespace {
+
+kda_status validate_bwd(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const void* s0, int s0_dtype, const void* d_out,
+                        const void* dsT, int dsT_dtype, const int32_t* cu, int32_t num_seqs,
+                        int32_t B, int64_t T, int32_t H, int32_t K, int32_t V, const float* dq,
+                        const float* dk, const float* dv, const float* dg, const float* dbeta,
+                        const float* ds0, int32_t* n_out) {
+  kda_status st = validate(q, k, v, g, beta, s0, s0_dtype, nullptr, KDA_FP32, cu, num_seqs, B, T,
+                           H, K, V, T > 0 ? d_out : nullptr, n_out, false);
+  if (st != KDA_OK) return st;
+  if (dsT != nullptr && dsT_dtype != KDA_BF16 && dsT_dtype != KDA_FP32)
+    return fail(KDA_ERR_DTYPE, "d_final_dtype=%d is not KDA_BF16 or KDA_FP32", dsT_dtype);
+  if (T > 0 && (!d_out || !dq || !dk || !dv || !dg || !dbeta))
+    return fail(KDA_ERR_NULL, "d_out, dq, dk, dv, dg and dbeta are required when T > 0");
+  if ((d_out && !aligned(d_out, 16)) || (dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)) ||
+      (dv && !aligned(dv, 16)) || (dg && !aligned(dg, 16)) || (dsT && !aligned(dsT, 16)) ||
+      (ds0 && !aligned(ds0, 16)))
+    return fail(KDA_ERR_ALIGN, "d_out, gradients and states must be 16-byte aligned");
+  if (dbeta && !aligned(dbeta, 4)) return fail(KDA_ERR_ALIGN, "dbeta must be 4-byte aligned");
+  return KDA_OK;
+}
+
+// Chunk slots of the backward: sequence n's chunk c is slot n + floor(bos_n / 64) + c.
+int64_t bwd_slots(int32_t N, int64_t rows) { return (int64_t)N + (rows + 63) / 64 + 1; }
+
+size_t bwd_workspace_bytes(int32_t N, int64_t rows, int32_t H) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nb = (size_t)bwd_slots(N, rows) * H;
+  return up(nb * kda::BwdTiles::floats_per_batch() * 4) + up((size_t)rows * H * 128 * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_bwd_check(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const void* initial_state,
+                         int initial_dtype, const void* d_out, const void* d_final_state,
+                         int d_final_dtype, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t B, int64_t T, int32_t H, int32_t K, int32_t V, const float* dq,
+                         const float* dk, const float* dv, const float* dg, const float* dbeta,
+                         const float* d_initial_state) {
+  (void)scale;
+  g_last_error.clear();
+  return validate_bwd(q, k, v, g, beta, initial_state, initial_dtype, d_out, d_final_state,
+                      d_final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, dq, dk, dv, dg, dbeta,
+                      d_initial_state, nullptr);
+}
+
+int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H) {
+  if (n_sequences <= 0 || rows < 0 || H <= 0) return -1;
+  return (int64_t)bwd_workspace_bytes(n_sequences, rows, H);
+}
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                   float scale, const void* initial_state, int initial_dtype, const void* d_out,
+                   const void* d_final_state, int d_final_dtype, const int32_t* cu_seqlens,
+                   int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                   float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                   float* d_initial_state, void* stream) {
+  g_last_error.clear();
+  int32_t N = 0;
+  kda_status st = validate_bwd(q, k, v, g, beta, initial_state, initial_dtype, d_out,
+                               d_final_state, d_final_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                               dq, dk, dv, dg, dbeta, d_initial_state, &N);
+  if (st != KDA_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = cu_seqlens ? T : (int64_t)B * T;
+  const size_t gbytes = (size_t)rows * H * 128 * 4;
+  hipError_t e = hipSuccess;
+  // rows outside every sequence get zero gradients
+  if (rows > 0) {
+    e = hipMemsetAsync(dq, 0, gbytes, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(dk, 0, gbytes, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(dv, 0, gbytes, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(dg, 0, gbytes, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(dbeta, 0, (size_t)rows * H * 4, hs);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "gradient clear: %s", hipGetErrorString(e));
+  }
+  int cus = 0;
+  if (device_cu_count(&cus) != 0)
+    return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
+  const int64_t nb = bwd_slots(N, rows) * H;
+  const size_t wbytes = bwd_workspace_bytes(N, rows, H);
+  hipMemPool_t pool = nullptr;
+  void* ws = nullptr;
+  e = workspace_pool(&pool);
+  if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, wbytes, pool, hs);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "backward workspace of %zu bytes: %s", wbytes, hipGetErrorString(e));
+  // carve the per-chunk tiles
+  kda::BwdTiles w{};
+  {
+    float* base = static_cast<float*>(ws);
+    size_t off = 0;
+    auto take = [&](size_t per) { float* r = base + off; off += (size_t)nb * per; return r; };
+    float** t1[] = {&w.G, &w.kg, &w.qg, &w.kh, &w.kp, &w.vv, &w.dO, &w.kk, &w.qq,
+                    &w.R, &w.U, &w.MtdO, &w.dU, &w.dY, &w.dqg, &w.dkg, &w.dkh, &w.dkp};
+    for (float** x : t1) *x = take(64 * 128);
+    float** t2[] = {&w.A, &w.P, &w.M, &w.T, &w.dM, &w.dA};
+    for (float** x : t2) *x = take(64 * 64);
+    w.F = take(128 * 64);
+    w.S = take(128 * 128);
+    w.X = take(128 * 128);
+    w.dSn = take(128 * 128);
+    w.beta = take(64);
+    w.gam = take(128);
+    w.valid = reinterpret_cast<int*>(take(1));
+  }
+  uint16_t* fwd_out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+                                                   ((nb * kda::BwdTiles::floats_per_batch() * 4 + 255) & ~(size_t)255));
+  hipError_t err = hipSuccess;
+  if (rows > 0) {
+    // forward pass with chunk checkpoints (no sequence splitting)
+    kda::Params p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.g = g;
+    p.beta = beta;
+    p.out = fwd_out;
+    p.s0 = initial_state;
+    p.s0_fp32 = initial_dtype == KDA_FP32;
+    p.cu = cu_seqlens;
+    p.T = T;
+    p.scale = scale;
+    p.nseq = N;
+    p.H = H;
+    p.cus = cus;
+    p.seg_min = seg_min_chunks();
+    p.ckpt = w.S;
+    const int nsplit = (int64_t)N * H >= cus ? 1 : 2;
+    err = kda::launch_fwd(p, nsplit, hs);
+    if (err == hipSuccess) {
+      kda::BwdParams bp{};
+      bp.q = p.q; bp.k = p.k; bp.v = p.v;
+      bp.dout = static_cast<const uint16_t*>(d_out);
+      bp.g = g; bp.beta = beta; bp.cu = cu_seqlens; bp.T = T; bp.scale = scale;
+      bp.nseq = N; bp.H = H;
+      bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32;
+      bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.ds0 = d_initial_state;
+      err = kda::launch_bwd(bp, w, nb, hs);
+    }
+  } else if (d_initial_state != nullptr) {
+    // no tokens: the initial-state gradient is the final-state gradient (or zero)
+    kda::BwdParams bp{};
+    bp.cu = cu_seqlens; bp.T = T; bp.nseq = N; bp.H = H;
+    bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32; bp.ds0 = d_initial_state;
+    err = kda::launch_bwd_scan_only(bp, hs);
+  }
+  const hipError_t e2 = hipFreeAsync(ws, hs);
+  if (err != hipSuccess) return fail(KDA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
+  if (e2 != hipSuccess) return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e2));
+  return KDA_OK;
+}
+
+}  // extern "C"

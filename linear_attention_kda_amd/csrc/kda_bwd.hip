@@ -1,0 +1,473 @@
+// Backward pass of the chunkwise KDA forward for gfx950 (MI355X).
+//
+// Per chunk (64 tokens of one sequence and head; local rows r, i; S the chunk's
+// start state, S' its end state), with G the within-chunk inclusive cumsum of g,
+// Gam = exp(G), gam = exp(G_last) [core.today "Kimi Linear 특집", ch.4 혁신 2,
+// state-update equation and its chunkwise form]:
+//   kg = K*Gam, qg = Q*Gam, kh = K/Gam, kp = kh*gam
+//   A  = strict_lower(diag(b) kg kh^T),  T = (I + A)^-1
+//   R  = V - kg S,  U = T diag(b) R,  M = lower_incl(qg kh^T)
+//   O  = scale (qg S + M U),  S' = Diag(gam) S + kp^T U
+// Reverse mode, given dO' = scale dO and dSn = dL/dS' (written out here):
+//   dU  = M^T dO' + kp dSn                dM  = lower_incl(dO' U^T)
+//   dY  = T^T dU                          dA  = strict_lower(-dY U^T)
+//   dqg = dO' S^T + dM kh                 dkp = U dSn^T
+//   dkg = diag(b) (dA kh - dY S^T)        dkh = dM^T qg + dA^T diag(b) kg
+//   dV  = diag(b) dY                      db_r = sum_j dY_rj R_rj + sum_i dA_ri (kg kh^T)_ri
+//   dS  = Diag(gam) dSn + qg^T dO' - kg^T diag(b) dY           (gradient at S)
+// and through the gates: dq = dqg Gam, dk = dkg Gam + dkh/Gam + dkp gam/Gam,
+//   dG_r = dqg qg + dkg kg - dkh kh - dkp kp (per channel),
+//   dG_last = sum_r dkp kp + gam * rowsum(S * dSn),  dg_t = sum_{r >= t} dG_r + dG_last.
+// The only serial dependency is dS across chunks: with F = kg^T diag(b) T^T
+// (128 x 64) and X = qg^T dO' - F M^T dO' (128 x 128), both chunk-local,
+//   dS = Diag(gam) dSn - F (kp dSn) + X.
+//
+// Layout: the forward pass writes every chunk's start state (fp32) to slot
+// n + floor(bos_n / 64) + c of sequence n's chunk c (slots are distinct across
+// sequences); batch index b = slot * H + h addresses every per-chunk tile.
+// Everything here is fp32: the chunk-local products run as batched tiled GEMMs
+// (VALU), the serial recurrence in one workgroup per (sequence, head).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;
+constexpr int C = 64;
+
+__device__ __forceinline__ float bf2f_u16(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ int64_t seq_bos(const BwdParams& p, int n) {
+  return p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
+}
+__device__ __forceinline__ int64_t seq_len_of(const BwdParams& p, int n) {
+  return p.cu ? (int64_t)p.cu[n + 1] - p.cu[n] : p.T;
+}
+
+// Sequence owning slot s: the largest n with n + floor(bos_n / 64) <= s.
+__device__ __forceinline__ int slot_seq(const BwdParams& p, int64_t s) {
+  int lo = 0, hi = p.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mid + seq_bos(p, mid) / C <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- batched GEMM
+// C[b] = rs[b] (.) (alpha op(A[b]) op(B[b]) + D[b]), then masked; row-major fp32.
+// op(A) is M x K: A stored [m][k] (TA false) or [k][m] (TA true); its k-th column
+// is scaled by ks[b][k] when ks is given.  op(B) is K x N: B stored [k][n] (TB
+// false) or [n][k] (TB true).  rs scales output rows.  mask: 0 none, 1 keep
+// n < m, 2 keep n <= m.  One workgroup computes a 64 x 64 tile; M, N, K are
+// multiples of 64, 64 and 16.
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  const float* A = a.A + b * a.sA;
+  const float* B = a.B + b * a.sB;
+  const float* ks = a.ks ? a.ks + b * a.sks : nullptr;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += 16) {
+    if (!TA) {
+      const int m = tid >> 2, k = (tid & 3) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(m0 + m) * a.lda + k0 + k);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[k + e][m] = ks ? vv[e] * ks[k0 + k + e] : vv[e];
+    } else {
+      const int k = tid >> 4, m = (tid & 15) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(k0 + k) * a.lda + m0 + m);
+      const float s = ks ? ks[k0 + k] : 1.f;
+      As[k][m] = v.x * s; As[k][m + 1] = v.y * s; As[k][m + 2] = v.z * s; As[k][m + 3] = v.w * s;
+    }
+    if (!TB) {
+      const int k = tid >> 4, n = (tid & 15) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * a.ldb + n0 + n);
+      Bs[k][n] = v.x; Bs[k][n + 1] = v.y; Bs[k][n + 2] = v.z; Bs[k][n + 3] = v.w;
+    } else {
+      const int n = tid >> 2, k = (tid & 3) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * a.ldb + k0 + k);
+      Bs[k][n] = v.x; Bs[k + 1][n] = v.y; Bs[k + 2][n] = v.z; Bs[k + 3][n] = v.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* Cb = a.C + b * a.sC;
+  const float* Db = a.Dm ? a.Dm + b * a.sD : nullptr;
+  const float* rs = a.rs ? a.rs + b * a.srs : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    const float r = rs ? rs[m] : 1.f;
+    float out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      float v = a.alpha * acc[i][j];
+      if (Db) v += Db[(int64_t)m * a.ldd + n];
+      v *= r;
+      if ((a.mask == 1 && n >= m) || (a.mask == 2 && n > m)) v = 0.f;
+      out[j] = v;
+    }
+    *reinterpret_cast<float4*>(Cb + (int64_t)m * a.ldc + n0 + tx * 4) =
+        make_float4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+// ---------------------------------------------------------------- chunk prep
+// One workgroup per batch (slot, head): loads the chunk's rows (zero past the
+// sequence), forms G, the gated tiles, dO' = scale dO and the per-row beta.
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) {
+  const int64_t bidx = blockIdx.x;
+  const int64_t slot = bidx / p.H;
+  const int h = (int)(bidx % p.H);
+  const int n = slot_seq(p, slot);
+  const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
+  const int64_t c = slot - (n + bos / C);
+  const int64_t rest = len - c * C;
+  const int valid = (c < 0 || rest <= 0) ? 0 : rest < C ? (int)rest : C;
+  const int t = threadIdx.x;
+  const int HD = p.H * D;
+  if (t < C) w.beta[bidx * C + t] = t < valid ? p.beta[(bos + c * C + t) * p.H + h] : 0.f;
+  if (t == 0) w.valid[bidx] = valid;
+  // thread t: channel t % 128, rows of parity t / 128
+  const int ch = t & 127, half = t >> 7;
+  // G: inclusive cumsum over the chunk (natural log), one channel per thread
+  __shared__ float gs[C][D];
+  for (int r = half; r < C; r += 2)
+    gs[r][ch] = r < valid ? p.g[((bos + c * C + r) * p.H + h) * D + ch] : 0.f;
+  __syncthreads();
+  if (half == 0) {
+    float run = 0.f;
+    for (int r = 0; r < C; ++r) { run += gs[r][ch]; gs[r][ch] = run; }
+  }
+  __syncthreads();
+  const float Glast = gs[C - 1][ch];
+  const float gam = expf(Glast);
+  if (half == 0) w.gam[bidx * D + ch] = gam;
+  const int64_t tb = bidx * (C * D);
+  for (int r = half; r < C; r += 2) {
+    const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
+    const bool in = r < valid;
+    const float qf = in ? bf2f_u16(p.q[row]) : 0.f;
+    const float kf = in ? bf2f_u16(p.k[row]) : 0.f;
+    const float vf = in ? bf2f_u16(p.v[row]) : 0.f;
+    const float df = in ? p.scale * bf2f_u16(p.dout[row]) : 0.f;
+    const float G = gs[r][ch];
+    const float e = expf(G), ei = expf(-G);
+    const int64_t o = tb + r * D + ch;
+    w.G[o] = G;
+    w.kg[o] = kf * e;
+    w.qg[o] = qf * e;
+    w.kh[o] = kf * ei;
+    w.kp[o] = kf * ei * gam;
+    w.vv[o] = vf;
+    w.dO[o] = df;
+    w.kk[o] = kf;
+    w.qq[o] = qf;
+  }
+}
+
+// ---------------------------------------------------------------- T = (I + A)^-1
+// A strictly lower 64 x 64; thread j forms column j by forward substitution.
+__global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* T) {
+  __shared__ float As[C][C + 1];
+  const int64_t b = blockIdx.x;
+  const int j = threadIdx.x;
+  for (int r = 0; r < C; ++r) As[r][j] = A[b * C * C + r * C + j];
+  __syncthreads();
+  float col[C];
+#pragma unroll
+  for (int r = 0; r < C; ++r) {
+    float v = r == j ? 1.f : 0.f;
+    if (r > j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) s = fmaf(As[r][i], col[i], s);
+      v = -s;
+    }
+    col[r] = v;
+  }
+#pragma unroll
+  for (int r = 0; r < C; ++r) T[b * C * C + r * C + j] = col[r];
+}
+
+// ---------------------------------------------------------------- serial dS
+// One workgroup per (sequence, head), chunks last to first:
+//   dSn(c) is stored for the chunk's gradient products, then
+//   dS = Diag(gam) dSn - F (kp dSn) + X  becomes the next dSn.
+// The sequence's initial-state gradient is the last dS.
+__global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
+  __shared__ float ds[D][D + 4];   // dSn, then the new dS
+  __shared__ float pp[C][D + 4];   // P = kp dSn
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int t = threadIdx.x;
+  const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
+  const int nch = (int)((len + C - 1) / C);
+  const size_t sd = (size_t)D * D;
+  // dS_final (or zero)
+  for (int x = t; x < D * D; x += 256) {
+    const int r = x / D, j = x % D;
+    float v = 0.f;
+    if (p.dsT) {
+      const size_t o = ((size_t)n * p.H + h) * sd + x;
+      v = p.dsT_fp32 ? static_cast<const float*>(p.dsT)[o] : bf2f_u16(static_cast<const uint16_t*>(p.dsT)[o]);
+    }
+    ds[r][j] = v;
+  }
+  __syncthreads();
+  const int jb = (t & 31) * 4;    // 4 value columns
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t bidx = (n + bos / C + c) * p.H + h;
+    // keep dSn for this chunk's products
+    float* dsn = w.dSn + bidx * sd;
+    for (int x = t; x < D * D; x += 256) dsn[x] = ds[x / D][x % D];
+    // P = kp dSn: rows 8 (t / 32) .. +7, columns jb .. jb+3
+    {
+      const float* kp = w.kp + bidx * (C * D);
+      const int r0 = (t >> 5) * 8;
+      float acc[8][4] = {};
+      for (int k = 0; k < D; ++k) {
+        const float4 bv = *reinterpret_cast<const float4*>(&ds[k][jb]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float av = kp[(r0 + i) * D + k];
+          acc[i][0] = fmaf(av, bv.x, acc[i][0]); acc[i][1] = fmaf(av, bv.y, acc[i][1]);
+          acc[i][2] = fmaf(av, bv.z, acc[i][2]); acc[i][3] = fmaf(av, bv.w, acc[i][3]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<float4*>(&pp[r0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+    __syncthreads();
+    // dS = gam (.) dSn - F P + X: rows 16 (t / 32) .. +15, columns jb .. jb+3
+    {
+      const float* F = w.F + bidx * (D * C);
+      const float* X = w.X + bidx * sd;
+      const float* gam = w.gam + bidx * D;
+      const int c0 = (t >> 5) * 16;
+      float acc[16][4];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float g = gam[c0 + i];
+        const float4 xv = *reinterpret_cast<const float4*>(&X[(c0 + i) * D + jb]);
+        acc[i][0] = g * ds[c0 + i][jb] + xv.x;
+        acc[i][1] = g * ds[c0 + i][jb + 1] + xv.y;
+        acc[i][2] = g * ds[c0 + i][jb + 2] + xv.z;
+        acc[i][3] = g * ds[c0 + i][jb + 3] + xv.w;
+      }
+      for (int r = 0; r < C; ++r) {
+        const float4 bv = *reinterpret_cast<const float4*>(&pp[r][jb]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float av = F[(c0 + i) * C + r];
+          acc[i][0] = fmaf(-av, bv.x, acc[i][0]); acc[i][1] = fmaf(-av, bv.y, acc[i][1]);
+          acc[i][2] = fmaf(-av, bv.z, acc[i][2]); acc[i][3] = fmaf(-av, bv.w, acc[i][3]);
+        }
+      }
+      __syncthreads();  // every read of dSn and P is done
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *reinterpret_cast<float4*>(&ds[c0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+    __syncthreads();
+  }
+  if (p.ds0) {
+    float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
+    for (int x = t; x < D * D; x += 256) o[x] = ds[x / D][x % D];
+  }
+}
+
+// ---------------------------------------------------------------- gates and scatter
+// One workgroup per batch: dq, dk, dv, dg, dbeta of the chunk's rows.
+__global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles w) {
+  const int64_t bidx = blockIdx.x;
+  const int valid = w.valid[bidx];
+  if (valid == 0) return;
+  const int64_t slot = bidx / p.H;
+  const int h = (int)(bidx % p.H);
+  const int n = slot_seq(p, slot);
+  const int64_t bos = seq_bos(p, n);
+  const int64_t c = slot - (n + bos / C);
+  const int t = threadIdx.x, ch = t & 127, half = t >> 7;
+  const int HD = p.H * D;
+  const int64_t tb = bidx * (C * D);
+  const float* beta = w.beta + bidx * C;
+  __shared__ float dGs[C][D];
+  __shared__ float red[2][D];
+  __shared__ float dbs[2][C];
+  // per row: dG, dq, dk, dv; per channel: dG_last pieces
+  float glast = 0.f;
+  for (int r = half; r < C; r += 2) {
+    const int64_t o = tb + r * D + ch;
+    const float G = w.G[o];
+    const float e = expf(G), ei = expf(-G);
+    const float gam = w.gam[bidx * D + ch];
+    const float dqg = w.dqg[o], dkg = w.dkg[o], dkh = w.dkh[o], dkp = w.dkp[o];
+    const float kf = w.kk[o], qf = w.qq[o];
+    const float kp = kf * ei * gam;
+    dGs[r][ch] = dqg * qf * e + dkg * kf * e - dkh * kf * ei - dkp * kp;
+    glast += dkp * kp;
+    if (r < valid) {
+      const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
+      p.dq[row] = dqg * e;
+      p.dk[row] = dkg * e + dkh * ei + dkp * gam * ei;
+      p.dv[row] = beta[r] * w.dY[o];
+    }
+  }
+  red[half][ch] = glast;
+  // dgam_direct: rowsum over j of S * dSn for channel ch (threads of half 0 and 1 split j)
+  {
+    const float* S = w.S + bidx * (size_t)(D * D);
+    const float* dsn = w.dSn + bidx * (size_t)(D * D);
+    float s = 0.f;
+    for (int j = half * 64; j < half * 64 + 64; ++j) s += S[ch * D + j] * dsn[ch * D + j];
+    __syncthreads();
+    red[half][ch] += s * w.gam[bidx * D + ch];
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float dGlast = red[0][ch] + red[1][ch];
+    // dg_t = sum_{r >= t} dG_r + dG_last
+    float run = dGlast;
+    for (int r = C - 1; r >= 0; --r) {
+      run += dGs[r][ch];
+      if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + ch] = run;
+    }
+  }
+  // dbeta_r = sum_j dY_rj R_rj + sum_i dA_ri P_ri (two threads per row)
+  if (t < 2 * C) {
+    const int r = t >> 1, part = t & 1;
+    float s = 0.f;
+    for (int j = part * 64; j < part * 64 + 64; ++j) s += w.dY[tb + r * D + j] * w.R[tb + r * D + j];
+    for (int i = part * 32; i < part * 32 + 32; ++i)
+      s += w.dA[bidx * C * C + r * C + i] * w.P[bidx * C * C + r * C + i];
+    dbs[part][r] = s;
+  }
+  __syncthreads();
+  if (t < valid) p.dbeta[(bos + c * C + t) * p.H + h] = dbs[0][t] + dbs[1][t];
+}
+
+void gemm(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.N / 64, a.M / 64, a.batches), block(256);
+  if (!ta && !tb) hipLaunchKernelGGL((bgemm_kernel<false, false>), grid, block, 0, s, a);
+  else if (!ta && tb) hipLaunchKernelGGL((bgemm_kernel<false, true>), grid, block, 0, s, a);
+  else if (ta && !tb) hipLaunchKernelGGL((bgemm_kernel<true, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bgemm_kernel<true, true>), grid, block, 0, s, a);
+}
+
+// op(A) M x K times op(B) K x N over every batch; strides are per-batch element counts.
+GemmArgs mm(int M, int N, int K, const float* A, int64_t sA, int lda, const float* B, int64_t sB,
+            int ldb, float* Cm, int64_t sC, int ldc, int batches) {
+  GemmArgs a{};
+  a.M = M; a.N = N; a.K = K;
+  a.A = A; a.sA = sA; a.lda = lda;
+  a.B = B; a.sB = sB; a.ldb = ldb;
+  a.C = Cm; a.sC = sC; a.ldc = ldc;
+  a.alpha = 1.f;
+  a.batches = batches;
+  return a;
+}
+
+}  // namespace
+
+size_t bwd_tile_floats() { return BwdTiles::floats_per_batch(); }
+
+hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t s) {
+  const BwdTiles w{};
+  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H)), dim3(256), 0, s, p, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+  const int NB = (int)batches;
+  const int64_t t1 = C * D, t2 = C * C, t3 = D * D, tf = D * C;
+  // chunk tiles
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(NB), dim3(256), 0, s, p, w);
+  // A = strict_lower(diag(b) kg kh^T), P = strict_lower(kg kh^T), M = lower_incl(qg kh^T)
+  {
+    GemmArgs a = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
+    a.mask = 1;
+    gemm(false, true, a, s);
+    a.C = w.A; a.rs = w.beta; a.srs = C;
+    gemm(false, true, a, s);
+    GemmArgs m = mm(C, C, D, w.qg, t1, D, w.kh, t1, D, w.M, t2, C, NB);
+    m.mask = 2;
+    gemm(false, true, m, s);
+  }
+  hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
+  // R = V - kg S;  U = T diag(b) R
+  {
+    GemmArgs a = mm(C, D, D, w.kg, t1, D, w.S, t3, D, w.R, t1, D, NB);
+    a.alpha = -1.f; a.Dm = w.vv; a.sD = t1; a.ldd = D;
+    gemm(false, false, a, s);
+    GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
+    u.ks = w.beta; u.sks = C;
+    gemm(false, false, u, s);
+  }
+  // MtdO = M^T dO';  F = kg^T diag(b) T^T;  X = qg^T dO' - F MtdO
+  {
+    gemm(true, false, mm(C, D, C, w.M, t2, C, w.dO, t1, D, w.MtdO, t1, D, NB), s);
+    GemmArgs f = mm(D, C, C, w.kg, t1, D, w.T, t2, C, w.F, tf, C, NB);
+    f.ks = w.beta; f.sks = C;
+    gemm(true, true, f, s);
+    gemm(true, false, mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB), s);
+    GemmArgs x = mm(D, D, C, w.F, tf, C, w.MtdO, t1, D, w.X, t3, D, NB);
+    x.alpha = -1.f; x.Dm = w.X; x.sD = t3; x.ldd = D;
+    gemm(false, false, x, s);
+  }
+  // serial recurrence of dS over chunks
+  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H)), dim3(256), 0, s, p, w);
+  // chunk gradients
+  {
+    GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
+    du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
+    gemm(false, false, du, s);
+    GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
+    dm.mask = 2;
+    gemm(false, true, dm, s);
+    gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
+    GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
+    da.alpha = -1.f; da.mask = 1;
+    gemm(false, true, da, s);
+    gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
+    GemmArgs q2 = mm(C, D, C, w.dM, t2, C, w.kh, t1, D, w.dqg, t1, D, NB);  // + dM kh
+    q2.Dm = w.dqg; q2.sD = t1; q2.ldd = D;
+    gemm(false, false, q2, s);
+    gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
+    gemm(false, false, mm(C, D, C, w.dA, t2, C, w.kh, t1, D, w.dkg, t1, D, NB), s);  // dA kh
+    GemmArgs k2 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // diag(b)(dA kh - dY S^T)
+    k2.alpha = -1.f; k2.Dm = w.dkg; k2.sD = t1; k2.ldd = D; k2.rs = w.beta; k2.srs = C;
+    gemm(false, true, k2, s);
+    gemm(true, false, mm(C, D, C, w.dM, t2, C, w.qg, t1, D, w.dkh, t1, D, NB), s);  // dM^T qg
+    GemmArgs h2 = mm(C, D, C, w.dA, t2, C, w.kg, t1, D, w.dkh, t1, D, NB);  // + dA^T diag(b) kg
+    h2.ks = w.beta; h2.sks = C; h2.Dm = w.dkh; h2.sD = t1; h2.ldd = D;
+    gemm(true, false, h2, s);
+  }
+  hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
+  return hipGetLastError();
+}
+
+}  // namespace kda

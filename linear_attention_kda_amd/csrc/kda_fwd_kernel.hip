@@ -274,6 +274,7 @@ struct Work {
   void* s1;        // where its end state goes, or null
   __bf16* o;       // output rows, bf16 [rows][H][128]
   uint16_t* sb;    // also the end state in the fix-up's bf16 operand order, or null
+  float* ck;       // checkpoint of the run's first chunk (chunk c at + c * H * 128 * 128), or null
 };
 
 // Buffer descriptor over `bytes` bytes from `base`; loads beyond the range return
@@ -824,6 +825,16 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 
     // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
     // (the prep waves store -K exp(G) and Q exp(G))
+    if (act && w.ck != nullptr) {  // the state entering this chunk, for the backward pass
+      float* ck = w.ck + (size_t)it * p.H * (D * D);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            ck[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = Sacc[ct][jt][t];
+    }
     if (act) {
       bf16x8 Sfrag[4][JT];  // bf16 copy of the state in the k-slot order of the products
 #pragma unroll
@@ -1261,6 +1272,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     }
     w.o = reinterpret_cast<__bf16*>(p.out);
     w.vzero = 0;
+    w.ck = p.ckpt == nullptr ? nullptr : p.ckpt + ((size_t)(n + bos / C) * p.H + w.h) * (D * D);
   } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
     const int sp = (kind + 1) >> 1;
     const bool ident = (kind & 1) == 0;
@@ -1272,6 +1284,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.s1 = p.st + ((size_t)((ident ? 1 : 2) * p.emax + slot0 + sp - 1) * p.H) * (D * D) + hd2;
     w.s1_fp32 = 1;
     w.o = reinterpret_cast<__bf16*>(ident ? p.out : p.o0);
+    w.ck = nullptr;
     w.vzero = ident ? 1 : 0;
     w.sb = nullptr;
   }

@@ -46,6 +46,10 @@ struct Params {
   uint16_t* o0;           // bf16 [rows][H][128]: outputs of later segments from a zero state
   float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
   uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
+  // Backward support: the fp32 state at the start of every chunk, at slot
+  // n + floor(bos_n / 64) + c of sequence n's chunk c ([slots][H][128][128]), or
+  // null.  Requires emax = 0 (no sequence splitting).
+  float* ckpt;
 };
 
 // Workspace bytes for splitting with `emax` state slots over `rows` packed
@@ -77,6 +81,61 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// ---- backward
+struct BwdParams {
+  const uint16_t* q;      // bf16 [rows][H][128]
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;   // bf16 [rows][H][128]: dL/do
+  const float* g;         // fp32 [rows][H][128]
+  const float* beta;      // fp32 [rows][H]
+  const int32_t* cu;      // [N+1] or null
+  int64_t T;              // tokens per batch row (fixed-length mode)
+  float scale;
+  int nseq;
+  int H;
+  const void* dsT;        // dL/dS_final [N][H][128][128] or null
+  int dsT_fp32;
+  float* dq;              // fp32 [rows][H][128]
+  float* dk;
+  float* dv;
+  float* dg;
+  float* dbeta;           // fp32 [rows][H]
+  float* ds0;             // fp32 [N][H][128][128] or null
+};
+
+// Per-chunk fp32 tiles of the backward, each an array over batches b = slot * H + h.
+struct BwdTiles {
+  // [b][64][128]
+  float *G, *kg, *qg, *kh, *kp, *vv, *dO, *kk, *qq, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkh, *dkp;
+  float *A, *P, *M, *T, *dM, *dA;   // [b][64][64]
+  float* F;                          // [b][128][64]
+  float *S, *X, *dSn;                // [b][128][128]; S: chunk start states (the checkpoints)
+  float* beta;                       // [b][64]
+  float* gam;                        // [b][128]
+  int* valid;                        // [b]
+  static constexpr size_t floats_per_batch() {
+    return 18 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 128 + 1;
+  }
+};
+
+struct GemmArgs {
+  int M, N, K, batches;
+  const float* A; int64_t sA; int lda;
+  const float* B; int64_t sB; int ldb;
+  float* C; int64_t sC; int ldc;
+  const float* Dm; int64_t sD; int ldd;   // added before the row scale, or null
+  const float* rs; int64_t srs;           // row scale of the output, or null
+  const float* ks; int64_t sks;           // scale of op(A)'s k-th column, or null
+  float alpha;
+  int mask;                               // 0 none, 1 keep n < m, 2 keep n <= m
+};
+
+size_t bwd_tile_floats();
+hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
+// The initial-state gradients alone, for calls without tokens.
+hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and

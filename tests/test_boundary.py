@@ -33,7 +33,8 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert header_functions() == ["kda_decode", "kda_decode_check", "kda_fwd", "kda_fwd_check",
+    assert header_functions() == ["kda_bwd", "kda_bwd_check", "kda_bwd_workspace_bytes",
+                                  "kda_decode", "kda_decode_check", "kda_fwd", "kda_fwd_check",
                                   "kda_gdn_decode", "kda_gdn_decode_check", "kda_gdn_fwd",
                                   "kda_gdn_fwd_check", "kda_last_error", "kda_plan",
                                   "kda_status_string"]
@@ -131,6 +132,39 @@ def test_gdn_checks_take_a_scalar_gate(lib):
     assert binding.gdn_decode_check(**dec_args(g=P + 2)) == ERR_ALIGN
     assert binding.gdn_decode_check(**dec_args(state_dtype=2)) == ERR_DTYPE
     assert binding.gdn_decode_check(**dec_args(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state=0)) == OK
+
+
+def bwd_args(**over):
+    a = dict(B=1, T=256, H=4, K=128, V=128, q=P, k=P + 0x1000, v=P + 0x2000, g=P + 0x3000,
+             beta=P + 0x4000, d_out=P + 0x5000, dq=P + 0x6000, dk=P + 0x7000, dv=P + 0x8000,
+             dg=P + 0x9000, dbeta=P + 0xa000)
+    a.update(over)
+    return a
+
+
+def test_bwd_check(lib):
+    assert binding.bwd_check(**bwd_args()) == OK
+    assert binding.bwd_check(**bwd_args(initial_state=P, initial_dtype=0, d_final_state=P + 0x100,
+                                        d_final_dtype=1, d_initial_state=P + 0x200)) == OK
+    assert binding.bwd_check(**bwd_args(cu_seqlens=P, num_seqs=3)) == OK
+    assert binding.bwd_check(**bwd_args(T=0, q=0, k=0, v=0, g=0, beta=0, d_out=0, dq=0, dk=0,
+                                        dv=0, dg=0, dbeta=0)) == OK
+    assert binding.bwd_check(**bwd_args(K=64)) == ERR_HEAD_DIM
+    assert binding.bwd_check(**bwd_args(d_out=0)) == ERR_NULL
+    assert binding.bwd_check(**bwd_args(dg=0)) == ERR_NULL
+    assert binding.bwd_check(**bwd_args(dq=P + 8)) == ERR_ALIGN
+    assert binding.bwd_check(**bwd_args(dbeta=P + 2)) == ERR_ALIGN
+    assert binding.bwd_check(**bwd_args(d_final_state=P, d_final_dtype=3)) == ERR_DTYPE
+    assert binding.bwd_check(**bwd_args(B=2, cu_seqlens=P, num_seqs=2)) == ERR_VARLEN_BATCH
+
+
+def test_bwd_workspace_bytes(lib):
+    # slots: N + ceil(rows / 64) + 1, each holding every head's per-chunk tiles
+    per = (18 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 128 + 1) * 4
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    nb = (1 + 8192 // 64 + 1) * 32
+    assert binding.bwd_workspace_bytes(1, 8192, 32) == up(nb * per) + up(8192 * 32 * 128 * 2)
+    assert binding.bwd_workspace_bytes(0, 8192, 32) == -1
 
 
 def test_state_dtype_ignored_for_absent_state(lib):
