@@ -26,7 +26,8 @@
 // n + floor(bos_n / 64) + c of sequence n's chunk c (slots are distinct across
 // sequences); batch index b = slot * H + h addresses every per-chunk tile.
 // Everything here is fp32: the chunk-local products run as batched tiled GEMMs
-// (VALU), the serial recurrence in one workgroup per (sequence, head).
+// (VALU), the serial recurrence in four workgroups per (sequence, head), one per
+// 32 value columns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -214,89 +215,103 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 }
 
 // ---------------------------------------------------------------- serial dS
-// One workgroup per (sequence, head), chunks last to first:
-//   dSn(c) is stored for the chunk's gradient products, then
-//   dS = Diag(gam) dSn - F (kp dSn) + X  becomes the next dSn.
-// The sequence's initial-state gradient is the last dS.
+// Column j of dS depends only on column j of dSn (Diag(gam), kp and F act on
+// rows), so each (sequence, head) runs as DSC workgroups of DSW value columns.
+// Chunks last to first: dSn(c) is stored for the chunk's gradient products,
+// then dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The
+// sequence's initial-state gradient is the last dS.
+constexpr int DSW = 32;            // value columns per workgroup
+constexpr int DSC = D / DSW;       // workgroups per (sequence, head)
+
 __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
-  __shared__ float ds[D][D + 4];   // dSn, then the new dS
-  __shared__ float pp[C][D + 4];   // P = kp dSn
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  __shared__ float ds[D][DSW + 4];   // dSn, then the new dS (this workgroup's columns)
+  __shared__ float pp[C][DSW + 4];   // P = kp dSn
+  const int pair = blockIdx.x / DSC, j0 = (blockIdx.x % DSC) * DSW;
+  const int n = pair / p.H, h = pair % p.H;
   const int t = threadIdx.x;
   const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
   const int nch = (int)((len + C - 1) / C);
   const size_t sd = (size_t)D * D;
-  // dS_final (or zero)
-  for (int x = t; x < D * D; x += 256) {
-    const int r = x / D, j = x % D;
+  for (int x = t; x < D * DSW; x += 256) {   // dS_final (or zero)
+    const int r = x / DSW, j = x % DSW;
     float v = 0.f;
     if (p.dsT) {
-      const size_t o = ((size_t)n * p.H + h) * sd + x;
+      const size_t o = ((size_t)n * p.H + h) * sd + (size_t)r * D + j0 + j;
       v = p.dsT_fp32 ? static_cast<const float*>(p.dsT)[o] : bf2f_u16(static_cast<const uint16_t*>(p.dsT)[o]);
     }
     ds[r][j] = v;
   }
   __syncthreads();
-  const int jb = (t & 31) * 4;    // 4 value columns
+  const int jb = (t & 7) * 4;   // 4 of this workgroup's columns
   for (int c = nch - 1; c >= 0; --c) {
     const int64_t bidx = (n + bos / C + c) * p.H + h;
-    // keep dSn for this chunk's products
     float* dsn = w.dSn + bidx * sd;
-    for (int x = t; x < D * D; x += 256) dsn[x] = ds[x / D][x % D];
-    // P = kp dSn: rows 8 (t / 32) .. +7, columns jb .. jb+3
-    {
+    for (int x = t; x < D * DSW; x += 256) dsn[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
+    {  // P = kp dSn: rows 2 (t / 8) .. +1
       const float* kp = w.kp + bidx * (C * D);
-      const int r0 = (t >> 5) * 8;
-      float acc[8][4] = {};
-      for (int k = 0; k < D; ++k) {
-        const float4 bv = *reinterpret_cast<const float4*>(&ds[k][jb]);
+      const int r0 = (t >> 3) * 2;
+      float acc[2][4] = {};
+      for (int k = 0; k < D; k += 4) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&kp[r0 * D + k]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&kp[(r0 + 1) * D + k]);
+        const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float av = kp[(r0 + i) * D + k];
-          acc[i][0] = fmaf(av, bv.x, acc[i][0]); acc[i][1] = fmaf(av, bv.y, acc[i][1]);
-          acc[i][2] = fmaf(av, bv.z, acc[i][2]); acc[i][3] = fmaf(av, bv.w, acc[i][3]);
+        for (int kk = 0; kk < 4; ++kk) {
+          const float4 bv = *reinterpret_cast<const float4*>(&ds[k + kk][jb]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            acc[i][0] = fmaf(av[i][kk], bv.x, acc[i][0]); acc[i][1] = fmaf(av[i][kk], bv.y, acc[i][1]);
+            acc[i][2] = fmaf(av[i][kk], bv.z, acc[i][2]); acc[i][3] = fmaf(av[i][kk], bv.w, acc[i][3]);
+          }
         }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 2; ++i)
         *reinterpret_cast<float4*>(&pp[r0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
     __syncthreads();
-    // dS = gam (.) dSn - F P + X: rows 16 (t / 32) .. +15, columns jb .. jb+3
-    {
+    {  // dS = gam (.) dSn - F P + X: rows 4 (t / 8) .. +3
       const float* F = w.F + bidx * (D * C);
       const float* X = w.X + bidx * sd;
       const float* gam = w.gam + bidx * D;
-      const int c0 = (t >> 5) * 16;
-      float acc[16][4];
+      const int c0 = (t >> 3) * 4;
+      float acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const float g = gam[c0 + i];
-        const float4 xv = *reinterpret_cast<const float4*>(&X[(c0 + i) * D + jb]);
+        const float4 xv = *reinterpret_cast<const float4*>(&X[(size_t)(c0 + i) * D + j0 + jb]);
         acc[i][0] = g * ds[c0 + i][jb] + xv.x;
         acc[i][1] = g * ds[c0 + i][jb + 1] + xv.y;
         acc[i][2] = g * ds[c0 + i][jb + 2] + xv.z;
         acc[i][3] = g * ds[c0 + i][jb + 3] + xv.w;
       }
-      for (int r = 0; r < C; ++r) {
-        const float4 bv = *reinterpret_cast<const float4*>(&pp[r][jb]);
+      for (int r = 0; r < C; r += 4) {
+        float fv[4][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float av = F[(c0 + i) * C + r];
-          acc[i][0] = fmaf(-av, bv.x, acc[i][0]); acc[i][1] = fmaf(-av, bv.y, acc[i][1]);
-          acc[i][2] = fmaf(-av, bv.z, acc[i][2]); acc[i][3] = fmaf(-av, bv.w, acc[i][3]);
+        for (int i = 0; i < 4; ++i) {
+          const float4 f4 = *reinterpret_cast<const float4*>(&F[(c0 + i) * C + r]);
+          fv[i][0] = f4.x; fv[i][1] = f4.y; fv[i][2] = f4.z; fv[i][3] = f4.w;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 bv = *reinterpret_cast<const float4*>(&pp[r + rr][jb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][0] = fmaf(-fv[i][rr], bv.x, acc[i][0]); acc[i][1] = fmaf(-fv[i][rr], bv.y, acc[i][1]);
+            acc[i][2] = fmaf(-fv[i][rr], bv.z, acc[i][2]); acc[i][3] = fmaf(-fv[i][rr], bv.w, acc[i][3]);
+          }
         }
       }
       __syncthreads();  // every read of dSn and P is done
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 4; ++i)
         *reinterpret_cast<float4*>(&ds[c0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
     __syncthreads();
   }
   if (p.ds0) {
     float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
-    for (int x = t; x < D * D; x += 256) o[x] = ds[x / D][x % D];
+    for (int x = t; x < D * DSW; x += 256) o[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
   }
 }
 
@@ -397,7 +412,7 @@ size_t bwd_tile_floats() { return BwdTiles::floats_per_batch(); }
 
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t s) {
   const BwdTiles w{};
-  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H)), dim3(256), 0, s, p, w);
+  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H * DSC)), dim3(256), 0, s, p, w);
   return hipGetLastError();
 }
 
@@ -439,7 +454,7 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     gemm(false, false, x, s);
   }
   // serial recurrence of dS over chunks
-  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H)), dim3(256), 0, s, p, w);
+  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H * DSC)), dim3(256), 0, s, p, w);
   // chunk gradients
   {
     GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
