@@ -224,6 +224,49 @@ def gdn_bench(wid: int, steps: int, warmup: int):
                          "kernel": "kda_gdn_fwd call", "algorithmic_bytes": nbytes}}
 
 
+def bwd_bench(wid: int, steps: int, warmup: int):
+    """The backward pass (kda_bwd) on workload `wid` with seeded upstream gradients."""
+    import torch
+
+    from linear_attention_kda_amd import binding, perfmodel
+    from linear_attention_kda_amd.workloads import make_inputs
+
+    x = make_inputs(wid, "cuda")
+    w = x["workload"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1400 + wid)
+    do = torch.randn(x["v"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+
+    def step():
+        binding.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["scale"],
+                    initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per token-head: q, k, v, dO bf16, g fp32, beta read; dq, dk, dv, dg fp32, dbeta written;
+    # per (sequence, head): the initial state read and its gradient written (fp32)
+    N, H = w.num_states, w.H
+    nbytes = w.tokens * H * (4 * 128 * 2 + 128 * 4 + 4 + 4 * 128 * 4 + 4) \
+        + (perfmodel.state_bytes(N, H, state_bytes_of(w.init_state)) if w.init_state else 0) \
+        + perfmodel.state_bytes(N, H, 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] bwd {w.name}: {ms:.3f} ms, {w.tokens / ms / 1e3:.2f} M tokens/s, "
+        f"{gbs:.0f} GB/s ({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return {"workload": f"backward, {w.name}", "unit": "tokens/s", "value": w.tokens / (ms * 1e-3),
+            "ms_per_step": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kda_bwd call", "algorithmic_bytes": nbytes}}
+
+
 def counter_run(wid: int):
     """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes.
 
@@ -265,6 +308,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate line")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward line")
+    ap.add_argument("--bwd-workload", type=int, default=1)
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--counters", action="store_true",
                     help="untimed run for hardware-counter passes: a 1 GiB device copy "
@@ -321,6 +366,10 @@ def main():
     if not args.no_gdn:
         gdn = gdn_bench(args.workload, args.steps, args.warmup)
 
+    bwd = None
+    if not args.no_bwd:
+        bwd = bwd_bench(args.bwd_workload, max(3, args.steps // 4), 1)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads of {w.name}")
@@ -356,6 +405,7 @@ def main():
         "secondary": secondary,
         "decode": decode,
         "gdn": gdn,
+        "bwd": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
