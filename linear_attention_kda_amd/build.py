@@ -15,8 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = [os.path.join(CSRC, "kda_api.cpp"), os.path.join(CSRC, "kda_fwd_kernel.hip"),
-           os.path.join(CSRC, "kda_decode_kernel.hip"), os.path.join(CSRC, "kda_bwd.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("kda_api.cpp", "kda_fwd_kernel.hip", "kda_gdn_kernel.hip", "kda_decode_kernel.hip",
+            "kda_bwd.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code; the host pass

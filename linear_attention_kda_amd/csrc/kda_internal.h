@@ -29,7 +29,6 @@ struct Params {
   const float* g;         // fp32 [rows][H][128], or [rows][H] when g_scalar
   const float* beta;      // fp32 [rows][H]
   uint16_t* out;          // bf16 [rows][H][128]
-  int g_scalar;           // one gate per token and head (Gated DeltaNet)
   const void* s0;         // [N][H][128][128] or null
   void* s1;               // [N][H][128][128] or null
   const int32_t* cu;      // [N+1] or null
@@ -50,6 +49,7 @@ struct Params {
   // n + floor(bos_n / 64) + c of sequence n's chunk c ([slots][H][128][128]), or
   // null.  Requires emax = 0 (no sequence splitting).
   float* ckpt;
+  int g_scalar;           // one gate per token and head (Gated DeltaNet)
 };
 
 // Workspace bytes for splitting with `emax` state slots over `rows` packed
@@ -141,6 +141,8 @@ hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
 // the segment scan and output fix-up kernels follow the main kernel.
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream);
+// The fused kernel alone with the scalar gate (p.g_scalar), wgs workgroups.
+hipError_t launch_fwd_main_scalar_gate(const Params& p, int nsplit, unsigned wgs, hipStream_t stream);
 
 }  // namespace kda
 
