@@ -24,7 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KDA fwd prefill tokens/s (H=32,d=128) at T=8K and 64K varlen; % of roofline"
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_kda_amd", "csrc", "kda_fwd_kernel.hip")
+# the sources of the measured kernels: the fused kernel body and its launch / tail kernel
+KERNEL_SRCS = [os.path.join(ROOT, "linear_attention_kda_amd", "csrc", f)
+               for f in ("kda_fwd_core.h", "kda_fwd_kernel.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_fwd_traffic.json")
 KERNEL_NAME = "kda_fwd call: kda_fwd_kernel + kda_tail_kernel (scan, fix-up)"
 
@@ -34,8 +36,11 @@ def log(msg):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def state_bytes_of(dtype_name):

@@ -7,7 +7,8 @@
  *   alpha_t = exp(g_t)   (a per-channel decay vector),
  *   o_t     = scale * S_t^T q_t   (readout after the update at t),
  *
- * with S a 128 x 128 (d_k x d_v) state
+ * with S a d x d (d_k x d_v) state, d = 128 (the published kernel's only
+ * size) or d = 64 / 256
  *   [core.today "Kimi Linear 특집", ch.4 혁신 1 (channel-wise gate) and 혁신 2
  *    (state-update equation); ch.2 (linear-attention readout Q(K^T V));
  *    ch.8 (fixed 128 x 128 state)].
@@ -17,7 +18,8 @@
  *
  * Argument conventions follow the kernel API the pages describe
  * [trend.ondo.sh "MoonshotAI/FlashKDA", section "커널 API와 제약 조건"]:
- * K = V = 128 only; variable-length packing through cu_seqlens requires
+ * K = V = 128 (kda_fwd and kda_gdn_fwd also take K = V = 64 or 256, see below;
+ * the other entry points take 128 only); variable-length packing through cu_seqlens requires
  * B = 1; the initial and final states are each bf16, fp32 or absent, and
  * must have the same dtype when both are given.
  *
@@ -67,7 +69,7 @@ typedef enum {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,         /* a required pointer is NULL */
-  KDA_ERR_HEAD_DIM = -2,     /* K or V is not 128 */
+  KDA_ERR_HEAD_DIM = -2,     /* K, V not a supported head dimension (see each call) */
   KDA_ERR_VARLEN_BATCH = -3, /* cu_seqlens given with B != 1 */
   KDA_ERR_STATE_DTYPE = -4,  /* both states given with different dtypes */
   KDA_ERR_DTYPE = -5,        /* a dtype argument is not a kda_dtype */
@@ -79,21 +81,21 @@ typedef enum {
 /*
  * kda_fwd — chunkwise KDA forward pass (prefill).
  *
- *  q, k, v    device, bf16, [B, T, H, 128] contiguous (channel fastest), 16-byte
+ *  q, k, v    device, bf16, [B, T, H, d] contiguous (channel fastest), 16-byte
  *             aligned.  The kernel does not normalise q or k.
- *  g          device, fp32, [B, T, H, 128], 16-byte aligned: the log-decay,
+ *  g          device, fp32, [B, T, H, d], 16-byte aligned: the log-decay,
  *             alpha = exp(g) taken as given (g <= 0 expected).  Range limit of
  *             the chunked evaluation: within each 16-token block aligned to the
  *             start of a 64-token chunk, the per-channel sum of -g must stay
  *             below 80 (g >= -5 everywhere is sufficient); beyond that the
  *             intra-chunk exponent factors overflow fp32.
  *  beta       device, fp32, [B, T, H], 4-byte aligned: write strength, as given.
- *  scale      multiplies every output (callers usually pass 1/sqrt(128)).
+ *  scale      multiplies every output (callers usually pass 1/sqrt(d)).
  *  initial_state / initial_dtype
- *             device, [N, H, 128, 128] (d_k-major: element (i, j) at i*128 + j),
+ *             device, [N, H, d, d] (d_k-major: element (i, j) at i*d + j),
  *             16-byte aligned, or NULL for a zero initial state.
  *  final_state / final_dtype
- *             device, [N, H, 128, 128], 16-byte aligned, or NULL when not
+ *             device, [N, H, d, d], 16-byte aligned, or NULL when not
  *             wanted.  It may alias initial_state (each state is read in full
  *             before it is overwritten).
  *  cu_seqlens device, int32, [num_seqs + 1], or NULL.  When given: B must be 1,
@@ -105,10 +107,18 @@ typedef enum {
  *             When NULL: every batch row is one sequence of T tokens, N = B,
  *             and num_seqs is ignored.
  *  B, T, H    batch rows, tokens per row (packed total when varlen), heads.
- *  K, V       head dimensions; must both be 128.
- *  out        device, bf16, [B, T, H, 128], 16-byte aligned; rows outside every
+ *  K, V       head dimensions d = K = V: 128, 64 or 256.
+ *  out        device, bf16, [B, T, H, d], 16-byte aligned; rows outside every
  *             sequence (varlen with cu_seqlens[num_seqs] < T) are not written.
  *  stream     hipStream_t to launch on (NULL = null stream).
+ *
+ * d = 64 and d = 256 run as two launches: every (chunk, head) first writes a
+ * record of its chunk-local operands (gated keys and queries, the transposed
+ * state-update operand, (I + A)^-1 diag(beta), the masked Q K^T and the chunk
+ * decay) into a workspace of kda_dim_workspace_bytes() bytes from the library's
+ * pool, then one workgroup per (sequence, head, value slice) walks the chunks in
+ * order.  These sizes never split sequences, and the 16-token range limit on g
+ * above applies to them as well.
  */
 kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float scale, const void* initial_state, int initial_dtype, void* final_state,
@@ -199,7 +209,7 @@ kda_status kda_decode_check(const void* q, const void* k, const void* v, const f
  *             aligned; range limit as kda_fwd's with the same g on every channel.
  * Every other argument, the layouts, the workspace, asynchrony and the status
  * codes are those of kda_fwd (the same kernels run; only the gate load differs,
- * and it reads 4 bytes per token and head instead of 512).
+ * and it reads 4 bytes per token and head instead of 4d).
  */
 kda_status kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, float scale, const void* initial_state,
@@ -272,6 +282,12 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
                          int32_t B, int64_t T, int32_t H, int32_t K, int32_t V, const float* dq,
                          const float* dk, const float* dv, const float* dg, const float* dbeta,
                          const float* d_initial_state);
+
+/* Workspace bytes kda_fwd / kda_gdn_fwd take at head dimension d = 64 or 256
+ * for N sequences over `rows` packed rows (T with cu_seqlens, else B*T) of H
+ * heads: one record per (chunk slot, head), N + ceil(rows / 64) + 1 slots
+ * (-1 for N <= 0, rows < 0, H <= 0 or another d).  Host only. */
+int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
  * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only. */

@@ -79,6 +79,8 @@ def load_library():
                                       _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         lib.kda_bwd_workspace_bytes.restype = _i64
         lib.kda_bwd_workspace_bytes.argtypes = [_i32, _i64, _i32]
+        lib.kda_dim_workspace_bytes.restype = _i64
+        lib.kda_dim_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32]
         lib.kda_plan.restype = ctypes.c_int
         lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
@@ -138,9 +140,9 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
         cu_seqlens=None, out=None, output_final_state: bool = False):
     """KDA chunkwise forward pass on the current HIP stream.
 
-    q, k, v: bf16 [B, T, H, 128]; g: fp32 [B, T, H, 128] (log-decay, alpha = exp(g));
-    beta: fp32 [B, T, H]; scale defaults to 1/sqrt(128); initial_state /
-    final_state: [N, H, 128, 128] bf16 or fp32 (same dtype when both given;
+    q, k, v: bf16 [B, T, H, d]; g: fp32 [B, T, H, d] (log-decay, alpha = exp(g));
+    d = 128, 64 or 256; beta: fp32 [B, T, H]; scale defaults to 1/sqrt(d);
+    initial_state / final_state: [N, H, d, d] bf16 or fp32 (same dtype when both given;
     final_state may be the same tensor as initial_state); cu_seqlens: int32
     [N+1] on the device (requires B = 1).  With output_final_state=True and no
     final_state tensor, one is allocated (dtype of initial_state, else fp32).
@@ -163,7 +165,7 @@ def _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
     import torch
     lib = load_library()
     if q.dim() != 4:
-        raise ValueError("q must be [B, T, H, 128]")
+        raise ValueError("q must be [B, T, H, K]")
     B, T, H, K = q.shape
     V = v.shape[-1]
     dev = q.device
@@ -303,6 +305,11 @@ def bwd_check(*, B, T, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, d_out=0, initial
                              dq, dk, dv, dg, dbeta, d_initial_state)
 
 
+def dim_workspace_bytes(n_sequences: int, rows: int, heads: int, head_dim: int) -> int:
+    """Workspace bytes of fwd() at head dimension 64 or 256 (-1 for other sizes)."""
+    return int(load_library().kda_dim_workspace_bytes(n_sequences, rows, heads, head_dim))
+
+
 def bwd_workspace_bytes(n_sequences: int, rows: int, heads: int) -> int:
     return int(load_library().kda_bwd_workspace_bytes(n_sequences, rows, heads))
 
@@ -319,7 +326,7 @@ def bwd(q, k, v, g, beta, d_out, scale: float | None = None, initial_state=None,
     import torch
     lib = load_library()
     if q.dim() != 4:
-        raise ValueError("q must be [B, T, H, 128]")
+        raise ValueError("q must be [B, T, H, K]")
     B, T, H, K = q.shape
     V = v.shape[-1]
     dev = q.device

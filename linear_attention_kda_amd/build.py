@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("kda_api.cpp", "kda_fwd_kernel.hip", "kda_gdn_kernel.hip", "kda_decode_kernel.hip",
-            "kda_bwd.hip")]
+           ("kda_api.cpp", "kda_fwd_kernel.hip", "kda_gdn_kernel.hip", "kda_fwd_dim.hip",
+            "kda_decode_kernel.hip", "kda_bwd.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code; the host pass

@@ -46,8 +46,8 @@ kda_status validate(const void* q, const void* k, const void* v, const float* g,
                     const void* s0, int s0_dtype, const void* s1, int s1_dtype, const int32_t* cu,
                     int32_t num_seqs, int32_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                     const void* out, int32_t* n_out, bool g_scalar) {
-  if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
-    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: only K = V = 128 is supported", K, V);
+  if (K != V || (K != 64 && K != KDA_HEAD_DIM && K != 256))
+    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: K = V in {64, 128, 256} is required", K, V);
   if (B <= 0 || H <= 0 || T < 0)
     return fail(KDA_ERR_SHAPE, "invalid sizes B=%d T=%lld H=%d", B, (long long)T, H);
   if (cu != nullptr) {
@@ -63,7 +63,7 @@ kda_status validate(const void* q, const void* k, const void* v, const float* g,
     return fail(KDA_ERR_STATE_DTYPE, "initial_state dtype %d differs from final_state dtype %d",
                 s0_dtype, s1_dtype);
   // sizes: element counts must fit int64, workgroup counts int32
-  const long double elems = (long double)B * (long double)T * (long double)H * KDA_HEAD_DIM;
+  const long double elems = (long double)B * (long double)T * (long double)H * K;
   if (elems > (long double)(INT64_MAX / 4))
     return fail(KDA_ERR_SHAPE, "tensor size overflows 64-bit indexing");
   if ((int64_t)N * H * 2 > (int64_t)INT_MAX - 64)
@@ -197,6 +197,58 @@ hipError_t workspace_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// Head dimensions 64 and 256: per-chunk records in a workspace from the pool,
+// then the serial state pass (no sequence splitting).
+kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, float scale, const void* initial_state,
+                        int initial_dtype, void* final_state, int final_dtype,
+                        const int32_t* cu_seqlens, int32_t N, int32_t B, int64_t T, int32_t H,
+                        int32_t D, void* out, void* stream, bool g_scalar) {
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = cu_seqlens ? T : (int64_t)B * T;
+  kda::DimParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.g = g;
+  p.g_scalar = g_scalar ? 1 : 0;
+  p.beta = beta;
+  p.out = static_cast<uint16_t*>(out);
+  p.s0 = initial_state;
+  p.s1 = final_state;
+  p.s0_fp32 = initial_dtype == KDA_FP32;
+  p.s1_fp32 = final_dtype == KDA_FP32;
+  p.cu = cu_seqlens;
+  p.T = T;
+  p.scale = scale;
+  p.nseq = N;
+  p.H = H;
+  p.D = D;
+  p.slots = rows > 0 ? kda::dim_slots(N, rows) : 0;
+  const size_t bytes = (size_t)p.slots * H * kda::dim_record_bytes(D);
+  void* ws = nullptr;
+  if (bytes > 0) {
+    hipMemPool_t pool = nullptr;
+    hipError_t e = workspace_pool(&pool);
+    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, hs);
+    if (e != hipSuccess)
+      return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+    p.ws = static_cast<char*>(ws);
+  }
+  if (log_enabled())
+    std::fprintf(stderr, "[kda] launch: %s D=%d N=%d H=%d T=%lld record_slots=%lld workspace=%zu\n",
+                 g_scalar ? "gdn" : "kda", D, N, H, (long long)T, (long long)p.slots, bytes);
+  const hipError_t err = kda::launch_fwd_dim(p, hs);
+  if (ws != nullptr) {
+    const hipError_t e = hipFreeAsync(ws, hs);
+    if (err == hipSuccess && e != hipSuccess)
+      return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
+  }
+  if (err != hipSuccess)
+    return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return KDA_OK;
+}
+
 kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     float scale, const void* initial_state, int initial_dtype, void* final_state,
                     int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
@@ -209,6 +261,9 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
                            g_scalar);
   if (st != KDA_OK) return st;
   if (T == 0 && final_state == nullptr) return KDA_OK;  // nothing observable to compute
+  if (K != KDA_HEAD_DIM)
+    return fwd_dim_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
+                        final_dtype, cu_seqlens, N, B, T, H, K, out, stream, g_scalar);
 
   int cus = 0;
   if (device_cu_count(&cus) != 0)
@@ -274,7 +329,7 @@ const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "required pointer is NULL";
-    case KDA_ERR_HEAD_DIM: return "head dimension must be 128";
+    case KDA_ERR_HEAD_DIM: return "unsupported head dimension";
     case KDA_ERR_VARLEN_BATCH: return "cu_seqlens requires B = 1";
     case KDA_ERR_STATE_DTYPE: return "initial and final state dtypes differ";
     case KDA_ERR_DTYPE: return "invalid dtype";
@@ -455,6 +510,8 @@ kda_status validate_bwd(const void* q, const void* k, const void* v, const float
                         int32_t B, int64_t T, int32_t H, int32_t K, int32_t V, const float* dq,
                         const float* dk, const float* dv, const float* dg, const float* dbeta,
                         const float* ds0, int32_t* n_out) {
+  if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
+    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: the backward pass takes K = V = 128 only", K, V);
   kda_status st = validate(q, k, v, g, beta, s0, s0_dtype, nullptr, KDA_FP32, cu, num_seqs, B, T,
                            H, K, V, T > 0 ? d_out : nullptr, n_out, false);
   if (st != KDA_OK) return st;
@@ -495,6 +552,12 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
   return validate_bwd(q, k, v, g, beta, initial_state, initial_dtype, d_out, d_final_state,
                       d_final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, dq, dk, dv, dg, dbeta,
                       d_initial_state, nullptr);
+}
+
+int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D) {
+  if (n_sequences <= 0 || rows < 0 || H <= 0 || (D != 64 && D != 256)) return -1;
+  if (rows == 0) return 0;
+  return kda::dim_slots(n_sequences, rows) * H * (int64_t)kda::dim_record_bytes(D);
 }
 
 int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H) {

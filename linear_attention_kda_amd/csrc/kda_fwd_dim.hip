@@ -1,0 +1,672 @@
+// Chunkwise Kimi Delta Attention forward at head dimension D = K = V in {64, 256}
+// for gfx950 (MI355X).
+//
+// The recurrence and its chunkwise algebra are those of the fused d = 128 kernel
+// [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update equation and the
+// chunkwise remark; ch.4 혁신 1, channel-wise gate; ch.2, readout].  Per chunk of
+// 64 tokens (local rows r, i), with G the within-chunk inclusive cumsum of g and
+// S the chunk's start state (D x D, S[c][j]: c key channel, j value channel):
+//   A[r][i] = b_r sum_c k_rc k_ic exp(G_rc - G_ic)   (i < r),   Tb = (I + A)^-1 diag(b)
+//   M[r][i] = sum_c q_rc k_ic exp(G_rc - G_ic)       (i <= r)
+//   Y = V - (K * exp(G)) S,   U = Tb Y
+//   O = scale ((Q * exp(G)) S + M U),   S' = Diag(exp(G_last)) S + (K * exp(G_last - G))^T U
+//
+// Two launches instead of one fused pipeline (the d = 128 kernel's LDS plan does
+// not scale to D = 256):
+//  1. dim_prep_kernel, one workgroup per (chunk, head), every chunk in parallel,
+//     writes the chunk's record: kg = K exp(G), qg = Q exp(G) ([64][D] bf16),
+//     kpt = (K exp(G_last - G))^T ([D][64] bf16), Tb as bf16 high and low parts
+//     ([64][64] each), M ([64][64] bf16, zero above the diagonal) and
+//     gam = exp(G_last) ([D] fp32).  A and M come from bf16 MFMA over panels of
+//     64 channels; the unit-lower inverse is fp32 forward substitution.
+//  2. dim_state_kernel, one workgroup per (sequence, head, value slice of 64
+//     columns at D = 64, 128 at D = 256),
+//     walks the chunks in order with the fp32 state slice in MFMA accumulators.
+//     U = Tb Y splits both operands into bf16 high and low parts (three
+//     products) so that the solve stays close to fp32.  The next chunk's record
+//     and value slice are loaded into registers while the current one computes
+//     and are staged through LDS.
+//
+// Exponent references in the prep: the rows of 16-row block b use X_b = G at the
+// last row of block b-1 (X_0 = 0).  Row operands K exp(G - X_rb), Q exp(G - X_rb)
+// and the column operand K exp(X_{ib+1} - G) are <= 1; the tile of block pair
+// (rb, ib) scales the column operand per channel by exp(X_rb - X_{ib+1}), which is
+// <= 1 off the diagonal and bounded by one block's decay on it: the per-channel
+// sum of -g over 16 tokens must stay below ~88 (natural log), the domain limit of
+// the d = 128 kernel as well.
+//
+// MFMA 16x16x32 bf16 operand layout (64 lanes, q = lane / 16, m = lane % 16):
+// A[m][8q+e], B[8q+e][m], D[4q+t][m].  Where a product consumes accumulators as
+// its B operand, both operands use the k order e <-> 32ks + 4q + e (e < 4),
+// 32ks + 16 + 4q + e - 4 (e >= 4), which is what two D-layout tiles hold per lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int C = 64;          // chunk length
+constexpr int NT = 256;        // threads per prep workgroup
+// State workgroups: 16 value columns per wave; 64 columns (4 waves) at D = 64,
+// 128 columns (8 waves) at D = 256, where the per-chunk operands are 4x larger.
+template <int D>
+struct Slice {
+  static constexpr int nv = D == 256 ? 128 : 64;   // value columns per workgroup
+  static constexpr int nt = 4 * nv;                // threads
+  static constexpr int occ = D == 256 ? 1 : 2;     // workgroups per CU (LDS-bound)
+};
+constexpr int PS = 64 + 8;     // LDS row stride (bf16) of 64-wide tiles: 144 B
+constexpr int AS = 64 + 4;     // LDS row stride (fp32) of A
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int kLptMax = 256;   // longest-first ordering of the state workgroups up to this many sequences
+
+// Byte offsets inside the record of one (chunk, head).
+template <int D>
+struct Rec {
+  static constexpr int kg = 0;
+  static constexpr int qg = kg + C * D * 2;
+  static constexpr int kpt = qg + C * D * 2;
+  static constexpr int thi = kpt + D * C * 2;
+  static constexpr int tlo = thi + C * C * 2;
+  static constexpr int mm = tlo + C * C * 2;
+  static constexpr int gam = mm + C * C * 2;
+  static constexpr int bytes = gam + D * 4;
+};
+static_assert(Rec<64>::bytes % 256 == 0 && Rec<256>::bytes % 256 == 0, "records stay 256-byte aligned");
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) {  // 16-byte aligned
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// Two 4-element runs (8-byte aligned) -> one operand in the permuted k order.
+__device__ __forceinline__ bf16x8 ld2x4(const __bf16* p0, const __bf16* p1) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p0);
+  const uint2 b = *reinterpret_cast<const uint2*>(p1);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+__device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
+  bf16x4 r;
+  r[0] = (__bf16)v[0];
+  r[1] = (__bf16)v[1];
+  r[2] = (__bf16)v[2];
+  r[3] = (__bf16)v[3];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 up4(bf16x4 v) {
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ int64_t seq_bos(const DimParams& p, int n) {
+  return p.cu ? (int64_t)__builtin_amdgcn_readfirstlane(p.cu[n]) : (int64_t)n * p.T;
+}
+__device__ __forceinline__ int64_t seq_len(const DimParams& p, int n) {
+  return p.cu ? (int64_t)__builtin_amdgcn_readfirstlane(p.cu[n + 1]) -
+                    __builtin_amdgcn_readfirstlane(p.cu[n])
+              : p.T;
+}
+
+// Sequence owning record slot s: the largest n with n + floor(bos_n / 64) <= s.
+__device__ __forceinline__ int slot_seq(const DimParams& p, int64_t s) {
+  int lo = 0, hi = p.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mid + seq_bos(p, mid) / C <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ============================================================================ prep
+// Block pairs (rb, ib), ib <= rb, numbered 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0)
+// 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3).
+template <int PR>
+struct Pair {
+  static constexpr int rb = PR < 1 ? 0 : PR < 3 ? 1 : PR < 6 ? 2 : 3;
+  static constexpr int ib = PR - rb * (rb + 1) / 2;
+};
+
+struct PrepSmem {
+  union {
+    struct {
+      __bf16 kr[C * PS];   // K exp(G - X_rb)   A row operand
+      __bf16 qr[C * PS];   // Q exp(G - X_rb)   M row operand
+    };
+    float as[C * AS];      // A (beta-scaled, strictly lower), after the last panel
+  };
+  __bf16 kh[C * PS];       // K exp(X_{ib+1} - G)   column operand
+  __bf16 kt[C * PS];       // (K exp(G_last - G))^T of the panel: [channel][row]
+  float bt[4][64];         // per row block and channel: sum of g log2(e)
+  float pf[10][64];        // exp2(X_rb - X_{ib+1}) per pair and channel
+  float bs[C];             // beta of the chunk
+};
+
+// One 64-channel panel's contribution to the A and M tiles of pair PR.
+template <int PR>
+__device__ __forceinline__ void pair_panel(const PrepSmem& sm, int q4, int m16, f32x4& a, f32x4& m) {
+  constexpr int rb = Pair<PR>::rb, ib = Pair<PR>::ib;
+  constexpr bool scaled = ib != rb - 1;   // the factor is 1 for ib = rb - 1
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c0 = 32 * ks + 8 * q4;
+    bf16x8 cf = ld8(&sm.kh[(16 * ib + m16) * PS + c0]);
+    if constexpr (scaled) {
+      const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[PR][c0]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[PR][c0 + 4]);
+      const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cf[e] = (__bf16)((float)cf[e] * fs[e]);
+    }
+    const bf16x8 kf = ld8(&sm.kr[(16 * rb + m16) * PS + c0]);
+    const bf16x8 qf = ld8(&sm.qr[(16 * rb + m16) * PS + c0]);
+    a = mfma32(cf, kf, a);   // D[i][r]: lane (q4, m16) holds i = 16 ib + 4 q4 + t, r = 16 rb + m16
+    m = mfma32(cf, qf, m);
+  }
+}
+
+// A (beta-scaled, strictly lower) into LDS and M (lower incl. the diagonal) into the record.
+template <int PR>
+__device__ __forceinline__ void pair_store(PrepSmem& sm, char* rec_mm, int q4, int m16, f32x4 a, f32x4 m) {
+  constexpr int rb = Pair<PR>::rb, ib = Pair<PR>::ib;
+  const int r = 16 * rb + m16;
+  const float br = sm.bs[r];
+  float va[4];
+  uint16_t vm[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = 16 * ib + 4 * q4 + t;
+    va[t] = i < r ? br * a[t] : 0.f;
+    vm[t] = f2bf(i <= r ? m[t] : 0.f);
+  }
+  *reinterpret_cast<float4*>(&sm.as[r * AS + 16 * ib + 4 * q4]) = make_float4(va[0], va[1], va[2], va[3]);
+  *reinterpret_cast<uint2*>(rec_mm + (r * C + 16 * ib + 4 * q4) * 2) =
+      make_uint2(vm[0] | ((uint32_t)vm[1] << 16), vm[2] | ((uint32_t)vm[3] << 16));
+}
+
+template <int D, bool GS>
+__global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
+  __shared__ PrepSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, m16 = lane & 15;
+  const int h = blockIdx.x % p.H;
+  const int64_t slot = blockIdx.x / p.H;
+  const int n = slot_seq(p, slot);
+  const int64_t bos = seq_bos(p, n), len = seq_len(p, n);
+  const int64_t c = slot - n - bos / C;
+  if (c * C >= len) return;   // past the sequence's last chunk (the same for the whole workgroup)
+  const int64_t row0 = bos + c * C;
+  const int rows = (int)(len - c * C < C ? len - c * C : C);
+  char* rec = p.ws + ((size_t)slot * p.H + h) * Rec<D>::bytes;
+  const size_t hs = (size_t)p.H * D;   // token stride of q, k, g (elements)
+
+  if (tid < C) sm.bs[tid] = tid < rows ? p.beta[(row0 + tid) * p.H + h] : 0.f;
+
+  f32x4 aA[3], aM[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) aA[j] = aM[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int pc = 0; pc < D / 64; ++pc) {
+    const int ch = 64 * pc + lane;
+    // this thread: channel ch, rows 16 wave .. +15
+    float gl[16], kv[16], qv[16];
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * wave + i;
+      const bool ok = r < rows;
+      const int64_t tok = row0 + r;
+      float gi = 0.f, ki = 0.f, qi = 0.f;
+      if (ok) {
+        gi = (GS ? p.g[tok * p.H + h] : p.g[tok * hs + (size_t)h * D + ch]) * LOG2E;
+        ki = bf2f(p.k[tok * hs + (size_t)h * D + ch]);
+        qi = bf2f(p.q[tok * hs + (size_t)h * D + ch]);
+      }
+      run += gi;
+      gl[i] = run;
+      kv[i] = ki;
+      qv[i] = qi;
+    }
+    sm.bt[wave][lane] = run;
+    __syncthreads();
+    float X[5];
+    X[0] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) X[b + 1] = X[b] + sm.bt[b][lane];
+    const float xr = wave == 0 ? X[0] : wave == 1 ? X[1] : wave == 2 ? X[2] : X[3];
+    const float xn = wave == 0 ? X[1] : wave == 1 ? X[2] : wave == 2 ? X[3] : X[4];
+    const float xl = X[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * wave + i;
+      const float G = xr + gl[i];
+      const float eg = ex2(G);
+      *reinterpret_cast<uint16_t*>(rec + Rec<D>::kg + (r * D + ch) * 2) = f2bf(kv[i] * eg);
+      *reinterpret_cast<uint16_t*>(rec + Rec<D>::qg + (r * D + ch) * 2) = f2bf(qv[i] * eg);
+      sm.kt[lane * PS + r] = (__bf16)(kv[i] * ex2(xl - G));
+      const float er = ex2(G - xr);
+      sm.kr[r * PS + lane] = (__bf16)(kv[i] * er);
+      sm.qr[r * PS + lane] = (__bf16)(qv[i] * er);
+      sm.kh[r * PS + lane] = (__bf16)(kv[i] * ex2(xn - G));
+    }
+    if (wave == 0) {
+      sm.pf[0][lane] = ex2(X[0] - X[1]);
+      sm.pf[1][lane] = ex2(X[1] - X[1]);
+      sm.pf[2][lane] = ex2(X[1] - X[2]);
+      sm.pf[3][lane] = ex2(X[2] - X[1]);
+      sm.pf[4][lane] = ex2(X[2] - X[2]);
+      sm.pf[5][lane] = ex2(X[2] - X[3]);
+      sm.pf[6][lane] = ex2(X[3] - X[1]);
+      sm.pf[7][lane] = ex2(X[3] - X[2]);
+      sm.pf[8][lane] = ex2(X[3] - X[3]);
+      sm.pf[9][lane] = ex2(X[3] - X[4]);
+      *reinterpret_cast<float*>(rec + Rec<D>::gam + ch * 4) = ex2(xl);
+    }
+    __syncthreads();
+    // kp^T rows of this panel: 64 channels x 128 bytes
+    for (int x = tid; x < 64 * 8; x += NT) {
+      const int cr = x >> 3, part = x & 7;
+      *reinterpret_cast<uint4*>(rec + Rec<D>::kpt + ((64 * pc + cr) * C + 8 * part) * 2) =
+          *reinterpret_cast<const uint4*>(&sm.kt[cr * PS + 8 * part]);
+    }
+    switch (wave) {
+      case 0:
+        pair_panel<0>(sm, q4, m16, aA[0], aM[0]);
+        pair_panel<1>(sm, q4, m16, aA[1], aM[1]);
+        pair_panel<8>(sm, q4, m16, aA[2], aM[2]);
+        break;
+      case 1:
+        pair_panel<2>(sm, q4, m16, aA[0], aM[0]);
+        pair_panel<3>(sm, q4, m16, aA[1], aM[1]);
+        pair_panel<4>(sm, q4, m16, aA[2], aM[2]);
+        break;
+      case 2:
+        pair_panel<5>(sm, q4, m16, aA[0], aM[0]);
+        pair_panel<6>(sm, q4, m16, aA[1], aM[1]);
+        break;
+      default:
+        pair_panel<7>(sm, q4, m16, aA[0], aM[0]);
+        pair_panel<9>(sm, q4, m16, aA[1], aM[1]);
+        break;
+    }
+    __syncthreads();   // the panel tiles are rewritten next (and A overlays kr, qr)
+  }
+
+  char* rmm = rec + Rec<D>::mm;
+  switch (wave) {
+    case 0:
+      pair_store<0>(sm, rmm, q4, m16, aA[0], aM[0]);
+      pair_store<1>(sm, rmm, q4, m16, aA[1], aM[1]);
+      pair_store<8>(sm, rmm, q4, m16, aA[2], aM[2]);
+      break;
+    case 1:
+      pair_store<2>(sm, rmm, q4, m16, aA[0], aM[0]);
+      pair_store<3>(sm, rmm, q4, m16, aA[1], aM[1]);
+      pair_store<4>(sm, rmm, q4, m16, aA[2], aM[2]);
+      break;
+    case 2:
+      pair_store<5>(sm, rmm, q4, m16, aA[0], aM[0]);
+      pair_store<6>(sm, rmm, q4, m16, aA[1], aM[1]);
+      break;
+    default:
+      pair_store<7>(sm, rmm, q4, m16, aA[0], aM[0]);
+      pair_store<9>(sm, rmm, q4, m16, aA[1], aM[1]);
+      break;
+  }
+  // M is zero above the diagonal blocks: (rb, ib) = (0,1..3), (1,2..3), (2,3)
+  for (int x = tid; x < 6 * 64; x += NT) {
+    const int blk = x >> 6, e = x & 63;   // 16 rows x 4 runs of 4 per block
+    const int rb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+    const int ib = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+    const int r = 16 * rb + (e >> 2), i = 16 * ib + 4 * (e & 3);
+    *reinterpret_cast<uint2*>(rmm + (r * C + i) * 2) = make_uint2(0u, 0u);
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // column j of T = (I + A)^-1 by forward substitution: T[r][j] = -sum_{i<r} A[r][i] T[i][j]
+    // for r > j (the terms with i < j vanish), T[j][j] = 1, zero above
+    const int j = lane;
+    float col[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) s = fmaf(sm.as[r * AS + i], col[i], s);
+      col[r] = r == j ? 1.f : -s;
+    }
+    const float bj = sm.bs[j];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const float x = col[r] * bj;
+      const __bf16 hi = (__bf16)x;
+      const __bf16 lo = (__bf16)(x - (float)hi);
+      *reinterpret_cast<__bf16*>(rec + Rec<D>::thi + (r * C + j) * 2) = hi;
+      *reinterpret_cast<__bf16*>(rec + Rec<D>::tlo + (r * C + j) * 2) = lo;
+    }
+  }
+}
+
+// ============================================================================ state pass
+template <int D>
+struct StateSmem {
+  __bf16 kg[C * (D + 8)];
+  __bf16 qg[C * (D + 8)];
+  __bf16 kpt[D * PS];
+  __bf16 thi[C * PS];
+  __bf16 tlo[C * PS];
+  __bf16 mm[C * PS];
+  __bf16 vs[C * (Slice<D>::nv + 8)];   // V of the chunk, this workgroup's columns
+  float gam[D];
+  int lens[kLptMax];
+  int order;
+};
+
+template <int D>
+struct Pieces {   // 16-byte pieces of one chunk's operands, in record order, then V
+  static constexpr int kg = C * D / 8;
+  static constexpr int kpt = D * C / 8;
+  static constexpr int tile = C * C / 8;
+  static constexpr int gam = D / 4;
+  static constexpr int rec = Rec<D>::bytes / 16;
+  static constexpr int v = C * Slice<D>::nv / 8;
+  static constexpr int total = rec + v;
+  static constexpr int per_thread = (total + Slice<D>::nt - 1) / Slice<D>::nt;
+  static_assert(rec == 2 * kg + kpt + 3 * tile + gam, "record layout");
+};
+
+template <int D>
+__device__ __forceinline__ void chunk_load(uint4* buf, const char* rec, const uint16_t* vrow0,
+                                           size_t vstride, int rows, int tid) {
+  using P = Pieces<D>;
+  constexpr int VP = Slice<D>::nv / 8;   // 16-byte pieces per row of the V slice
+#pragma unroll
+  for (int i = 0; i < P::per_thread; ++i) {
+    const int x = tid + Slice<D>::nt * i;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (x < P::rec) {
+      u = *reinterpret_cast<const uint4*>(rec + (size_t)x * 16);
+    } else if (x < P::total) {
+      const int y = x - P::rec, row = y / VP, part = y % VP;
+      if (row < rows) u = *reinterpret_cast<const uint4*>(vrow0 + row * vstride + 8 * part);
+    }
+    buf[i] = u;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void chunk_stage(StateSmem<D>& sm, const uint4* buf, int tid) {
+  using P = Pieces<D>;
+  constexpr int KS = D + 8;
+  constexpr int VS = Slice<D>::nv + 8;
+  constexpr int VP = Slice<D>::nv / 8;
+#pragma unroll
+  for (int i = 0; i < P::per_thread; ++i) {
+    const int x = tid + Slice<D>::nt * i;
+    __bf16* dst;
+    if (x < P::kg) {
+      dst = &sm.kg[(x / (D / 8)) * KS + 8 * (x % (D / 8))];
+    } else if (x < 2 * P::kg) {
+      const int y = x - P::kg;
+      dst = &sm.qg[(y / (D / 8)) * KS + 8 * (y % (D / 8))];
+    } else if (x < 2 * P::kg + P::kpt) {
+      const int y = x - 2 * P::kg;
+      dst = &sm.kpt[(y >> 3) * PS + 8 * (y & 7)];
+    } else if (x < 2 * P::kg + P::kpt + P::tile) {
+      const int y = x - 2 * P::kg - P::kpt;
+      dst = &sm.thi[(y >> 3) * PS + 8 * (y & 7)];
+    } else if (x < 2 * P::kg + P::kpt + 2 * P::tile) {
+      const int y = x - 2 * P::kg - P::kpt - P::tile;
+      dst = &sm.tlo[(y >> 3) * PS + 8 * (y & 7)];
+    } else if (x < 2 * P::kg + P::kpt + 3 * P::tile) {
+      const int y = x - 2 * P::kg - P::kpt - 2 * P::tile;
+      dst = &sm.mm[(y >> 3) * PS + 8 * (y & 7)];
+    } else if (x < P::rec) {
+      const int y = x - (P::rec - P::gam);
+      *reinterpret_cast<uint4*>(&sm.gam[4 * y]) = buf[i];
+      continue;
+    } else if (x < P::total) {
+      const int y = x - P::rec;
+      dst = &sm.vs[(y / VP) * VS + 8 * (y % VP)];
+    } else {
+      continue;
+    }
+    *reinterpret_cast<uint4*>(dst) = buf[i];
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(DimParams p) {
+  constexpr int KS = D + 8;
+  constexpr int NV = Slice<D>::nv;
+  constexpr int VS = NV + 8;
+  constexpr int NTS = Slice<D>::nt;
+  constexpr int NCB = D / 16;   // 16-row tiles of the state slice per wave
+  constexpr int NKS = D / 32;   // k-steps over the channels
+  constexpr int NSL = D / NV;   // value slices per (sequence, head)
+  __shared__ StateSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4_ = lane >> 4, m16_ = lane & 15;
+
+  // workgroup -> (rank, head, value slice); the slices of one (sequence, head) share an XCD
+  const int grp = blockIdx.x / (8 * NSL), rem = blockIdx.x % (8 * NSL);
+  const int split = rem / 8;
+  const int pidx = grp * 8 + rem % 8;
+  const int rank = pidx / p.H, h = pidx % p.H;
+  if (rank >= p.nseq) return;
+  int n = rank;
+  if (p.cu != nullptr && p.nseq > 1 && p.nseq <= kLptMax) {   // longest sequences first
+    for (int s = tid; s < p.nseq; s += NTS) sm.lens[s] = p.cu[s + 1] - p.cu[s];
+    __syncthreads();
+    for (int s = tid; s < p.nseq; s += NTS) {
+      const int ls = sm.lens[s];
+      int rk = 0;
+      for (int j = 0; j < p.nseq; ++j) {
+        const int lj = sm.lens[j];
+        rk += (lj > ls) || (lj == ls && j < s);
+      }
+      if (rk == rank) sm.order = s;
+    }
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(sm.order);
+  }
+  const int64_t bos = seq_bos(p, n), len = seq_len(p, n);
+  const int nch = (int)((len + C - 1) / C);
+  const int jw = split * NV + 16 * wave;   // this wave's first value column
+  const size_t hs = (size_t)p.H * D;
+  const size_t sbase = ((size_t)n * p.H + h) * D * D;
+
+  // the state slice: st[cb][t] = S[16 cb + 4 q4 + t][jw + m16]
+  f32x4 st[NCB];
+  const size_t soff = sbase + (size_t)(4 * q4_) * D + jw + m16_;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) st[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.s0 != nullptr) {
+    if (p.s0_fp32) {
+      const float* s = static_cast<const float*>(p.s0) + soff;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[cb][t] = s[(16 * cb + t) * D];
+    } else {
+      const uint16_t* s = static_cast<const uint16_t*>(p.s0) + soff;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) st[cb][t] = bf2f(s[(16 * cb + t) * D]);
+    }
+  }
+
+  const int64_t slot0 = n + bos / C;
+  auto rec_of = [&](int c) { return p.ws + ((size_t)(slot0 + c) * p.H + h) * Rec<D>::bytes; };
+  auto vrow_of = [&](int c) { return p.v + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + split * NV; };
+  auto rows_of = [&](int c) { return (int)(len - (int64_t)c * C < C ? len - (int64_t)c * C : C); };
+
+  uint4 buf[Pieces<D>::per_thread];
+  if (nch > 0) chunk_load<D>(buf, rec_of(0), vrow_of(0), hs, rows_of(0), tid);
+
+  for (int c = 0; c < nch; ++c) {
+    // lane indices through an empty asm: addresses are formed where they are used
+    // instead of being kept live across the loop
+    int ti = tid, q4 = q4_, m16 = m16_;
+    asm volatile("" : "+v"(ti), "+v"(q4), "+v"(m16));
+    __syncthreads();   // the previous chunk's operands are no longer read
+    chunk_stage<D>(sm, buf, ti);
+    __syncthreads();
+    if (c + 1 < nch) chunk_load<D>(buf, rec_of(c + 1), vrow_of(c + 1), hs, rows_of(c + 1), ti);
+
+    // P1 = kg S, P2 = qg S (rows 16 rb + 4 q4 + t, column jw + m16)
+    f32x4 p1[4], p2[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) p1[rb] = p2[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 sf = cat(cvt4(st[2 * ks]), cvt4(st[2 * ks + 1]));
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const __bf16* kp = &sm.kg[(16 * rb + m16) * KS + 32 * ks + 4 * q4];
+        const __bf16* qp = &sm.qg[(16 * rb + m16) * KS + 32 * ks + 4 * q4];
+        p1[rb] = mfma32(ld2x4(kp, kp + 16), sf, p1[rb]);
+        p2[rb] = mfma32(ld2x4(qp, qp + 16), sf, p2[rb]);
+      }
+      // keep the operand loads of later k-steps from being hoisted (register pressure)
+      if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // Y = V - P1 as bf16 high and low parts, in the permuted k order over rows
+    bf16x8 zh[2], zl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x4 hi[2], lo[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int rb = 2 * ks + s;
+        f32x4 y;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          y[t] = (float)sm.vs[(16 * rb + 4 * q4 + t) * VS + 16 * wave + m16] - p1[rb][t];
+        hi[s] = cvt4(y);
+        lo[s] = cvt4(y - up4(hi[s]));
+      }
+      zh[ks] = cat(hi[0], hi[1]);
+      zl[ks] = cat(lo[0], lo[1]);
+    }
+    // U = Tb Y (Tb is lower triangular: block row ib needs k-steps 0 .. ib / 2)
+    f32x4 u[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      u[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks <= ib / 2; ++ks) {
+        const __bf16* th = &sm.thi[(16 * ib + m16) * PS + 32 * ks + 4 * q4];
+        const __bf16* tl = &sm.tlo[(16 * ib + m16) * PS + 32 * ks + 4 * q4];
+        const bf16x8 a = ld2x4(th, th + 16);
+        u[ib] = mfma32(a, zh[ks], u[ib]);
+        u[ib] = mfma32(a, zl[ks], u[ib]);
+        u[ib] = mfma32(ld2x4(tl, tl + 16), zh[ks], u[ib]);
+      }
+    }
+    bf16x8 uf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) uf[ks] = cat(cvt4(u[2 * ks]), cvt4(u[2 * ks + 1]));
+
+    // O = scale (P2 + M U)
+    const int rows = rows_of(c);
+    uint16_t* orow = p.out + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + jw + m16;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 o = p2[rb];
+#pragma unroll
+      for (int ks = 0; ks <= rb / 2; ++ks) {
+        const __bf16* mp = &sm.mm[(16 * rb + m16) * PS + 32 * ks + 4 * q4];
+        o = mfma32(ld2x4(mp, mp + 16), uf[ks], o);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * rb + 4 * q4 + t;
+        if (r < rows) orow[(size_t)r * hs] = f2bf(p.scale * o[t]);
+      }
+    }
+
+    // S' = Diag(gam) S + kpt U
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[16 * cb + 4 * q4]);
+      st[cb][0] *= gm.x;
+      st[cb][1] *= gm.y;
+      st[cb][2] *= gm.z;
+      st[cb][3] *= gm.w;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const __bf16* kp = &sm.kpt[(16 * cb + m16) * PS + 32 * ks + 4 * q4];
+        st[cb] = mfma32(ld2x4(kp, kp + 16), uf[ks], st[cb]);
+      }
+      if (cb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (p.s1 != nullptr) {
+    if (p.s1_fp32) {
+      float* s = static_cast<float*>(p.s1) + soff;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[(16 * cb + t) * D] = st[cb][t];
+    } else {
+      uint16_t* s = static_cast<uint16_t*>(p.s1) + soff;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[(16 * cb + t) * D] = f2bf(st[cb][t]);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_dim(const DimParams& p, hipStream_t stream) {
+  if (p.slots > 0) {
+    const dim3 grid((unsigned)(p.slots * p.H));
+    if (p.g_scalar) hipLaunchKernelGGL((dim_prep_kernel<D, true>), grid, dim3(NT), 0, stream, p);
+    else hipLaunchKernelGGL((dim_prep_kernel<D, false>), grid, dim3(NT), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t wgs = ((int64_t)p.nseq * p.H + 7) / 8 * 8 * (D / Slice<D>::nv);
+  hipLaunchKernelGGL(dim_state_kernel<D>, dim3((unsigned)wgs), dim3(Slice<D>::nt), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dim_record_bytes(int D) {
+  return D == 64 ? (size_t)Rec<64>::bytes : D == 256 ? (size_t)Rec<256>::bytes : 0;
+}
+
+int64_t dim_slots(int64_t nseq, int64_t rows) { return nseq + (rows + C - 1) / C + 1; }
+
+hipError_t launch_fwd_dim(const DimParams& p, hipStream_t stream) {
+  if (p.D == 64) return launch_dim<64>(p, stream);
+  if (p.D == 256) return launch_dim<256>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -137,6 +137,36 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
 // The initial-state gradients alone, for calls without tokens.
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 
+// Forward pass at head dimension D = K = V in {64, 256}: a chunk-parallel
+// prep kernel writes one record of per-chunk operands for every (chunk, head)
+// into the workspace, then a serial kernel walks each (sequence, head, 64
+// value columns) through its chunks.  Chunk c of sequence n uses record slot
+// n + floor(bos_n / 64) + c; dim_slots() bounds the slot count.
+struct DimParams {
+  const uint16_t* q;      // bf16 [rows][H][D]
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* g;         // fp32 [rows][H][D], or [rows][H] when g_scalar
+  const float* beta;      // fp32 [rows][H]
+  uint16_t* out;          // bf16 [rows][H][D]
+  const void* s0;         // [N][H][D][D] or null
+  void* s1;               // [N][H][D][D] or null
+  const int32_t* cu;      // [N+1] or null
+  int64_t T;              // tokens per batch row (fixed-length mode)
+  int64_t slots;          // record slots in the workspace
+  float scale;
+  int s0_fp32;
+  int s1_fp32;
+  int nseq;
+  int H;
+  int D;
+  int g_scalar;
+  char* ws;               // [slots][H] records of dim_record_bytes(D) bytes
+};
+size_t dim_record_bytes(int D);
+int64_t dim_slots(int64_t nseq, int64_t rows);
+hipError_t launch_fwd_dim(const DimParams& p, hipStream_t stream);
+
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
 // the segment scan and output fix-up kernels follow the main kernel.

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == ["kda_bwd", "kda_bwd_check", "kda_bwd_workspace_bytes",
-                                  "kda_decode", "kda_decode_check", "kda_fwd", "kda_fwd_check",
+                                  "kda_decode", "kda_decode_check", "kda_dim_workspace_bytes",
+                                  "kda_fwd", "kda_fwd_check",
                                   "kda_gdn_decode", "kda_gdn_decode_check", "kda_gdn_fwd",
                                   "kda_gdn_fwd_check", "kda_last_error", "kda_plan",
                                   "kda_status_string"]
@@ -55,6 +56,9 @@ def ok_args(**over):
 
 def test_check_accepts_valid_arguments(lib):
     assert binding.fwd_check(**ok_args()) == OK
+    assert binding.fwd_check(**ok_args(K=64, V=64)) == OK
+    assert binding.fwd_check(**ok_args(K=256, V=256)) == OK
+    assert binding.gdn_fwd_check(**ok_args(K=256, V=256, g=P + 4)) == OK
     assert binding.fwd_check(**ok_args(initial_state=P, initial_dtype=0, final_state=P,
                                        final_dtype=0)) == OK
     assert binding.fwd_check(**ok_args(cu_seqlens=P, num_seqs=3)) == OK
@@ -64,6 +68,8 @@ def test_check_accepts_valid_arguments(lib):
 @pytest.mark.parametrize("over,status", [
     (dict(K=64), ERR_HEAD_DIM),
     (dict(V=256), ERR_HEAD_DIM),
+    (dict(K=96, V=96), ERR_HEAD_DIM),
+    (dict(K=512, V=512), ERR_HEAD_DIM),
     (dict(B=2, cu_seqlens=P, num_seqs=2), ERR_VARLEN_BATCH),
     (dict(cu_seqlens=P, num_seqs=0), ERR_SHAPE),
     (dict(initial_state=P, initial_dtype=0, final_state=P + 64, final_dtype=1), ERR_STATE_DTYPE),
@@ -102,6 +108,7 @@ def test_decode_check_accepts_valid_arguments(lib):
 @pytest.mark.parametrize("over,status", [
     (dict(K=64), ERR_HEAD_DIM),
     (dict(V=256), ERR_HEAD_DIM),
+    (dict(K=64, V=64), ERR_HEAD_DIM),
     (dict(N=-1), ERR_SHAPE),
     (dict(H=0), ERR_SHAPE),
     (dict(state_dtype=2), ERR_DTYPE),
@@ -150,6 +157,7 @@ def test_bwd_check(lib):
     assert binding.bwd_check(**bwd_args(T=0, q=0, k=0, v=0, g=0, beta=0, d_out=0, dq=0, dk=0,
                                         dv=0, dg=0, dbeta=0)) == OK
     assert binding.bwd_check(**bwd_args(K=64)) == ERR_HEAD_DIM
+    assert binding.bwd_check(**bwd_args(K=64, V=64)) == ERR_HEAD_DIM
     assert binding.bwd_check(**bwd_args(d_out=0)) == ERR_NULL
     assert binding.bwd_check(**bwd_args(dg=0)) == ERR_NULL
     assert binding.bwd_check(**bwd_args(dq=P + 8)) == ERR_ALIGN
@@ -165,6 +173,18 @@ def test_bwd_workspace_bytes(lib):
     nb = (1 + 8192 // 64 + 1) * 32
     assert binding.bwd_workspace_bytes(1, 8192, 32) == up(nb * per) + up(8192 * 32 * 128 * 2)
     assert binding.bwd_workspace_bytes(0, 8192, 32) == -1
+
+
+def test_dim_workspace_bytes(lib):
+    # one record per (chunk slot, head); slots: N + ceil(rows / 64) + 1.  A record
+    # holds kg, qg, kp^T (64 x d bf16 each), three 64 x 64 bf16 tiles and d fp32.
+    for d in (64, 256):
+        rec = 3 * 64 * d * 2 + 3 * 64 * 64 * 2 + d * 4
+        assert binding.dim_workspace_bytes(16, 65536, 32, d) == (16 + 1024 + 1) * 32 * rec
+        assert binding.dim_workspace_bytes(1, 65, 2, d) == (1 + 2 + 1) * 2 * rec
+        assert binding.dim_workspace_bytes(3, 0, 2, d) == 0
+    assert binding.dim_workspace_bytes(1, 64, 1, 128) == -1
+    assert binding.dim_workspace_bytes(0, 64, 1, 64) == -1
 
 
 def test_state_dtype_ignored_for_absent_state(lib):

@@ -198,7 +198,7 @@ def test_deterministic():
 
 
 def test_rejects_bad_head_dim():
-    x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros(1, 8, 1, 96, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(binding.KdaError) as e:
         binding.fwd(x, x, x, x.float(), torch.zeros(1, 8, 1, device=DEV))
     assert e.value.status == -2
