@@ -229,6 +229,57 @@ def gdn_bench(wid: int, steps: int, warmup: int):
                          "kernel": "kda_gdn_fwd call", "algorithmic_bytes": nbytes}}
 
 
+def dim_bench(wid: int, d: int, steps: int, warmup: int):
+    """kda_fwd at head dimension d (64 or 256) on workload `wid`'s shape: the same
+    lengths, heads and state dtype, inputs drawn with the same recipe at size d."""
+    import torch
+
+    from linear_attention_kda_amd import binding, perfmodel
+    from linear_attention_kda_amd.workloads import WORKLOADS, random_inputs, varlen_lengths
+
+    w = WORKLOADS[wid]
+    lengths = None
+    if w.n_seqs:
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(w.seed)
+        lengths = varlen_lengths(w.n_seqs, w.T, gen)
+    x = random_inputs(w.B, w.T, w.H, d, d, seed=w.seed + 7919 + d, device="cuda",
+                      g_lo=w.g_lo, g_hi=w.g_hi, init_state=w.init_state, lengths=lengths)
+    N, H = w.num_states, w.H
+    sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    final = torch.empty(N, H, d, d, dtype=sdt[w.final_state], device="cuda") \
+        if w.final_state else None
+    out = torch.empty_like(x["v"])
+
+    def step():
+        binding.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
+                    initial_state=x["initial_state"], final_state=final,
+                    cu_seqlens=x["cu_seqlens"], out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = perfmodel.workload_bytes(w.tokens, H, N, state_bytes_of(w.init_state),
+                                      state_bytes_of(w.final_state), d=d)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] d={d} {w.name}: {ms:.3f} ms, {w.tokens / ms / 1e3:.2f} M tokens/s, "
+        f"{gbs:.0f} GB/s ({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
+    return {"workload": f"head dim {d}, {w.name}", "head_dim": d, "unit": "tokens/s",
+            "value": w.tokens / (ms * 1e-3), "ms_per_step": ms,
+            "workspace_bytes": binding.dim_workspace_bytes(N, w.tokens, H, d),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "kda_fwd call at d=%d: dim_prep_kernel + dim_state_kernel" % d,
+                         "algorithmic_bytes": nbytes}}
+
+
 def bwd_bench(wid: int, steps: int, warmup: int):
     """The backward pass (kda_bwd) on workload `wid` with seeded upstream gradients."""
     import torch
@@ -314,6 +365,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step line")
     ap.add_argument("--no-gdn", action="store_true", help="skip the scalar-gate line")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward line")
+    ap.add_argument("--no-dims", action="store_true", help="skip the head dim 64 / 256 lines")
     ap.add_argument("--bwd-workload", type=int, default=1)
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--counters", action="store_true",
@@ -371,6 +423,10 @@ def main():
     if not args.no_gdn:
         gdn = gdn_bench(args.workload, args.steps, args.warmup)
 
+    dims = None
+    if not args.no_dims:
+        dims = [dim_bench(args.workload, d, args.steps, args.warmup) for d in (64, 256)]
+
     bwd = None
     if not args.no_bwd:
         bwd = bwd_bench(args.bwd_workload, max(3, args.steps // 4), 1)
@@ -410,6 +466,7 @@ def main():
         "secondary": secondary,
         "decode": decode,
         "gdn": gdn,
+        "head_dims": dims,
         "bwd": bwd,
         "cpu_baseline": cpu,
     }

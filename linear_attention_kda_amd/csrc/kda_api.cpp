@@ -68,6 +68,9 @@ kda_status validate(const void* q, const void* k, const void* v, const float* g,
     return fail(KDA_ERR_SHAPE, "tensor size overflows 64-bit indexing");
   if ((int64_t)N * H * 2 > (int64_t)INT_MAX - 64)
     return fail(KDA_ERR_SHAPE, "N*H=%lld too large", (long long)N * H);
+  // a chunk's rows of every head stay within 32-bit buffer offsets
+  if ((int64_t)H * K > (int64_t)1 << 22)
+    return fail(KDA_ERR_SHAPE, "H*K=%lld too large (at most 4194304)", (long long)H * K);
   if (T > 0) {
     if (!q || !k || !v || !g || !beta || !out)
       return fail(KDA_ERR_NULL, "q, k, v, g, beta and out are required when T > 0");

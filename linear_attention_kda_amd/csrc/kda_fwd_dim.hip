@@ -52,6 +52,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int C = 64;          // chunk length
+constexpr int PS = 64 + 8;     // row stride (bf16) of 64-wide tiles: 144 B
 constexpr int NT = 256;        // threads per prep workgroup
 // State workgroups: 16 value columns per wave; 64 columns (4 waves) at D = 64,
 // 128 columns (8 waves) at D = 256, where the per-chunk operands are 4x larger.
@@ -61,21 +62,23 @@ struct Slice {
   static constexpr int nt = 4 * nv;                // threads
   static constexpr int occ = D == 256 ? 1 : 2;     // workgroups per CU (LDS-bound)
 };
-constexpr int PS = 64 + 8;     // LDS row stride (bf16) of 64-wide tiles: 144 B
 constexpr int AS = 64 + 4;     // LDS row stride (fp32) of A
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int kLptMax = 256;   // longest-first ordering of the state workgroups up to this many sequences
 
-// Byte offsets inside the record of one (chunk, head).
+// Byte offsets inside the record of one (chunk, head).  Rows are padded exactly
+// as the state kernel's LDS tiles (8 bf16 per row) so that staging a record is a
+// straight copy; the padding is never written or read.
 template <int D>
 struct Rec {
+  static constexpr int ks = D + 8;     // row stride (bf16) of kg and qg
   static constexpr int kg = 0;
-  static constexpr int qg = kg + C * D * 2;
-  static constexpr int kpt = qg + C * D * 2;
-  static constexpr int thi = kpt + D * C * 2;
-  static constexpr int tlo = thi + C * C * 2;
-  static constexpr int mm = tlo + C * C * 2;
-  static constexpr int gam = mm + C * C * 2;
+  static constexpr int qg = kg + C * ks * 2;
+  static constexpr int kpt = qg + C * ks * 2;
+  static constexpr int thi = kpt + D * PS * 2;
+  static constexpr int tlo = thi + C * PS * 2;
+  static constexpr int mm = tlo + C * PS * 2;
+  static constexpr int gam = mm + C * PS * 2;
   static constexpr int bytes = gam + D * 4;
 };
 static_assert(Rec<64>::bytes % 256 == 0 && Rec<256>::bytes % 256 == 0, "records stay 256-byte aligned");
@@ -116,6 +119,15 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// Buffer descriptor over `bytes` bytes from `base`: loads beyond the range return
+// zero and stores beyond it are dropped (raw buffer, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ int64_t seq_bos(const DimParams& p, int n) {
   return p.cu ? (int64_t)__builtin_amdgcn_readfirstlane(p.cu[n]) : (int64_t)n * p.T;
 }
@@ -153,10 +165,16 @@ struct PrepSmem {
     };
     float as[C * AS];      // A (beta-scaled, strictly lower), after the last panel
   };
-  __bf16 kh[C * PS];       // K exp(X_{ib+1} - G)   column operand
-  __bf16 kt[C * PS];       // (K exp(G_last - G))^T of the panel: [channel][row]
+  union {
+    struct {
+      __bf16 kh[C * PS];   // K exp(X_{ib+1} - G)   column operand
+      __bf16 kt[C * PS];   // (K exp(G_last - G))^T of the panel: [channel][row]
+    };
+    float ts[C * AS];      // T = (I + A)^-1 (lower blocks), after the last panel
+  };
   float bt[4][64];         // per row block and channel: sum of g log2(e)
   float pf[10][64];        // exp2(X_rb - X_{ib+1}) per pair and channel
+  float wb[3][256];        // sum_m A_{rb,m} T_{m,ib} of one level of the inverse
   float bs[C];             // beta of the chunk
 };
 
@@ -184,8 +202,9 @@ __device__ __forceinline__ void pair_panel(const PrepSmem& sm, int q4, int m16, 
 }
 
 // A (beta-scaled, strictly lower) into LDS and M (lower incl. the diagonal) into the record.
-template <int PR>
-__device__ __forceinline__ void pair_store(PrepSmem& sm, char* rec_mm, int q4, int m16, f32x4 a, f32x4 m) {
+template <int D, int PR>
+__device__ __forceinline__ void pair_store(PrepSmem& sm, __amdgpu_buffer_rsrc_t rrec, int q4, int m16,
+                                           f32x4 a, f32x4 m) {
   constexpr int rb = Pair<PR>::rb, ib = Pair<PR>::ib;
   const int r = 16 * rb + m16;
   const float br = sm.bs[r];
@@ -198,8 +217,9 @@ __device__ __forceinline__ void pair_store(PrepSmem& sm, char* rec_mm, int q4, i
     vm[t] = f2bf(i <= r ? m[t] : 0.f);
   }
   *reinterpret_cast<float4*>(&sm.as[r * AS + 16 * ib + 4 * q4]) = make_float4(va[0], va[1], va[2], va[3]);
-  *reinterpret_cast<uint2*>(rec_mm + (r * C + 16 * ib + 4 * q4) * 2) =
-      make_uint2(vm[0] | ((uint32_t)vm[1] << 16), vm[2] | ((uint32_t)vm[3] << 16));
+  const uint2 mv = make_uint2(vm[0] | ((uint32_t)vm[1] << 16), vm[2] | ((uint32_t)vm[3] << 16));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mv),
+                                        rrec, (r * PS + 16 * ib + 4 * q4) * 2, Rec<D>::mm, 0);
 }
 
 template <int D, bool GS>
@@ -216,35 +236,49 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
   if (c * C >= len) return;   // past the sequence's last chunk (the same for the whole workgroup)
   const int64_t row0 = bos + c * C;
   const int rows = (int)(len - c * C < C ? len - c * C : C);
-  char* rec = p.ws + ((size_t)slot * p.H + h) * Rec<D>::bytes;
-  const size_t hs = (size_t)p.H * D;   // token stride of q, k, g (elements)
+  const int hs = p.H * D;      // token stride of q, k, g (elements); the host bounds H * D
+  // descriptors over the chunk's rows: rows past the sequence read as zero
+  const size_t t0 = (size_t)row0 * hs + (size_t)h * D;
+  const auto rq = rsrc(p.q + t0, ((rows - 1) * hs + D) * 2);
+  const auto rk = rsrc(p.k + t0, ((rows - 1) * hs + D) * 2);
+  const auto rg = GS ? rsrc(p.g + (size_t)row0 * p.H + h, ((rows - 1) * p.H + 1) * 4)
+                     : rsrc(p.g + t0, ((rows - 1) * hs + D) * 4);
+  const auto rb_ = rsrc(p.beta + (size_t)row0 * p.H + h, ((rows - 1) * p.H + 1) * 4);
+  const auto rrec = rsrc(p.ws + ((size_t)slot * p.H + h) * Rec<D>::bytes, Rec<D>::bytes);
 
-  if (tid < C) sm.bs[tid] = tid < rows ? p.beta[(row0 + tid) * p.H + h] : 0.f;
+  if (tid < C) sm.bs[tid] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb_, tid * p.H * 4, 0, 0));
 
   f32x4 aA[3], aM[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) aA[j] = aM[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // raw loads of one panel (channels 64 pc + lane, rows 16 wave .. +15), issued a
+  // panel ahead so that they overlap the previous panel's tile products
+  float graw[16];
+  uint32_t kraw[16], qraw[16];
+  auto load_panel = [&](int pc) {
+    const int ch = 64 * pc + lane;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * wave + i;
+      graw[i] = GS ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 0, r * p.H * 4, 0))
+                   : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, ch * 4, r * hs * 4, 0));
+      kraw[i] = __builtin_amdgcn_raw_buffer_load_b16(rk, ch * 2, r * hs * 2, 0);
+      qraw[i] = __builtin_amdgcn_raw_buffer_load_b16(rq, ch * 2, r * hs * 2, 0);
+    }
+  };
+  load_panel(0);
+
   for (int pc = 0; pc < D / 64; ++pc) {
     const int ch = 64 * pc + lane;
-    // this thread: channel ch, rows 16 wave .. +15
     float gl[16], kv[16], qv[16];
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = 16 * wave + i;
-      const bool ok = r < rows;
-      const int64_t tok = row0 + r;
-      float gi = 0.f, ki = 0.f, qi = 0.f;
-      if (ok) {
-        gi = (GS ? p.g[tok * p.H + h] : p.g[tok * hs + (size_t)h * D + ch]) * LOG2E;
-        ki = bf2f(p.k[tok * hs + (size_t)h * D + ch]);
-        qi = bf2f(p.q[tok * hs + (size_t)h * D + ch]);
-      }
-      run += gi;
+      run += graw[i] * LOG2E;
       gl[i] = run;
-      kv[i] = ki;
-      qv[i] = qi;
+      kv[i] = __uint_as_float(kraw[i] << 16);
+      qv[i] = __uint_as_float(qraw[i] << 16);
     }
     sm.bt[wave][lane] = run;
     __syncthreads();
@@ -260,8 +294,8 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
       const int r = 16 * wave + i;
       const float G = xr + gl[i];
       const float eg = ex2(G);
-      *reinterpret_cast<uint16_t*>(rec + Rec<D>::kg + (r * D + ch) * 2) = f2bf(kv[i] * eg);
-      *reinterpret_cast<uint16_t*>(rec + Rec<D>::qg + (r * D + ch) * 2) = f2bf(qv[i] * eg);
+      __builtin_amdgcn_raw_buffer_store_b16(f2bf(kv[i] * eg), rrec, ch * 2, Rec<D>::kg + r * Rec<D>::ks * 2, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(f2bf(qv[i] * eg), rrec, ch * 2, Rec<D>::qg + r * Rec<D>::ks * 2, 0);
       sm.kt[lane * PS + r] = (__bf16)(kv[i] * ex2(xl - G));
       const float er = ex2(G - xr);
       sm.kr[r * PS + lane] = (__bf16)(kv[i] * er);
@@ -279,14 +313,17 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
       sm.pf[7][lane] = ex2(X[3] - X[2]);
       sm.pf[8][lane] = ex2(X[3] - X[3]);
       sm.pf[9][lane] = ex2(X[3] - X[4]);
-      *reinterpret_cast<float*>(rec + Rec<D>::gam + ch * 4) = ex2(xl);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ex2(xl)), rrec, ch * 4, Rec<D>::gam, 0);
     }
     __syncthreads();
+    if (pc + 1 < D / 64) load_panel(pc + 1);
     // kp^T rows of this panel: 64 channels x 128 bytes
+#pragma unroll
     for (int x = tid; x < 64 * 8; x += NT) {
       const int cr = x >> 3, part = x & 7;
-      *reinterpret_cast<uint4*>(rec + Rec<D>::kpt + ((64 * pc + cr) * C + 8 * part) * 2) =
-          *reinterpret_cast<const uint4*>(&sm.kt[cr * PS + 8 * part]);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(&sm.kt[cr * PS + 8 * part])), rrec,
+          (cr * PS + 8 * part) * 2, Rec<D>::kpt + 64 * pc * PS * 2, 0);
     }
     switch (wave) {
       case 0:
@@ -308,28 +345,27 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
         pair_panel<9>(sm, q4, m16, aA[1], aM[1]);
         break;
     }
-    __syncthreads();   // the panel tiles are rewritten next (and A overlays kr, qr)
+    __syncthreads();   // the panel tiles are rewritten next (and A, T overlay them)
   }
 
-  char* rmm = rec + Rec<D>::mm;
   switch (wave) {
     case 0:
-      pair_store<0>(sm, rmm, q4, m16, aA[0], aM[0]);
-      pair_store<1>(sm, rmm, q4, m16, aA[1], aM[1]);
-      pair_store<8>(sm, rmm, q4, m16, aA[2], aM[2]);
+      pair_store<D, 0>(sm, rrec, q4, m16, aA[0], aM[0]);
+      pair_store<D, 1>(sm, rrec, q4, m16, aA[1], aM[1]);
+      pair_store<D, 8>(sm, rrec, q4, m16, aA[2], aM[2]);
       break;
     case 1:
-      pair_store<2>(sm, rmm, q4, m16, aA[0], aM[0]);
-      pair_store<3>(sm, rmm, q4, m16, aA[1], aM[1]);
-      pair_store<4>(sm, rmm, q4, m16, aA[2], aM[2]);
+      pair_store<D, 2>(sm, rrec, q4, m16, aA[0], aM[0]);
+      pair_store<D, 3>(sm, rrec, q4, m16, aA[1], aM[1]);
+      pair_store<D, 4>(sm, rrec, q4, m16, aA[2], aM[2]);
       break;
     case 2:
-      pair_store<5>(sm, rmm, q4, m16, aA[0], aM[0]);
-      pair_store<6>(sm, rmm, q4, m16, aA[1], aM[1]);
+      pair_store<D, 5>(sm, rrec, q4, m16, aA[0], aM[0]);
+      pair_store<D, 6>(sm, rrec, q4, m16, aA[1], aM[1]);
       break;
     default:
-      pair_store<7>(sm, rmm, q4, m16, aA[0], aM[0]);
-      pair_store<9>(sm, rmm, q4, m16, aA[1], aM[1]);
+      pair_store<D, 7>(sm, rrec, q4, m16, aA[0], aM[0]);
+      pair_store<D, 9>(sm, rrec, q4, m16, aA[1], aM[1]);
       break;
   }
   // M is zero above the diagonal blocks: (rb, ib) = (0,1..3), (1,2..3), (2,3)
@@ -338,119 +374,138 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
     const int rb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
     const int ib = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
     const int r = 16 * rb + (e >> 2), i = 16 * ib + 4 * (e & 3);
-    *reinterpret_cast<uint2*>(rmm + (r * C + i) * 2) = make_uint2(0u, 0u);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rrec,
+                                          (r * PS + i) * 2, Rec<D>::mm, 0);
   }
   __syncthreads();
 
-  if (wave == 0) {
-    // column j of T = (I + A)^-1 by forward substitution: T[r][j] = -sum_{i<r} A[r][i] T[i][j]
-    // for r > j (the terms with i < j vanish), T[j][j] = 1, zero above
-    const int j = lane;
-    float col[C];
+  // T = (I + A)^-1 by 16-row blocks: the diagonal blocks by forward substitution
+  // (wave b, lane j < 16: column j of block b), then level by level
+  //   T_{rb,ib} = -T_{rb,rb} sum_{m=ib}^{rb-1} A_{rb,m} T_{m,ib},  rb - ib = 1, 2, 3
+  // (from (I + A) T = I: the off-diagonal blocks of I + A are those of A).
+  if (lane < 16) {
+    const int b0 = 16 * wave, j = lane;
+    float col[16];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float s = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s = fmaf(sm.as[r * AS + i], col[i], s);
-      col[r] = r == j ? 1.f : -s;
+      for (int i = 0; i < r; ++i) {
+        if (i & 1) s1 = fmaf(sm.as[(b0 + r) * AS + b0 + i], col[i], s1);
+        else s0 = fmaf(sm.as[(b0 + r) * AS + b0 + i], col[i], s0);
+      }
+      col[r] = r == j ? 1.f : -(s0 + s1);
     }
-    const float bj = sm.bs[j];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      const float x = col[r] * bj;
-      const __bf16 hi = (__bf16)x;
-      const __bf16 lo = (__bf16)(x - (float)hi);
-      *reinterpret_cast<__bf16*>(rec + Rec<D>::thi + (r * C + j) * 2) = hi;
-      *reinterpret_cast<__bf16*>(rec + Rec<D>::tlo + (r * C + j) * 2) = lo;
+    for (int r = 0; r < 16; ++r) sm.ts[(b0 + r) * AS + b0 + j] = col[r];
+  }
+  __syncthreads();
+  {
+    const int i16 = tid >> 4, j16 = tid & 15;
+#pragma unroll
+    for (int L = 1; L < 4; ++L) {
+#pragma unroll
+      for (int ib = 0; ib + L < 4; ++ib) {
+        const int rb = ib + L;
+        float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+        for (int k = 16 * ib; k < 16 * rb; ++k) {
+          const float t = sm.as[(16 * rb + i16) * AS + k] * sm.ts[k * AS + 16 * ib + j16];
+          if (k & 1) w1 += t;
+          else w0 += t;
+        }
+        sm.wb[ib][tid] = w0 + w1;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ib = 0; ib + L < 4; ++ib) {
+        const int rb = ib + L;
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t = fmaf(sm.ts[(16 * rb + i16) * AS + 16 * rb + k], sm.wb[ib][16 * k + j16], t);
+        sm.ts[(16 * rb + i16) * AS + 16 * ib + j16] = -t;
+      }
+      __syncthreads();
     }
+  }
+  // Tb = T diag(beta) as bf16 high and low parts: thread t, row t / 4, columns 16 (t % 4) .. +15
+  {
+    const int r = tid >> 2, cb = tid & 3;
+    uint32_t hv[8], lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 16 * cb + 2 * e + u;
+        x2[u] = cb > (r >> 4) ? 0.f : sm.ts[r * AS + j] * sm.bs[j];
+      }
+      const __bf16 h0 = (__bf16)x2[0], h1 = (__bf16)x2[1];
+      const __bf16 l0 = (__bf16)(x2[0] - (float)h0), l1 = (__bf16)(x2[1] - (float)h1);
+      hv[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lv[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    const int off = (r * PS + 16 * cb) * 2;
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{hv[0], hv[1], hv[2], hv[3]}, rrec, off, Rec<D>::thi, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{hv[4], hv[5], hv[6], hv[7]}, rrec, off + 16, Rec<D>::thi, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{lv[0], lv[1], lv[2], lv[3]}, rrec, off, Rec<D>::tlo, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{lv[4], lv[5], lv[6], lv[7]}, rrec, off + 16, Rec<D>::tlo, 0);
   }
 }
 
 // ============================================================================ state pass
 template <int D>
 struct StateSmem {
-  __bf16 kg[C * (D + 8)];
-  __bf16 qg[C * (D + 8)];
-  __bf16 kpt[D * PS];
-  __bf16 thi[C * PS];
-  __bf16 tlo[C * PS];
-  __bf16 mm[C * PS];
-  __bf16 vs[C * (Slice<D>::nv + 8)];   // V of the chunk, this workgroup's columns
-  float gam[D];
+  alignas(16) char rec[Rec<D>::bytes];      // the chunk's record, byte for byte
+  __bf16 vs[C * (Slice<D>::nv + 8)];       // V of the chunk, this workgroup's columns
   int lens[kLptMax];
   int order;
+  __device__ const __bf16* tile(int off) const { return reinterpret_cast<const __bf16*>(rec + off); }
 };
 
 template <int D>
-struct Pieces {   // 16-byte pieces of one chunk's operands, in record order, then V
-  static constexpr int kg = C * D / 8;
-  static constexpr int kpt = D * C / 8;
-  static constexpr int tile = C * C / 8;
-  static constexpr int gam = D / 4;
+struct Pieces {   // 16-byte pieces of one chunk's operands per thread: the record, then V
+  static constexpr int nt = Slice<D>::nt;
   static constexpr int rec = Rec<D>::bytes / 16;
-  static constexpr int v = C * Slice<D>::nv / 8;
-  static constexpr int total = rec + v;
-  static constexpr int per_thread = (total + Slice<D>::nt - 1) / Slice<D>::nt;
-  static_assert(rec == 2 * kg + kpt + 3 * tile + gam, "record layout");
+  static constexpr int full = rec / nt;                  // record rounds every thread takes
+  static constexpr int tail = rec - full * nt;           // threads with one more piece
+  static constexpr int vp = Slice<D>::nv / 8;            // V pieces per row
+  static constexpr int vr = C * vp / nt;                 // V rounds
+  static constexpr int per_thread = full + (tail ? 1 : 0) + vr;
+  static_assert(C * vp % nt == 0, "V pieces spread evenly");
 };
 
+// The next chunk's record and V slice into registers.  Pieces past the record,
+// and V rows past the sequence, read as zero through the descriptors.
 template <int D>
-__device__ __forceinline__ void chunk_load(uint4* buf, const char* rec, const uint16_t* vrow0,
-                                           size_t vstride, int rows, int tid) {
+__device__ __forceinline__ void chunk_load(u32x4* buf, __amdgpu_buffer_rsrc_t rrec,
+                                           __amdgpu_buffer_rsrc_t rv, int vrow_bytes, int tid) {
   using P = Pieces<D>;
-  constexpr int VP = Slice<D>::nv / 8;   // 16-byte pieces per row of the V slice
 #pragma unroll
-  for (int i = 0; i < P::per_thread; ++i) {
-    const int x = tid + Slice<D>::nt * i;
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (x < P::rec) {
-      u = *reinterpret_cast<const uint4*>(rec + (size_t)x * 16);
-    } else if (x < P::total) {
-      const int y = x - P::rec, row = y / VP, part = y % VP;
-      if (row < rows) u = *reinterpret_cast<const uint4*>(vrow0 + row * vstride + 8 * part);
-    }
-    buf[i] = u;
+  for (int i = 0; i < P::full + (P::tail ? 1 : 0); ++i)
+    buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rrec, (tid + P::nt * i) * 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < P::vr; ++i) {
+    const int y = tid + P::nt * i, row = y / P::vp, part = y % P::vp;
+    buf[P::full + (P::tail ? 1 : 0) + i] =
+        __builtin_amdgcn_raw_buffer_load_b128(rv, row * vrow_bytes + 16 * part, 0, 0);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void chunk_stage(StateSmem<D>& sm, const uint4* buf, int tid) {
+__device__ __forceinline__ void chunk_stage(StateSmem<D>& sm, const u32x4* buf, int tid) {
   using P = Pieces<D>;
-  constexpr int KS = D + 8;
   constexpr int VS = Slice<D>::nv + 8;
-  constexpr int VP = Slice<D>::nv / 8;
 #pragma unroll
-  for (int i = 0; i < P::per_thread; ++i) {
-    const int x = tid + Slice<D>::nt * i;
-    __bf16* dst;
-    if (x < P::kg) {
-      dst = &sm.kg[(x / (D / 8)) * KS + 8 * (x % (D / 8))];
-    } else if (x < 2 * P::kg) {
-      const int y = x - P::kg;
-      dst = &sm.qg[(y / (D / 8)) * KS + 8 * (y % (D / 8))];
-    } else if (x < 2 * P::kg + P::kpt) {
-      const int y = x - 2 * P::kg;
-      dst = &sm.kpt[(y >> 3) * PS + 8 * (y & 7)];
-    } else if (x < 2 * P::kg + P::kpt + P::tile) {
-      const int y = x - 2 * P::kg - P::kpt;
-      dst = &sm.thi[(y >> 3) * PS + 8 * (y & 7)];
-    } else if (x < 2 * P::kg + P::kpt + 2 * P::tile) {
-      const int y = x - 2 * P::kg - P::kpt - P::tile;
-      dst = &sm.tlo[(y >> 3) * PS + 8 * (y & 7)];
-    } else if (x < 2 * P::kg + P::kpt + 3 * P::tile) {
-      const int y = x - 2 * P::kg - P::kpt - 2 * P::tile;
-      dst = &sm.mm[(y >> 3) * PS + 8 * (y & 7)];
-    } else if (x < P::rec) {
-      const int y = x - (P::rec - P::gam);
-      *reinterpret_cast<uint4*>(&sm.gam[4 * y]) = buf[i];
-      continue;
-    } else if (x < P::total) {
-      const int y = x - P::rec;
-      dst = &sm.vs[(y / VP) * VS + 8 * (y % VP)];
-    } else {
-      continue;
-    }
-    *reinterpret_cast<uint4*>(dst) = buf[i];
+  for (int i = 0; i < P::full; ++i)
+    *reinterpret_cast<u32x4*>(sm.rec + 16 * (tid + P::nt * i)) = buf[i];
+  if (P::tail && tid < P::tail)
+    *reinterpret_cast<u32x4*>(sm.rec + 16 * (tid + P::nt * P::full)) = buf[P::full];
+#pragma unroll
+  for (int i = 0; i < P::vr; ++i) {
+    const int y = tid + P::nt * i;
+    *reinterpret_cast<u32x4*>(&sm.vs[(y / P::vp) * VS + 8 * (y % P::vp)]) =
+        buf[P::full + (P::tail ? 1 : 0) + i];
   }
 }
 
@@ -518,12 +573,19 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
   }
 
   const int64_t slot0 = n + bos / C;
-  auto rec_of = [&](int c) { return p.ws + ((size_t)(slot0 + c) * p.H + h) * Rec<D>::bytes; };
-  auto vrow_of = [&](int c) { return p.v + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + split * NV; };
+  const int hsb = p.H * D * 2;   // token stride of v and out in bytes; the host bounds H * D
   auto rows_of = [&](int c) { return (int)(len - (int64_t)c * C < C ? len - (int64_t)c * C : C); };
+  auto rec_of = [&](int c) {
+    return rsrc(p.ws + ((size_t)(slot0 + c) * p.H + h) * Rec<D>::bytes, Rec<D>::bytes);
+  };
+  // this slice's V columns of the chunk's rows (later rows read as zero)
+  auto v_of = [&](int c) {
+    return rsrc(p.v + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + split * NV,
+                (rows_of(c) - 1) * hsb + NV * 2);
+  };
 
-  uint4 buf[Pieces<D>::per_thread];
-  if (nch > 0) chunk_load<D>(buf, rec_of(0), vrow_of(0), hs, rows_of(0), tid);
+  u32x4 buf[Pieces<D>::per_thread];
+  if (nch > 0) chunk_load<D>(buf, rec_of(0), v_of(0), hsb, tid);
 
   for (int c = 0; c < nch; ++c) {
     // lane indices through an empty asm: addresses are formed where they are used
@@ -533,7 +595,7 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
     __syncthreads();   // the previous chunk's operands are no longer read
     chunk_stage<D>(sm, buf, ti);
     __syncthreads();
-    if (c + 1 < nch) chunk_load<D>(buf, rec_of(c + 1), vrow_of(c + 1), hs, rows_of(c + 1), ti);
+    if (c + 1 < nch) chunk_load<D>(buf, rec_of(c + 1), v_of(c + 1), hsb, ti);
 
     // P1 = kg S, P2 = qg S (rows 16 rb + 4 q4 + t, column jw + m16)
     f32x4 p1[4], p2[4];
@@ -544,8 +606,8 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
       const bf16x8 sf = cat(cvt4(st[2 * ks]), cvt4(st[2 * ks + 1]));
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const __bf16* kp = &sm.kg[(16 * rb + m16) * KS + 32 * ks + 4 * q4];
-        const __bf16* qp = &sm.qg[(16 * rb + m16) * KS + 32 * ks + 4 * q4];
+        const __bf16* kp = sm.tile(Rec<D>::kg) + (16 * rb + m16) * KS + 32 * ks + 4 * q4;
+        const __bf16* qp = sm.tile(Rec<D>::qg) + (16 * rb + m16) * KS + 32 * ks + 4 * q4;
         p1[rb] = mfma32(ld2x4(kp, kp + 16), sf, p1[rb]);
         p2[rb] = mfma32(ld2x4(qp, qp + 16), sf, p2[rb]);
       }
@@ -577,8 +639,8 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
       u[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks <= ib / 2; ++ks) {
-        const __bf16* th = &sm.thi[(16 * ib + m16) * PS + 32 * ks + 4 * q4];
-        const __bf16* tl = &sm.tlo[(16 * ib + m16) * PS + 32 * ks + 4 * q4];
+        const __bf16* th = sm.tile(Rec<D>::thi) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
+        const __bf16* tl = sm.tile(Rec<D>::tlo) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
         const bf16x8 a = ld2x4(th, th + 16);
         u[ib] = mfma32(a, zh[ks], u[ib]);
         u[ib] = mfma32(a, zl[ks], u[ib]);
@@ -589,35 +651,34 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) uf[ks] = cat(cvt4(u[2 * ks]), cvt4(u[2 * ks + 1]));
 
-    // O = scale (P2 + M U)
-    const int rows = rows_of(c);
-    uint16_t* orow = p.out + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + jw + m16;
+    // O = scale (P2 + M U); rows past the sequence are dropped by the descriptor
+    const auto ro = rsrc(p.out + (size_t)(bos + (int64_t)c * C) * hs + (size_t)h * D + jw,
+                         (rows_of(c) - 1) * hsb + 32);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       f32x4 o = p2[rb];
 #pragma unroll
       for (int ks = 0; ks <= rb / 2; ++ks) {
-        const __bf16* mp = &sm.mm[(16 * rb + m16) * PS + 32 * ks + 4 * q4];
+        const __bf16* mp = sm.tile(Rec<D>::mm) + (16 * rb + m16) * PS + 32 * ks + 4 * q4;
         o = mfma32(ld2x4(mp, mp + 16), uf[ks], o);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 16 * rb + 4 * q4 + t;
-        if (r < rows) orow[(size_t)r * hs] = f2bf(p.scale * o[t]);
-      }
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(p.scale * o[t]), ro, m16 * 2,
+                                              (16 * rb + 4 * q4 + t) * hsb, 0);
     }
 
     // S' = Diag(gam) S + kpt U
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[16 * cb + 4 * q4]);
+      const float4 gm = *reinterpret_cast<const float4*>(sm.rec + Rec<D>::gam + (16 * cb + 4 * q4) * 4);
       st[cb][0] *= gm.x;
       st[cb][1] *= gm.y;
       st[cb][2] *= gm.z;
       st[cb][3] *= gm.w;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* kp = &sm.kpt[(16 * cb + m16) * PS + 32 * ks + 4 * q4];
+        const __bf16* kp = sm.tile(Rec<D>::kpt) + (16 * cb + m16) * PS + 32 * ks + 4 * q4;
         st[cb] = mfma32(ld2x4(kp, kp + 16), uf[ks], st[cb]);
       }
       if (cb % 4 == 3) __builtin_amdgcn_sched_barrier(0);

@@ -32,13 +32,13 @@ def state_bytes(n_states: int, H: int, dtype_bytes: int, d: int = D) -> int:
 
 
 def workload_bytes(tokens: int, H: int, n_states: int, init_bytes: int | None,
-                   final_bytes: int | None, scalar_gate: bool = False) -> int:
-    """Compulsory bytes of one pass over `tokens` packed tokens with H heads."""
-    b = tokens * H * bytes_per_token_head(scalar_gate=scalar_gate)
+                   final_bytes: int | None, scalar_gate: bool = False, d: int = D) -> int:
+    """Compulsory bytes of one pass over `tokens` packed tokens with H heads of size d."""
+    b = tokens * H * bytes_per_token_head(d, scalar_gate=scalar_gate)
     if init_bytes:
-        b += state_bytes(n_states, H, init_bytes)
+        b += state_bytes(n_states, H, init_bytes, d)
     if final_bytes:
-        b += state_bytes(n_states, H, final_bytes)
+        b += state_bytes(n_states, H, final_bytes, d)
     return b
 
 

@@ -78,6 +78,7 @@ def test_check_accepts_valid_arguments(lib):
     (dict(B=0), ERR_SHAPE),
     (dict(H=0), ERR_SHAPE),
     (dict(T=-1), ERR_SHAPE),
+    (dict(H=32769), ERR_SHAPE),
     (dict(q=0), ERR_NULL),
     (dict(beta=0), ERR_NULL),
     (dict(out=0), ERR_NULL),
@@ -177,9 +178,10 @@ def test_bwd_workspace_bytes(lib):
 
 def test_dim_workspace_bytes(lib):
     # one record per (chunk slot, head); slots: N + ceil(rows / 64) + 1.  A record
-    # holds kg, qg, kp^T (64 x d bf16 each), three 64 x 64 bf16 tiles and d fp32.
+    # holds kg, qg (64 rows of d + 8 bf16), kp^T (d rows of 72 bf16), three tiles of
+    # 64 rows of 72 bf16 and d fp32.
     for d in (64, 256):
-        rec = 3 * 64 * d * 2 + 3 * 64 * 64 * 2 + d * 4
+        rec = 2 * 64 * (d + 8) * 2 + d * 72 * 2 + 3 * 64 * 72 * 2 + d * 4
         assert binding.dim_workspace_bytes(16, 65536, 32, d) == (16 + 1024 + 1) * 32 * rec
         assert binding.dim_workspace_bytes(1, 65, 2, d) == (1 + 2 + 1) * 2 * rec
         assert binding.dim_workspace_bytes(3, 0, 2, d) == 0
