@@ -517,6 +517,7 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
   constexpr int NTS = Slice<D>::nt;
   constexpr int NCB = D / 16;   // 16-row tiles of the state slice per wave
   constexpr int NKS = D / 32;   // k-steps over the channels
+  constexpr int KG = D == 64 ? 2 : 1;   // k-steps per group of the first products
   constexpr int NSL = D / NV;   // value slices per (sequence, head)
   __shared__ StateSmem<D> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -597,22 +598,54 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
     __syncthreads();
     if (c + 1 < nch) chunk_load<D>(buf, rec_of(c + 1), v_of(c + 1), hsb, ti);
 
-    // P1 = kg S, P2 = qg S (rows 16 rb + 4 q4 + t, column jw + m16)
+    // The products of each phase read their LDS operand fragments first: the
+    // scheduling groups keep the reads ahead of the MFMAs, so that LDS latency is
+    // paid once per group instead of once per product.
+    // V of this wave's columns, read now and used after the first products
+    float vv[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vv[rb][t] = (float)sm.vs[(16 * rb + 4 * q4 + t) * VS + 16 * wave + m16];
+
+    // P1 = kg S, P2 = qg S (rows 16 rb + 4 q4 + t, column jw + m16), KG k-steps per group
     f32x4 p1[4], p2[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) p1[rb] = p2[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 sf = cat(cvt4(st[2 * ks]), cvt4(st[2 * ks + 1]));
+    for (int k0 = 0; k0 < NKS; k0 += KG) {
+      bf16x8 ka[KG][4], qa[KG][4];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const __bf16* kp = sm.tile(Rec<D>::kg) + (16 * rb + m16) * KS + 32 * ks + 4 * q4;
-        const __bf16* qp = sm.tile(Rec<D>::qg) + (16 * rb + m16) * KS + 32 * ks + 4 * q4;
-        p1[rb] = mfma32(ld2x4(kp, kp + 16), sf, p1[rb]);
-        p2[rb] = mfma32(ld2x4(qp, qp + 16), sf, p2[rb]);
+      for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const __bf16* kp = sm.tile(Rec<D>::kg) + (16 * rb + m16) * KS + 32 * (k0 + kk) + 4 * q4;
+          const __bf16* qp = sm.tile(Rec<D>::qg) + (16 * rb + m16) * KS + 32 * (k0 + kk) + 4 * q4;
+          ka[kk][rb] = ld2x4(kp, kp + 16);
+          qa[kk][rb] = ld2x4(qp, qp + 16);
+        }
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk) {
+        const bf16x8 sf = cat(cvt4(st[2 * (k0 + kk)]), cvt4(st[2 * (k0 + kk) + 1]));
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          p1[rb] = mfma32(ka[kk][rb], sf, p1[rb]);
+          p2[rb] = mfma32(qa[kk][rb], sf, p2[rb]);
+        }
       }
-      // keep the operand loads of later k-steps from being hoisted (register pressure)
-      if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 * KG, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * KG, 0);   // then the products
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Tb fragments of the solve: block pairs (ib, ks) with ks <= ib / 2
+    bf16x8 tha[6], tla[6];
+#pragma unroll
+    for (int e = 0; e < 6; ++e) {
+      const int ib = e < 2 ? e : 2 + (e - 2) / 2, ks = e < 2 ? 0 : (e - 2) % 2;
+      const __bf16* th = sm.tile(Rec<D>::thi) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
+      const __bf16* tl = sm.tile(Rec<D>::tlo) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
+      tha[e] = ld2x4(th, th + 16);
+      tla[e] = ld2x4(tl, tl + 16);
     }
     // Y = V - P1 as bf16 high and low parts, in the permuted k order over rows
     bf16x8 zh[2], zl[2];
@@ -624,8 +657,7 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
         const int rb = 2 * ks + s;
         f32x4 y;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          y[t] = (float)sm.vs[(16 * rb + 4 * q4 + t) * VS + 16 * wave + m16] - p1[rb][t];
+        for (int t = 0; t < 4; ++t) y[t] = vv[rb][t] - p1[rb][t];
         hi[s] = cvt4(y);
         lo[s] = cvt4(y - up4(hi[s]));
       }
@@ -635,17 +667,24 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
     // U = Tb Y (Tb is lower triangular: block row ib needs k-steps 0 .. ib / 2)
     f32x4 u[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      u[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ib = 0; ib < 4; ++ib) u[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks <= ib / 2; ++ks) {
-        const __bf16* th = sm.tile(Rec<D>::thi) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
-        const __bf16* tl = sm.tile(Rec<D>::tlo) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
-        const bf16x8 a = ld2x4(th, th + 16);
-        u[ib] = mfma32(a, zh[ks], u[ib]);
-        u[ib] = mfma32(a, zl[ks], u[ib]);
-        u[ib] = mfma32(ld2x4(tl, tl + 16), zh[ks], u[ib]);
-      }
+    for (int e = 0; e < 6; ++e) {
+      const int ib = e < 2 ? e : 2 + (e - 2) / 2, ks = e < 2 ? 0 : (e - 2) % 2;
+      u[ib] = mfma32(tha[e], zh[ks], u[ib]);
+      u[ib] = mfma32(tha[e], zl[ks], u[ib]);
+      u[ib] = mfma32(tla[e], zh[ks], u[ib]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 18, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // M fragments, read before the output products
+    bf16x8 ma[6];
+#pragma unroll
+    for (int e = 0; e < 6; ++e) {
+      const int rb = e < 2 ? e : 2 + (e - 2) / 2, ks = e < 2 ? 0 : (e - 2) % 2;
+      const __bf16* mp = sm.tile(Rec<D>::mm) + (16 * rb + m16) * PS + 32 * ks + 4 * q4;
+      ma[e] = ld2x4(mp, mp + 16);
     }
     bf16x8 uf[2];
 #pragma unroll
@@ -658,30 +697,41 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
     for (int rb = 0; rb < 4; ++rb) {
       f32x4 o = p2[rb];
 #pragma unroll
-      for (int ks = 0; ks <= rb / 2; ++ks) {
-        const __bf16* mp = sm.tile(Rec<D>::mm) + (16 * rb + m16) * PS + 32 * ks + 4 * q4;
-        o = mfma32(ld2x4(mp, mp + 16), uf[ks], o);
-      }
+      for (int ks = 0; ks <= rb / 2; ++ks) o = mfma32(ma[rb < 2 ? rb : 2 + 2 * (rb - 2) + ks], uf[ks], o);
+      // lane-dependent row part in the vector offset, the block's row in the scalar one
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_raw_buffer_store_b16(f2bf(p.scale * o[t]), ro, m16 * 2,
-                                              (16 * rb + 4 * q4 + t) * hsb, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(p.scale * o[t]), ro, (4 * q4 + t) * hsb + m16 * 2,
+                                              16 * rb * hsb, 0);
     }
 
-    // S' = Diag(gam) S + kpt U
+    // S' = Diag(gam) S + kpt U, four 16-row tiles per group
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const float4 gm = *reinterpret_cast<const float4*>(sm.rec + Rec<D>::gam + (16 * cb + 4 * q4) * 4);
-      st[cb][0] *= gm.x;
-      st[cb][1] *= gm.y;
-      st[cb][2] *= gm.z;
-      st[cb][3] *= gm.w;
+    for (int c0 = 0; c0 < NCB; c0 += 4) {
+      bf16x8 kf[4][2];
+      float4 gm[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* kp = sm.tile(Rec<D>::kpt) + (16 * cb + m16) * PS + 32 * ks + 4 * q4;
-        st[cb] = mfma32(ld2x4(kp, kp + 16), uf[ks], st[cb]);
+      for (int cc = 0; cc < 4; ++cc) {
+        gm[cc] = *reinterpret_cast<const float4*>(sm.rec + Rec<D>::gam + (16 * (c0 + cc) + 4 * q4) * 4);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const __bf16* kp = sm.tile(Rec<D>::kpt) + (16 * (c0 + cc) + m16) * PS + 32 * ks + 4 * q4;
+          kf[cc][ks] = ld2x4(kp, kp + 16);
+        }
       }
-      if (cb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int cb = c0 + cc;
+        st[cb][0] *= gm[cc].x;
+        st[cb][1] *= gm[cc].y;
+        st[cb][2] *= gm[cc].z;
+        st[cb][3] *= gm[cc].w;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) st[cb] = mfma32(kf[cc][ks], uf[ks], st[cb]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
