@@ -172,9 +172,13 @@ struct PrepSmem {
     };
     float ts[C * AS];      // T = (I + A)^-1 (lower blocks), after the last panel
   };
-  float bt[4][64];         // per row block and channel: sum of g log2(e)
-  float pf[10][64];        // exp2(X_rb - X_{ib+1}) per pair and channel
-  float wb[3][256];        // sum_m A_{rb,m} T_{m,ib} of one level of the inverse
+  union {
+    struct {
+      float bt[4][64];     // per row block and channel: sum of g log2(e)
+      float pf[10][64];    // exp2(X_rb - X_{ib+1}) per pair and channel
+    };
+    float wb[3][256];      // sum_m A_{rb,m} T_{m,ib} of one level of the inverse, after the panels
+  };
   float bs[C];             // beta of the chunk
 };
 
