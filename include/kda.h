@@ -18,8 +18,8 @@
  *
  * Argument conventions follow the kernel API the pages describe
  * [trend.ondo.sh "MoonshotAI/FlashKDA", section "커널 API와 제약 조건"]:
- * K = V = 128 (kda_fwd and kda_gdn_fwd also take K = V = 64 or 256, see below;
- * the other entry points take 128 only); variable-length packing through cu_seqlens requires
+ * K = V = 128 (the forward and decode calls also take K = V = 64 or 256, see
+ * below; the backward takes 128 only); variable-length packing through cu_seqlens requires
  * B = 1; the initial and final states are each bf16, fp32 or absent, and
  * must have the same dtype when both are given.
  *
@@ -170,17 +170,18 @@ kda_status kda_plan(int32_t n_sequences, int64_t T, int32_t H, int32_t varlen, i
  * -- the same step kda_fwd takes per token, so a prefill's final state can be
  * continued here.
  *
- *  q, k, v       device, bf16, [N, H, 128] (one token per sequence), 16-byte aligned.
- *  g             device, fp32, [N, H, 128], 16-byte aligned (log-decay).
+ *  q, k, v       device, bf16, [N, H, d] (one token per sequence), 16-byte aligned;
+ *                d = K = V is 128, 64 or 256.
+ *  g             device, fp32, [N, H, d], 16-byte aligned (log-decay).
  *  beta          device, fp32, [N, H], 4-byte aligned.
- *  state         device, [slots, H, 128, 128] (d_k-major), bf16 or fp32 per
+ *  state         device, [slots, H, d, d] (d_k-major), bf16 or fp32 per
  *                state_dtype, 16-byte aligned; read and overwritten in place
  *                (bf16 states are rounded to nearest even on store).
  *  state_indices device, int32, [N], or NULL: the slot s(n) of each sequence
  *                (NULL: s(n) = n).  A negative entry skips the sequence: neither
  *                its state nor its output row is touched.  Distinct sequences must
  *                name distinct slots (not checked).
- *  out           device, bf16, [N, H, 128], 16-byte aligned.
+ *  out           device, bf16, [N, H, d], 16-byte aligned.
  *  stream        hipStream_t (NULL = null stream); asynchronous like kda_fwd.
  * Memory: no workspace; each (sequence, head) reads and writes its state once.
  * Errors: as kda_fwd (KDA_ERR_HEAD_DIM, KDA_ERR_SHAPE for N < 0 or H <= 0,

@@ -234,10 +234,10 @@ def gdn_decode_check(*, N, H, K=D, V=D, q=0, k=0, v=0, g=0, beta=0, out=0, state
 def decode(q, k, v, g, beta, state, scale: float | None = None, state_indices=None, out=None):
     """One recurrent KDA step per sequence on the current HIP stream; `state` is updated in place.
 
-    q, k, v: bf16 [N, H, 128] (one token per sequence); g: fp32 [N, H, 128];
-    beta: fp32 [N, H]; state: [slots, H, 128, 128] bf16 or fp32; state_indices:
+    q, k, v: bf16 [N, H, d] (one token per sequence, d = 128, 64 or 256); g: fp32
+    [N, H, d]; beta: fp32 [N, H]; state: [slots, H, d, d] bf16 or fp32; state_indices:
     optional int32 [N] slot per sequence (negative: skip); scale defaults to
-    1/sqrt(128).  Returns out (bf16 [N, H, 128]).
+    1/sqrt(d).  Returns out (bf16 [N, H, d]).
     """
     return _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate=False)
 
@@ -251,7 +251,7 @@ def _decode(q, k, v, g, beta, state, scale, state_indices, out, scalar_gate):
     import torch
     lib = load_library()
     if q.dim() != 3:
-        raise ValueError("q must be [N, H, 128]")
+        raise ValueError("q must be [N, H, d]")
     N, H, K = q.shape
     V = v.shape[-1]
     dev = q.device

@@ -409,8 +409,8 @@ kda_status validate_decode(const void* q, const void* k, const void* v, const fl
                            const float* beta, const void* state, int state_dtype,
                            const int32_t* state_indices, int32_t N, int32_t H, int32_t K,
                            int32_t V, const void* out, bool g_scalar) {
-  if (K != KDA_HEAD_DIM || V != KDA_HEAD_DIM)
-    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: only K = V = 128 is supported", K, V);
+  if (K != V || (K != 64 && K != KDA_HEAD_DIM && K != 256))
+    return fail(KDA_ERR_HEAD_DIM, "K=%d V=%d: K = V in {64, 128, 256} is required", K, V);
   if (N < 0 || H <= 0) return fail(KDA_ERR_SHAPE, "invalid sizes N=%d H=%d", N, H);
   if ((int64_t)N * H > (int64_t)INT_MAX)
     return fail(KDA_ERR_SHAPE, "N*H=%lld too large", (long long)N * H);
@@ -453,6 +453,7 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const float*
   p.state_fp32 = state_dtype == KDA_FP32;
   p.nseq = N;
   p.H = H;
+  p.D = K;
   if (log_enabled())
     std::fprintf(stderr, "[kda] decode: %s N=%d H=%d state=%s indexed=%d\n", g_scalar ? "gdn" : "kda",
                  N, H, p.state_fp32 ? "fp32" : "bf16", state_indices != nullptr);

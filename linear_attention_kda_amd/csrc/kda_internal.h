@@ -65,14 +65,15 @@ int workspace_slots(int cus, int H);
 
 // One decode step: one token per sequence, state updated in place.
 struct DecodeParams {
-  const uint16_t* q;      // bf16 [N][H][128]
+  const uint16_t* q;      // bf16 [N][H][D]
   const uint16_t* k;
   const uint16_t* v;
-  const float* g;         // fp32 [N][H][128], or [N][H] when g_scalar
+  const float* g;         // fp32 [N][H][D], or [N][H] when g_scalar
   const float* beta;      // fp32 [N][H]
-  uint16_t* out;          // bf16 [N][H][128]
+  uint16_t* out;          // bf16 [N][H][D]
   int g_scalar;           // one gate per token and head (Gated DeltaNet)
-  void* state;            // [slots][H][128][128], bf16 or fp32
+  int D;                  // head dimension: 64, 128 or 256
+  void* state;            // [slots][H][D][D], bf16 or fp32
   const int32_t* idx;     // [N] state slot of each sequence (negative: skip), or null (slot n)
   float scale;
   int state_fp32;

@@ -102,6 +102,8 @@ def dec_args(**over):
 
 def test_decode_check_accepts_valid_arguments(lib):
     assert binding.decode_check(**dec_args()) == OK
+    assert binding.decode_check(**dec_args(K=64, V=64)) == OK
+    assert binding.decode_check(**dec_args(K=256, V=256)) == OK
     assert binding.decode_check(**dec_args(state_dtype=0, state_indices=P + 0x8000)) == OK
     assert binding.decode_check(**dec_args(N=0, q=0, k=0, v=0, g=0, beta=0, out=0, state=0)) == OK
 
@@ -109,7 +111,7 @@ def test_decode_check_accepts_valid_arguments(lib):
 @pytest.mark.parametrize("over,status", [
     (dict(K=64), ERR_HEAD_DIM),
     (dict(V=256), ERR_HEAD_DIM),
-    (dict(K=64, V=64), ERR_HEAD_DIM),
+    (dict(K=96, V=96), ERR_HEAD_DIM),
     (dict(N=-1), ERR_SHAPE),
     (dict(H=0), ERR_SHAPE),
     (dict(state_dtype=2), ERR_DTYPE),

@@ -45,9 +45,9 @@ def _gpu_required():
     binding.load_library()
 
 
-def step_inputs(N, H, seed, T=1, state="fp32"):
+def step_inputs(N, H, seed, T=1, state="fp32", D=128):
     """T tokens for each of N sequences, packed as [N, T, H, .] rows, and start states."""
-    x = random_inputs(N, T, H, seed=seed, device=DEV, init_state=state)
+    x = random_inputs(N, T, H, D, D, seed=seed, device=DEV, init_state=state)
     return x
 
 
@@ -58,11 +58,12 @@ def oracle_steps(x):
     return o, S
 
 
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("state", ["fp32", "bf16"])
-def test_decode_single_step(state):
+def test_decode_single_step(state, D):
     N, H = 12, 4
-    announce(f"decode single step N={N} H={H} state={state}")
-    x = step_inputs(N, H, seed=40, state=state)
+    announce(f"decode single step N={N} H={H} state={state} d={D}")
+    x = step_inputs(N, H, seed=40, state=state, D=D)
     o_ref, S_ref = oracle_steps(x)
     S = x["initial_state"].clone()
     out = binding.decode(x["q"][:, 0].contiguous(), x["k"][:, 0].contiguous(),
@@ -75,10 +76,11 @@ def test_decode_single_step(state):
     assert e_o <= TOL and e_s <= TOL
 
 
-def test_decode_chained_steps():
+@pytest.mark.parametrize("D", [128, 64, 256])
+def test_decode_chained_steps(D):
     N, H, T = 6, 3, 24
-    announce(f"decode {T} chained steps N={N} H={H}")
-    x = step_inputs(N, H, seed=41, T=T)
+    announce(f"decode {T} chained steps N={N} H={H} d={D}")
+    x = step_inputs(N, H, seed=41, T=T, D=D)
     o_ref, S_ref = oracle_steps(x)
     S = x["initial_state"].clone()
     outs = []
@@ -122,11 +124,12 @@ def test_decode_state_indices_and_skip():
     assert torch.equal(pool[untouched], before[untouched])
 
 
-def test_decode_continues_a_prefill():
+@pytest.mark.parametrize("D", [128, 64, 256])
+def test_decode_continues_a_prefill(D):
     """kda_fwd over T tokens, then kda_decode of token T+1 == kda_fwd over T+1 tokens."""
     H, T = 4, 300
-    announce(f"prefill {T} tokens then decode one, H={H}")
-    x = random_inputs(1, T + 1, H, seed=44, device=DEV, init_state="fp32")
+    announce(f"prefill {T} tokens then decode one, H={H} d={D}")
+    x = random_inputs(1, T + 1, H, D, D, seed=44, device=DEV, init_state="fp32")
     pre = {k: x[k][:, :T].contiguous() for k in ("q", "k", "v", "g", "beta")}
     _, S = binding.fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], x["scale"],
                        initial_state=x["initial_state"], output_final_state=True)
