@@ -148,17 +148,18 @@ def cpu_baseline(x, heads: int, min_seconds: float = 10.0):
                         f"{len(hs)} of {w.H} heads ({dt:.1f} s); value scaled to all heads"))
 
 
-def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32):
-    """One decode step for N sequences x H heads with fp32 states: HBM-bound on the state."""
+def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32, d: int = 128):
+    """One decode step for N sequences x H heads of size d with fp32 states: HBM-bound
+    on the state."""
     import torch
 
     from linear_attention_kda_amd import binding, perfmodel
     from linear_attention_kda_amd.workloads import random_inputs
 
-    x = random_inputs(N, 1, H, seed=1300, device="cuda", init_state="fp32")
+    x = random_inputs(N, 1, H, d, d, seed=1300, device="cuda", init_state="fp32")
     one = {k: x[k][:, 0].contiguous() for k in ("q", "k", "v", "g", "beta")}
     S = x["initial_state"]
-    out = torch.empty(N, H, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(N, H, d, dtype=torch.bfloat16, device="cuda")
 
     def step():
         binding.decode(one["q"], one["k"], one["v"], one["g"], one["beta"], S, x["scale"], out=out)
@@ -174,11 +175,12 @@ def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     # per (sequence, head): state read + write (fp32), q/k/v/o bf16, g fp32, beta
-    nbytes = N * H * (2 * 128 * 128 * 4 + 4 * 128 * 2 + 128 * 4 + 4)
+    nbytes = N * H * (2 * d * d * 4 + 4 * d * 2 + d * 4 + 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] decode N={N} H={H} fp32 state: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s "
+    tag = "" if d == 128 else f" d={d}"
+    log(f"[bench] decode{tag} N={N} H={H} fp32 state: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s "
         f"({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
-    return {"workload": f"decode step N={N} sequences H={H} fp32 state", "unit": "steps/s",
+    return {"workload": f"decode step N={N} sequences H={H}{tag} fp32 state", "unit": "steps/s",
             "value": 1e3 / ms, "us_per_step": ms * 1e3, "tokens_per_s": N * 1e3 / ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
@@ -416,8 +418,10 @@ def main():
         del x2
 
     decode = None
+    decode_dims = None
     if not args.no_decode:
         decode = decode_bench(max(args.steps, 20), args.warmup)
+        decode_dims = [decode_bench(max(args.steps, 20), args.warmup, d=d) for d in (64, 256)]
 
     gdn = None
     if not args.no_gdn:
@@ -465,6 +469,7 @@ def main():
                  "flops_model": "6Td^2+3TCd+TC^2 per head"},
         "secondary": secondary,
         "decode": decode,
+        "decode_head_dims": decode_dims,
         "gdn": gdn,
         "head_dims": dims,
         "bwd": bwd,

@@ -16,9 +16,11 @@
 // columns each; columns never mix) at D = 256.  With NC columns per workgroup,
 // thread t owns value columns 4 (t % (NC/4)) .. +3 and key rows t / (NC/4) + RG r,
 // RG = threads / (NC/4) row groups: every state row slice is read by NC/4
-// consecutive threads as one contiguous run.  D = 128: 256 threads, 8 row groups
-// of 16 rows; D = 64: 256 threads, 16 groups of 4 rows; D = 256: 1024 threads, 32
-// groups of 8 rows.  The two column dot products (S~^T k, S~^T q) are summed over
+// consecutive threads as one contiguous run.  D = 128: 512 threads, 16 row groups
+// of 8 rows; D = 64: 256 threads, 16 groups of 4 rows; D = 256: 1024 threads, 32
+// groups of 8 rows.  Eight rows of four columns per thread (32 state values) kept
+// the most loads in flight: at D = 128 it reached 77% of HBM bandwidth against 70%
+// with 256 threads of 16 rows.  The two column dot products (S~^T k, S~^T q) are summed over
 // the row groups in LDS; the state stays in registers between its load and its
 // store.
 #include <hip/hip_runtime.h>
@@ -34,7 +36,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned v2u;
 
 template <int D>
 struct Dec {
-  static constexpr int nt = D == 256 ? 1024 : 256;   // threads per workgroup
+  static constexpr int nt = D == 256 ? 1024 : D == 128 ? 512 : 256;   // threads per workgroup
   static constexpr int cs = D == 256 ? 2 : 1;         // workgroups per (sequence, head), by columns
   static constexpr int nc = D / cs;                   // value columns per workgroup
   static constexpr int cg = nc / 4;                   // column groups of 4
