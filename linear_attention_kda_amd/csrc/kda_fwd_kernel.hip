@@ -205,12 +205,13 @@ __device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f, bf1
       sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
 }
 
-// This workgroup's contiguous share of `units` fix-up units: o = O0 + S_p^T Q~ for
-// every row of each unit's chunk.  The next unit's loads are in flight while the
-// current one is multiplied; S_p is reloaded only when the segment or head changes.
+// This workgroup's contiguous share of `units` fix-up units, spread over the
+// workgroups first .. gridDim.x - 1: o = O0 + S_p^T Q~ for every row of each
+// unit's chunk.  The next unit's loads are in flight while the current one is
+// multiplied; S_p is reloaded only when the segment or head changes.
 __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0, int units,
-                          __bf16* ot) {
-  const int G = gridDim.x, b = blockIdx.x;
+                          __bf16* ot, int first) {
+  const int G = gridDim.x - first, b = blockIdx.x - first;
   const int u_lo = (int)((int64_t)units * b / G), u_hi = (int)((int64_t)units * (b + 1) / G);
   if (u_lo >= u_hi) return;
   const int tid = threadIdx.x;
@@ -287,9 +288,13 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
     // segment-1 fix-ups (they need only S_1, written by the main kernel)
     const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
     for (int u = blockIdx.x; u < nscan; u += gridDim.x) scan_unit(p, v, M, u, slt);
-    fix_range(p, v, M, v.uoff, 1, __builtin_amdgcn_readfirstlane(v.hdr[4]), ot);
+    // with workgroups to spare, the fix-ups go to those without a scan unit and run
+    // beside the scan instead of after it
+    const int first = nscan < (int)gridDim.x ? nscan : 0;
+    if ((int)blockIdx.x >= first)
+      fix_range(p, v, M, v.uoff, 1, __builtin_amdgcn_readfirstlane(v.hdr[4]), ot, first);
   } else {
-    fix_range(p, v, M, v.voff, 2, __builtin_amdgcn_readfirstlane(v.hdr[5]), ot);
+    fix_range(p, v, M, v.voff, 2, __builtin_amdgcn_readfirstlane(v.hdr[5]), ot, 0);
   }
 }
 
