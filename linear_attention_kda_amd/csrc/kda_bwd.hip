@@ -152,30 +152,36 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) 
   const int HD = p.H * D;
   if (t < C) w.beta[bidx * C + t] = t < valid ? p.beta[(bos + c * C + t) * p.H + h] : 0.f;
   if (t == 0) w.valid[bidx] = valid;
-  // thread t: channel t % 128, rows of parity t / 128
-  const int ch = t & 127, half = t >> 7;
-  // G: inclusive cumsum over the chunk (natural log), one channel per thread
-  __shared__ float gs[C][D];
-  for (int r = half; r < C; r += 2)
-    gs[r][ch] = r < valid ? p.g[((bos + c * C + r) * p.H + h) * D + ch] : 0.f;
-  __syncthreads();
-  if (half == 0) {
-    float run = 0.f;
-    for (int r = 0; r < C; ++r) { run += gs[r][ch]; gs[r][ch] = run; }
+  // thread t: channel t % 128, rows 32 (t / 128) .. +31
+  const int ch = t & 127, half = t >> 7, r0 = 32 * half;
+  // G: inclusive cumsum over the chunk (natural log): each thread sums its 32 rows in
+  // registers, then the second half adds the first half's total
+  __shared__ float tot[2][D];
+  float gv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int r = r0 + i;
+    gv[i] = r < valid ? p.g[((bos + c * C + r) * p.H + h) * D + ch] : 0.f;
   }
+#pragma unroll
+  for (int i = 1; i < 32; ++i) gv[i] += gv[i - 1];
+  tot[half][ch] = gv[31];
   __syncthreads();
-  const float Glast = gs[C - 1][ch];
+  const float off = half ? tot[0][ch] : 0.f;
+  const float Glast = tot[0][ch] + tot[1][ch];
   const float gam = expf(Glast);
   if (half == 0) w.gam[bidx * D + ch] = gam;
   const int64_t tb = bidx * (C * D);
-  for (int r = half; r < C; r += 2) {
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int r = r0 + i;
     const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
     const bool in = r < valid;
     const float qf = in ? bf2f_u16(p.q[row]) : 0.f;
     const float kf = in ? bf2f_u16(p.k[row]) : 0.f;
     const float vf = in ? bf2f_u16(p.v[row]) : 0.f;
     const float df = in ? p.scale * bf2f_u16(p.dout[row]) : 0.f;
-    const float G = gs[r][ch];
+    const float G = gv[i] + off;
     const float e = expf(G), ei = expf(-G);
     const int64_t o = tb + r * D + ch;
     w.G[o] = G;
@@ -332,7 +338,8 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
   const float* beta = w.beta + bidx * C;
   __shared__ float dGs[C][D];
   __shared__ float red[2][D];
-  __shared__ float dbs[2][C];
+  __shared__ float rowsum[D];
+  __shared__ float dbs[C];
   // per row: dG, dq, dk, dv; per channel: dG_last pieces
   float glast = 0.f;
   for (int r = half; r < C; r += 2) {
@@ -353,14 +360,28 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
     }
   }
   red[half][ch] = glast;
-  // dgam_direct: rowsum over j of S * dSn for channel ch (threads of half 0 and 1 split j)
+  // dgam_direct: gam_c times the row sum over j of S * dSn for every channel c.  Sixteen
+  // lanes share a row, each with eight consecutive entries (coalesced), and their sums
+  // meet through lane exchanges within the sixteen.
   {
     const float* S = w.S + bidx * (size_t)(D * D);
     const float* dsn = w.dSn + bidx * (size_t)(D * D);
-    float s = 0.f;
-    for (int j = half * 64; j < half * 64 + 64; ++j) s += S[ch * D + j] * dsn[ch * D + j];
+    const int jq = t & 15;
+#pragma unroll 2
+    for (int it = 0; it < D / 16; ++it) {
+      const int r = 16 * it + (t >> 4);
+      const float4 a0 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq);
+      const float4 a1 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq);
+      const float4 b1 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq + 4);
+      float sum = a0.x * b0.x + a0.y * b0.y + a0.z * b0.z + a0.w * b0.w +
+                  a1.x * b1.x + a1.y * b1.y + a1.z * b1.z + a1.w * b1.w;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      if (jq == 0) rowsum[r] = sum;
+    }
     __syncthreads();
-    red[half][ch] += s * w.gam[bidx * D + ch];
+    red[half][ch] += half == 0 ? rowsum[ch] * w.gam[bidx * D + ch] : 0.f;
   }
   __syncthreads();
   if (half == 0) {
@@ -372,17 +393,29 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
       if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + ch] = run;
     }
   }
-  // dbeta_r = sum_j dY_rj R_rj + sum_i dA_ri P_ri (two threads per row)
-  if (t < 2 * C) {
-    const int r = t >> 1, part = t & 1;
-    float s = 0.f;
-    for (int j = part * 64; j < part * 64 + 64; ++j) s += w.dY[tb + r * D + j] * w.R[tb + r * D + j];
-    for (int i = part * 32; i < part * 32 + 32; ++i)
-      s += w.dA[bidx * C * C + r * C + i] * w.P[bidx * C * C + r * C + i];
-    dbs[part][r] = s;
+  // dbeta_r = sum_j dY_rj R_rj + sum_i dA_ri P_ri: sixteen lanes per row, as above
+  {
+    const int jq = t & 15;
+#pragma unroll
+    for (int it = 0; it < C / 16; ++it) {
+      const int r = 16 * it + (t >> 4);
+      const float* dy = w.dY + tb + (size_t)r * D + 8 * jq;
+      const float* rr = w.R + tb + (size_t)r * D + 8 * jq;
+      const float* da = w.dA + bidx * C * C + (size_t)r * C + 4 * jq;
+      const float* pp = w.P + bidx * C * C + (size_t)r * C + 4 * jq;
+      const float4 y0 = *reinterpret_cast<const float4*>(dy), y1 = *reinterpret_cast<const float4*>(dy + 4);
+      const float4 q0 = *reinterpret_cast<const float4*>(rr), q1 = *reinterpret_cast<const float4*>(rr + 4);
+      const float4 a = *reinterpret_cast<const float4*>(da), b = *reinterpret_cast<const float4*>(pp);
+      float sum = y0.x * q0.x + y0.y * q0.y + y0.z * q0.z + y0.w * q0.w +
+                  y1.x * q1.x + y1.y * q1.y + y1.z * q1.z + y1.w * q1.w +
+                  a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      if (jq == 0) dbs[r] = sum;
+    }
   }
   __syncthreads();
-  if (t < valid) p.dbeta[(bos + c * C + t) * p.H + h] = dbs[0][t] + dbs[1][t];
+  if (t < valid) p.dbeta[(bos + c * C + t) * p.H + h] = dbs[t];
 }
 
 void gemm(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
