@@ -26,7 +26,7 @@
 // n + floor(bos_n / 64) + c of sequence n's chunk c (slots are distinct across
 // sequences); batch index b = slot * H + h addresses every per-chunk tile.
 // Everything here is fp32: the chunk-local products run as batched tiled GEMMs
-// (VALU), the serial recurrence in four workgroups per (sequence, head), one per
+// (fp32 matrix cores), the serial recurrence in four workgroups per (sequence, head), one per
 // 32 value columns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -66,17 +66,33 @@ __device__ __forceinline__ int slot_seq(const BwdParams& p, int64_t s) {
 // false) or [n][k] (TB true).  rs scales output rows.  mask: 0 none, 1 keep
 // n < m, 2 keep n <= m.  One workgroup computes a 64 x 64 tile; M, N, K are
 // multiples of 64, 64 and 16.
+//
+// The products run on the fp32 matrix cores (16 x 16 x 4 per instruction, fp32
+// operands and accumulation): twice the rate of unpacked fp32 FMAs.  Each wave
+// owns a 32 x 32 quarter of the tile as 2 x 2 blocks; for step k of four, lane
+// (q4, m16) supplies op(A)[16i + m16][k] and op(B)[k][16j + m16] with k = 4s + q4,
+// and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.
+typedef float bg_f32x4 __attribute__((ext_vector_type(4)));
+
 template <bool TA, bool TB>
 __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  // k-major tiles; a row stride of 80 floats puts lane groups q4 and q4 + 1 on
+  // disjoint banks for the operand reads
+  __shared__ float As[16][80];
+  __shared__ float Bs[16][80];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
+  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
   const int64_t b = blockIdx.z;
   const float* A = a.A + b * a.sA;
   const float* B = a.B + b * a.sB;
   const float* ks = a.ks ? a.ks + b * a.sks : nullptr;
-  float acc[4][4] = {};
+  bg_f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < a.K; k0 += 16) {
     if (!TA) {
       const int m = tid >> 2, k = (tid & 3) * 4;
@@ -88,12 +104,12 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
       const int k = tid >> 4, m = (tid & 15) * 4;
       const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(k0 + k) * a.lda + m0 + m);
       const float s = ks ? ks[k0 + k] : 1.f;
-      As[k][m] = v.x * s; As[k][m + 1] = v.y * s; As[k][m + 2] = v.z * s; As[k][m + 3] = v.w * s;
+      *reinterpret_cast<float4*>(&As[k][m]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
     }
     if (!TB) {
       const int k = tid >> 4, n = (tid & 15) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * a.ldb + n0 + n);
-      Bs[k][n] = v.x; Bs[k][n + 1] = v.y; Bs[k][n + 2] = v.z; Bs[k][n + 3] = v.w;
+      *reinterpret_cast<float4*>(&Bs[k][n]) =
+          *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * a.ldb + n0 + n);
     } else {
       const int n = tid >> 2, k = (tid & 3) * 4;
       const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * a.ldb + k0 + k);
@@ -101,16 +117,14 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int k = 4 * s4 + q4;
+      const float a0 = As[k][wm + m16], a1 = As[k][wm + 16 + m16];
+      const float b0 = Bs[k][wn + m16], b1 = Bs[k][wn + 16 + m16];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
@@ -118,22 +132,21 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   const float* Db = a.Dm ? a.Dm + b * a.sD : nullptr;
   const float* rs = a.rs ? a.rs + b * a.srs : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    const float r = rs ? rs[m] : 1.f;
-    float out[4];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      float v = a.alpha * acc[i][j];
-      if (Db) v += Db[(int64_t)m * a.ldd + n];
-      v *= r;
-      if ((a.mask == 1 && n >= m) || (a.mask == 2 && n > m)) v = 0.f;
-      out[j] = v;
+    for (int t = 0; t < 4; ++t) {
+      const int m = m0 + wm + 16 * i + 4 * q4 + t;
+      const float r = rs ? rs[m] : 1.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn + 16 * j + m16;
+        float v = a.alpha * acc[i][j][t];
+        if (Db) v += Db[(int64_t)m * a.ldd + n];
+        v *= r;
+        if ((a.mask == 1 && n >= m) || (a.mask == 2 && n > m)) v = 0.f;
+        Cb[(int64_t)m * a.ldc + n] = v;
+      }
     }
-    *reinterpret_cast<float4*>(Cb + (int64_t)m * a.ldc + n0 + tx * 4) =
-        make_float4(out[0], out[1], out[2], out[3]);
-  }
 }
 
 // ---------------------------------------------------------------- chunk prep
@@ -222,14 +235,20 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 
 // ---------------------------------------------------------------- serial dS
 // Column j of dS depends only on column j of dSn (Diag(gam), kp and F act on
-// rows), so each (sequence, head) runs as DSC workgroups of DSW value columns.
-// Chunks last to first: dSn(c) is stored for the chunk's gradient products,
-// then dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The
-// sequence's initial-state gradient is the last dS.
-constexpr int DSW = 32;            // value columns per workgroup
-constexpr int DSC = D / DSW;       // workgroups per (sequence, head)
-
+// rows), so each (sequence, head) runs as D / DSW workgroups of DSW value
+// columns.  Chunks last to first: dSn(c) is stored for the chunk's gradient
+// products, then dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The
+// sequence's initial-state gradient is the last dS.  The loop is serial and
+// VALU-bound inside a workgroup of four waves, so with few (sequence, head)
+// pairs the columns are cut finer (DSW 16) to occupy more compute units and
+// halve each workgroup's work per chunk.
+template <int DSW>
 __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
+  constexpr int DSC = D / DSW;       // workgroups per (sequence, head)
+  constexpr int CG = DSW / 4;        // column groups of 4
+  constexpr int RP = C * CG / 256;   // rows of P per thread
+  constexpr int RF = D * CG / 256;   // rows of dS per thread
+  static_assert(RP >= 1 && RF >= 1 && C * CG % 256 == 0, "slice width");
   __shared__ float ds[D][DSW + 4];   // dSn, then the new dS (this workgroup's columns)
   __shared__ float pp[C][DSW + 4];   // P = kp dSn
   const int pair = blockIdx.x / DSC, j0 = (blockIdx.x % DSC) * DSW;
@@ -248,42 +267,45 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
     ds[r][j] = v;
   }
   __syncthreads();
-  const int jb = (t & 7) * 4;   // 4 of this workgroup's columns
+  const int jb = (t % CG) * 4;   // 4 of this workgroup's columns
   for (int c = nch - 1; c >= 0; --c) {
     const int64_t bidx = (n + bos / C + c) * p.H + h;
     float* dsn = w.dSn + bidx * sd;
     for (int x = t; x < D * DSW; x += 256) dsn[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
-    {  // P = kp dSn: rows 2 (t / 8) .. +1
+    {  // P = kp dSn: rows RP (t / CG) .. +RP-1
       const float* kp = w.kp + bidx * (C * D);
-      const int r0 = (t >> 3) * 2;
-      float acc[2][4] = {};
+      const int r0 = (t / CG) * RP;
+      float acc[RP][4] = {};
       for (int k = 0; k < D; k += 4) {
-        const float4 a0 = *reinterpret_cast<const float4*>(&kp[r0 * D + k]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&kp[(r0 + 1) * D + k]);
-        const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
+        float av[RP][4];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&kp[(r0 + i) * D + k]);
+          av[i][0] = a4.x; av[i][1] = a4.y; av[i][2] = a4.z; av[i][3] = a4.w;
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const float4 bv = *reinterpret_cast<const float4*>(&ds[k + kk][jb]);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
+          for (int i = 0; i < RP; ++i) {
             acc[i][0] = fmaf(av[i][kk], bv.x, acc[i][0]); acc[i][1] = fmaf(av[i][kk], bv.y, acc[i][1]);
             acc[i][2] = fmaf(av[i][kk], bv.z, acc[i][2]); acc[i][3] = fmaf(av[i][kk], bv.w, acc[i][3]);
           }
         }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RP; ++i)
         *reinterpret_cast<float4*>(&pp[r0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
     __syncthreads();
-    {  // dS = gam (.) dSn - F P + X: rows 4 (t / 8) .. +3
+    {  // dS = gam (.) dSn - F P + X: rows RF (t / CG) .. +RF-1
       const float* F = w.F + bidx * (D * C);
       const float* X = w.X + bidx * sd;
       const float* gam = w.gam + bidx * D;
-      const int c0 = (t >> 3) * 4;
-      float acc[4][4];
+      const int c0 = (t / CG) * RF;
+      float acc[RF][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RF; ++i) {
         const float g = gam[c0 + i];
         const float4 xv = *reinterpret_cast<const float4*>(&X[(size_t)(c0 + i) * D + j0 + jb]);
         acc[i][0] = g * ds[c0 + i][jb] + xv.x;
@@ -292,9 +314,9 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
         acc[i][3] = g * ds[c0 + i][jb + 3] + xv.w;
       }
       for (int r = 0; r < C; r += 4) {
-        float fv[4][4];
+        float fv[RF][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < RF; ++i) {
           const float4 f4 = *reinterpret_cast<const float4*>(&F[(c0 + i) * C + r]);
           fv[i][0] = f4.x; fv[i][1] = f4.y; fv[i][2] = f4.z; fv[i][3] = f4.w;
         }
@@ -302,7 +324,7 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
         for (int rr = 0; rr < 4; ++rr) {
           const float4 bv = *reinterpret_cast<const float4*>(&pp[r + rr][jb]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < RF; ++i) {
             acc[i][0] = fmaf(-fv[i][rr], bv.x, acc[i][0]); acc[i][1] = fmaf(-fv[i][rr], bv.y, acc[i][1]);
             acc[i][2] = fmaf(-fv[i][rr], bv.z, acc[i][2]); acc[i][3] = fmaf(-fv[i][rr], bv.w, acc[i][3]);
           }
@@ -310,7 +332,7 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
       }
       __syncthreads();  // every read of dSn and P is done
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RF; ++i)
         *reinterpret_cast<float4*>(&ds[c0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
     __syncthreads();
@@ -319,6 +341,16 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
     float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
     for (int x = t; x < D * DSW; x += 256) o[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
   }
+}
+
+// The scan's launch: 32-column slices once four per (sequence, head) fill the
+// 256 compute units, 16-column slices below that.
+void launch_ds_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s) {
+  const int64_t pairs = (int64_t)p.nseq * p.H;
+  if (pairs * (D / 32) >= 256)
+    hipLaunchKernelGGL(bwd_ds_scan_kernel<32>, dim3((unsigned)(pairs * (D / 32))), dim3(256), 0, s, p, w);
+  else
+    hipLaunchKernelGGL(bwd_ds_scan_kernel<16>, dim3((unsigned)(pairs * (D / 16))), dim3(256), 0, s, p, w);
 }
 
 // ---------------------------------------------------------------- gates and scatter
@@ -445,7 +477,7 @@ size_t bwd_tile_floats() { return BwdTiles::floats_per_batch(); }
 
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t s) {
   const BwdTiles w{};
-  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H * DSC)), dim3(256), 0, s, p, w);
+  launch_ds_scan(p, w, s);
   return hipGetLastError();
 }
 
@@ -487,7 +519,7 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     gemm(false, false, x, s);
   }
   // serial recurrence of dS over chunks
-  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(p.nseq * p.H * DSC)), dim3(256), 0, s, p, w);
+  launch_ds_scan(p, w, s);
   // chunk gradients
   {
     GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO

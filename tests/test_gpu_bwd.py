@@ -105,6 +105,16 @@ def test_bwd_value_split_plan():
     check_bwd(x, do, dsT)
 
 
+def test_bwd_many_pairs():
+    """64 (sequence, head) pairs: the state-gradient scan runs 32-column slices
+    (fewer pairs run 16-column slices, as every other case here does)."""
+    lengths = [70, 1, 130, 64, 0, 200, 33, 65, 128, 17, 90, 2, 150, 64, 40, 99]
+    announce(f"bwd varlen {len(lengths)} sequences H=4")
+    x = random_inputs(1, sum(lengths), 4, seed=82, device=DEV, init_state="fp32", lengths=lengths)
+    do, dsT = upstream(x, 83)
+    check_bwd(x, do, dsT)
+
+
 def test_bwd_no_tokens():
     """T = 0: the initial-state gradient is the final-state gradient."""
     x = random_inputs(2, 0, 2, seed=78, device=DEV, init_state="fp32")
