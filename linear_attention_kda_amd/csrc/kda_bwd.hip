@@ -71,56 +71,54 @@ __device__ __forceinline__ int slot_seq(const BwdParams& p, int64_t s) {
 // operands and accumulation): twice the rate of unpacked fp32 FMAs.  Each wave
 // owns a 32 x 32 quarter of the tile as 2 x 2 blocks; for step k of four, lane
 // (q4, m16) supplies op(A)[16i + m16][k] and op(B)[k][16j + m16] with k = 4s + q4,
-// and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.
+// and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.  Where an output
+// is a sum of two products, both accumulate in the same registers (bgemm2_kernel).
 typedef float bg_f32x4 __attribute__((ext_vector_type(4)));
 
+// k-major tiles; a row stride of 80 floats puts lane groups q4 and q4 + 1 on
+// disjoint banks for the operand reads
+struct BgTiles {
+  float A[16][80];
+  float B[16][80];
+};
+
+// acc += sign * op(A) op(B) over K for the 64 x 64 tile at (m0, n0); op(A)'s
+// k-th column is scaled by ks[k] when ks is given (sign is +-1: exact).
 template <bool TA, bool TB>
-__global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
-  // k-major tiles; a row stride of 80 floats puts lane groups q4 and q4 + 1 on
-  // disjoint banks for the operand reads
-  __shared__ float As[16][80];
-  __shared__ float Bs[16][80];
+__device__ __forceinline__ void bg_accumulate(bg_f32x4 (&acc)[2][2], BgTiles& sm, const float* A,
+                                              int lda, const float* B, int ldb, int K,
+                                              const float* ks, float sign, int m0, int n0) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
   const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  const float* A = a.A + b * a.sA;
-  const float* B = a.B + b * a.sB;
-  const float* ks = a.ks ? a.ks + b * a.sks : nullptr;
-  bg_f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.K; k0 += 16) {
+  for (int k0 = 0; k0 < K; k0 += 16) {
     if (!TA) {
       const int m = tid >> 2, k = (tid & 3) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(m0 + m) * a.lda + k0 + k);
+      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(m0 + m) * lda + k0 + k);
       const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) As[k + e][m] = ks ? vv[e] * ks[k0 + k + e] : vv[e];
+      for (int e = 0; e < 4; ++e) sm.A[k + e][m] = (ks ? vv[e] * ks[k0 + k + e] : vv[e]) * sign;
     } else {
       const int k = tid >> 4, m = (tid & 15) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(k0 + k) * a.lda + m0 + m);
-      const float s = ks ? ks[k0 + k] : 1.f;
-      *reinterpret_cast<float4*>(&As[k][m]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
+      const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(k0 + k) * lda + m0 + m);
+      const float s = (ks ? ks[k0 + k] : 1.f) * sign;
+      *reinterpret_cast<float4*>(&sm.A[k][m]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
     }
     if (!TB) {
       const int k = tid >> 4, n = (tid & 15) * 4;
-      *reinterpret_cast<float4*>(&Bs[k][n]) =
-          *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * a.ldb + n0 + n);
+      *reinterpret_cast<float4*>(&sm.B[k][n]) =
+          *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * ldb + n0 + n);
     } else {
       const int n = tid >> 2, k = (tid & 3) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * a.ldb + k0 + k);
-      Bs[k][n] = v.x; Bs[k + 1][n] = v.y; Bs[k + 2][n] = v.z; Bs[k + 3][n] = v.w;
+      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * ldb + k0 + k);
+      sm.B[k][n] = v.x; sm.B[k + 1][n] = v.y; sm.B[k + 2][n] = v.z; sm.B[k + 3][n] = v.w;
     }
     __syncthreads();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int k = 4 * s4 + q4;
-      const float a0 = As[k][wm + m16], a1 = As[k][wm + 16 + m16];
-      const float b0 = Bs[k][wn + m16], b1 = Bs[k][wn + 16 + m16];
+      const float a0 = sm.A[k][wm + m16], a1 = sm.A[k][wm + 16 + m16];
+      const float b0 = sm.B[k][wn + m16], b1 = sm.B[k][wn + 16 + m16];
       acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
@@ -128,6 +126,13 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
+}
+
+// C = rs (.) (alpha acc + D), masked, for the tile at (m0, n0) of batch b.
+__device__ __forceinline__ void bg_store(const bg_f32x4 (&acc)[2][2], const GemmArgs& a, int64_t b,
+                                         int m0, int n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m16 = lane & 15, q4 = lane >> 4;
+  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
   float* Cb = a.C + b * a.sC;
   const float* Db = a.Dm ? a.Dm + b * a.sD : nullptr;
   const float* rs = a.rs ? a.rs + b * a.srs : nullptr;
@@ -147,6 +152,50 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
         Cb[(int64_t)m * a.ldc + n] = v;
       }
     }
+}
+
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
+  __shared__ BgTiles sm;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  bg_f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_store(acc, a, b, m0, n0);
+}
+
+// A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
+// so that the first product never goes through memory.
+struct Gemm2Args {
+  GemmArgs a;                              // first product, output, row scale, mask
+  const float* A2; int64_t sA2; int lda2;
+  const float* B2; int64_t sB2; int ldb2;
+  int K2;
+  const float* ks2; int64_t sks2;
+  float sign2;                             // +-1
+};
+
+template <bool TA, bool TB, bool TA2, bool TB2>
+__global__ void __launch_bounds__(256) bgemm2_kernel(Gemm2Args g) {
+  __shared__ BgTiles sm;
+  const GemmArgs& a = g.a;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  bg_f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_accumulate<TA2, TB2>(acc, sm, g.A2 + b * g.sA2, g.lda2, g.B2 + b * g.sB2, g.ldb2, g.K2,
+                          g.ks2 ? g.ks2 + b * g.sks2 : nullptr, g.sign2, m0, n0);
+  bg_store(acc, a, b, m0, n0);
 }
 
 // ---------------------------------------------------------------- chunk prep
@@ -458,6 +507,20 @@ void gemm(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL((bgemm_kernel<true, true>), grid, block, 0, s, a);
 }
 
+// C = op(A) op(B) + sign2 op(A2) op(B2) with `first`'s output, row scale and mask;
+// `second` supplies A2, B2, K2 and the column scale of op(A2).
+template <bool TA, bool TB, bool TA2, bool TB2>
+void gemm2(const GemmArgs& first, const GemmArgs& second, float sign2, hipStream_t s) {
+  Gemm2Args g{};
+  g.a = first;
+  g.A2 = second.A; g.sA2 = second.sA; g.lda2 = second.lda;
+  g.B2 = second.B; g.sB2 = second.sB; g.ldb2 = second.ldb;
+  g.K2 = second.K; g.ks2 = second.ks; g.sks2 = second.sks;
+  g.sign2 = sign2;
+  const dim3 grid(first.N / 64, first.M / 64, first.batches), block(256);
+  hipLaunchKernelGGL((bgemm2_kernel<TA, TB, TA2, TB2>), grid, block, 0, s, g);
+}
+
 // op(A) M x K times op(B) K x N over every batch; strides are per-batch element counts.
 GemmArgs mm(int M, int N, int K, const float* A, int64_t sA, int lda, const float* B, int64_t sB,
             int ldb, float* Cm, int64_t sC, int ldc, int batches) {
@@ -513,10 +576,8 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     GemmArgs f = mm(D, C, C, w.kg, t1, D, w.T, t2, C, w.F, tf, C, NB);
     f.ks = w.beta; f.sks = C;
     gemm(true, true, f, s);
-    gemm(true, false, mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB), s);
-    GemmArgs x = mm(D, D, C, w.F, tf, C, w.MtdO, t1, D, w.X, t3, D, NB);
-    x.alpha = -1.f; x.Dm = w.X; x.sD = t3; x.ldd = D;
-    gemm(false, false, x, s);
+    gemm2<true, false, false, false>(mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB),
+                                     mm(D, D, C, w.F, tf, C, w.MtdO, t1, D, nullptr, 0, 0, NB), -1.f, s);
   }
   // serial recurrence of dS over chunks
   launch_ds_scan(p, w, s);
@@ -532,19 +593,17 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
     da.alpha = -1.f; da.mask = 1;
     gemm(false, true, da, s);
-    gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
-    GemmArgs q2 = mm(C, D, C, w.dM, t2, C, w.kh, t1, D, w.dqg, t1, D, NB);  // + dM kh
-    q2.Dm = w.dqg; q2.sD = t1; q2.ldd = D;
-    gemm(false, false, q2, s);
+    gemm2<false, true, false, false>(mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB),  // dO' S^T
+                                     mm(C, D, C, w.dM, t2, C, w.kh, t1, D, nullptr, 0, 0, NB),  // + dM kh
+                                     1.f, s);
     gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
-    gemm(false, false, mm(C, D, C, w.dA, t2, C, w.kh, t1, D, w.dkg, t1, D, NB), s);  // dA kh
-    GemmArgs k2 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // diag(b)(dA kh - dY S^T)
-    k2.alpha = -1.f; k2.Dm = w.dkg; k2.sD = t1; k2.ldd = D; k2.rs = w.beta; k2.srs = C;
-    gemm(false, true, k2, s);
-    gemm(true, false, mm(C, D, C, w.dM, t2, C, w.qg, t1, D, w.dkh, t1, D, NB), s);  // dM^T qg
-    GemmArgs h2 = mm(C, D, C, w.dA, t2, C, w.kg, t1, D, w.dkh, t1, D, NB);  // + dA^T diag(b) kg
-    h2.ks = w.beta; h2.sks = C; h2.Dm = w.dkh; h2.sD = t1; h2.ldd = D;
-    gemm(true, false, h2, s);
+    GemmArgs k1 = mm(C, D, C, w.dA, t2, C, w.kh, t1, D, w.dkg, t1, D, NB);  // diag(b)(dA kh - dY S^T)
+    k1.rs = w.beta; k1.srs = C;
+    gemm2<false, false, false, true>(k1, mm(C, D, D, w.dY, t1, D, w.S, t3, D, nullptr, 0, 0, NB), -1.f, s);
+    GemmArgs h2 = mm(C, D, C, w.dA, t2, C, w.kg, t1, D, nullptr, 0, 0, NB);  // + dA^T diag(b) kg
+    h2.ks = w.beta; h2.sks = C;
+    gemm2<true, false, true, false>(mm(C, D, C, w.dM, t2, C, w.qg, t1, D, w.dkh, t1, D, NB), h2,  // dM^T qg
+                                    1.f, s);
   }
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
   return hipGetLastError();
