@@ -169,6 +169,27 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   bg_store(acc, a, b, m0, n0);
 }
 
+// One product stored twice: to a.C with a's row scale, and to C2 with row scale
+// rs2 (or none); the mask and alpha are shared.
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256) bgemm_two_out_kernel(GemmArgs a, float* C2, const float* rs2,
+                                                             int64_t srs2) {
+  __shared__ BgTiles sm;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  bg_f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_store(acc, a, b, m0, n0);
+  GemmArgs a2 = a;
+  a2.C = C2; a2.rs = rs2; a2.srs = srs2;
+  bg_store(acc, a2, b, m0, n0);
+}
+
 // A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
 // so that the first product never goes through memory.
 struct Gemm2Args {
@@ -553,9 +574,8 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   {
     GemmArgs a = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
     a.mask = 1;
-    gemm(false, true, a, s);
-    a.C = w.A; a.rs = w.beta; a.srs = C;
-    gemm(false, true, a, s);
+    hipLaunchKernelGGL((bgemm_two_out_kernel<false, true>), dim3(a.N / 64, a.M / 64, a.batches),
+                       dim3(256), 0, s, a, w.A, w.beta, (int64_t)C);
     GemmArgs m = mm(C, C, D, w.qg, t1, D, w.kh, t1, D, w.M, t2, C, NB);
     m.mask = 2;
     gemm(false, true, m, s);
