@@ -64,33 +64,36 @@ __device__ __forceinline__ int slot_seq(const BwdParams& p, int64_t s) {
 // op(A) is M x K: A stored [m][k] (TA false) or [k][m] (TA true); its k-th column
 // is scaled by ks[b][k] when ks is given.  op(B) is K x N: B stored [k][n] (TB
 // false) or [n][k] (TB true).  rs scales output rows.  mask: 0 none, 1 keep
-// n < m, 2 keep n <= m.  One workgroup computes a 64 x 64 tile; M, N, K are
-// multiples of 64, 64 and 16.
+// n < m, 2 keep n <= m.  One workgroup computes a 64 x 64 or 64 x 128 tile; M, N,
+// K are multiples of 64, 64 and 16.
 //
 // The products run on the fp32 matrix cores (16 x 16 x 4 per instruction, fp32
 // operands and accumulation): twice the rate of unpacked fp32 FMAs.  Each wave
-// owns a 32 x 32 quarter of the tile as 2 x 2 blocks; for step k of four, lane
+// owns a quarter of the tile as 2 x (NT / 32) blocks; for step k of four, lane
 // (q4, m16) supplies op(A)[16i + m16][k] and op(B)[k][16j + m16] with k = 4s + q4,
 // and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.  Where an output
 // is a sum of two products, both accumulate in the same registers (bgemm2_kernel).
 typedef float bg_f32x4 __attribute__((ext_vector_type(4)));
 
-// k-major tiles; a row stride of 80 floats puts lane groups q4 and q4 + 1 on
-// disjoint banks for the operand reads
+// k-major tiles; a row stride of 16 mod 32 floats puts lane groups q4 and q4 + 1
+// on disjoint banks for the operand reads.  NT is the tile's width (64 or 128).
+template <int NT>
 struct BgTiles {
   float A[16][80];
-  float B[16][80];
+  float B[16][NT + 16];
 };
 
-// acc += sign * op(A) op(B) over K for the 64 x 64 tile at (m0, n0); op(A)'s
-// k-th column is scaled by ks[k] when ks is given (sign is +-1: exact).
-template <bool TA, bool TB>
-__device__ __forceinline__ void bg_accumulate(bg_f32x4 (&acc)[2][2], BgTiles& sm, const float* A,
-                                              int lda, const float* B, int ldb, int K,
-                                              const float* ks, float sign, int m0, int n0) {
+// acc += sign * op(A) op(B) over K for the 64 x NT tile at (m0, n0); op(A)'s
+// k-th column is scaled by ks[k] when ks is given (sign is +-1: exact).  Wave w
+// owns rows 32 (w / 2) .. +31 and columns (NT / 2)(w % 2) .. + NT / 2 - 1.
+template <int NT, bool TA, bool TB>
+__device__ __forceinline__ void bg_accumulate(bg_f32x4 (&acc)[2][NT / 32], BgTiles<NT>& sm,
+                                              const float* A, int lda, const float* B, int ldb,
+                                              int K, const float* ks, float sign, int m0, int n0) {
+  constexpr int JN = NT / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
-  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
+  const int wm = 32 * (wave >> 1), wn = (NT / 2) * (wave & 1);
   for (int k0 = 0; k0 < K; k0 += 16) {
     if (!TA) {
       const int m = tid >> 2, k = (tid & 3) * 4;
@@ -104,35 +107,40 @@ __device__ __forceinline__ void bg_accumulate(bg_f32x4 (&acc)[2][2], BgTiles& sm
       const float s = (ks ? ks[k0 + k] : 1.f) * sign;
       *reinterpret_cast<float4*>(&sm.A[k][m]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
     }
-    if (!TB) {
-      const int k = tid >> 4, n = (tid & 15) * 4;
-      *reinterpret_cast<float4*>(&sm.B[k][n]) =
-          *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * ldb + n0 + n);
-    } else {
-      const int n = tid >> 2, k = (tid & 3) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * ldb + k0 + k);
-      sm.B[k][n] = v.x; sm.B[k + 1][n] = v.y; sm.B[k + 2][n] = v.z; sm.B[k + 3][n] = v.w;
+#pragma unroll
+    for (int h = 0; h < NT / 64; ++h) {
+      if (!TB) {
+        const int k = tid >> 4, n = 64 * h + (tid & 15) * 4;
+        *reinterpret_cast<float4*>(&sm.B[k][n]) =
+            *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * ldb + n0 + n);
+      } else {
+        const int n = 64 * h + (tid >> 2), k = (tid & 3) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * ldb + k0 + k);
+        sm.B[k][n] = v.x; sm.B[k + 1][n] = v.y; sm.B[k + 2][n] = v.z; sm.B[k + 3][n] = v.w;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int k = 4 * s4 + q4;
       const float a0 = sm.A[k][wm + m16], a1 = sm.A[k][wm + 16 + m16];
-      const float b0 = sm.B[k][wn + m16], b1 = sm.B[k][wn + 16 + m16];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        const float bj = sm.B[k][wn + 16 * j + m16];
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bj, acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bj, acc[1][j], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
 }
 
 // C = rs (.) (alpha acc + D), masked, for the tile at (m0, n0) of batch b.
-__device__ __forceinline__ void bg_store(const bg_f32x4 (&acc)[2][2], const GemmArgs& a, int64_t b,
-                                         int m0, int n0) {
+template <int NT>
+__device__ __forceinline__ void bg_store(const bg_f32x4 (&acc)[2][NT / 32], const GemmArgs& a,
+                                         int64_t b, int m0, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m16 = lane & 15, q4 = lane >> 4;
-  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
+  const int wm = 32 * (wave >> 1), wn = (NT / 2) * (wave & 1);
   float* Cb = a.C + b * a.sC;
   const float* Db = a.Dm ? a.Dm + b * a.sD : nullptr;
   const float* rs = a.rs ? a.rs + b * a.srs : nullptr;
@@ -143,7 +151,7 @@ __device__ __forceinline__ void bg_store(const bg_f32x4 (&acc)[2][2], const Gemm
       const int m = m0 + wm + 16 * i + 4 * q4 + t;
       const float r = rs ? rs[m] : 1.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NT / 32; ++j) {
         const int n = n0 + wn + 16 * j + m16;
         float v = a.alpha * acc[i][j][t];
         if (Db) v += Db[(int64_t)m * a.ldd + n];
@@ -154,40 +162,42 @@ __device__ __forceinline__ void bg_store(const bg_f32x4 (&acc)[2][2], const Gemm
     }
 }
 
-template <bool TA, bool TB>
-__global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
-  __shared__ BgTiles sm;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  bg_f32x4 acc[2][2];
+template <int NT>
+__device__ __forceinline__ void bg_zero(bg_f32x4 (&acc)[2][NT / 32]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
-  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
-                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_store(acc, a, b, m0, n0);
+    for (int j = 0; j < NT / 32; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int NT, bool TA, bool TB>
+__global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
+  __shared__ BgTiles<NT> sm;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  bg_f32x4 acc[2][NT / 32];
+  bg_zero<NT>(acc);
+  bg_accumulate<NT, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                            a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_store<NT>(acc, a, b, m0, n0);
 }
 
 // One product stored twice: to a.C with a's row scale, and to C2 with row scale
-// rs2 (or none); the mask and alpha are shared.
+// rs2 (or none); the mask and alpha are shared.  64-wide tiles.
 template <bool TA, bool TB>
 __global__ void __launch_bounds__(256) bgemm_two_out_kernel(GemmArgs a, float* C2, const float* rs2,
                                                              int64_t srs2) {
-  __shared__ BgTiles sm;
+  __shared__ BgTiles<64> sm;
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
   const int64_t b = blockIdx.z;
   bg_f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
-  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
-                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_store(acc, a, b, m0, n0);
+  bg_zero<64>(acc);
+  bg_accumulate<64, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                            a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_store<64>(acc, a, b, m0, n0);
   GemmArgs a2 = a;
   a2.C = C2; a2.rs = rs2; a2.srs = srs2;
-  bg_store(acc, a2, b, m0, n0);
+  bg_store<64>(acc, a2, b, m0, n0);
 }
 
 // A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
@@ -201,22 +211,19 @@ struct Gemm2Args {
   float sign2;                             // +-1
 };
 
-template <bool TA, bool TB, bool TA2, bool TB2>
+template <int NT, bool TA, bool TB, bool TA2, bool TB2>
 __global__ void __launch_bounds__(256) bgemm2_kernel(Gemm2Args g) {
-  __shared__ BgTiles sm;
+  __shared__ BgTiles<NT> sm;
   const GemmArgs& a = g.a;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * NT, m0 = blockIdx.y * 64;
   const int64_t b = blockIdx.z;
-  bg_f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = bg_f32x4{0.f, 0.f, 0.f, 0.f};
-  bg_accumulate<TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
-                        a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_accumulate<TA2, TB2>(acc, sm, g.A2 + b * g.sA2, g.lda2, g.B2 + b * g.sB2, g.ldb2, g.K2,
-                          g.ks2 ? g.ks2 + b * g.sks2 : nullptr, g.sign2, m0, n0);
-  bg_store(acc, a, b, m0, n0);
+  bg_f32x4 acc[2][NT / 32];
+  bg_zero<NT>(acc);
+  bg_accumulate<NT, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
+                            a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
+  bg_accumulate<NT, TA2, TB2>(acc, sm, g.A2 + b * g.sA2, g.lda2, g.B2 + b * g.sB2, g.ldb2, g.K2,
+                              g.ks2 ? g.ks2 + b * g.sks2 : nullptr, g.sign2, m0, n0);
+  bg_store<NT>(acc, a, b, m0, n0);
 }
 
 // ---------------------------------------------------------------- chunk prep
@@ -520,12 +527,19 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
   if (t < valid) p.dbeta[(bos + c * C + t) * p.H + h] = dbs[t];
 }
 
+template <int NT>
+void gemm_nt(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(a.N / NT, a.M / 64, a.batches), block(256);
+  if (!ta && !tb) hipLaunchKernelGGL((bgemm_kernel<NT, false, false>), grid, block, 0, s, a);
+  else if (!ta && tb) hipLaunchKernelGGL((bgemm_kernel<NT, false, true>), grid, block, 0, s, a);
+  else if (ta && !tb) hipLaunchKernelGGL((bgemm_kernel<NT, true, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bgemm_kernel<NT, true, true>), grid, block, 0, s, a);
+}
+
+// 64 x 128 tiles where N allows (op(A) is then read once per row block), else 64 x 64.
 void gemm(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(a.N / 64, a.M / 64, a.batches), block(256);
-  if (!ta && !tb) hipLaunchKernelGGL((bgemm_kernel<false, false>), grid, block, 0, s, a);
-  else if (!ta && tb) hipLaunchKernelGGL((bgemm_kernel<false, true>), grid, block, 0, s, a);
-  else if (ta && !tb) hipLaunchKernelGGL((bgemm_kernel<true, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((bgemm_kernel<true, true>), grid, block, 0, s, a);
+  if (a.N % 128 == 0) gemm_nt<128>(ta, tb, a, s);
+  else gemm_nt<64>(ta, tb, a, s);
 }
 
 // C = op(A) op(B) + sign2 op(A2) op(B2) with `first`'s output, row scale and mask;
@@ -538,8 +552,12 @@ void gemm2(const GemmArgs& first, const GemmArgs& second, float sign2, hipStream
   g.B2 = second.B; g.sB2 = second.sB; g.ldb2 = second.ldb;
   g.K2 = second.K; g.ks2 = second.ks; g.sks2 = second.sks;
   g.sign2 = sign2;
-  const dim3 grid(first.N / 64, first.M / 64, first.batches), block(256);
-  hipLaunchKernelGGL((bgemm2_kernel<TA, TB, TA2, TB2>), grid, block, 0, s, g);
+  if (first.N % 128 == 0)
+    hipLaunchKernelGGL((bgemm2_kernel<128, TA, TB, TA2, TB2>), dim3(first.N / 128, first.M / 64, first.batches),
+                       dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((bgemm2_kernel<64, TA, TB, TA2, TB2>), dim3(first.N / 64, first.M / 64, first.batches),
+                       dim3(256), 0, s, g);
 }
 
 // op(A) M x K times op(B) K x N over every batch; strides are per-batch element counts.
