@@ -281,8 +281,6 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) 
     w.kp[o] = kf * ei * gam;
     w.vv[o] = vf;
     w.dO[o] = df;
-    w.kk[o] = kf;
-    w.qq[o] = qf;
   }
 }
 
@@ -457,12 +455,14 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
     const float e = expf(G), ei = expf(-G);
     const float gam = w.gam[bidx * D + ch];
     const float dqg = w.dqg[o], dkg = w.dkg[o], dkh = w.dkh[o], dkp = w.dkp[o];
-    const float kf = w.kk[o], qf = w.qq[o];
+    // k and q straight from the inputs (exact in fp32; zero past the sequence's end)
+    const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
+    const float kf = r < valid ? bf2f_u16(p.k[row]) : 0.f;
+    const float qf = r < valid ? bf2f_u16(p.q[row]) : 0.f;
     const float kp = kf * ei * gam;
     dGs[r][ch] = dqg * qf * e + dkg * kf * e - dkh * kf * ei - dkp * kp;
     glast += dkp * kp;
     if (r < valid) {
-      const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
       p.dq[row] = dqg * e;
       p.dk[row] = dkg * e + dkh * ei + dkp * gam * ei;
       p.dv[row] = beta[r] * w.dY[o];

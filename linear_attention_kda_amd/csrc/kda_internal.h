@@ -109,7 +109,7 @@ struct BwdParams {
 // Per-chunk fp32 tiles of the backward, each an array over batches b = slot * H + h.
 struct BwdTiles {
   // [b][64][128]
-  float *G, *kg, *qg, *kh, *kp, *vv, *dO, *kk, *qq, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkh, *dkp;
+  float *G, *kg, *qg, *kh, *kp, *vv, *dO, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkh, *dkp;
   float *A, *P, *M, *T, *dM, *dA;   // [b][64][64]
   float* F;                          // [b][128][64]
   float *S, *X, *dSn;                // [b][128][128]; S: chunk start states (the checkpoints)
@@ -117,7 +117,7 @@ struct BwdTiles {
   float* gam;                        // [b][128]
   int* valid;                        // [b]
   static constexpr size_t floats_per_batch() {
-    return 18 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 128 + 1;
+    return 16 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 128 + 1;
   }
 };
 
