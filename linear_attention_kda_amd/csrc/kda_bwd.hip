@@ -182,22 +182,58 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   bg_store<NT>(acc, a, b, m0, n0);
 }
 
-// One product stored twice: to a.C with a's row scale, and to C2 with row scale
-// rs2 (or none); the mask and alpha are shared.  64-wide tiles.
-template <bool TA, bool TB>
-__global__ void __launch_bounds__(256) bgemm_two_out_kernel(GemmArgs a, float* C2, const float* rs2,
-                                                             int64_t srs2) {
-  __shared__ BgTiles<64> sm;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+// The three products of kh^T in one pass, with kh staged once: P = strict_lower(kg kh^T),
+// A = diag(beta) P (from the same accumulators) and M = lower_incl(qg kh^T).  The
+// 64 x 64 x 128 products use 64-wide tiles; `a` carries kg, kh and P.
+__global__ void __launch_bounds__(256) bgemm_pam_kernel(GemmArgs a, const float* qg, float* Aout,
+                                                        float* Mout, const float* beta) {
+  __shared__ float Bk[16][80];   // kh^T slice, [k][n]
+  __shared__ float Ak[16][80];   // kg^T slice, [k][m]
+  __shared__ float Aq[16][80];   // qg^T slice, [k][m]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
+  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
   const int64_t b = blockIdx.z;
-  bg_f32x4 acc[2][2];
-  bg_zero<64>(acc);
-  bg_accumulate<64, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
-                            a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_store<64>(acc, a, b, m0, n0);
-  GemmArgs a2 = a;
-  a2.C = C2; a2.rs = rs2; a2.srs = srs2;
-  bg_store<64>(acc, a2, b, m0, n0);
+  const float* kg = a.A + b * a.sA;
+  const float* kh = a.B + b * a.sB;
+  const float* qb = qg + b * a.sA;
+  bg_f32x4 accP[2][2], accM[2][2];
+  bg_zero<64>(accP);
+  bg_zero<64>(accM);
+  for (int k0 = 0; k0 < a.K; k0 += 16) {
+    // rows tid / 4 of kg, qg and kh, four consecutive k each
+    const int r = tid >> 2, k = (tid & 3) * 4;
+    const float4 vk = *reinterpret_cast<const float4*>(kg + (int64_t)r * a.lda + k0 + k);
+    const float4 vq = *reinterpret_cast<const float4*>(qb + (int64_t)r * a.lda + k0 + k);
+    const float4 vh = *reinterpret_cast<const float4*>(kh + (int64_t)r * a.ldb + k0 + k);
+    Ak[k][r] = vk.x; Ak[k + 1][r] = vk.y; Ak[k + 2][r] = vk.z; Ak[k + 3][r] = vk.w;
+    Aq[k][r] = vq.x; Aq[k + 1][r] = vq.y; Aq[k + 2][r] = vq.z; Aq[k + 3][r] = vq.w;
+    Bk[k][r] = vh.x; Bk[k + 1][r] = vh.y; Bk[k + 2][r] = vh.z; Bk[k + 3][r] = vh.w;
+    __syncthreads();
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int kk = 4 * s4 + q4;
+      const float b0 = Bk[kk][wn + m16], b1 = Bk[kk][wn + 16 + m16];
+      const float k0v = Ak[kk][wm + m16], k1v = Ak[kk][wm + 16 + m16];
+      const float q0v = Aq[kk][wm + m16], q1v = Aq[kk][wm + 16 + m16];
+      accP[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0v, b0, accP[0][0], 0, 0, 0);
+      accP[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0v, b1, accP[0][1], 0, 0, 0);
+      accP[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1v, b0, accP[1][0], 0, 0, 0);
+      accP[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1v, b1, accP[1][1], 0, 0, 0);
+      accM[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(q0v, b0, accM[0][0], 0, 0, 0);
+      accM[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(q0v, b1, accM[0][1], 0, 0, 0);
+      accM[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(q1v, b0, accM[1][0], 0, 0, 0);
+      accM[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(q1v, b1, accM[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  GemmArgs o = a;                  // P: strict lower
+  o.mask = 1; o.rs = nullptr;
+  bg_store<64>(accP, o, b, 0, 0);
+  o.C = Aout; o.rs = beta; o.srs = 64;   // A = diag(beta) P
+  bg_store<64>(accP, o, b, 0, 0);
+  o.C = Mout; o.rs = nullptr; o.mask = 2; // M: lower, diagonal included
+  bg_store<64>(accM, o, b, 0, 0);
 }
 
 // A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
@@ -590,13 +626,8 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(NB), dim3(256), 0, s, p, w);
   // A = strict_lower(diag(b) kg kh^T), P = strict_lower(kg kh^T), M = lower_incl(qg kh^T)
   {
-    GemmArgs a = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
-    a.mask = 1;
-    hipLaunchKernelGGL((bgemm_two_out_kernel<false, true>), dim3(a.N / 64, a.M / 64, a.batches),
-                       dim3(256), 0, s, a, w.A, w.beta, (int64_t)C);
-    GemmArgs m = mm(C, C, D, w.qg, t1, D, w.kh, t1, D, w.M, t2, C, NB);
-    m.mask = 2;
-    gemm(false, true, m, s);
+    const GemmArgs a = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
+    hipLaunchKernelGGL(bgemm_pam_kernel, dim3(1, 1, NB), dim3(256), 0, s, a, w.qg, w.A, w.M, w.beta);
   }
   hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
   // R = V - kg S;  U = T diag(b) R
