@@ -182,58 +182,57 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   bg_store<NT>(acc, a, b, m0, n0);
 }
 
-// The three products of kh^T in one pass, with kh staged once: P = strict_lower(kg kh^T),
-// A = diag(beta) P (from the same accumulators) and M = lower_incl(qg kh^T).  The
-// 64 x 64 x 128 products use 64-wide tiles; `a` carries kg, kh and P.
-__global__ void __launch_bounds__(256) bgemm_pam_kernel(GemmArgs a, const float* qg, float* Aout,
-                                                        float* Mout, const float* beta) {
-  __shared__ float Bk[16][80];   // kh^T slice, [k][n]
-  __shared__ float Ak[16][80];   // kg^T slice, [k][m]
-  __shared__ float Aq[16][80];   // qg^T slice, [k][m]
+// Two 64 x 64 products that share their right operand, X1 B^T and X2 B^T, with B
+// staged once (all three stored [64][K]).  `o1` carries X1, B and the first output
+// (mask, alpha, row scale); `o1b`, if its C is set, stores the same accumulators a
+// second time with its own mask, alpha and row scale; `o2` carries X2 in A and the
+// second output.  Used for P = strict_lower(kg kh^T) with A = diag(beta) P and
+// M = lower_incl(qg kh^T), and for dM = lower_incl(dO' U^T) with
+// dA = strict_lower(-dY U^T).
+__global__ void __launch_bounds__(256) bgemm_shared_b_kernel(GemmArgs o1, GemmArgs o1b, GemmArgs o2) {
+  __shared__ float Bs[16][80];   // B^T slice, [k][n]
+  __shared__ float X1s[16][80];  // X1^T slice, [k][m]
+  __shared__ float X2s[16][80];  // X2^T slice, [k][m]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
   const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
   const int64_t b = blockIdx.z;
-  const float* kg = a.A + b * a.sA;
-  const float* kh = a.B + b * a.sB;
-  const float* qb = qg + b * a.sA;
-  bg_f32x4 accP[2][2], accM[2][2];
-  bg_zero<64>(accP);
-  bg_zero<64>(accM);
-  for (int k0 = 0; k0 < a.K; k0 += 16) {
-    // rows tid / 4 of kg, qg and kh, four consecutive k each
+  const float* x1 = o1.A + b * o1.sA;
+  const float* bm = o1.B + b * o1.sB;
+  const float* x2 = o2.A + b * o2.sA;
+  bg_f32x4 acc1[2][2], acc2[2][2];
+  bg_zero<64>(acc1);
+  bg_zero<64>(acc2);
+  for (int k0 = 0; k0 < o1.K; k0 += 16) {
+    // rows tid / 4 of X1, X2 and B, four consecutive k each
     const int r = tid >> 2, k = (tid & 3) * 4;
-    const float4 vk = *reinterpret_cast<const float4*>(kg + (int64_t)r * a.lda + k0 + k);
-    const float4 vq = *reinterpret_cast<const float4*>(qb + (int64_t)r * a.lda + k0 + k);
-    const float4 vh = *reinterpret_cast<const float4*>(kh + (int64_t)r * a.ldb + k0 + k);
-    Ak[k][r] = vk.x; Ak[k + 1][r] = vk.y; Ak[k + 2][r] = vk.z; Ak[k + 3][r] = vk.w;
-    Aq[k][r] = vq.x; Aq[k + 1][r] = vq.y; Aq[k + 2][r] = vq.z; Aq[k + 3][r] = vq.w;
-    Bk[k][r] = vh.x; Bk[k + 1][r] = vh.y; Bk[k + 2][r] = vh.z; Bk[k + 3][r] = vh.w;
+    const float4 v1 = *reinterpret_cast<const float4*>(x1 + (int64_t)r * o1.lda + k0 + k);
+    const float4 v2 = *reinterpret_cast<const float4*>(x2 + (int64_t)r * o2.lda + k0 + k);
+    const float4 vb = *reinterpret_cast<const float4*>(bm + (int64_t)r * o1.ldb + k0 + k);
+    X1s[k][r] = v1.x; X1s[k + 1][r] = v1.y; X1s[k + 2][r] = v1.z; X1s[k + 3][r] = v1.w;
+    X2s[k][r] = v2.x; X2s[k + 1][r] = v2.y; X2s[k + 2][r] = v2.z; X2s[k + 3][r] = v2.w;
+    Bs[k][r] = vb.x; Bs[k + 1][r] = vb.y; Bs[k + 2][r] = vb.z; Bs[k + 3][r] = vb.w;
     __syncthreads();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int kk = 4 * s4 + q4;
-      const float b0 = Bk[kk][wn + m16], b1 = Bk[kk][wn + 16 + m16];
-      const float k0v = Ak[kk][wm + m16], k1v = Ak[kk][wm + 16 + m16];
-      const float q0v = Aq[kk][wm + m16], q1v = Aq[kk][wm + 16 + m16];
-      accP[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0v, b0, accP[0][0], 0, 0, 0);
-      accP[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(k0v, b1, accP[0][1], 0, 0, 0);
-      accP[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1v, b0, accP[1][0], 0, 0, 0);
-      accP[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(k1v, b1, accP[1][1], 0, 0, 0);
-      accM[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(q0v, b0, accM[0][0], 0, 0, 0);
-      accM[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(q0v, b1, accM[0][1], 0, 0, 0);
-      accM[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(q1v, b0, accM[1][0], 0, 0, 0);
-      accM[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(q1v, b1, accM[1][1], 0, 0, 0);
+      const float b0 = Bs[kk][wn + m16], b1 = Bs[kk][wn + 16 + m16];
+      const float a0 = X1s[kk][wm + m16], a1 = X1s[kk][wm + 16 + m16];
+      const float c0 = X2s[kk][wm + m16], c1 = X2s[kk][wm + 16 + m16];
+      acc1[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc1[0][0], 0, 0, 0);
+      acc1[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc1[0][1], 0, 0, 0);
+      acc1[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc1[1][0], 0, 0, 0);
+      acc1[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc1[1][1], 0, 0, 0);
+      acc2[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(c0, b0, acc2[0][0], 0, 0, 0);
+      acc2[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(c0, b1, acc2[0][1], 0, 0, 0);
+      acc2[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(c1, b0, acc2[1][0], 0, 0, 0);
+      acc2[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(c1, b1, acc2[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
-  GemmArgs o = a;                  // P: strict lower
-  o.mask = 1; o.rs = nullptr;
-  bg_store<64>(accP, o, b, 0, 0);
-  o.C = Aout; o.rs = beta; o.srs = 64;   // A = diag(beta) P
-  bg_store<64>(accP, o, b, 0, 0);
-  o.C = Mout; o.rs = nullptr; o.mask = 2; // M: lower, diagonal included
-  bg_store<64>(accM, o, b, 0, 0);
+  bg_store<64>(acc1, o1, b, 0, 0);
+  if (o1b.C) bg_store<64>(acc1, o1b, b, 0, 0);
+  bg_store<64>(acc2, o2, b, 0, 0);
 }
 
 // A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
@@ -626,8 +625,13 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(NB), dim3(256), 0, s, p, w);
   // A = strict_lower(diag(b) kg kh^T), P = strict_lower(kg kh^T), M = lower_incl(qg kh^T)
   {
-    const GemmArgs a = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
-    hipLaunchKernelGGL(bgemm_pam_kernel, dim3(1, 1, NB), dim3(256), 0, s, a, w.qg, w.A, w.M, w.beta);
+    GemmArgs p1 = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
+    p1.mask = 1;
+    GemmArgs a1 = p1;
+    a1.C = w.A; a1.rs = w.beta; a1.srs = C;
+    GemmArgs m2 = mm(C, C, D, w.qg, t1, D, w.kh, t1, D, w.M, t2, C, NB);
+    m2.mask = 2;
+    hipLaunchKernelGGL(bgemm_shared_b_kernel, dim3(1, 1, NB), dim3(256), 0, s, p1, a1, m2);
   }
   hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
   // R = V - kg S;  U = T diag(b) R
@@ -655,13 +659,15 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
     du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
     gemm(false, false, du, s);
-    GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
-    dm.mask = 2;
-    gemm(false, true, dm, s);
     gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
-    GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
-    da.alpha = -1.f; da.mask = 1;
-    gemm(false, true, da, s);
+    {
+      GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
+      dm.mask = 2;
+      GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
+      da.alpha = -1.f; da.mask = 1;
+      GemmArgs none{};
+      hipLaunchKernelGGL(bgemm_shared_b_kernel, dim3(1, 1, NB), dim3(256), 0, s, dm, none, da);
+    }
     gemm2<false, true, false, false>(mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB),  // dO' S^T
                                      mm(C, D, C, w.dM, t2, C, w.kh, t1, D, nullptr, 0, 0, NB),  // + dM kh
                                      1.f, s);
