@@ -9,6 +9,10 @@ reported under "secondary".  Prints one JSON line on stdout; progress goes to
 stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+
+Also timed, each with its own roofline: the 4 x 32K continuation workload
+(fp32 states) and the T = 1M long-context workload (under "other_workloads";
+the latter's oracle runs on 4 heads, "cpu_baseline_long_context").
 """
 from __future__ import annotations
 
@@ -47,7 +51,12 @@ def state_bytes_of(dtype_name):
     return {None: 0, "bf16": 2, "fp32": 4}[dtype_name]
 
 
-def time_workload(wid: int, steps: int, warmup: int):
+def time_workload(wid: int, steps: int, warmup: int, copies: int = 1):
+    """Time `steps` kda_fwd calls on workload `wid` after `warmup` untimed ones.
+
+    With copies > 1 the calls rotate over that many copies of the inputs and
+    outputs, so that a working set smaller than the 256 MB Infinity Cache is
+    not served from it on the next call."""
     import torch
 
     from linear_attention_kda_amd import binding, perfmodel
@@ -58,17 +67,21 @@ def time_workload(wid: int, steps: int, warmup: int):
     dev = x["q"].device
     N, H = w.num_states, w.H
     sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
-    final = torch.empty(N, H, 128, 128, dtype=sdt[w.final_state], device=dev) \
-        if w.final_state else None
-    out = torch.empty_like(x["v"])
+    sets = []
+    for c in range(copies):
+        xi = x if c == 0 else {k: (v.clone() if torch.is_tensor(v) else v) for k, v in x.items()}
+        final = torch.empty(N, H, 128, 128, dtype=sdt[w.final_state], device=dev) \
+            if w.final_state else None
+        sets.append((xi, final, torch.empty_like(x["v"])))
 
-    def step():
-        binding.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
-                    initial_state=x["initial_state"], final_state=final,
-                    cu_seqlens=x["cu_seqlens"], out=out)
+    def step(i):
+        xi, final, out = sets[i % copies]
+        binding.fwd(xi["q"], xi["k"], xi["v"], xi["g"], xi["beta"], xi["scale"],
+                    initial_state=xi["initial_state"], final_state=final,
+                    cu_seqlens=xi["cu_seqlens"], out=out)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -78,7 +91,7 @@ def time_workload(wid: int, steps: int, warmup: int):
     t0.record()
     for i in range(steps):
         starts[i].record()
-        step()
+        step(i)
         ends[i].record()
     t1.record()
     torch.cuda.synchronize()
@@ -94,17 +107,43 @@ def time_workload(wid: int, steps: int, warmup: int):
         workload=w, tokens=tokens, N=N, H=H, total_ms=total_ms, wall_s=wall,
         ms_per_step=total_ms / steps, kernel_ms=kernel_ms,
         kernel_ms_median=statistics.median(launch_ms), kernel_ms_min=min(launch_ms),
+        kernel_ms_max=max(launch_ms),
         tokens_per_s=tokens * steps / (total_ms * 1e-3),
         bytes_per_launch=nbytes, flops_per_launch=flops,
         achieved_gbs=nbytes / (kernel_ms * 1e-3) / 1e9,
         achieved_tflops=flops / (kernel_ms * 1e-3) / 1e12,
-        lengths=x["lengths"],
+        lengths=x["lengths"], copies=copies,
     )
     res["hbm_frac"] = res["achieved_gbs"] / perfmodel.HBM_PEAK_GBS
     res["mfma_frac"] = res["achieved_tflops"] / perfmodel.BF16_PEAK_TFLOPS
-    host = None
-    del out, final
-    return res, x, host
+    del sets
+    return res, x, None
+
+
+def workload_line(r):
+    """The JSON object of a timed workload other than the headline one."""
+    from linear_attention_kda_amd import perfmodel
+    w = r["workload"]
+    return {"workload": w.name, "value": r["tokens_per_s"], "unit": "tokens/s",
+            "ms_per_step": r["ms_per_step"], "kernel_ms": r["kernel_ms"],
+            "kernel_ms_range": [r["kernel_ms_min"], r["kernel_ms_max"]],
+            "input_copies": r["copies"], "state_dtype": w.final_state,
+            "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"],
+                         "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r["hbm_frac"], "traffic": None,
+                         "algorithmic_bytes": r["bytes_per_launch"]},
+            "mfma_frac": r["mfma_frac"]}
+
+
+def input_copies(wid: int) -> int:
+    """Two input copies when one set would fit twice in the 256 MB Infinity Cache's reach
+    (the T = 8K workload's 406 MB), one otherwise."""
+    from linear_attention_kda_amd import perfmodel
+    from linear_attention_kda_amd.workloads import WORKLOADS
+    w = WORKLOADS[wid]
+    nbytes = perfmodel.workload_bytes(w.tokens, w.H, w.num_states, state_bytes_of(w.init_state),
+                                      state_bytes_of(w.final_state))
+    return 2 if nbytes < (1 << 30) else 1
 
 
 def measured_traffic(wid: int):
@@ -119,10 +158,8 @@ def measured_traffic(wid: int):
     return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
 
 
-def cpu_baseline(x, heads: int, min_seconds: float = 10.0):
+def cpu_baseline(x, heads: int, min_seconds: float = 10.0, max_passes: int = 1 << 30):
     """The fp64 oracle, as it stands, on `heads` heads of the same workload."""
-    import numpy as np  # noqa: F401
-
     from oracle import oracle
     w = x["workload"]
     hs = list(range(min(heads, w.H)))
@@ -136,16 +173,21 @@ def cpu_baseline(x, heads: int, min_seconds: float = 10.0):
     tasks = w.num_states * len(hs) * (128 // col_block)
     # Whole passes over the sample until at least min_seconds of CPU work.
     passes, dt = 0, 0.0
-    while passes == 0 or dt < min_seconds:
+    while passes == 0 or (dt < min_seconds and passes < max_passes):
         t0 = time.perf_counter()
         oracle.fwd(*args, x["scale"], s0, cu_seqlens=cu, col_block=col_block)
         dt += time.perf_counter() - t0
         passes += 1
-    tokens_equiv = passes * w.tokens * len(hs) / w.H  # all-head-equivalent tokens
-    return dict(value=tokens_equiv / dt, unit="tokens/s", cores=min(threads, tasks),
-                kind="oracle",
-                sample=(f"{w.name}: {passes} pass(es) over all {w.tokens} tokens of "
-                        f"{len(hs)} of {w.H} heads ({dt:.1f} s); value scaled to all heads"))
+    head_tokens = passes * w.tokens * len(hs)
+    tokens_equiv = head_tokens / w.H  # all-head-equivalent tokens
+    res = dict(value=tokens_equiv / dt, unit="tokens/s", cores=min(threads, tasks),
+               nproc=os.cpu_count(), kind="oracle",
+               sample=(f"{w.name}: {passes} pass(es) over all {w.tokens} tokens of "
+                       f"{len(hs)} of {w.H} heads ({dt:.1f} s); value scaled to all heads"))
+    if len(hs) < w.H:
+        res["head_tokens_per_s"] = head_tokens / dt
+        res["heads_run"] = len(hs)
+    return res
 
 
 def decode_bench(steps: int, warmup: int, N: int = 256, H: int = 32, d: int = 128):
@@ -325,15 +367,18 @@ def bwd_bench(wid: int, steps: int, warmup: int):
                          "kernel": "kda_bwd call", "algorithmic_bytes": nbytes}}
 
 
-def counter_run(wid: int):
-    """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes.
+def counter_run(wid: int, target: str = "fwd"):
+    """Launch sequence profiled by the hardware-counter passes.
 
-    The copy moves exactly 1 GiB in each direction, so its counter readings
-    give the factor that turns a counter reading into bytes."""
+    The copy moves exactly 1 GiB in each direction, so its FETCH_SIZE /
+    WRITE_SIZE readings give the factor that turns a counter reading into
+    bytes.  Then two launches of `target` on workload `wid`: the d = 128
+    forward (fwd), the scalar-gate forward (gdn), the forward at head
+    dimension 64 or 256 (dim64, dim256) or the backward (bwd)."""
     import torch
 
     from linear_attention_kda_amd import binding
-    from linear_attention_kda_amd.workloads import make_inputs
+    from linear_attention_kda_amd.workloads import WORKLOADS, make_inputs, random_inputs, varlen_lengths
 
     a = torch.rand(1 << 28, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -341,18 +386,41 @@ def counter_run(wid: int):
         b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    x = make_inputs(wid, "cuda")
-    w = x["workload"]
     sdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
-    final = torch.empty(w.num_states, w.H, 128, 128, dtype=sdt[w.final_state],
+    if target in ("dim64", "dim256"):
+        d = int(target[3:])
+        w = WORKLOADS[wid]
+        lengths = None
+        if w.n_seqs:
+            gen = torch.Generator(device="cpu")
+            gen.manual_seed(w.seed)
+            lengths = varlen_lengths(w.n_seqs, w.T, gen)
+        x = random_inputs(w.B, w.T, w.H, d, d, seed=w.seed + 7919 + d, device="cuda",
+                          g_lo=w.g_lo, g_hi=w.g_hi, init_state=w.init_state, lengths=lengths)
+    else:
+        d = 128
+        x = make_inputs(wid, "cuda")
+        w = x["workload"]
+    final = torch.empty(w.num_states, w.H, d, d, dtype=sdt[w.final_state],
                         device="cuda") if w.final_state else None
     out = torch.empty_like(x["v"])
+    gs = x["g"][..., 0].contiguous() if target == "gdn" else None
+    do = None
+    if target == "bwd":
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(1400 + wid)
+        do = torch.randn(x["v"].shape, generator=gen, device="cuda").to(torch.bfloat16)
     for _ in range(2):
-        binding.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["scale"],
-                    initial_state=x["initial_state"], final_state=final,
-                    cu_seqlens=x["cu_seqlens"], out=out)
+        if target == "bwd":
+            binding.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["scale"],
+                        initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"])
+        else:
+            fn = binding.gdn_fwd if target == "gdn" else binding.fwd
+            fn(x["q"], x["k"], x["v"], gs if target == "gdn" else x["g"], x["beta"], x["scale"],
+               initial_state=x["initial_state"], final_state=final,
+               cu_seqlens=x["cu_seqlens"], out=out)
     torch.cuda.synchronize()
-    log(f"[bench] counter run done: 2 copies of 1 GiB, 2 launches of {w.name}")
+    log(f"[bench] counter run done: 2 copies of 1 GiB, 2 launches of {target} on {w.name}")
 
 
 def main():
@@ -369,7 +437,12 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward line")
     ap.add_argument("--no-dims", action="store_true", help="skip the head dim 64 / 256 lines")
     ap.add_argument("--bwd-workload", type=int, default=1)
+    ap.add_argument("--also", type=int, nargs="*", default=[3, 4],
+                    help="further workloads timed with their own lines (default: 3 4)")
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--counter-target", default="fwd",
+                    choices=["fwd", "gdn", "dim64", "dim256", "bwd"],
+                    help="what --counters launches (on --workload)")
     ap.add_argument("--counters", action="store_true",
                     help="untimed run for hardware-counter passes: a 1 GiB device copy "
                          "(the calibration kernel) twice, then two launches of the workload")
@@ -390,7 +463,7 @@ def main():
     binding.load_library()
 
     if args.counters:
-        counter_run(args.workload)
+        counter_run(args.workload, args.counter_target)
         return
 
     log(f"[bench] workload {args.workload}, warmup {args.warmup}, steps {args.steps}")
@@ -405,17 +478,35 @@ def main():
     secondary = None
     if args.secondary >= 0 and args.secondary != args.workload:
         log(f"[bench] secondary workload {args.secondary}")
-        r2, x2, _ = time_workload(args.secondary, args.steps, args.warmup)
+        r2, x2, _ = time_workload(args.secondary, args.steps, args.warmup,
+                                  copies=input_copies(args.secondary))
         w2 = r2["workload"]
-        log(f"[bench] {w2.name}: {r2['kernel_ms']:.3f} ms, "
+        log(f"[bench] {w2.name}: {r2['kernel_ms']:.3f} ms ({r2['copies']} input copies), "
             f"{r2['tokens_per_s'] / 1e6:.2f} M tokens/s, {100 * r2['hbm_frac']:.1f}% of HBM peak")
-        secondary = {"workload": w2.name, "value": r2["tokens_per_s"], "unit": "tokens/s",
-                     "ms_per_step": r2["ms_per_step"],
-                     "roofline": {"bound": "hbm", "achieved": r2["achieved_gbs"],
-                                  "peak": perfmodel.HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": r2["hbm_frac"], "traffic": None},
-                     "mfma_frac": r2["mfma_frac"]}
+        secondary = workload_line(r2)
         del x2
+
+    # the other full-size workloads: 4 x 32K continuation (fp32 states), T = 1M
+    others = []
+    cpu_long = None
+    for wid in args.also:
+        if wid in (args.workload, args.secondary):
+            continue
+        st = args.steps if wid != 4 else max(3, args.steps // 5)
+        wu = args.warmup if wid != 4 else 1
+        log(f"[bench] workload {wid}, warmup {wu}, steps {st}")
+        r3, x3, _ = time_workload(wid, st, wu, copies=input_copies(wid))
+        w3 = r3["workload"]
+        log(f"[bench] {w3.name}: {r3['kernel_ms']:.3f} ms, {r3['tokens_per_s'] / 1e6:.2f} M "
+            f"tokens/s, {100 * r3['hbm_frac']:.1f}% of HBM peak")
+        others.append(workload_line(r3))
+        if wid == 4 and not args.no_cpu_baseline:
+            # the long-context oracle on 4 heads, one pass over all 1M tokens
+            log(f"[bench] cpu baseline: oracle on 4 heads of {w3.name}")
+            cpu_long = cpu_baseline(x3, 4, min_seconds=0.0, max_passes=1)
+            log(f"[bench] cpu baseline {cpu_long['head_tokens_per_s']:.1f} head-tokens/s "
+                f"(4 of 32 heads) on {cpu_long['cores']} threads")
+        del x3
 
     decode = None
     decode_dims = None
@@ -439,7 +530,8 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_heads} heads of {w.name}")
         cpu = cpu_baseline(x, args.cpu_heads)
-        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads "
+            f"({cpu['nproc']} host cpus)")
 
     line = {
         "metric": METRIC,
@@ -468,12 +560,14 @@ def main():
                  "unit": "TFLOP/s", "frac": r["mfma_frac"],
                  "flops_model": "6Td^2+3TCd+TC^2 per head"},
         "secondary": secondary,
+        "other_workloads": others,
         "decode": decode,
         "decode_head_dims": decode_dims,
         "gdn": gdn,
         "head_dims": dims,
         "bwd": bwd,
         "cpu_baseline": cpu,
+        "cpu_baseline_long_context": cpu_long,
     }
     print(json.dumps(line), flush=True)
 
