@@ -75,7 +75,9 @@ typedef enum {
   KDA_ERR_DTYPE = -5,        /* a dtype argument is not a kda_dtype */
   KDA_ERR_SHAPE = -6,        /* B, H, num_seqs <= 0, T < 0, or sizes overflow */
   KDA_ERR_ALIGN = -7,        /* a pointer is not aligned as required below */
-  KDA_ERR_HIP = -8           /* the HIP runtime reported an error (see kda_last_error) */
+  KDA_ERR_HIP = -8,          /* the HIP runtime reported an error (see kda_last_error) */
+  KDA_ERR_WORKSPACE = -9     /* kda_fwd_noalloc: the call needs more workspace than its
+                                static scratch holds */
 } kda_status;
 
 /*

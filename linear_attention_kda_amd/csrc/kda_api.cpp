@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -114,62 +115,90 @@ bool seq_split_enabled() {
   return !(e != nullptr && e[0] == '0' && e[1] == '\0');
 }
 
-// The device's segment plan for N equal sequences of c chunks (fixed-length
-// batches): does it split them?  Same rule as the kernels' plan.
-bool fixed_length_splits(int64_t N, int64_t c, int64_t H, int64_t cus, int seg_min, int emax) {
-  if (c <= seg_min) return false;
+// The device's segment length for N equal sequences of c chunks (fixed-length
+// batches) with emax state slots and ucap fix-up units, or 0 when it does not
+// split them.  Same rule as the kernels' plan.
+int64_t fixed_length_segment(int64_t N, int64_t c, int64_t H, int64_t cus, int seg_min,
+                             int64_t emax, int64_t ucap) {
+  if (c <= seg_min || emax <= 0) return 0;
   auto fits = [&](int64_t m) {
-    return kda::kSlackDen * H * (N * c + N * (c > m ? c - m : 0)) <= kda::kSlackNum * m * cus;
+    const int64_t extra = c > m ? N * (c - m) : 0;
+    const int64_t slots = c > m ? N * ((c - 1) / m) : 0;
+    return kda::kSlackDen * H * (N * c + extra) <= kda::kSlackNum * m * cus && slots <= emax &&
+           H * extra <= ucap;
   };
-  if (!fits(c)) return false;
+  if (!fits(c)) return 0;
   int64_t lo = seg_min, hi = c;
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo) / 2;
     if (fits(mid)) hi = mid;
     else lo = mid + 1;
   }
-  return hi < c && N * ((c + hi - 1) / hi - 1) <= emax;
+  return hi < c ? hi : 0;
 }
 
 struct LaunchPlan {
   int nsplit;     // value-column slices per (sequence, head)
   int emax;       // segment state slots (0: no sequence splitting)
+  int ucap;       // fix-up units (one 64 x 128 output block each)
   int seg_min;
   int64_t workgroups;
   size_t workspace;
 };
 
 // rows: packed rows (T with cu_seqlens, else B*T); T: tokens per row, or the
-// packed total with cu_seqlens.
-LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus) {
+// packed total with cu_seqlens.  cap_bytes > 0 bounds the workspace (a
+// caller-provided buffer): the state slots and fix-up units are then sized to
+// it, and the device plan splits sequences only as far as they fit.
+LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus,
+                     size_t cap_bytes = 0) {
   LaunchPlan lp{};
   lp.seg_min = seg_min_chunks();
   const int forced = forced_splits();
   const int64_t c_max = (T + KDA_CHUNK - 1) / KDA_CHUNK;  // chunks of the longest possible sequence
-  int emax = 0;
+  int64_t emax = 0, ucap = 0;
   // the device plan counts chunks and fix-up units in 32-bit integers
   const int64_t chunks = (varlen ? c_max + N : (int64_t)N * c_max);
   const bool small_enough = chunks < (1LL << 30) && chunks * H < (1LL << 30);
   if (seq_split_enabled() && forced != 2 && N <= kda::kSortLimit && c_max > lp.seg_min &&
       small_enough) {
-    emax = kda::workspace_slots(cus, H);
-    if (emax > 512) emax = 512;
-    if (emax > 0 && !varlen && !fixed_length_splits(N, c_max, H, cus, lp.seg_min, emax)) emax = 0;
+    emax = std::min(kda::workspace_slots(cus, H), 512);
+    ucap = chunks * H;  // every chunk past a first segment, at most
+    if (cap_bytes > 0) {  // slots first (at most half the buffer), then fix-up blocks
+      const size_t slot = kda::workspace_slot_bytes(H);
+      emax = std::min<int64_t>(emax, (int64_t)(cap_bytes / 2 / slot));
+      const size_t rest = cap_bytes - kda::workspace_layout(0, H, (int)emax).total;
+      ucap = std::min<int64_t>(ucap, (int64_t)(rest / kda::kUnitBytes) - 1);
+      if (ucap < H) emax = 0;  // not one chunk of every head fits
+    }
+    if (emax > 0 && !varlen) {  // the host knows the device's plan exactly: size to it
+      const int64_t M = fixed_length_segment(N, c_max, H, cus, lp.seg_min, emax, ucap);
+      if (M == 0) {
+        emax = 0;
+      } else {
+        emax = N * ((c_max - 1) / M);
+        ucap = H * N * (c_max - M);
+      }
+    }
   }
-  lp.emax = emax;
+  if (emax <= 0) emax = ucap = 0;
+  lp.emax = (int)emax;
+  lp.ucap = (int)ucap;
   // one workgroup per (sequence, head) already covers the CUs: no value split
   lp.nsplit = forced ? forced : (emax > 0 || (int64_t)N * H >= cus) ? 1 : 2;
-  if (emax > 0 && lp.nsplit != 1) lp.emax = emax = 0;
-  const int64_t groups = (int64_t)N + (emax > 0 ? 2 * (int64_t)emax : 0);
+  if (emax > 0 && lp.nsplit != 1) lp.emax = lp.ucap = 0;
+  const int64_t groups = (int64_t)N + (lp.emax > 0 ? 2 * (int64_t)lp.emax : 0);
   lp.workgroups = (groups * H + 7) / 8 * 8 * lp.nsplit;
-  const int64_t rows = varlen ? T : (int64_t)N * T;
-  lp.workspace = emax > 0 ? kda::workspace_layout(rows, H, emax).total : 0;
+  lp.workspace = lp.emax > 0 ? kda::workspace_layout(lp.ucap, H, lp.emax).total : 0;
   return lp;
 }
 
-// Library-owned stream-ordered pool for the splitting workspace, one per device.
-// It keeps what it has reserved (release threshold at maximum), so after the
-// first call of a given size a workspace costs no allocation from the driver.
+// Library-owned stream-ordered pool for the workspaces, one per device.  It keeps
+// up to kPoolKeepBytes reserved between calls (so a repeated call of the same
+// size costs no allocation from the driver) and hands anything above that back
+// at the next synchronisation.
+constexpr uint64_t kPoolKeepBytes = 2ull << 30;
+
 hipError_t workspace_pool(hipMemPool_t* out) {
   static std::mutex mu;
   static hipMemPool_t pools[64] = {};
@@ -188,7 +217,7 @@ hipError_t workspace_pool(hipMemPool_t* out) {
     hipMemPool_t pool = nullptr;
     err = hipMemPoolCreate(&pool, &props);
     if (err != hipSuccess) return err;
-    uint64_t keep = UINT64_MAX;
+    uint64_t keep = kPoolKeepBytes;
     err = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
     if (err != hipSuccess) {
       (void)hipMemPoolDestroy(pool);
@@ -206,7 +235,8 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
                         const float* beta, float scale, const void* initial_state,
                         int initial_dtype, void* final_state, int final_dtype,
                         const int32_t* cu_seqlens, int32_t N, int32_t B, int64_t T, int32_t H,
-                        int32_t D, void* out, void* stream, bool g_scalar) {
+                        int32_t D, void* out, void* stream, bool g_scalar,
+                        const kda::ExtWorkspace* ext) {
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const int64_t rows = cu_seqlens ? T : (int64_t)B * T;
   kda::DimParams p{};
@@ -230,7 +260,13 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
   p.slots = rows > 0 ? kda::dim_slots(N, rows) : 0;
   const size_t bytes = (size_t)p.slots * H * kda::dim_record_bytes(D);
   void* ws = nullptr;
-  if (bytes > 0) {
+  if (bytes > 0 && ext != nullptr) {
+    if (bytes > ext->bytes)
+      return fail(KDA_ERR_WORKSPACE,
+                  "head dimension %d needs %zu bytes of per-chunk records, more than the %zu "
+                  "bytes of the static scratch", D, bytes, ext->bytes);
+    p.ws = static_cast<char*>(ext->ptr);
+  } else if (bytes > 0) {
     hipMemPool_t pool = nullptr;
     hipError_t e = workspace_pool(&pool);
     if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, hs);
@@ -239,8 +275,9 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
     p.ws = static_cast<char*>(ws);
   }
   if (log_enabled())
-    std::fprintf(stderr, "[kda] launch: %s D=%d N=%d H=%d T=%lld record_slots=%lld workspace=%zu\n",
-                 g_scalar ? "gdn" : "kda", D, N, H, (long long)T, (long long)p.slots, bytes);
+    std::fprintf(stderr, "[kda] launch: %s D=%d N=%d H=%d T=%lld record_slots=%lld workspace=%zu%s\n",
+                 g_scalar ? "gdn" : "kda", D, N, H, (long long)T, (long long)p.slots, bytes,
+                 ext ? " (static scratch)" : "");
   const hipError_t err = kda::launch_fwd_dim(p, hs);
   if (ws != nullptr) {
     const hipError_t e = hipFreeAsync(ws, hs);
@@ -252,11 +289,15 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
   return KDA_OK;
 }
 
+}  // namespace
+
+namespace kda {
+
 kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     float scale, const void* initial_state, int initial_dtype, void* final_state,
                     int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
                     int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream,
-                    bool g_scalar) {
+                    bool g_scalar, const ExtWorkspace* ext) {
   g_last_error.clear();
   int32_t N = 0;
   kda_status st = validate(q, k, v, g, beta, initial_state, initial_dtype, final_state,
@@ -266,12 +307,12 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   if (T == 0 && final_state == nullptr) return KDA_OK;  // nothing observable to compute
   if (K != KDA_HEAD_DIM)
     return fwd_dim_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
-                        final_dtype, cu_seqlens, N, B, T, H, K, out, stream, g_scalar);
+                        final_dtype, cu_seqlens, N, B, T, H, K, out, stream, g_scalar, ext);
 
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const LaunchPlan lp = make_plan(N, T, H, cu_seqlens != nullptr, cus);
+  const LaunchPlan lp = make_plan(N, T, H, cu_seqlens != nullptr, cus, ext ? ext->bytes : 0);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
 
   kda::Params p{};
@@ -295,24 +336,34 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   p.seg_min = lp.seg_min;
   void* ws = nullptr;
   if (lp.emax > 0) {
-    hipMemPool_t pool = nullptr;
-    hipError_t e = workspace_pool(&pool);
-    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, lp.workspace, pool, hs);
-    if (e != hipSuccess)
-      return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", lp.workspace, hipGetErrorString(e));
-    const kda::WorkspaceLayout wl =
-        kda::workspace_layout(cu_seqlens ? T : (int64_t)B * T, H, lp.emax);
+    char* base = nullptr;
+    if (ext != nullptr) {
+      if (lp.workspace > ext->bytes)  // the plan is sized to the scratch: never taken
+        return fail(KDA_ERR_WORKSPACE, "split plan needs %zu bytes, the static scratch holds %zu",
+                    lp.workspace, ext->bytes);
+      base = static_cast<char*>(ext->ptr);
+    } else {
+      hipMemPool_t pool = nullptr;
+      hipError_t e = workspace_pool(&pool);
+      if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, lp.workspace, pool, hs);
+      if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", lp.workspace, hipGetErrorString(e));
+      base = static_cast<char*>(ws);
+    }
+    const kda::WorkspaceLayout wl = kda::workspace_layout(lp.ucap, H, lp.emax);
     p.emax = lp.emax;
-    p.o0 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.o0);
-    p.st = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.st);
-    p.sb = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.sb);
+    p.ucap = lp.ucap;
+    p.o0 = reinterpret_cast<uint16_t*>(base + wl.o0);
+    p.st = reinterpret_cast<float*>(base + wl.st);
+    p.sb = reinterpret_cast<uint16_t*>(base + wl.sb);
   }
   if (log_enabled())
     std::fprintf(stderr,
                  "[kda] launch: %s N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
-                 "segment_slots=%d workspace=%zu\n",
+                 "segment_slots=%d fixup_units=%d workspace=%zu%s\n",
                  g_scalar ? "gdn" : "kda", N, H, (long long)T, lp.nsplit, cus,
-                 cu_seqlens != nullptr, lp.emax, lp.workspace);
+                 cu_seqlens != nullptr, lp.emax, lp.ucap, lp.workspace,
+                 ext ? " (static scratch)" : "");
   const hipError_t err = kda::launch_fwd(p, lp.nsplit, hs);
   if (ws != nullptr) {
     const hipError_t e = hipFreeAsync(ws, hs);
@@ -324,7 +375,9 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   return KDA_OK;
 }
 
-}  // namespace
+kda_status record_failure(kda_status st, const char* text) { return fail(st, "%s", text); }
+
+}  // namespace kda
 
 extern "C" {
 
@@ -339,6 +392,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_SHAPE: return "invalid sizes";
     case KDA_ERR_ALIGN: return "misaligned pointer";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_WORKSPACE: return "call needs more workspace than the static scratch holds";
     default: return "unknown status";
   }
 }
@@ -388,8 +442,9 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
                    float scale, const void* initial_state, int initial_dtype, void* final_state,
                    int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
                    int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream) {
-  return fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state, final_dtype,
-                  cu_seqlens, num_seqs, B, T, H, K, V, out, stream, false);
+  return kda::fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
+                       final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out, stream, false,
+                       nullptr);
 }
 
 kda_status kda_gdn_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -397,8 +452,9 @@ kda_status kda_gdn_fwd(const void* q, const void* k, const void* v, const float*
                        int initial_dtype, void* final_state, int final_dtype,
                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
                        int32_t H, int32_t K, int32_t V, void* out, void* stream) {
-  return fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state, final_dtype,
-                  cu_seqlens, num_seqs, B, T, H, K, V, out, stream, true);
+  return kda::fwd_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
+                       final_dtype, cu_seqlens, num_seqs, B, T, H, K, V, out, stream, true,
+                       nullptr);
 }
 
 }  // extern "C"

@@ -278,7 +278,9 @@ struct Work {
   int vzero;       // values read as zero
   const void* s0;  // this (sequence, head)'s 128 x 128 start state
   void* s1;        // where its end state goes, or null
-  __bf16* o;       // output rows, bf16 [rows][H][128]
+  __bf16* o;       // output rows of the run's first chunk for head h (bf16)
+  int orow;        // elements between output rows (H * 128, or 128 in a fix-up block)
+  int64_t ochunk;  // elements between the first rows of consecutive chunks
   uint16_t* sb;    // also the end state in the fix-up's bf16 operand order, or null
   float* ck;       // checkpoint of the run's first chunk (chunk c at + c * H * 128 * 128), or null
 };
@@ -820,10 +822,8 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16]);
   }
 
-  const int HD = p.H * D;
   for (int it = -1; it < w.nchunks; ++it) {
     const bool act = it >= 0;
-    const int64_t tok0 = w.bos + (int64_t)it * C;
     const int64_t rest = w.len - (int64_t)it * C;
     const int valid = rest < C ? (int)rest : C;
     f32x4 Z[4][JT];   // beta * Y, rows 16b + 4q4 + t, column m16
@@ -915,8 +915,8 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
         }
       }
       // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor)
-      const auto orsrc = rsrc(w.o + tok0 * HD + (int64_t)w.h * D, valid * HD * 2);
-      const int ovo = (m16 * HD + jw_base + 4 * q4) * 2;  // lane part of the store offset
+      const auto orsrc = rsrc(w.o + (int64_t)it * w.ochunk, valid * w.orow * 2);
+      const int ovo = (m16 * w.orow + jw_base + 4 * q4) * 2;  // lane part of the store offset
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + m16;
@@ -936,7 +936,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           const uint2 ov = pack4(o[0], o[1], o[2], o[3]);
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-              ovo + 32 * jt, 16 * rt * HD * 2, 0);
+              ovo + 32 * jt, 16 * rt * w.orow * 2, 0);
         }
       }
       // S <- Diag(exp(G_last)) S + K'^T U
@@ -1099,11 +1099,19 @@ __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
     }
     mx = wave_max(mx);
     sum = wave_sum(sum);
+    // fits(m): segments of m chunks balance the device, and the workspace holds
+    // their state slots (emax) and fix-up output blocks (ucap); each condition
+    // only gets easier as m grows
     auto fits = [&](int m) {
-      int extra = 0;
-      for (int i = lane; i < N; i += 64) extra += max(0, v.lens[i] - m);
+      int extra = 0, slots = 0;
+      for (int i = lane; i < N; i += 64) {
+        extra += max(0, v.lens[i] - m);
+        slots += v.lens[i] > m ? (v.lens[i] - 1) / m : 0;
+      }
       extra = wave_sum(extra);
-      return (long long)kSlackDen * p.H * ((long long)sum + extra) <= (long long)kSlackNum * m * p.cus;
+      slots = wave_sum(slots);
+      return (long long)kSlackDen * p.H * ((long long)sum + extra) <= (long long)kSlackNum * m * p.cus &&
+             slots <= p.emax && (long long)p.H * extra <= p.ucap;
     };
     int M = kNoSplit;
     if (p.emax > 0 && mx > p.seg_min && fits(mx)) {
@@ -1114,11 +1122,6 @@ __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
         else lo = mid + 1;
       }
       if (hi < mx) M = hi;
-    }
-    if (M != kNoSplit) {  // the workspace holds emax segment states per head
-      int slots = 0;
-      for (int i = lane; i < N; i += 64) slots += seq_counts(v.lens[i], M, p.H).slots;
-      if (wave_sum(slots) > p.emax) M = kNoSplit;
     }
     // exclusive prefix sums over contiguous runs of sequences, one run per lane
     const int per = (N + 63) / 64;
@@ -1223,6 +1226,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
 
   // ---- task of this rank: longest first (ties by sequence, then segment)
   int n = rank, kind = 0, M = kNoSplit, slot0 = 0;
+  int ubase1 = 0, ubase2 = 0;  // first fix-up unit of (n, h) in segment 1 / in the later ones
   const bool planned = p.nseq <= kSortLimit && (p.emax > 0 || (p.cu != nullptr && p.nseq > 1));
   if (planned) {
     const PlanView v = plan_view(reinterpret_cast<int*>(sm.kg), p.nseq, p.emax);
@@ -1244,6 +1248,12 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     kind = __builtin_amdgcn_readfirstlane(v.gk[g]);
     M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
     slot0 = __builtin_amdgcn_readfirstlane(v.soff[n]);
+    if (kind != 0) {  // fix-up units numbered by head, then chunk (the tail kernel's order)
+      const int c = __builtin_amdgcn_readfirstlane(v.lens[n]);
+      ubase1 = __builtin_amdgcn_readfirstlane(v.uoff[n]) + w.h * min(c - M, M);
+      ubase2 = __builtin_amdgcn_readfirstlane(v.hdr[4]) + __builtin_amdgcn_readfirstlane(v.voff[n]) +
+               w.h * (c - 2 * M);
+    }
     __syncthreads();  // the scratch is reused by the prep waves
   } else if (rank >= p.nseq) {
     return;
@@ -1278,7 +1288,9 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
            : static_cast<char*>(p.s1) + ((size_t)n * p.H * (D * D) + hd2) * (p.s1_fp32 ? 4 : 2);
       w.s1_fp32 = p.s1_fp32;
     }
-    w.o = reinterpret_cast<__bf16*>(p.out);
+    w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * D) + (int64_t)w.h * D;
+    w.orow = p.H * D;
+    w.ochunk = (int64_t)C * p.H * D;
     w.vzero = 0;
     w.ck = p.ckpt == nullptr ? nullptr : p.ckpt + ((size_t)(n + bos / C) * p.H + w.h) * (D * D);
   } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
@@ -1291,7 +1303,16 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.s0 = nullptr;
     w.s1 = p.st + ((size_t)((ident ? 1 : 2) * p.emax + slot0 + sp - 1) * p.H) * (D * D) + hd2;
     w.s1_fp32 = 1;
-    w.o = reinterpret_cast<__bf16*>(ident ? p.out : p.o0);
+    if (ident) {  // Q~ into the output rows
+      w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * D) + (int64_t)w.h * D;
+      w.orow = p.H * D;
+      w.ochunk = (int64_t)C * p.H * D;
+    } else {      // O0 into the fix-up blocks of its units, one 64 x 128 block per chunk
+      const int ub = sp == 1 ? ubase1 : ubase2 + (sp - 2) * M;
+      w.o = reinterpret_cast<__bf16*>(p.o0) + (int64_t)ub * (C * D);
+      w.orow = D;
+      w.ochunk = (int64_t)C * D;
+    }
     w.ck = nullptr;
     w.vzero = ident ? 1 : 0;
     w.sb = nullptr;

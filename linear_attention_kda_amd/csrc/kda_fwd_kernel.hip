@@ -137,6 +137,7 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
 // M + min(c - M, M) - 1, later-segment units (seg0 = 2) chunks 2M .. c - 1.
 struct FixUnit {
   int i, h, ch, slot, valid;
+  int ob;          // the unit's O0 block: units of segment 1 first, then the later ones
   int64_t tok0;
 };
 
@@ -144,6 +145,7 @@ __device__ __forceinline__ FixUnit fix_decode(const Params& p, const PlanView& v
                                               int seg0, int u) {
   FixUnit f;
   f.i = __builtin_amdgcn_readfirstlane(find_seq(off, p.nseq, u));
+  f.ob = seg0 == 1 ? u : __builtin_amdgcn_readfirstlane(v.hdr[4]) + u;
   const int r = u - __builtin_amdgcn_readfirstlane(off[f.i]);
   const int c = __builtin_amdgcn_readfirstlane(v.lens[f.i]);
   const int n = seg0 == 1 ? min(c - M, M) : c - 2 * M;  // chunks per head in this range
@@ -181,7 +183,7 @@ __device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, Fix
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
   const int HD = p.H * D;
   const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
-  const auto zrsrc = rsrc(p.o0 + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
+  const auto zrsrc = rsrc(p.o0 + (int64_t)f.ob * (C * D), f.valid * D * 2);
 #pragma unroll
   for (int x = 0; x < 4; ++x)
     L.qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
@@ -190,7 +192,7 @@ __device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, Fix
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
       L.zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
-          zrsrc, ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+          zrsrc, ((16 * tt + m16) * D + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
 }
 
 // S_p^T as the products' A operand (bf16, the order the segment's first run wrote).
@@ -205,14 +207,11 @@ __device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f, bf1
       sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
 }
 
-// This workgroup's contiguous share of `units` fix-up units, spread over the
-// workgroups first .. gridDim.x - 1: o = O0 + S_p^T Q~ for every row of each
-// unit's chunk.  The next unit's loads are in flight while the current one is
-// multiplied; S_p is reloaded only when the segment or head changes.
-__device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0, int units,
-                          __bf16* ot, int first) {
-  const int G = gridDim.x - first, b = blockIdx.x - first;
-  const int u_lo = (int)((int64_t)units * b / G), u_hi = (int)((int64_t)units * (b + 1) / G);
+// Fix-up units [u_lo, u_hi) of this workgroup: o = O0 + S_p^T Q~ for every row
+// of each unit's chunk.  The next unit's loads are in flight while the current
+// one is multiplied; S_p is reloaded only when the segment or head changes.
+__device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0,
+                          int u_lo, int u_hi, __bf16* ot) {
   if (u_lo >= u_hi) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,18 +282,22 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
   // wave-uniform unit values keep every buffer descriptor scalar
   const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
   if (M == kNoSplit) return;
+  const int G = gridDim.x, b = blockIdx.x;
   if (phase == 0) {
-    // scan units spread over the grid, then every workgroup's share of the
+    // scan units spread over the grid, then this workgroup's share of the
     // segment-1 fix-ups (they need only S_1, written by the main kernel)
     const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
-    for (int u = blockIdx.x; u < nscan; u += gridDim.x) scan_unit(p, v, M, u, slt);
+    for (int u = b; u < nscan; u += G) scan_unit(p, v, M, u, slt);
     // with workgroups to spare, the fix-ups go to those without a scan unit and run
     // beside the scan instead of after it
-    const int first = nscan < (int)gridDim.x ? nscan : 0;
-    if ((int)blockIdx.x >= first)
-      fix_range(p, v, M, v.uoff, 1, __builtin_amdgcn_readfirstlane(v.hdr[4]), ot, first);
+    const int F = __builtin_amdgcn_readfirstlane(v.hdr[4]);
+    const int first = nscan < G ? nscan : 0;
+    if (b >= first)
+      fix_range(p, v, M, v.uoff, 1, (int)((int64_t)F * (b - first) / (G - first)),
+                (int)((int64_t)F * (b - first + 1) / (G - first)), ot);
   } else {
-    fix_range(p, v, M, v.voff, 2, __builtin_amdgcn_readfirstlane(v.hdr[5]), ot, 0);
+    const int F = __builtin_amdgcn_readfirstlane(v.hdr[5]);
+    fix_range(p, v, M, v.voff, 2, (int)((int64_t)F * b / G), (int)((int64_t)F * (b + 1) / G), ot);
   }
 }
 
@@ -302,15 +305,17 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
 
 int workspace_slots(int cus, int H) { return (H > 0 && H < cus) ? cus / H + 1 : 0; }
 
-WorkspaceLayout workspace_layout(int64_t rows, int H, int emax) {
+WorkspaceLayout workspace_layout(int64_t ucap, int H, int emax) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout l;
   l.o0 = 0;
-  l.st = up((size_t)rows * H * D * 2);
+  l.st = up((size_t)ucap * kUnitBytes);
   l.sb = l.st + up((size_t)3 * emax * H * D * D * 4);
   l.total = l.sb + up((size_t)emax * H * D * D * 2);
   return l;
 }
+
+size_t workspace_slot_bytes(int H) { return (size_t)H * D * D * (3 * 4 + 2); }
 
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;

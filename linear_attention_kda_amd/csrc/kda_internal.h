@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 // Sequences are ordered longest-first, and long ones split into segments, only
@@ -42,7 +44,9 @@ struct Params {
   int cus;                // parallel width the segment plan fills (compute units)
   int seg_min;            // shortest sequence, in chunks, that may be split
   int emax;               // segment state slots in the workspace; 0 disables splitting
-  uint16_t* o0;           // bf16 [rows][H][128]: outputs of later segments from a zero state
+  int ucap;               // fix-up units the workspace's output blocks hold
+  uint16_t* o0;           // bf16 [ucap][64][128]: outputs of later segments from a zero
+                          // state, one 64-row block per fix-up unit (sequence, head, chunk)
   float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
   uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
   // Backward support: the fp32 state at the start of every chunk, at slot
@@ -52,12 +56,15 @@ struct Params {
   int g_scalar;           // one gate per token and head (Gated DeltaNet)
 };
 
-// Workspace bytes for splitting with `emax` state slots over `rows` packed
-// rows of H heads, and the offsets of its three parts.
+// Workspace bytes for splitting with `emax` state slots and `ucap` fix-up
+// units of H heads, and the offsets of its three parts.
 struct WorkspaceLayout {
   size_t o0, st, sb, total;
 };
-WorkspaceLayout workspace_layout(int64_t rows, int H, int emax);
+WorkspaceLayout workspace_layout(int64_t ucap, int H, int emax);
+// Bytes of one state slot (all heads) and of one fix-up unit's output block.
+size_t workspace_slot_bytes(int H);
+constexpr size_t kUnitBytes = 64 * 128 * 2;
 
 // State slots a plan can use on `cus` compute units with H heads: the plan
 // never needs more than cus / H extra segments.
@@ -167,6 +174,23 @@ struct DimParams {
 size_t dim_record_bytes(int D);
 int64_t dim_slots(int64_t nseq, int64_t rows);
 hipError_t launch_fwd_dim(const DimParams& p, hipStream_t stream);
+
+// A caller-provided workspace: the forward pass sizes its plan to it instead of
+// taking memory from the library's pool.
+struct ExtWorkspace {
+  void* ptr;
+  size_t bytes;
+};
+
+// kda_fwd / kda_gdn_fwd (g_scalar), with the workspace from `ext` instead of the
+// library's pool when ext is not null.
+kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    float scale, const void* initial_state, int initial_dtype, void* final_state,
+                    int final_dtype, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                    int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream,
+                    bool g_scalar, const ExtWorkspace* ext);
+// Records the text of a failure (kda_last_error) and returns st.
+kda_status record_failure(kda_status st, const char* text);
 
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and

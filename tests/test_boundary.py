@@ -195,9 +195,11 @@ def test_state_dtype_ignored_for_absent_state(lib):
     assert binding.fwd_check(**ok_args(initial_dtype=7)) == OK
 
 
-def _split_workspace(rows, H, emax):
-    up = lambda x: (x + 255) // 256 * 256
-    return up(rows * H * 128 * 2) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
+def _split_workspace(units, H, emax):
+    """Fix-up output blocks (64 x 128 bf16 per unit), then the fp32 segment states,
+    maps and end states, then their bf16 fix-up copies."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return up(units * 64 * 128 * 2) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
 
 
 def test_plan_value_split(lib, monkeypatch):
@@ -212,13 +214,18 @@ def test_plan_value_split(lib, monkeypatch):
     assert binding.plan(3, 256, 3, False, 256) == (32, 2, 0)   # 9 pairs padded to 16, times 2
     # H >= CUs: never split
     assert binding.plan(1, 8192, 256, False, 256) == (256, 1, 0)
-    # one 8K sequence, 32 heads: split (segment slots 256/32 + 1 = 9); the grid
-    # covers the sequence plus two runs per possible extra segment
-    assert binding.plan(1, 8192, 32, False, 256) == ((1 + 18) * 32, 1, _split_workspace(8192, 32, 9))
+    # one 8K sequence (128 chunks), 32 heads: the host evaluates the device's rule,
+    # 32 (128 + (128 - M)) <= 0.95 * 256 M  ->  M = 30, i.e. 5 segments: 4 state slots
+    # and 98 chunks past the first segment per head (3136 fix-up units); the grid
+    # covers the sequence plus two runs per extra segment
+    assert binding.plan(1, 8192, 32, False, 256) == ((1 + 8) * 32, 1, _split_workspace(3136, 32, 4))
     # 16 equal sequences of 128 chunks on 256 CUs: 512 pairs already fill the CUs
     assert binding.plan(16, 8192, 32, False, 256) == (512, 1, 0)
-    # varlen: the lengths live on the device, so the plan allows splitting
-    assert binding.plan(16, 65536, 32, True, 256) == ((16 + 18) * 32, 1, _split_workspace(65536, 32, 9))
+    # varlen: the lengths live on the device, so the plan allows splitting with
+    # 256/32 + 1 = 9 state slots and a fix-up block for every chunk that could need
+    # one (65536 / 64 + 16 chunks per head)
+    assert binding.plan(16, 65536, 32, True, 256) == ((16 + 18) * 32, 1,
+                                                      _split_workspace(1040 * 32, 32, 9))
     with pytest.raises(binding.KdaError):
         binding.plan(0, 256, 32, False, 256)
 
