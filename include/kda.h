@@ -128,6 +128,33 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
                    int64_t T, int32_t H, int32_t K, int32_t V, void* out, void* stream);
 
 /*
+ * kda_fwd_noalloc — kda_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, layouts, results and status codes as kda_fwd;
+ * it calls no hipMalloc, hipFree or allocating library routine.  Its workspace
+ * is a static device array of KDA_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held from the first call on that GPU until the process ends:
+ *   d = 128: the plan for splitting long sequences into segments is sized to
+ *            the scratch (segment state slots and the 64 x 128 output blocks
+ *            of the later segments' chunks); sequences are split only as far
+ *            as those fit, so every size runs, very long ones in fewer and
+ *            longer segments than kda_fwd would use;
+ *   d = 64, 256: the per-chunk records must fit (slots x H x record bytes, see
+ *            kda_dim_workspace_bytes); larger calls return KDA_ERR_WORKSPACE
+ *            before any launch.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (concurrent streams, threads) race and must be serialised by the caller.
+ * Nothing in the scratch needs clearing between calls: each call writes every
+ * entry it reads.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+kda_status kda_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float scale, const void* initial_state,
+                           int initial_dtype, void* final_state, int final_dtype,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int64_t T,
+                           int32_t H, int32_t K, int32_t V, void* out, void* stream);
+
+/*
  * kda_fwd_check — the host-side validation kda_fwd performs, without any
  * launch or device access (pointers are only tested for NULL and alignment).
  * Same arguments and status codes as kda_fwd.

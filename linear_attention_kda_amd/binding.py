@@ -64,8 +64,9 @@ def load_library():
         lib.kda_decode_check.restype = ctypes.c_int
         lib.kda_decode_check.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                          ctypes.c_int, _vp, _i32, _i32, _i32, _i32, _vp]
-        for name in ("kda_gdn_fwd", "kda_gdn_fwd_check", "kda_gdn_decode", "kda_gdn_decode_check"):
-            base = getattr(lib, name.replace("gdn_", ""))
+        for name in ("kda_gdn_fwd", "kda_gdn_fwd_check", "kda_gdn_decode", "kda_gdn_decode_check",
+                     "kda_fwd_noalloc"):
+            base = getattr(lib, name.replace("gdn_", "").replace("_noalloc", ""))
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = base.argtypes
@@ -152,6 +153,15 @@ def fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_
                 output_final_state, scalar_gate=False)
 
 
+def fwd_noalloc(q, k, v, g, beta, scale: float | None = None, initial_state=None,
+                final_state=None, cu_seqlens=None, out=None, output_final_state: bool = False):
+    """fwd() through kda_fwd_noalloc: the library allocates no device memory and uses
+    its static per-GPU scratch (KDA_NOALLOC_SCRATCH_BYTES) as the workspace.  out and
+    final_state are allocated here (by torch) only when not given."""
+    return _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
+                output_final_state, scalar_gate=False, noalloc=True)
+
+
 def gdn_fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, final_state=None,
             cu_seqlens=None, out=None, output_final_state: bool = False):
     """Scalar-gate (Gated DeltaNet) forward: as fwd() with g fp32 [B, T, H], one
@@ -161,7 +171,7 @@ def gdn_fwd(q, k, v, g, beta, scale: float | None = None, initial_state=None, fi
 
 
 def _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
-         output_final_state, scalar_gate):
+         output_final_state, scalar_gate, noalloc=False):
     import torch
     lib = load_library()
     if q.dim() != 4:
@@ -204,14 +214,15 @@ def _fwd(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens, out,
         scale = 1.0 / math.sqrt(K)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     stream = torch.cuda.current_stream(dev).cuda_stream
-    entry = lib.kda_gdn_fwd if scalar_gate else lib.kda_fwd
+    entry = lib.kda_gdn_fwd if scalar_gate else lib.kda_fwd_noalloc if noalloc else lib.kda_fwd
     with torch.cuda.device(dev):
         st = entry(ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), float(scale),
                    ptr(initial_state), _state_dtype(initial_state), ptr(final_state),
                    _state_dtype(final_state), ptr(cu_seqlens), num_seqs, B, T, H, K, V,
                    ptr(out), stream)
     if st != 0:
-        raise KdaError(st, "kda_gdn_fwd" if scalar_gate else "kda_fwd", _detail(lib, st))
+        raise KdaError(st, "kda_gdn_fwd" if scalar_gate else "kda_fwd_noalloc" if noalloc
+                       else "kda_fwd", _detail(lib, st))
     return (out, final_state) if final_state is not None else out
 
 

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_expected_entry_points():
     assert header_functions() == ["kda_bwd", "kda_bwd_check", "kda_bwd_workspace_bytes",
                                   "kda_decode", "kda_decode_check", "kda_dim_workspace_bytes",
-                                  "kda_fwd", "kda_fwd_check",
+                                  "kda_fwd", "kda_fwd_check", "kda_fwd_noalloc",
                                   "kda_gdn_decode", "kda_gdn_decode_check", "kda_gdn_fwd",
                                   "kda_gdn_fwd_check", "kda_last_error", "kda_plan",
                                   "kda_status_string"]
