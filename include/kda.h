@@ -39,7 +39,9 @@
  * or frees it.  A call that may split sequences takes a workspace (size from
  * kda_plan) from a stream-ordered memory pool the library owns, one per
  * device, and returns it to the pool in stream order at the end of the call;
- * the pool keeps its memory for later calls until the process ends.
+ * the pool keeps up to 2 GiB reserved for later calls and hands the rest back
+ * to the device at the next synchronisation.  kda_fwd_noalloc uses a static
+ * scratch instead and allocates nothing.
  * Asynchrony: kda_fwd enqueues work on `stream` (a hipStream_t, or NULL for
  * the null stream) and returns; results are valid after the caller
  * synchronises that stream.  Calls are thread-safe (the pool is created under
@@ -291,8 +293,10 @@ kda_status kda_gdn_decode_check(const void* q, const void* k, const void* v, con
  *  d_initial_state  device, fp32, [N, H, 128, 128], 16-byte aligned, or NULL when
  *                   not wanted (output).
  * Rows outside every sequence (varlen) get zero gradients.  Range limit: the
- * per-channel sum of -g over each 64-token chunk must stay below 80 (natural
- * log); the chunk-local factors exp(+-G) are formed in fp32.
+ * same as kda_fwd's (within each 16-token block aligned to the start of a
+ * 64-token chunk, the per-channel sum of -g below 80; g >= -5 everywhere is
+ * sufficient): every product that pairs exp(G_r) with exp(-G_i) inside a chunk
+ * is evaluated with the same 16-row block references as the forward pass.
  * Memory: a workspace of kda_bwd_workspace_bytes(N, rows, H) bytes (rows = T with
  * cu_seqlens, else B*T) taken from the library's stream-ordered pool for the
  * call.  Asynchrony and errors as kda_fwd.
@@ -320,7 +324,13 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
 int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
- * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only. */
+ * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  It is
+ *   (N + ceil(rows / 64) + 1) * H * 819,972 bytes of per-chunk fp32 tiles
+ *   (every (chunk, head)'s operands, products and state checkpoints),
+ *   plus rows * H * 256 bytes for the forward pass's outputs,
+ * about 12.8 KB per token and head: on a 288 GB device, rows * H of about 22
+ * million at most (T = 8K at H = 32 takes 3.5 GB).  A call that cannot get it
+ * returns KDA_ERR_HIP. */
 int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H);
 
 #ifdef __cplusplus

@@ -18,6 +18,13 @@
 // and through the gates: dq = dqg Gam, dk = dkg Gam + dkh/Gam + dkp gam/Gam,
 //   dG_r = dqg qg + dkg kg - dkh kh - dkp kp (per channel),
 //   dG_last = sum_r dkp kp + gam * rowsum(S * dSn),  dg_t = sum_{r >= t} dG_r + dG_last.
+// kh = K/Gam is never formed: over a whole chunk exp(-G) overflows fp32 long before
+// the recurrence does.  Every product that pairs exp(G_r) with exp(-G_i) -- P, M and
+// the terms dM kh, dA kh and dkh through the gates -- is evaluated directly as
+// sum_i W_ri x_i exp(G_r - G_i) per channel with the 16-row block references of the
+// forward pass (bwd_pm_kernel, bwd_gated_kernel), so the backward accepts every g the
+// forward accepts; the other products only see Gam <= 1, kp = K exp(G_last - G) <= 1
+// and the state.
 // The only serial dependency is dS across chunks: with F = kg^T diag(b) T^T
 // (128 x 64) and X = qg^T dO' - F M^T dO' (128 x 128), both chunk-local,
 //   dS = Diag(gam) dSn - F (kp dSn) + X.
@@ -263,7 +270,8 @@ __global__ void __launch_bounds__(256) bgemm2_kernel(Gemm2Args g) {
 
 // ---------------------------------------------------------------- chunk prep
 // One workgroup per batch (slot, head): loads the chunk's rows (zero past the
-// sequence), forms G, the gated tiles, dO' = scale dO and the per-row beta.
+// sequence), forms G, the gated tiles K Gam, Q Gam and K exp(G_last - G) (all <= 1
+// for g <= 0), dO' = scale dO and the per-row beta.
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) {
   const int64_t bidx = blockIdx.x;
   const int64_t slot = bidx / p.H;
@@ -307,15 +315,354 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) 
     const float vf = in ? bf2f_u16(p.v[row]) : 0.f;
     const float df = in ? p.scale * bf2f_u16(p.dout[row]) : 0.f;
     const float G = gv[i] + off;
-    const float e = expf(G), ei = expf(-G);
+    const float e = expf(G);
     const int64_t o = tb + r * D + ch;
     w.G[o] = G;
     w.kg[o] = kf * e;
     w.qg[o] = qf * e;
-    w.kh[o] = kf * ei;
-    w.kp[o] = kf * ei * gam;
+    w.kp[o] = kf * expf(Glast - G);
     w.vv[o] = vf;
     w.dO[o] = df;
+  }
+}
+
+// ---------------------------------------------------------------- block references
+// For a chunk with G the cumulative log-decay, X_b = G at the last row of block b - 1
+// (X_0 = 0, X_4 = G_last), rows r in block rb and i in block ib <= rb:
+//   exp(G_r - G_i) = F_r w(rb, ib) H_i,  F_r = exp(G_r - X_rb),  H_i = exp(X_{ib+1} - G_i),
+//   w(rb, ib) = exp(X_rb - X_{ib+1})
+// per channel.  For g <= 0, F, H <= 1 and w <= 1 off the diagonal blocks; on a diagonal
+// block w = exp(-sum of g over the block), finite while that sum stays below ~88 -- the
+// forward pass's own limit [core.today "Kimi Linear 특집", ch.4 혁신 2, chunkwise form].
+// Block pairs are numbered p = rb (rb + 1) / 2 + ib.
+constexpr int kPairs = 10;
+
+__device__ __forceinline__ int bwd_pair(int rb, int ib) { return rb * (rb + 1) / 2 + ib; }
+
+__device__ __forceinline__ void bwd_chunk_rows(const BwdParams& p, int64_t bidx, int& h, int64_t& bos,
+                                               int64_t& c, int& valid, int& n) {
+  const int64_t slot = bidx / p.H;
+  h = (int)(bidx % p.H);
+  n = slot_seq(p, slot);
+  bos = seq_bos(p, n);
+  const int64_t len = seq_len_of(p, n);
+  c = slot - (n + bos / C);
+  const int64_t rest = len - c * C;
+  valid = (c < 0 || rest <= 0) ? 0 : rest < C ? (int)rest : C;
+}
+
+// ---------------------------------------------------------------- P, A and M
+// P = strict_lower(K K^T gated), A = diag(beta) P, M = lower_incl(Q K^T gated):
+// P_ri = sum_c k_rc k_ic exp(G_rc - G_ic) = sum_c (k F)_rc (k H)_ic w(rb, ib)_c, and M
+// likewise with q in the row operand, on the fp32 matrix cores (16 x 16 x 4).  One
+// workgroup per batch; each wave takes two or three of the ten lower block pairs (both
+// products share the column operand), the blocks above the diagonal are zero.
+constexpr int PMS = D + 4;  // row stride (fp32) of the staged operands
+struct alignas(16) PmSmem {
+  float kF[C][PMS];
+  float qF[C][PMS];
+  float kH[C][PMS];
+  float wf[kPairs][D];
+  float X[5][D];
+  float tot[2][D];
+  float beta[C];
+};
+
+__device__ __forceinline__ void pm_pair(const PmSmem& sm, const BwdTiles& w, int64_t bidx, int pr) {
+  const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+  const int ib = pr - rb * (rb + 1) / 2;
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, m16 = lane & 15;
+  bg_f32x4 ap = bg_f32x4{0.f, 0.f, 0.f, 0.f}, am = ap;
+  // channel 16j + 4q4 + s4 of instruction s4: four consecutive channels per lane
+  for (int j = 0; j < D / 16; ++j) {
+    const int c0 = 16 * j + 4 * q4;
+    const float4 kf = *reinterpret_cast<const float4*>(&sm.kF[16 * rb + m16][c0]);
+    const float4 qf = *reinterpret_cast<const float4*>(&sm.qF[16 * rb + m16][c0]);
+    const float4 kh = *reinterpret_cast<const float4*>(&sm.kH[16 * ib + m16][c0]);
+    const float4 wv = *reinterpret_cast<const float4*>(&sm.wf[pr][c0]);
+    const float av[4] = {kf.x, kf.y, kf.z, kf.w}, qv[4] = {qf.x, qf.y, qf.z, qf.w};
+    const float bv[4] = {kh.x * wv.x, kh.y * wv.y, kh.z * wv.z, kh.w * wv.w};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      ap = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s4], bv[s4], ap, 0, 0, 0);
+      am = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s4], bv[s4], am, 0, 0, 0);
+    }
+  }
+  // lane holds rows 16 rb + 4 q4 + t, column 16 ib + m16
+  const int i = 16 * ib + m16;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 16 * rb + 4 * q4 + t;
+    const float pv = i < r ? ap[t] : 0.f;
+    const int64_t o = bidx * (C * C) + (int64_t)r * C + i;
+    w.P[o] = pv;
+    w.A[o] = sm.beta[r] * pv;
+    w.M[o] = i <= r ? am[t] : 0.f;
+  }
+}
+
+__global__ void __launch_bounds__(256) bwd_pm_kernel(BwdParams p, BwdTiles w) {
+  __shared__ PmSmem sm;
+  const int64_t bidx = blockIdx.x;
+  int h, valid, n;
+  int64_t bos, c;
+  bwd_chunk_rows(p, bidx, h, bos, c, valid, n);
+  const int t = threadIdx.x;
+  const int HD = p.H * D;
+  if (t < C) sm.beta[t] = w.beta[bidx * C + t];
+  // thread t: channels 4 (t % 32) .. +3, rows 8 (t / 32) .. +7; every load is issued
+  // before the first use (G as formed by the prep, k and q from the inputs)
+  const int cg = t & 31, rg = t >> 5, c4 = 4 * cg;
+  const float* Gb = w.G + bidx * (C * D);
+  float4 Gv[8], Xv[5];
+  uint2 kv[8], qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * rg + i;
+    Gv[i] = *reinterpret_cast<const float4*>(Gb + r * D + c4);
+    const bool in = r < valid;
+    const int64_t row = (bos + c * C + (in ? r : 0)) * (int64_t)HD + (int64_t)h * D + c4;
+    kv[i] = in ? *reinterpret_cast<const uint2*>(p.k + row) : make_uint2(0u, 0u);
+    qv[i] = in ? *reinterpret_cast<const uint2*>(p.q + row) : make_uint2(0u, 0u);
+  }
+  Xv[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int b = 1; b <= 4; ++b) Xv[b] = *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
+  if (t < 32) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) *reinterpret_cast<float4*>(&sm.X[b][c4]) = Xv[b];
+  }
+  {
+    const int b = rg >> 1;  // the 16-row block of this thread's rows
+    const float xb[4] = {Xv[b].x, Xv[b].y, Xv[b].z, Xv[b].w};
+    const float xe[4] = {Xv[b + 1].x, Xv[b + 1].y, Xv[b + 1].z, Xv[b + 1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * rg + i;
+      const float g4[4] = {Gv[i].x, Gv[i].y, Gv[i].z, Gv[i].w};
+      const float kf[4] = {bf2f_u16(kv[i].x & 0xffff), bf2f_u16(kv[i].x >> 16),
+                           bf2f_u16(kv[i].y & 0xffff), bf2f_u16(kv[i].y >> 16)};
+      const float qf[4] = {bf2f_u16(qv[i].x & 0xffff), bf2f_u16(qv[i].x >> 16),
+                           bf2f_u16(qv[i].y & 0xffff), bf2f_u16(qv[i].y >> 16)};
+      float kF[4], qF[4], kH[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
+        kF[e] = kf[e] * F;
+        qF[e] = qf[e] * F;
+        kH[e] = kf[e] * H;
+      }
+      *reinterpret_cast<float4*>(&sm.kF[r][c4]) = make_float4(kF[0], kF[1], kF[2], kF[3]);
+      *reinterpret_cast<float4*>(&sm.qF[r][c4]) = make_float4(qF[0], qF[1], qF[2], qF[3]);
+      *reinterpret_cast<float4*>(&sm.kH[r][c4]) = make_float4(kH[0], kH[1], kH[2], kH[3]);
+    }
+  }
+  __syncthreads();  // the block references in LDS
+  for (int x = t; x < kPairs * D; x += 256) {
+    const int pr = x / D, cc = x % D;
+    const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+    const int ib = pr - rb * (rb + 1) / 2;
+    sm.wf[pr][cc] = expf(sm.X[rb][cc] - sm.X[ib + 1][cc]);
+  }
+  // blocks above the diagonal
+  for (int x = t; x < C * C; x += 256) {
+    const int r = x / C, i = x % C;
+    if ((i >> 4) > (r >> 4)) {
+      const int64_t o = bidx * (C * C) + x;
+      w.P[o] = 0.f;
+      w.A[o] = 0.f;
+      w.M[o] = 0.f;
+    }
+  }
+  __syncthreads();
+  // pairs (0,0) (1,0) (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3)
+  switch (__builtin_amdgcn_readfirstlane(t >> 6)) {
+    case 0: pm_pair(sm, w, bidx, 0); pm_pair(sm, w, bidx, 1); pm_pair(sm, w, bidx, 8); break;
+    case 1: pm_pair(sm, w, bidx, 2); pm_pair(sm, w, bidx, 3); pm_pair(sm, w, bidx, 4); break;
+    case 2: pm_pair(sm, w, bidx, 5); pm_pair(sm, w, bidx, 6); break;
+    default: pm_pair(sm, w, bidx, 7); pm_pair(sm, w, bidx, 9); break;
+  }
+}
+
+// ---------------------------------------------------------------- gated triangle products
+// The gradient terms that pair exp(G_r) with exp(-G_i), per channel c:
+//   dqi_r = sum_{i <= r} dM_ri k_i exp(G_r - G_i)          (dM kh, through qg's gate)
+//   dka_r = beta_r sum_{i < r} dA_ri k_i exp(G_r - G_i)    (diag(b) dA kh, through kg's gate)
+//   dkh_i = sum_{r >= i} (dM_ri q_r + dA_ri beta_r k_r) exp(G_r - G_i)   (dkh through kh)
+// With the block references, dqi_r = F_r sum_{ib <= rb} w(rb, ib) [dM_(rb,ib) (k H)_ib]_r and
+// dkh_i = H_i sum_{rb >= ib} w(rb, ib) [dM_(rb,ib)^T (q F)_rb + dA_(rb,ib)^T (b k F)_rb]_i, each
+// bracket a 16 x 16 x 16 product on the fp32 matrix cores (dM, dA are already masked).  One
+// workgroup per (batch, 32-channel slice); wave v forms row block v of dqi and dka and row
+// block v of dkh, five block products of each kind per wave.
+constexpr int GSL = 32, GSS = GSL + 4;
+struct alignas(16) GatedSmem {
+  float kH[C][GSS];
+  float qF[C][GSS];
+  float bkF[C][GSS];
+  float G[C][GSS];
+  float dM[C][C + 4];
+  float dA[C][C + 4];
+  float wf[kPairs][GSL];
+  float X[5][GSL];
+  float beta[C];
+};
+
+__global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w) {
+  __shared__ GatedSmem sm;
+  const int64_t bidx = blockIdx.x / (D / GSL);
+  const int c0 = (blockIdx.x % (D / GSL)) * GSL;
+  int h, valid, n;
+  int64_t bos, c;
+  bwd_chunk_rows(p, bidx, h, bos, c, valid, n);
+  if (valid == 0) return;  // the finalize writes nothing for this batch
+  const int t = threadIdx.x;
+  const int HD = p.H * D;
+  const float* Gb = w.G + bidx * (C * D) + c0;
+  // every load first: thread t takes channels 4 (t % 8) .. +3 of the slice and rows
+  // 2 (t / 8) .. +1 (G, k, q), and 16 entries each of dM and dA
+  const int cg = t & 7, rg = t >> 3, c4 = 4 * cg;
+  const float bt = t < C ? w.beta[bidx * C + t] : 0.f;
+  float4 Gv[2], Xv[5], mv[4], av[4];
+  uint2 kv[2], qv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 2 * rg + i;
+    Gv[i] = *reinterpret_cast<const float4*>(Gb + r * D + c4);
+    const bool in = r < valid;
+    const int64_t row = (bos + c * C + (in ? r : 0)) * (int64_t)HD + (int64_t)h * D + c0 + c4;
+    kv[i] = in ? *reinterpret_cast<const uint2*>(p.k + row) : make_uint2(0u, 0u);
+    qv[i] = in ? *reinterpret_cast<const uint2*>(p.q + row) : make_uint2(0u, 0u);
+  }
+  Xv[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int b = 1; b <= 4; ++b) Xv[b] = *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = t + 256 * j, r = x >> 4, i4 = (x & 15) * 4;
+    mv[j] = *reinterpret_cast<const float4*>(w.dM + bidx * (C * C) + r * C + i4);
+    av[j] = *reinterpret_cast<const float4*>(w.dA + bidx * (C * C) + r * C + i4);
+  }
+  if (t < C) sm.beta[t] = bt;
+  if (t < 8) {
+#pragma unroll
+    for (int b = 0; b < 5; ++b) *reinterpret_cast<float4*>(&sm.X[b][c4]) = Xv[b];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = t + 256 * j, r = x >> 4, i4 = (x & 15) * 4;
+    *reinterpret_cast<float4*>(&sm.dM[r][i4]) = mv[j];
+    *reinterpret_cast<float4*>(&sm.dA[r][i4]) = av[j];
+  }
+  __syncthreads();  // beta
+  {
+    const int b = rg >> 3;  // the 16-row block of this thread's rows
+    const float xb[4] = {Xv[b].x, Xv[b].y, Xv[b].z, Xv[b].w};
+    const float xe[4] = {Xv[b + 1].x, Xv[b + 1].y, Xv[b + 1].z, Xv[b + 1].w};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 2 * rg + i;
+      const float g4[4] = {Gv[i].x, Gv[i].y, Gv[i].z, Gv[i].w};
+      const float kf[4] = {bf2f_u16(kv[i].x & 0xffff), bf2f_u16(kv[i].x >> 16),
+                           bf2f_u16(kv[i].y & 0xffff), bf2f_u16(kv[i].y >> 16)};
+      const float qf[4] = {bf2f_u16(qv[i].x & 0xffff), bf2f_u16(qv[i].x >> 16),
+                           bf2f_u16(qv[i].y & 0xffff), bf2f_u16(qv[i].y >> 16)};
+      const float br = sm.beta[r];
+      float kH[4], qF[4], bkF[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
+        kH[e] = kf[e] * H;
+        qF[e] = qf[e] * F;
+        bkF[e] = br * kf[e] * F;
+      }
+      *reinterpret_cast<float4*>(&sm.G[r][c4]) = Gv[i];
+      *reinterpret_cast<float4*>(&sm.kH[r][c4]) = make_float4(kH[0], kH[1], kH[2], kH[3]);
+      *reinterpret_cast<float4*>(&sm.qF[r][c4]) = make_float4(qF[0], qF[1], qF[2], qF[3]);
+      *reinterpret_cast<float4*>(&sm.bkF[r][c4]) = make_float4(bkF[0], bkF[1], bkF[2], bkF[3]);
+    }
+    for (int x = t; x < kPairs * GSL; x += 256) {
+      const int pr = x / GSL, ch = x % GSL;
+      const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+      const int ib = pr - rb * (rb + 1) / 2;
+      sm.wf[pr][ch] = expf(sm.X[rb][ch] - sm.X[ib + 1][ch]);
+    }
+  }
+  __syncthreads();
+  const int v = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63, q4 = lane >> 4, m16 = lane & 15;
+  const bg_f32x4 z4 = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- row form: rows of block rb = v
+  {
+    const int rb = v;
+    bg_f32x4 aq[2] = {z4, z4}, ak[2] = {z4, z4};
+    for (int ib = 0; ib <= rb; ++ib) {
+      bg_f32x4 tq[2] = {z4, z4}, tk[2] = {z4, z4};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int i = 16 * ib + 4 * s4 + q4;  // the contraction row of this lane
+        const float am = sm.dM[16 * rb + m16][i], aa = sm.dA[16 * rb + m16][i];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float bk = sm.kH[i][16 * ct + m16];
+          tq[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(am, bk, tq[ct], 0, 0, 0);
+          tk[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa, bk, tk[ct], 0, 0, 0);
+        }
+      }
+      const int pr = bwd_pair(rb, ib);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float wv = sm.wf[pr][16 * ct + m16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aq[ct][e] = fmaf(wv, tq[ct][e], aq[ct][e]);
+          ak[ct][e] = fmaf(wv, tk[ct][e], ak[ct][e]);
+        }
+      }
+    }
+    // lane holds rows 16 rb + 4 q4 + e, channel 16 ct + m16 of the slice
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * q4 + e, cc = 16 * ct + m16;
+        const float F = expf(sm.G[r][cc] - sm.X[rb][cc]);
+        const int64_t o = bidx * (C * D) + (int64_t)r * D + c0 + cc;
+        w.MtdO[o] = F * aq[ct][e];               // dqi
+        w.dU[o] = sm.beta[r] * F * ak[ct][e];    // dka
+      }
+  }
+  // ---- column form: rows of block ib = v
+  {
+    const int ib = v;
+    bg_f32x4 ah[2] = {z4, z4};
+    for (int rb = ib; rb < 4; ++rb) {
+      bg_f32x4 th[2] = {z4, z4};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 16 * rb + 4 * s4 + q4;  // the contraction row of this lane
+        const float am = sm.dM[r][16 * ib + m16], aa = sm.dA[r][16 * ib + m16];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          th[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(am, sm.qF[r][16 * ct + m16], th[ct], 0, 0, 0);
+          th[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa, sm.bkF[r][16 * ct + m16], th[ct], 0, 0, 0);
+        }
+      }
+      const int pr = bwd_pair(rb, ib);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float wv = sm.wf[pr][16 * ct + m16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ah[ct][e] = fmaf(wv, th[ct][e], ah[ct][e]);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * ib + 4 * q4 + e, cc = 16 * ct + m16;
+        const float H = expf(sm.X[ib + 1][cc] - sm.G[i][cc]);
+        w.dkh[bidx * (C * D) + (int64_t)i * D + c0 + cc] = H * ah[ct][e];
+      }
   }
 }
 
@@ -483,23 +830,31 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
   __shared__ float rowsum[D];
   __shared__ float dbs[C];
   // per row: dG, dq, dk, dv; per channel: dG_last pieces
+  // The gradients through each gate, ungated:
+  //   dq  = (dO' S^T) Gam + dqi                       (dqg Gam)
+  //   dkg = -diag(b) (dY S^T) Gam + dka                (dkg Gam)
+  //   dkh                                              (dkh / Gam, formed ungated)
+  //   dkp = (U dSn^T) exp(G_last - G)                  (dkp gam / Gam)
+  // so that dqg qg = dq q, dkg kg = dkg' k, dkh kh = dkh' k and dkp kp = dkp' k.
   float glast = 0.f;
+  const float Glast = w.G[tb + (C - 1) * D + ch];
   for (int r = half; r < C; r += 2) {
     const int64_t o = tb + r * D + ch;
     const float G = w.G[o];
-    const float e = expf(G), ei = expf(-G);
-    const float gam = w.gam[bidx * D + ch];
-    const float dqg = w.dqg[o], dkg = w.dkg[o], dkh = w.dkh[o], dkp = w.dkp[o];
+    const float e = expf(G), el = expf(Glast - G);
+    const float dq = w.dqg[o] * e + w.MtdO[o];
+    const float dkg = w.dkg[o] * e + w.dU[o];
+    const float dkh = w.dkh[o];
+    const float dkp = w.dkp[o] * el;
     // k and q straight from the inputs (exact in fp32; zero past the sequence's end)
     const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
     const float kf = r < valid ? bf2f_u16(p.k[row]) : 0.f;
     const float qf = r < valid ? bf2f_u16(p.q[row]) : 0.f;
-    const float kp = kf * ei * gam;
-    dGs[r][ch] = dqg * qf * e + dkg * kf * e - dkh * kf * ei - dkp * kp;
-    glast += dkp * kp;
+    dGs[r][ch] = dq * qf + (dkg - dkh - dkp) * kf;
+    glast += dkp * kf;
     if (r < valid) {
-      p.dq[row] = dqg * e;
-      p.dk[row] = dkg * e + dkh * ei + dkp * gam * ei;
+      p.dq[row] = dq;
+      p.dk[row] = dkg + dkh + dkp;
       p.dv[row] = beta[r] * w.dY[o];
     }
   }
@@ -623,16 +978,8 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   const int64_t t1 = C * D, t2 = C * C, t3 = D * D, tf = D * C;
   // chunk tiles
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(NB), dim3(256), 0, s, p, w);
-  // A = strict_lower(diag(b) kg kh^T), P = strict_lower(kg kh^T), M = lower_incl(qg kh^T)
-  {
-    GemmArgs p1 = mm(C, C, D, w.kg, t1, D, w.kh, t1, D, w.P, t2, C, NB);
-    p1.mask = 1;
-    GemmArgs a1 = p1;
-    a1.C = w.A; a1.rs = w.beta; a1.srs = C;
-    GemmArgs m2 = mm(C, C, D, w.qg, t1, D, w.kh, t1, D, w.M, t2, C, NB);
-    m2.mask = 2;
-    hipLaunchKernelGGL(bgemm_shared_b_kernel, dim3(1, 1, NB), dim3(256), 0, s, p1, a1, m2);
-  }
+  // P = strict_lower(K K^T gated), A = diag(b) P, M = lower_incl(Q K^T gated)
+  hipLaunchKernelGGL(bwd_pm_kernel, dim3(NB), dim3(256), 0, s, p, w);
   hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
   // R = V - kg S;  U = T diag(b) R
   {
@@ -668,17 +1015,14 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
       GemmArgs none{};
       hipLaunchKernelGGL(bgemm_shared_b_kernel, dim3(1, 1, NB), dim3(256), 0, s, dm, none, da);
     }
-    gemm2<false, true, false, false>(mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB),  // dO' S^T
-                                     mm(C, D, C, w.dM, t2, C, w.kh, t1, D, nullptr, 0, 0, NB),  // + dM kh
-                                     1.f, s);
+    gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
     gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
-    GemmArgs k1 = mm(C, D, C, w.dA, t2, C, w.kh, t1, D, w.dkg, t1, D, NB);  // diag(b)(dA kh - dY S^T)
-    k1.rs = w.beta; k1.srs = C;
-    gemm2<false, false, false, true>(k1, mm(C, D, D, w.dY, t1, D, w.S, t3, D, nullptr, 0, 0, NB), -1.f, s);
-    GemmArgs h2 = mm(C, D, C, w.dA, t2, C, w.kg, t1, D, nullptr, 0, 0, NB);  // + dA^T diag(b) kg
-    h2.ks = w.beta; h2.sks = C;
-    gemm2<true, false, true, false>(mm(C, D, C, w.dM, t2, C, w.qg, t1, D, w.dkh, t1, D, NB), h2,  // dM^T qg
-                                    1.f, s);
+    GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
+    k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
+    gemm(false, true, k1, s);
+    // dM kh, diag(b) dA kh and dkh through the gates, with block references: into the
+    // tiles MtdO and dU (free once dU and dY exist) and dkh
+    hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
   }
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
   return hipGetLastError();

@@ -144,3 +144,30 @@ def test_bwd_full_size_sampled_heads():
     print("    " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
     for k, e in errs.items():
         assert e <= TOL, f"{k} rel err {e:.3e}"
+
+
+def test_bwd_strong_decay_edge_of_range():
+    """g down to -5 (the forward's documented limit) and up to -1e-4: the per-channel
+    decay over a 64-token chunk reaches ~300 in natural log, far past what a chunk-wide
+    exp(-G) could hold in fp32; the backward's block references keep every factor finite."""
+    announce("bwd strong decay g in [-5, -1e-4]")
+    x = random_inputs(1, 640, 2, seed=84, device=DEV, g_lo=1e-4, g_hi=5.0, init_state="fp32")
+    do, dsT = upstream(x, 85)
+    check_bwd(x, do, dsT)
+
+
+def test_bwd_mixed_decay_chunks():
+    """Chunks with strong decay on a quarter of the channels (-g in [1.5, 4.5]) among
+    chunks of ordinary decay, within one sequence, with varlen packing."""
+    lengths = [600, 77]
+    announce(f"bwd mixed decay regimes, varlen {lengths}")
+    x = random_inputs(1, sum(lengths), 2, seed=86, device=DEV, init_state="bf16", lengths=lengths)
+    gen = torch.Generator().manual_seed(87)
+    g = x["g"].cpu()
+    strong = -(1.5 + 3.0 * torch.rand(g.shape, generator=gen))
+    chan = torch.rand(1, 1, g.shape[2], g.shape[3], generator=gen) < 0.25
+    for a, b in ((64, 128), (256, 320), (500, 640)):
+        g[:, a:b] = torch.where(chan, strong[:, a:b], g[:, a:b])
+    x["g"] = g.to(DEV)
+    do, dsT = upstream(x, 88)
+    check_bwd(x, do, dsT)
