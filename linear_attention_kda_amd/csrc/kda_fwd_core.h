@@ -926,8 +926,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 #pragma unroll
           for (int ks = 0; ks <= (rt >> 1); ++ks) {
             const __bf16* rowp = &sm.mm[r * QS + 32 * ks + 4 * q4];
-            if ((rt & 1) == 0 && ks == (rt >> 1))  // M block (rt, rt + 1) is zero: 16-wide k
-              o = mfma16(U[2 * ks][jt], ld4(rowp), o);
+            // M block (rt, rt + 1) is zero: its half of the k range is zero in both
+            // operands (the LDS above the diagonal is never written).  The chain keeps
+            // one MFMA shape: a 16x16x16 issued right behind a 16x16x32 whose result it
+            // accumulates onto has given wrong sums on gfx950.
+            if ((rt & 1) == 0 && ks == (rt >> 1))
+              o = mfma32(cat(U[2 * ks][jt], bf16x4{}), cat(ld4(rowp), bf16x4{}), o);
             else
               o = mfma32(cat(U[2 * ks][jt], U[2 * ks + 1][jt]), ld2x4(rowp, rowp + 16), o);
           }

@@ -4,9 +4,9 @@ scalar-gate oracle, through the C ABI.
 The gate is one log-decay per token and head; the inputs reuse the KDA recipe
 and take the first channel of its per-channel gate as the scalar gate (same
 distribution).  Bar: max|x - x_ref| / max|x_ref| <= 1e-2 for outputs and final
-states.  One case also checks that the scalar-gate path gives bit-identical
-results to kda_fwd fed the same gate on every channel (the kernels after the
-gate load are shared).
+states, and per (sequence, head) for the 64K varlen workload.  One case also
+checks that the scalar-gate path gives bit-identical results to kda_fwd fed the
+same gate on every channel (the kernels after the gate load are shared).
 """
 import sys
 
@@ -113,6 +113,7 @@ def test_gdn_is_kda_with_the_gate_on_every_channel(monkeypatch, seg_min):
     announce(f"gdn vs kda with repeated gate, seg_min={seg_min}")
     x = gdn_inputs(1, 700, 3, seed=62)
     out_g, fin_g = run_gdn(x)
+    check_gdn(x, out_g, fin_g)
     g_rep = x["gs"][..., None].expand(-1, -1, -1, 128).contiguous()
     fin_k = torch.empty_like(fin_g)
     out_k, fin_k = binding.fwd(x["q"], x["k"], x["v"], g_rep, x["beta"], x["scale"],
@@ -120,6 +121,44 @@ def test_gdn_is_kda_with_the_gate_on_every_channel(monkeypatch, seg_min):
     torch.cuda.synchronize()
     assert torch.equal(out_g, out_k)
     assert torch.equal(fin_g, fin_k)
+
+
+def test_gdn_strong_decay():
+    """Scalar gate down to -5 per token: the chunk's decay reaches ~300 (natural log),
+    so the 16-row block references carry the tile products."""
+    announce("gdn strong decay g in [-5, -1e-4]")
+    x = random_inputs(1, 640, 2, seed=64, device=DEV, g_lo=1e-4, g_hi=5.0, init_state="fp32")
+    x["gs"] = x["g"][..., 0].contiguous()
+    out, fin = run_gdn(x)
+    check_gdn(x, out, fin)
+
+
+def test_gdn_varlen_workload_all_heads():
+    """The scalar-gate bench workload: 16 packed sequences, 65,536 tokens, H = 32, bf16
+    states, every head, with the per-(sequence, head) bar."""
+    from linear_attention_kda_amd.workloads import make_inputs
+    announce("gdn 64K varlen workload, all heads")
+    x = make_inputs(2, DEV)
+    x["gs"] = x["g"][..., 0].contiguous()
+    out, fin = run_gdn(x)
+    check_gdn(x, out, fin)
+    o_ref, S_ref = oracle.gdn_fwd(x["q"].cpu(), x["k"].cpu(), x["v"].cpu(), x["gs"].cpu(),
+                                  x["beta"].cpu(), x["scale"], x["initial_state"].cpu(),
+                                  cu_seqlens=x["cu_seqlens"].cpu())
+    o = host(out)
+    cu = [int(c) for c in x["cu_seqlens"].cpu()]
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        a, b = cu[n], cu[n + 1]
+        if b <= a:
+            continue
+        num = np.abs(o[0, a:b] - o_ref[0, a:b]).max(axis=(0, 2))
+        den = np.abs(o_ref[0, a:b]).max(axis=(0, 2))
+        worst = max(worst, float((num / np.maximum(den, 1e-30)).max()))
+    f = host(fin)
+    ws = float((np.abs(f - S_ref).max(axis=(2, 3)) / np.maximum(np.abs(S_ref).max(axis=(2, 3)), 1e-30)).max())
+    print(f"    worst per-(sequence, head): out {worst:.3e}, state {ws:.3e}", flush=True)
+    assert worst <= TOL and ws <= TOL
 
 
 def test_gdn_full_size_sampled_heads():
