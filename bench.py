@@ -329,7 +329,8 @@ def dim_bench(wid: int, d: int, steps: int, warmup: int):
             "workspace_bytes": binding.dim_workspace_bytes(N, w.tokens, H, d),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "kda_fwd call at d=%d: dim_prep_kernel + dim_state_kernel" % d,
+                         "kernel": ("kda_fwd call at d=64: kda_fwd_kernel<1, false, 64>" if d == 64 else
+                                    "kda_fwd call at d=%d: dim_prep_kernel + dim_state_kernel" % d),
                          "algorithmic_bytes": nbytes}}
 
 

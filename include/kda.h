@@ -116,13 +116,15 @@ typedef enum {
  *             sequence (varlen with cu_seqlens[num_seqs] < T) are not written.
  *  stream     hipStream_t to launch on (NULL = null stream).
  *
- * d = 64 and d = 256 run as two launches: every (chunk, head) first writes a
- * record of its chunk-local operands (gated keys and queries, the transposed
- * state-update operand, (I + A)^-1 diag(beta), the masked Q K^T and the chunk
- * decay) into a workspace of kda_dim_workspace_bytes() bytes from the library's
- * pool, then one workgroup per (sequence, head, value slice) walks the chunks in
- * order.  These sizes never split sequences, and the 16-token range limit on g
- * above applies to them as well.
+ * d = 64 runs on the d = 128 kernel with the key channels past 64 read as zero,
+ * one workgroup per (sequence, head) and no workspace.  d = 256 runs as two
+ * launches: every (chunk, head) first writes a record of its chunk-local
+ * operands (gated keys and queries, the transposed state-update operand,
+ * (I + A)^-1 diag(beta), the masked Q K^T and the chunk decay) into a workspace
+ * of kda_dim_workspace_bytes() bytes from the library's pool, then one
+ * workgroup per (sequence, head, value slice) walks the chunks in order.  These
+ * sizes never split sequences, and the 16-token range limit on g above applies
+ * to them as well.
  */
 kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float scale, const void* initial_state, int initial_dtype, void* final_state,
@@ -141,7 +143,8 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
  *            of the later segments' chunks); sequences are split only as far
  *            as those fit, so every size runs, very long ones in fewer and
  *            longer segments than kda_fwd would use;
- *   d = 64, 256: the per-chunk records must fit (slots x H x record bytes, see
+ *   d = 64:  no workspace;
+ *   d = 256: the per-chunk records must fit (slots x H x record bytes, see
  *            kda_dim_workspace_bytes); larger calls return KDA_ERR_WORKSPACE
  *            before any launch.
  * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU
@@ -319,8 +322,9 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
 
 /* Workspace bytes kda_fwd / kda_gdn_fwd take at head dimension d = 64 or 256
  * for N sequences over `rows` packed rows (T with cu_seqlens, else B*T) of H
- * heads: one record per (chunk slot, head), N + ceil(rows / 64) + 1 slots
- * (-1 for N <= 0, rows < 0, H <= 0 or another d).  Host only. */
+ * heads: none at d = 64; at d = 256 one record per (chunk slot, head),
+ * N + ceil(rows / 64) + 1 slots (-1 for N <= 0, rows < 0, H <= 0 or another d).
+ * Host only. */
 int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H

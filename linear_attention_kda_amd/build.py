@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("kda_api.cpp", "kda_fwd_kernel.hip", "kda_gdn_kernel.hip", "kda_fwd_dim.hip",
-            "kda_decode_kernel.hip", "kda_bwd.hip", "kda_noalloc.hip")]
+            "kda_decode_kernel.hip", "kda_bwd.hip", "kda_noalloc.hip", "kda_fwd_hd64_kernel.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code; the host pass

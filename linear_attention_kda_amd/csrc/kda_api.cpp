@@ -193,6 +193,15 @@ LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus,
   return lp;
 }
 
+// One workgroup per (sequence, head), no value split and no sequence splitting.
+LaunchPlan single_slice_plan(int32_t N, int32_t H) {
+  LaunchPlan lp{};
+  lp.nsplit = 1;
+  lp.seg_min = seg_min_chunks();
+  lp.workgroups = ((int64_t)N * H + 7) / 8 * 8;
+  return lp;
+}
+
 // Library-owned stream-ordered pool for the workspaces, one per device.  It keeps
 // up to kPoolKeepBytes reserved between calls (so a repeated call of the same
 // size costs no allocation from the driver) and hands anything above that back
@@ -229,8 +238,8 @@ hipError_t workspace_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// Head dimensions 64 and 256: per-chunk records in a workspace from the pool,
-// then the serial state pass (no sequence splitting).
+// Head dimension 256: per-chunk records in a workspace from the pool, then the
+// serial state pass (no sequence splitting).
 kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, float scale, const void* initial_state,
                         int initial_dtype, void* final_state, int final_dtype,
@@ -305,14 +314,18 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
                            g_scalar);
   if (st != KDA_OK) return st;
   if (T == 0 && final_state == nullptr) return KDA_OK;  // nothing observable to compute
-  if (K != KDA_HEAD_DIM)
+  if (K == 256)
     return fwd_dim_impl(q, k, v, g, beta, scale, initial_state, initial_dtype, final_state,
                         final_dtype, cu_seqlens, N, B, T, H, K, out, stream, g_scalar, ext);
 
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const LaunchPlan lp = make_plan(N, T, H, cu_seqlens != nullptr, cus, ext ? ext->bytes : 0);
+  // K = 64 runs the fused kernel in one 64-column slice per (sequence, head), without
+  // splitting sequences: no workspace
+  const LaunchPlan lp = K == KDA_HEAD_DIM
+      ? make_plan(N, T, H, cu_seqlens != nullptr, cus, ext ? ext->bytes : 0)
+      : single_slice_plan(N, H);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
 
   kda::Params p{};
@@ -332,6 +345,7 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   p.scale = scale;
   p.nseq = N;
   p.H = H;
+  p.dk = K;
   p.cus = cus;
   p.seg_min = lp.seg_min;
   void* ws = nullptr;
@@ -359,9 +373,9 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   }
   if (log_enabled())
     std::fprintf(stderr,
-                 "[kda] launch: %s N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
+                 "[kda] launch: %s D=%d N=%d H=%d T=%lld value_splits=%d cus=%d varlen=%d "
                  "segment_slots=%d fixup_units=%d workspace=%zu%s\n",
-                 g_scalar ? "gdn" : "kda", N, H, (long long)T, lp.nsplit, cus,
+                 g_scalar ? "gdn" : "kda", K, N, H, (long long)T, lp.nsplit, cus,
                  cu_seqlens != nullptr, lp.emax, lp.ucap, lp.workspace,
                  ext ? " (static scratch)" : "");
   const hipError_t err = kda::launch_fwd(p, lp.nsplit, hs);
@@ -616,7 +630,7 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
 
 int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D) {
   if (n_sequences <= 0 || rows < 0 || H <= 0 || (D != 64 && D != 256)) return -1;
-  if (rows == 0) return 0;
+  if (rows == 0 || D == 64) return 0;
   return kda::dim_slots(n_sequences, rows) * H * (int64_t)kda::dim_record_bytes(D);
 }
 
@@ -702,6 +716,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     p.cus = cus;
     p.seg_min = seg_min_chunks();
     p.ckpt = w.S;
+    p.dk = KDA_HEAD_DIM;
     const int nsplit = (int64_t)N * H >= cus ? 1 : 2;
     err = kda::launch_fwd(p, nsplit, hs);
     if (err == hipSuccess) {

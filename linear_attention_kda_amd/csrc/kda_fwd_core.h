@@ -173,16 +173,17 @@ __device__ __forceinline__ int pair_ib(int p) { return p - (pair_rb(p) * (pair_r
 //  * block references: rows Kr = K F (A) and Qr = Q F (M), column Kh = K H
 //    scaled per channel by exp(X_rb - X_{ib+1}) (skipped for ib == rb - 1,
 //    where the factor is 1).
-template <int NV, int PR, bool FAST>
+template <int NV, int PR, bool FAST, int DK>
 __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16) {
   constexpr int rb = PR < 1 ? 0 : PR < 3 ? 1 : PR < 6 ? 2 : 3;
   constexpr int ib = PR - rb * (rb + 1) / 2;
   constexpr bool scaled = !FAST && ib != rb - 1;
   const __bf16* krow = FAST ? sm.kg : sm.kr;
   const __bf16* qrow = FAST ? sm.qg : sm.qr;
-  bf16x8 cf[4], kf[4], qf[4];
+  constexpr int KS = DK / 32;  // 32-channel slices (channels past DK are zero)
+  bf16x8 cf[KS], kf[KS], qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const int c0 = 32 * ks + 8 * q4;
     const __bf16* cp = &sm.kh[(16 * ib + m16) * TS + c0];
     const __bf16* kp = &krow[(16 * rb + m16) * TS + c0];
@@ -193,7 +194,7 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16) {
   }
   if constexpr (scaled) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 32 * ks + 8 * q4;
       const float4 f0 = *reinterpret_cast<const float4*>(&sm.pf[PR * D + c0]);
       const float4 f1 = *reinterpret_cast<const float4*>(&sm.pf[PR * D + c0 + 4]);
@@ -205,7 +206,7 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16) {
   f32x4 ta = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 tm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     ta = mfma32(cf[ks], kf[ks], ta);  // D[i][r]
     tm = mfma32(cf[ks], qf[ks], tm);
   }
@@ -228,26 +229,26 @@ __device__ __forceinline__ void tile_pair(Smem<NV>& sm, int q4, int m16) {
   *reinterpret_cast<uint2*>(&sm.mm[r * QS + 16 * ib + 4 * q4]) = pack4(vm[0], vm[1], vm[2], vm[3]);
 }
 
-template <int NV, bool FAST>
+template <int NV, bool FAST, int DK>
 __device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m16) {
   switch (wave) {
     case 0:
-      tile_pair<NV, 0, FAST>(sm, q4, m16);
-      tile_pair<NV, 1, FAST>(sm, q4, m16);
-      tile_pair<NV, 8, FAST>(sm, q4, m16);
+      tile_pair<NV, 0, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 1, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 8, FAST, DK>(sm, q4, m16);
       break;
     case 1:
-      tile_pair<NV, 2, FAST>(sm, q4, m16);
-      tile_pair<NV, 3, FAST>(sm, q4, m16);
-      tile_pair<NV, 4, FAST>(sm, q4, m16);
+      tile_pair<NV, 2, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 3, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 4, FAST, DK>(sm, q4, m16);
       break;
     case 2:
-      tile_pair<NV, 5, FAST>(sm, q4, m16);
-      tile_pair<NV, 6, FAST>(sm, q4, m16);
+      tile_pair<NV, 5, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 6, FAST, DK>(sm, q4, m16);
       break;
     default:
-      tile_pair<NV, 7, FAST>(sm, q4, m16);
-      tile_pair<NV, 9, FAST>(sm, q4, m16);
+      tile_pair<NV, 7, FAST, DK>(sm, q4, m16);
+      tile_pair<NV, 9, FAST, DK>(sm, q4, m16);
       break;
   }
 }
@@ -257,14 +258,14 @@ __device__ __forceinline__ void tile_pairs(Smem<NV>& sm, int wave, int q4, int m
 // the seven pairs that scale their column operand spread two per wave.  The
 // pairs of a wave are independent straight-line code, so their loads and
 // products overlap.
-template <int NV>
+template <int NV, int DK>
 __device__ __forceinline__ void build_tiles(Smem<NV>& sm, int wave, int q4_, int m16_) {
   // lane indices through an empty asm: the tile addresses are then formed here on
   // every call instead of being kept live (or spilled) across the whole loop
   int q4 = q4_, m16 = m16_;
   asm volatile("" : "+v"(q4), "+v"(m16));
-  if (__builtin_amdgcn_readfirstlane(sm.chunk_ref)) tile_pairs<NV, true>(sm, wave, q4, m16);
-  else tile_pairs<NV, false>(sm, wave, q4, m16);
+  if (__builtin_amdgcn_readfirstlane(sm.chunk_ref)) tile_pairs<NV, true, DK>(sm, wave, q4, m16);
+  else tile_pairs<NV, false, DK>(sm, wave, q4, m16);
 }
 
 struct Work {
@@ -344,16 +345,16 @@ struct ChunkSrc {
   __amdgpu_buffer_rsrc_t g, q, k, v, b;
 };
 
-template <bool GS>
+template <bool GS, int DK>
 __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, int ch) {
   const int64_t tok0 = w.bos + (int64_t)ch * C;
   const int64_t rest = w.len - (int64_t)ch * C;
   // chunks past the end of the sequence get empty descriptors: every load is zero
   const int valid = rest <= 0 ? 0 : rest < C ? (int)rest : C;
-  const int HD = p.H * D;
-  const int64_t base = tok0 * HD + (int64_t)w.h * D;
+  const int HD = p.H * DK;
+  const int64_t base = tok0 * HD + (int64_t)w.h * DK;
   ChunkSrc s;
-  // the gate: per channel [rows][H][128], or one value per token and head [rows][H]
+  // the gate: per channel [rows][H][DK], or one value per token and head [rows][H]
   s.g = GS ? rsrc(p.g + tok0 * p.H + w.h, valid * p.H * 4) : rsrc(p.g + base, valid * HD * 4);
   s.q = rsrc(p.q + base, valid * HD * 2);
   s.k = rsrc(p.k + base, valid * HD * 2);
@@ -364,21 +365,32 @@ __device__ __forceinline__ ChunkSrc chunk_src(const Params& p, const Work& w, in
 
 // Prep thread t loads rows 8*rg..8*rg+7, channels 4*cg..4*cg+3 (rg = t/32,
 // cg = t%32), in pieces so that each register set is refilled as soon as the
-// previous chunk has consumed it.
-template <int NV, bool GS>
+// previous chunk has consumed it.  With a head dimension DK < 128 the channels
+// from DK on read as zero: those lanes take an offset past every descriptor's
+// range (2^31: above any range, and with the row offset still below 2^32, since
+// H * DK <= 2^22), so the chunk runs as a 128-channel one whose extra key
+// channels are zero and leave the recurrence unchanged.
+template <int DK>
+__device__ __forceinline__ int chan_offset(int cg, int vo) {
+  if constexpr (DK == 128) return vo;
+  else return 4 * cg < DK ? vo : (int)0x80000000u;
+}
+
+template <int NV, bool GS, int DK>
 __device__ __forceinline__ void load_g(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t) {
   const int rg = t >> 5, cg = t & 31;
   if constexpr (GS) {
     // one gate per row, the same for the thread's four channels
-    const int H = HD / D;
+    const int H = HD / DK;
+    const int vo = chan_offset<DK>(cg, rg * 8 * H * 4);
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) {
-      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.g, rg * 8 * H * 4, r8 * H * 4, 0));
+      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.g, vo, r8 * H * 4, 0));
       R.g[r8] = make_float4(x, x, x, x);
     }
     return;
   }
-  const int vo = rg * 8 * HD * 4 + 16 * cg;  // lane part; the row goes in soffset
+  const int vo = chan_offset<DK>(cg, rg * 8 * HD * 4 + 16 * cg);  // lane part; the row goes in soffset
 #pragma unroll
   for (int r8 = 0; r8 < 8; ++r8) {
     const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(s.g, vo, r8 * HD * 4, 0);
@@ -386,10 +398,10 @@ __device__ __forceinline__ void load_g(ChunkRegs<NV>& R, const ChunkSrc& s, int 
   }
 }
 
-template <int NV>
+template <int NV, int DK>
 __device__ __forceinline__ void load_qk(ChunkRegs<NV>& R, const ChunkSrc& s, int HD, int t, int r8) {
   const int rg = t >> 5, cg = t & 31;
-  const int vo = rg * 8 * HD * 2 + 8 * cg;
+  const int vo = chan_offset<DK>(cg, rg * 8 * HD * 2 + 8 * cg);
   const auto qv = __builtin_amdgcn_raw_buffer_load_b64(s.q, vo, r8 * HD * 2, 0);
   const auto kv = __builtin_amdgcn_raw_buffer_load_b64(s.k, vo, r8 * HD * 2, 0);
   R.q[r8] = make_uint2(qv[0], qv[1]);
@@ -416,19 +428,19 @@ __device__ __forceinline__ void load_beta(ChunkRegs<NV>& R, const ChunkSrc& s, i
   R.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.b, (t & 63) * H * 4, 0, 0));
 }
 
-template <int NV, bool GS>
+template <int NV, bool GS, int DK>
 __device__ __forceinline__ void load_chunk(ChunkRegs<NV>& R, const Params& p, const Work& w,
                                            int ch, int t) {
-  const ChunkSrc s = chunk_src<GS>(p, w, ch);
-  const int HD = p.H * D;
+  const ChunkSrc s = chunk_src<GS, DK>(p, w, ch);
+  const int HD = p.H * DK;
   // the scheduling barriers keep this issue order, which the loop's memory-counter
   // waits assume on entry as well
   load_beta<NV>(R, s, p.H, t);
   __builtin_amdgcn_sched_barrier(0);
-  load_g<NV, GS>(R, s, HD, t);
+  load_g<NV, GS, DK>(R, s, HD, t);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, s, HD, t, r8);
+  for (int r8 = 0; r8 < 8; ++r8) load_qk<NV, DK>(R, s, HD, t, r8);
   __builtin_amdgcn_sched_barrier(0);
   load_v<NV>(R, s, HD, t);
 }
@@ -471,7 +483,7 @@ __device__ __forceinline__ void diag_inverse(Smem<NV>& sm, int b, int q4, int m1
   *reinterpret_cast<float4*>(&sm.li[(16 * b + m16) * LS + 4 * q4]) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-template <int NV, bool GS>
+template <int NV, bool GS, int DK>
 __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const Work& w) {
   const int t = threadIdx.x - (NT - NP);   // 0..255
   const int pw = __builtin_amdgcn_readfirstlane(t >> 6);  // prep wave 0..3 (wave-uniform)
@@ -480,7 +492,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
   const int blk = pw;                      // 16-row block of this thread's rows
   const bool second = (rg & 1) != 0;       // rows 8..15 of the block
   constexpr int VPT = NV / 32;             // value columns per thread
-  const int HD = p.H * D;
+  const int HD = p.H * DK;
   // wave-uniform 0/1 selectors of this wave's block (multiplied in, never branched on)
   const float m0 = blk == 0 ? 1.f : 0.f, m1 = blk == 1 ? 1.f : 0.f;
   const float m2 = blk == 2 ? 1.f : 0.f, m3 = blk == 3 ? 1.f : 0.f;
@@ -502,7 +514,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
   }
 
   ChunkRegs<NV> R;
-  load_chunk<NV, GS>(R, p, w, 0, t);
+  load_chunk<NV, GS, DK>(R, p, w, 0, t);
 
   // Iteration it prepares chunk pc = it + 1 while the state waves run chunk it.
   // The loop body has no branches around its loads, so the memory-counter waits
@@ -548,7 +560,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 
     // ---- phase B: gated operand tiles of chunk pc
     {
-      const ChunkSrc nsrc = chunk_src<GS>(p, w, pc + 1);
+      const ChunkSrc nsrc = chunk_src<GS, DK>(p, w, pc + 1);
       // beta of the next chunk is fetched first: the next phase A waits only for
       // beta and g (the memory counter retires loads in order)
       if (t < C) sm.beta[t] = R.beta;
@@ -734,7 +746,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
           }
         }
       }
-      load_g<NV, GS>(R, nsrc, HD, t);  // the decays of this chunk are consumed
+      load_g<NV, GS, DK>(R, nsrc, HD, t);  // the decays of this chunk are consumed
     }
     __syncthreads();  // (B) the state waves are done with -A, M, K'^T and exp(G_last)
 
@@ -744,7 +756,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       // q, k and v of chunk pc are consumed once V^T is stored; the next chunk's are
       // fetched after this phase's stores, which would otherwise wait behind the
       // issue of the loads
-      const ChunkSrc nsrc = chunk_src<GS>(p, w, pc + 1);
+      const ChunkSrc nsrc = chunk_src<GS, DK>(p, w, pc + 1);
       // V^T (channel-major)
 #pragma unroll
       for (int e = 0; e < VPT; ++e) {
@@ -767,7 +779,7 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
       }
       if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
 #pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV>(R, nsrc, HD, t, r8);
+      for (int r8 = 0; r8 < 8; ++r8) load_qk<NV, DK>(R, nsrc, HD, t, r8);
       load_v<NV>(R, nsrc, HD, t);
     }
     __syncthreads();  // (C) chunk pc fully published
@@ -780,8 +792,10 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 }
 
 // ============================================================================ state waves
-template <int JT>
+template <int JT, int DK>
 __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, const Work& w) {
+  constexpr int CT = DK / 16;   // 16-row tiles of the state (key channels)
+  constexpr int KS = DK / 32;   // 32-channel slices of the products over the key channels
   const int tid = threadIdx.x;
   const int wave = tid >> 6;  // 0..3
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
@@ -789,14 +803,14 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
   const int jl_base = 16 * JT * wave;          // first column within the slice
 
   // Sacc[ct][jt][t] = S[16ct + 4q4 + t][jw_base + 16jt + m16]
-  f32x4 Sacc[8][JT];
+  f32x4 Sacc[CT][JT];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) Sacc[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (w.s0_mode == 3) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -805,21 +819,21 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
   } else if (w.s0_mode == 2) {
     const float* s0 = reinterpret_cast<const float*>(w.s0);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          Sacc[ct][jt][t] = s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16];
+          Sacc[ct][jt][t] = s0[(16 * ct + 4 * q4 + t) * DK + jw_base + 16 * jt + m16];
   } else if (w.s0_mode == 1) {
     const __bf16* s0 = reinterpret_cast<const __bf16*>(w.s0);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16]);
+          Sacc[ct][jt][t] = bf2f(s0[(16 * ct + 4 * q4 + t) * DK + jw_base + 16 * jt + m16]);
   }
 
   for (int it = -1; it < w.nchunks; ++it) {
@@ -831,12 +845,12 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
 
     // ---- phase A: Y = V - (K exp(G)) S -> Z = beta * Y;  O^T = S^T (Q exp(G))^T
     // (the prep waves store -K exp(G) and Q exp(G))
-    if (act && w.ck != nullptr) {  // the state entering this chunk, for the backward pass
+    if (DK == 128 && act && w.ck != nullptr) {  // the state entering this chunk, for the backward pass
       // one lane offset; the row and column-tile terms are scalar offsets
       const auto crs = rsrc(w.ck + (size_t)it * p.H * (D * D), D * D * 4);
       const int lo = ((4 * q4) * D + jw_base + m16) * 4;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
@@ -859,7 +873,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
       // one 32-channel slice of the bf16 state copy at a time (k-slot order of the
       // products), so that only a quarter of it is live
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         bf16x8 Sfrag[JT];
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) Sfrag[jt] = cat(cvt4(Sacc[2 * ks][jt]), cvt4(Sacc[2 * ks + 1][jt]));
@@ -945,7 +959,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
       }
       // S <- Diag(exp(G_last)) S + K'^T U
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         const float4 gc = *reinterpret_cast<const float4*>(&sm.gamc[16 * ct + 4 * q4]);
         const float gv[4] = {gc.x, gc.y, gc.z, gc.w};
 #pragma unroll
@@ -965,7 +979,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     __syncthreads();  // (B)
 
     // ---- phase C: A and M tiles of the next chunk
-    if (it + 1 < w.nchunks) build_tiles(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16);
+    if (it + 1 < w.nchunks) build_tiles<64 * JT, DK>(sm, __builtin_amdgcn_readfirstlane(wave), q4, m16);
     __syncthreads();  // (C)
   }
 
@@ -973,28 +987,28 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
     if (w.s1_fp32) {
       float* s1 = reinterpret_cast<float*>(w.s1);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = Sacc[ct][jt][t];
+            s1[(16 * ct + 4 * q4 + t) * DK + jw_base + 16 * jt + m16] = Sacc[ct][jt][t];
     } else {
       __bf16* s1 = reinterpret_cast<__bf16*>(w.s1);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            s1[(16 * ct + 4 * q4 + t) * D + jw_base + 16 * jt + m16] = (__bf16)Sacc[ct][jt][t];
+            s1[(16 * ct + 4 * q4 + t) * DK + jw_base + 16 * jt + m16] = (__bf16)Sacc[ct][jt][t];
     }
   }
-  if (w.sb != nullptr) {
+  if (DK == 128 && w.sb != nullptr) {
     // element (k, j) at [k/32][j/16][16 ((k/8) % 4) + j % 16][k % 8]: this lane's
     // rows 16ct + 4q4 .. +3 of column j are four consecutive entries
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         const int k0 = 16 * ct + 4 * q4;
@@ -1209,16 +1223,17 @@ __device__ __forceinline__ int find_seq(const int* off, int N, int x) {
 // ============================================================================ main kernel
 // GS: the gate is one scalar per token and head (Gated DeltaNet), broadcast over
 // the key channels as it is loaded; everything after the load is the KDA path.
-template <int JT, bool GS>
+template <int JT, bool GS, int DK>
 __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   constexpr int NV = 64 * JT;  // value columns per workgroup
+  static_assert(DK == 128 || (DK == 64 && JT == 1), "head dimension 128, or 64 in one slice");
   __shared__ Smem<NV> sm;
   static_assert(plan_ints(kSortLimit, 512, true) * 4 <= 5 * sizeof(sm.kg),
                 "the plan fits in the operand tiles");
   const int tid = threadIdx.x;
 
   // ---- workgroup -> (task rank, head, value slice); slices of one head share an XCD
-  const int nsplit = 128 / NV;
+  const int nsplit = DK / NV;
   const int grp = blockIdx.x / (8 * nsplit);
   const int rem = blockIdx.x % (8 * nsplit);
   const int split = rem / 8;
@@ -1274,14 +1289,15 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     bos = (int64_t)n * p.T;
     len = p.T;
   }
-  const size_t hd2 = (size_t)w.h * (D * D);
+  const size_t hd2 = (size_t)w.h * (D * D);   // a state slot of the split workspace
+  const size_t hdk = (size_t)w.h * (DK * DK);  // the head's state in s0 / s1
   const bool seq_split = M != kNoSplit && len > (int64_t)M * C;
   if (kind == 0) {  // the sequence, or its first segment, from the true initial state
     w.bos = bos;
     w.len = seq_split ? (int64_t)M * C : len;
     w.s0_mode = p.s0 == nullptr ? 0 : p.s0_fp32 ? 2 : 1;
     w.s0 = p.s0 == nullptr ? nullptr
-         : static_cast<const char*>(p.s0) + ((size_t)n * p.H * (D * D) + hd2) * (p.s0_fp32 ? 4 : 2);
+         : static_cast<const char*>(p.s0) + ((size_t)n * p.H * (DK * DK) + hdk) * (p.s0_fp32 ? 4 : 2);
     w.sb = nullptr;
     if (seq_split) {  // the start state of segment 1, also as the fix-up operand
       w.s1 = p.st + ((size_t)slot0 * p.H) * (D * D) + hd2;
@@ -1289,12 +1305,12 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
       w.sb = p.sb + ((size_t)slot0 * p.H) * (D * D) + hd2;
     } else {
       w.s1 = p.s1 == nullptr ? nullptr
-           : static_cast<char*>(p.s1) + ((size_t)n * p.H * (D * D) + hd2) * (p.s1_fp32 ? 4 : 2);
+           : static_cast<char*>(p.s1) + ((size_t)n * p.H * (DK * DK) + hdk) * (p.s1_fp32 ? 4 : 2);
       w.s1_fp32 = p.s1_fp32;
     }
-    w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * D) + (int64_t)w.h * D;
-    w.orow = p.H * D;
-    w.ochunk = (int64_t)C * p.H * D;
+    w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * DK) + (int64_t)w.h * DK;
+    w.orow = p.H * DK;
+    w.ochunk = (int64_t)C * p.H * DK;
     w.vzero = 0;
     w.ck = p.ckpt == nullptr ? nullptr : p.ckpt + ((size_t)(n + bos / C) * p.H + w.h) * (D * D);
   } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
@@ -1324,8 +1340,8 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   w.nchunks = (int)((w.len + C - 1) / C);
 
   // Both roles execute the same barrier sequence; the branch is uniform per wave.
-  if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT>(sm, p, w);
-  else prep_loop<NV, GS>(sm, p, w);
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) < 4) state_loop<JT, DK>(sm, p, w);
+  else prep_loop<NV, GS, DK>(sm, p, w);
 }
 
 }  // namespace

@@ -1,5 +1,7 @@
-// Chunkwise Kimi Delta Attention forward at head dimension D = K = V in {64, 256}
-// for gfx950 (MI355X).
+// Chunkwise Kimi Delta Attention forward at head dimension D = K = V = 256 for
+// gfx950 (MI355X).  The templates below are written for D in {64, 256}; only
+// D = 256 is launched: head dimension 64 runs on the fused kernel
+// (kda_fwd_hd64_kernel.hip), which is faster.
 //
 // The recurrence and its chunkwise algebra are those of the fused d = 128 kernel
 // [core.today "Kimi Linear 특집", ch.4 혁신 2, state-update equation and the
@@ -772,14 +774,11 @@ hipError_t launch_dim(const DimParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t dim_record_bytes(int D) {
-  return D == 64 ? (size_t)Rec<64>::bytes : D == 256 ? (size_t)Rec<256>::bytes : 0;
-}
+size_t dim_record_bytes(int D) { return D == 256 ? (size_t)Rec<256>::bytes : 0; }
 
 int64_t dim_slots(int64_t nseq, int64_t rows) { return nseq + (rows + C - 1) / C + 1; }
 
 hipError_t launch_fwd_dim(const DimParams& p, hipStream_t stream) {
-  if (p.D == 64) return launch_dim<64>(p, stream);
   if (p.D == 256) return launch_dim<256>(p, stream);
   return hipErrorInvalidValue;
 }

@@ -319,6 +319,11 @@ size_t workspace_slot_bytes(int H) { return (size_t)H * D * D * (3 * 4 + 2); }
 
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
+  if (p.dk == 64) {  // one slice, no splitting, no checkpoints
+    if (nsplit != 1 || p.emax != 0 || p.ckpt != nullptr) return hipErrorInvalidValue;
+    return launch_fwd_main_hd64(p, (unsigned)(((int64_t)p.nseq * p.H + 7) / 8 * 8), stream);
+  }
+  if (p.dk != 128) return hipErrorInvalidValue;
   if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr))
     return hipErrorInvalidValue;
   // task groups: every sequence, plus two runs per extra segment (fewer than
@@ -330,8 +335,8 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (p.g_scalar) {
     err = launch_fwd_main_scalar_gate(p, nsplit, (unsigned)wgs, stream);
   } else {
-    if (nsplit == 1) hipLaunchKernelGGL((kda_fwd_kernel<2, false>), dim3((unsigned)wgs), block, 0, stream, p);
-    else hipLaunchKernelGGL((kda_fwd_kernel<1, false>), dim3((unsigned)wgs), block, 0, stream, p);
+    if (nsplit == 1) hipLaunchKernelGGL((kda_fwd_kernel<2, false, 128>), dim3((unsigned)wgs), block, 0, stream, p);
+    else hipLaunchKernelGGL((kda_fwd_kernel<1, false, 128>), dim3((unsigned)wgs), block, 0, stream, p);
     err = hipGetLastError();
   }
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;

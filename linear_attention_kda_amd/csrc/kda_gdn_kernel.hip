@@ -9,8 +9,8 @@ namespace kda {
 
 hipError_t launch_fwd_main_scalar_gate(const Params& p, int nsplit, unsigned wgs, hipStream_t stream) {
   const dim3 block(NT);
-  if (nsplit == 1) hipLaunchKernelGGL((kda_fwd_kernel<2, true>), dim3(wgs), block, 0, stream, p);
-  else hipLaunchKernelGGL((kda_fwd_kernel<1, true>), dim3(wgs), block, 0, stream, p);
+  if (nsplit == 1) hipLaunchKernelGGL((kda_fwd_kernel<2, true, 128>), dim3(wgs), block, 0, stream, p);
+  else hipLaunchKernelGGL((kda_fwd_kernel<1, true, 128>), dim3(wgs), block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -54,6 +54,10 @@ struct Params {
   // null.  Requires emax = 0 (no sequence splitting).
   float* ckpt;
   int g_scalar;           // one gate per token and head (Gated DeltaNet)
+  // Key/value head dimension: 128, or 64 (q, k, v, g, out and the states laid out
+  // with 64 channels; the kernel runs it as a 128-channel problem whose key
+  // channels past 64 are zero, in one 64-column value slice, without splitting).
+  int dk;
 };
 
 // Workspace bytes for splitting with `emax` state slots and `ucap` fix-up
@@ -194,10 +198,13 @@ kda_status record_failure(kda_status st, const char* text);
 
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
-// the segment scan and output fix-up kernels follow the main kernel.
+// the segment scan and output fix-up kernels follow the main kernel.  At
+// p.dk = 64, nsplit must be 1 and p.emax 0.
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream);
 // The fused kernel alone with the scalar gate (p.g_scalar), wgs workgroups.
 hipError_t launch_fwd_main_scalar_gate(const Params& p, int nsplit, unsigned wgs, hipStream_t stream);
+// The fused kernel alone at head dimension 64 (either gate), wgs workgroups.
+hipError_t launch_fwd_main_hd64(const Params& p, unsigned wgs, hipStream_t stream);
 
 }  // namespace kda
 

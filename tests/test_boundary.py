@@ -179,14 +179,15 @@ def test_bwd_workspace_bytes(lib):
 
 
 def test_dim_workspace_bytes(lib):
-    # one record per (chunk slot, head); slots: N + ceil(rows / 64) + 1.  A record
-    # holds kg, qg (64 rows of d + 8 bf16), kp^T (d rows of 72 bf16), three tiles of
-    # 64 rows of 72 bf16 and d fp32.
-    for d in (64, 256):
-        rec = 2 * 64 * (d + 8) * 2 + d * 72 * 2 + 3 * 64 * 72 * 2 + d * 4
-        assert binding.dim_workspace_bytes(16, 65536, 32, d) == (16 + 1024 + 1) * 32 * rec
-        assert binding.dim_workspace_bytes(1, 65, 2, d) == (1 + 2 + 1) * 2 * rec
-        assert binding.dim_workspace_bytes(3, 0, 2, d) == 0
+    # d = 256: one record per (chunk slot, head); slots: N + ceil(rows / 64) + 1.  A
+    # record holds kg, qg (64 rows of d + 8 bf16), kp^T (d rows of 72 bf16), three
+    # tiles of 64 rows of 72 bf16 and d fp32.  d = 64 runs on the fused kernel: none.
+    d = 256
+    rec = 2 * 64 * (d + 8) * 2 + d * 72 * 2 + 3 * 64 * 72 * 2 + d * 4
+    assert binding.dim_workspace_bytes(16, 65536, 32, d) == (16 + 1024 + 1) * 32 * rec
+    assert binding.dim_workspace_bytes(1, 65, 2, d) == (1 + 2 + 1) * 2 * rec
+    assert binding.dim_workspace_bytes(3, 0, 2, d) == 0
+    assert binding.dim_workspace_bytes(16, 65536, 32, 64) == 0
     assert binding.dim_workspace_bytes(1, 64, 1, 128) == -1
     assert binding.dim_workspace_bytes(0, 64, 1, 64) == -1
 
