@@ -151,10 +151,10 @@ struct LaunchPlan {
 // caller-provided buffer): the state slots and fix-up units are then sized to
 // it, and the device plan splits sequences only as far as they fit.
 LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus,
-                     size_t cap_bytes = 0) {
+                     size_t cap_bytes = 0, bool value_split = true) {
   LaunchPlan lp{};
   lp.seg_min = seg_min_chunks();
-  const int forced = forced_splits();
+  const int forced = value_split ? forced_splits() : 0;
   const int64_t c_max = (T + KDA_CHUNK - 1) / KDA_CHUNK;  // chunks of the longest possible sequence
   int64_t emax = 0, ucap = 0;
   // the device plan counts chunks and fix-up units in 32-bit integers
@@ -185,20 +185,11 @@ LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus,
   lp.emax = (int)emax;
   lp.ucap = (int)ucap;
   // one workgroup per (sequence, head) already covers the CUs: no value split
-  lp.nsplit = forced ? forced : (emax > 0 || (int64_t)N * H >= cus) ? 1 : 2;
+  lp.nsplit = forced ? forced : (!value_split || emax > 0 || (int64_t)N * H >= cus) ? 1 : 2;
   if (emax > 0 && lp.nsplit != 1) lp.emax = lp.ucap = 0;
   const int64_t groups = (int64_t)N + (lp.emax > 0 ? 2 * (int64_t)lp.emax : 0);
   lp.workgroups = (groups * H + 7) / 8 * 8 * lp.nsplit;
   lp.workspace = lp.emax > 0 ? kda::workspace_layout(lp.ucap, H, lp.emax).total : 0;
-  return lp;
-}
-
-// One workgroup per (sequence, head), no value split and no sequence splitting.
-LaunchPlan single_slice_plan(int32_t N, int32_t H) {
-  LaunchPlan lp{};
-  lp.nsplit = 1;
-  lp.seg_min = seg_min_chunks();
-  lp.workgroups = ((int64_t)N * H + 7) / 8 * 8;
   return lp;
 }
 
@@ -321,11 +312,9 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  // K = 64 runs the fused kernel in one 64-column slice per (sequence, head), without
-  // splitting sequences: no workspace
-  const LaunchPlan lp = K == KDA_HEAD_DIM
-      ? make_plan(N, T, H, cu_seqlens != nullptr, cus, ext ? ext->bytes : 0)
-      : single_slice_plan(N, H);
+  // K = 64 runs the fused kernel in one 64-column slice per (sequence, head, segment)
+  const LaunchPlan lp = make_plan(N, T, H, cu_seqlens != nullptr, cus, ext ? ext->bytes : 0,
+                                  K == KDA_HEAD_DIM);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
 
   kda::Params p{};

@@ -1004,16 +1004,16 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
             s1[(16 * ct + 4 * q4 + t) * DK + jw_base + 16 * jt + m16] = (__bf16)Sacc[ct][jt][t];
     }
   }
-  if (DK == 128 && w.sb != nullptr) {
-    // element (k, j) at [k/32][j/16][16 ((k/8) % 4) + j % 16][k % 8]: this lane's
-    // rows 16ct + 4q4 .. +3 of column j are four consecutive entries
+  if (w.sb != nullptr) {
+    // element (k, j) at [k/32][j/16][16 ((k/8) % 4) + j % 16][k % 8] (k, j < DK): this
+    // lane's rows 16ct + 4q4 .. +3 of column j are four consecutive entries
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         const int k0 = 16 * ct + 4 * q4;
         const int jg = (jw_base >> 4) + jt;
-        uint16_t* dst = w.sb + (((k0 >> 5) * 8 + jg) * 64 + 16 * ((k0 >> 3) & 3) + m16) * 8 + (k0 & 7);
+        uint16_t* dst = w.sb + (((k0 >> 5) * (DK / 16) + jg) * 64 + 16 * ((k0 >> 3) & 3) + m16) * 8 + (k0 & 7);
         *reinterpret_cast<uint2*>(dst) = pack4(Sacc[ct][jt][0], Sacc[ct][jt][1], Sacc[ct][jt][2], Sacc[ct][jt][3]);
       }
   }
@@ -1289,7 +1289,8 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     bos = (int64_t)n * p.T;
     len = p.T;
   }
-  const size_t hd2 = (size_t)w.h * (D * D);   // a state slot of the split workspace
+  const size_t hd2 = (size_t)w.h * (D * D);   // a state slot of the split workspace (its
+                                               // first DK x DK entries used, row stride DK)
   const size_t hdk = (size_t)w.h * (DK * DK);  // the head's state in s0 / s1
   const bool seq_split = M != kNoSplit && len > (int64_t)M * C;
   if (kind == 0) {  // the sequence, or its first segment, from the true initial state
@@ -1324,10 +1325,11 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.s1 = p.st + ((size_t)((ident ? 1 : 2) * p.emax + slot0 + sp - 1) * p.H) * (D * D) + hd2;
     w.s1_fp32 = 1;
     if (ident) {  // Q~ into the output rows
-      w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * D) + (int64_t)w.h * D;
-      w.orow = p.H * D;
-      w.ochunk = (int64_t)C * p.H * D;
+      w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * DK) + (int64_t)w.h * DK;
+      w.orow = p.H * DK;
+      w.ochunk = (int64_t)C * p.H * DK;
     } else {      // O0 into the fix-up blocks of its units, one 64 x 128 block per chunk
+                  // (its first DK columns used)
       const int ub = sp == 1 ? ubase1 : ubase2 + (sp - 2) * M;
       w.o = reinterpret_cast<__bf16*>(p.o0) + (int64_t)ub * (C * D);
       w.orow = D;

@@ -37,18 +37,23 @@ __device__ __forceinline__ void split_hilo(const float* f, bf16x8& hi, bf16x8& l
 }
 
 // One scan unit: columns 16cb .. 16cb+15 of the states of split sequence
-// `sidx`, head h.  The block lives transposed in LDS, slt[j][k].  A_p S_p runs on
-// bf16 16x16x32 products of high and low parts (the low-by-low term dropped);
-// wave w forms rows 32w .. 32w+31.
+// `sidx`, head h, at head dimension DK (the states are DK x DK with row stride
+// DK, in slots of 128 x 128).  The block lives transposed in LDS, slt[j][k].
+// A_p S_p runs on bf16 16x16x32 products of high and low parts (the low-by-low
+// term dropped); wave w forms rows DK/4 w .. DK/4 w + DK/4 - 1.
+template <int DK>
 __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, int M, int u, float* slt) {
+  constexpr int NB = DK / 16;   // 16-column blocks of a state
+  constexpr int KS = DK / 32;   // 32-row slices of the product's k range
+  constexpr int IT = DK / 64;   // 16-row tiles per wave
   const int N = p.nseq, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
   const size_t slot_stride = (size_t)p.H * (D * D);
-  // u = (split sequence * 8 + column block) * H + head: the eight column blocks of one
+  // u = (split sequence * NB + column block) * H + head: the column blocks of one
   // (sequence, head), which all read the same A_p, land on one XCD when 8 divides H
   // (workgroups go to XCDs round robin)
-  const int sidx = u / (p.H * 8), cb = (u / p.H) % 8, h = u % p.H;
+  const int sidx = u / (p.H * NB), cb = (u / p.H) % NB, h = u % p.H;
   const int i = __builtin_amdgcn_readfirstlane(find_seq(v.xoff, N, sidx));
   const int c = __builtin_amdgcn_readfirstlane(v.lens[i]), P = (c + M - 1) / M;
   const int slot0 = __builtin_amdgcn_readfirstlane(v.soff[i]);
@@ -56,43 +61,46 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
   {  // S_1 (row-major in the workspace) -> slt
     const float* s1 = p.st + slot0 * slot_stride + hd2 + 16 * cb;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < NB; ++x) {
       const int k = 16 * x + (tid >> 4), j = tid & 15;
-      slt[j * SLT + k] = s1[(size_t)k * D + j];
+      slt[j * SLT + k] = s1[(size_t)k * DK + j];
     }
   }
   __syncthreads();
   for (int sp = 1; sp < P; ++sp) {
     const int slot = slot0 + sp - 1;
-    // rows 32w + 16it + m16 of A_p (k = 32ks + 8q4 .. +7) and the matching
+    // rows DK/4 w + 16it + m16 of A_p (k = 32ks + 8q4 .. +7) and the matching
     // entries of B_p, all loads in flight before the products
     const float* am = p.st + ((size_t)p.emax + slot) * slot_stride + hd2;
     const float* bm = p.st + ((size_t)2 * p.emax + slot) * slot_stride + hd2 + 16 * cb + m16;
-    float4 ar[2][4][2];
+    const int row0 = (DK / 4) * wave;
+    float4 ar[IT][KS][2];
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float* rp = am + (size_t)(32 * wave + 16 * it + m16) * D + 32 * ks + 8 * q4;
+      for (int ks = 0; ks < KS; ++ks) {
+        const float* rp = am + (size_t)(row0 + 16 * it + m16) * DK + 32 * ks + 8 * q4;
         ar[it][ks][0] = *reinterpret_cast<const float4*>(rp);
         ar[it][ks][1] = *reinterpret_cast<const float4*>(rp + 4);
       }
-    f32x4 acc[2];
+    f32x4 acc[IT];
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[it][t] = bm[(size_t)(32 * wave + 16 * it + 4 * q4 + t) * D];
+      for (int t = 0; t < 4; ++t) acc[it][t] = bm[(size_t)(row0 + 16 * it + 4 * q4 + t) * DK];
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
-    if (sp >= 2) {  // fix-up operand copy of S_p: element (k, j) at [k/32][j/16][16 ((k/8)%4) + j%16][k%8]
-      const int ks = tid >> 6;
+    // fix-up operand copy of S_p: element (k, j) at [k/32][j/16][16 ((k/8)%4) + j%16][k%8],
+    // one 32-row slice per wave
+    if (sp >= 2 && wave < KS) {
+      const int ks = wave;
       const float4 f0 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4]);
       const float4 f1 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4 + 4]);
       const uint2 lo = pack4(f0.x, f0.y, f0.z, f0.w), hi = pack4(f1.x, f1.y, f1.z, f1.w);
-      uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * 8 + cb) * 64 + lane) * 8;
+      uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * NB + cb) * 64 + lane) * 8;
       *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       // B operand: S_p[32ks + 8q4 + e][m16] = slt[m16][32ks + 8q4 + e]
       const float4 g0 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4]);
       const float4 g1 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4 + 4]);
@@ -100,7 +108,7 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
       bf16x8 sh, sl;
       split_hilo(sf, sh, sl);
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
+      for (int it = 0; it < IT; ++it) {
         const float af[8] = {ar[it][ks][0].x, ar[it][ks][0].y, ar[it][ks][0].z, ar[it][ks][0].w,
                              ar[it][ks][1].x, ar[it][ks][1].y, ar[it][ks][1].z, ar[it][ks][1].w};
         bf16x8 ah, al;
@@ -111,21 +119,21 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
       }
     }
     __syncthreads();  // every read of S_p is done
-    // lane holds S_{p+1}[32w + 16it + 4q4 + t][m16]: four consecutive entries of slt row m16
+    // lane holds S_{p+1}[row0 + 16it + 4q4 + t][m16]: four consecutive entries of slt row m16
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-      *reinterpret_cast<float4*>(&slt[m16 * SLT + 32 * wave + 16 * it + 4 * q4]) =
+    for (int it = 0; it < IT; ++it)
+      *reinterpret_cast<float4*>(&slt[m16 * SLT + row0 + 16 * it + 4 * q4]) =
           make_float4(acc[it][0], acc[it][1], acc[it][2], acc[it][3]);
     __syncthreads();
   }
   if (p.s1 != nullptr) {
-    const size_t base = ((size_t)i * p.H) * (D * D) + hd2 + 16 * cb;
+    const size_t base = ((size_t)i * p.H + h) * (DK * DK) + 16 * cb;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < NB; ++x) {
       const int k = 16 * x + (tid >> 4), j = tid & 15;
       const float val = slt[j * SLT + k];
-      if (p.s1_fp32) static_cast<float*>(p.s1)[base + (size_t)k * D + j] = val;
-      else static_cast<__bf16*>(p.s1)[base + (size_t)k * D + j] = (__bf16)val;
+      if (p.s1_fp32) static_cast<float*>(p.s1)[base + (size_t)k * DK + j] = val;
+      else static_cast<__bf16*>(p.s1)[base + (size_t)k * DK + j] = (__bf16)val;
     }
   }
   __syncthreads();  // before the next unit overwrites the block
@@ -171,70 +179,92 @@ __device__ __forceinline__ FixUnit fix_decode(const Params& p, const PlanView& v
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
-// Q~ rows of the unit's chunk (rows past `valid` read as zero) and its O0 entries.
-struct FixLoads {
-  u32x4 qv[4];
-  u32x2 zv[4][2];
+// At head dimension DK: a row of Q~ is DK/8 loads of 16 bytes, so 2048/DK rows go
+// in one pass of the 256 threads; wave w forms output columns DK/4 w .. + DK/4 - 1
+// (JJ = DK/64 tiles of 16).
+template <int DK>
+struct FixShape {
+  static constexpr int TPR = DK / 8;        // threads per Q~ row
+  static constexpr int RPS = TAIL_NT / TPR;  // Q~ rows per pass
+  static constexpr int QP = C / RPS;        // passes over the chunk's 64 rows
+  static constexpr int JJ = DK / 64;        // 16-column output tiles per wave
+  static constexpr int KS = DK / 32;        // 32-channel slices of the products
+  static constexpr int NB = DK / 16;        // 16-column blocks of a state
 };
 
-__device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, FixLoads& L) {
+// Q~ rows of the unit's chunk (rows past `valid` read as zero) and its O0 entries.
+template <int DK>
+struct FixLoads {
+  u32x4 qv[FixShape<DK>::QP];
+  u32x2 zv[4][FixShape<DK>::JJ];
+};
+
+template <int DK>
+__device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, FixLoads<DK>& L) {
+  using F = FixShape<DK>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
-  const int HD = p.H * D;
-  const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
+  const int HD = p.H * DK;
+  const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * DK, f.valid * HD * 2);
   const auto zrsrc = rsrc(p.o0 + (int64_t)f.ob * (C * D), f.valid * D * 2);
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-    L.qv[x] = __builtin_amdgcn_raw_buffer_load_b128(orsrc, ((16 * x + (tid >> 4)) * HD + 8 * (tid & 15)) * 2, 0, 0);
+  for (int x = 0; x < F::QP; ++x)
+    L.qv[x] = __builtin_amdgcn_raw_buffer_load_b128(
+        orsrc, ((F::RPS * x + tid / F::TPR) * HD + 8 * (tid % F::TPR)) * 2, 0, 0);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < F::JJ; ++jj)
       L.zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
-          zrsrc, ((16 * tt + m16) * D + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+          zrsrc, ((16 * tt + m16) * D + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
 }
 
 // S_p^T as the products' A operand (bf16, the order the segment's first run wrote).
-__device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f, bf16x8 (&sa)[4][2]) {
+template <int DK>
+__device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f,
+                                          bf16x8 (&sa)[FixShape<DK>::KS][FixShape<DK>::JJ]) {
+  using F = FixShape<DK>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)f.slot * p.H + f.h) * (D * D);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < F::KS; ++ks)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-      sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * 8 + 2 * wave + jj) * 64 + lane) * 8);
+    for (int jj = 0; jj < F::JJ; ++jj)
+      sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * F::NB + F::JJ * wave + jj) * 64 + lane) * 8);
 }
 
 // Fix-up units [u_lo, u_hi) of this workgroup: o = O0 + S_p^T Q~ for every row
 // of each unit's chunk.  The next unit's loads are in flight while the current
 // one is multiplied; S_p is reloaded only when the segment or head changes.
+template <int DK>
 __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0,
                           int u_lo, int u_hi, __bf16* ot) {
+  using F = FixShape<DK>;
   if (u_lo >= u_hi) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
-  const int HD = p.H * D;
+  const int HD = p.H * DK;
   FixUnit cur = fix_decode(p, v, M, off, seg0, u_lo);
-  FixLoads L;
-  fix_issue(p, cur, L);
-  bf16x8 sa[4][2];
-  fix_state(p, cur, sa);
+  FixLoads<DK> L;
+  fix_issue<DK>(p, cur, L);
+  bf16x8 sa[F::KS][F::JJ];
+  fix_state<DK>(p, cur, sa);
   for (int u = u_lo; u < u_hi; ++u) {
     // stage Q~ of the current unit (its B operand order) in LDS
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      uint2* dst = reinterpret_cast<uint2*>(&ot[(16 * x + (tid >> 4)) * TS + 8 * (tid & 15)]);
+    for (int x = 0; x < F::QP; ++x) {
+      uint2* dst = reinterpret_cast<uint2*>(&ot[(F::RPS * x + tid / F::TPR) * TS + 8 * (tid % F::TPR)]);
       dst[0] = make_uint2(L.qv[x][0], L.qv[x][1]);
       dst[1] = make_uint2(L.qv[x][2], L.qv[x][3]);
     }
-    f32x4 z[4][2];
+    f32x4 z[4][F::JJ];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+      for (int jj = 0; jj < F::JJ; ++jj) {
         float f[4];
         unpack4(make_uint2(L.zv[tt][jj][0], L.zv[tt][jj][1]), f);
         z[tt][jj] = f32x4{f[0], f[1], f[2], f[3]};
@@ -243,35 +273,36 @@ __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* 
     const bool more = u + 1 < u_hi;
     if (more) {
       cur = fix_decode(p, v, M, off, seg0, u + 1);
-      fix_issue(p, cur, L);  // the next unit's loads fly during this unit's products
+      fix_issue<DK>(p, cur, L);  // the next unit's loads fly during this unit's products
     }
     __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < F::KS; ++ks) {
         const __bf16* bp = &ot[(16 * tt + m16) * TS + 32 * ks + 8 * q4];
         const bf16x8 bb = ld2x4(bp, bp + 4);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) z[tt][jj] = mfma32(sa[ks][jj], bb, z[tt][jj]);
+        for (int jj = 0; jj < F::JJ; ++jj) z[tt][jj] = mfma32(sa[ks][jj], bb, z[tt][jj]);
       }
     }
-    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = 2 wave + jj
-    const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * D, f.valid * HD * 2);
+    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = JJ wave + jj
+    const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * DK, f.valid * HD * 2);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+      for (int jj = 0; jj < F::JJ; ++jj) {
         const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(u32x2, ov), orsrc,
-            ((16 * tt + m16) * HD + 16 * (2 * wave + jj) + 4 * q4) * 2, 0, 0);
+            ((16 * tt + m16) * HD + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
       }
-    if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state(p, cur, sa);
+    if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state<DK>(p, cur, sa);
     __syncthreads();  // before the next unit's staging
   }
 }
 
+template <int DK>
 __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phase) {
   extern __shared__ int plan_lds[];
   __shared__ __attribute__((aligned(16))) float slt[16 * SLT];
@@ -286,18 +317,18 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
   if (phase == 0) {
     // scan units spread over the grid, then this workgroup's share of the
     // segment-1 fix-ups (they need only S_1, written by the main kernel)
-    const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * 8;
-    for (int u = b; u < nscan; u += G) scan_unit(p, v, M, u, slt);
+    const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * (DK / 16);
+    for (int u = b; u < nscan; u += G) scan_unit<DK>(p, v, M, u, slt);
     // with workgroups to spare, the fix-ups go to those without a scan unit and run
     // beside the scan instead of after it
     const int F = __builtin_amdgcn_readfirstlane(v.hdr[4]);
     const int first = nscan < G ? nscan : 0;
     if (b >= first)
-      fix_range(p, v, M, v.uoff, 1, (int)((int64_t)F * (b - first) / (G - first)),
-                (int)((int64_t)F * (b - first + 1) / (G - first)), ot);
+      fix_range<DK>(p, v, M, v.uoff, 1, (int)((int64_t)F * (b - first) / (G - first)),
+                    (int)((int64_t)F * (b - first + 1) / (G - first)), ot);
   } else {
     const int F = __builtin_amdgcn_readfirstlane(v.hdr[5]);
-    fix_range(p, v, M, v.voff, 2, (int)((int64_t)F * b / G), (int)((int64_t)F * (b + 1) / G), ot);
+    fix_range<DK>(p, v, M, v.voff, 2, (int)((int64_t)F * b / G), (int)((int64_t)F * (b + 1) / G), ot);
   }
 }
 
@@ -319,11 +350,7 @@ size_t workspace_slot_bytes(int H) { return (size_t)H * D * D * (3 * 4 + 2); }
 
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
-  if (p.dk == 64) {  // one slice, no splitting, no checkpoints
-    if (nsplit != 1 || p.emax != 0 || p.ckpt != nullptr) return hipErrorInvalidValue;
-    return launch_fwd_main_hd64(p, (unsigned)(((int64_t)p.nseq * p.H + 7) / 8 * 8), stream);
-  }
-  if (p.dk != 128) return hipErrorInvalidValue;
+  if (p.dk != 128 && (p.dk != 64 || nsplit != 1 || p.ckpt != nullptr)) return hipErrorInvalidValue;
   if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr))
     return hipErrorInvalidValue;
   // task groups: every sequence, plus two runs per extra segment (fewer than
@@ -332,7 +359,9 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   const int64_t wgs = (groups * p.H + 7) / 8 * 8 * nsplit;
   const dim3 block(NT);
   hipError_t err;
-  if (p.g_scalar) {
+  if (p.dk == 64) {  // one 64-column slice, either gate
+    err = launch_fwd_main_hd64(p, (unsigned)wgs, stream);
+  } else if (p.g_scalar) {
     err = launch_fwd_main_scalar_gate(p, nsplit, (unsigned)wgs, stream);
   } else {
     if (nsplit == 1) hipLaunchKernelGGL((kda_fwd_kernel<2, false, 128>), dim3((unsigned)wgs), block, 0, stream, p);
@@ -341,11 +370,13 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   }
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;
   const size_t plan_bytes = (size_t)plan_ints(p.nseq, 0, false) * sizeof(int);
-  hipLaunchKernelGGL(kda_tail_kernel, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 0);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kda_tail_kernel, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, 1);
-  return hipGetLastError();
+  for (int phase = 0; phase < 2; ++phase) {
+    if (p.dk == 64) hipLaunchKernelGGL(kda_tail_kernel<64>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, phase);
+    else hipLaunchKernelGGL(kda_tail_kernel<128>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, phase);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -56,7 +56,9 @@ struct Params {
   int g_scalar;           // one gate per token and head (Gated DeltaNet)
   // Key/value head dimension: 128, or 64 (q, k, v, g, out and the states laid out
   // with 64 channels; the kernel runs it as a 128-channel problem whose key
-  // channels past 64 are zero, in one 64-column value slice, without splitting).
+  // channels past 64 are zero, in one 64-column value slice).  The split
+  // workspace keeps its 128 x 128 slots and 64 x 128 output blocks; at 64 their
+  // first 64 x 64 entries (row stride 64) and first 64 columns are used.
   int dk;
 };
 
@@ -199,7 +201,7 @@ kda_status record_failure(kda_status st, const char* text);
 // Enqueue the forward pass; nsplit in {1, 2} value-column slices per (sequence,
 // head).  With p.emax > 0 (nsplit must be 1) long sequences may be split, and
 // the segment scan and output fix-up kernels follow the main kernel.  At
-// p.dk = 64, nsplit must be 1 and p.emax 0.
+// p.dk = 64, nsplit must be 1 and there are no checkpoints.
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream);
 // The fused kernel alone with the scalar gate (p.g_scalar), wgs workgroups.
 hipError_t launch_fwd_main_scalar_gate(const Params& p, int nsplit, unsigned wgs, hipStream_t stream);

@@ -155,6 +155,34 @@ def test_scalar_gate(D):
     check(o, f, o_ref, f_ref, "scalar gate")
 
 
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_d64_split_sequences(monkeypatch, state):
+    """d = 64 with sequences split into segments of 3 chunks (KDA_SEG_MIN=3): segment
+    0 from the true initial state, zero- and identity-start runs of the later segments,
+    the segment scan and the output fix-ups, at head dimension 64 (fixed length)."""
+    monkeypatch.setenv("KDA_SEG_MIN", "3")
+    B, T, H = 1, 1500, 2
+    announce(f"d=64 split B={B} T={T} H={H} state={state}, seg_min=3")
+    x = inputs(64, B, T, H, seed=570 + len(state), state=state)
+    fd = {"fp32": torch.float32, "bf16": torch.bfloat16}[state]
+    o, f = run(x, final_dtype=fd)
+    o_ref, f_ref = reference(x)
+    check(o, f, o_ref, f_ref, "split fixed length")
+
+
+@pytest.mark.parametrize("scalar_gate", [False, True])
+def test_d64_split_varlen(monkeypatch, scalar_gate):
+    """d = 64, varlen with an empty and a short sequence among split ones, both gates."""
+    monkeypatch.setenv("KDA_SEG_MIN", "3")
+    lengths = [900, 0, 1300, 5, 64, 451]
+    announce(f"d=64 split varlen {lengths} H=3 scalar_gate={scalar_gate}, seg_min=3")
+    x = inputs(64, 1, sum(lengths), 3, seed=580 + scalar_gate, lengths=lengths)
+    o, f = run(x, scalar_gate=scalar_gate)
+    o_ref, f_ref = reference(x, scalar_gate=scalar_gate)
+    check(o, f, o_ref, f_ref, "split varlen")
+    assert torch.equal(f[1], x["initial_state"][1])
+
+
 @pytest.mark.parametrize("D", DIMS)
 def test_no_tokens_copies_the_state(D):
     announce(f"d={D} T=0")
@@ -167,8 +195,9 @@ def test_no_tokens_copies_the_state(D):
 @pytest.mark.parametrize("D", DIMS)
 def test_full_size_varlen_sampled_heads(D):
     """The 64K-token varlen workload (16 sequences, H = 32, bf16 states) at head
-    dimension D in the launch configuration the benchmark times; two seeded heads
-    are compared with the oracle in full."""
+    dimension D in the launch configuration the benchmark times (at d = 64 the long
+    sequences split into segments); two seeded heads are compared with the oracle in
+    full."""
     w = WORKLOADS[2]
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed)
@@ -178,8 +207,25 @@ def test_full_size_varlen_sampled_heads(D):
                       init_state=w.init_state, lengths=lengths)
     o, f = run(x, final_dtype=torch.bfloat16)
     heads = sample_heads(2, 2)
+    if D == 64:  # every head, with the per-(sequence, head) bar as well
+        heads = list(range(w.H))
     sub = {k: (x[k][:, :, heads].contiguous() if k in ("q", "k", "v", "g", "beta") else x[k])
            for k in x}
     sub["initial_state"] = x["initial_state"][:, heads].contiguous()
     o_ref, f_ref = reference(sub)
-    check(o[:, :, heads], f[:, heads], o_ref, f_ref, f"heads {heads}")
+    check(o[:, :, heads], f[:, heads], o_ref, f_ref, f"heads {heads[0]}..{heads[-1]}")
+    if D == 64:
+        oh, fh = host(o[:, :, heads]), host(f[:, heads])
+        cu = [int(c) for c in x["cu_seqlens"].cpu()]
+        worst_o = worst_s = 0.0
+        for n in range(len(cu) - 1):
+            a, b = cu[n], cu[n + 1]
+            if b > a:
+                num = np.abs(oh[0, a:b] - o_ref[0, a:b]).max(axis=(0, 2))
+                den = np.abs(o_ref[0, a:b]).max(axis=(0, 2))
+                worst_o = max(worst_o, float((num / np.maximum(den, 1e-30)).max()))
+            num = np.abs(fh[n] - f_ref[n]).max(axis=(1, 2))
+            den = np.abs(f_ref[n]).max(axis=(1, 2))
+            worst_s = max(worst_s, float((num / np.maximum(den, 1e-30)).max()))
+        print(f"    worst per-(sequence, head): out {worst_o:.3e}, state {worst_s:.3e}", flush=True)
+        assert worst_o <= TOL and worst_s <= TOL
