@@ -1050,6 +1050,7 @@ __device__ __forceinline__ int64_t seq_len(const Params& p, int i) {
 struct PlanView {
   int* hdr;   // [0] M (kNoSplit: nothing split) [1] task groups [2] state slots
               // [3] split sequences [4] fix-up units of segment 1 [5] of later segments
+              // [6] chunks of the longest sequence
   int* lens;  // [N]   chunks of each sequence
   int* goff;  // [N+1] first task group of each sequence
   int* soff;  // [N+1] first state slot (slot of segment p >= 1: soff + p - 1)
@@ -1180,6 +1181,7 @@ __device__ void build_plan(const Params& p, const PlanView& v, bool groups) {
       v.hdr[3] = ex;
       v.hdr[4] = eu;
       v.hdr[5] = ev;
+      v.hdr[6] = mx;
     }
   }
   __syncthreads();

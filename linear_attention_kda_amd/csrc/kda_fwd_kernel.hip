@@ -308,10 +308,17 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
   __shared__ __attribute__((aligned(16))) float slt[16 * SLT];
   __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
   const int N = p.nseq;
+  // The second launch has no work when no sequence has more than two segments (the
+  // first launch records that): it then ends before building the plan.
+  const auto frsrc = rsrc(p.tail_flag, 4);
+  if (phase == 1 && __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(frsrc, 0, 0, 0)) == 0)
+    return;
   const PlanView v = plan_view(plan_lds, N, 0);
   build_plan(p, v, false);
   // wave-uniform unit values keep every buffer descriptor scalar
   const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
+  if (phase == 0 && blockIdx.x == 0 && threadIdx.x == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(M != kNoSplit && v.hdr[5] > 0 ? 1u : 0u, frsrc, 0, 0, 0);
   if (M == kNoSplit) return;
   const int G = gridDim.x, b = blockIdx.x;
   if (phase == 0) {
@@ -319,10 +326,14 @@ __global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phas
     // segment-1 fix-ups (they need only S_1, written by the main kernel)
     const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * (DK / 16);
     for (int u = b; u < nscan; u += G) scan_unit<DK>(p, v, M, u, slt);
-    // with workgroups to spare, the fix-ups go to those without a scan unit and run
-    // beside the scan instead of after it
+    // With workgroups to spare and a scan of several steps, the fix-ups go to those
+    // without a scan unit and run beside the scan instead of after it.  A one-step
+    // scan (two segments at most) ends long before the fix-ups: then every
+    // workgroup takes its share of them, after its scan unit.
     const int F = __builtin_amdgcn_readfirstlane(v.hdr[4]);
-    const int first = nscan < G ? nscan : 0;
+    const int mx = __builtin_amdgcn_readfirstlane(v.hdr[6]);
+    const bool one_step = (mx + M - 1) / M <= 2;
+    const int first = (!one_step && nscan < G) ? nscan : 0;
     if (b >= first)
       fix_range<DK>(p, v, M, v.uoff, 1, (int)((int64_t)F * (b - first) / (G - first)),
                     (int)((int64_t)F * (b - first + 1) / (G - first)), ot);
@@ -342,7 +353,8 @@ WorkspaceLayout workspace_layout(int64_t ucap, int H, int emax) {
   l.o0 = 0;
   l.st = up((size_t)ucap * kUnitBytes);
   l.sb = l.st + up((size_t)3 * emax * H * D * D * 4);
-  l.total = l.sb + up((size_t)emax * H * D * D * 2);
+  l.flag = l.sb + up((size_t)emax * H * D * D * 2);
+  l.total = l.flag + 256;
   return l;
 }
 
@@ -351,7 +363,8 @@ size_t workspace_slot_bytes(int H) { return (size_t)H * D * D * (3 * 4 + 2); }
 hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
   if (p.dk != 128 && (p.dk != 64 || nsplit != 1 || p.ckpt != nullptr)) return hipErrorInvalidValue;
-  if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr))
+  if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr ||
+                     p.tail_flag == nullptr))
     return hipErrorInvalidValue;
   // task groups: every sequence, plus two runs per extra segment (fewer than
   // 2 * emax of them when splitting)

@@ -49,6 +49,7 @@ struct Params {
                           // state, one 64-row block per fix-up unit (sequence, head, chunk)
   float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
   uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
+  int* tail_flag;         // one int: whether the fix-up launch of the later segments has work
   // Backward support: the fp32 state at the start of every chunk, at slot
   // n + floor(bos_n / 64) + c of sequence n's chunk c ([slots][H][128][128]), or
   // null.  Requires emax = 0 (no sequence splitting).
@@ -65,7 +66,7 @@ struct Params {
 // Workspace bytes for splitting with `emax` state slots and `ucap` fix-up
 // units of H heads, and the offsets of its three parts.
 struct WorkspaceLayout {
-  size_t o0, st, sb, total;
+  size_t o0, st, sb, flag, total;
 };
 WorkspaceLayout workspace_layout(int64_t ucap, int H, int emax);
 // Bytes of one state slot (all heads) and of one fix-up unit's output block.
