@@ -229,6 +229,27 @@ hipError_t workspace_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// A second stream per device, created on first use (default priority), on which
+// the backward's checkpointing forward pass runs beside the chunk-local tiles.
+hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    err = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (err != hipSuccess) {
+      streams[dev] = nullptr;
+      return err;
+    }
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+
 // Head dimension 256: per-chunk records in a workspace from the pool, then the
 // serial state pass (no sequence splitting).
 kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float* g,
@@ -708,17 +729,37 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     p.ckpt = w.S;
     p.dk = KDA_HEAD_DIM;
     const int nsplit = (int64_t)N * H >= cus ? 1 : 2;
-    err = kda::launch_fwd(p, nsplit, hs);
+    kda::BwdParams bp{};
+    bp.q = p.q; bp.k = p.k; bp.v = p.v;
+    bp.dout = static_cast<const uint16_t*>(d_out);
+    bp.g = g; bp.beta = beta; bp.cu = cu_seqlens; bp.T = T; bp.scale = scale;
+    bp.nseq = N; bp.H = H;
+    bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.ds0 = d_initial_state;
+    // The checkpointing forward runs on a side stream while the chunk-local tiles,
+    // which need no checkpoint, run on the caller's stream; the rest waits for both.
+    // Once the fork is recorded, the caller's stream always waits for the side
+    // stream before the workspace is released.
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    err = side_stream(&side);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventRecord(fork, hs);
     if (err == hipSuccess) {
-      kda::BwdParams bp{};
-      bp.q = p.q; bp.k = p.k; bp.v = p.v;
-      bp.dout = static_cast<const uint16_t*>(d_out);
-      bp.g = g; bp.beta = beta; bp.cu = cu_seqlens; bp.T = T; bp.scale = scale;
-      bp.nseq = N; bp.H = H;
-      bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32;
-      bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.ds0 = d_initial_state;
-      err = kda::launch_bwd(bp, w, nb, hs);
+      err = hipStreamWaitEvent(side, fork, 0);
+      if (err == hipSuccess) err = kda::launch_fwd(p, nsplit, side);
+      if (err == hipSuccess) err = kda::launch_bwd_chunk_local(bp, w, nb, hs);
+      hipError_t ej = hipEventRecord(join, side);
+      if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, join, 0);
+      if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
+        (void)hipStreamSynchronize(side);
+        if (err == hipSuccess) err = ej;
+      }
+      if (err == hipSuccess) err = kda::launch_bwd_from_states(bp, w, nb, hs);
     }
+    if (fork != nullptr) (void)hipEventDestroy(fork);
+    if (join != nullptr) (void)hipEventDestroy(join);
   } else if (d_initial_state != nullptr) {
     // no tokens: the initial-state gradient is the final-state gradient (or zero)
     kda::BwdParams bp{};

@@ -973,7 +973,7 @@ hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
   const int NB = (int)batches;
   const int64_t t1 = C * D, t2 = C * C, t3 = D * D, tf = D * C;
   // chunk tiles
@@ -981,15 +981,6 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   // P = strict_lower(K K^T gated), A = diag(b) P, M = lower_incl(Q K^T gated)
   hipLaunchKernelGGL(bwd_pm_kernel, dim3(NB), dim3(256), 0, s, p, w);
   hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
-  // R = V - kg S;  U = T diag(b) R
-  {
-    GemmArgs a = mm(C, D, D, w.kg, t1, D, w.S, t3, D, w.R, t1, D, NB);
-    a.alpha = -1.f; a.Dm = w.vv; a.sD = t1; a.ldd = D;
-    gemm(false, false, a, s);
-    GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
-    u.ks = w.beta; u.sks = C;
-    gemm(false, false, u, s);
-  }
   // MtdO = M^T dO';  F = kg^T diag(b) T^T;  X = qg^T dO' - F MtdO
   {
     gemm(true, false, mm(C, D, C, w.M, t2, C, w.dO, t1, D, w.MtdO, t1, D, NB), s);
@@ -998,6 +989,21 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
     gemm(true, true, f, s);
     gemm2<true, false, false, false>(mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB),
                                      mm(D, D, C, w.F, tf, C, w.MtdO, t1, D, nullptr, 0, 0, NB), -1.f, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_from_states(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+  const int NB = (int)batches;
+  const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
+  // R = V - kg S;  U = T diag(b) R
+  {
+    GemmArgs a = mm(C, D, D, w.kg, t1, D, w.S, t3, D, w.R, t1, D, NB);
+    a.alpha = -1.f; a.Dm = w.vv; a.sD = t1; a.ldd = D;
+    gemm(false, false, a, s);
+    GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
+    u.ks = w.beta; u.sks = C;
+    gemm(false, false, u, s);
   }
   // serial recurrence of dS over chunks
   launch_ds_scan(p, w, s);
@@ -1026,6 +1032,11 @@ hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hi
   }
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+  const hipError_t e = launch_bwd_chunk_local(p, w, batches, s);
+  return e != hipSuccess ? e : launch_bwd_from_states(p, w, batches, s);
 }
 
 }  // namespace kda

@@ -149,6 +149,12 @@ struct GemmArgs {
 
 size_t bwd_tile_floats();
 hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
+// The two halves of launch_bwd: the chunk-local tiles that need no state
+// checkpoint (prep, P / A / M, the inverse, M^T dO', F and X), then everything
+// from the checkpoints on.  The first may run while the checkpointing forward
+// pass still runs; the second must follow both.
+hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
+hipError_t launch_bwd_from_states(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
 // The initial-state gradients alone, for calls without tokens.
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 
