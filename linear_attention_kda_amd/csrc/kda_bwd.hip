@@ -692,122 +692,144 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 
 // ---------------------------------------------------------------- serial dS
 // Column j of dS depends only on column j of dSn (Diag(gam), kp and F act on
-// rows), so each (sequence, head) runs as D / DSW workgroups of DSW value
-// columns.  Chunks last to first: dSn(c) is stored for the chunk's gradient
-// products, then dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The
-// sequence's initial-state gradient is the last dS.  The loop is serial and
-// VALU-bound inside a workgroup of four waves, so with few (sequence, head)
-// pairs the columns are cut finer (DSW 16) to occupy more compute units and
-// halve each workgroup's work per chunk.
-template <int DSW>
-__global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
-  constexpr int DSC = D / DSW;       // workgroups per (sequence, head)
-  constexpr int CG = DSW / 4;        // column groups of 4
-  constexpr int RP = C * CG / 256;   // rows of P per thread
-  constexpr int RF = D * CG / 256;   // rows of dS per thread
-  static_assert(RP >= 1 && RF >= 1 && C * CG % 256 == 0, "slice width");
-  __shared__ float ds[D][DSW + 4];   // dSn, then the new dS (this workgroup's columns)
-  __shared__ float pp[C][DSW + 4];   // P = kp dSn
-  const int pair = blockIdx.x / DSC, j0 = (blockIdx.x % DSC) * DSW;
-  const int n = pair / p.H, h = pair % p.H;
-  const int t = threadIdx.x;
-  const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
-  const int nch = (int)((len + C - 1) / C);
-  const size_t sd = (size_t)D * D;
-  for (int x = t; x < D * DSW; x += 256) {   // dS_final (or zero)
-    const int r = x / DSW, j = x % DSW;
-    float v = 0.f;
-    if (p.dsT) {
-      const size_t o = ((size_t)n * p.H + h) * sd + (size_t)r * D + j0 + j;
-      v = p.dsT_fp32 ? static_cast<const float*>(p.dsT)[o] : bf2f_u16(static_cast<const uint16_t*>(p.dsT)[o]);
-    }
-    ds[r][j] = v;
-  }
-  __syncthreads();
-  const int jb = (t % CG) * 4;   // 4 of this workgroup's columns
-  for (int c = nch - 1; c >= 0; --c) {
-    const int64_t bidx = (n + bos / C + c) * p.H + h;
-    float* dsn = w.dSn + bidx * sd;
-    for (int x = t; x < D * DSW; x += 256) dsn[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
-    {  // P = kp dSn: rows RP (t / CG) .. +RP-1
-      const float* kp = w.kp + bidx * (C * D);
-      const int r0 = (t / CG) * RP;
-      float acc[RP][4] = {};
-      for (int k = 0; k < D; k += 4) {
-        float av[RP][4];
+// rows), so each (sequence, head) runs as D / 16 workgroups of 16 value columns.
+// Chunks last to first: dSn(c) is stored for the chunk's gradient products, then
+// dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The sequence's
+// initial-state gradient is the last dS.
+//  * Both products run on the fp32 matrix cores (16x16x4): wave w forms rows
+//    16w .. 16w+15 of P = kp dSn and rows 32w .. 32w+31 of dS.  The k index of a
+//    product is permuted so that each lane's A operand is one contiguous run
+//    (k = 32q + s for P, 16q + s for F P over steps s), loaded as float4s.
+//  * dS stays in the MFMA accumulators (rows 32w + 16it + 4q + t, column m); a
+//    transposed copy in LDS is the B operand of the next chunk's P, and P goes
+//    through LDS (transposed) as the B operand of F P.
+//  * The next chunk's kp, F, X and gam are loaded into registers while the
+//    current chunk computes, so the serial loop does not wait on memory.
+//  * The 8 column slices of one (sequence, head) run on one XCD (workgroups go
+//    to the XCDs round robin), so the chunk's kp and F, which every slice reads,
+//    come from that XCD's L2 after the first slice's fetch.
+struct ScanOps {
+  float4 kp[8];       // kp[16w + m][32q .. 32q + 31]
+  float4 f[2][4];     // F[32w + 16it + m][16q .. 16q + 15]
+  float x[2][4];      // X[32w + 16it + 4q + t][j0 + m]
+  float4 gam[2];      // gam[32w + 16it + 4q .. + 3]
+};
+
+__device__ __forceinline__ void scan_fetch(const BwdTiles& w, int64_t bidx, int j0, int wave, int q, int m,
+                                           ScanOps& o) {
+  const float* kp = w.kp + bidx * (C * D) + (16 * wave + m) * D + 32 * q;
 #pragma unroll
-        for (int i = 0; i < RP; ++i) {
-          const float4 a4 = *reinterpret_cast<const float4*>(&kp[(r0 + i) * D + k]);
-          av[i][0] = a4.x; av[i][1] = a4.y; av[i][2] = a4.z; av[i][3] = a4.w;
-        }
+  for (int i = 0; i < 8; ++i) o.kp[i] = *reinterpret_cast<const float4*>(kp + 4 * i);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const float4 bv = *reinterpret_cast<const float4*>(&ds[k + kk][jb]);
+  for (int it = 0; it < 2; ++it) {
+    const float* F = w.F + bidx * (D * C) + (32 * wave + 16 * it + m) * C + 16 * q;
 #pragma unroll
-          for (int i = 0; i < RP; ++i) {
-            acc[i][0] = fmaf(av[i][kk], bv.x, acc[i][0]); acc[i][1] = fmaf(av[i][kk], bv.y, acc[i][1]);
-            acc[i][2] = fmaf(av[i][kk], bv.z, acc[i][2]); acc[i][3] = fmaf(av[i][kk], bv.w, acc[i][3]);
-          }
-        }
-      }
+    for (int i = 0; i < 4; ++i) o.f[it][i] = *reinterpret_cast<const float4*>(F + 4 * i);
+    const int r0 = 32 * wave + 16 * it + 4 * q;
+    const float* X = w.X + bidx * (D * D) + (size_t)r0 * D + j0 + m;
 #pragma unroll
-      for (int i = 0; i < RP; ++i)
-        *reinterpret_cast<float4*>(&pp[r0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    }
-    __syncthreads();
-    {  // dS = gam (.) dSn - F P + X: rows RF (t / CG) .. +RF-1
-      const float* F = w.F + bidx * (D * C);
-      const float* X = w.X + bidx * sd;
-      const float* gam = w.gam + bidx * D;
-      const int c0 = (t / CG) * RF;
-      float acc[RF][4];
-#pragma unroll
-      for (int i = 0; i < RF; ++i) {
-        const float g = gam[c0 + i];
-        const float4 xv = *reinterpret_cast<const float4*>(&X[(size_t)(c0 + i) * D + j0 + jb]);
-        acc[i][0] = g * ds[c0 + i][jb] + xv.x;
-        acc[i][1] = g * ds[c0 + i][jb + 1] + xv.y;
-        acc[i][2] = g * ds[c0 + i][jb + 2] + xv.z;
-        acc[i][3] = g * ds[c0 + i][jb + 3] + xv.w;
-      }
-      for (int r = 0; r < C; r += 4) {
-        float fv[RF][4];
-#pragma unroll
-        for (int i = 0; i < RF; ++i) {
-          const float4 f4 = *reinterpret_cast<const float4*>(&F[(c0 + i) * C + r]);
-          fv[i][0] = f4.x; fv[i][1] = f4.y; fv[i][2] = f4.z; fv[i][3] = f4.w;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 bv = *reinterpret_cast<const float4*>(&pp[r + rr][jb]);
-#pragma unroll
-          for (int i = 0; i < RF; ++i) {
-            acc[i][0] = fmaf(-fv[i][rr], bv.x, acc[i][0]); acc[i][1] = fmaf(-fv[i][rr], bv.y, acc[i][1]);
-            acc[i][2] = fmaf(-fv[i][rr], bv.z, acc[i][2]); acc[i][3] = fmaf(-fv[i][rr], bv.w, acc[i][3]);
-          }
-        }
-      }
-      __syncthreads();  // every read of dSn and P is done
-#pragma unroll
-      for (int i = 0; i < RF; ++i)
-        *reinterpret_cast<float4*>(&ds[c0 + i][jb]) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    }
-    __syncthreads();
-  }
-  if (p.ds0) {
-    float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
-    for (int x = t; x < D * DSW; x += 256) o[(size_t)(x / DSW) * D + j0 + x % DSW] = ds[x / DSW][x % DSW];
+    for (int t = 0; t < 4; ++t) o.x[it][t] = X[(size_t)t * D];
+    o.gam[it] = *reinterpret_cast<const float4*>(w.gam + bidx * D + r0);
   }
 }
 
-// The scan's launch: 32-column slices once four per (sequence, head) fill the
-// 256 compute units, 16-column slices below that.
+__global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
+  constexpr int DSW = 16, DSC = D / DSW;
+  __shared__ float dsT[DSW][D + 4];   // dSn, transposed: dsT[j][k]
+  __shared__ float pT[DSW][C + 4];    // P = kp dSn, transposed: pT[j][r]
+  // workgroup b: slice (b / 8) % DSC of pair (b / (8 DSC)) * 8 + b % 8, so that all
+  // slices of a pair share b % 8 (their XCD)
+  const int b = blockIdx.x;
+  const int pair = (b / (8 * DSC)) * 8 + b % 8, j0 = ((b / 8) % DSC) * DSW;
+  if (pair >= p.nseq * p.H) return;   // the same for the whole workgroup
+  const int n = pair / p.H, h = pair % p.H;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63, q = lane >> 4, m = lane & 15;
+  const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
+  const int nch = (int)((len + C - 1) / C);
+  const size_t sd = (size_t)D * D;
+  // this lane's dS entries: rows 32w + 16it + 4q + tt, column j0 + m
+  bg_f32x4 ds[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      float v = 0.f;
+      if (p.dsT) {
+        const size_t o = ((size_t)n * p.H + h) * sd + (size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m;
+        v = p.dsT_fp32 ? static_cast<const float*>(p.dsT)[o] : bf2f_u16(static_cast<const uint16_t*>(p.dsT)[o]);
+      }
+      ds[it][tt] = v;
+    }
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+    *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
+  ScanOps cur, nxt;
+  if (nch > 0) scan_fetch(w, (n + bos / C + nch - 1) * p.H + h, j0, wave, q, m, cur);
+  __syncthreads();
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t bidx = (n + bos / C + c) * p.H + h;
+    if (c > 0) scan_fetch(w, bidx - p.H, j0, wave, q, m, nxt);   // chunk c - 1: in flight meanwhile
+    {  // dSn(c) for the chunk's gradient products
+      float* dsn = w.dSn + bidx * sd;
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          dsn[(size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m] = ds[it][tt];
+    }
+    {  // P rows 16w .. 16w+15 = kp dSn, k = 32q + s
+      bg_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 bv = *reinterpret_cast<const float4*>(&dsT[m][32 * q + 4 * i]);
+        const float av[4] = {cur.kp[i].x, cur.kp[i].y, cur.kp[i].z, cur.kp[i].w};
+        const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc, 0, 0, 0);
+      }
+      *reinterpret_cast<float4*>(&pT[m][16 * wave + 4 * q]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();  // P complete; every read of dsT done
+    // dS = gam (.) dSn + X - F P, k = 16q + s
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const float gv[4] = {cur.gam[it].x, cur.gam[it].y, cur.gam[it].z, cur.gam[it].w};
+      bg_f32x4 acc;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = fmaf(gv[tt], ds[it][tt], cur.x[it][tt]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 bv = *reinterpret_cast<const float4*>(&pT[m][16 * q + 4 * i]);
+        const float av[4] = {-cur.f[it][i].x, -cur.f[it][i].y, -cur.f[it][i].z, -cur.f[it][i].w};
+        const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc, 0, 0, 0);
+      }
+      ds[it] = acc;
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
+    __syncthreads();  // the new dS is in place; every read of pT done
+    if (c > 0) cur = nxt;
+  }
+  if (p.ds0) {
+    float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) o[(size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m] = ds[it][tt];
+  }
+}
+
+// The scan's launch: 16-column slices, eight per (sequence, head); the grid is a
+// multiple of 64 workgroups (the XCD-aware mapping) and the extra ones exit at once.
 void launch_ds_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s) {
   const int64_t pairs = (int64_t)p.nseq * p.H;
-  if (pairs * (D / 32) >= 256)
-    hipLaunchKernelGGL(bwd_ds_scan_kernel<32>, dim3((unsigned)(pairs * (D / 32))), dim3(256), 0, s, p, w);
-  else
-    hipLaunchKernelGGL(bwd_ds_scan_kernel<16>, dim3((unsigned)(pairs * (D / 16))), dim3(256), 0, s, p, w);
+  const int64_t groups = (pairs + 7) / 8;
+  hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(groups * 8 * (D / 16))), dim3(256), 0, s, p, w);
 }
 
 // ---------------------------------------------------------------- gates and scatter
