@@ -779,35 +779,42 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
         for (int tt = 0; tt < 4; ++tt)
           dsn[(size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m] = ds[it][tt];
     }
-    {  // P rows 16w .. 16w+15 = kp dSn, k = 32q + s
-      bg_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    {  // P rows 16w .. 16w+15 = kp dSn, k = 32q + s, in four independent chains
+      bg_f32x4 acc[4] = {};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float4 bv = *reinterpret_cast<const float4*>(&dsT[m][32 * q + 4 * i]);
         const float av[4] = {cur.kp[i].x, cur.kp[i].y, cur.kp[i].z, cur.kp[i].w};
         const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc[e], 0, 0, 0);
       }
-      *reinterpret_cast<float4*>(&pT[m][16 * wave + 4 * q]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      const bg_f32x4 pv = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      *reinterpret_cast<float4*>(&pT[m][16 * wave + 4 * q]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
     }
     __syncthreads();  // P complete; every read of dsT done
-    // dS = gam (.) dSn + X - F P, k = 16q + s
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const float gv[4] = {cur.gam[it].x, cur.gam[it].y, cur.gam[it].z, cur.gam[it].w};
-      bg_f32x4 acc;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = fmaf(gv[tt], ds[it][tt], cur.x[it][tt]);
+    // dS = gam (.) dSn + X - F P, k = 16q + s, in two independent chains per row tile
+    {
+      bg_f32x4 acc[2][2] = {};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 bv = *reinterpret_cast<const float4*>(&pT[m][16 * q + 4 * i]);
-        const float av[4] = {-cur.f[it][i].x, -cur.f[it][i].y, -cur.f[it][i].z, -cur.f[it][i].w};
         const float bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc, 0, 0, 0);
+        for (int it = 0; it < 2; ++it) {
+          const float av[4] = {cur.f[it][i].x, cur.f[it][i].y, cur.f[it][i].z, cur.f[it][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[it][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc[it][e & 1], 0, 0, 0);
+        }
       }
-      ds[it] = acc;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const float gv[4] = {cur.gam[it].x, cur.gam[it].y, cur.gam[it].z, cur.gam[it].w};
+        const bg_f32x4 fp = acc[it][0] + acc[it][1];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) ds[it][tt] = fmaf(gv[tt], ds[it][tt], cur.x[it][tt]) - fp[tt];
+      }
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it)
