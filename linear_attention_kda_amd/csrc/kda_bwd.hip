@@ -271,7 +271,10 @@ __global__ void __launch_bounds__(256) bgemm2_kernel(Gemm2Args g) {
 // ---------------------------------------------------------------- chunk prep
 // One workgroup per batch (slot, head): loads the chunk's rows (zero past the
 // sequence), forms G, the gated tiles K Gam, Q Gam and K exp(G_last - G) (all <= 1
-// for g <= 0), dO' = scale dO and the per-row beta.
+// for g <= 0), dO' = scale dO and the per-row beta.  Thread t owns channels
+// 4 (t % 32) .. +3 of rows 8 (t / 32) .. +7: 16-byte loads of g, 8-byte loads of
+// q, k, v and dO, 16-byte stores of every tile; the exponentials are exp2 of
+// G log2(e).
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) {
   const int64_t bidx = blockIdx.x;
   const int64_t slot = bidx / p.H;
@@ -282,47 +285,72 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) 
   const int64_t rest = len - c * C;
   const int valid = (c < 0 || rest <= 0) ? 0 : rest < C ? (int)rest : C;
   const int t = threadIdx.x;
-  const int HD = p.H * D;
+  const int64_t HD = (int64_t)p.H * D;
   if (t < C) w.beta[bidx * C + t] = t < valid ? p.beta[(bos + c * C + t) * p.H + h] : 0.f;
   if (t == 0) w.valid[bidx] = valid;
-  // thread t: channel t % 128, rows 32 (t / 128) .. +31
-  const int ch = t & 127, half = t >> 7, r0 = 32 * half;
-  // G: inclusive cumsum over the chunk (natural log): each thread sums its 32 rows in
-  // registers, then the second half adds the first half's total
-  __shared__ float tot[2][D];
-  float gv[32];
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int c4 = 4 * (t & 31), rg = t >> 5, r0 = 8 * rg;
+  const int64_t tok0 = bos + c * C;
+  // G: inclusive cumsum over the chunk (natural log): each thread sums its 8 rows in
+  // registers, then adds the totals of the row groups before it
+  __shared__ float4 tot[8][32];
+  float4 gv[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int r = r0 + i;
-    gv[i] = r < valid ? p.g[((bos + c * C + r) * p.H + h) * D + ch] : 0.f;
+    gv[i] = r < valid ? *reinterpret_cast<const float4*>(&p.g[((tok0 + r) * p.H + h) * D + c4])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
-  for (int i = 1; i < 32; ++i) gv[i] += gv[i - 1];
-  tot[half][ch] = gv[31];
+  for (int i = 1; i < 8; ++i) {
+    gv[i].x += gv[i - 1].x; gv[i].y += gv[i - 1].y; gv[i].z += gv[i - 1].z; gv[i].w += gv[i - 1].w;
+  }
+  tot[rg][t & 31] = gv[7];
   __syncthreads();
-  const float off = half ? tot[0][ch] : 0.f;
-  const float Glast = tot[0][ch] + tot[1][ch];
-  const float gam = expf(Glast);
-  if (half == 0) w.gam[bidx * D + ch] = gam;
+  float4 off = make_float4(0.f, 0.f, 0.f, 0.f), gl = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 v = tot[k][t & 31];
+    if (k < rg) { off.x += v.x; off.y += v.y; off.z += v.z; off.w += v.w; }
+    gl.x += v.x; gl.y += v.y; gl.z += v.z; gl.w += v.w;
+  }
+  const float glast[4] = {gl.x, gl.y, gl.z, gl.w};
+  if (rg == 0)
+    *reinterpret_cast<float4*>(&w.gam[bidx * D + c4]) =
+        make_float4(exp2f(gl.x * kLog2e), exp2f(gl.y * kLog2e), exp2f(gl.z * kLog2e), exp2f(gl.w * kLog2e));
   const int64_t tb = bidx * (C * D);
-#pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     const int r = r0 + i;
-    const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
+    const int64_t row = (tok0 + r) * HD + (int64_t)h * D + c4;
     const bool in = r < valid;
-    const float qf = in ? bf2f_u16(p.q[row]) : 0.f;
-    const float kf = in ? bf2f_u16(p.k[row]) : 0.f;
-    const float vf = in ? bf2f_u16(p.v[row]) : 0.f;
-    const float df = in ? p.scale * bf2f_u16(p.dout[row]) : 0.f;
-    const float G = gv[i] + off;
-    const float e = expf(G);
-    const int64_t o = tb + r * D + ch;
-    w.G[o] = G;
-    w.kg[o] = kf * e;
-    w.qg[o] = qf * e;
-    w.kp[o] = kf * expf(Glast - G);
-    w.vv[o] = vf;
-    w.dO[o] = df;
+    const uint2 zero = make_uint2(0u, 0u);
+    const uint2 qu = in ? *reinterpret_cast<const uint2*>(&p.q[row]) : zero;
+    const uint2 ku = in ? *reinterpret_cast<const uint2*>(&p.k[row]) : zero;
+    const uint2 vu = in ? *reinterpret_cast<const uint2*>(&p.v[row]) : zero;
+    const uint2 du = in ? *reinterpret_cast<const uint2*>(&p.dout[row]) : zero;
+    const float qf[4] = {bf2f_u16(qu.x & 0xffffu), bf2f_u16(qu.x >> 16), bf2f_u16(qu.y & 0xffffu), bf2f_u16(qu.y >> 16)};
+    const float kf[4] = {bf2f_u16(ku.x & 0xffffu), bf2f_u16(ku.x >> 16), bf2f_u16(ku.y & 0xffffu), bf2f_u16(ku.y >> 16)};
+    const float vf[4] = {bf2f_u16(vu.x & 0xffffu), bf2f_u16(vu.x >> 16), bf2f_u16(vu.y & 0xffffu), bf2f_u16(vu.y >> 16)};
+    const float df[4] = {bf2f_u16(du.x & 0xffffu), bf2f_u16(du.x >> 16), bf2f_u16(du.y & 0xffffu), bf2f_u16(du.y >> 16)};
+    const float gr[4] = {gv[i].x + off.x, gv[i].y + off.y, gv[i].z + off.z, gv[i].w + off.w};
+    float o_g[4], o_kg[4], o_qg[4], o_kp[4], o_d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float eg = exp2f(gr[e] * kLog2e);
+      o_g[e] = gr[e];
+      o_kg[e] = kf[e] * eg;
+      o_qg[e] = qf[e] * eg;
+      o_kp[e] = kf[e] * exp2f((glast[e] - gr[e]) * kLog2e);
+      o_d[e] = p.scale * df[e];
+    }
+    const int64_t o = tb + r * D + c4;
+    *reinterpret_cast<float4*>(&w.G[o]) = make_float4(o_g[0], o_g[1], o_g[2], o_g[3]);
+    *reinterpret_cast<float4*>(&w.kg[o]) = make_float4(o_kg[0], o_kg[1], o_kg[2], o_kg[3]);
+    *reinterpret_cast<float4*>(&w.qg[o]) = make_float4(o_qg[0], o_qg[1], o_qg[2], o_qg[3]);
+    *reinterpret_cast<float4*>(&w.kp[o]) = make_float4(o_kp[0], o_kp[1], o_kp[2], o_kp[3]);
+    *reinterpret_cast<float4*>(&w.vv[o]) = make_float4(vf[0], vf[1], vf[2], vf[3]);
+    *reinterpret_cast<float4*>(&w.dO[o]) = make_float4(o_d[0], o_d[1], o_d[2], o_d[3]);
   }
 }
 
