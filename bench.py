@@ -326,7 +326,8 @@ def dim_bench(wid: int, d: int, steps: int, warmup: int):
         f"{gbs:.0f} GB/s ({100 * gbs / perfmodel.HBM_PEAK_GBS:.1f}% of HBM peak)")
     return {"workload": f"head dim {d}, {w.name}", "head_dim": d, "unit": "tokens/s",
             "value": w.tokens / (ms * 1e-3), "ms_per_step": ms,
-            "workspace_bytes": binding.dim_workspace_bytes(N, w.tokens, H, d),
+            "workspace_bytes": (binding.plan(N, w.T, H, bool(w.n_seqs), 0)[2] if d == 64
+                                else binding.dim_workspace_bytes(N, w.tokens, H, d)),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": perfmodel.HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gbs / perfmodel.HBM_PEAK_GBS, "traffic": None,
                          "kernel": ("kda_fwd call at d=64: kda_fwd_kernel<1, false, 64>" if d == 64 else

@@ -44,9 +44,9 @@
  * scratch instead and allocates nothing.
  * Asynchrony: kda_fwd enqueues work on `stream` (a hipStream_t, or NULL for
  * the null stream) and returns; results are valid after the caller
- * synchronises that stream.  Calls are thread-safe (the pool is created under
- * a lock; otherwise no global mutable state except the thread-local error
- * text).
+ * synchronises that stream.  Calls are thread-safe (the pool, and kda_bwd's
+ * side stream, are created under a lock; otherwise no global mutable state
+ * except the thread-local error text).
  * Errors: invalid arguments are rejected before any launch with a negative
  * status and no output touched; kda_last_error() then holds a description.
  * There is no fallback path.
@@ -116,8 +116,10 @@ typedef enum {
  *             sequence (varlen with cu_seqlens[num_seqs] < T) are not written.
  *  stream     hipStream_t to launch on (NULL = null stream).
  *
- * d = 64 runs on the d = 128 kernel with the key channels past 64 read as zero,
- * one workgroup per (sequence, head) and no workspace.  d = 256 runs as two
+ * d = 64 runs on the d = 128 kernels with the key channels past 64 read as
+ * zero, one 64-column value slice per (sequence, head, segment): the same plan,
+ * sequence splitting and workspace as d = 128 (kda_plan), with value_splits
+ * always 1.  d = 256 runs as two
  * launches: every (chunk, head) first writes a record of its chunk-local
  * operands (gated keys and queries, the transposed state-update operand,
  * (I + A)^-1 diag(beta), the masked Q K^T and the chunk decay) into a workspace
@@ -143,7 +145,7 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, 
  *            of the later segments' chunks); sequences are split only as far
  *            as those fit, so every size runs, very long ones in fewer and
  *            longer segments than kda_fwd would use;
- *   d = 64:  no workspace;
+ *   d = 64:  as d = 128;
  *   d = 256: the per-chunk records must fit (slots x H x record bytes, see
  *            kda_dim_workspace_bytes); larger calls return KDA_ERR_WORKSPACE
  *            before any launch.
@@ -188,7 +190,9 @@ const char* kda_last_error(void);
  *                    0 when no sequence can be split (the call then launches
  *                    the main kernel only).
  * The environment variable KDA_VSPLIT (1 or 2) overrides the slice count
- * (2 also turns sequence splitting off).  Host only; returns KDA_ERR_SHAPE for
+ * (2 also turns sequence splitting off).  At head dimension 64 kda_fwd uses
+ * the same plan with one value slice (value_splits 1, KDA_VSPLIT ignored) and
+ * the same workspace.  Host only; returns KDA_ERR_SHAPE for
  * N <= 0, H <= 0 or T < 0, KDA_ERR_NULL for NULL outputs, KDA_ERR_HIP if the
  * device query fails.
  */
@@ -320,11 +324,11 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
                          const float* dk, const float* dv, const float* dg, const float* dbeta,
                          const float* d_initial_state);
 
-/* Workspace bytes kda_fwd / kda_gdn_fwd take at head dimension d = 64 or 256
+/* Per-chunk record bytes kda_fwd / kda_gdn_fwd take at head dimension d = 256
  * for N sequences over `rows` packed rows (T with cu_seqlens, else B*T) of H
- * heads: none at d = 64; at d = 256 one record per (chunk slot, head),
- * N + ceil(rows / 64) + 1 slots (-1 for N <= 0, rows < 0, H <= 0 or another d).
- * Host only. */
+ * heads: one record per (chunk slot, head), N + ceil(rows / 64) + 1 slots.
+ * 0 for d = 64, which takes kda_plan's workspace instead (-1 for N <= 0,
+ * rows < 0, H <= 0 or another d).  Host only. */
 int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
