@@ -37,16 +37,25 @@
  *
  * Ownership: every pointer is caller-owned memory; the library never retains
  * or frees it.  A call that may split sequences takes a workspace (size from
- * kda_plan) from a stream-ordered memory pool the library owns, one per
- * device, and returns it to the pool in stream order at the end of the call;
- * the pool keeps up to 2 GiB reserved for later calls and hands the rest back
- * to the device at the next synchronisation.  kda_fwd_noalloc uses a static
- * scratch instead and allocates nothing.
+ * kda_plan) that the library owns.  It keeps one workspace per stream (per
+ * stream and thread for hipStreamPerThread), at most four of up to 2 GiB in
+ * total per device, and reuses it for later calls on that stream, which orders
+ * them; a call enqueues no synchronisation of its own.  A kept workspace that
+ * must grow is reallocated after its stream has drained (a host wait); when a
+ * new stream's workspace does not fit, every kept workspace of the device is
+ * freed after the device has drained.  A workspace larger than 2 GiB comes
+ * from a stream-ordered pool for that call alone.  kda_release_workspaces()
+ * frees the kept workspaces of the current device.  A stream handle that is
+ * destroyed and created again names a new stream: synchronise a stream before
+ * destroying it while calls on it may still run.  kda_fwd_noalloc uses a
+ * static scratch instead and allocates nothing.
  * Asynchrony: kda_fwd enqueues work on `stream` (a hipStream_t, or NULL for
  * the null stream) and returns; results are valid after the caller
- * synchronises that stream.  Calls are thread-safe (the pool, and kda_bwd's
- * side stream, are created under a lock; otherwise no global mutable state
- * except the thread-local error text).
+ * synchronises that stream.  A call waits for the device on the host only when
+ * a kept workspace is reallocated.  Calls are thread-safe: the kept workspaces
+ * of a device are taken under a lock held while a call enqueues its work, and
+ * the pool and kda_bwd's side stream are created under a lock; otherwise there
+ * is no global mutable state except the thread-local error text.
  * Errors: invalid arguments are rejected before any launch with a negative
  * status and no output touched; kda_last_error() then holds a description.
  * There is no fallback path.
@@ -123,10 +132,10 @@ typedef enum {
  * launches: every (chunk, head) first writes a record of its chunk-local
  * operands (gated keys and queries, the transposed state-update operand,
  * (I + A)^-1 diag(beta), the masked Q K^T and the chunk decay) into a workspace
- * of kda_dim_workspace_bytes() bytes from the library's pool, then one
- * workgroup per (sequence, head, value slice) walks the chunks in order.  These
- * sizes never split sequences, and the 16-token range limit on g above applies
- * to them as well.
+ * of kda_dim_workspace_bytes() bytes taken like kda_fwd's workspace (see
+ * Ownership), then one workgroup per (sequence, head, value slice) walks the
+ * chunks in order.  d = 256 never splits sequences.  The 16-token range limit
+ * on g above applies at both sizes.
  */
 kda_status kda_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float scale, const void* initial_state, int initial_dtype, void* final_state,
@@ -186,7 +195,7 @@ const char* kda_last_error(void);
  *   workgroups       workgroups of the main kernel (some exit at once when
  *                    fewer sequences are split than the bound allows);
  *   value_splits     value-column slices per (sequence, head), 1 or 2;
- *   workspace_bytes  device workspace a call takes from the library's pool;
+ *   workspace_bytes  device workspace a call takes (see Ownership);
  *                    0 when no sequence can be split (the call then launches
  *                    the main kernel only).
  * The environment variable KDA_VSPLIT (1 or 2) overrides the slice count
@@ -305,8 +314,8 @@ kda_status kda_gdn_decode_check(const void* q, const void* k, const void* v, con
  * sufficient): every product that pairs exp(G_r) with exp(-G_i) inside a chunk
  * is evaluated with the same 16-row block references as the forward pass.
  * Memory: a workspace of kda_bwd_workspace_bytes(N, rows, H) bytes (rows = T with
- * cu_seqlens, else B*T) taken from the library's stream-ordered pool for the
- * call.  Asynchrony and errors as kda_fwd.
+ * cu_seqlens, else B*T), taken like kda_fwd's workspace (see Ownership).
+ * Asynchrony and errors as kda_fwd.
  */
 kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                    float scale, const void* initial_state, int initial_dtype, const void* d_out,
@@ -330,6 +339,12 @@ kda_status kda_bwd_check(const void* q, const void* k, const void* v, const floa
  * 0 for d = 64, which takes kda_plan's workspace instead (-1 for N <= 0,
  * rows < 0, H <= 0 or another d).  Host only. */
 int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, int32_t D);
+
+/* kda_release_workspaces — frees the workspaces the library keeps between calls
+ * on the current device, after the device has drained (a host wait); later
+ * calls allocate again.  It takes the lock the calls take, so it may run
+ * beside calls on other threads.  Returns KDA_ERR_HIP on a runtime error. */
+kda_status kda_release_workspaces(void);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
  * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  It is

@@ -82,6 +82,8 @@ def load_library():
         lib.kda_bwd_workspace_bytes.argtypes = [_i32, _i64, _i32]
         lib.kda_dim_workspace_bytes.restype = _i64
         lib.kda_dim_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32]
+        lib.kda_release_workspaces.restype = ctypes.c_int
+        lib.kda_release_workspaces.argtypes = []
         lib.kda_plan.restype = ctypes.c_int
         lib.kda_plan.argtypes = [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32),
                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
@@ -103,6 +105,17 @@ def _state_dtype(t) -> int:
     if t.dtype == torch.float32:
         return KDA_FP32
     raise TypeError(f"states must be bfloat16 or float32, got {t.dtype}")
+
+
+def release_workspaces(device=None):
+    """Free the workspaces the library keeps between calls on `device` (default:
+    torch's current device), after the calls that used them have finished."""
+    import torch
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        st = lib.kda_release_workspaces()
+    if st != 0:
+        raise KdaError(st, "kda_release_workspaces", _detail(lib, st))
 
 
 def plan(n_sequences: int, T: int, heads: int, varlen: bool = False,

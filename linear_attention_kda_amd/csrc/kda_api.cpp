@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <thread>
 
 #include "../../include/kda.h"
 #include "kda_internal.h"
@@ -250,7 +251,148 @@ hipError_t side_stream(hipStream_t* out) {
   return hipSuccess;
 }
 
-// Head dimension 256: per-chunk records in a workspace from the pool, then the
+// Workspaces kept between calls.  Taken from the pool per call, a workspace made
+// the next call's hipMallocFromPoolAsync wait on the host until the previous
+// call's kernels had finished; an event recorded per call to order reuse across
+// streams costs the device a few microseconds between calls.  A workspace is
+// therefore kept per stream and reused by later calls on that stream, which the
+// stream itself orders: a call enqueues no synchronisation of its own.  The
+// per-thread default stream is one handle for many streams, so its buffers are
+// also keyed by the calling thread.  At most kCacheEntries buffers of
+// kCacheBytes in total are kept per device.  A buffer that must grow is freed
+// after its stream has drained (host wait); when a new stream's buffer does not
+// fit, every kept buffer is freed after the device has drained.  Larger
+// workspaces come from the pool for the one call.  A lease holds its device's
+// lock from acquire() to release(), i.e. while the call enqueues its work.
+constexpr size_t kCacheBytes = 2ull << 30;
+constexpr size_t kCacheGrain = 32ull << 20;
+constexpr int kCacheEntries = 4;
+
+struct CacheEntry {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipStream_t stream = nullptr;
+  std::thread::id thread;  // set for the per-thread default stream only
+};
+
+struct DeviceCache {
+  std::mutex mu;
+  CacheEntry e[kCacheEntries];
+};
+
+DeviceCache g_cache[64];
+
+// Frees every kept buffer of a device once the device has drained.
+hipError_t drop_all(DeviceCache& c) {
+  bool any = false;
+  for (const CacheEntry& x : c.e) any = any || x.ptr != nullptr;
+  if (!any) return hipSuccess;
+  hipError_t err = hipDeviceSynchronize();
+  for (CacheEntry& x : c.e) {
+    if (x.ptr != nullptr) {
+      const hipError_t e = hipFree(x.ptr);
+      if (err == hipSuccess) err = e;
+    }
+    x = CacheEntry{};
+  }
+  return err;
+}
+
+class Workspace {
+ public:
+  Workspace() = default;
+  Workspace(const Workspace&) = delete;
+  Workspace& operator=(const Workspace&) = delete;
+  ~Workspace() { (void)release(); }
+
+  // A workspace of at least `bytes` bytes for work enqueued on `hs`.
+  hipError_t acquire(size_t bytes, hipStream_t hs) {
+    hs_ = hs;
+    if (bytes == 0) return hipSuccess;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    const size_t need = (bytes + kCacheGrain - 1) / kCacheGrain * kCacheGrain;
+    if (need <= kCacheBytes) {
+      DeviceCache& c = g_cache[dev];
+      lock_ = std::unique_lock<std::mutex>(c.mu);
+      const std::thread::id tid =
+          hs == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+      CacheEntry* mine = nullptr;
+      size_t total = 0;
+      for (CacheEntry& x : c.e) {
+        total += x.bytes;
+        if (x.ptr != nullptr && x.stream == hs && x.thread == tid) mine = &x;
+      }
+      if (mine != nullptr && mine->bytes < need) {  // grow: free after this stream's work
+        err = hipStreamSynchronize(hs);
+        const hipError_t e = hipFree(mine->ptr);
+        if (err == hipSuccess) err = e;
+        total -= mine->bytes;
+        *mine = CacheEntry{};
+        if (err != hipSuccess) {
+          lock_.unlock();
+          return err;
+        }
+        mine = nullptr;
+      }
+      if (mine == nullptr) {
+        CacheEntry* slot = nullptr;
+        for (CacheEntry& x : c.e)
+          if (x.ptr == nullptr) { slot = &x; break; }
+        if (slot == nullptr || total + need > kCacheBytes) {
+          err = drop_all(c);
+          slot = &c.e[0];
+          if (err != hipSuccess) {
+            lock_.unlock();
+            return err;
+          }
+        }
+        err = hipMalloc(&slot->ptr, need);
+        if (err != hipSuccess) {
+          *slot = CacheEntry{};
+          lock_.unlock();
+          return err;
+        }
+        slot->bytes = need;
+        slot->stream = hs;
+        slot->thread = tid;
+        mine = slot;
+      }
+      ptr_ = mine->ptr;
+      return hipSuccess;
+    }
+    hipMemPool_t pool = nullptr;
+    err = workspace_pool(&pool);
+    if (err == hipSuccess) err = hipMallocFromPoolAsync(&pooled_, bytes, pool, hs);
+    if (err != hipSuccess) pooled_ = nullptr;
+    ptr_ = pooled_;
+    return err;
+  }
+
+  void* ptr() const { return ptr_; }
+
+  // Called once every launch of the call has been enqueued on the stream.
+  hipError_t release() {
+    hipError_t err = hipSuccess;
+    if (pooled_ != nullptr) {
+      err = hipFreeAsync(pooled_, hs_);
+      pooled_ = nullptr;
+    }
+    ptr_ = nullptr;
+    if (lock_.owns_lock()) lock_.unlock();
+    return err;
+  }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  void* ptr_ = nullptr;
+  void* pooled_ = nullptr;
+  hipStream_t hs_ = nullptr;
+};
+
+// Head dimension 256: per-chunk records in a workspace (kept between calls), then the
 // serial state pass (no sequence splitting).
 kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, float scale, const void* initial_state,
@@ -280,7 +422,7 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
   p.D = D;
   p.slots = rows > 0 ? kda::dim_slots(N, rows) : 0;
   const size_t bytes = (size_t)p.slots * H * kda::dim_record_bytes(D);
-  void* ws = nullptr;
+  Workspace ws;
   if (bytes > 0 && ext != nullptr) {
     if (bytes > ext->bytes)
       return fail(KDA_ERR_WORKSPACE,
@@ -288,23 +430,19 @@ kda_status fwd_dim_impl(const void* q, const void* k, const void* v, const float
                   "bytes of the static scratch", D, bytes, ext->bytes);
     p.ws = static_cast<char*>(ext->ptr);
   } else if (bytes > 0) {
-    hipMemPool_t pool = nullptr;
-    hipError_t e = workspace_pool(&pool);
-    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, bytes, pool, hs);
+    const hipError_t e = ws.acquire(bytes, hs);
     if (e != hipSuccess)
       return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
-    p.ws = static_cast<char*>(ws);
+    p.ws = static_cast<char*>(ws.ptr());
   }
   if (log_enabled())
     std::fprintf(stderr, "[kda] launch: %s D=%d N=%d H=%d T=%lld record_slots=%lld workspace=%zu%s\n",
                  g_scalar ? "gdn" : "kda", D, N, H, (long long)T, (long long)p.slots, bytes,
                  ext ? " (static scratch)" : "");
   const hipError_t err = kda::launch_fwd_dim(p, hs);
-  if (ws != nullptr) {
-    const hipError_t e = hipFreeAsync(ws, hs);
-    if (err == hipSuccess && e != hipSuccess)
-      return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
-  }
+  const hipError_t e = ws.release();
+  if (err == hipSuccess && e != hipSuccess)
+    return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
   if (err != hipSuccess)
     return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return KDA_OK;
@@ -358,7 +496,7 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
   p.dk = K;
   p.cus = cus;
   p.seg_min = lp.seg_min;
-  void* ws = nullptr;
+  Workspace ws;
   if (lp.emax > 0) {
     char* base = nullptr;
     if (ext != nullptr) {
@@ -367,12 +505,10 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
                     lp.workspace, ext->bytes);
       base = static_cast<char*>(ext->ptr);
     } else {
-      hipMemPool_t pool = nullptr;
-      hipError_t e = workspace_pool(&pool);
-      if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, lp.workspace, pool, hs);
+      const hipError_t e = ws.acquire(lp.workspace, hs);
       if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "workspace of %zu bytes: %s", lp.workspace, hipGetErrorString(e));
-      base = static_cast<char*>(ws);
+      base = static_cast<char*>(ws.ptr());
     }
     const kda::WorkspaceLayout wl = kda::workspace_layout(lp.ucap, H, lp.emax);
     p.emax = lp.emax;
@@ -390,11 +526,9 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
                  cu_seqlens != nullptr, lp.emax, lp.ucap, lp.workspace,
                  ext ? " (static scratch)" : "");
   const hipError_t err = kda::launch_fwd(p, lp.nsplit, hs);
-  if (ws != nullptr) {
-    const hipError_t e = hipFreeAsync(ws, hs);
-    if (err == hipSuccess && e != hipSuccess)
-      return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
-  }
+  const hipError_t e = ws.release();
+  if (err == hipSuccess && e != hipSuccess)
+    return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e));
   if (err != hipSuccess)
     return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return KDA_OK;
@@ -423,6 +557,21 @@ const char* kda_status_string(int status) {
 }
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status kda_release_workspaces(void) {
+  g_last_error.clear();
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess && (dev < 0 || dev >= 64)) err = hipErrorInvalidDevice;
+  if (err == hipSuccess) {
+    DeviceCache& c = g_cache[dev];
+    std::lock_guard<std::mutex> lock(c.mu);
+    err = drop_all(c);
+  }
+  if (err != hipSuccess)
+    return fail(KDA_ERR_HIP, "releasing the workspaces: %s", hipGetErrorString(err));
+  return KDA_OK;
+}
 
 kda_status kda_fwd_check(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float scale, const void* initial_state,
@@ -680,16 +829,14 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
   const int64_t nb = bwd_slots(N, rows) * H;
   const size_t wbytes = bwd_workspace_bytes(N, rows, H);
-  hipMemPool_t pool = nullptr;
-  void* ws = nullptr;
-  e = workspace_pool(&pool);
-  if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, wbytes, pool, hs);
+  Workspace ws;
+  e = ws.acquire(wbytes, hs);
   if (e != hipSuccess)
     return fail(KDA_ERR_HIP, "backward workspace of %zu bytes: %s", wbytes, hipGetErrorString(e));
   // carve the per-chunk tiles
   kda::BwdTiles w{};
   {
-    float* base = static_cast<float*>(ws);
+    float* base = static_cast<float*>(ws.ptr());
     size_t off = 0;
     auto take = [&](size_t per) { float* r = base + off; off += (size_t)nb * per; return r; };
     float** t1[] = {&w.G, &w.kg, &w.qg, &w.kp, &w.vv, &w.dO,
@@ -705,7 +852,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     w.gam = take(128);
     w.valid = reinterpret_cast<int*>(take(1));
   }
-  uint16_t* fwd_out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) +
+  uint16_t* fwd_out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws.ptr()) +
                                                    ((nb * kda::BwdTiles::floats_per_batch() * 4 + 255) & ~(size_t)255));
   hipError_t err = hipSuccess;
   if (rows > 0) {
@@ -767,7 +914,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32; bp.ds0 = d_initial_state;
     err = kda::launch_bwd_scan_only(bp, hs);
   }
-  const hipError_t e2 = hipFreeAsync(ws, hs);
+  const hipError_t e2 = ws.release();
   if (err != hipSuccess) return fail(KDA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(err));
   if (e2 != hipSuccess) return fail(KDA_ERR_HIP, "workspace release: %s", hipGetErrorString(e2));
   return KDA_OK;

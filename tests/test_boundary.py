@@ -38,7 +38,7 @@ def test_header_declares_expected_entry_points():
                                   "kda_fwd", "kda_fwd_check", "kda_fwd_noalloc",
                                   "kda_gdn_decode", "kda_gdn_decode_check", "kda_gdn_fwd",
                                   "kda_gdn_fwd_check", "kda_last_error", "kda_plan",
-                                  "kda_status_string"]
+                                  "kda_release_workspaces", "kda_status_string"]
 
 
 def test_library_exports_every_header_symbol(lib):
