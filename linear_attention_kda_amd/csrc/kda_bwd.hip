@@ -189,59 +189,6 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   bg_store<NT>(acc, a, b, m0, n0);
 }
 
-// Two 64 x 64 products that share their right operand, X1 B^T and X2 B^T, with B
-// staged once (all three stored [64][K]).  `o1` carries X1, B and the first output
-// (mask, alpha, row scale); `o1b`, if its C is set, stores the same accumulators a
-// second time with its own mask, alpha and row scale; `o2` carries X2 in A and the
-// second output.  Used for P = strict_lower(kg kh^T) with A = diag(beta) P and
-// M = lower_incl(qg kh^T), and for dM = lower_incl(dO' U^T) with
-// dA = strict_lower(-dY U^T).
-__global__ void __launch_bounds__(256) bgemm_shared_b_kernel(GemmArgs o1, GemmArgs o1b, GemmArgs o2) {
-  __shared__ float Bs[16][80];   // B^T slice, [k][n]
-  __shared__ float X1s[16][80];  // X1^T slice, [k][m]
-  __shared__ float X2s[16][80];  // X2^T slice, [k][m]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, q4 = lane >> 4;
-  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
-  const int64_t b = blockIdx.z;
-  const float* x1 = o1.A + b * o1.sA;
-  const float* bm = o1.B + b * o1.sB;
-  const float* x2 = o2.A + b * o2.sA;
-  bg_f32x4 acc1[2][2], acc2[2][2];
-  bg_zero<64>(acc1);
-  bg_zero<64>(acc2);
-  for (int k0 = 0; k0 < o1.K; k0 += 16) {
-    // rows tid / 4 of X1, X2 and B, four consecutive k each
-    const int r = tid >> 2, k = (tid & 3) * 4;
-    const float4 v1 = *reinterpret_cast<const float4*>(x1 + (int64_t)r * o1.lda + k0 + k);
-    const float4 v2 = *reinterpret_cast<const float4*>(x2 + (int64_t)r * o2.lda + k0 + k);
-    const float4 vb = *reinterpret_cast<const float4*>(bm + (int64_t)r * o1.ldb + k0 + k);
-    X1s[k][r] = v1.x; X1s[k + 1][r] = v1.y; X1s[k + 2][r] = v1.z; X1s[k + 3][r] = v1.w;
-    X2s[k][r] = v2.x; X2s[k + 1][r] = v2.y; X2s[k + 2][r] = v2.z; X2s[k + 3][r] = v2.w;
-    Bs[k][r] = vb.x; Bs[k + 1][r] = vb.y; Bs[k + 2][r] = vb.z; Bs[k + 3][r] = vb.w;
-    __syncthreads();
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int kk = 4 * s4 + q4;
-      const float b0 = Bs[kk][wn + m16], b1 = Bs[kk][wn + 16 + m16];
-      const float a0 = X1s[kk][wm + m16], a1 = X1s[kk][wm + 16 + m16];
-      const float c0 = X2s[kk][wm + m16], c1 = X2s[kk][wm + 16 + m16];
-      acc1[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc1[0][0], 0, 0, 0);
-      acc1[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc1[0][1], 0, 0, 0);
-      acc1[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc1[1][0], 0, 0, 0);
-      acc1[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc1[1][1], 0, 0, 0);
-      acc2[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(c0, b0, acc2[0][0], 0, 0, 0);
-      acc2[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(c0, b1, acc2[0][1], 0, 0, 0);
-      acc2[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(c1, b0, acc2[1][0], 0, 0, 0);
-      acc2[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(c1, b1, acc2[1][1], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-  bg_store<64>(acc1, o1, b, 0, 0);
-  if (o1b.C) bg_store<64>(acc1, o1b, b, 0, 0);
-  bg_store<64>(acc2, o2, b, 0, 0);
-}
-
 // A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
 // so that the first product never goes through memory.
 struct Gemm2Args {
@@ -1050,50 +997,60 @@ hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_from_states(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+// Products that need the checkpoints but not the state gradients: R, U, dO' S^T
+// and dM.  They may run beside the scan.
+hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
+                                     hipStream_t s) {
   const int NB = (int)batches;
   const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
   // R = V - kg S;  U = T diag(b) R
-  {
-    GemmArgs a = mm(C, D, D, w.kg, t1, D, w.S, t3, D, w.R, t1, D, NB);
-    a.alpha = -1.f; a.Dm = w.vv; a.sD = t1; a.ldd = D;
-    gemm(false, false, a, s);
-    GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
-    u.ks = w.beta; u.sks = C;
-    gemm(false, false, u, s);
-  }
-  // serial recurrence of dS over chunks
+  GemmArgs a = mm(C, D, D, w.kg, t1, D, w.S, t3, D, w.R, t1, D, NB);
+  a.alpha = -1.f; a.Dm = w.vv; a.sD = t1; a.ldd = D;
+  gemm(false, false, a, s);
+  GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
+  u.ks = w.beta; u.sks = C;
+  gemm(false, false, u, s);
+  gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
+  GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
+  dm.mask = 2;
+  gemm(false, true, dm, s);
+  (void)p;
+  return hipGetLastError();
+}
+
+// The serial recurrence of dS over chunks: it reads only chunk-local tiles.
+hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s) {
   launch_ds_scan(p, w, s);
-  // chunk gradients
-  {
-    GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
-    du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
-    gemm(false, false, du, s);
-    gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
-    {
-      GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
-      dm.mask = 2;
-      GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
-      da.alpha = -1.f; da.mask = 1;
-      GemmArgs none{};
-      hipLaunchKernelGGL(bgemm_shared_b_kernel, dim3(1, 1, NB), dim3(256), 0, s, dm, none, da);
-    }
-    gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
-    gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
-    GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
-    k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
-    gemm(false, true, k1, s);
-    // dM kh, diag(b) dA kh and dkh through the gates, with block references: into the
-    // tiles MtdO and dU (free once dU and dY exist) and dkh
-    hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
-  }
+  return hipGetLastError();
+}
+
+// Everything that needs the state gradients, after the scan and the state products.
+hipError_t launch_bwd_grads(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
+  const int NB = (int)batches;
+  const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
+  GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
+  du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
+  gemm(false, false, du, s);
+  gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
+  GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
+  da.alpha = -1.f; da.mask = 1;
+  gemm(false, true, da, s);
+  gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
+  GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
+  k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
+  gemm(false, true, k1, s);
+  // dM kh, diag(b) dA kh and dkh through the gates, with block references: into the
+  // tiles MtdO and dU (free once dU and dY exist) and dkh
+  hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
-  const hipError_t e = launch_bwd_chunk_local(p, w, batches, s);
-  return e != hipSuccess ? e : launch_bwd_from_states(p, w, batches, s);
+  hipError_t e = launch_bwd_chunk_local(p, w, batches, s);
+  if (e == hipSuccess) e = launch_bwd_state_products(p, w, batches, s);
+  if (e == hipSuccess) e = launch_bwd_scan(p, w, s);
+  return e != hipSuccess ? e : launch_bwd_grads(p, w, batches, s);
 }
 
 }  // namespace kda

@@ -149,12 +149,18 @@ struct GemmArgs {
 
 size_t bwd_tile_floats();
 hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
-// The two halves of launch_bwd: the chunk-local tiles that need no state
-// checkpoint (prep, P / A / M, the inverse, M^T dO', F and X), then everything
-// from the checkpoints on.  The first may run while the checkpointing forward
-// pass still runs; the second must follow both.
+// The parts of launch_bwd, in dependency order:
+//  * chunk_local: the tiles that need no state checkpoint (prep, P / A / M, the
+//    inverse, M^T dO', F and X); it may run beside the checkpointing forward pass;
+//  * state_products: R, U, dO' S^T and dM, after chunk_local and the forward pass;
+//  * scan: the state gradients over the chunks, after chunk_local only, so that it
+//    may run beside state_products;
+//  * grads: the rest, after state_products and scan.
 hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
-hipError_t launch_bwd_from_states(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
+hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
+                                     hipStream_t stream);
+hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t stream);
+hipError_t launch_bwd_grads(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
 // The initial-state gradients alone, for calls without tokens.
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 
