@@ -516,7 +516,7 @@ kda_status fwd_impl(const void* q, const void* k, const void* v, const float* g,
     p.o0 = reinterpret_cast<uint16_t*>(base + wl.o0);
     p.st = reinterpret_cast<float*>(base + wl.st);
     p.sb = reinterpret_cast<uint16_t*>(base + wl.sb);
-    p.tail_flag = reinterpret_cast<int*>(base + wl.flag);
+    p.state_flags = reinterpret_cast<int*>(base + wl.flag);
   }
   if (log_enabled())
     std::fprintf(stderr,

@@ -1233,6 +1233,9 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
   static_assert(plan_ints(kSortLimit, 512, true) * 4 <= 5 * sizeof(sm.kg),
                 "the plan fits in the operand tiles");
   const int tid = threadIdx.x;
+  // the tail kernel's publication counters start at zero
+  if (blockIdx.x == 0 && p.state_flags != nullptr)
+    for (int i = tid; i < p.emax * p.H; i += NT) p.state_flags[i] = 0;
 
   // ---- workgroup -> (task rank, head, value slice); slices of one head share an XCD
   const int nsplit = DK / NV;

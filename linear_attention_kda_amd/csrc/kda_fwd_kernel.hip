@@ -12,20 +12,37 @@ namespace kda {
 namespace {
 
 // ============================================================================ scan and fix-up
-// Two launches follow the main kernel when sequences were split.
-//  * phase 0: the scan, one unit per (split sequence, head, 16-column block of
-//    the state): S_1 is segment 0's end state; for p = 1 .. P-1 it forms
-//    S_{p+1} = A_p S_p + B_p in fp32 and stores the bf16 operand copy of S_p for
-//    p >= 2 (segment 0's task stored that of S_1); S_P is the final state.  The
-//    same launch fixes up the outputs of segment 1, which need only S_1.
-//  * phase 1: the output fix-up of the later segments.
-// A fix-up unit is one chunk of one (sequence, head): o_t = O0_t + S_p^T Q~_t,
-// with Q~ read from (and o written back to) the output rows.  Every load of a
-// unit is issued at its start.  Wave w forms output columns 32w..32w+31 as
-// O^T = S_p^T Q~^T on bf16 MFMA 16x16x32; Q~ is staged through LDS so that each
-// wave reads all 64 tokens.  The plan lives in dynamic LDS (plan_ints(N, 0,
-// false) ints); every launch walks its units in a grid-stride loop.
+// One launch follows the main kernel when sequences were split.
+//  * Scan units, one per (split sequence, head, 16-column block of the state), in
+//    the first workgroups: S_1 is segment 0's end state; for p = 1 .. P-1 a unit
+//    forms S_{p+1} = A_p S_p + B_p in fp32, and in step p >= 2 it stores the bf16
+//    fix-up operand of S_p and then publishes it (below); S_P is the final state.
+//  * Fix-up units: one chunk of one (sequence, head), o_t = O0_t + S_p^T Q~_t,
+//    with Q~ read from (and o written back to) the output rows.  Units of segment
+//    1 need only S_1, which the main kernel stored; a unit of a later segment
+//    first waits until every column block of its S_p has been published.
+// Publication: the scan's stores of the operand copy are device-scope (sc1, written
+// through to the point of coherence of all XCDs), every wave waits for its stores
+// to complete, and after a barrier one thread adds 1 to the (slot, head) counter
+// with a device-scope atomic.  A waiting workgroup polls the counter with
+// device-scope loads until it reaches the number of column blocks, then reads the
+// copy with device-scope loads, so no XCD's L2 can serve it stale.  The counters
+// are zeroed by the main kernel.  Scan units never wait, and they occupy the
+// lowest workgroup indices, which are dispatched first, so a waiting workgroup
+// never holds back the work it waits for; the wait is bounded all the same.
+// Every load of a fix-up unit is issued at its start.  Wave w forms output columns
+// 32w..32w+31 as O^T = S_p^T Q~^T on bf16 MFMA 16x16x32; Q~ is staged through LDS
+// so that each wave reads all 64 tokens.  The plan lives in dynamic LDS
+// (plan_ints(N, 0, false) ints).
 constexpr int TAIL_NT = 256;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+// cache policy of a buffer access: device scope (sc1), coherent across the XCDs
+constexpr int kDeviceScope = 16;
+// polls of a publication counter before a wait gives up (~1-2 s): reached only if the
+// scan never published, which would be a defect; the unit then runs on whatever the
+// operand holds instead of hanging the device
+constexpr int kWaitPolls = 1 << 20;
 constexpr int SLT = D + 4;  // row stride (fp32) of the scan's state block, stored transposed
 
 __device__ __forceinline__ void split_hilo(const float* f, bf16x8& hi, bf16x8& lo) {
@@ -91,13 +108,14 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
     // fix-up operand copy of S_p: element (k, j) at [k/32][j/16][16 ((k/8)%4) + j%16][k%8],
     // one 32-row slice per wave
-    if (sp >= 2 && wave < KS) {
+    if (sp >= 2 && wave < KS) {  // device-scope stores: published after the products
       const int ks = wave;
       const float4 f0 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4]);
       const float4 f1 = *reinterpret_cast<const float4*>(&slt[m16 * SLT + 32 * ks + 8 * q4 + 4]);
       const uint2 lo = pack4(f0.x, f0.y, f0.z, f0.w), hi = pack4(f1.x, f1.y, f1.z, f1.w);
-      uint16_t* dst = p.sb + slot * slot_stride + hd2 + ((ks * NB + cb) * 64 + lane) * 8;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      const auto srs = rsrc(p.sb + slot * slot_stride + hd2, D * D * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo.x, lo.y, hi.x, hi.y}, srs,
+                                             ((ks * NB + cb) * 64 + lane) * 16, 0, kDeviceScope);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -118,7 +136,11 @@ __device__ __forceinline__ void scan_unit(const Params& p, const PlanView& v, in
         acc[it] = mfma32(al, sh, acc[it]);
       }
     }
+    if (sp >= 2) __builtin_amdgcn_s_waitcnt(0);  // this wave's copy stores have completed
     __syncthreads();  // every read of S_p is done
+    if (sp >= 2 && tid == 0)  // publish the copy of S_p (column block cb)
+      __hip_atomic_fetch_add(p.state_flags + (size_t)slot * p.H + h, 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     // lane holds S_{p+1}[row0 + 16it + 4q4 + t][m16]: four consecutive entries of slt row m16
 #pragma unroll
     for (int it = 0; it < IT; ++it)
@@ -176,8 +198,6 @@ __device__ __forceinline__ FixUnit fix_decode(const Params& p, const PlanView& v
   return f;
 }
 
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 // At head dimension DK: a row of Q~ is DK/8 loads of 16 bytes, so 2048/DK rows go
 // in one pass of the 256 threads; wave w forms output columns DK/4 w .. + DK/4 - 1
@@ -220,27 +240,43 @@ __device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, Fix
           zrsrc, ((16 * tt + m16) * D + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
 }
 
-// S_p^T as the products' A operand (bf16, the order the segment's first run wrote).
-template <int DK>
+// S_p^T as the products' A operand (bf16, the order the segment's first run or the
+// scan wrote).  LATER: a state the scan published in this launch, read at device scope
+// once its counter is full.
+template <int DK, bool LATER>
 __device__ __forceinline__ void fix_state(const Params& p, const FixUnit& f,
                                           bf16x8 (&sa)[FixShape<DK>::KS][FixShape<DK>::JJ]) {
   using F = FixShape<DK>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const __bf16* sbp = reinterpret_cast<const __bf16*>(p.sb) + ((size_t)f.slot * p.H + f.h) * (D * D);
+  if (LATER) {
+    if (threadIdx.x == 0) {
+      const int* flag = p.state_flags + (size_t)f.slot * p.H + f.h;
+      for (int n = 0; n < kWaitPolls; ++n) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= F::NB) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
+  }
+  const auto srs = rsrc(p.sb + ((size_t)f.slot * p.H + f.h) * (D * D), D * D * 2);
 #pragma unroll
   for (int ks = 0; ks < F::KS; ++ks)
 #pragma unroll
-    for (int jj = 0; jj < F::JJ; ++jj)
-      sa[ks][jj] = *reinterpret_cast<const bf16x8*>(sbp + ((ks * F::NB + F::JJ * wave + jj) * 64 + lane) * 8);
+    for (int jj = 0; jj < F::JJ; ++jj) {
+      const int off = ((ks * F::NB + F::JJ * wave + jj) * 64 + lane) * 16;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, LATER ? kDeviceScope : 0);
+      sa[ks][jj] = __builtin_bit_cast(bf16x8, x);
+    }
 }
 
 // Fix-up units [u_lo, u_hi) of this workgroup: o = O0 + S_p^T Q~ for every row
 // of each unit's chunk.  The next unit's loads are in flight while the current
 // one is multiplied; S_p is reloaded only when the segment or head changes.
-template <int DK>
-__device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off, int seg0,
+template <int DK, int SEG0>
+__device__ void fix_range(const Params& p, const PlanView& v, int M, const int* off,
                           int u_lo, int u_hi, __bf16* ot) {
+  constexpr int seg0 = SEG0;
   using F = FixShape<DK>;
   if (u_lo >= u_hi) return;
   const int tid = threadIdx.x;
@@ -251,7 +287,7 @@ __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* 
   FixLoads<DK> L;
   fix_issue<DK>(p, cur, L);
   bf16x8 sa[F::KS][F::JJ];
-  fix_state<DK>(p, cur, sa);
+  fix_state<DK, SEG0 == 2>(p, cur, sa);
   for (int u = u_lo; u < u_hi; ++u) {
     // stage Q~ of the current unit (its B operand order) in LDS
 #pragma unroll
@@ -297,50 +333,44 @@ __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* 
             __builtin_bit_cast(u32x2, ov), orsrc,
             ((16 * tt + m16) * HD + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
       }
-    if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state<DK>(p, cur, sa);
+    if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state<DK, SEG0 == 2>(p, cur, sa);
     __syncthreads();  // before the next unit's staging
   }
 }
 
 template <int DK>
-__global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p, int phase) {
+__global__ void __launch_bounds__(TAIL_NT, 3) kda_tail_kernel(Params p) {
   extern __shared__ int plan_lds[];
   __shared__ __attribute__((aligned(16))) float slt[16 * SLT];
   __shared__ __attribute__((aligned(16))) __bf16 ot[C * TS];
   const int N = p.nseq;
-  // The second launch has no work when no sequence has more than two segments (the
-  // first launch records that): it then ends before building the plan.
-  const auto frsrc = rsrc(p.tail_flag, 4);
-  if (phase == 1 && __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(frsrc, 0, 0, 0)) == 0)
-    return;
   const PlanView v = plan_view(plan_lds, N, 0);
   build_plan(p, v, false);
   // wave-uniform unit values keep every buffer descriptor scalar
   const int M = __builtin_amdgcn_readfirstlane(v.hdr[0]);
-  if (phase == 0 && blockIdx.x == 0 && threadIdx.x == 0)
-    __builtin_amdgcn_raw_buffer_store_b32(M != kNoSplit && v.hdr[5] > 0 ? 1u : 0u, frsrc, 0, 0, 0);
   if (M == kNoSplit) return;
   const int G = gridDim.x, b = blockIdx.x;
-  if (phase == 0) {
-    // scan units spread over the grid, then this workgroup's share of the
-    // segment-1 fix-ups (they need only S_1, written by the main kernel)
-    const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * (DK / 16);
-    for (int u = b; u < nscan; u += G) scan_unit<DK>(p, v, M, u, slt);
-    // With workgroups to spare and a scan of several steps, the fix-ups go to those
-    // without a scan unit and run beside the scan instead of after it.  A one-step
-    // scan (two segments at most) ends long before the fix-ups: then every
-    // workgroup takes its share of them, after its scan unit.
-    const int F = __builtin_amdgcn_readfirstlane(v.hdr[4]);
-    const int mx = __builtin_amdgcn_readfirstlane(v.hdr[6]);
-    const bool one_step = (mx + M - 1) / M <= 2;
-    const int first = (!one_step && nscan < G) ? nscan : 0;
-    if (b >= first)
-      fix_range<DK>(p, v, M, v.uoff, 1, (int)((int64_t)F * (b - first) / (G - first)),
-                    (int)((int64_t)F * (b - first + 1) / (G - first)), ot);
-  } else {
-    const int F = __builtin_amdgcn_readfirstlane(v.hdr[5]);
-    fix_range<DK>(p, v, M, v.voff, 2, (int)((int64_t)F * b / G), (int)((int64_t)F * (b + 1) / G), ot);
-  }
+  // Scan units go to the first S workgroups (each may take several); at least a
+  // compute unit's worth of workgroups remains for the fix-ups.
+  const int nscan = __builtin_amdgcn_readfirstlane(v.hdr[3]) * p.H * (DK / 16);
+  const int S = min(nscan, G - p.cus);
+  if (b < S)
+    for (int u = b; u < nscan; u += S) scan_unit<DK>(p, v, M, u, slt);
+  // Segment-1 fix-ups need only S_1.  With a scan of several steps they go to the
+  // workgroups without scan units; a one-step scan (two segments at most) ends long
+  // before them, and then every workgroup takes its share, after its scan units.
+  const int F1 = __builtin_amdgcn_readfirstlane(v.hdr[4]);
+  const int mx = __builtin_amdgcn_readfirstlane(v.hdr[6]);
+  const bool one_step = (mx + M - 1) / M <= 2;
+  const int first = one_step ? 0 : S;
+  if (b >= first)
+    fix_range<DK, 1>(p, v, M, v.uoff, (int)((int64_t)F1 * (b - first) / (G - first)),
+                     (int)((int64_t)F1 * (b - first + 1) / (G - first)), ot);
+  // Later segments: only workgroups without scan units wait for published states.
+  const int F2 = __builtin_amdgcn_readfirstlane(v.hdr[5]);
+  if (b >= S && F2 > 0)
+    fix_range<DK, 2>(p, v, M, v.voff, (int)((int64_t)F2 * (b - S) / (G - S)),
+                     (int)((int64_t)F2 * (b - S + 1) / (G - S)), ot);
 }
 
 }  // namespace
@@ -354,7 +384,7 @@ WorkspaceLayout workspace_layout(int64_t ucap, int H, int emax) {
   l.st = up((size_t)ucap * kUnitBytes);
   l.sb = l.st + up((size_t)3 * emax * H * D * D * 4);
   l.flag = l.sb + up((size_t)emax * H * D * D * 2);
-  l.total = l.flag + 256;
+  l.total = l.flag + up((size_t)emax * H * 4);
   return l;
 }
 
@@ -364,7 +394,7 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   if (nsplit != 1 && nsplit != 2) return hipErrorInvalidValue;
   if (p.dk != 128 && (p.dk != 64 || nsplit != 1 || p.ckpt != nullptr)) return hipErrorInvalidValue;
   if (p.emax > 0 && (nsplit != 1 || p.o0 == nullptr || p.st == nullptr || p.sb == nullptr ||
-                     p.tail_flag == nullptr))
+                     p.state_flags == nullptr))
     return hipErrorInvalidValue;
   // task groups: every sequence, plus two runs per extra segment (fewer than
   // 2 * emax of them when splitting)
@@ -383,13 +413,9 @@ hipError_t launch_fwd(const Params& p, int nsplit, hipStream_t stream) {
   }
   if (err != hipSuccess || p.emax == 0 || p.nseq > kSortLimit) return err;
   const size_t plan_bytes = (size_t)plan_ints(p.nseq, 0, false) * sizeof(int);
-  for (int phase = 0; phase < 2; ++phase) {
-    if (p.dk == 64) hipLaunchKernelGGL(kda_tail_kernel<64>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, phase);
-    else hipLaunchKernelGGL(kda_tail_kernel<128>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p, phase);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
+  if (p.dk == 64) hipLaunchKernelGGL(kda_tail_kernel<64>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p);
+  else hipLaunchKernelGGL(kda_tail_kernel<128>, dim3(3 * p.cus), dim3(TAIL_NT), plan_bytes, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace kda

@@ -49,7 +49,8 @@ struct Params {
                           // state, one 64-row block per fix-up unit (sequence, head, chunk)
   float* st;              // fp32 [3][emax][H][128][128]: segment start states, A maps, B states
   uint16_t* sb;           // bf16 [emax][H][128*128]: segment start states, fix-up operand order
-  int* tail_flag;         // one int: whether the fix-up launch of the later segments has work
+  int* state_flags;       // [emax][H]: scan column blocks that have published the fix-up
+                          // operand of that slot's start state (zeroed by the main kernel)
   // Backward support: the fp32 state at the start of every chunk, at slot
   // n + floor(bos_n / 64) + c of sequence n's chunk c ([slots][H][128][128]), or
   // null.  Requires emax = 0 (no sequence splitting).

@@ -198,11 +198,11 @@ def test_state_dtype_ignored_for_absent_state(lib):
 
 def _split_workspace(units, H, emax):
     """Fix-up output blocks (64 x 128 bf16 per unit), then the fp32 segment states,
-    maps and end states, then their bf16 fix-up copies, then 256 bytes for the flag
-    of the second fix-up launch."""
+    maps and end states, then their bf16 fix-up copies, then one int32 per (state
+    slot, head): the counter through which the scan publishes each start state."""
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     return (up(units * 64 * 128 * 2) + up(3 * emax * H * 128 * 128 * 4) + up(emax * H * 128 * 128 * 2)
-            + 256)
+            + up(emax * H * 4))
 
 
 def test_plan_value_split(lib, monkeypatch):
