@@ -883,38 +883,11 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     bp.nseq = N; bp.H = H;
     bp.dsT = d_final_state; bp.dsT_fp32 = d_final_dtype == KDA_FP32;
     bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dg = dg; bp.dbeta = dbeta; bp.ds0 = d_initial_state;
-    // Two streams.  The side stream runs the checkpointing forward pass, then the
-    // products that need the checkpoints (R, U, dO' S^T, dM); the caller's stream
-    // runs the chunk-local tiles, which need no checkpoint, then the state-gradient
-    // scan beside those products; the remaining gradients wait for both.  Once the
-    // fork is recorded, the caller's stream always waits for the side stream
-    // before the call returns.
+    // the checkpointing forward pass and the products that need its checkpoints run
+    // on a second stream of the library's, beside the work that does not
     hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, local = nullptr, join = nullptr;
     err = side_stream(&side);
-    if (err == hipSuccess) err = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
-    if (err == hipSuccess) err = hipEventCreateWithFlags(&local, hipEventDisableTiming);
-    if (err == hipSuccess) err = hipEventCreateWithFlags(&join, hipEventDisableTiming);
-    if (err == hipSuccess) err = hipEventRecord(fork, hs);
-    if (err == hipSuccess) {
-      err = hipStreamWaitEvent(side, fork, 0);
-      if (err == hipSuccess) err = kda::launch_fwd(p, nsplit, side);
-      if (err == hipSuccess) err = kda::launch_bwd_chunk_local(bp, w, nb, hs);
-      if (err == hipSuccess) err = hipEventRecord(local, hs);
-      if (err == hipSuccess) err = hipStreamWaitEvent(side, local, 0);
-      if (err == hipSuccess) err = kda::launch_bwd_state_products(bp, w, nb, side);
-      if (err == hipSuccess) err = kda::launch_bwd_scan(bp, w, hs);
-      hipError_t ej = hipEventRecord(join, side);
-      if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, join, 0);
-      if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
-        (void)hipStreamSynchronize(side);
-        if (err == hipSuccess) err = ej;
-      }
-      if (err == hipSuccess) err = kda::launch_bwd_grads(bp, w, nb, hs);
-    }
-    if (fork != nullptr) (void)hipEventDestroy(fork);
-    if (local != nullptr) (void)hipEventDestroy(local);
-    if (join != nullptr) (void)hipEventDestroy(join);
+    if (err == hipSuccess) err = kda::launch_bwd_streams(p, nsplit, bp, w, nb, hs, side);
   } else if (d_initial_state != nullptr) {
     // no tokens: the initial-state gradient is the final-state gradient (or zero)
     kda::BwdParams bp{};

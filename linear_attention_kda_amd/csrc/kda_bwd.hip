@@ -1024,33 +1024,85 @@ hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s)
   return hipGetLastError();
 }
 
-// Everything that needs the state gradients, after the scan and the state products.
-hipError_t launch_bwd_grads(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
-  const int NB = (int)batches;
+// The gradient products after the scan.  dU = kp dSn + M^T dO' and dY = T^T dU need
+// the scan only; dA = strict_lower(-dY U^T), -diag(b) dY S^T and the gated terms
+// also need the state products (U, dM); dkp = U dSn^T needs both but nothing else
+// here, so it may run beside them.
+void launch_dudy(const BwdTiles& w, int NB, hipStream_t s) {
   const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
   GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
   du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
   gemm(false, false, du, s);
   gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
+}
+
+void launch_dkp(const BwdTiles& w, int NB, hipStream_t s) {
+  const int64_t t1 = C * D, t3 = D * D;
+  gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
+}
+
+void launch_da_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) {
+  const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
   GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
   da.alpha = -1.f; da.mask = 1;
   gemm(false, true, da, s);
-  gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
   GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
   k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
   gemm(false, true, k1, s);
   // dM kh, diag(b) dA kh and dkh through the gates, with block references: into the
   // tiles MtdO and dU (free once dU and dY exist) and dkh
   hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, s, p, w);
-  return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t s) {
-  hipError_t e = launch_bwd_chunk_local(p, w, batches, s);
-  if (e == hipSuccess) e = launch_bwd_state_products(p, w, batches, s);
-  if (e == hipSuccess) e = launch_bwd_scan(p, w, s);
-  return e != hipSuccess ? e : launch_bwd_grads(p, w, batches, s);
+hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
+                              int64_t batches, hipStream_t hs, hipStream_t side) {
+  const int NB = (int)batches;
+  // Caller's stream:  chunk-local tiles | scan | dU, dY | (state products) dA, dkg, gated | (dkp) finalize
+  // Side stream:      (fork) forward with checkpoints | (chunk-local) state products | (scan) dkp
+  // Once the fork is recorded, the caller's stream always waits for the side stream
+  // before this returns, so that later work on it (and the workspace's next use)
+  // follows everything enqueued here.
+  hipEvent_t ev[5] = {};
+  enum { kFork, kLocal, kProducts, kScan, kJoin };
+  hipError_t err = hipSuccess;
+  for (int i = 0; i < 5 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventRecord(ev[kFork], hs);
+  if (err == hipSuccess) {
+    auto on_side = [&](hipEvent_t after, auto&& launch) {  // side stream: wait, then enqueue
+      if (err == hipSuccess) err = hipStreamWaitEvent(side, after, 0);
+      if (err == hipSuccess) err = launch();
+    };
+    on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
+    if (err == hipSuccess) err = launch_bwd_chunk_local(p, w, batches, hs);
+    if (err == hipSuccess) err = hipEventRecord(ev[kLocal], hs);
+    on_side(ev[kLocal], [&] { return launch_bwd_state_products(p, w, batches, side); });
+    if (err == hipSuccess) err = hipEventRecord(ev[kProducts], side);
+    if (err == hipSuccess) err = launch_bwd_scan(p, w, hs);
+    if (err == hipSuccess) err = hipEventRecord(ev[kScan], hs);
+    on_side(ev[kScan], [&] { launch_dkp(w, NB, side); return hipGetLastError(); });
+    if (err == hipSuccess) {
+      launch_dudy(w, NB, hs);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
+    if (err == hipSuccess) {
+      launch_da_dkg_gated(p, w, NB, hs);
+      err = hipGetLastError();
+    }
+    hipError_t ej = hipEventRecord(ev[kJoin], side);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, ev[kJoin], 0);
+    if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
+      (void)hipStreamSynchronize(side);
+      if (err == hipSuccess) err = ej;
+    }
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, hs, p, w);
+      err = hipGetLastError();
+    }
+  }
+  for (hipEvent_t e : ev)
+    if (e != nullptr) (void)hipEventDestroy(e);
+  return err;
 }
 
 }  // namespace kda

@@ -149,19 +149,23 @@ struct GemmArgs {
 };
 
 size_t bwd_tile_floats();
-hipError_t launch_bwd(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
-// The parts of launch_bwd, in dependency order:
+// The backward pass on two streams: the checkpointing forward pass (`fwd`, with
+// fwd_splits value slices) and the products that need the checkpoints run on
+// `side` beside the chunk-local tiles and the state-gradient scan on `hs`; `hs`
+// waits for `side` before the last kernel, so that everything enqueued is ordered
+// before later work on `hs`.  Parts, in dependency order:
 //  * chunk_local: the tiles that need no state checkpoint (prep, P / A / M, the
-//    inverse, M^T dO', F and X); it may run beside the checkpointing forward pass;
+//    inverse, M^T dO', F and X);
 //  * state_products: R, U, dO' S^T and dM, after chunk_local and the forward pass;
-//  * scan: the state gradients over the chunks, after chunk_local only, so that it
-//    may run beside state_products;
-//  * grads: the rest, after state_products and scan.
+//  * scan: the state gradients over the chunks, after chunk_local only;
+//  * then dU and dY (after the scan), dkp (after the scan and the state products,
+//    on `side`), dA, dkg and the gated terms (after both), and the finalize.
 hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
 hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
                                      hipStream_t stream);
 hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t stream);
-hipError_t launch_bwd_grads(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
+hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
+                              int64_t batches, hipStream_t hs, hipStream_t side);
 // The initial-state gradients alone, for calls without tokens.
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 
