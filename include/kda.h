@@ -348,7 +348,7 @@ kda_status kda_release_workspaces(void);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
  * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  It is
- *   (N + ceil(rows / 64) + 1) * H * 819,972 bytes of per-chunk fp32 tiles
+ *   (N + ceil(rows / 64) + 1) * H * 820,484 bytes of per-chunk fp32 tiles
  *   (every (chunk, head)'s operands, products and state checkpoints),
  *   plus rows * H * 256 bytes for the forward pass's outputs,
  * about 12.8 KB per token and head: on a 288 GB device, rows * H of about 22

@@ -850,6 +850,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     w.dSn = take(128 * 128);
     w.beta = take(64);
     w.gam = take(128);
+    w.dgl = take(128);
     w.valid = reinterpret_cast<int*>(take(1));
   }
   uint16_t* fwd_out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws.ptr()) +

@@ -815,7 +815,71 @@ void launch_ds_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- gates and scatter
-// One workgroup per batch: dq, dk, dv, dg, dbeta of the chunk's rows.
+// Terms that need no gated gradient, on the side stream while the gated terms run:
+//  * the state's direct share of dG_last, gam_c sum_j S_cj dSn_cj per channel c;
+//  * dbeta_r = sum_j dY_rj R_rj + sum_i dA_ri P_ri and dv_r = beta_r dY_r per row.
+// Sixteen lanes share a row, each with eight consecutive entries (coalesced), and
+// their sums meet through lane exchanges within the sixteen.
+__global__ void __launch_bounds__(256) bwd_state_term_kernel(BwdParams p, BwdTiles w) {
+  const int64_t bidx = blockIdx.x;
+  if (w.valid[bidx] == 0) return;
+  const int t = threadIdx.x, jq = t & 15;
+  const float* S = w.S + bidx * (size_t)(D * D);
+  const float* dsn = w.dSn + bidx * (size_t)(D * D);
+#pragma unroll 2
+  for (int it = 0; it < D / 16; ++it) {
+    const int r = 16 * it + (t >> 4);
+    const float4 a0 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq);
+    const float4 a1 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq);
+    const float4 b1 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq + 4);
+    float sum = a0.x * b0.x + a0.y * b0.y + a0.z * b0.z + a0.w * b0.w +
+                a1.x * b1.x + a1.y * b1.y + a1.z * b1.z + a1.w * b1.w;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+    if (jq == 0) w.dgl[bidx * D + r] = sum * w.gam[bidx * D + r];
+  }
+}
+
+__global__ void __launch_bounds__(256) bwd_dbeta_dv_kernel(BwdParams p, BwdTiles w) {
+  const int64_t bidx = blockIdx.x;
+  const int valid = w.valid[bidx];
+  if (valid == 0) return;
+  const int64_t slot = bidx / p.H;
+  const int h = (int)(bidx % p.H);
+  const int n = slot_seq(p, slot);
+  const int64_t bos = seq_bos(p, n);
+  const int64_t c = slot - (n + bos / C);
+  const int t = threadIdx.x, jq = t & 15;
+  const int64_t tb = bidx * (C * D);
+  const float* beta = w.beta + bidx * C;
+#pragma unroll
+  for (int it = 0; it < C / 16; ++it) {
+    const int r = 16 * it + (t >> 4);
+    const float* dy = w.dY + tb + (size_t)r * D + 8 * jq;
+    const float* rr = w.R + tb + (size_t)r * D + 8 * jq;
+    const float* da = w.dA + bidx * C * C + (size_t)r * C + 4 * jq;
+    const float* pp = w.P + bidx * C * C + (size_t)r * C + 4 * jq;
+    const float4 y0 = *reinterpret_cast<const float4*>(dy), y1 = *reinterpret_cast<const float4*>(dy + 4);
+    const float4 q0 = *reinterpret_cast<const float4*>(rr), q1 = *reinterpret_cast<const float4*>(rr + 4);
+    const float4 a = *reinterpret_cast<const float4*>(da), b = *reinterpret_cast<const float4*>(pp);
+    float sum = y0.x * q0.x + y0.y * q0.y + y0.z * q0.z + y0.w * q0.w +
+                y1.x * q1.x + y1.y * q1.y + y1.z * q1.z + y1.w * q1.w +
+                a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+    if (r < valid) {
+      const int64_t row = (bos + c * C + r) * (int64_t)p.H + h;
+      if (jq == 0) p.dbeta[row] = sum;
+      const float br = beta[r];
+      float* dv = p.dv + row * D + 8 * jq;
+      *reinterpret_cast<float4*>(dv) = make_float4(br * y0.x, br * y0.y, br * y0.z, br * y0.w);
+      *reinterpret_cast<float4*>(dv + 4) = make_float4(br * y1.x, br * y1.y, br * y1.z, br * y1.w);
+    }
+  }
+}
+
+// One workgroup per batch: dq, dk and dg of the chunk's rows.
 __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles w) {
   const int64_t bidx = blockIdx.x;
   const int valid = w.valid[bidx];
@@ -828,12 +892,9 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
   const int t = threadIdx.x, ch = t & 127, half = t >> 7;
   const int HD = p.H * D;
   const int64_t tb = bidx * (C * D);
-  const float* beta = w.beta + bidx * C;
   __shared__ float dGs[C][D];
   __shared__ float red[2][D];
-  __shared__ float rowsum[D];
-  __shared__ float dbs[C];
-  // per row: dG, dq, dk, dv; per channel: dG_last pieces
+  // per row: dG, dq, dk; per channel: dG_last pieces
   // The gradients through each gate, ungated:
   //   dq  = (dO' S^T) Gam + dqi                       (dqg Gam)
   //   dkg = -diag(b) (dY S^T) Gam + dka                (dkg Gam)
@@ -859,36 +920,13 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
     if (r < valid) {
       p.dq[row] = dq;
       p.dk[row] = dkg + dkh + dkp;
-      p.dv[row] = beta[r] * w.dY[o];
     }
   }
   red[half][ch] = glast;
-  // dgam_direct: gam_c times the row sum over j of S * dSn for every channel c.  Sixteen
-  // lanes share a row, each with eight consecutive entries (coalesced), and their sums
-  // meet through lane exchanges within the sixteen.
-  {
-    const float* S = w.S + bidx * (size_t)(D * D);
-    const float* dsn = w.dSn + bidx * (size_t)(D * D);
-    const int jq = t & 15;
-#pragma unroll 2
-    for (int it = 0; it < D / 16; ++it) {
-      const int r = 16 * it + (t >> 4);
-      const float4 a0 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq);
-      const float4 a1 = *reinterpret_cast<const float4*>(S + (size_t)r * D + 8 * jq + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq);
-      const float4 b1 = *reinterpret_cast<const float4*>(dsn + (size_t)r * D + 8 * jq + 4);
-      float sum = a0.x * b0.x + a0.y * b0.y + a0.z * b0.z + a0.w * b0.w +
-                  a1.x * b1.x + a1.y * b1.y + a1.z * b1.z + a1.w * b1.w;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
-      if (jq == 0) rowsum[r] = sum;
-    }
-    __syncthreads();
-    red[half][ch] += half == 0 ? rowsum[ch] * w.gam[bidx * D + ch] : 0.f;
-  }
   __syncthreads();
   if (half == 0) {
-    const float dGlast = red[0][ch] + red[1][ch];
+    // dG_last: the kp terms of both halves and the state's direct share
+    const float dGlast = red[0][ch] + red[1][ch] + w.dgl[bidx * D + ch];
     // dg_t = sum_{r >= t} dG_r + dG_last
     float run = dGlast;
     for (int r = C - 1; r >= 0; --r) {
@@ -896,29 +934,6 @@ __global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles
       if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + ch] = run;
     }
   }
-  // dbeta_r = sum_j dY_rj R_rj + sum_i dA_ri P_ri: sixteen lanes per row, as above
-  {
-    const int jq = t & 15;
-#pragma unroll
-    for (int it = 0; it < C / 16; ++it) {
-      const int r = 16 * it + (t >> 4);
-      const float* dy = w.dY + tb + (size_t)r * D + 8 * jq;
-      const float* rr = w.R + tb + (size_t)r * D + 8 * jq;
-      const float* da = w.dA + bidx * C * C + (size_t)r * C + 4 * jq;
-      const float* pp = w.P + bidx * C * C + (size_t)r * C + 4 * jq;
-      const float4 y0 = *reinterpret_cast<const float4*>(dy), y1 = *reinterpret_cast<const float4*>(dy + 4);
-      const float4 q0 = *reinterpret_cast<const float4*>(rr), q1 = *reinterpret_cast<const float4*>(rr + 4);
-      const float4 a = *reinterpret_cast<const float4*>(da), b = *reinterpret_cast<const float4*>(pp);
-      float sum = y0.x * q0.x + y0.y * q0.y + y0.z * q0.z + y0.w * q0.w +
-                  y1.x * q1.x + y1.y * q1.y + y1.z * q1.z + y1.w * q1.w +
-                  a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
-      if (jq == 0) dbs[r] = sum;
-    }
-  }
-  __syncthreads();
-  if (t < valid) p.dbeta[(bos + c * C + t) * p.H + h] = dbs[t];
 }
 
 template <int NT>
@@ -1041,11 +1056,15 @@ void launch_dkp(const BwdTiles& w, int NB, hipStream_t s) {
   gemm(false, true, mm(C, D, D, w.U, t1, D, w.dSn, t3, D, w.dkp, t1, D, NB), s);  // dkp = U dSn^T
 }
 
-void launch_da_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) {
-  const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
+void launch_da(const BwdTiles& w, int NB, hipStream_t s) {
+  const int64_t t1 = C * D, t2 = C * C;
   GemmArgs da = mm(C, C, D, w.dY, t1, D, w.U, t1, D, w.dA, t2, C, NB);  // dA = strict_lower(-dY U^T)
   da.alpha = -1.f; da.mask = 1;
   gemm(false, true, da, s);
+}
+
+void launch_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) {
+  const int64_t t1 = C * D, t3 = D * D;
   GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
   k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
   gemm(false, true, k1, s);
@@ -1057,20 +1076,28 @@ void launch_da_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStrea
 hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
                               int64_t batches, hipStream_t hs, hipStream_t side) {
   const int NB = (int)batches;
-  // Caller's stream:  chunk-local tiles | scan | dU, dY | (state products) dA, dkg, gated | (dkp) finalize
-  // Side stream:      (fork) forward with checkpoints | (chunk-local) state products | (scan) dkp
+  // Caller's stream:  chunk-local tiles | scan | dU, dY | (state products) dA | dkg, gated
+  //                   | (side) finalize
+  // Side stream:      (fork) forward with checkpoints | (chunk-local) state products
+  //                   | (scan) dkp, the state term of dG_last | (dA) dbeta, dv
   // Once the fork is recorded, the caller's stream always waits for the side stream
   // before this returns, so that later work on it (and the workspace's next use)
   // follows everything enqueued here.
-  hipEvent_t ev[5] = {};
-  enum { kFork, kLocal, kProducts, kScan, kJoin };
+  hipEvent_t ev[6] = {};
+  enum { kFork, kLocal, kProducts, kScan, kDA, kJoin };
   hipError_t err = hipSuccess;
-  for (int i = 0; i < 5 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  for (int i = 0; i < 6 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
   if (err == hipSuccess) err = hipEventRecord(ev[kFork], hs);
   if (err == hipSuccess) {
     auto on_side = [&](hipEvent_t after, auto&& launch) {  // side stream: wait, then enqueue
       if (err == hipSuccess) err = hipStreamWaitEvent(side, after, 0);
       if (err == hipSuccess) err = launch();
+    };
+    auto on_hs = [&](auto&& launch) {
+      if (err == hipSuccess) {
+        launch();
+        err = hipGetLastError();
+      }
     };
     on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
     if (err == hipSuccess) err = launch_bwd_chunk_local(p, w, batches, hs);
@@ -1079,26 +1106,27 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
     if (err == hipSuccess) err = hipEventRecord(ev[kProducts], side);
     if (err == hipSuccess) err = launch_bwd_scan(p, w, hs);
     if (err == hipSuccess) err = hipEventRecord(ev[kScan], hs);
-    on_side(ev[kScan], [&] { launch_dkp(w, NB, side); return hipGetLastError(); });
-    if (err == hipSuccess) {
-      launch_dudy(w, NB, hs);
-      err = hipGetLastError();
-    }
+    on_side(ev[kScan], [&] {
+      launch_dkp(w, NB, side);
+      hipLaunchKernelGGL(bwd_state_term_kernel, dim3(NB), dim3(256), 0, side, p, w);
+      return hipGetLastError();
+    });
+    on_hs([&] { launch_dudy(w, NB, hs); });
     if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
-    if (err == hipSuccess) {
-      launch_da_dkg_gated(p, w, NB, hs);
-      err = hipGetLastError();
-    }
+    on_hs([&] { launch_da(w, NB, hs); });
+    if (err == hipSuccess) err = hipEventRecord(ev[kDA], hs);
+    on_side(ev[kDA], [&] {
+      hipLaunchKernelGGL(bwd_dbeta_dv_kernel, dim3(NB), dim3(256), 0, side, p, w);
+      return hipGetLastError();
+    });
+    on_hs([&] { launch_dkg_gated(p, w, NB, hs); });
     hipError_t ej = hipEventRecord(ev[kJoin], side);
     if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, ev[kJoin], 0);
     if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
       (void)hipStreamSynchronize(side);
       if (err == hipSuccess) err = ej;
     }
-    if (err == hipSuccess) {
-      hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, hs, p, w);
-      err = hipGetLastError();
-    }
+    on_hs([&] { hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, hs, p, w); });
   }
   for (hipEvent_t e : ev)
     if (e != nullptr) (void)hipEventDestroy(e);

@@ -130,9 +130,10 @@ struct BwdTiles {
   float *S, *X, *dSn;                // [b][128][128]; S: chunk start states (the checkpoints)
   float* beta;                       // [b][64]
   float* gam;                        // [b][128]
+  float* dgl;                        // [b][128]: the state's direct share of dG_last
   int* valid;                        // [b]
   static constexpr size_t floats_per_batch() {
-    return 15 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 128 + 1;
+    return 15 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1;
   }
 };
 
