@@ -194,10 +194,10 @@ LaunchPlan make_plan(int32_t N, int64_t T, int32_t H, bool varlen, int32_t cus,
   return lp;
 }
 
-// Library-owned stream-ordered pool for the workspaces, one per device.  It keeps
-// up to kPoolKeepBytes reserved between calls (so a repeated call of the same
-// size costs no allocation from the driver) and hands anything above that back
-// at the next synchronisation.
+// Library-owned stream-ordered pool, one per device, for the workspaces too large
+// to keep between calls (see Workspace below).  It keeps up to kPoolKeepBytes
+// reserved (so a repeated call of the same size maps no new device memory) and
+// hands anything above that back at the next synchronisation.
 constexpr uint64_t kPoolKeepBytes = 2ull << 30;
 
 hipError_t workspace_pool(hipMemPool_t* out) {
