@@ -813,17 +813,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
   if (st != KDA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const int64_t rows = cu_seqlens ? T : (int64_t)B * T;
-  const size_t gbytes = (size_t)rows * H * 128 * 4;
   hipError_t e = hipSuccess;
-  // rows outside every sequence get zero gradients
-  if (rows > 0) {
-    e = hipMemsetAsync(dq, 0, gbytes, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(dk, 0, gbytes, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(dv, 0, gbytes, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(dg, 0, gbytes, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(dbeta, 0, (size_t)rows * H * 4, hs);
-    if (e != hipSuccess) return fail(KDA_ERR_HIP, "gradient clear: %s", hipGetErrorString(e));
-  }
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");

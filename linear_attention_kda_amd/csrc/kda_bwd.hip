@@ -814,6 +814,25 @@ void launch_ds_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s) {
   hipLaunchKernelGGL(bwd_ds_scan_kernel, dim3((unsigned)(groups * 8 * (D / 16))), dim3(256), 0, s, p, w);
 }
 
+// ---------------------------------------------------------------- rows past the sequences
+// With cu_seqlens, rows cu_seqlens[num_seqs] .. T - 1 belong to no sequence and get
+// zero gradients (every other row is written by the finalize and dbeta / dv
+// kernels).  Their extent is known on the device only, so a kernel clears them.
+__global__ void __launch_bounds__(256) bwd_clear_tail_kernel(BwdParams p) {
+  const int64_t r0 = p.cu[p.nseq];
+  const int64_t n = (p.T - r0) * p.H;   // (row, head) pairs to clear
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n * (D / 4); i += stride) {
+    const int64_t o = r0 * p.H * (D / 4) + i;   // float4 index
+    reinterpret_cast<float4*>(p.dq)[o] = z;
+    reinterpret_cast<float4*>(p.dk)[o] = z;
+    reinterpret_cast<float4*>(p.dv)[o] = z;
+    reinterpret_cast<float4*>(p.dg)[o] = z;
+    if (i < n) p.dbeta[r0 * p.H + i] = 0.f;
+  }
+}
+
 // ---------------------------------------------------------------- gates and scatter
 // Terms that need no gated gradient, on the side stream while the gated terms run:
 //  * the state's direct share of dG_last, gam_c sum_j S_cj dSn_cj per channel c;
@@ -1087,6 +1106,10 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
   enum { kFork, kLocal, kProducts, kScan, kDA, kJoin };
   hipError_t err = hipSuccess;
   for (int i = 0; i < 6 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  if (err == hipSuccess && p.cu != nullptr) {
+    hipLaunchKernelGGL(bwd_clear_tail_kernel, dim3(512), dim3(256), 0, hs, p);
+    err = hipGetLastError();
+  }
   if (err == hipSuccess) err = hipEventRecord(ev[kFork], hs);
   if (err == hipSuccess) {
     auto on_side = [&](hipEvent_t after, auto&& launch) {  // side stream: wait, then enqueue

@@ -90,6 +90,26 @@ def test_bwd_varlen():
     check_bwd(x, do, dsT)
 
 
+def test_bwd_rows_past_the_last_sequence():
+    """cu_seqlens[num_seqs] < T: the rows past the last sequence get exactly zero
+    gradients (cleared on the device), the others match the oracle."""
+    from linear_attention_kda_amd.workloads import cu_from_lengths
+    lengths, pad = [70, 0, 129], 37
+    total = sum(lengths)
+    announce(f"bwd varlen {lengths} + {pad} rows past the last sequence")
+    x = random_inputs(1, total + pad, 2, seed=84, device=DEV, init_state="fp32",
+                      n_states=len(lengths))
+    x["cu_seqlens"] = cu_from_lengths(lengths, DEV)
+    do, dsT = upstream(x, 85)
+    gr = binding.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["scale"],
+                     initial_state=x["initial_state"], d_final_state=dsT,
+                     cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.count_nonzero(gr[k][:, total:]).item() == 0, k
+    check_bwd(x, do, dsT)
+
+
 def test_bwd_without_final_state_gradient():
     announce("bwd B=1 T=190 H=2, no dS_final")
     x = random_inputs(1, 190, 2, seed=74, device=DEV, init_state="fp32")
