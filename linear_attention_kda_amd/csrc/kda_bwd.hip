@@ -1031,8 +1031,8 @@ hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t
   return hipGetLastError();
 }
 
-// Products that need the checkpoints but not the state gradients: R, U, dO' S^T
-// and dM.  They may run beside the scan.
+// Products that need the checkpoints but not the state gradients: R, U and dM.
+// They may run beside the scan.
 hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
                                      hipStream_t s) {
   const int NB = (int)batches;
@@ -1044,12 +1044,17 @@ hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int6
   GemmArgs u = mm(C, D, C, w.T, t2, C, w.R, t1, D, w.U, t1, D, NB);
   u.ks = w.beta; u.sks = C;
   gemm(false, false, u, s);
-  gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);  // dO' S^T
   GemmArgs dm = mm(C, C, D, w.dO, t1, D, w.U, t1, D, w.dM, t2, C, NB);  // dM = lower_incl(dO' U^T)
   dm.mask = 2;
   gemm(false, true, dm, s);
   (void)p;
   return hipGetLastError();
+}
+
+// dO' S^T: needs the checkpoints only, and only the finalize reads it.
+void launch_dos(const BwdTiles& w, int NB, hipStream_t s) {
+  const int64_t t1 = C * D, t3 = D * D;
+  gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);
 }
 
 // The serial recurrence of dS over chunks: it reads only chunk-local tiles.
@@ -1097,8 +1102,8 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
   const int NB = (int)batches;
   // Caller's stream:  chunk-local tiles | scan | dU, dY | (state products) dA | dkg, gated
   //                   | (side) finalize
-  // Side stream:      (fork) forward with checkpoints | (chunk-local) state products
-  //                   | (scan) dkp, the state term of dG_last | (dA) dbeta, dv
+  // Side stream:      (fork) forward with checkpoints | (chunk-local) R, U, dM
+  //                   | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
   // Once the fork is recorded, the caller's stream always waits for the side stream
   // before this returns, so that later work on it (and the workspace's next use)
   // follows everything enqueued here.
@@ -1132,6 +1137,7 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
     on_side(ev[kScan], [&] {
       launch_dkp(w, NB, side);
       hipLaunchKernelGGL(bwd_state_term_kernel, dim3(NB), dim3(256), 0, side, p, w);
+      launch_dos(w, NB, side);
       return hipGetLastError();
     });
     on_hs([&] { launch_dudy(w, NB, hs); });

@@ -157,10 +157,11 @@ size_t bwd_tile_floats();
 // before later work on `hs`.  Parts, in dependency order:
 //  * chunk_local: the tiles that need no state checkpoint (prep, P / A / M, the
 //    inverse, M^T dO', F and X);
-//  * state_products: R, U, dO' S^T and dM, after chunk_local and the forward pass;
+//  * state_products: R, U and dM, after chunk_local and the forward pass;
 //  * scan: the state gradients over the chunks, after chunk_local only;
-//  * then dU and dY (after the scan), dkp (after the scan and the state products,
-//    on `side`), dA, dkg and the gated terms (after both), and the finalize.
+//  * then dU and dY (after the scan), dkp, the state term of dG_last and dO' S^T
+//    (after the scan and the state products, on `side`), dA, dkg and the gated
+//    terms (after both), dbeta and dv (after dA, on `side`), and the finalize.
 hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
 hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
                                      hipStream_t stream);
