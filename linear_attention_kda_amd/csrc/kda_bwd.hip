@@ -78,8 +78,7 @@ __device__ __forceinline__ int slot_seq(const BwdParams& p, int64_t s) {
 // operands and accumulation): twice the rate of unpacked fp32 FMAs.  Each wave
 // owns a quarter of the tile as 2 x (NT / 32) blocks; for step k of four, lane
 // (q4, m16) supplies op(A)[16i + m16][k] and op(B)[k][16j + m16] with k = 4s + q4,
-// and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.  Where an output
-// is a sum of two products, both accumulate in the same registers (bgemm2_kernel).
+// and holds C[16i + 4q4 + t][16j + m16] (t < 4) of each block.
 typedef float bg_f32x4 __attribute__((ext_vector_type(4)));
 
 // k-major tiles; a row stride of 16 mod 32 floats puts lane groups q4 and q4 + 1
@@ -186,32 +185,6 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
   bg_zero<NT>(acc);
   bg_accumulate<NT, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
                             a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_store<NT>(acc, a, b, m0, n0);
-}
-
-// A sum of two products in one pass, C = rs (.) (op(A) op(B) + sign2 op(A2) op(B2)),
-// so that the first product never goes through memory.
-struct Gemm2Args {
-  GemmArgs a;                              // first product, output, row scale, mask
-  const float* A2; int64_t sA2; int lda2;
-  const float* B2; int64_t sB2; int ldb2;
-  int K2;
-  const float* ks2; int64_t sks2;
-  float sign2;                             // +-1
-};
-
-template <int NT, bool TA, bool TB, bool TA2, bool TB2>
-__global__ void __launch_bounds__(256) bgemm2_kernel(Gemm2Args g) {
-  __shared__ BgTiles<NT> sm;
-  const GemmArgs& a = g.a;
-  const int n0 = blockIdx.x * NT, m0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  bg_f32x4 acc[2][NT / 32];
-  bg_zero<NT>(acc);
-  bg_accumulate<NT, TA, TB>(acc, sm, a.A + b * a.sA, a.lda, a.B + b * a.sB, a.ldb, a.K,
-                            a.ks ? a.ks + b * a.sks : nullptr, 1.f, m0, n0);
-  bg_accumulate<NT, TA2, TB2>(acc, sm, g.A2 + b * g.sA2, g.lda2, g.B2 + b * g.sB2, g.ldb2, g.K2,
-                              g.ks2 ? g.ks2 + b * g.sks2 : nullptr, g.sign2, m0, n0);
   bg_store<NT>(acc, a, b, m0, n0);
 }
 
@@ -668,17 +641,19 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 // ---------------------------------------------------------------- serial dS
 // Column j of dS depends only on column j of dSn (Diag(gam), kp and F act on
 // rows), so each (sequence, head) runs as D / 16 workgroups of 16 value columns.
-// Chunks last to first: dSn(c) is stored for the chunk's gradient products, then
-// dS = Diag(gam) dSn - F (kp dSn) + X becomes the next dSn.  The sequence's
+// Chunks last to first: dSn(c) is stored for the chunk's gradient products, the
+// chunk's dU = kp dSn + M^T dO' is formed and stored, and
+// dS = Diag(gam) dSn - F dU + qg^T dO' becomes the next dSn (the same as
+// Diag(gam) dSn - F (kp dSn) + X with X = qg^T dO' - F M^T dO').  The sequence's
 // initial-state gradient is the last dS.
 //  * Both products run on the fp32 matrix cores (16x16x4): wave w forms rows
-//    16w .. 16w+15 of P = kp dSn and rows 32w .. 32w+31 of dS.  The k index of a
+//    16w .. 16w+15 of dU = kp dSn + M^T dO' and rows 32w .. 32w+31 of dS.  The k index of a
 //    product is permuted so that each lane's A operand is one contiguous run
 //    (k = 32q + s for P, 16q + s for F P over steps s), loaded as float4s.
 //  * dS stays in the MFMA accumulators (rows 32w + 16it + 4q + t, column m); a
-//    transposed copy in LDS is the B operand of the next chunk's P, and P goes
-//    through LDS (transposed) as the B operand of F P.
-//  * The next chunk's kp, F, X and gam are loaded into registers while the
+//    transposed copy in LDS is the B operand of the next chunk's kp dSn, and dU
+//    goes through LDS (transposed) as the B operand of F dU.
+//  * The next chunk's kp, F, qg^T dO', M^T dO' and gam are loaded into registers while the
 //    current chunk computes, so the serial loop does not wait on memory.
 //  * The 8 column slices of one (sequence, head) run on one XCD (workgroups go
 //    to the XCDs round robin), so the chunk's kp and F, which every slice reads,
@@ -686,7 +661,8 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 struct ScanOps {
   float4 kp[8];       // kp[16w + m][32q .. 32q + 31]
   float4 f[2][4];     // F[32w + 16it + m][16q .. 16q + 15]
-  float x[2][4];      // X[32w + 16it + 4q + t][j0 + m]
+  float x[2][4];      // (qg^T dO')[32w + 16it + 4q + t][j0 + m]
+  float mt[4];        // (M^T dO')[16w + 4q + t][j0 + m]
   float4 gam[2];      // gam[32w + 16it + 4q .. + 3]
 };
 
@@ -695,6 +671,9 @@ __device__ __forceinline__ void scan_fetch(const BwdTiles& w, int64_t bidx, int 
   const float* kp = w.kp + bidx * (C * D) + (16 * wave + m) * D + 32 * q;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o.kp[i] = *reinterpret_cast<const float4*>(kp + 4 * i);
+  const float* mt = w.MtdO + bidx * (C * D) + (size_t)(16 * wave + 4 * q) * D + j0 + m;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o.mt[t] = mt[(size_t)t * D];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const float* F = w.F + bidx * (D * C) + (32 * wave + 16 * it + m) * C + 16 * q;
@@ -711,7 +690,7 @@ __device__ __forceinline__ void scan_fetch(const BwdTiles& w, int64_t bidx, int 
 __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles w) {
   constexpr int DSW = 16, DSC = D / DSW;
   __shared__ float dsT[DSW][D + 4];   // dSn, transposed: dsT[j][k]
-  __shared__ float pT[DSW][C + 4];    // P = kp dSn, transposed: pT[j][r]
+  __shared__ float pT[DSW][C + 4];    // dU = kp dSn + M^T dO', transposed: pT[j][r]
   // workgroup b: slice (b / 8) % DSC of pair (b / (8 DSC)) * 8 + b % 8, so that all
   // slices of a pair share b % 8 (their XCD)
   const int b = blockIdx.x;
@@ -754,7 +733,7 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
         for (int tt = 0; tt < 4; ++tt)
           dsn[(size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m] = ds[it][tt];
     }
-    {  // P rows 16w .. 16w+15 = kp dSn, k = 32q + s, in four independent chains
+    {  // dU rows 16w .. 16w+15 = kp dSn + M^T dO', k = 32q + s, in four independent chains
       bg_f32x4 acc[4] = {};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -765,10 +744,17 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bw[e], acc[e], 0, 0, 0);
       }
       const bg_f32x4 pv = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      *reinterpret_cast<float4*>(&pT[m][16 * wave + 4 * q]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+      float du[4];
+      float* dug = w.dU + bidx * (C * D) + (size_t)(16 * wave + 4 * q) * D + j0 + m;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        du[tt] = pv[tt] + cur.mt[tt];
+        dug[(size_t)tt * D] = du[tt];
+      }
+      *reinterpret_cast<float4*>(&pT[m][16 * wave + 4 * q]) = make_float4(du[0], du[1], du[2], du[3]);
     }
-    __syncthreads();  // P complete; every read of dsT done
-    // dS = gam (.) dSn + X - F P, k = 16q + s, in two independent chains per row tile
+    __syncthreads();  // dU complete; every read of dsT done
+    // dS = gam (.) dSn + qg^T dO' - F dU, k = 16q + s, in two independent chains per row tile
     {
       bg_f32x4 acc[2][2] = {};
 #pragma unroll
@@ -970,24 +956,6 @@ void gemm(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
   else gemm_nt<64>(ta, tb, a, s);
 }
 
-// C = op(A) op(B) + sign2 op(A2) op(B2) with `first`'s output, row scale and mask;
-// `second` supplies A2, B2, K2 and the column scale of op(A2).
-template <bool TA, bool TB, bool TA2, bool TB2>
-void gemm2(const GemmArgs& first, const GemmArgs& second, float sign2, hipStream_t s) {
-  Gemm2Args g{};
-  g.a = first;
-  g.A2 = second.A; g.sA2 = second.sA; g.lda2 = second.lda;
-  g.B2 = second.B; g.sB2 = second.sB; g.ldb2 = second.ldb;
-  g.K2 = second.K; g.ks2 = second.ks; g.sks2 = second.sks;
-  g.sign2 = sign2;
-  if (first.N % 128 == 0)
-    hipLaunchKernelGGL((bgemm2_kernel<128, TA, TB, TA2, TB2>), dim3(first.N / 128, first.M / 64, first.batches),
-                       dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((bgemm2_kernel<64, TA, TB, TA2, TB2>), dim3(first.N / 64, first.M / 64, first.batches),
-                       dim3(256), 0, s, g);
-}
-
 // op(A) M x K times op(B) K x N over every batch; strides are per-batch element counts.
 GemmArgs mm(int M, int N, int K, const float* A, int64_t sA, int lda, const float* B, int64_t sB,
             int ldb, float* Cm, int64_t sC, int ldc, int batches) {
@@ -1019,14 +987,13 @@ hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t
   // P = strict_lower(K K^T gated), A = diag(b) P, M = lower_incl(Q K^T gated)
   hipLaunchKernelGGL(bwd_pm_kernel, dim3(NB), dim3(256), 0, s, p, w);
   hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NB), dim3(64), 0, s, w.A, w.T);
-  // MtdO = M^T dO';  F = kg^T diag(b) T^T;  X = qg^T dO' - F MtdO
+  // the scan's chunk-local operands: MtdO = M^T dO';  F = kg^T diag(b) T^T;  X = qg^T dO'
   {
     gemm(true, false, mm(C, D, C, w.M, t2, C, w.dO, t1, D, w.MtdO, t1, D, NB), s);
     GemmArgs f = mm(D, C, C, w.kg, t1, D, w.T, t2, C, w.F, tf, C, NB);
     f.ks = w.beta; f.sks = C;
     gemm(true, true, f, s);
-    gemm2<true, false, false, false>(mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB),
-                                     mm(D, D, C, w.F, tf, C, w.MtdO, t1, D, nullptr, 0, 0, NB), -1.f, s);
+    gemm(true, false, mm(D, D, C, w.qg, t1, D, w.dO, t1, D, w.X, t3, D, NB), s);
   }
   return hipGetLastError();
 }
@@ -1063,16 +1030,13 @@ hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t s)
   return hipGetLastError();
 }
 
-// The gradient products after the scan.  dU = kp dSn + M^T dO' and dY = T^T dU need
-// the scan only; dA = strict_lower(-dY U^T), -diag(b) dY S^T and the gated terms
+// The gradient products after the scan.  dY = T^T dU needs the scan only (it forms
+// dU); dA = strict_lower(-dY U^T), -diag(b) dY S^T and the gated terms
 // also need the state products (U, dM); dkp = U dSn^T needs both but nothing else
 // here, so it may run beside them.
-void launch_dudy(const BwdTiles& w, int NB, hipStream_t s) {
-  const int64_t t1 = C * D, t2 = C * C, t3 = D * D;
-  GemmArgs du = mm(C, D, D, w.kp, t1, D, w.dSn, t3, D, w.dU, t1, D, NB);  // dU = kp dSn + MtdO
-  du.Dm = w.MtdO; du.sD = t1; du.ldd = D;
-  gemm(false, false, du, s);
-  gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);  // dY = T^T dU
+void launch_dy(const BwdTiles& w, int NB, hipStream_t s) {  // dY = T^T dU (the scan formed dU)
+  const int64_t t1 = C * D, t2 = C * C;
+  gemm(true, false, mm(C, D, C, w.T, t2, C, w.dU, t1, D, w.dY, t1, D, NB), s);
 }
 
 void launch_dkp(const BwdTiles& w, int NB, hipStream_t s) {
@@ -1100,7 +1064,7 @@ void launch_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t
 hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
                               int64_t batches, hipStream_t hs, hipStream_t side) {
   const int NB = (int)batches;
-  // Caller's stream:  chunk-local tiles | scan | dU, dY | (state products) dA | dkg, gated
+  // Caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA | dkg, gated
   //                   | (side) finalize
   // Side stream:      (fork) forward with checkpoints | (chunk-local) R, U, dM
   //                   | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
@@ -1140,7 +1104,7 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
       launch_dos(w, NB, side);
       return hipGetLastError();
     });
-    on_hs([&] { launch_dudy(w, NB, hs); });
+    on_hs([&] { launch_dy(w, NB, hs); });
     if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
     on_hs([&] { launch_da(w, NB, hs); });
     if (err == hipSuccess) err = hipEventRecord(ev[kDA], hs);
