@@ -26,15 +26,16 @@
 // forward accepts; the other products only see Gam <= 1, kp = K exp(G_last - G) <= 1
 // and the state.
 // The only serial dependency is dS across chunks: with F = kg^T diag(b) T^T
-// (128 x 64) and X = qg^T dO' - F M^T dO' (128 x 128), both chunk-local,
-//   dS = Diag(gam) dSn - F (kp dSn) + X.
+// (128 x 64) and X = qg^T dO' (128 x 128), both chunk-local,
+//   dU = kp dSn + M^T dO',   dS = Diag(gam) dSn - F dU + X.
 //
 // Layout: the forward pass writes every chunk's start state (fp32) to slot
 // n + floor(bos_n / 64) + c of sequence n's chunk c (slots are distinct across
 // sequences); batch index b = slot * H + h addresses every per-chunk tile.
 // Everything here is fp32: the chunk-local products run as batched tiled GEMMs
-// (fp32 matrix cores), the serial recurrence in four workgroups per (sequence, head), one per
-// 32 value columns.
+// (fp32 matrix cores), the serial recurrence in eight workgroups per (sequence,
+// head), one per 16 value columns.  launch_bwd_streams (at the end) orders the
+// launches on the caller's stream and a second one.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
