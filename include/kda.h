@@ -348,11 +348,11 @@ kda_status kda_release_workspaces(void);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
  * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  It is
- *   (N + ceil(rows / 64) + 1) * H * 820,484 bytes of per-chunk fp32 tiles
+ *   (N + ceil(rows / 64) + 1) * H * 787,716 bytes of per-chunk fp32 tiles
  *   (every (chunk, head)'s operands, products and state checkpoints),
  *   plus rows * H * 256 bytes for the forward pass's outputs,
- * about 12.8 KB per token and head: on a 288 GB device, rows * H of about 22
- * million at most (T = 8K at H = 32 takes 3.5 GB).  A call that cannot get it
+ * about 12.6 KB per token and head: on a 288 GB device, rows * H of about 22
+ * million at most (T = 8K at H = 32 takes 3.3 GB).  A call that cannot get it
  * returns KDA_ERR_HIP. */
 int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H);
 

@@ -830,7 +830,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     size_t off = 0;
     auto take = [&](size_t per) { float* r = base + off; off += (size_t)nb * per; return r; };
     float** t1[] = {&w.G, &w.kg, &w.qg, &w.kp, &w.vv, &w.dO,
-                    &w.R, &w.U, &w.MtdO, &w.dU, &w.dY, &w.dqg, &w.dkg, &w.dkh, &w.dkp};
+                    &w.R, &w.U, &w.MtdO, &w.dU, &w.dY, &w.dqg, &w.dkg, &w.dkp};
     for (float** x : t1) *x = take(64 * 128);
     float** t2[] = {&w.A, &w.P, &w.M, &w.T, &w.dM, &w.dA};
     for (float** x : t2) *x = take(64 * 64);

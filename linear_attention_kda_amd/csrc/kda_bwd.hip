@@ -442,11 +442,25 @@ __global__ void __launch_bounds__(256) bwd_pm_kernel(BwdParams p, BwdTiles w) {
 // dkh_i = H_i sum_{rb >= ib} w(rb, ib) [dM_(rb,ib)^T (q F)_rb + dA_(rb,ib)^T (b k F)_rb]_i, each
 // bracket a 16 x 16 x 16 product on the fp32 matrix cores (dM, dA are already masked).  One
 // workgroup per (batch, 32-channel slice); wave v forms row block v of dqi and dka and row
-// block v of dkh, five block products of each kind per wave.
+// block v of dkh, five block products of each kind per wave.  The same workgroup then
+// finishes its channels: the gradients through each gate, ungated,
+//   dq  = (dO' S^T) Gam + dqi                        (dqg Gam)
+//   dkg = -diag(b) (dY S^T) Gam + dka                 (dkg Gam)
+//   dkh                                               (dkh / Gam, formed ungated)
+//   dkp = (U dSn^T) exp(G_last - G)                   (dkp gam / Gam)
+// so that dqg qg = dq q, dkg kg = dkg' k, dkh kh = dkh' k and dkp kp = dkp' k; then
+// dG_r = dq q + (dkg - dkh - dkp) k per channel, dq, dk = dkg + dkh + dkp, and
+// dg_t = sum_{r >= t} dG_r + dG_last with dG_last = sum_r dkp k + the state term.
 constexpr int GSL = 32, GSS = GSL + 4;
 struct alignas(16) GatedSmem {
-  float kH[C][GSS];
-  float qF[C][GSS];
+  union {
+    float kH[C][GSS];
+    float dG[C][GSS];      // per row and channel, once the products are done
+  };
+  union {
+    float qF[C][GSS];
+    float gl[16][GSL];     // partial sums of dkp k over rows, once the products are done
+  };
   float bkF[C][GSS];
   float G[C][GSS];
   float dM[C][C + 4];
@@ -491,6 +505,24 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
     mv[j] = *reinterpret_cast<const float4*>(w.dM + bidx * (C * C) + r * C + i4);
     av[j] = *reinterpret_cast<const float4*>(w.dA + bidx * (C * C) + r * C + i4);
   }
+  // the finishing step's operands at the product layout (lane (q4, m16) of wave v:
+  // rows 16 v + 4 q4 + e, channels 16 ct + m16 of the slice): issued now, used last
+  const int v0 = t >> 6, q40 = (t & 63) >> 4, m160 = t & 15;
+  float fq[2][4], fk[2][4], fp[2][4];
+  uint32_t kq[2][4];   // k (low half) and q (high half) as bf16
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * v0 + 4 * q40 + e, cc = 16 * ct + m160;
+      const int64_t o = bidx * (C * D) + (int64_t)r * D + c0 + cc;
+      fq[ct][e] = w.dqg[o];
+      fk[ct][e] = w.dkg[o];
+      fp[ct][e] = w.dkp[o];
+      const bool in = r < valid;
+      const int64_t row = (bos + c * C + (in ? r : 0)) * (int64_t)HD + (int64_t)h * D + c0 + cc;
+      kq[ct][e] = in ? (uint32_t)p.k[row] | ((uint32_t)p.q[row] << 16) : 0u;
+    }
   if (t < C) sm.beta[t] = bt;
   if (t < 8) {
 #pragma unroll
@@ -540,6 +572,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
   const int v = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63, q4 = lane >> 4, m16 = lane & 15;
   const bg_f32x4 z4 = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  float dqi[2][4], dka[2][4], dkh[2][4];
   // ---- row form: rows of block rb = v
   {
     const int rb = v;
@@ -575,9 +608,8 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * q4 + e, cc = 16 * ct + m16;
         const float F = expf(sm.G[r][cc] - sm.X[rb][cc]);
-        const int64_t o = bidx * (C * D) + (int64_t)r * D + c0 + cc;
-        w.MtdO[o] = F * aq[ct][e];               // dqi
-        w.dU[o] = sm.beta[r] * F * ak[ct][e];    // dka
+        dqi[ct][e] = F * aq[ct][e];
+        dka[ct][e] = sm.beta[r] * F * ak[ct][e];
       }
   }
   // ---- column form: rows of block ib = v
@@ -610,8 +642,47 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * ib + 4 * q4 + e, cc = 16 * ct + m16;
         const float H = expf(sm.X[ib + 1][cc] - sm.G[i][cc]);
-        w.dkh[bidx * (C * D) + (int64_t)i * D + c0 + cc] = H * ah[ct][e];
+        dkh[ct][e] = H * ah[ct][e];
       }
+  }
+  __syncthreads();  // every read of kH and qF is done: dG and gl overlay them
+  // ---- finish the slice's channels: dq, dk, and dG for the reverse sum
+  {
+    float glp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * v + 4 * q4 + e, cc = 16 * ct + m16;
+        const float G = sm.G[r][cc];
+        const float eg = expf(G), el = expf(sm.G[C - 1][cc] - G);
+        const float dq = fq[ct][e] * eg + dqi[ct][e];
+        const float dkg = fk[ct][e] * eg + dka[ct][e];
+        const float dkp = fp[ct][e] * el;
+        const float kf = bf2f_u16((uint16_t)(kq[ct][e] & 0xffff));
+        const float qf = bf2f_u16((uint16_t)(kq[ct][e] >> 16));
+        sm.dG[r][cc] = dq * qf + (dkg - dkh[ct][e] - dkp) * kf;
+        glp[ct] += dkp * kf;
+        if (r < valid) {
+          const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + c0 + cc;
+          p.dq[row] = dq;
+          p.dk[row] = dkg + dkh[ct][e] + dkp;
+        }
+      }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) sm.gl[4 * v + q4][16 * ct + m16] = glp[ct];
+  }
+  __syncthreads();
+  if (t < GSL) {
+    // dG_last: the kp terms of every row and the state's direct share
+    float run = w.dgl[bidx * D + c0 + t];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) run += sm.gl[x][t];
+    // dg_t = sum_{r >= t} dG_r + dG_last
+    for (int r = C - 1; r >= 0; --r) {
+      run += sm.dG[r][t];
+      if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + c0 + t] = run;
+    }
   }
 }
 
@@ -885,63 +956,6 @@ __global__ void __launch_bounds__(256) bwd_dbeta_dv_kernel(BwdParams p, BwdTiles
   }
 }
 
-// One workgroup per batch: dq, dk and dg of the chunk's rows.
-__global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams p, BwdTiles w) {
-  const int64_t bidx = blockIdx.x;
-  const int valid = w.valid[bidx];
-  if (valid == 0) return;
-  const int64_t slot = bidx / p.H;
-  const int h = (int)(bidx % p.H);
-  const int n = slot_seq(p, slot);
-  const int64_t bos = seq_bos(p, n);
-  const int64_t c = slot - (n + bos / C);
-  const int t = threadIdx.x, ch = t & 127, half = t >> 7;
-  const int HD = p.H * D;
-  const int64_t tb = bidx * (C * D);
-  __shared__ float dGs[C][D];
-  __shared__ float red[2][D];
-  // per row: dG, dq, dk; per channel: dG_last pieces
-  // The gradients through each gate, ungated:
-  //   dq  = (dO' S^T) Gam + dqi                       (dqg Gam)
-  //   dkg = -diag(b) (dY S^T) Gam + dka                (dkg Gam)
-  //   dkh                                              (dkh / Gam, formed ungated)
-  //   dkp = (U dSn^T) exp(G_last - G)                  (dkp gam / Gam)
-  // so that dqg qg = dq q, dkg kg = dkg' k, dkh kh = dkh' k and dkp kp = dkp' k.
-  float glast = 0.f;
-  const float Glast = w.G[tb + (C - 1) * D + ch];
-  for (int r = half; r < C; r += 2) {
-    const int64_t o = tb + r * D + ch;
-    const float G = w.G[o];
-    const float e = expf(G), el = expf(Glast - G);
-    const float dq = w.dqg[o] * e + w.MtdO[o];
-    const float dkg = w.dkg[o] * e + w.dU[o];
-    const float dkh = w.dkh[o];
-    const float dkp = w.dkp[o] * el;
-    // k and q straight from the inputs (exact in fp32; zero past the sequence's end)
-    const int64_t row = (bos + c * C + r) * (int64_t)HD + (int64_t)h * D + ch;
-    const float kf = r < valid ? bf2f_u16(p.k[row]) : 0.f;
-    const float qf = r < valid ? bf2f_u16(p.q[row]) : 0.f;
-    dGs[r][ch] = dq * qf + (dkg - dkh - dkp) * kf;
-    glast += dkp * kf;
-    if (r < valid) {
-      p.dq[row] = dq;
-      p.dk[row] = dkg + dkh + dkp;
-    }
-  }
-  red[half][ch] = glast;
-  __syncthreads();
-  if (half == 0) {
-    // dG_last: the kp terms of both halves and the state's direct share
-    const float dGlast = red[0][ch] + red[1][ch] + w.dgl[bidx * D + ch];
-    // dg_t = sum_{r >= t} dG_r + dG_last
-    float run = dGlast;
-    for (int r = C - 1; r >= 0; --r) {
-      run += dGs[r][ch];
-      if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + ch] = run;
-    }
-  }
-}
-
 template <int NT>
 void gemm_nt(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
   const dim3 grid(a.N / NT, a.M / 64, a.batches), block(256);
@@ -1052,30 +1066,33 @@ void launch_da(const BwdTiles& w, int NB, hipStream_t s) {
   gemm(false, true, da, s);
 }
 
-void launch_dkg_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) {
+void launch_dkg(const BwdTiles& w, int NB, hipStream_t s) {
   const int64_t t1 = C * D, t3 = D * D;
   GemmArgs k1 = mm(C, D, D, w.dY, t1, D, w.S, t3, D, w.dkg, t1, D, NB);  // -diag(b) dY S^T
   k1.rs = w.beta; k1.srs = C; k1.alpha = -1.f;
   gemm(false, true, k1, s);
-  // dM kh, diag(b) dA kh and dkh through the gates, with block references: into the
-  // tiles MtdO and dU (free once dU and dY exist) and dkh
+}
+
+// dM kh, diag(b) dA kh and dkh through the gates, with block references, and the
+// final dq, dk and dg of every valid row
+void launch_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) {
   hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
 }
 
 hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
                               int64_t batches, hipStream_t hs, hipStream_t side) {
   const int NB = (int)batches;
-  // Caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA | dkg, gated
-  //                   | (side) finalize
+  // Caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA | dkg
+  //                   | (side terms) gated terms with dq, dk, dg | (side) end
   // Side stream:      (fork) forward with checkpoints | (chunk-local) R, U, dM
   //                   | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
   // Once the fork is recorded, the caller's stream always waits for the side stream
   // before this returns, so that later work on it (and the workspace's next use)
   // follows everything enqueued here.
-  hipEvent_t ev[6] = {};
-  enum { kFork, kLocal, kProducts, kScan, kDA, kJoin };
+  hipEvent_t ev[7] = {};
+  enum { kFork, kLocal, kProducts, kScan, kSideTerms, kDA, kJoin };
   hipError_t err = hipSuccess;
-  for (int i = 0; i < 6 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  for (int i = 0; i < 7 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
   if (err == hipSuccess && p.cu != nullptr) {
     hipLaunchKernelGGL(bwd_clear_tail_kernel, dim3(512), dim3(256), 0, hs, p);
     err = hipGetLastError();
@@ -1105,6 +1122,7 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
       launch_dos(w, NB, side);
       return hipGetLastError();
     });
+    if (err == hipSuccess) err = hipEventRecord(ev[kSideTerms], side);
     on_hs([&] { launch_dy(w, NB, hs); });
     if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
     on_hs([&] { launch_da(w, NB, hs); });
@@ -1113,14 +1131,15 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
       hipLaunchKernelGGL(bwd_dbeta_dv_kernel, dim3(NB), dim3(256), 0, side, p, w);
       return hipGetLastError();
     });
-    on_hs([&] { launch_dkg_gated(p, w, NB, hs); });
+    on_hs([&] { launch_dkg(w, NB, hs); });
+    if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kSideTerms], 0);
+    on_hs([&] { launch_gated(p, w, NB, hs); });
     hipError_t ej = hipEventRecord(ev[kJoin], side);
     if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, ev[kJoin], 0);
     if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
       (void)hipStreamSynchronize(side);
       if (err == hipSuccess) err = ej;
     }
-    on_hs([&] { hipLaunchKernelGGL(bwd_finalize_kernel, dim3(NB), dim3(256), 0, hs, p, w); });
   }
   for (hipEvent_t e : ev)
     if (e != nullptr) (void)hipEventDestroy(e);

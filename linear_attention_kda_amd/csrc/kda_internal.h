@@ -124,7 +124,7 @@ struct BwdParams {
 // Per-chunk fp32 tiles of the backward, each an array over batches b = slot * H + h.
 struct BwdTiles {
   // [b][64][128]
-  float *G, *kg, *qg, *kp, *vv, *dO, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkh, *dkp;
+  float *G, *kg, *qg, *kp, *vv, *dO, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkp;
   float *A, *P, *M, *T, *dM, *dA;   // [b][64][64]
   float* F;                          // [b][128][64]
   float *S, *X, *dSn;                // [b][128][128]; S: chunk start states (the checkpoints)
@@ -133,7 +133,7 @@ struct BwdTiles {
   float* dgl;                        // [b][128]: the state's direct share of dG_last
   int* valid;                        // [b]
   static constexpr size_t floats_per_batch() {
-    return 15 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1;
+    return 14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1;
   }
 };
 

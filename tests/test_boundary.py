@@ -171,7 +171,7 @@ def test_bwd_check(lib):
 
 def test_bwd_workspace_bytes(lib):
     # slots: N + ceil(rows / 64) + 1, each holding every head's per-chunk tiles
-    per = (15 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1) * 4
+    per = (14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1) * 4
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     nb = (1 + 8192 // 64 + 1) * 32
     assert binding.bwd_workspace_bytes(1, 8192, 32) == up(nb * per) + up(8192 * 32 * 128 * 2)
