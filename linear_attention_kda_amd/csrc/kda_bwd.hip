@@ -305,25 +305,30 @@ __device__ __forceinline__ void bwd_chunk_rows(const BwdParams& p, int64_t bidx,
 // P_ri = sum_c k_rc k_ic exp(G_rc - G_ic) = sum_c (k F)_rc (k H)_ic w(rb, ib)_c, and M
 // likewise with q in the row operand, on the fp32 matrix cores (16 x 16 x 4).  One
 // workgroup per batch; each wave takes two or three of the ten lower block pairs (both
-// products share the column operand), the blocks above the diagonal are zero.
-constexpr int PMS = D + 4;  // row stride (fp32) of the staged operands
+// products share the column operand), the blocks above the diagonal are zero.  The
+// channels go through LDS in two halves of 64 (the products accumulate over both), so
+// that two workgroups fit a CU; the second half's loads are issued before the first
+// half's products.
+constexpr int PMH = 64;        // channels per half
+constexpr int PMS = PMH + 4;   // row stride (fp32) of the staged operands
 struct alignas(16) PmSmem {
   float kF[C][PMS];
   float qF[C][PMS];
   float kH[C][PMS];
-  float wf[kPairs][D];
-  float X[5][D];
-  float tot[2][D];
+  float wf[kPairs][PMH];
+  float X[5][PMH];
   float beta[C];
 };
 
-__device__ __forceinline__ void pm_pair(const PmSmem& sm, const BwdTiles& w, int64_t bidx, int pr) {
+// One half's contribution to pair pr's P and M tiles (lane holds rows 16 rb + 4 q4 + t,
+// column 16 ib + m16).
+__device__ __forceinline__ void pm_pair_acc(const PmSmem& sm, int pr, bg_f32x4& ap, bg_f32x4& am) {
   const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
   const int ib = pr - rb * (rb + 1) / 2;
   const int lane = threadIdx.x & 63, q4 = lane >> 4, m16 = lane & 15;
-  bg_f32x4 ap = bg_f32x4{0.f, 0.f, 0.f, 0.f}, am = ap;
   // channel 16j + 4q4 + s4 of instruction s4: four consecutive channels per lane
-  for (int j = 0; j < D / 16; ++j) {
+#pragma unroll
+  for (int j = 0; j < PMH / 16; ++j) {
     const int c0 = 16 * j + 4 * q4;
     const float4 kf = *reinterpret_cast<const float4*>(&sm.kF[16 * rb + m16][c0]);
     const float4 qf = *reinterpret_cast<const float4*>(&sm.qF[16 * rb + m16][c0]);
@@ -337,7 +342,13 @@ __device__ __forceinline__ void pm_pair(const PmSmem& sm, const BwdTiles& w, int
       am = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[s4], bv[s4], am, 0, 0, 0);
     }
   }
-  // lane holds rows 16 rb + 4 q4 + t, column 16 ib + m16
+}
+
+__device__ __forceinline__ void pm_pair_store(const PmSmem& sm, const BwdTiles& w, int64_t bidx, int pr,
+                                              const bg_f32x4& ap, const bg_f32x4& am) {
+  const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+  const int ib = pr - rb * (rb + 1) / 2;
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, m16 = lane & 15;
   const int i = 16 * ib + m16;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -350,69 +361,96 @@ __device__ __forceinline__ void pm_pair(const PmSmem& sm, const BwdTiles& w, int
   }
 }
 
-__global__ void __launch_bounds__(256) bwd_pm_kernel(BwdParams p, BwdTiles w) {
+// Thread t's share of one channel half: channels 4 (t % 16) .. +3 of the half, rows
+// 4 (t / 16) .. +3 (G as formed by the prep, k and q from the inputs), and the block
+// references of its 16-row block b = t / 64: X_b (zero for b = 0) and X_{b+1}, with X_j
+// the G row 16 j - 1.
+struct PmLoads {
+  float4 G[4], xb, xe;
+  uint2 k[4], q[4];
+};
+
+__device__ __forceinline__ void pm_load(const BwdParams& p, const BwdTiles& w, int64_t bidx, int h,
+                                        int64_t bos, int64_t c, int valid, int half, PmLoads& L) {
+  const int t = threadIdx.x, c4 = PMH * half + 4 * (t & 15), rg = t >> 4, b = rg >> 2;
+  const int HD = p.H * D;
+  const float* Gb = w.G + bidx * (C * D);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * rg + i;
+    L.G[i] = *reinterpret_cast<const float4*>(Gb + r * D + c4);
+    const bool in = r < valid;
+    const int64_t row = (bos + c * C + (in ? r : 0)) * (int64_t)HD + (int64_t)h * D + c4;
+    L.k[i] = in ? *reinterpret_cast<const uint2*>(p.k + row) : make_uint2(0u, 0u);
+    L.q[i] = in ? *reinterpret_cast<const uint2*>(p.q + row) : make_uint2(0u, 0u);
+  }
+  L.xb = b == 0 ? make_float4(0.f, 0.f, 0.f, 0.f)
+                : *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
+  L.xe = *reinterpret_cast<const float4*>(Gb + (16 * b + 15) * D + c4);
+}
+
+// The half's operands into LDS: K F, Q F, K H, the block references and the pair
+// factors w(rb, ib) = exp(X_rb - X_{ib+1}).  Ends with a barrier.
+__device__ __forceinline__ void pm_stage(PmSmem& sm, const PmLoads& L) {
+  const int t = threadIdx.x, cl = 4 * (t & 15), rg = t >> 4;
+  const float xb[4] = {L.xb.x, L.xb.y, L.xb.z, L.xb.w};
+  const float xe[4] = {L.xe.x, L.xe.y, L.xe.z, L.xe.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * rg + i;
+    const float g4[4] = {L.G[i].x, L.G[i].y, L.G[i].z, L.G[i].w};
+    const float kf[4] = {bf2f_u16(L.k[i].x & 0xffff), bf2f_u16(L.k[i].x >> 16),
+                         bf2f_u16(L.k[i].y & 0xffff), bf2f_u16(L.k[i].y >> 16)};
+    const float qf[4] = {bf2f_u16(L.q[i].x & 0xffff), bf2f_u16(L.q[i].x >> 16),
+                         bf2f_u16(L.q[i].y & 0xffff), bf2f_u16(L.q[i].y >> 16)};
+    float kF[4], qF[4], kH[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
+      kF[e] = kf[e] * F;
+      qF[e] = qf[e] * F;
+      kH[e] = kf[e] * H;
+    }
+    *reinterpret_cast<float4*>(&sm.kF[r][cl]) = make_float4(kF[0], kF[1], kF[2], kF[3]);
+    *reinterpret_cast<float4*>(&sm.qF[r][cl]) = make_float4(qF[0], qF[1], qF[2], qF[3]);
+    *reinterpret_cast<float4*>(&sm.kH[r][cl]) = make_float4(kH[0], kH[1], kH[2], kH[3]);
+  }
+  // the first row group of each block holds X_b and X_{b+1}
+  if ((rg & 3) == 0) {
+    const int b = rg >> 2;
+    if (b == 0) *reinterpret_cast<float4*>(&sm.X[0][cl]) = L.xb;
+    *reinterpret_cast<float4*>(&sm.X[b + 1][cl]) = L.xe;
+  }
+  __syncthreads();  // the block references in LDS
+  for (int x = t; x < kPairs * PMH; x += 256) {
+    const int pr = x / PMH, cc = x % PMH;
+    const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+    const int ib = pr - rb * (rb + 1) / 2;
+    sm.wf[pr][cc] = expf(sm.X[rb][cc] - sm.X[ib + 1][cc]);
+  }
+  __syncthreads();
+}
+
+// pairs (0,0) (1,0) (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3)
+// (one 4-bit pair index per slot, no table in memory)
+__device__ __forceinline__ int pm_wave_pair(int wave, int k) {
+  const unsigned packed = wave == 0 ? 0x810u : wave == 1 ? 0x432u : wave == 2 ? 0x65u : 0x97u;
+  return (int)((packed >> (4 * k)) & 15u);
+}
+
+__global__ void __launch_bounds__(256, 2) bwd_pm_kernel(BwdParams p, BwdTiles w) {
   __shared__ PmSmem sm;
   const int64_t bidx = blockIdx.x;
   int h, valid, n;
   int64_t bos, c;
   bwd_chunk_rows(p, bidx, h, bos, c, valid, n);
   const int t = threadIdx.x;
-  const int HD = p.H * D;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   if (t < C) sm.beta[t] = w.beta[bidx * C + t];
-  // thread t: channels 4 (t % 32) .. +3, rows 8 (t / 32) .. +7; every load is issued
-  // before the first use (G as formed by the prep, k and q from the inputs)
-  const int cg = t & 31, rg = t >> 5, c4 = 4 * cg;
-  const float* Gb = w.G + bidx * (C * D);
-  float4 Gv[8], Xv[5];
-  uint2 kv[8], qv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * rg + i;
-    Gv[i] = *reinterpret_cast<const float4*>(Gb + r * D + c4);
-    const bool in = r < valid;
-    const int64_t row = (bos + c * C + (in ? r : 0)) * (int64_t)HD + (int64_t)h * D + c4;
-    kv[i] = in ? *reinterpret_cast<const uint2*>(p.k + row) : make_uint2(0u, 0u);
-    qv[i] = in ? *reinterpret_cast<const uint2*>(p.q + row) : make_uint2(0u, 0u);
-  }
-  Xv[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int b = 1; b <= 4; ++b) Xv[b] = *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
-  if (t < 32) {
-#pragma unroll
-    for (int b = 0; b < 5; ++b) *reinterpret_cast<float4*>(&sm.X[b][c4]) = Xv[b];
-  }
-  {
-    const int b = rg >> 1;  // the 16-row block of this thread's rows
-    const float xb[4] = {Xv[b].x, Xv[b].y, Xv[b].z, Xv[b].w};
-    const float xe[4] = {Xv[b + 1].x, Xv[b + 1].y, Xv[b + 1].z, Xv[b + 1].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 8 * rg + i;
-      const float g4[4] = {Gv[i].x, Gv[i].y, Gv[i].z, Gv[i].w};
-      const float kf[4] = {bf2f_u16(kv[i].x & 0xffff), bf2f_u16(kv[i].x >> 16),
-                           bf2f_u16(kv[i].y & 0xffff), bf2f_u16(kv[i].y >> 16)};
-      const float qf[4] = {bf2f_u16(qv[i].x & 0xffff), bf2f_u16(qv[i].x >> 16),
-                           bf2f_u16(qv[i].y & 0xffff), bf2f_u16(qv[i].y >> 16)};
-      float kF[4], qF[4], kH[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
-        kF[e] = kf[e] * F;
-        qF[e] = qf[e] * F;
-        kH[e] = kf[e] * H;
-      }
-      *reinterpret_cast<float4*>(&sm.kF[r][c4]) = make_float4(kF[0], kF[1], kF[2], kF[3]);
-      *reinterpret_cast<float4*>(&sm.qF[r][c4]) = make_float4(qF[0], qF[1], qF[2], qF[3]);
-      *reinterpret_cast<float4*>(&sm.kH[r][c4]) = make_float4(kH[0], kH[1], kH[2], kH[3]);
-    }
-  }
-  __syncthreads();  // the block references in LDS
-  for (int x = t; x < kPairs * D; x += 256) {
-    const int pr = x / D, cc = x % D;
-    const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
-    const int ib = pr - rb * (rb + 1) / 2;
-    sm.wf[pr][cc] = expf(sm.X[rb][cc] - sm.X[ib + 1][cc]);
-  }
+  PmLoads L;
+  pm_load(p, w, bidx, h, bos, c, valid, 0, L);
+  pm_stage(sm, L);
+  pm_load(p, w, bidx, h, bos, c, valid, 1, L);   // in flight during the first half's products
   // blocks above the diagonal
   for (int x = t; x < C * C; x += 256) {
     const int r = x / C, i = x % C;
@@ -423,14 +461,20 @@ __global__ void __launch_bounds__(256) bwd_pm_kernel(BwdParams p, BwdTiles w) {
       w.M[o] = 0.f;
     }
   }
-  __syncthreads();
-  // pairs (0,0) (1,0) (3,2); (1,1) (2,0) (2,1); (2,2) (3,0); (3,1) (3,3)
-  switch (__builtin_amdgcn_readfirstlane(t >> 6)) {
-    case 0: pm_pair(sm, w, bidx, 0); pm_pair(sm, w, bidx, 1); pm_pair(sm, w, bidx, 8); break;
-    case 1: pm_pair(sm, w, bidx, 2); pm_pair(sm, w, bidx, 3); pm_pair(sm, w, bidx, 4); break;
-    case 2: pm_pair(sm, w, bidx, 5); pm_pair(sm, w, bidx, 6); break;
-    default: pm_pair(sm, w, bidx, 7); pm_pair(sm, w, bidx, 9); break;
-  }
+  const bg_f32x4 z4 = bg_f32x4{0.f, 0.f, 0.f, 0.f};
+  bg_f32x4 ap[3] = {z4, z4, z4}, am[3] = {z4, z4, z4};
+  const int npairs = wave < 2 ? 3 : 2;
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < npairs) pm_pair_acc(sm, pm_wave_pair(wave, k), ap[k], am[k]);
+  __syncthreads();  // the first half's operands are read
+  pm_stage(sm, L);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < npairs) pm_pair_acc(sm, pm_wave_pair(wave, k), ap[k], am[k]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    if (k < npairs) pm_pair_store(sm, w, bidx, pm_wave_pair(wave, k), ap[k], am[k]);
 }
 
 // ---------------------------------------------------------------- gated triangle products
@@ -484,8 +528,9 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
   // every load first: thread t takes channels 4 (t % 8) .. +3 of the slice and rows
   // 2 (t / 8) .. +1 (G, k, q), and 16 entries each of dM and dA
   const int cg = t & 7, rg = t >> 3, c4 = 4 * cg;
+  const int b = rg >> 3;  // the 16-row block of this thread's rows
   const float bt = t < C ? w.beta[bidx * C + t] : 0.f;
-  float4 Gv[2], Xv[5], mv[4], av[4];
+  float4 Gv[2], mv[4], av[4];
   uint2 kv[2], qv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -496,9 +541,11 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
     kv[i] = in ? *reinterpret_cast<const uint2*>(p.k + row) : make_uint2(0u, 0u);
     qv[i] = in ? *reinterpret_cast<const uint2*>(p.q + row) : make_uint2(0u, 0u);
   }
-  Xv[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int b = 1; b <= 4; ++b) Xv[b] = *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
+  // the block references of this thread's block: X_b (zero for b = 0) and X_{b+1}, with
+  // X_j the G row 16 j - 1 (loaded as such: an indexed register array would go to scratch)
+  const float4 xb4 = b == 0 ? make_float4(0.f, 0.f, 0.f, 0.f)
+                            : *reinterpret_cast<const float4*>(Gb + (16 * b - 1) * D + c4);
+  const float4 xe4 = *reinterpret_cast<const float4*>(Gb + (16 * b + 15) * D + c4);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int x = t + 256 * j, r = x >> 4, i4 = (x & 15) * 4;
@@ -524,9 +571,9 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       kq[ct][e] = in ? (uint32_t)p.k[row] | ((uint32_t)p.q[row] << 16) : 0u;
     }
   if (t < C) sm.beta[t] = bt;
-  if (t < 8) {
-#pragma unroll
-    for (int b = 0; b < 5; ++b) *reinterpret_cast<float4*>(&sm.X[b][c4]) = Xv[b];
+  if ((rg & 7) == 0) {  // the first row group of each block
+    if (b == 0) *reinterpret_cast<float4*>(&sm.X[0][c4]) = xb4;
+    *reinterpret_cast<float4*>(&sm.X[b + 1][c4]) = xe4;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -536,9 +583,8 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
   }
   __syncthreads();  // beta
   {
-    const int b = rg >> 3;  // the 16-row block of this thread's rows
-    const float xb[4] = {Xv[b].x, Xv[b].y, Xv[b].z, Xv[b].w};
-    const float xe[4] = {Xv[b + 1].x, Xv[b + 1].y, Xv[b + 1].z, Xv[b + 1].w};
+    const float xb[4] = {xb4.x, xb4.y, xb4.z, xb4.w};
+    const float xe[4] = {xe4.x, xe4.y, xe4.z, xe4.w};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 2 * rg + i;
