@@ -288,6 +288,10 @@ constexpr int kPairs = 10;
 
 __device__ __forceinline__ int bwd_pair(int rb, int ib) { return rb * (rb + 1) / 2 + ib; }
 
+// exp(x) for a natural-log argument on the hardware exp2 (one multiply and v_exp_f32; the
+// rounding of x log2(e) adds a relative error of about |x| 6e-8, results below 2^-126 flush)
+__device__ __forceinline__ float exp_n(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 __device__ __forceinline__ void bwd_chunk_rows(const BwdParams& p, int64_t bidx, int& h, int64_t& bos,
                                                int64_t& c, int& valid, int& n) {
   const int64_t slot = bidx / p.H;
@@ -406,7 +410,7 @@ __device__ __forceinline__ void pm_stage(PmSmem& sm, const PmLoads& L) {
     float kF[4], qF[4], kH[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
+      const float F = exp_n(g4[e] - xb[e]), H = exp_n(xe[e] - g4[e]);
       kF[e] = kf[e] * F;
       qF[e] = qf[e] * F;
       kH[e] = kf[e] * H;
@@ -426,7 +430,7 @@ __device__ __forceinline__ void pm_stage(PmSmem& sm, const PmLoads& L) {
     const int pr = x / PMH, cc = x % PMH;
     const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
     const int ib = pr - rb * (rb + 1) / 2;
-    sm.wf[pr][cc] = expf(sm.X[rb][cc] - sm.X[ib + 1][cc]);
+    sm.wf[pr][cc] = exp_n(sm.X[rb][cc] - sm.X[ib + 1][cc]);
   }
   __syncthreads();
 }
@@ -511,6 +515,7 @@ struct alignas(16) GatedSmem {
   float dA[C][C + 4];
   float wf[kPairs][GSL];
   float X[5][GSL];
+  float part[8][GSL];      // sums of dG over 8-row groups, for the reverse sum
   float beta[C];
 };
 
@@ -597,7 +602,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       float kH[4], qF[4], bkF[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float F = expf(g4[e] - xb[e]), H = expf(xe[e] - g4[e]);
+        const float F = exp_n(g4[e] - xb[e]), H = exp_n(xe[e] - g4[e]);
         kH[e] = kf[e] * H;
         qF[e] = qf[e] * F;
         bkF[e] = br * kf[e] * F;
@@ -611,7 +616,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       const int pr = x / GSL, ch = x % GSL;
       const int rb = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
       const int ib = pr - rb * (rb + 1) / 2;
-      sm.wf[pr][ch] = expf(sm.X[rb][ch] - sm.X[ib + 1][ch]);
+      sm.wf[pr][ch] = exp_n(sm.X[rb][ch] - sm.X[ib + 1][ch]);
     }
   }
   __syncthreads();
@@ -653,7 +658,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * q4 + e, cc = 16 * ct + m16;
-        const float F = expf(sm.G[r][cc] - sm.X[rb][cc]);
+        const float F = exp_n(sm.G[r][cc] - sm.X[rb][cc]);
         dqi[ct][e] = F * aq[ct][e];
         dka[ct][e] = sm.beta[r] * F * ak[ct][e];
       }
@@ -687,7 +692,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * ib + 4 * q4 + e, cc = 16 * ct + m16;
-        const float H = expf(sm.X[ib + 1][cc] - sm.G[i][cc]);
+        const float H = exp_n(sm.X[ib + 1][cc] - sm.G[i][cc]);
         dkh[ct][e] = H * ah[ct][e];
       }
   }
@@ -701,7 +706,7 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * v + 4 * q4 + e, cc = 16 * ct + m16;
         const float G = sm.G[r][cc];
-        const float eg = expf(G), el = expf(sm.G[C - 1][cc] - G);
+        const float eg = exp_n(G), el = exp_n(sm.G[C - 1][cc] - G);
         const float dq = fq[ct][e] * eg + dqi[ct][e];
         const float dkg = fk[ct][e] * eg + dka[ct][e];
         const float dkp = fp[ct][e] * el;
@@ -719,15 +724,31 @@ __global__ void __launch_bounds__(256) bwd_gated_kernel(BwdParams p, BwdTiles w)
     for (int ct = 0; ct < 2; ++ct) sm.gl[4 * v + q4][16 * ct + m16] = glp[ct];
   }
   __syncthreads();
-  if (t < GSL) {
-    // dG_last: the kp terms of every row and the state's direct share
-    float run = w.dgl[bidx * D + c0 + t];
+  // dg_t = dG_last + sum_{r >= t} dG_r, with dG_last the kp terms of every row and the
+  // state's direct share: thread t takes channel t % 32 and rows 8 (t / 32) .. +7; the
+  // eight row groups' sums go through LDS, then each thread walks its rows last first
+  {
+    const int ch = t & (GSL - 1), g8 = t >> 5;
+    float dgv[8], part = 0.f;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) run += sm.gl[x][t];
-    // dg_t = sum_{r >= t} dG_r + dG_last
-    for (int r = C - 1; r >= 0; --r) {
-      run += sm.dG[r][t];
-      if (r < valid) p.dg[((bos + c * C + r) * (int64_t)p.H + h) * D + c0 + t] = run;
+    for (int i = 0; i < 8; ++i) {
+      dgv[i] = sm.dG[8 * g8 + i][ch];
+      part += dgv[i];
+    }
+    sm.part[g8][ch] = part;
+    float run = w.dgl[bidx * D + c0 + ch];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) run += sm.gl[x][ch];
+    __syncthreads();  // the row groups' sums
+#pragma unroll
+    for (int g = 1; g < 8; ++g)
+      if (g > g8) run += sm.part[g][ch];
+    float* dg = p.dg + ((bos + c * C) * (int64_t)p.H + h) * D + c0 + ch;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      const int r = 8 * g8 + i;
+      run += dgv[i];
+      if (r < valid) dg[(int64_t)r * p.H * D] = run;
     }
   }
 }
