@@ -347,13 +347,19 @@ int64_t kda_dim_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H, in
 kda_status kda_release_workspaces(void);
 
 /* Workspace bytes kda_bwd takes for N sequences over `rows` packed rows of H
- * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  It is
- *   (N + ceil(rows / 64) + 1) * H * 787,716 bytes of per-chunk fp32 tiles
- *   (every (chunk, head)'s operands, products and state checkpoints),
- *   plus rows * H * 256 bytes for the forward pass's outputs,
- * about 12.6 KB per token and head: on a 288 GB device, rows * H of about 22
- * million at most (T = 8K at H = 32 takes 3.3 GB).  A call that cannot get it
- * returns KDA_ERR_HIP. */
+ * heads (-1 for N <= 0, rows < 0 or H <= 0).  Host only.  With
+ * s = N + ceil(rows / 64) + 1 chunk slots, it is (each term rounded up to 256 B)
+ *   g * H * 722,180 bytes of per-chunk fp32 tiles for one group of g slots
+ *     (operands and products), g = min(s, floor(8 GiB / (H * 722,180)));
+ *   s * H * 65,536 bytes of fp32 state checkpoints (every chunk's start state);
+ *   2 * H * 65,536 bytes of state-gradient carries when g < s;
+ *   rows * H * 256 bytes for the forward pass's outputs.
+ * Inputs longer than one group go through in groups of g slots, the last group
+ * first, so the size grows by about 1.25 KB per token and head beyond 8 GiB (T = 8K
+ * at H = 32: one group, 3.3 GB; T = 1M at H = 32: 45 groups, 52 GB).  The environment
+ * variable KDA_BWD_GROUP_SLOTS, read at each call, sets g instead (g >= 1; the
+ * results do not depend on it).  A call that cannot get the workspace returns
+ * KDA_ERR_HIP. */
 int64_t kda_bwd_workspace_bytes(int32_t n_sequences, int64_t rows, int32_t H);
 
 #ifdef __cplusplus

@@ -764,11 +764,38 @@ kda_status validate_bwd(const void* q, const void* k, const void* v, const float
 // Chunk slots of the backward: sequence n's chunk c is slot n + floor(bos_n / 64) + c.
 int64_t bwd_slots(int32_t N, int64_t rows) { return (int64_t)N + (rows + 63) / 64 + 1; }
 
-size_t bwd_workspace_bytes(int32_t N, int64_t rows, int32_t H) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t nb = (size_t)bwd_slots(N, rows) * H;
-  return up(nb * kda::BwdTiles::floats_per_batch() * 4) + up((size_t)rows * H * 128 * 2);
+// The backward's per-chunk tiles cover at most this many bytes at once; longer inputs
+// go through in groups of chunk slots (KDA_BWD_GROUP_SLOTS sets the group size).
+constexpr size_t kBwdGroupBytes = size_t(8) << 30;
+
+int64_t bwd_group_slots(int32_t N, int64_t rows, int32_t H) {
+  const int64_t slots = bwd_slots(N, rows);
+  int64_t g = 0;
+  const char* e = std::getenv("KDA_BWD_GROUP_SLOTS");
+  if (e != nullptr && e[0] != '\0') g = std::strtoll(e, nullptr, 10);
+  if (g < 1) g = (int64_t)(kBwdGroupBytes / ((size_t)H * kda::BwdTiles::floats_per_batch() * 4));
+  return g < 1 ? 1 : g > slots ? slots : g;
 }
+
+// Workspace regions: one group's tiles, the checkpoints of every slot, two carry
+// buffers when there is more than one group, the forward pass's outputs.
+struct BwdLayout {
+  size_t tiles, ckpt, carry, out, total;
+};
+
+BwdLayout bwd_layout(int32_t N, int64_t rows, int32_t H) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int64_t slots = bwd_slots(N, rows), gs = bwd_group_slots(N, rows, H);
+  BwdLayout l{};
+  l.tiles = up((size_t)gs * H * kda::BwdTiles::floats_per_batch() * 4);
+  l.ckpt = up((size_t)slots * H * kda::BwdTiles::ckpt_floats_per_batch() * 4);
+  l.carry = gs < slots ? up((size_t)2 * H * 128 * 128 * 4) : 0;
+  l.out = up((size_t)rows * H * 128 * 2);
+  l.total = l.tiles + l.ckpt + l.carry + l.out;
+  return l;
+}
+
+size_t bwd_workspace_bytes(int32_t N, int64_t rows, int32_t H) { return bwd_layout(N, rows, H).total; }
 
 }  // namespace
 
@@ -817,16 +844,20 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
   int cus = 0;
   if (device_cu_count(&cus) != 0)
     return fail(KDA_ERR_HIP, "cannot query the compute-unit count of the current device");
-  const int64_t nb = bwd_slots(N, rows) * H;
-  const size_t wbytes = bwd_workspace_bytes(N, rows, H);
+  const int64_t slots = bwd_slots(N, rows), gslots = bwd_group_slots(N, rows, H);
+  const int64_t nb = gslots * H;   // batches of one group
+  const BwdLayout lay = bwd_layout(N, rows, H);
+  const size_t wbytes = lay.total;
   Workspace ws;
   e = ws.acquire(wbytes, hs);
   if (e != hipSuccess)
     return fail(KDA_ERR_HIP, "backward workspace of %zu bytes: %s", wbytes, hipGetErrorString(e));
-  // carve the per-chunk tiles
+  // carve one group's per-chunk tiles, then the checkpoints, the carries and the
+  // forward pass's outputs
   kda::BwdTiles w{};
+  char* const wbase = static_cast<char*>(ws.ptr());
   {
-    float* base = static_cast<float*>(ws.ptr());
+    float* base = reinterpret_cast<float*>(wbase);
     size_t off = 0;
     auto take = [&](size_t per) { float* r = base + off; off += (size_t)nb * per; return r; };
     float** t1[] = {&w.G, &w.kg, &w.qg, &w.kp, &w.vv, &w.dO,
@@ -835,16 +866,16 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     float** t2[] = {&w.A, &w.P, &w.M, &w.T, &w.dM, &w.dA};
     for (float** x : t2) *x = take(64 * 64);
     w.F = take(128 * 64);
-    w.S = take(128 * 128);
     w.X = take(128 * 128);
     w.dSn = take(128 * 128);
     w.beta = take(64);
     w.gam = take(128);
     w.dgl = take(128);
     w.valid = reinterpret_cast<int*>(take(1));
+    w.S = reinterpret_cast<float*>(wbase + lay.tiles);
   }
-  uint16_t* fwd_out = reinterpret_cast<uint16_t*>(static_cast<char*>(ws.ptr()) +
-                                                   ((nb * kda::BwdTiles::floats_per_batch() * 4 + 255) & ~(size_t)255));
+  float* carry = lay.carry ? reinterpret_cast<float*>(wbase + lay.tiles + lay.ckpt) : nullptr;
+  uint16_t* fwd_out = reinterpret_cast<uint16_t*>(wbase + lay.tiles + lay.ckpt + lay.carry);
   hipError_t err = hipSuccess;
   if (rows > 0) {
     // forward pass with chunk checkpoints (no sequence splitting)
@@ -878,7 +909,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, const float* g, 
     // on a second stream of the library's, beside the work that does not
     hipStream_t side = nullptr;
     err = side_stream(&side);
-    if (err == hipSuccess) err = kda::launch_bwd_streams(p, nsplit, bp, w, nb, hs, side);
+    if (err == hipSuccess) err = kda::launch_bwd_streams(p, nsplit, bp, w, slots, gslots, carry, hs, side);
   } else if (d_initial_state != nullptr) {
     // no tokens: the initial-state gradient is the final-state gradient (or zero)
     kda::BwdParams bp{};

@@ -197,8 +197,8 @@ __global__ void __launch_bounds__(256) bgemm_kernel(GemmArgs a) {
 // q, k, v and dO, 16-byte stores of every tile; the exponentials are exp2 of
 // G log2(e).
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdTiles w) {
-  const int64_t bidx = blockIdx.x;
-  const int64_t slot = bidx / p.H;
+  const int64_t bidx = blockIdx.x;   // the group's batch (tile index)
+  const int64_t slot = p.slot0 + bidx / p.H;
   const int h = (int)(bidx % p.H);
   const int n = slot_seq(p, slot);
   const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
@@ -292,10 +292,12 @@ __device__ __forceinline__ int bwd_pair(int rb, int ib) { return rb * (rb + 1) /
 // rounding of x log2(e) adds a relative error of about |x| 6e-8, results below 2^-126 flush)
 __device__ __forceinline__ float exp_n(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Sequence, head, first row and valid rows of the group's batch bidx (a tile index).
 __device__ __forceinline__ void bwd_chunk_rows(const BwdParams& p, int64_t bidx, int& h, int64_t& bos,
                                                int64_t& c, int& valid, int& n) {
-  const int64_t slot = bidx / p.H;
-  h = (int)(bidx % p.H);
+  const int64_t gb = p.slot0 * p.H + bidx;
+  const int64_t slot = gb / p.H;
+  h = (int)(gb % p.H);
   n = slot_seq(p, slot);
   bos = seq_bos(p, n);
   const int64_t len = seq_len_of(p, n);
@@ -842,15 +844,26 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
   const int64_t bos = seq_bos(p, n), len = seq_len_of(p, n);
   const int nch = (int)((len + C - 1) / C);
   const size_t sd = (size_t)D * D;
-  // this lane's dS entries: rows 32w + 16it + 4q + tt, column j0 + m
+  // the sequence's chunks in this group's slots: c_lo .. c_hi - 1 (chunk c is slot
+  // s_first + c); a sequence without chunks belongs to the group holding slot s_first
+  const int64_t s_first = n + bos / C;
+  const int64_t lo = p.slot0 > s_first ? p.slot0 - s_first : 0;
+  const int64_t hi = p.slot1 - s_first < nch ? p.slot1 - s_first : nch;
+  if (nch == 0 ? (s_first < p.slot0 || s_first >= p.slot1) : lo >= hi) return;  // uniform
+  const int c_lo = (int)lo, c_hi = (int)hi;
+  // this lane's dS entries: rows 32w + 16it + 4q + tt, column j0 + m; the scan starts
+  // from dL/dS_final at the sequence's last chunk, else from the group above's carry
   bg_f32x4 ds[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
+      const size_t e = (size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m;
       float v = 0.f;
-      if (p.dsT) {
-        const size_t o = ((size_t)n * p.H + h) * sd + (size_t)(32 * wave + 16 * it + 4 * q + tt) * D + j0 + m;
+      if (c_hi < nch) {
+        v = p.carry_in[(size_t)h * sd + e];
+      } else if (p.dsT) {
+        const size_t o = ((size_t)n * p.H + h) * sd + e;
         v = p.dsT_fp32 ? static_cast<const float*>(p.dsT)[o] : bf2f_u16(static_cast<const uint16_t*>(p.dsT)[o]);
       }
       ds[it][tt] = v;
@@ -859,11 +872,12 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
   for (int it = 0; it < 2; ++it)
     *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
   ScanOps cur, nxt;
-  if (nch > 0) scan_fetch(w, (n + bos / C + nch - 1) * p.H + h, j0, wave, q, m, cur);
+  const int64_t b_first = (s_first - p.slot0) * p.H + h;   // tile index of chunk 0 (may be negative)
+  if (c_hi > c_lo) scan_fetch(w, b_first + (int64_t)(c_hi - 1) * p.H, j0, wave, q, m, cur);
   __syncthreads();
-  for (int c = nch - 1; c >= 0; --c) {
-    const int64_t bidx = (n + bos / C + c) * p.H + h;
-    if (c > 0) scan_fetch(w, bidx - p.H, j0, wave, q, m, nxt);   // chunk c - 1: in flight meanwhile
+  for (int c = c_hi - 1; c >= c_lo; --c) {
+    const int64_t bidx = b_first + (int64_t)c * p.H;
+    if (c > c_lo) scan_fetch(w, bidx - p.H, j0, wave, q, m, nxt);   // chunk c - 1: in flight meanwhile
     {  // dSn(c) for the chunk's gradient products
       float* dsn = w.dSn + bidx * sd;
 #pragma unroll
@@ -920,10 +934,11 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
     for (int it = 0; it < 2; ++it)
       *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
     __syncthreads();  // the new dS is in place; every read of pT done
-    if (c > 0) cur = nxt;
+    if (c > c_lo) cur = nxt;
   }
-  if (p.ds0) {
-    float* o = p.ds0 + ((size_t)n * p.H + h) * sd;
+  // the sequence's initial-state gradient, or the carry for the group below
+  float* o = c_lo > 0 ? p.carry_out + (size_t)h * sd : p.ds0 ? p.ds0 + ((size_t)n * p.H + h) * sd : nullptr;
+  if (o != nullptr) {
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -989,7 +1004,7 @@ __global__ void __launch_bounds__(256) bwd_dbeta_dv_kernel(BwdParams p, BwdTiles
   const int64_t bidx = blockIdx.x;
   const int valid = w.valid[bidx];
   if (valid == 0) return;
-  const int64_t slot = bidx / p.H;
+  const int64_t slot = p.slot0 + bidx / p.H;
   const int h = (int)(bidx % p.H);
   const int n = slot_seq(p, slot);
   const int64_t bos = seq_bos(p, n);
@@ -1053,11 +1068,13 @@ GemmArgs mm(int M, int N, int K, const float* A, int64_t sA, int lda, const floa
 
 }  // namespace
 
-size_t bwd_tile_floats() { return BwdTiles::floats_per_batch(); }
 
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t s) {
   const BwdTiles w{};
-  launch_ds_scan(p, w, s);
+  BwdParams q = p;   // without tokens sequence n sits at slot n: one group of every slot
+  q.slot0 = 0;
+  q.slot1 = (int64_t)p.nseq + 1;
+  launch_ds_scan(q, w, s);
   return hipGetLastError();
 }
 
@@ -1146,22 +1163,23 @@ void launch_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) 
   hipLaunchKernelGGL(bwd_gated_kernel, dim3((unsigned)NB * (D / GSL)), dim3(256), 0, s, p, w);
 }
 
-hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
-                              int64_t batches, hipStream_t hs, hipStream_t side) {
-  const int NB = (int)batches;
-  // Caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA | dkg
-  //                   | (side terms) gated terms with dq, dk, dg | (side) end
-  // Side stream:      (fork) forward with checkpoints | (chunk-local) R, U, dM
-  //                   | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
+hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p0, const BwdTiles& w0,
+                              int64_t slots, int64_t group_slots, float* carry, hipStream_t hs,
+                              hipStream_t side) {
+  // Per group, caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA
+  //                   | dkg | (side terms) gated terms with dq, dk, dg | (side) end
+  // Side stream:      (fork) forward with checkpoints, first group only | (chunk-local) R, U,
+  //                   dM | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
   // Once the fork is recorded, the caller's stream always waits for the side stream
   // before this returns, so that later work on it (and the workspace's next use)
-  // follows everything enqueued here.
+  // follows everything enqueued here; each group's tiles are reused by the next group
+  // only after that group's end on both streams.
   hipEvent_t ev[7] = {};
   enum { kFork, kLocal, kProducts, kScan, kSideTerms, kDA, kJoin };
   hipError_t err = hipSuccess;
   for (int i = 0; i < 7 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
-  if (err == hipSuccess && p.cu != nullptr) {
-    hipLaunchKernelGGL(bwd_clear_tail_kernel, dim3(512), dim3(256), 0, hs, p);
+  if (err == hipSuccess && p0.cu != nullptr) {
+    hipLaunchKernelGGL(bwd_clear_tail_kernel, dim3(512), dim3(256), 0, hs, p0);
     err = hipGetLastError();
   }
   if (err == hipSuccess) err = hipEventRecord(ev[kFork], hs);
@@ -1176,36 +1194,50 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
         err = hipGetLastError();
       }
     };
-    on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
-    if (err == hipSuccess) err = launch_bwd_chunk_local(p, w, batches, hs);
-    if (err == hipSuccess) err = hipEventRecord(ev[kLocal], hs);
-    on_side(ev[kLocal], [&] { return launch_bwd_state_products(p, w, batches, side); });
-    if (err == hipSuccess) err = hipEventRecord(ev[kProducts], side);
-    if (err == hipSuccess) err = launch_bwd_scan(p, w, hs);
-    if (err == hipSuccess) err = hipEventRecord(ev[kScan], hs);
-    on_side(ev[kScan], [&] {
-      launch_dkp(w, NB, side);
-      hipLaunchKernelGGL(bwd_state_term_kernel, dim3(NB), dim3(256), 0, side, p, w);
-      launch_dos(w, NB, side);
-      return hipGetLastError();
-    });
-    if (err == hipSuccess) err = hipEventRecord(ev[kSideTerms], side);
-    on_hs([&] { launch_dy(w, NB, hs); });
-    if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
-    on_hs([&] { launch_da(w, NB, hs); });
-    if (err == hipSuccess) err = hipEventRecord(ev[kDA], hs);
-    on_side(ev[kDA], [&] {
-      hipLaunchKernelGGL(bwd_dbeta_dv_kernel, dim3(NB), dim3(256), 0, side, p, w);
-      return hipGetLastError();
-    });
-    on_hs([&] { launch_dkg(w, NB, hs); });
-    if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kSideTerms], 0);
-    on_hs([&] { launch_gated(p, w, NB, hs); });
-    hipError_t ej = hipEventRecord(ev[kJoin], side);
-    if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, ev[kJoin], 0);
-    if (ej != hipSuccess) {  // cannot order the side stream's work: wait on the host
+    const size_t sd = (size_t)D * D * p0.H;
+    int k = 0;
+    for (int64_t slot1 = slots; slot1 > 0 && err == hipSuccess; slot1 -= group_slots, ++k) {
+      const int64_t slot0 = slot1 > group_slots ? slot1 - group_slots : 0;
+      BwdParams p = p0;
+      p.slot0 = slot0;
+      p.slot1 = slot1;
+      p.carry_in = carry ? carry + ((k + 1) & 1) * sd : nullptr;
+      p.carry_out = carry ? carry + (k & 1) * sd : nullptr;
+      BwdTiles w = w0;
+      w.S = w0.S + (size_t)slot0 * sd;
+      const int64_t batches = (slot1 - slot0) * p.H;
+      const int NB = (int)batches;
+      if (k == 0) on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
+      if (err == hipSuccess) err = launch_bwd_chunk_local(p, w, batches, hs);
+      if (err == hipSuccess) err = hipEventRecord(ev[kLocal], hs);
+      on_side(ev[kLocal], [&] { return launch_bwd_state_products(p, w, batches, side); });
+      if (err == hipSuccess) err = hipEventRecord(ev[kProducts], side);
+      if (err == hipSuccess) err = launch_bwd_scan(p, w, hs);
+      if (err == hipSuccess) err = hipEventRecord(ev[kScan], hs);
+      on_side(ev[kScan], [&] {
+        launch_dkp(w, NB, side);
+        hipLaunchKernelGGL(bwd_state_term_kernel, dim3(NB), dim3(256), 0, side, p, w);
+        launch_dos(w, NB, side);
+        return hipGetLastError();
+      });
+      if (err == hipSuccess) err = hipEventRecord(ev[kSideTerms], side);
+      on_hs([&] { launch_dy(w, NB, hs); });
+      if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
+      on_hs([&] { launch_da(w, NB, hs); });
+      if (err == hipSuccess) err = hipEventRecord(ev[kDA], hs);
+      on_side(ev[kDA], [&] {
+        hipLaunchKernelGGL(bwd_dbeta_dv_kernel, dim3(NB), dim3(256), 0, side, p, w);
+        return hipGetLastError();
+      });
+      on_hs([&] { launch_dkg(w, NB, hs); });
+      if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kSideTerms], 0);
+      on_hs([&] { launch_gated(p, w, NB, hs); });
+      // the group's end on both streams before the next group reuses the tiles
+      if (err == hipSuccess) err = hipEventRecord(ev[kJoin], side);
+      if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kJoin], 0);
+    }
+    if (err != hipSuccess) {  // the side stream's work may be unordered: wait on the host
       (void)hipStreamSynchronize(side);
-      if (err == hipSuccess) err = ej;
     }
   }
   for (hipEvent_t e : ev)

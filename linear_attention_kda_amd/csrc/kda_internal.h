@@ -119,6 +119,15 @@ struct BwdParams {
   float* dg;
   float* dbeta;           // fp32 [rows][H]
   float* ds0;             // fp32 [N][H][128][128] or null
+  // The slot group of one pass: batches b = slot * H + h with slot0 <= slot < slot1.
+  // The per-chunk tiles hold the group's batches only (tile index b - slot0 * H).
+  // A sequence that continues past slot1 starts its state-gradient scan from
+  // carry_in; one that continues below slot0 leaves its dS in carry_out (both
+  // [H][128][128]; at most one sequence crosses each group boundary).
+  int64_t slot0;
+  int64_t slot1;
+  const float* carry_in;
+  float* carry_out;
 };
 
 // Per-chunk fp32 tiles of the backward, each an array over batches b = slot * H + h.
@@ -127,14 +136,18 @@ struct BwdTiles {
   float *G, *kg, *qg, *kp, *vv, *dO, *R, *U, *MtdO, *dU, *dY, *dqg, *dkg, *dkp;
   float *A, *P, *M, *T, *dM, *dA;   // [b][64][64]
   float* F;                          // [b][128][64]
-  float *S, *X, *dSn;                // [b][128][128]; S: chunk start states (the checkpoints)
+  float *X, *dSn;                    // [b][128][128]
+  float* S;                          // [b][128][128]: chunk start states (the checkpoints); an
+                                     // array over every slot, S pointing at the group's first batch
   float* beta;                       // [b][64]
   float* gam;                        // [b][128]
   float* dgl;                        // [b][128]: the state's direct share of dG_last
   int* valid;                        // [b]
+  // fp32 words per batch of a group, and of the checkpoints (every slot)
   static constexpr size_t floats_per_batch() {
-    return 14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1;
+    return 14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 2 * 128 * 128 + 64 + 2 * 128 + 1;
   }
+  static constexpr size_t ckpt_floats_per_batch() { return 128 * 128; }
 };
 
 struct GemmArgs {
@@ -149,12 +162,16 @@ struct GemmArgs {
   int mask;                               // 0 none, 1 keep n < m, 2 keep n <= m
 };
 
-size_t bwd_tile_floats();
 // The backward pass on two streams: the checkpointing forward pass (`fwd`, with
 // fwd_splits value slices) and the products that need the checkpoints run on
 // `side` beside the chunk-local tiles and the state-gradient scan on `hs`; `hs`
 // waits for `side` before the last kernel, so that everything enqueued is ordered
-// before later work on `hs`.  Parts, in dependency order:
+// before later work on `hs`.  The chunk slots go in groups of at most group_slots,
+// the last group first, each group through every part below with the tiles of
+// `w` (sized for one group; w.S the checkpoints of every slot); the forward pass
+// runs once, before the first group's state products.  `carry` holds two
+// [H][128][128] state-gradient buffers (null when one group covers every slot).
+// Parts, in dependency order:
 //  * chunk_local: the tiles that need no state checkpoint (prep, P / A / M, the
 //    inverse, M^T dO', F and X);
 //  * state_products: R, U and dM, after chunk_local and the forward pass;
@@ -167,7 +184,8 @@ hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int6
                                      hipStream_t stream);
 hipError_t launch_bwd_scan(const BwdParams& p, const BwdTiles& w, hipStream_t stream);
 hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p, const BwdTiles& w,
-                              int64_t batches, hipStream_t hs, hipStream_t side);
+                              int64_t slots, int64_t group_slots, float* carry, hipStream_t hs,
+                              hipStream_t side);
 // The initial-state gradients alone, for calls without tokens.
 hipError_t launch_bwd_scan_only(const BwdParams& p, hipStream_t stream);
 

@@ -169,13 +169,33 @@ def test_bwd_check(lib):
     assert binding.bwd_check(**bwd_args(B=2, cu_seqlens=P, num_seqs=2)) == ERR_VARLEN_BATCH
 
 
-def test_bwd_workspace_bytes(lib):
-    # slots: N + ceil(rows / 64) + 1, each holding every head's per-chunk tiles
-    per = (14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 3 * 128 * 128 + 64 + 2 * 128 + 1) * 4
+def bwd_ws_formula(N, rows, H, g=None):
+    # s = N + ceil(rows / 64) + 1 slots; one group of g slots holds every head's
+    # per-chunk tiles, the checkpoints cover every slot, two carries when g < s
+    per = (14 * 64 * 128 + 6 * 64 * 64 + 128 * 64 + 2 * 128 * 128 + 64 + 2 * 128 + 1) * 4
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    nb = (1 + 8192 // 64 + 1) * 32
-    assert binding.bwd_workspace_bytes(1, 8192, 32) == up(nb * per) + up(8192 * 32 * 128 * 2)
+    s = N + (rows + 63) // 64 + 1
+    if g is None:
+        g = (8 << 30) // (H * per)
+    g = max(1, min(g, s))
+    return (up(g * H * per) + up(s * H * 128 * 128 * 4) + (up(2 * H * 128 * 128 * 4) if g < s else 0)
+            + up(rows * H * 128 * 2))
+
+
+def test_bwd_workspace_bytes(lib, monkeypatch):
+    monkeypatch.delenv("KDA_BWD_GROUP_SLOTS", raising=False)
+    assert binding.bwd_workspace_bytes(1, 8192, 32) == bwd_ws_formula(1, 8192, 32)
+    assert binding.bwd_workspace_bytes(1, 8192, 32) == 3344007424        # one group
+    assert binding.bwd_workspace_bytes(1, 1 << 20, 32) == bwd_ws_formula(1, 1 << 20, 32)
+    assert binding.bwd_workspace_bytes(1, 1 << 20, 32) < 52 * 10**9      # 45 groups
+    assert binding.bwd_workspace_bytes(16, 65536, 32) == bwd_ws_formula(16, 65536, 32)
     assert binding.bwd_workspace_bytes(0, 8192, 32) == -1
+    # the group size knob: read at each call, clamped to [1, slots]
+    for g in (1, 7, 130, 10**6):
+        monkeypatch.setenv("KDA_BWD_GROUP_SLOTS", str(g))
+        assert binding.bwd_workspace_bytes(1, 8192, 32) == bwd_ws_formula(1, 8192, 32, g), g
+    monkeypatch.setenv("KDA_BWD_GROUP_SLOTS", "0")   # not >= 1: the default
+    assert binding.bwd_workspace_bytes(1, 8192, 32) == bwd_ws_formula(1, 8192, 32)
 
 
 def test_dim_workspace_bytes(lib):

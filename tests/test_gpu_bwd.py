@@ -135,6 +135,43 @@ def test_bwd_many_pairs():
     check_bwd(x, do, dsT)
 
 
+GROUP_CASES = [(1, True), (2, True), (3, True), (5, True), (2, False), (3, False)]
+
+
+@pytest.mark.parametrize("group,varlen", GROUP_CASES)
+def test_bwd_slot_groups_match_one_group(group, varlen, monkeypatch):
+    """Chunk slots taken in groups (KDA_BWD_GROUP_SLOTS), the last group first, give
+    the same bytes as one group of every slot: no arithmetic depends on the grouping.
+    Sequences cross group boundaries, one spans several groups, one is empty, and the
+    rows past the last sequence stay zero."""
+    from linear_attention_kda_amd.workloads import cu_from_lengths
+    if varlen:
+        lengths, pad = [1, 64, 0, 300, 65, 150, 33], 20
+        x = random_inputs(1, sum(lengths) + pad, 2, seed=90, device=DEV, init_state="fp32",
+                          n_states=len(lengths))
+        x["cu_seqlens"] = cu_from_lengths(lengths, DEV)
+    else:
+        x = random_inputs(2, 300, 2, seed=92, device=DEV, init_state="bf16")
+    announce(f"bwd slot groups of {group}, varlen={varlen}")
+    do, dsT = upstream(x, 91)
+
+    def run():
+        gr = binding.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["scale"],
+                         initial_state=x["initial_state"], d_final_state=dsT,
+                         cu_seqlens=x["cu_seqlens"])
+        torch.cuda.synchronize()
+        return gr
+
+    monkeypatch.delenv("KDA_BWD_GROUP_SLOTS", raising=False)
+    ref = run()
+    monkeypatch.setenv("KDA_BWD_GROUP_SLOTS", str(group))
+    got = run()
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        assert torch.equal(got[k], ref[k]), f"{k} differs with groups of {group}"
+    if group == 3:   # and against the oracle, grouped
+        check_bwd(x, do, dsT)
+
+
 def test_bwd_no_tokens():
     """T = 0: the initial-state gradient is the final-state gradient."""
     x = random_inputs(2, 0, 2, seed=78, device=DEV, init_state="fp32")
