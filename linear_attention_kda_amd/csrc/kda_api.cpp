@@ -366,6 +366,14 @@ class Workspace {
     hipMemPool_t pool = nullptr;
     err = workspace_pool(&pool);
     if (err == hipSuccess) err = hipMallocFromPoolAsync(&pooled_, bytes, pool, hs);
+    if (err == hipErrorOutOfMemory) {
+      // earlier calls' workspaces, freed on their streams, may still be held by the
+      // pool until a synchronisation: wait for the device, hand them back, retry once
+      (void)hipGetLastError();
+      err = hipDeviceSynchronize();
+      if (err == hipSuccess) err = hipMemPoolTrimTo(pool, 0);
+      if (err == hipSuccess) err = hipMallocFromPoolAsync(&pooled_, bytes, pool, hs);
+    }
     if (err != hipSuccess) pooled_ = nullptr;
     ptr_ = pooled_;
     return err;
