@@ -54,7 +54,8 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int C = 64;          // chunk length
-constexpr int PS = 64 + 8;     // row stride (bf16) of 64-wide tiles: 144 B
+constexpr int PS = 64 + 8;     // row stride (bf16) of the prep's 64-wide LDS tiles: 144 B
+constexpr int RS = 64 + 4;     // row stride (bf16) of the record's 64-wide tiles: 136 B
 constexpr int NT = 256;        // threads per prep workgroup
 // State workgroups: 16 value columns per wave; 64 columns (4 waves) at D = 64,
 // 128 columns (8 waves) at D = 256, where the per-chunk operands are 4x larger.
@@ -69,18 +70,20 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int kLptMax = 256;   // longest-first ordering of the state workgroups up to this many sequences
 
 // Byte offsets inside the record of one (chunk, head).  Rows are padded exactly
-// as the state kernel's LDS tiles (8 bf16 per row) so that staging a record is a
-// straight copy; the padding is never written or read.
+// as the state kernel's LDS tiles (4 bf16 per row: row strides of 2 dwords modulo
+// the 32 LDS banks, so that the 8-byte operand reads of 16 rows spread over every
+// bank) so that staging a record is a straight copy; the padding is never written
+// or read.
 template <int D>
 struct Rec {
-  static constexpr int ks = D + 8;     // row stride (bf16) of kg and qg
+  static constexpr int ks = D + 4;     // row stride (bf16) of kg and qg
   static constexpr int kg = 0;
   static constexpr int qg = kg + C * ks * 2;
   static constexpr int kpt = qg + C * ks * 2;
-  static constexpr int thi = kpt + D * PS * 2;
-  static constexpr int tlo = thi + C * PS * 2;
-  static constexpr int mm = tlo + C * PS * 2;
-  static constexpr int gam = mm + C * PS * 2;
+  static constexpr int thi = kpt + D * RS * 2;
+  static constexpr int tlo = thi + C * RS * 2;
+  static constexpr int mm = tlo + C * RS * 2;
+  static constexpr int gam = mm + C * RS * 2;
   static constexpr int bytes = gam + D * 4;
 };
 static_assert(Rec<64>::bytes % 256 == 0 && Rec<256>::bytes % 256 == 0, "records stay 256-byte aligned");
@@ -225,7 +228,7 @@ __device__ __forceinline__ void pair_store(PrepSmem& sm, __amdgpu_buffer_rsrc_t 
   *reinterpret_cast<float4*>(&sm.as[r * AS + 16 * ib + 4 * q4]) = make_float4(va[0], va[1], va[2], va[3]);
   const uint2 mv = make_uint2(vm[0] | ((uint32_t)vm[1] << 16), vm[2] | ((uint32_t)vm[3] << 16));
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mv),
-                                        rrec, (r * PS + 16 * ib + 4 * q4) * 2, Rec<D>::mm, 0);
+                                        rrec, (r * RS + 16 * ib + 4 * q4) * 2, Rec<D>::mm, 0);
 }
 
 template <int D, bool GS>
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
       const int cr = x >> 3, part = x & 7;
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(u32x4, *reinterpret_cast<const uint4*>(&sm.kt[cr * PS + 8 * part])), rrec,
-          (cr * PS + 8 * part) * 2, Rec<D>::kpt + 64 * pc * PS * 2, 0);
+          (cr * RS + 8 * part) * 2, Rec<D>::kpt + 64 * pc * RS * 2, 0);
     }
     switch (wave) {
       case 0:
@@ -381,7 +384,7 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
     const int ib = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
     const int r = 16 * rb + (e >> 2), i = 16 * ib + 4 * (e & 3);
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rrec,
-                                          (r * PS + i) * 2, Rec<D>::mm, 0);
+                                          (r * RS + i) * 2, Rec<D>::mm, 0);
   }
   __syncthreads();
 
@@ -451,7 +454,7 @@ __global__ void __launch_bounds__(NT) dim_prep_kernel(DimParams p) {
       hv[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
       lv[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
     }
-    const int off = (r * PS + 16 * cb) * 2;
+    const int off = (r * RS + 16 * cb) * 2;
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{hv[0], hv[1], hv[2], hv[3]}, rrec, off, Rec<D>::thi, 0);
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{hv[4], hv[5], hv[6], hv[7]}, rrec, off + 16, Rec<D>::thi, 0);
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{lv[0], lv[1], lv[2], lv[3]}, rrec, off, Rec<D>::tlo, 0);
@@ -517,7 +520,7 @@ __device__ __forceinline__ void chunk_stage(StateSmem<D>& sm, const u32x4* buf, 
 
 template <int D>
 __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(DimParams p) {
-  constexpr int KS = D + 8;
+  constexpr int KS = Rec<D>::ks;
   constexpr int NV = Slice<D>::nv;
   constexpr int VS = NV + 8;
   constexpr int NTS = Slice<D>::nt;
@@ -648,8 +651,8 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
 #pragma unroll
     for (int e = 0; e < 6; ++e) {
       const int ib = e < 2 ? e : 2 + (e - 2) / 2, ks = e < 2 ? 0 : (e - 2) % 2;
-      const __bf16* th = sm.tile(Rec<D>::thi) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
-      const __bf16* tl = sm.tile(Rec<D>::tlo) + (16 * ib + m16) * PS + 32 * ks + 4 * q4;
+      const __bf16* th = sm.tile(Rec<D>::thi) + (16 * ib + m16) * RS + 32 * ks + 4 * q4;
+      const __bf16* tl = sm.tile(Rec<D>::tlo) + (16 * ib + m16) * RS + 32 * ks + 4 * q4;
       tha[e] = ld2x4(th, th + 16);
       tla[e] = ld2x4(tl, tl + 16);
     }
@@ -689,7 +692,7 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
 #pragma unroll
     for (int e = 0; e < 6; ++e) {
       const int rb = e < 2 ? e : 2 + (e - 2) / 2, ks = e < 2 ? 0 : (e - 2) % 2;
-      const __bf16* mp = sm.tile(Rec<D>::mm) + (16 * rb + m16) * PS + 32 * ks + 4 * q4;
+      const __bf16* mp = sm.tile(Rec<D>::mm) + (16 * rb + m16) * RS + 32 * ks + 4 * q4;
       ma[e] = ld2x4(mp, mp + 16);
     }
     bf16x8 uf[2];
@@ -721,7 +724,7 @@ __global__ void __launch_bounds__(Slice<D>::nt, Slice<D>::occ) dim_state_kernel(
         gm[cc] = *reinterpret_cast<const float4*>(sm.rec + Rec<D>::gam + (16 * (c0 + cc) + 4 * q4) * 4);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const __bf16* kp = sm.tile(Rec<D>::kpt) + (16 * (c0 + cc) + m16) * PS + 32 * ks + 4 * q4;
+          const __bf16* kp = sm.tile(Rec<D>::kpt) + (16 * (c0 + cc) + m16) * RS + 32 * ks + 4 * q4;
           kf[cc][ks] = ld2x4(kp, kp + 16);
         }
       }

@@ -200,10 +200,11 @@ def test_bwd_workspace_bytes(lib, monkeypatch):
 
 def test_dim_workspace_bytes(lib):
     # d = 256: one record per (chunk slot, head); slots: N + ceil(rows / 64) + 1.  A
-    # record holds kg, qg (64 rows of d + 8 bf16), kp^T (d rows of 72 bf16), three
-    # tiles of 64 rows of 72 bf16 and d fp32.  d = 64 runs on the fused kernel: none.
+    # record holds kg, qg (64 rows of d + 4 bf16), kp^T (d rows of 68 bf16), three
+    # tiles of 64 rows of 68 bf16 and d fp32.  d = 64 runs on the fused kernel: none.
     d = 256
-    rec = 2 * 64 * (d + 8) * 2 + d * 72 * 2 + 3 * 64 * 72 * 2 + d * 4
+    rec = 2 * 64 * (d + 4) * 2 + d * 68 * 2 + 3 * 64 * 68 * 2 + d * 4
+    assert rec == 128512
     assert binding.dim_workspace_bytes(16, 65536, 32, d) == (16 + 1024 + 1) * 32 * rec
     assert binding.dim_workspace_bytes(1, 65, 2, d) == (1 + 2 + 1) * 2 * rec
     assert binding.dim_workspace_bytes(3, 0, 2, d) == 0
