@@ -79,7 +79,7 @@ constexpr int D = 128;       // head dimension
 constexpr int NT = 512;      // threads per workgroup: 4 state waves + 4 prep waves
 constexpr int NP = 256;      // prep threads
 constexpr int TS = D + 4;    // row stride (bf16) of token-major [64][128] tiles: 264 B
-constexpr int CS = C + 4;    // row stride (bf16) of channel-major [.][64] tiles: 136 B
+constexpr int CS = C + 12;   // row stride (bf16) of channel-major [.][64] tiles: 152 B (room for tcol)
 constexpr int QS = C + 4;    // row stride (bf16) of [64][64] tiles: 136 B
 constexpr int LS = 16 + 4;   // row stride (fp32) of the diagonal-block inverses
 constexpr int NS = 16 + 4;   // row stride (fp32) of the diagonal blocks of A
@@ -158,6 +158,14 @@ __device__ __forceinline__ bf16x4 cvt4(f32x4 v) {
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// Column offset of the channel-major tiles V^T and K'^T: the 64 columns of row r
+// start at column 4 ((r >> 4) & 3) of its 76.  The prep's 8-byte stores put rows 4
+// apart in one instruction, and 8-byte LDS accesses are served 16 lanes at a time
+// over 32 banks, where rows 4 apart fall 8 banks apart (24 with the 38-dword rows):
+// four lanes would share each bank pair.  The offset spreads them; the readers take
+// 16 consecutive rows, which share one offset (known where the row block is).
+__device__ __forceinline__ int tcol(int row, int col) { return col + 4 * ((row >> 4) & 3); }
 
 // (rb, ib) enumeration of the 10 lower-triangular 16x16 block pairs.
 __device__ __forceinline__ int pair_rb(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
@@ -767,15 +775,15 @@ __device__ __forceinline__ void prep_loop(Smem<NV>& sm, const Params& p, const W
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           pw2[j] = __builtin_amdgcn_perm(R.v[2 * j + 1][e >> 1], R.v[2 * j][e >> 1], sel);
-        const int o = (VPT * cg + e) * CS + rg * 8;
-        *reinterpret_cast<uint2*>(&sm.vt[o]) = make_uint2(pw2[0], pw2[1]);
-        *reinterpret_cast<uint2*>(&sm.vt[o + 4]) = make_uint2(pw2[2], pw2[3]);
+        const int row = VPT * cg + e;
+        *reinterpret_cast<uint2*>(&sm.vt[row * CS + tcol(row, rg * 8)]) = make_uint2(pw2[0], pw2[1]);
+        *reinterpret_cast<uint2*>(&sm.vt[row * CS + tcol(row, rg * 8 + 4)]) = make_uint2(pw2[2], pw2[3]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int o = (4 * cg + e) * CS + rg * 8;
-        *reinterpret_cast<uint2*>(&sm.kpt[o]) = kpt_hold[e][0];
-        *reinterpret_cast<uint2*>(&sm.kpt[o + 4]) = kpt_hold[e][1];
+        const int row = 4 * cg + e;
+        *reinterpret_cast<uint2*>(&sm.kpt[row * CS + tcol(row, rg * 8)]) = kpt_hold[e][0];
+        *reinterpret_cast<uint2*>(&sm.kpt[row * CS + tcol(row, rg * 8 + 4)]) = kpt_hold[e][1];
       }
       if (rg == 0) *reinterpret_cast<float4*>(&sm.gamc[4 * cg]) = gamc_hold;
 #pragma unroll
@@ -866,7 +874,7 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
         for (int jt = 0; jt < JT; ++jt) {
           const int jl = jl_base + 16 * jt + m16;
           float vv[4];
-          unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + 16 * b + 4 * q4]), vv);
+          unpack4(*reinterpret_cast<const uint2*>(&sm.vt[jl * CS + tcol(jl, 16 * b + 4 * q4)]), vv);
           Z[b][jt] = f32x4{vv[0], vv[1], vv[2], vv[3]};
           O[b][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -969,8 +977,10 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           for (int t = 0; t < 4; ++t) s[t] *= gv[t];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const __bf16* rowp = &sm.kpt[(16 * ct + m16) * CS + 32 * ks + 4 * q4];
-            s = mfma32(ld2x4(rowp, rowp + 16), cat(U[2 * ks][jt], U[2 * ks + 1][jt]), s);
+            const int row = 16 * ct + m16;
+            const __bf16* rowp = &sm.kpt[row * CS];
+            s = mfma32(ld2x4(rowp + tcol(row, 32 * ks + 4 * q4), rowp + tcol(row, 32 * ks + 16 + 4 * q4)),
+                       cat(U[2 * ks][jt], U[2 * ks + 1][jt]), s);
           }
           Sacc[ct][jt] = s;
         }
