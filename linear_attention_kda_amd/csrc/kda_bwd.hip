@@ -84,11 +84,18 @@ typedef float bg_f32x4 __attribute__((ext_vector_type(4)));
 
 // k-major tiles; a row stride of 16 mod 32 floats puts lane groups q4 and q4 + 1
 // on disjoint banks for the operand reads.  NT is the tile's width (64 or 128).
+// Column c of row k is stored at bg_col(k, c) = c ^ 8 ((k >> 2) & 3): a transposed
+// operand is staged four k rows per group of lanes (rows 4 apart: the same banks
+// with this stride), and the XOR puts the four groups on different banks; it
+// moves whole 8-column blocks, so runs of four columns stay together, and the
+// reads take one k per step, whose XOR is a constant there.
 template <int NT>
 struct BgTiles {
   float A[16][80];
   float B[16][NT + 16];
 };
+
+__device__ __forceinline__ int bg_col(int k, int c) { return c ^ (8 * ((k >> 2) & 3)); }
 
 // acc += sign * op(A) op(B) over K for the 64 x NT tile at (m0, n0); op(A)'s
 // k-th column is scaled by ks[k] when ks is given (sign is +-1: exact).  Wave w
@@ -107,33 +114,34 @@ __device__ __forceinline__ void bg_accumulate(bg_f32x4 (&acc)[2][NT / 32], BgTil
       const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(m0 + m) * lda + k0 + k);
       const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.A[k + e][m] = (ks ? vv[e] * ks[k0 + k + e] : vv[e]) * sign;
+      for (int e = 0; e < 4; ++e) sm.A[k + e][bg_col(k + e, m)] = (ks ? vv[e] * ks[k0 + k + e] : vv[e]) * sign;
     } else {
       const int k = tid >> 4, m = (tid & 15) * 4;
       const float4 v = *reinterpret_cast<const float4*>(A + (int64_t)(k0 + k) * lda + m0 + m);
       const float s = (ks ? ks[k0 + k] : 1.f) * sign;
-      *reinterpret_cast<float4*>(&sm.A[k][m]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
+      *reinterpret_cast<float4*>(&sm.A[k][bg_col(k, m)]) = make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
     }
 #pragma unroll
     for (int h = 0; h < NT / 64; ++h) {
       if (!TB) {
         const int k = tid >> 4, n = 64 * h + (tid & 15) * 4;
-        *reinterpret_cast<float4*>(&sm.B[k][n]) =
+        *reinterpret_cast<float4*>(&sm.B[k][bg_col(k, n)]) =
             *reinterpret_cast<const float4*>(B + (int64_t)(k0 + k) * ldb + n0 + n);
       } else {
         const int n = 64 * h + (tid >> 2), k = (tid & 3) * 4;
         const float4 v = *reinterpret_cast<const float4*>(B + (int64_t)(n0 + n) * ldb + k0 + k);
-        sm.B[k][n] = v.x; sm.B[k + 1][n] = v.y; sm.B[k + 2][n] = v.z; sm.B[k + 3][n] = v.w;
+        const int nc = bg_col(k, n);   // rows k .. k + 3 share the XOR
+        sm.B[k][nc] = v.x; sm.B[k + 1][nc] = v.y; sm.B[k + 2][nc] = v.z; sm.B[k + 3][nc] = v.w;
       }
     }
     __syncthreads();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int k = 4 * s4 + q4;
-      const float a0 = sm.A[k][wm + m16], a1 = sm.A[k][wm + 16 + m16];
+      const float a0 = sm.A[k][bg_col(k, wm + m16)], a1 = sm.A[k][bg_col(k, wm + 16 + m16)];
 #pragma unroll
       for (int j = 0; j < JN; ++j) {
-        const float bj = sm.B[k][wn + 16 * j + m16];
+        const float bj = sm.B[k][bg_col(k, wn + 16 * j + m16)];
         acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bj, acc[0][j], 0, 0, 0);
         acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bj, acc[1][j], 0, 0, 0);
       }
