@@ -101,7 +101,9 @@ typedef enum {
  *             the chunked evaluation: within each 16-token block aligned to the
  *             start of a 64-token chunk, the per-channel sum of -g must stay
  *             below 80 (g >= -5 everywhere is sufficient); beyond that the
- *             intra-chunk exponent factors overflow fp32.
+ *             intra-chunk exponent factors overflow fp32, and the outputs from
+ *             the first such chunk on and the sequence's final state come out
+ *             non-finite (inf or NaN).
  *  beta       device, fp32, [B, T, H], 4-byte aligned: write strength, as given.
  *  scale      multiplies every output (callers usually pass 1/sqrt(d)).
  *  initial_state / initial_dtype

@@ -229,6 +229,26 @@ def test_strong_decay_edge_of_range():
     check(x, out, fin)
 
 
+def test_beyond_range_is_non_finite_not_silent():
+    """Past the documented limit (here -g = 7 on four channels over one 16-token
+    block: a block decay of 112 in natural log) the block's exponent factor
+    overflows fp32.  The rows before that chunk still match the oracle, and the
+    overflow shows as non-finite values in the chunk's outputs and in the final
+    state."""
+    announce("g beyond the range limit: non-finite outputs from the overflowing chunk")
+    x = random_inputs(1, 256, 1, seed=16, device=DEV, init_state="fp32")
+    g = x["g"].cpu()
+    g[:, 144:160, :, 0:4] = -7.0
+    x["g"] = g.to(DEV)
+    out, fin = run_gpu(x, final_dtype=torch.float32)
+    o = host(out)
+    o_ref, _ = oracle_ref(x, None, None, None)
+    assert np.isfinite(o[:, :128]).all()
+    assert rel_err(o[:, :128], o_ref[:, :128]) <= TOL
+    assert not np.isfinite(o[:, 128:192]).all(), "overflow left every output of the chunk finite"
+    assert not np.isfinite(host(fin)).all()
+
+
 def test_mixed_decay_chunks():
     """Chunks whose decay over the chunk exceeds the chunk-level exponent range
     (here -g up to 4.5 on some channels) take the 16-row block references, the
