@@ -203,6 +203,34 @@ def test_bwd_full_size_sampled_heads():
         assert e <= TOL, f"{k} rel err {e:.3e}"
 
 
+def test_bwd_full_size_varlen_groups_match_one_group(monkeypatch):
+    """The 64K-token varlen workload (16 sequences, H = 32) runs in three slot groups by
+    default, with group boundaries inside sequences; one group of every slot gives the
+    same bytes."""
+    from linear_attention_kda_amd.workloads import make_inputs
+    x = make_inputs(2, DEV)
+    N = x["cu_seqlens"].numel() - 1
+    rows, H = x["q"].shape[1], x["q"].shape[2]
+    do, dsT = upstream(x, 83)
+
+    def run():
+        gr = binding.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["scale"],
+                         initial_state=x["initial_state"], d_final_state=dsT,
+                         cu_seqlens=x["cu_seqlens"])
+        torch.cuda.synchronize()
+        return gr
+
+    monkeypatch.delenv("KDA_BWD_GROUP_SLOTS", raising=False)
+    ws_default = binding.bwd_workspace_bytes(N, rows, H)
+    announce(f"bwd 64K varlen H={H}: default groups ({ws_default / 2**30:.1f} GiB) vs one group")
+    got = run()
+    monkeypatch.setenv("KDA_BWD_GROUP_SLOTS", str(10**6))
+    assert binding.bwd_workspace_bytes(N, rows, H) > ws_default   # the default did group
+    ref = run()
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        assert torch.equal(got[k], ref[k]), f"{k} differs between grouped and one-group runs"
+
+
 def test_bwd_strong_decay_edge_of_range():
     """g down to -5 (the forward's documented limit) and up to -1e-4: the per-channel
     decay over a 64-token chunk reaches ~300 in natural log, far past what a chunk-wide
