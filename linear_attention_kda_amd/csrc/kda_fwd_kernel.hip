@@ -322,17 +322,26 @@ __device__ void fix_range(const Params& p, const PlanView& v, int M, const int* 
         for (int jj = 0; jj < F::JJ; ++jj) z[tt][jj] = mfma32(sa[ks][jj], bb, z[tt][jj]);
       }
     }
-    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = JJ wave + jj
-    const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * DK, f.valid * HD * 2);
+    // lane holds o[token 16tt + m16][columns 16jt + 4q4 .. +3], jt = JJ wave + jj.  The
+    // rows go out through the Q~ tile (every wave's reads of it are done at the barrier):
+    // each thread stores 16 bytes that continue its neighbour's along the row, instead of
+    // 8 bytes in each of 16 rows per instruction
+    __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int jj = 0; jj < F::JJ; ++jj) {
-        const uint2 ov = pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u32x2, ov), orsrc,
-            ((16 * tt + m16) * HD + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
-      }
+      for (int jj = 0; jj < F::JJ; ++jj)
+        *reinterpret_cast<uint2*>(&ot[(16 * tt + m16) * TS + 16 * (F::JJ * wave + jj) + 4 * q4]) =
+            pack4(z[tt][jj][0], z[tt][jj][1], z[tt][jj][2], z[tt][jj][3]);
+    __syncthreads();
+    const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * DK, f.valid * HD * 2);
+#pragma unroll
+    for (int x = 0; x < F::QP; ++x) {  // rows past `valid` fall outside the descriptor
+      const int row = F::RPS * x + tid / F::TPR, c8 = 8 * (tid % F::TPR);
+      const uint2 a = *reinterpret_cast<const uint2*>(&ot[row * TS + c8]);
+      const uint2 b = *reinterpret_cast<const uint2*>(&ot[row * TS + c8 + 4]);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, b.x, b.y}, orsrc, (row * HD + c8) * 2, 0, 0);
+    }
     if (more && (cur.slot != f.slot || cur.h != f.h)) fix_state<DK, SEG0 == 2>(p, cur, sa);
     __syncthreads();  // before the next unit's staging
   }
