@@ -285,6 +285,7 @@ struct Work {
   int s0_mode;     // start state: 0 zero, 1 bf16 at s0, 2 fp32 at s0, 3 identity
   int s1_fp32;     // end state stored as fp32 (else bf16)
   int vzero;       // values read as zero
+  int o_lane;      // outputs are a fix-up block's O0, stored in the fix-up's lane order
   const void* s0;  // this (sequence, head)'s 128 x 128 start state
   void* s1;        // where its end state goes, or null
   __bf16* o;       // output rows of the run's first chunk for head h (bf16)
@@ -936,9 +937,15 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           U[b][jt] = cvt4(u);
         }
       }
-      // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor)
-      const auto orsrc = rsrc(w.o + (int64_t)it * w.ochunk, valid * w.orow * 2);
-      const int ovo = (m16 * w.orow + jw_base + 4 * q4) * 2;  // lane part of the store offset
+      // O^T += U^T M^T, store (rows past `valid` fall outside the descriptor).  An O0
+      // block goes in the order its fix-up reads it: the 8 bytes of lane l of wave w for
+      // row block rt and column tile jt at (((4 w + rt) JT + jt) 64 + l) 8, every store one
+      // contiguous 512-byte run (rows past `valid` are written too; their fix-up outputs
+      // are dropped)
+      const bool olane = w.o_lane != 0;
+      const auto orsrc = rsrc(w.o + (int64_t)it * w.ochunk, olane ? C * D * 2 : valid * w.orow * 2);
+      const int ovo = olane ? lane * 8 : (m16 * w.orow + jw_base + 4 * q4) * 2;  // lane part of the offset
+      const int swave = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + m16;
@@ -961,8 +968,8 @@ __device__ __forceinline__ void state_loop(Smem<64 * JT>& sm, const Params& p, c
           for (int t = 0; t < 4; ++t) o[t] *= p.scale;  // Q exp(G) and M are unscaled
           const uint2 ov = pack4(o[0], o[1], o[2], o[3]);
           __builtin_amdgcn_raw_buffer_store_b64(
-              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc,
-              ovo + 32 * jt, 16 * rt * w.orow * 2, 0);
+              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, ov), orsrc, ovo,
+              olane ? ((4 * swave + rt) * JT + jt) * 512 : 16 * rt * w.orow * 2 + 32 * jt, 0);
         }
       }
       // S <- Diag(exp(G_last)) S + K'^T U
@@ -1327,6 +1334,7 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
     w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * DK) + (int64_t)w.h * DK;
     w.orow = p.H * DK;
     w.ochunk = (int64_t)C * p.H * DK;
+    w.o_lane = 0;
     w.vzero = 0;
     w.ck = p.ckpt == nullptr ? nullptr : p.ckpt + ((size_t)(n + bos / C) * p.H + w.h) * (D * D);
   } else {  // segment sp >= 1 from a zero start (odd kind) or from the identity (even kind)
@@ -1343,12 +1351,14 @@ __global__ void __launch_bounds__(NT, 1) kda_fwd_kernel(Params p) {
       w.o = reinterpret_cast<__bf16*>(p.out) + w.bos * (p.H * DK) + (int64_t)w.h * DK;
       w.orow = p.H * DK;
       w.ochunk = (int64_t)C * p.H * DK;
+      w.o_lane = 0;
     } else {      // O0 into the fix-up blocks of its units, one 64 x 128 block per chunk
                   // (its first DK columns used)
       const int ub = sp == 1 ? ubase1 : ubase2 + (sp - 2) * M;
       w.o = reinterpret_cast<__bf16*>(p.o0) + (int64_t)ub * (C * D);
       w.orow = D;
       w.ochunk = (int64_t)C * D;
+      w.o_lane = 1;
     }
     w.ck = nullptr;
     w.vzero = ident ? 1 : 0;

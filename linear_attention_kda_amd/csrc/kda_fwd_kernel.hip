@@ -224,10 +224,12 @@ __device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, Fix
   using F = FixShape<DK>;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, q4 = lane >> 4, m16 = lane & 15;
+  const int lane = tid & 63;
   const int HD = p.H * DK;
   const auto orsrc = rsrc(p.out + f.tok0 * HD + (int64_t)f.h * DK, f.valid * HD * 2);
-  const auto zrsrc = rsrc(p.o0 + (int64_t)f.ob * (C * D), f.valid * D * 2);
+  // the O0 block in the order the main kernel stored it: lane l of wave w reads rows
+  // 16 tt + m16, columns 16 (JJ w + jj) + 4 q4 .. +3 from (((4 w + tt) JJ + jj) 64 + l) 8
+  const auto zrsrc = rsrc(p.o0 + (int64_t)f.ob * (C * D), C * D * 2);
 #pragma unroll
   for (int x = 0; x < F::QP; ++x)
     L.qv[x] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -237,7 +239,7 @@ __device__ __forceinline__ void fix_issue(const Params& p, const FixUnit& f, Fix
 #pragma unroll
     for (int jj = 0; jj < F::JJ; ++jj)
       L.zv[tt][jj] = __builtin_amdgcn_raw_buffer_load_b64(
-          zrsrc, ((16 * tt + m16) * D + 16 * (F::JJ * wave + jj) + 4 * q4) * 2, 0, 0);
+          zrsrc, lane * 8, ((4 * wave + tt) * F::JJ + jj) * 512, 0);
 }
 
 // S_p^T as the products' A operand (bf16, the order the segment's first run or the
