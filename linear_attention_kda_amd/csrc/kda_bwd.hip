@@ -802,8 +802,9 @@ __global__ void __launch_bounds__(64) bwd_inverse_kernel(const float* A, float* 
 //  * dS stays in the MFMA accumulators (rows 32w + 16it + 4q + t, column m); a
 //    transposed copy in LDS is the B operand of the next chunk's kp dSn, and dU
 //    goes through LDS (transposed) as the B operand of F dU.
-//  * The next chunk's kp, F, qg^T dO', M^T dO' and gam are loaded into registers while the
-//    current chunk computes, so the serial loop does not wait on memory.
+//  * The operands (kp, F, qg^T dO', M^T dO', gam) of the next two chunks are in flight
+//    while a chunk computes: three register sets in rotation, the loop unrolled by three
+//    so that no copy between sets waits for a load.
 //  * The 8 column slices of one (sequence, head) run on one XCD (workgroups go
 //    to the XCDs round robin), so the chunk's kp and F, which every slice reads,
 //    come from that XCD's L2 after the first slice's fetch.
@@ -879,13 +880,13 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
 #pragma unroll
   for (int it = 0; it < 2; ++it)
     *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
-  ScanOps cur, nxt;
   const int64_t b_first = (s_first - p.slot0) * p.H + h;   // tile index of chunk 0 (may be negative)
-  if (c_hi > c_lo) scan_fetch(w, b_first + (int64_t)(c_hi - 1) * p.H, j0, wave, q, m, cur);
-  __syncthreads();
-  for (int c = c_hi - 1; c >= c_lo; --c) {
+  auto fetch = [&](int c, ScanOps& o) __attribute__((always_inline)) {
+    scan_fetch(w, b_first + (int64_t)c * p.H, j0, wave, q, m, o);
+  };
+  // one chunk of the recurrence with its operands in `cur`
+  auto step = [&](int c, const ScanOps& cur) __attribute__((always_inline)) {
     const int64_t bidx = b_first + (int64_t)c * p.H;
-    if (c > c_lo) scan_fetch(w, bidx - p.H, j0, wave, q, m, nxt);   // chunk c - 1: in flight meanwhile
     {  // dSn(c) for the chunk's gradient products
       float* dsn = w.dSn + bidx * sd;
 #pragma unroll
@@ -942,7 +943,23 @@ __global__ void __launch_bounds__(256) bwd_ds_scan_kernel(BwdParams p, BwdTiles 
     for (int it = 0; it < 2; ++it)
       *reinterpret_cast<float4*>(&dsT[m][32 * wave + 16 * it + 4 * q]) = make_float4(ds[it][0], ds[it][1], ds[it][2], ds[it][3]);
     __syncthreads();  // the new dS is in place; every read of pT done
-    if (c > c_lo) cur = nxt;
+  };
+  // Chunks last to first with two chunks' operands in flight ahead of the one being
+  // computed: three operand sets in rotation, the loop unrolled by three so that no
+  // copy between sets waits for a load.
+  ScanOps o0, o1, o2;
+  if (c_hi - 1 >= c_lo) fetch(c_hi - 1, o0);
+  if (c_hi - 2 >= c_lo) fetch(c_hi - 2, o1);
+  __syncthreads();
+  for (int c = c_hi - 1; c >= c_lo; c -= 3) {
+    if (c - 2 >= c_lo) fetch(c - 2, o2);
+    step(c, o0);
+    if (c - 1 < c_lo) break;
+    if (c - 3 >= c_lo) fetch(c - 3, o0);
+    step(c - 1, o1);
+    if (c - 2 < c_lo) break;
+    if (c - 4 >= c_lo) fetch(c - 4, o1);
+    step(c - 2, o2);
   }
   // the sequence's initial-state gradient, or the carry for the group below
   float* o = c_lo > 0 ? p.carry_out + (size_t)h * sd : p.ds0 ? p.ds0 + ((size_t)n * p.H + h) * sd : nullptr;
