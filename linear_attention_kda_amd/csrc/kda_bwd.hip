@@ -1142,7 +1142,7 @@ hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int6
   return hipGetLastError();
 }
 
-// dO' S^T: needs the checkpoints only, and only the finalize reads it.
+// dO' S^T: needs the checkpoints only, and only the gated kernel reads it.
 void launch_dos(const BwdTiles& w, int NB, hipStream_t s) {
   const int64_t t1 = C * D, t3 = D * D;
   gemm(false, true, mm(C, D, D, w.dO, t1, D, w.S, t3, D, w.dqg, t1, D, NB), s);
@@ -1191,18 +1191,19 @@ void launch_gated(const BwdParams& p, const BwdTiles& w, int NB, hipStream_t s) 
 hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams& p0, const BwdTiles& w0,
                               int64_t slots, int64_t group_slots, float* carry, hipStream_t hs,
                               hipStream_t side) {
-  // Per group, caller's stream:  chunk-local tiles | scan (and dU) | dY | (state products) dA
-  //                   | dkg | (side terms) gated terms with dq, dk, dg | (side) end
+  // Per group, caller's stream:  chunk-local tiles | scan (and dU) | dY | (forward) dkg,
+  //                   dO' S^T | (state products) dA | (side terms) gated terms with dq, dk, dg
+  //                   | (side) end
   // Side stream:      (fork) forward with checkpoints, first group only | (chunk-local) R, U,
-  //                   dM | (scan) dkp, the state term of dG_last, dO' S^T | (dA) dbeta, dv
+  //                   dM | (scan) dkp, the state term of dG_last | (dA) dbeta, dv
   // Once the fork is recorded, the caller's stream always waits for the side stream
   // before this returns, so that later work on it (and the workspace's next use)
   // follows everything enqueued here; each group's tiles are reused by the next group
   // only after that group's end on both streams.
-  hipEvent_t ev[7] = {};
-  enum { kFork, kLocal, kProducts, kScan, kSideTerms, kDA, kJoin };
+  hipEvent_t ev[8] = {};
+  enum { kFork, kFwd, kLocal, kProducts, kScan, kSideTerms, kDA, kJoin };
   hipError_t err = hipSuccess;
-  for (int i = 0; i < 7 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  for (int i = 0; i < 8 && err == hipSuccess; ++i) err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
   if (err == hipSuccess && p0.cu != nullptr) {
     hipLaunchKernelGGL(bwd_clear_tail_kernel, dim3(512), dim3(256), 0, hs, p0);
     err = hipGetLastError();
@@ -1232,7 +1233,10 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
       w.S = w0.S + (size_t)slot0 * sd;
       const int64_t batches = (slot1 - slot0) * p.H;
       const int NB = (int)batches;
-      if (k == 0) on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
+      if (k == 0) {
+        on_side(ev[kFork], [&] { return launch_fwd(fwd, fwd_splits, side); });
+        if (err == hipSuccess) err = hipEventRecord(ev[kFwd], side);   // the checkpoints exist
+      }
       if (err == hipSuccess) err = launch_bwd_chunk_local(p, w, batches, hs);
       if (err == hipSuccess) err = hipEventRecord(ev[kLocal], hs);
       on_side(ev[kLocal], [&] { return launch_bwd_state_products(p, w, batches, side); });
@@ -1242,11 +1246,17 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
       on_side(ev[kScan], [&] {
         launch_dkp(w, NB, side);
         hipLaunchKernelGGL(bwd_state_term_kernel, dim3(NB), dim3(256), 0, side, p, w);
-        launch_dos(w, NB, side);
         return hipGetLastError();
       });
       if (err == hipSuccess) err = hipEventRecord(ev[kSideTerms], side);
+      // the products that need only dY and the checkpoints run while the side stream
+      // finishes the state products
       on_hs([&] { launch_dy(w, NB, hs); });
+      if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kFwd], 0);
+      on_hs([&] {
+        launch_dkg(w, NB, hs);
+        launch_dos(w, NB, hs);
+      });
       if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kProducts], 0);
       on_hs([&] { launch_da(w, NB, hs); });
       if (err == hipSuccess) err = hipEventRecord(ev[kDA], hs);
@@ -1254,7 +1264,6 @@ hipError_t launch_bwd_streams(const Params& fwd, int fwd_splits, const BwdParams
         hipLaunchKernelGGL(bwd_dbeta_dv_kernel, dim3(NB), dim3(256), 0, side, p, w);
         return hipGetLastError();
       });
-      on_hs([&] { launch_dkg(w, NB, hs); });
       if (err == hipSuccess) err = hipStreamWaitEvent(hs, ev[kSideTerms], 0);
       on_hs([&] { launch_gated(p, w, NB, hs); });
       // the group's end on both streams before the next group reuses the tiles

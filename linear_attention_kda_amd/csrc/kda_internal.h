@@ -176,9 +176,10 @@ struct GemmArgs {
 //    inverse, M^T dO', F and X);
 //  * state_products: R, U and dM, after chunk_local and the forward pass;
 //  * scan: the state gradients over the chunks, after chunk_local only;
-//  * then dU and dY (after the scan), dkp, the state term of dG_last and dO' S^T
-//    (after the scan and the state products, on `side`), dA, dkg and the gated
-//    terms (after both), dbeta and dv (after dA, on `side`), and the finalize.
+//  * then dY (after the scan, which forms dU), -diag(b) dY S^T and dO' S^T (after the
+//    forward pass), dA (after the state products), dkp and the state term of dG_last
+//    (after the scan and the state products, on `side`), the gated terms with dq, dk
+//    and dg (after all of these), dbeta and dv (after dA, on `side`).
 hipError_t launch_bwd_chunk_local(const BwdParams& p, const BwdTiles& w, int64_t batches, hipStream_t stream);
 hipError_t launch_bwd_state_products(const BwdParams& p, const BwdTiles& w, int64_t batches,
                                      hipStream_t stream);
