@@ -28,3 +28,17 @@ def test_varlen_workload_bytes():
     # 65536 tokens, 32 heads, bf16 states in and out for 16 sequences
     b = perfmodel.workload_bytes(65536, 32, 16, 2, 2)
     assert b == 65536 * 32 * 1540 + 2 * 16 * 32 * 128 * 128 * 2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch) exits with
+    status 2 and says so, before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args],
+                           capture_output=True, text=True, env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, (args, env, r.stderr[-300:])
+        assert "one GPU" in r.stderr
